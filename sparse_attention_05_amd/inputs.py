@@ -1,0 +1,333 @@
+"""Seeded synthetic inputs for the DSA decode path.
+
+This module only *makes* inputs: it draws seeded random numbers and stores
+them in the formats the caches use on the device (fp32, bf16 bit patterns,
+OCP fp8-e4m3 codes with a per-row bf16 scale). It holds none of the
+method's arithmetic (no indexer scoring, no selection, no attention); the
+oracle and the HIP path each decode these arrays with their own code.
+
+Shapes and distributions follow the workloads the DSA pages describe:
+a 576-d latent KV row per token (512 latent + 64 RoPE, "GLM-5: from Vibe
+Coding to Agentic Engineering", section 2.1, Multi-latent Attention), a
+128-d indexer key per token with 32 or 64 indexer heads ("Zhipu AI / GLM",
+section 9.1, "DSA index 32x128, top-k 2,048"), and k = 2048.
+
+Every generator is deterministic in its seed: one ``SeedSequence(seed)`` is
+spawned into child streams in a fixed tensor order, so every tensor is
+reproducible on its own and on any machine.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+LATENT_DIM = 576
+VALUE_DIM = 512
+ROPE_DIM = 64
+
+# Child-stream order for SeedSequence.spawn: never reorder, only append.
+_STREAMS = ("q_idx", "head_w", "k_idx", "q_abs", "latent", "boost", "proto", "drift")
+
+
+@dataclass
+class DSAProblem:
+    """One batch of DSA inputs in device storage formats.
+
+    Indexer: ``q_idx`` [R, H_I, D_I], ``head_w`` [R, H_I] fp32, ``k_idx``
+    [rows, D_I] (+ ``k_scale`` [rows] bf16 bits when the keys are fp8).
+    Attention: ``q_abs`` [R, H, 576], ``latent`` [rows, 576].
+    Sequence b owns cache rows ``row_off[b] .. row_off[b]+seq_len[b]-1``;
+    query r belongs to sequence ``q_seq[r]`` at position ``q_pos[r]`` and its
+    candidates are keys 0..q_pos[r] of that sequence.
+
+    Storage: dtype tags are "f32" (float32), "bf16" (uint16 bit patterns)
+    and "fp8_e4m3" (uint8 OCP E4M3FN codes).
+    """
+
+    name: str
+    q_idx: np.ndarray
+    head_w: np.ndarray
+    k_idx: np.ndarray
+    k_scale: Optional[np.ndarray]
+    q_abs: np.ndarray
+    latent: np.ndarray
+    row_off: np.ndarray
+    seq_len: np.ndarray
+    q_seq: np.ndarray
+    q_pos: np.ndarray
+    k: int
+    scale: float
+    act_dtype: str  # dtype of q_idx, q_abs and latent
+    key_dtype: str  # dtype of k_idx
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def R(self) -> int:
+        return int(self.q_pos.shape[0])
+
+    @property
+    def B(self) -> int:
+        return int(self.row_off.shape[0])
+
+    @property
+    def H_I(self) -> int:
+        return int(self.q_idx.shape[1])
+
+    @property
+    def D_I(self) -> int:
+        return int(self.q_idx.shape[2])
+
+    @property
+    def H(self) -> int:
+        return int(self.q_abs.shape[1])
+
+    @property
+    def cache_rows(self) -> int:
+        return int(self.k_idx.shape[0])
+
+    @property
+    def max_n(self) -> int:
+        return int(self.q_pos.max()) + 1
+
+    def is_decode(self) -> bool:
+        """One query per sequence, at its last position."""
+        return (self.R == self.B and np.array_equal(self.q_seq, np.arange(self.B))
+                and np.array_equal(self.q_pos, self.seq_len - 1))
+
+
+# --------------------------------------------------------------------------
+# storage encoders (input preparation only)
+# --------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_round_up(x: np.ndarray) -> np.ndarray:
+    """Smallest bf16 not below each positive float32 value (bits)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = f32_to_bf16_bits(x)
+    back = (b.astype(np.uint32) << 16).view(np.float32)
+    return np.where(back < x, b + 1, b).astype(np.uint16)
+
+
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Encode float32 values as OCP E4M3FN codes (nearest, ties to even).
+
+    Inputs must lie within +-448. torch's float8_e4m3fn cast is the encoder.
+    """
+    import torch
+
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.size and float(np.abs(x).max()) > 448.0:
+        raise ValueError("e4m3 input out of range")
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0,
+                 chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, std^2) samples stored as bf16 bits, generated in bounded chunks."""
+    total = int(np.prod(shape))
+    out = np.empty(total, dtype=np.uint16)
+    for lo in range(0, total, chunk):
+        hi = min(total, lo + chunk)
+        v = rng.standard_normal(hi - lo, dtype=np.float32)
+        if std != 1.0:
+            v *= np.float32(std)
+        out[lo:hi] = f32_to_bf16_bits(v)
+    return out.reshape(shape)
+
+
+def _streams(seed: int):
+    children = np.random.SeedSequence(seed).spawn(len(_STREAMS))
+    return {name: np.random.Generator(np.random.PCG64(c)) for name, c in zip(_STREAMS, children)}
+
+
+def _offsets(seq_lens: Sequence[int]) -> np.ndarray:
+    off = np.zeros(len(seq_lens), dtype=np.int64)
+    if len(seq_lens) > 1:
+        off[1:] = np.cumsum(np.asarray(seq_lens[:-1], dtype=np.int64))
+    return off
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+
+def tiny_config(seed: int = 0, quantized: bool = False, n_keys: int = 512,
+                n_queries: int = 16, k: int = 64) -> DSAProblem:
+    """The tiny CPU-checkable case: one causal sequence of 512 keys with 16
+    queries at the last positions; indexer 4 heads x 64, fp32; k = 64;
+    attention 8 heads over fp32 576-d latent rows; scale 1/sqrt(192).
+
+    ``quantized=True`` draws every indexer input from a small integer grid
+    (q, k in {-4..3}, w in eighths) so every score is exact in fp32 under any
+    summation order.
+    """
+    st = _streams(seed)
+    H_I, D_I, H = 4, 64, 8
+    if quantized:
+        q_idx = st["q_idx"].integers(-4, 4, size=(n_queries, H_I, D_I)).astype(np.float32)
+        k_idx = st["k_idx"].integers(-4, 4, size=(n_keys, D_I)).astype(np.float32)
+        head_w = (st["head_w"].integers(1, 9, size=(n_queries, H_I)) / 8.0).astype(np.float32)
+    else:
+        q_idx = st["q_idx"].standard_normal((n_queries, H_I, D_I), dtype=np.float32)
+        k_idx = st["k_idx"].standard_normal((n_keys, D_I), dtype=np.float32)
+        head_w = st["head_w"].random((n_queries, H_I), dtype=np.float32)
+    q_abs = st["q_abs"].standard_normal((n_queries, H, LATENT_DIM), dtype=np.float32)
+    latent = (st["latent"].standard_normal((n_keys, LATENT_DIM), dtype=np.float32)
+              * np.float32(0.1))
+    return DSAProblem(
+        name="tiny-quantized" if quantized else "tiny",
+        q_idx=q_idx, head_w=head_w, k_idx=k_idx, k_scale=None,
+        q_abs=q_abs, latent=latent,
+        row_off=np.zeros(1, np.int64), seq_len=np.array([n_keys], np.int32),
+        q_seq=np.zeros(n_queries, np.int32),
+        q_pos=np.arange(n_keys - n_queries, n_keys, dtype=np.int32),
+        k=k, scale=1.0 / math.sqrt(192.0), act_dtype="f32", key_dtype="f32",
+        meta={"seed": seed},
+    )
+
+
+def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: int = 128,
+                  H: int = 64, k: int = 2048, key_dtype: str = "bf16",
+                  boost_frac: float = 0.0, boost_sigma: float = 4.0,
+                  tie_levels: int = 0, latent_std: float = 0.1,
+                  name: str = "decode") -> DSAProblem:
+    """Decode batch: one new query per sequence at its last position.
+
+    * indexer queries N(0,1) bf16, head weights U(0,1) fp32, keys N(0,1);
+    * ``key_dtype="fp8_e4m3"`` stores keys as OCP E4M3FN codes with a per-row
+      bf16 scale = (row max |k|) / 448, rounded up so no code saturates;
+    * ``boost_frac`` > 0 adds, to that seeded fraction of each sequence's
+      keys, a vector along the sequence's mean indexer query, sized so the
+      mean per-head dot of a boosted key rises by ``boost_sigma`` standard
+      deviations of the dot (sqrt(D_I) for unit-variance inputs) -- salient
+      tokens with heavy-tailed scores;
+    * ``tie_levels`` > 0 makes every indexer key one of ``tie_levels``
+      prototype rows with entries in {-4..3}, indexer queries in {-4..3} and
+      head weights in {1/8..8/8}: every score of a query takes one of at most
+      ``tie_levels`` values, all exact in fp32, so large tie classes straddle
+      the k-th rank;
+    * absorbed queries N(0,1) bf16, latent rows N(0, latent_std^2) bf16.
+    """
+    st = _streams(seed)
+    B = len(seq_lens)
+    seq_lens = [int(s) for s in seq_lens]
+    rows = int(sum(seq_lens))
+    row_off = _offsets(seq_lens)
+
+    if tie_levels:
+        q_f = st["q_idx"].integers(-4, 4, size=(B, H_I, D_I)).astype(np.float32)
+        head_w = (st["head_w"].integers(1, 9, size=(B, H_I)) / 8.0).astype(np.float32)
+        protos = st["proto"].integers(-4, 4, size=(tie_levels, D_I)).astype(np.float32)
+        choice = st["k_idx"].integers(0, tie_levels, size=rows)
+        k_f = protos[choice]
+        q_idx = f32_to_bf16_bits(q_f)
+        k_store = f32_to_bf16_bits(k_f)
+        k_scale = None
+        if key_dtype != "bf16":
+            raise ValueError("tie-class inputs are stored as bf16")
+    else:
+        q_idx = _normal_bf16(st["q_idx"], (B, H_I, D_I))
+        head_w = st["head_w"].random((B, H_I), dtype=np.float32)
+        k_scale = None
+        if key_dtype == "bf16" and not boost_frac:
+            k_store = _normal_bf16(st["k_idx"], (rows, D_I))
+        else:
+            k_f = st["k_idx"].standard_normal((rows, D_I), dtype=np.float32)
+            if boost_frac:
+                q_vals = (q_idx.astype(np.uint32) << 16).view(np.float32).reshape(B, H_I, D_I)
+                rb = st["boost"]
+                for b in range(B):
+                    mean_q = q_vals[b].mean(axis=0)
+                    u = mean_q / np.linalg.norm(mean_q)
+                    per_head = q_vals[b] @ u            # dot of each head's query with u
+                    amp = boost_sigma * math.sqrt(D_I) / float(per_head.mean())
+                    nb = seq_lens[b]
+                    sel = rb.random(nb) < boost_frac
+                    seg = k_f[row_off[b]:row_off[b] + nb]
+                    seg[sel] += np.float32(amp) * u.astype(np.float32)
+            if key_dtype == "bf16":
+                k_store = f32_to_bf16_bits(k_f)
+            elif key_dtype == "fp8_e4m3":
+                rowmax = np.abs(k_f).max(axis=1)
+                rowmax = np.where(rowmax > 0, rowmax, np.float32(1.0))
+                k_scale = bf16_bits_round_up(rowmax / np.float32(448.0))
+                sc = (k_scale.astype(np.uint32) << 16).view(np.float32)
+                k_store = f32_to_e4m3_codes(np.clip(k_f / sc[:, None], -448.0, 448.0))
+            else:
+                raise ValueError(f"unknown key dtype {key_dtype}")
+
+    q_abs = _normal_bf16(st["q_abs"], (B, H, LATENT_DIM))
+    latent = _normal_bf16(st["latent"], (rows, LATENT_DIM), std=latent_std)
+    seq_len = np.asarray(seq_lens, np.int32)
+    return DSAProblem(
+        name=name, q_idx=q_idx, head_w=head_w, k_idx=k_store, k_scale=k_scale,
+        q_abs=q_abs, latent=latent, row_off=row_off, seq_len=seq_len,
+        q_seq=np.arange(B, dtype=np.int32), q_pos=seq_len - 1,
+        k=k, scale=1.0 / math.sqrt(192.0), act_dtype="bf16", key_dtype=key_dtype,
+        meta={"seed": seed, "boost_frac": boost_frac, "tie_levels": tie_levels},
+    )
+
+
+def prefill_config(T: int = 8192, seed: int = 0, H_I: int = 64, D_I: int = 128,
+                   H: int = 64, k: int = 2048, drift: float | None = None,
+                   query_rows: Optional[np.ndarray] = None,
+                   name: str = "prefill") -> DSAProblem:
+    """Causal prefill of one T-token sequence: query t scores keys 0..t.
+
+    Indexer keys N(0,1) plus a linear positional drift ``drift*(s/(T-1))*u``
+    along a seeded unit vector u, and every indexer query gets ``+u``, so
+    later keys score higher on average (a recency bias). The default drift
+    is sqrt(D_I): the mean per-head dot rises by one dot standard deviation
+    from the first key to the last. ``query_rows`` restricts the queries to
+    those positions (all T when None).
+    """
+    st = _streams(seed)
+    if drift is None:
+        drift = math.sqrt(D_I)
+    u = st["drift"].standard_normal(D_I).astype(np.float32)
+    u /= np.linalg.norm(u)
+    pos = np.arange(T, dtype=np.int32) if query_rows is None else np.asarray(query_rows, np.int32)
+    R = int(pos.shape[0])
+    q_f = st["q_idx"].standard_normal((T, H_I, D_I), dtype=np.float32)[pos] + u
+    k_f = st["k_idx"].standard_normal((T, D_I), dtype=np.float32)
+    k_f += (np.float32(drift) * (np.arange(T, dtype=np.float32) / max(T - 1, 1)))[:, None] * u
+    head_w = st["head_w"].random((T, H_I), dtype=np.float32)[pos]
+    q_abs = _normal_bf16(st["q_abs"], (T, H, LATENT_DIM))[pos]
+    latent = _normal_bf16(st["latent"], (T, LATENT_DIM), std=0.1)
+    return DSAProblem(
+        name=name, q_idx=f32_to_bf16_bits(q_f), head_w=head_w,
+        k_idx=f32_to_bf16_bits(k_f), k_scale=None, q_abs=q_abs, latent=latent,
+        row_off=np.zeros(1, np.int64), seq_len=np.array([T], np.int32),
+        q_seq=np.zeros(R, np.int32), q_pos=pos.copy(), k=k,
+        scale=1.0 / math.sqrt(192.0), act_dtype="bf16", key_dtype="bf16",
+        meta={"seed": seed, "drift": drift},
+    )
+
+
+# Named workloads. The full sizes are the measured shapes; the "small"
+# variants keep the structure at sizes the oracle finishes in seconds.
+def workload(name: str, seed: int = 0) -> DSAProblem:
+    if name == "tiny":
+        return tiny_config(seed)
+    if name == "tiny-quantized":
+        return tiny_config(seed, quantized=True)
+    if name == "decode-32k":
+        return decode_config([32768] * 4, seed=seed, name=name)
+    if name == "decode-128k-fp8":
+        return decode_config([131072] * 7 + [200000], seed=seed, key_dtype="fp8_e4m3",
+                             boost_frac=0.02, name=name)
+    if name == "ties-64k":
+        return decode_config([65536] * 16, seed=seed, tie_levels=8, name=name)
+    if name == "prefill-8k":
+        return prefill_config(8192, seed=seed, name=name)
+    raise KeyError(name)

@@ -1,0 +1,87 @@
+"""The pins have teeth: each plausible oracle mistake, planted here on the
+CPU by swapping one oracle function for a mutated copy, makes at least one
+pin fail. The real oracle is restored after every case."""
+import numpy as np
+import pytest
+
+from oracle import dsa_oracle as O
+import test_oracle_attention as TA
+import test_oracle_indexer as TI
+import test_oracle_topk as TT
+
+
+def _no_relu(q, w, keys):
+    return ((keys @ q.T) @ w).astype(np.float32)
+
+
+def _w_reversed(q, w, keys):
+    z = keys @ q.T
+    return (np.where(z > 0, z, 0) @ w[::-1]).astype(np.float32)
+
+
+def _unstable(scores, k):
+    s = np.asarray(scores, np.float32).astype(np.float64)
+    order = np.argsort(-s, kind="stable")[::-1]
+    order = order[np.argsort(-s[order], kind="stable")]   # ties end up high index first
+    out = np.full(k, -1, np.int32)
+    out[:min(k, s.size)] = order[:min(k, s.size)]
+    return out
+
+
+def _ascending(scores, k):
+    s = np.asarray(scores, np.float32).astype(np.float64)
+    order = np.argsort(s, kind="stable")
+    out = np.full(k, -1, np.int32)
+    out[:min(k, s.size)] = order[:min(k, s.size)]
+    return out
+
+
+def _value_from_rope_end(q, rows, scale):
+    p, logits = O.attention_weights(q, rows, scale)
+    mx = logits.max(axis=1)
+    return p @ rows[:, 64:], mx + np.log(np.exp(logits - mx[:, None]).sum(axis=1))
+
+
+def _no_scale(q, rows, scale):
+    return _orig_attn(q, rows, 1.0)
+
+
+def _latent_only_logits(q, rows, scale):
+    return _orig_attn(q[:, :512], rows[:, :512], scale) if rows.shape[0] else _orig_attn(q, rows, scale)
+
+
+_orig_attn = O.sparse_mla_row
+
+
+def _causal_off_by_one(prob, rows=None):
+    rows = range(prob.R) if rows is None else rows
+    q_all = O.decode(prob.q_idx, prob.act_dtype)
+    w_all = np.asarray(prob.head_w, np.float64)
+    return [O.index_scores_row(q_all[r], w_all[r], O.indexer_keys(prob, int(prob.q_seq[r]), int(prob.q_pos[r])))
+            for r in rows]
+
+
+def _fp8_no_scale(prob, b, n):
+    lo = int(prob.row_off[b])
+    return O.decode(prob.k_idx[lo:lo + n], prob.key_dtype)
+
+
+CASES = [
+    ("index_scores_row", _no_relu, [TI.test_relu_zeroes_negative_dots, TI.test_golden_hand_case]),
+    ("index_scores_row", _w_reversed, [TI.test_head_weights_follow_their_head]),
+    ("index_scores", _causal_off_by_one, [TI.test_causal_bound_includes_own_key]),
+    ("indexer_keys", _fp8_no_scale, [TI.test_fp8_keys_use_row_scale]),
+    ("topk_row", _unstable, [TT.test_all_equal_is_index_order, TT.test_golden_hand_case]),
+    ("topk_row", _ascending, [TT.test_strictly_increasing_gives_latest_first]),
+    ("sparse_mla_row", _value_from_rope_end, [TA.test_single_key_gives_its_value_rows, TA.test_golden_hand_case]),
+    ("sparse_mla_row", _no_scale, [TA.test_dense_equals_sdpa_when_k_covers_context]),
+    ("sparse_mla_row", _latent_only_logits, [TA.test_golden_hand_case]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", CASES, ids=[f"{c[0]}:{c[1].__name__}" for c in CASES])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setattr(O, name, mutant)
+    for pin in pins:
+        with pytest.raises(AssertionError):
+            pin()

@@ -1,0 +1,91 @@
+"""Whole-path pins of the oracle and checks of the seeded input generators."""
+import numpy as np
+import torch
+
+from oracle import dsa_oracle as O
+from sparse_attention_05_amd import inputs
+from test_oracle_topk import brute_topk_np
+
+
+def _check_index_invariants(idx, q_pos, k):
+    for r in range(idx.shape[0]):
+        n = int(q_pos[r]) + 1
+        k_eff = min(k, n)
+        row = idx[r]
+        assert (row[:k_eff] >= 0).all() and (row[:k_eff] <= q_pos[r]).all()
+        assert len(set(row[:k_eff].tolist())) == k_eff
+        assert (row[k_eff:] == -1).all()
+
+
+def test_tiny_pipeline_invariants_and_repeatability():
+    p = inputs.tiny_config(seed=0)
+    s1, i1, o1, l1 = O.dsa_forward(p)
+    s2, i2, o2, l2 = O.dsa_forward(p)
+    _check_index_invariants(i1, p.q_pos, p.k)
+    assert np.array_equal(i1, i2) and np.array_equal(o1, o2)
+    for r in range(p.R):
+        assert np.array_equal(i1[r], brute_topk_np(s1[r], p.k))
+    assert o1.shape == (16, 8, 512) and l1.shape == (16, 8)
+
+
+def test_tie_classes_give_few_exact_levels():
+    p = inputs.decode_config([3000, 4100], seed=4, H_I=16, H=16, k=256, tie_levels=8)
+    scores = O.index_scores(p)
+    for r, s in enumerate(scores):
+        assert len(np.unique(s)) <= 8
+        # eighths of integers, small enough to be exact in fp32
+        assert np.array_equal(s * 8, np.round(s * 8))
+        assert np.abs(s).max() < 2 ** 21
+        idx = O.topk_row(s, p.k)
+        assert np.array_equal(idx, brute_topk_np(s, p.k))
+        thr = s[idx[-1]]
+        assert (s == thr).sum() > (s[idx] == thr).sum()   # the class straddles k
+
+
+def test_generators_are_seeded():
+    a = inputs.decode_config([300, 500], seed=7, H_I=16, H=16, k=64)
+    b = inputs.decode_config([300, 500], seed=7, H_I=16, H=16, k=64)
+    c = inputs.decode_config([300, 500], seed=8, H_I=16, H=16, k=64)
+    for f in ("q_idx", "head_w", "k_idx", "q_abs", "latent"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+        assert not np.array_equal(getattr(a, f), getattr(c, f))
+    assert a.row_off.tolist() == [0, 300] and a.q_pos.tolist() == [299, 499]
+    assert a.is_decode()
+
+
+def test_bf16_encoder_matches_torch_rounding():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * 10).astype(np.float32)
+    ours = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_fp8_keys_round_trip_within_half_step():
+    p = inputs.decode_config([257, 300], seed=1, H_I=16, H=16, k=64, key_dtype="fp8_e4m3",
+                             boost_frac=0.05)
+    k = O.indexer_keys(p, 0, 257)
+    sc = O.bf16_to_f64(p.k_scale[:257])
+    assert (sc > 0).all()
+    # every code is finite and the largest magnitude of a row sits near 448*scale
+    assert np.isfinite(k).all()
+    assert (np.abs(k).max(axis=1) <= 448 * sc).all()
+    # scale is rowmax/448 rounded up to bf16, so the largest code lands on 416 or 448
+    assert (np.abs(k).max(axis=1) >= 416 * sc).all()
+
+
+def test_boost_raises_selected_scores():
+    p = inputs.decode_config([4000], seed=2, H_I=64, H=16, k=256, key_dtype="fp8_e4m3",
+                             boost_frac=0.02)
+    s = O.index_scores(p)[0]
+    top = O.topk_row(s, 80)
+    # the boosted 2% dominate the top of the ranking
+    assert np.median(s[top]) > np.median(s) + 4 * s.std()
+
+
+def test_prefill_subset_rows_match_full_rows():
+    full = inputs.prefill_config(T=300, seed=3, H_I=16, H=16, k=64)
+    sub = inputs.prefill_config(T=300, seed=3, H_I=16, H=16, k=64, query_rows=np.array([0, 150, 299]))
+    assert np.array_equal(sub.q_idx, full.q_idx[[0, 150, 299]])
+    assert np.array_equal(sub.q_abs, full.q_abs[[0, 150, 299]])
+    assert np.array_equal(sub.k_idx, full.k_idx)
