@@ -1,0 +1,201 @@
+"""Benchmark of the DSA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode-32k]
+
+A step is one fused decode (lightning indexer -> deterministic top-k ->
+sparse MLA) over a batch of 4 sequences at 32,768 tokens of context, k=2048,
+64 indexer heads x 128 and 64 MLA heads over 576-d bf16 latent rows (one new
+query per sequence, so tokens/step = batch). Inputs are seeded synthetic
+arrays, resident in HBM before timing starts; the step cycles through
+several copies of the caches so that repeats cannot be served from the
+256 MB Infinity Cache.
+
+Prints one JSON line with the metric, the dominant kernel's roofline
+(the indexer key stream, bound by HBM) and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode tokens/s @32K ctx, k=2048; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(p) -> int:
+    """Algorithmic HBM bytes of one decode step: every candidate indexer key,
+    every selected latent row, the queries, weights and the outputs."""
+    esz = {"bf16": 2, "f32": 4, "fp8_e4m3": 1}
+    n = p.seq_len.astype(int)
+    keys = int(n.sum()) * p.D_I * esz[p.key_dtype] + (int(n.sum()) * 2 if p.key_dtype == "fp8_e4m3" else 0)
+    k_eff = [min(p.k, int(x)) for x in n]
+    gather = sum(k_eff) * 576 * esz[p.act_dtype]
+    small = (p.B * p.H_I * p.D_I * esz[p.act_dtype] + p.B * p.H_I * 4 + p.B * p.H * 576 * esz[p.act_dtype]
+             + p.B * p.H * 512 * 4 + p.B * p.H * 4 + p.B * p.k * 4)
+    return keys + gather + small
+
+
+def indexer_bytes(p) -> int:
+    """Algorithmic bytes of one indexer launch: per candidate key its D_I
+    elements (+2 B row scale for fp8) read and its fp32 score written; per
+    query its H_I x D_I query and H_I weights."""
+    esz = {"bf16": 2, "f32": 4, "fp8_e4m3": 1}
+    n = int(p.seq_len.astype(int).sum())
+    per_key = p.D_I * esz[p.key_dtype] + (2 if p.key_dtype == "fp8_e4m3" else 0) + 4
+    per_query = p.H_I * p.D_I * esz[p.act_dtype] + p.H_I * 4
+    return n * per_key + p.B * per_query
+
+
+def pmc_traffic(kernel_src: str, workload: str):
+    """HBM traffic of the indexer from committed rocprofv3 counter runs, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"index_scores_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = open(kernel_src, "rb").read()
+        if rec.get("kernel_sha256") != hashlib.sha256(src).hexdigest():
+            return None
+        return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(p, budget_s: float):
+    from oracle import dsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        O.dsa_forward(p, rows=[rows % p.R])
+        rows += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} decode rows of the same workload (full indexer over "
+                      f"{int(p.seq_len[0])} keys, stable-sort top-k, fp64 attention), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode-32k")
+    ap.add_argument("--sets", type=int, default=0, help="input copies cycled through (0: auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sparse_attention_05_amd import dsa, inputs
+
+    torch.cuda.set_device(0)
+    log(f"bench: generating {args.workload}")
+    p = inputs.workload(args.workload, seed=0)
+    if not p.is_decode():
+        raise SystemExit("bench.py times decode workloads")
+    max_len = int(p.seq_len.max())
+    sb = step_bytes(p)
+    n_sets = args.sets or max(2, math.ceil(2 * MALL_BYTES / sb))
+    base = inputs.to_torch(p, "cuda")
+    sets = [base] + [type(base)(**{k: (v.clone() if v is not None else None) for k, v in vars(base).items()})
+                     for _ in range(n_sets - 1)]
+    calls = [dsa.DecodeCall(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len, max_len,
+                            p.k, p.scale, k_scale=d.k_scale) for d in sets]
+    log(f"bench: {n_sets} input sets of {sb / 1e6:.1f} MB algorithmic traffic per step")
+
+    # determinism check on set 0 (not timed)
+    o0, l0, i0 = (x.clone() for x in calls[0]())
+    for i in range(args.warmup):
+        calls[i % n_sets]()
+    torch.cuda.synchronize()
+    o1, l1, i1 = calls[0]()
+    torch.cuda.synchronize()
+    deterministic = bool(torch.equal(o0, o1) and torch.equal(l0, l1) and torch.equal(i0, i1))
+
+    # ---- timed region: K fused decode steps ---------------------------------------------
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        calls[i % n_sets]()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    tok_s = p.B / (ms_step * 1e-3)
+    log(f"bench: {ms_step * 1e3:.2f} us/step, {tok_s:,.0f} tokens/s (wall {wall:.3f} s)")
+
+    # ---- the dominant kernel alone: K back-to-back indexer launches ----------------------
+    scores = [torch.empty((p.B, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
+    for i in range(min(args.warmup, n_sets)):
+        d = sets[i]
+        dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, max_len, k_scale=d.k_scale,
+                             scores=scores[i])
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        d = sets[i % n_sets]
+        dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, max_len, k_scale=d.k_scale,
+                             scores=scores[i % n_sets])
+    end.record()
+    torch.cuda.synchronize()
+    idx_us = start.elapsed_time(end) * 1e3 / args.steps
+    ib = indexer_bytes(p)
+    achieved = ib / (idx_us * 1e-6) / 1e9
+    log(f"bench: indexer {idx_us:.2f} us/launch, {achieved:,.0f} GB/s algorithmic")
+
+    traffic = pmc_traffic(os.path.join(ROOT, "sparse_attention_05_amd", "csrc", "index_scores.hip"), args.workload)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        cpu = cpu_baseline(p, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if p.act_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": p.B, "context": max_len, "k": p.k,
+                   "indexer_heads": p.H_I, "indexer_dim": p.D_I, "indexer_keys": p.key_dtype,
+                   "mla_heads": p.H, "latent_dim": 576, "input_sets": n_sets},
+        "step_hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
+        "step_algorithmic_bytes": sb,
+        "deterministic": deterministic,
+        "roofline": {"kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "bytes_per_launch": ib, "us_per_launch": idx_us},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * dsa.h -- C ABI of libdsa.so, the MI355X (gfx950) DeepSeek Sparse Attention
+ * decode path: lightning indexer -> deterministic top-k -> absorbed sparse MLA.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a device pointer (HBM), allocated and
+ *   owned by the caller; the library never allocates, frees or keeps them.
+ *   Scalars are host values. `stream` is a hipStream_t (NULL = the default
+ *   stream); every call only enqueues work on it and returns without waiting.
+ * Caches.  Indexer keys and latent rows are flat row arrays shared by B
+ *   sequences: sequence b owns rows row_off[b] .. row_off[b] + len_b - 1 of
+ *   a cache of `cache_rows` rows. Query r belongs to sequence q_seq[r]
+ *   (q_seq == NULL means query r belongs to sequence r) at 0-based position
+ *   q_pos[r]; its candidate keys are positions 0 .. q_pos[r] of that sequence
+ *   (the query's own key included). Decode is R == B, q_seq == NULL,
+ *   q_pos[b] = len_b - 1; causal prefill is B == 1, q_pos[r] = r.
+ * Device metadata (row_off, q_seq, q_pos, seq_len, idx) is trusted: the
+ *   preconditions q_pos[r] < max_n, 0 <= q_seq[r] < B and
+ *   row_off[q_seq[r]] + q_pos[r] < cache_rows are not checked on the host.
+ *   Kernels clamp every address so a violation cannot read or write outside
+ *   the caller's buffers; the values computed for such queries are then
+ *   unspecified.
+ * Errors.  Argument errors are found on the host before anything is
+ *   enqueued and returned synchronously (nothing is written). A failed
+ *   launch returns DSA_ERR_HIP; dsa_last_error() gives its text.
+ * Determinism.  For fixed inputs, shapes and device, every output is bitwise
+ *   identical from run to run: no floating-point atomics, fixed reduction
+ *   orders, and integer-only selection.
+ * dtypes.  DSA_BF16 arrays hold bfloat16 bit patterns, DSA_FP8_E4M3 arrays
+ *   OCP FP8 E4M3FN codes (max 448, no infinities), DSA_F32 IEEE float32.
+ *
+ * Citations name the pages that describe the method: "GLM-5: from Vibe
+ * Coding to Agentic Engineering" (paper notes, sections 2.1, 2.1.1, 2.1.2,
+ * 3.2), "Zhipu AI / GLM: From Blank Infilling to Compaction-Aware Agentic
+ * RL" (sections 9.1, 9.3, 11.1) and "GLM-5 Notes" (DSA, Replay).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  DSA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent          */
+  DSA_ERR_DTYPE = 3,       /* dtype or dtype combination not provided         */
+  DSA_ERR_ALIGN = 4,       /* a streamed / gathered array is not 16-B aligned */
+  DSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
+  DSA_ERR_UNSUPPORTED = 6, /* supported by the method, not by this library    */
+  DSA_ERR_HIP = 7          /* the HIP runtime reported an error               */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype;
+
+/* Fixed row geometry of the absorbed MLA cache: 512 latent + 64 RoPE dims
+ * ("GLM-5: from Vibe Coding...", section 2.1: a 576-dim latent KV cache;
+ * "Zhipu AI / GLM", section 9.1: KV rank 512, 64 RoPE dims). */
+#define DSA_LATENT_DIM 576
+#define DSA_VALUE_DIM 512
+/* Largest k this library selects (the pages use k = 2048 throughout). */
+#define DSA_MAX_TOPK 2048
+
+/* Entry ids for dsa_workspace_size. */
+#define DSA_ENTRY_INDEX_SCORES 0
+#define DSA_ENTRY_TOPK 1
+#define DSA_ENTRY_SPARSE_MLA 2
+#define DSA_ENTRY_DECODE 3
+
+/*
+ * dsa_index_scores -- lightning-indexer scores.
+ * The indexer scores every past key so the top-k can keep the important
+ * tokens ("GLM-5: from Vibe Coding...", section 2.1.2: the lightning indexer
+ * gives token-level sparsity; section 3.2: an extra indexer retrieves the
+ * top-k key-value pairs; "Zhipu AI / GLM", section 9.1: DSA index 32 x 128).
+ * The pages give no formula; this library computes the DeepSeek-V3.2 form
+ *
+ *   scores[r, s] = sum_h head_w[r, h] * ReLU( sum_d q_idx[r, h, d] * key_s[d] )
+ *
+ * for s = 0 .. q_pos[r], fp32 accumulation, fp32 result. Entries s > q_pos[r]
+ * of a row are not written.
+ *
+ *   q_idx    [R, H_I, D_I]  q_dtype: DSA_BF16 or DSA_F32
+ *   head_w   [R, H_I]       fp32
+ *   k_idx    [cache_rows, D_I]  k_dtype: DSA_BF16 (with q BF16), DSA_FP8_E4M3
+ *            (with q BF16; key = e4m3(code) * bf16(k_scale[row])), DSA_F32
+ *            (with q F32). 16-B aligned.
+ *   k_scale  [cache_rows] bf16 bits; required iff k_dtype == DSA_FP8_E4M3,
+ *            otherwise ignored.
+ *   row_off  [B] int64;  q_seq [R] int32 or NULL;  q_pos [R] int32
+ *   H_I in 1..64, D_I in {64, 128}; max_n >= 1 bounds q_pos[r] + 1.
+ *   scores   [R, ld_scores] fp32, ld_scores >= max_n, 16-B aligned rows
+ *            (ld_scores % 4 == 0).
+ */
+dsa_status dsa_index_scores(const void* q_idx, int32_t q_dtype, const float* head_w,
+                            const void* k_idx, int32_t k_dtype, const uint16_t* k_scale,
+                            int64_t cache_rows, const int64_t* row_off, int32_t B,
+                            const int32_t* q_seq, const int32_t* q_pos, int32_t R,
+                            int32_t H_I, int32_t D_I, int32_t max_n,
+                            float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * dsa_topk -- deterministic top-k over each score row.
+ * k = 2048 ("Zhipu AI / GLM", sections 9.3 and 11.1). The selection must be
+ * reproducible bit for bit: a non-deterministic top-k desynchronised
+ * rollout and training and collapsed RL; the pages' fix is a deterministic
+ * top-k ("GLM-5: from Vibe Coding...", section 3.2; "GLM-5 Notes", Replay).
+ *
+ * For row r with n = q_pos[r] + 1 candidates and k_eff = min(k, n):
+ * idx_out[r, 0:k_eff] are the first k_eff keys of the stable descending
+ * sort of scores[r, 0:n] (equal scores: lower key index first; -0.0 ranks
+ * equal to +0.0), idx_out[r, k_eff:k] = -1. Selection and ordering are
+ * integer operations on an order-preserving 32-bit image of each score, so
+ * the result is unique and identical on every run. NaN scores are outside
+ * the contract.
+ *
+ *   scores   [R, ld_scores] fp32, ld_scores % 4 == 0, 16-B aligned
+ *   q_pos    [R] int32; max_n bounds q_pos[r] + 1 (host value)
+ *   k        1 .. DSA_MAX_TOPK
+ *   idx_out  [R, k] int32 (positions within the query's sequence)
+ *   workspace: dsa_workspace_size(DSA_ENTRY_TOPK, ...) bytes (may be 0 -> NULL ok)
+ */
+dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos,
+                    int32_t R, int32_t max_n, int32_t k, int32_t* idx_out,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_sparse_mla_attn -- absorbed (MQA-form) MLA attention over the selected
+ * keys only ("GLM-5: from Vibe Coding...", section 3.2: attention is computed
+ * sparsely on the retrieved subset; section 2.1: 576-dim latent KV cache and
+ * 576-dim dot products in decoding). One latent row per token is shared by all
+ * heads; all 576 dims form the key, the first 512 the value:
+ *
+ *   l_j      = scale * q_abs[r, h, :] . latent[row(idx[r, j]), :]
+ *   out[r,h] = sum_j softmax(l)_j * latent[row(idx[r, j]), 0:512]
+ *   lse[r,h] = log sum_j exp(l_j)   (natural log)
+ *
+ * over the entries j < k with idx[r, j] >= 0 (-1 entries are skipped);
+ * row(s) = row_off[q_seq[r]] + s. bf16/fp32 inputs, fp32 accumulation and
+ * outputs. The key-split plan depends only on (R, H, k) and the device, so
+ * the same indices give bitwise identical outputs (index replay: "GLM-5
+ * Notes", Replay; "GLM-5: from Vibe Coding...", section 3.2).
+ *
+ *   q_abs    [R, H, 576]  dtype DSA_BF16 or DSA_F32 (latent has the same dtype)
+ *   latent   [cache_rows, 576], 16-B aligned
+ *   idx      [R, k] int32;  k in 1 .. DSA_MAX_TOPK;  H in 1 .. 128
+ *   out      [R, H, 512] fp32;  lse [R, H] fp32 or NULL
+ *   workspace: dsa_workspace_size(DSA_ENTRY_SPARSE_MLA, R, 0, k, H) bytes
+ * A row with no valid index gets out = 0 and lse = -inf.
+ */
+dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* latent,
+                               int64_t cache_rows, const int64_t* row_off, int32_t B,
+                               const int32_t* q_seq, const int32_t* idx, int32_t k,
+                               int32_t R, int32_t H, float scale, float* out, float* lse,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_decode_fused -- one decode step: indexer -> top-k -> sparse MLA for B
+ * sequences with one new query each (q_pos[b] = seq_len[b] - 1, the new
+ * token's key and latent row already appended). Enqueues the same kernels
+ * as the three entry points above, with the scores (and the indices when
+ * idx_out is NULL) kept in the workspace; the attention split plan equals
+ * dsa_sparse_mla_attn's, so replaying the recorded idx_out through
+ * dsa_sparse_mla_attn reproduces out and lse bitwise.
+ *
+ *   q_idx [B, H_I, D_I], head_w [B, H_I], k_idx/k_scale as in dsa_index_scores
+ *   q_abs [B, H, 576], latent [cache_rows, 576]: act_dtype (DSA_BF16 or
+ *   DSA_F32) is the dtype of q_idx, q_abs and latent; k_dtype as in
+ *   dsa_index_scores.
+ *   seq_len [B] int32 (1 <= seq_len[b] <= max_len), row_off [B] int64
+ *   out [B, H, 512] fp32, lse [B, H] or NULL, idx_out [B, k] int32 or NULL
+ *   workspace: dsa_workspace_size(DSA_ENTRY_DECODE, B, max_len, k, H) bytes
+ */
+dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* k_idx,
+                            int32_t k_dtype, const uint16_t* k_scale, const void* q_abs,
+                            const void* latent, int32_t act_dtype, int64_t cache_rows,
+                            const int64_t* row_off, const int32_t* seq_len, int32_t B,
+                            int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k,
+                            float scale, float* out, float* lse, int32_t* idx_out,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_workspace_size -- bytes of workspace an entry point needs.
+ * entry: one of DSA_ENTRY_*; rows = R (or B for DSA_ENTRY_DECODE);
+ * max_len = longest sequence (decode) or max_n (top-k); k; H = MLA heads.
+ * Returns 0 when the entry needs none; the result is a multiple of 256.
+ * It queries the current device (the split plan depends on its CU count).
+ */
+size_t dsa_workspace_size(int32_t entry, int32_t rows, int32_t max_len, int32_t k, int32_t H);
+
+/* Text of a status code (static storage). */
+const char* dsa_status_string(int32_t status);
+
+/* Text of the last DSA_ERR_HIP on the calling thread (static per thread). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

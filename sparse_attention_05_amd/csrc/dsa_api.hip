@@ -1,0 +1,201 @@
+// C ABI of libdsa.so (declared in include/dsa.h): argument validation on the
+// host, workspace layout, and the enqueue order of the fused decode step.
+#include <stdio.h>
+#include <string.h>
+
+#include "dsa.h"
+#include "dsa_common.hpp"
+#include "dsa_internal.hpp"
+
+namespace dsa {
+
+namespace {
+thread_local char g_last_error[256] = "";
+
+dsa_status hip_fail(hipError_t e) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s (%d): %s", hipGetErrorName(e), int(e), hipGetErrorString(e));
+  return DSA_ERR_HIP;
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+size_t align256(size_t x) {
+  return (x + 255) / 256 * 256;
+}
+
+constexpr int kMaxTopkRow = 1 << 20;  // longest score row the top-k accepts
+
+dsa_status check_index_args(const void* q, int q_dtype, const float* w, const void* keys, int k_dtype,
+                            const uint16_t* k_scale, int64_t cache_rows, const int64_t* row_off, int B,
+                            int R, int H_I, int D_I, int max_n) {
+  if (!q || !w || !keys || !row_off) return DSA_ERR_NULL;
+  if (k_dtype == DSA_FP8_E4M3 && !k_scale) return DSA_ERR_NULL;
+  if (R < 0 || B < 1 || cache_rows < 1 || max_n < 1) return DSA_ERR_SHAPE;
+  if (H_I < 1 || H_I > 64) return DSA_ERR_UNSUPPORTED;
+  if (D_I != 64 && D_I != 128) return DSA_ERR_UNSUPPORTED;
+  const bool ok = (q_dtype == DSA_F32 && k_dtype == DSA_F32) || (q_dtype == DSA_BF16 && k_dtype == DSA_BF16) ||
+                  (q_dtype == DSA_BF16 && k_dtype == DSA_FP8_E4M3);
+  if (!ok) return DSA_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(keys)) return DSA_ERR_ALIGN;
+  if (k_dtype == DSA_FP8_E4M3 && (reinterpret_cast<uintptr_t>(k_scale) & 1u)) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+dsa_status check_attn_args(const void* q_abs, int dtype, const void* latent, int64_t cache_rows,
+                           const int64_t* row_off, int B, const int32_t* idx, int k, int R, int H,
+                           const float* out) {
+  if (!q_abs || !latent || !row_off || !idx || !out) return DSA_ERR_NULL;
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (R < 0 || B < 1 || cache_rows < 1) return DSA_ERR_SHAPE;
+  if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
+  if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+size_t decode_ws_bytes(int B, int max_len, int k, int H) {
+  const int64_t ld = (int64_t(max_len) + 3) / 4 * 4;
+  return align256(size_t(B) * ld * sizeof(float)) + align256(size_t(B) * k * sizeof(int32_t)) +
+         plan_attention(B, H, k).ws_bytes;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" {
+
+dsa_status dsa_index_scores(const void* q_idx, int32_t q_dtype, const float* head_w, const void* k_idx,
+                            int32_t k_dtype, const uint16_t* k_scale, int64_t cache_rows,
+                            const int64_t* row_off, int32_t B, const int32_t* q_seq, const int32_t* q_pos,
+                            int32_t R, int32_t H_I, int32_t D_I, int32_t max_n, float* scores,
+                            int64_t ld_scores, void* stream) {
+  dsa_status st = check_index_args(q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, R,
+                                   H_I, D_I, max_n);
+  if (st != DSA_OK) return st;
+  if (!q_pos || !scores) return DSA_ERR_NULL;
+  if (!q_seq && R != B) return DSA_ERR_SHAPE;
+  if (ld_scores < max_n || (ld_scores & 3)) return DSA_ERR_SHAPE;
+  if (!aligned16(scores)) return DSA_ERR_ALIGN;
+  IndexArgs a{q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, q_seq, q_pos, nullptr,
+              R, H_I, D_I, max_n, scores, ld_scores};
+  hipError_t e = launch_index_scores(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : hip_fail(e);
+}
+
+dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t R, int32_t max_n,
+                    int32_t k, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!scores || !q_pos || !idx_out) return DSA_ERR_NULL;
+  if (R < 0 || max_n < 1) return DSA_ERR_SHAPE;
+  if (max_n > kMaxTopkRow) return DSA_ERR_UNSUPPORTED;
+  if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
+  if (ld_scores < max_n || (ld_scores & 3)) return DSA_ERR_SHAPE;
+  if (!aligned16(scores)) return DSA_ERR_ALIGN;
+  TopkArgs a{scores, ld_scores, q_pos, nullptr, R, max_n, k, idx_out};
+  hipError_t e = launch_topk(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : hip_fail(e);
+}
+
+dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* latent, int64_t cache_rows,
+                               const int64_t* row_off, int32_t B, const int32_t* q_seq, const int32_t* idx,
+                               int32_t k, int32_t R, int32_t H, float scale, float* out, float* lse,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_attn_args(q_abs, dtype, latent, cache_rows, row_off, B, idx, k, R, H, out);
+  if (st != DSA_OK) return st;
+  if (!q_seq && R != B) return DSA_ERR_SHAPE;
+  const AttnPlan plan = plan_attention(R, H, k);
+  if (plan.ws_bytes && (!workspace || ws_bytes < plan.ws_bytes)) return DSA_ERR_WORKSPACE;
+  if (plan.ws_bytes && !aligned16(workspace)) return DSA_ERR_ALIGN;
+  AttnArgs a{q_abs, dtype, latent, cache_rows, row_off, B, q_seq, idx, k, R, H, scale, out, lse, workspace};
+  hipError_t e = launch_sparse_mla(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : hip_fail(e);
+}
+
+dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* k_idx, int32_t k_dtype,
+                            const uint16_t* k_scale, const void* q_abs, const void* latent, int32_t act_dtype,
+                            int64_t cache_rows, const int64_t* row_off, const int32_t* seq_len, int32_t B,
+                            int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k, float scale,
+                            float* out, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  dsa_status st = check_index_args(q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, B,
+                                   H_I, D_I, max_len);
+  if (st != DSA_OK) return st;
+  if (!seq_len || !q_abs || !latent || !out) return DSA_ERR_NULL;
+  if (act_dtype != DSA_F32 && act_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (max_len > kMaxTopkRow) return DSA_ERR_UNSUPPORTED;
+  if (k < 1 || k > DSA_MAX_TOPK || H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
+  if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
+  const size_t need = decode_ws_bytes(B, max_len, k, H);
+  if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSA_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t ld = (int64_t(max_len) + 3) / 4 * 4;
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + align256(size_t(B) * ld * sizeof(float)));
+  void* attn_ws = ws + align256(size_t(B) * ld * sizeof(float)) + align256(size_t(B) * k * sizeof(int32_t));
+  if (idx_out) idx = idx_out;
+
+  IndexArgs ia{q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, nullptr, nullptr,
+               seq_len, B, H_I, D_I, max_len, scores, ld};
+  hipError_t e = launch_index_scores(ia, s);
+  if (e != hipSuccess) return hip_fail(e);
+  TopkArgs ta{scores, ld, nullptr, seq_len, B, max_len, k, idx};
+  e = launch_topk(ta, s);
+  if (e != hipSuccess) return hip_fail(e);
+  const AttnPlan plan = plan_attention(B, H, k);
+  AttnArgs aa{q_abs, act_dtype, latent, cache_rows, row_off, B, nullptr, idx, k, B, H, scale, out, lse, attn_ws};
+  e = launch_sparse_mla(aa, plan, s);
+  return e == hipSuccess ? DSA_OK : hip_fail(e);
+}
+
+size_t dsa_workspace_size(int32_t entry, int32_t rows, int32_t max_len, int32_t k, int32_t H) {
+  if (rows < 0 || k < 1 || H < 1) return 0;
+  switch (entry) {
+    case DSA_ENTRY_SPARSE_MLA:
+      return plan_attention(rows, H, k).ws_bytes;
+    case DSA_ENTRY_DECODE:
+      return decode_ws_bytes(rows, max_len < 1 ? 1 : max_len, k, H);
+    default:
+      return 0;
+  }
+}
+
+const char* dsa_status_string(int32_t status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case DSA_ERR_DTYPE: return "dtype or dtype combination not provided";
+    case DSA_ERR_ALIGN: return "an array is not aligned as required";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_UNSUPPORTED: return "shape not supported by this library";
+    case DSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) {
+  return g_last_error;
+}
+
+}  // extern "C"

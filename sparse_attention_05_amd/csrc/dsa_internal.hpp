@@ -1,0 +1,69 @@
+// Host-side launchers behind the C ABI (include/dsa.h). Each enqueues its
+// kernels on `stream` and returns the launch status; arguments were already
+// validated by the entry point.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct IndexArgs {
+  const void* q;
+  int q_dtype;
+  const float* w;
+  const void* keys;
+  int k_dtype;
+  const uint16_t* k_scale;
+  int64_t cache_rows;
+  const int64_t* row_off;
+  int B;
+  const int32_t* q_seq;  // NULL: query r is sequence r
+  const int32_t* q_pos;  // NULL: q_pos[r] = seq_len[r] - 1 (decode form)
+  const int32_t* seq_len;
+  int R, H_I, D_I, max_n;
+  float* scores;
+  int64_t ld;
+};
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
+
+struct TopkArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* q_pos;    // NULL: use seq_len - 1
+  const int32_t* seq_len;
+  int R, max_n, k;
+  int32_t* idx;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+
+struct AttnPlan {
+  int splits;           // key splits per query row
+  int keys_per_split;   // multiple of 32
+  int head_blocks;      // ceil(H / 64)
+  int waves;            // waves per workgroup (16 heads each)
+  size_t ws_bytes;      // partial-result workspace (0 when splits == 1)
+};
+AttnPlan plan_attention(int R, int H, int k);
+
+struct AttnArgs {
+  const void* q;
+  int dtype;
+  const void* latent;
+  int64_t cache_rows;
+  const int64_t* row_off;
+  int B;
+  const int32_t* q_seq;
+  const int32_t* idx;
+  int k, R, H;
+  float scale;
+  float* out;
+  float* lse;
+  void* ws;
+};
+hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace dsa

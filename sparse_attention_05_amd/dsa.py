@@ -1,0 +1,206 @@
+"""Python binding of libdsa.so (include/dsa.h): argument marshalling only.
+
+Each function has the name of the C entry point it calls. Tensors must be
+contiguous CUDA (HIP) tensors; the functions pass their ``data_ptr()`` and
+torch's current stream, allocate outputs and workspace with torch when the
+caller does not pass them, and raise ``DSAError`` on a non-OK status. Every
+step of the computation runs in the library's HIP kernels; importing this
+module fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_DTYPE, DSA_ERR_ALIGN, DSA_ERR_WORKSPACE, \
+    DSA_ERR_UNSUPPORTED, DSA_ERR_HIP = range(8)
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+DSA_ENTRY_INDEX_SCORES, DSA_ENTRY_TOPK, DSA_ENTRY_SPARSE_MLA, DSA_ENTRY_DECODE = 0, 1, 2, 3
+DSA_LATENT_DIM, DSA_VALUE_DIM, DSA_MAX_TOPK = 576, 512, 2048
+
+# C signatures, in the order of include/dsa.h.
+_P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "dsa_index_scores": (_I32, [_P, _I32, _P, _P, _I32, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
+                                _P, _I64, _P]),
+    "dsa_topk": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "dsa_sparse_mla_attn": (_I32, [_P, _I32, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _F32, _P, _P,
+                                   _P, _SZ, _P]),
+    "dsa_decode_fused": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I64, _P, _P, _I32, _I32, _I32, _I32,
+                                _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
+    "dsa_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "dsa_status_string": (ctypes.c_char_p, [_I32]),
+    "dsa_last_error": (ctypes.c_char_p, []),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_05_amd.build` "
+                          "(the DSA path has no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = dsa_status_string(status)
+        if status == DSA_ERR_HIP:
+            msg += ": " + (lib.dsa_last_error() or b"").decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != DSA_OK:
+        raise DSAError(status, where)
+
+
+def dsa_status_string(status: int) -> str:
+    return lib.dsa_status_string(int(status)).decode()
+
+
+def dsa_workspace_size(entry: int, rows: int, max_len: int, k: int, H: int) -> int:
+    return int(lib.dsa_workspace_size(entry, rows, max_len, k, H))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DSA_F32
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DSA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _workspace(nbytes: int, ws: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    return ws
+
+
+def dsa_index_scores(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor,
+                     row_off: torch.Tensor, q_pos: torch.Tensor, max_n: int, *,
+                     k_scale: Optional[torch.Tensor] = None, q_seq: Optional[torch.Tensor] = None,
+                     scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Indexer scores [R, ld] (fp32); entries past q_pos[r] are left untouched."""
+    R, H_I, D_I = q_idx.shape
+    if scores is None:
+        ld = (max_n + 3) // 4 * 4
+        scores = torch.empty((R, ld), dtype=torch.float32, device=q_idx.device)
+    st = lib.dsa_index_scores(
+        _ptr(q_idx), _dtype_code(q_idx), _ptr(head_w), _ptr(k_idx), _dtype_code(k_idx), _ptr(k_scale),
+        k_idx.shape[0], _ptr(row_off), row_off.numel(), _ptr(q_seq), _ptr(q_pos), R, H_I, D_I, max_n,
+        _ptr(scores), scores.shape[1], _stream(stream))
+    _check(st, "dsa_index_scores")
+    return scores
+
+
+def dsa_topk(scores: torch.Tensor, q_pos: torch.Tensor, max_n: int, k: int, *,
+             idx_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Deterministic top-k indices [R, k] (int32, rank order, -1 padded)."""
+    R = scores.shape[0]
+    if idx_out is None:
+        idx_out = torch.empty((R, k), dtype=torch.int32, device=scores.device)
+    st = lib.dsa_topk(_ptr(scores), scores.shape[1], _ptr(q_pos), R, max_n, k, _ptr(idx_out), None, 0,
+                      _stream(stream))
+    _check(st, "dsa_topk")
+    return idx_out
+
+
+def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, row_off: torch.Tensor,
+                        idx: torch.Tensor, scale: float, *, q_seq: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        want_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Sparse absorbed MLA: (out [R, H, 512] fp32, lse [R, H] fp32)."""
+    R, H, _ = q_abs.shape
+    k = idx.shape[1]
+    dev = q_abs.device
+    if out is None:
+        out = torch.empty((R, H, DSA_VALUE_DIM), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    nbytes = dsa_workspace_size(DSA_ENTRY_SPARSE_MLA, R, 0, k, H)
+    workspace = _workspace(nbytes, workspace, dev)
+    st = lib.dsa_sparse_mla_attn(
+        _ptr(q_abs), _dtype_code(q_abs), _ptr(latent), latent.shape[0], _ptr(row_off), row_off.numel(),
+        _ptr(q_seq), _ptr(idx), k, R, H, float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "dsa_sparse_mla_attn")
+    return out, lse
+
+
+class DecodeCall:
+    """A pre-marshalled dsa_decode_fused call: validates and allocates once,
+    then each ``__call__`` enqueues one decode step with no Python-side
+    allocation. Used where per-step host overhead matters."""
+
+    def __init__(self, q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
+                 scale: float, *, k_scale=None, out=None, lse=None, idx_out=None, want_lse=True,
+                 record_idx=True, workspace=None):
+        B, H_I, D_I = q_idx.shape
+        H = q_abs.shape[1]
+        dev = q_idx.device
+        self.out = out if out is not None else torch.empty((B, H, DSA_VALUE_DIM), dtype=torch.float32, device=dev)
+        self.lse = lse if lse is not None or not want_lse else torch.empty((B, H), dtype=torch.float32, device=dev)
+        self.idx = idx_out if idx_out is not None or not record_idx else \
+            torch.empty((B, k), dtype=torch.int32, device=dev)
+        nbytes = dsa_workspace_size(DSA_ENTRY_DECODE, B, max_len, k, H)
+        self.workspace = _workspace(nbytes, workspace, dev)
+        if _dtype_code(q_idx) != _dtype_code(q_abs) or _dtype_code(q_abs) != _dtype_code(latent):
+            raise TypeError("q_idx, q_abs and latent must share one dtype")
+        self._keep = (q_idx, head_w, k_idx, k_scale, q_abs, latent, row_off, seq_len)
+        self._args = (
+            _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _dtype_code(k_idx), _ptr(k_scale), _ptr(q_abs), _ptr(latent),
+            _dtype_code(q_abs), k_idx.shape[0], _ptr(row_off), _ptr(seq_len), B, max_len, H_I, D_I, H, k,
+            float(scale), _ptr(self.out), _ptr(self.lse), _ptr(self.idx), _ptr(self.workspace),
+            self.workspace.numel() * self.workspace.element_size())
+
+    def __call__(self, stream=None):
+        st = lib.dsa_decode_fused(*self._args, _stream(stream))
+        _check(st, "dsa_decode_fused")
+        return self.out, self.lse, self.idx
+
+
+def dsa_decode_fused(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
+                     scale: float, *, k_scale=None, out=None, lse=None, idx_out=None, want_lse=True,
+                     record_idx=True, workspace=None, stream=None):
+    """One decode step; returns (out [B,H,512], lse [B,H] or None, idx [B,k] or None)."""
+    call = DecodeCall(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len, k, scale,
+                      k_scale=k_scale, out=out, lse=lse, idx_out=idx_out, want_lse=want_lse,
+                      record_idx=record_idx, workspace=workspace)
+    return call(stream)

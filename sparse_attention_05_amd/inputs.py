@@ -199,7 +199,7 @@ def tiny_config(seed: int = 0, quantized: bool = False, n_keys: int = 512,
 def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: int = 128,
                   H: int = 64, k: int = 2048, key_dtype: str = "bf16",
                   boost_frac: float = 0.0, boost_sigma: float = 4.0,
-                  tie_levels: int = 0, latent_std: float = 0.1,
+                  tie_levels: int = 0, latent_std: float = 0.1, q_abs_std: float = 1.0,
                   name: str = "decode") -> DSAProblem:
     """Decode batch: one new query per sequence at its last position.
 
@@ -216,7 +216,8 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
       head weights in {1/8..8/8}: every score of a query takes one of at most
       ``tie_levels`` values, all exact in fp32, so large tie classes straddle
       the k-th rank;
-    * absorbed queries N(0,1) bf16, latent rows N(0, latent_std^2) bf16.
+    * absorbed queries N(0, q_abs_std^2) bf16, latent rows N(0, latent_std^2)
+      bf16.
     """
     st = _streams(seed)
     B = len(seq_lens)
@@ -266,7 +267,7 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
             else:
                 raise ValueError(f"unknown key dtype {key_dtype}")
 
-    q_abs = _normal_bf16(st["q_abs"], (B, H, LATENT_DIM))
+    q_abs = _normal_bf16(st["q_abs"], (B, H, LATENT_DIM), std=q_abs_std)
     latent = _normal_bf16(st["latent"], (rows, LATENT_DIM), std=latent_std)
     seq_len = np.asarray(seq_lens, np.int32)
     return DSAProblem(
@@ -331,3 +332,29 @@ def workload(name: str, seed: int = 0) -> DSAProblem:
     if name == "prefill-8k":
         return prefill_config(8192, seed=seed, name=name)
     raise KeyError(name)
+
+
+def to_torch(prob: DSAProblem, device="cuda"):
+    """Copy a problem's arrays to torch tensors on ``device`` (bit-exact:
+    bf16 bit patterns become torch.bfloat16, fp8 codes stay uint8)."""
+    import types
+    import torch
+
+    def t(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        if dt == "fp8_e4m3":
+            return torch.from_numpy(a.view(np.uint8)).to(device)
+        if dt == "f32":
+            return torch.from_numpy(a.astype(np.float32, copy=False)).to(device)
+        return torch.from_numpy(a).to(device)
+
+    return types.SimpleNamespace(
+        q_idx=t(prob.q_idx, prob.act_dtype), head_w=t(prob.head_w, "f32"),
+        k_idx=t(prob.k_idx, prob.key_dtype),
+        k_scale=None if prob.k_scale is None else t(prob.k_scale.view(np.int16), None),
+        q_abs=t(prob.q_abs, prob.act_dtype), latent=t(prob.latent, prob.act_dtype),
+        row_off=t(prob.row_off.astype(np.int64), None), seq_len=t(prob.seq_len.astype(np.int32), None),
+        q_seq=t(prob.q_seq.astype(np.int32), None), q_pos=t(prob.q_pos.astype(np.int32), None),
+    )

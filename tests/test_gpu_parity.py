@@ -1,0 +1,313 @@
+"""GPU parity: every entry point of libdsa.so against the oracle, at sizes
+the oracle finishes in seconds (several tiles, ragged tails, edge cases).
+
+Top-k is compared array-exactly with the oracle applied to the *same* fp32
+scores; scores are compared bit-for-bit on exact-arithmetic inputs and
+within the summation error bound otherwise; attention within the
+tolerances of dsa_check. Outputs are poisoned before each call so unwritten
+elements show.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import dsa_oracle as O
+from sparse_attention_05_amd import inputs
+import dsa_check as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from sparse_attention_05_amd import dsa as mod
+    return mod
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------------------
+# top-k on identical scores
+# ------------------------------------------------------------------------------
+
+def _score_rows(kind, n, rng):
+    if kind == "normal":
+        return rng.standard_normal(n).astype(np.float32)
+    if kind == "ties8":
+        return (rng.integers(0, 8, n) / 8.0).astype(np.float32)
+    if kind == "equal":
+        return np.full(n, 3.25, np.float32)
+    if kind == "zeros":
+        return np.where(rng.random(n) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    if kind == "relu":  # half the scores ReLU-killed to +0 or -0, a positive tail
+        v = np.maximum(rng.standard_normal(n), 0).astype(np.float32)
+        return np.where((v == 0) & (rng.random(n) < 0.5), np.float32(-0.0), v).astype(np.float32)
+    if kind == "increasing":
+        return np.arange(n, dtype=np.float32)
+    if kind == "wide":  # magnitudes over the whole fp32 range, both signs, denormals
+        e = rng.uniform(-140, 120, n)
+        return (np.sign(rng.standard_normal(n)) * np.exp2(e)).astype(np.float32)
+    raise KeyError(kind)
+
+
+def _run_topk(dsa, rows, k):
+    import torch
+    R = len(rows)
+    max_n = max(len(x) for x in rows)
+    ld = (max_n + 3) // 4 * 4
+    S = np.full((R, ld), np.nan, np.float32)   # entries past n are garbage by contract
+    for r, x in enumerate(rows):
+        S[r, :len(x)] = x
+    q_pos = np.array([len(x) - 1 for x in rows], np.int32)
+    s_d = torch.from_numpy(S).cuda()
+    q_d = torch.from_numpy(q_pos).cuda()
+    idx = torch.randint(-7, 1 << 30, (R, k), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(s_d, q_d, max_n, k, idx_out=idx)
+    return idx.cpu().numpy()
+
+
+TOPK_CASES = [
+    ("normal", [1, 2, 63, 64, 65, 2047, 2048, 2049, 4095, 4096, 4097], 2048),
+    ("normal", [10000, 16384, 16385, 32767, 32768], 2048),
+    ("normal", [32769, 65536, 100003], 2048),
+    ("normal", [200000], 2048),
+    ("normal", [5000, 70000], 1),
+    ("normal", [5000, 4097], 777),
+    ("ties8", [4096, 4097, 65536], 2048),
+    ("ties8", [200000], 2048),
+    ("equal", [3000, 40000], 2048),
+    ("zeros", [9000, 50000], 2048),
+    ("relu", [32768], 2048),
+    ("increasing", [32768, 2100], 2048),
+    ("wide", [32768, 3000, 80000], 2048),
+]
+
+
+@pytest.mark.parametrize("kind,lens,k", TOPK_CASES, ids=[f"{c[0]}-{len(c[1])}rows-k{c[2]}" for c in TOPK_CASES])
+def test_topk_matches_oracle_on_identical_scores(dsa, kind, lens, k):
+    rng = np.random.default_rng(zlib.crc32(repr((kind, lens, k)).encode()))
+    rows = [_score_rows(kind, n, rng) for n in lens]
+    _say("topk", kind, lens, k)
+    got = _run_topk(dsa, rows, k)
+    for r, x in enumerate(rows):
+        want = O.topk_row(x, k)
+        assert np.array_equal(got[r], want), f"row {r} (n={len(x)}): first diff at {np.argmax(got[r] != want)}"
+
+
+def test_topk_is_repeatable(dsa):
+    rng = np.random.default_rng(11)
+    rows = [_score_rows("ties8", n, rng) for n in (65536, 33000, 4097)]
+    first = _run_topk(dsa, rows, 2048)
+    for _ in range(10):
+        assert np.array_equal(_run_topk(dsa, rows, 2048), first)
+
+
+# ------------------------------------------------------------------------------
+# indexer scores
+# ------------------------------------------------------------------------------
+
+def _gpu_scores(dsa, prob, d=None):
+    import torch
+    d = d or inputs.to_torch(prob)
+    ld = (prob.max_n + 3) // 4 * 4
+    scores = torch.full((prob.R, ld), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, prob.max_n, k_scale=d.k_scale,
+                         q_seq=d.q_seq, scores=scores)
+    return scores.cpu().numpy(), d
+
+
+def test_scores_exact_on_integer_inputs_fp32(dsa):
+    p = inputs.tiny_config(seed=0, quantized=True)
+    got, _ = _gpu_scores(dsa, p)
+    ref = O.index_scores(p)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(got[r, :n], ref[r]), f"row {r}"
+        assert np.isnan(got[r, n:]).all()   # past q_pos: untouched
+
+
+def test_scores_exact_on_tie_class_inputs_bf16(dsa):
+    p = inputs.decode_config([5000, 4097, 3, 700], seed=1, tie_levels=8, k=2048)
+    got, _ = _gpu_scores(dsa, p)
+    ref = O.index_scores(p)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(got[r, :n], ref[r]), f"row {r}"
+
+
+@pytest.mark.parametrize("case", ["tiny", "bf16", "bf16-h32", "fp8", "fp8-boost"])
+def test_scores_within_error_bound(dsa, case):
+    if case == "tiny":
+        p = inputs.tiny_config(seed=3)
+    elif case == "bf16":
+        p = inputs.decode_config([3000, 4096, 5000, 65], seed=2, k=2048)
+    elif case == "bf16-h32":
+        p = inputs.decode_config([3001, 1000], seed=2, H_I=32, k=2048)
+    elif case == "fp8":
+        p = inputs.decode_config([3000, 4100, 129], seed=4, key_dtype="fp8_e4m3", k=2048)
+    else:
+        p = inputs.decode_config([6000, 2500], seed=5, key_dtype="fp8_e4m3", boost_frac=0.02, k=2048)
+    _say("scores", case)
+    got, _ = _gpu_scores(dsa, p)
+    for r in range(p.R):
+        C.assert_scores_close(p, r, got[r])
+
+
+def test_fp8_codes_decode_exactly(dsa):
+    # Row s holds code (s*128 + d) mod 256 in dim d: every code appears. Two
+    # heads read dim d with signs +1/-1 and weights 1 and 0.5, so the score is
+    # v (v >= 0) or -0.5 v (v < 0) for the decoded value v = e4m3(code) * scale.
+    D = 128
+    codes = ((np.arange(2)[:, None] * 128 + np.arange(D)[None, :]) % 256).astype(np.uint8)
+    codes = np.repeat(codes, 64, axis=0)                     # 128 keys
+    bad = (codes & 0x7F) == 0x7F                              # NaN codes
+    codes[bad] = 0
+    n = codes.shape[0]
+    R = D
+    q = np.zeros((R, 2, D), np.float32)
+    for r in range(R):
+        q[r, 0, r] = 1.0
+        q[r, 1, r] = -1.0
+    q_bits = inputs.f32_to_bf16_bits(q)
+    scale = inputs.f32_to_bf16_bits(np.full(n, 0.5, np.float32))
+    p = inputs.DSAProblem(
+        name="fp8-codes", q_idx=q_bits, head_w=np.tile(np.array([[1.0, 0.5]], np.float32), (R, 1)),
+        k_idx=codes, k_scale=scale, q_abs=np.zeros((R, 1, 576), np.uint16),
+        latent=np.zeros((n, 576), np.uint16), row_off=np.zeros(1, np.int64),
+        seq_len=np.array([n], np.int32), q_seq=np.zeros(R, np.int32),
+        q_pos=np.full(R, n - 1, np.int32), k=8, scale=1.0, act_dtype="bf16", key_dtype="fp8_e4m3")
+    got, _ = _gpu_scores(dsa, p)
+    ref = O.index_scores(p)
+    for r in range(R):
+        assert np.array_equal(got[r, :n], ref[r]), f"dim {r}"
+
+
+# ------------------------------------------------------------------------------
+# sparse attention
+# ------------------------------------------------------------------------------
+
+def _gpu_attn(dsa, prob, idx, d=None):
+    import torch
+    d = d or inputs.to_torch(prob)
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
+    out = torch.full((prob.R, prob.H, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((prob.R, prob.H), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx_d, prob.scale, q_seq=d.q_seq, out=out, lse=lse)
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("H,k,std", [(64, 2048, 1.0), (64, 2048, 30.0), (8, 64, 1.0), (72, 256, 1.0),
+                                     (128, 512, 3.0), (16, 1, 1.0), (64, 100, 1.0)])
+def test_attention_matches_oracle(dsa, H, k, std):
+    p = inputs.decode_config([3000, 2500, 4096], seed=6, H=H, k=k, q_abs_std=std)
+    rng = np.random.default_rng(H * 7 + k)
+    idx = np.full((p.R, k), -1, np.int32)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        m = min(k, n) if r != 1 else min(k, n) // 2 + (k == 1)   # row 1: a ragged -1 tail
+        idx[r, :m] = rng.choice(n, size=m, replace=False)
+    _say("attention", H, k, std)
+    out, lse = _gpu_attn(dsa, p, idx)
+    ref, lse_ref = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref, lse, lse_ref)
+
+
+def test_attention_holes_and_empty_rows(dsa):
+    p = inputs.decode_config([3000, 2500, 4096, 100], seed=7, H=64, k=2048)
+    rng = np.random.default_rng(0)
+    idx = rng.integers(0, 100, (p.R, 2048)).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.3] = -1      # holes anywhere, duplicates allowed
+    idx[3] = -1                                # a row with no valid key
+    out, lse = _gpu_attn(dsa, p, idx)
+    ref, lse_ref = O.sparse_mla(p, idx)
+    assert (out[3] == 0).all() and np.isneginf(lse[3]).all()
+    C.assert_attn_close(out[:3], ref[:3], lse[:3], lse_ref[:3])
+
+
+# ------------------------------------------------------------------------------
+# whole path
+# ------------------------------------------------------------------------------
+
+def _pipeline(dsa, p):
+    """index_scores -> topk -> sparse_mla through the three entry points."""
+    import torch
+    scores, d = _gpu_scores(dsa, p)
+    s_d = torch.from_numpy(scores).cuda()
+    idx = torch.full((p.R, p.k), 12345, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(s_d, d.q_pos, p.max_n, p.k, idx_out=idx)
+    out, lse = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx, p.scale, q_seq=d.q_seq)
+    return scores, idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+
+
+def test_tiny_pipeline_fp32(dsa):
+    p = inputs.tiny_config(seed=0)
+    scores, idx, out, lse = _pipeline(dsa, p)
+    C.assert_index_invariants(idx, p.q_pos, p.k)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        ref, bound = C.assert_scores_close(p, r, scores[r])
+        assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k))
+        C.near_tie_swaps(idx[r], O.topk_row(ref.astype(np.float32), p.k), ref, bound)
+    ref_o, ref_l = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l, fp32=True)
+
+
+def test_tiny_quantized_pipeline_is_exact_end_to_end(dsa):
+    p = inputs.tiny_config(seed=0, quantized=True)
+    scores, idx, out, lse = _pipeline(dsa, p)
+    _, ref_idx, ref_o, ref_l = O.dsa_forward(p)
+    assert np.array_equal(idx, ref_idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l, fp32=True)
+
+
+def _fused(dsa, p, d, ws=None):
+    import torch
+    out = torch.full((p.B, p.H, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((p.B, p.H), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((p.B, p.k), 777, dtype=torch.int32, device="cuda")
+    dsa.dsa_decode_fused(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len,
+                         int(p.seq_len.max()), p.k, p.scale, k_scale=d.k_scale, out=out, lse=lse,
+                         idx_out=idx, workspace=ws)
+    return out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("key_dtype", ["bf16", "fp8_e4m3"])
+def test_fused_decode_matches_entry_points_and_oracle(dsa, key_dtype):
+    p = inputs.decode_config([4096, 3000, 2049, 1500, 7001], seed=8, k=2048, key_dtype=key_dtype,
+                             boost_frac=0.02 if key_dtype == "fp8_e4m3" else 0.0)
+    d = inputs.to_torch(p)
+    out, lse, idx = _fused(dsa, p, d)
+    scores, idx2, out2, lse2 = _pipeline(dsa, p)
+    # the fused step enqueues the same kernels: identical bits
+    assert np.array_equal(idx, idx2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    C.assert_index_invariants(idx, p.q_pos, p.k)
+    swaps = 0
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k))
+        ref, bound = C.assert_scores_close(p, r, scores[r])
+        swaps += C.near_tie_swaps(idx[r], O.topk_row(ref.astype(np.float32), p.k), ref, bound)
+    _say("near-tie swaps vs oracle scores:", swaps)
+    ref_o, ref_l = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l)
+
+
+def test_fused_decode_repeatable_and_replayable(dsa):
+    import torch
+    p = inputs.decode_config([8192, 8192, 6000, 8192], seed=9, tie_levels=8, k=2048)
+    d = inputs.to_torch(p)
+    runs = [_fused(dsa, p, d) for _ in range(3)]
+    for o, l, i in runs[1:]:
+        assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1]) and np.array_equal(i, runs[0][2])
+    out, lse, idx = runs[0]
+    _, ref_idx, ref_o, ref_l = O.dsa_forward(p)
+    assert np.array_equal(idx, ref_idx)            # exact scores: end-to-end equality
+    rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale)
+    assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
+    C.assert_attn_close(out, ref_o, lse, ref_l)
