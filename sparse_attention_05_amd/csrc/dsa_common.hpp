@@ -59,4 +59,58 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// ---- wave64 primitives on DPP (VALU lane moves, no LDS round trip) ----------------
+// DPP controls (GFX9): quad_perm 0x00-0xFF, row_shr:n 0x110+n, row_mirror 0x140,
+// row_half_mirror 0x141, row_bcast:15 0x142, row_bcast:31 0x143. Lanes whose
+// source is out of range or masked off read 0 (bound_ctrl).
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROW_MASK, BANK_MASK, true));
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  uint32_t x = v;
+  x += dpp_u32<0x111>(v);
+  x += dpp_u32<0x112>(v);
+  x += dpp_u32<0x113>(v);
+  x += dpp_u32<0x114, 0xF, 0xE>(x);
+  x += dpp_u32<0x118, 0xF, 0xC>(x);
+  x += dpp_u32<0x142, 0xA, 0xF>(x);
+  x += dpp_u32<0x143, 0xC, 0xF>(x);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+// Sum of the 8 lanes 8j..8j+7 that contain this lane, in every one of them.
+__device__ __forceinline__ uint32_t octet_sum(uint32_t x) {
+  x += dpp_u32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_u32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_u32<0x141>(x);  // row_half_mirror
+  return x;
+}
+
+// Wave-uniform max / min / sum.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp_u32<0xB1>(x));
+  x = max(x, dpp_u32<0x4E>(x));
+  x = max(x, dpp_u32<0x141>(x));
+  x = max(x, dpp_u32<0x140>(x));
+  return max(max(lane_value(x, 0), lane_value(x, 16)), max(lane_value(x, 32), lane_value(x, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  x = min(x, dpp_u32<0xB1>(x));
+  x = min(x, dpp_u32<0x4E>(x));
+  x = min(x, dpp_u32<0x141>(x));
+  x = min(x, dpp_u32<0x140>(x));
+  return min(min(lane_value(x, 0), lane_value(x, 16)), min(lane_value(x, 32), lane_value(x, 48)));
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return lane_value(wave_incl_scan(x), 63);
+}
+
 }  // namespace dsa

@@ -3,47 +3,553 @@
 // The pages require the DSA selection to be reproducible bit for bit: a
 // non-deterministic large-k top-k desynchronised rollout and training and
 // collapsed RL ("GLM-5: from Vibe Coding to Agentic Engineering", section
-// 3.2; "Zhipu AI / GLM", section 9.3; "GLM-5 Notes", Replay). Here the result
-// is *unique by definition* -- the first k of the stable descending sort,
-// ties to the lower key index -- and the kernel computes that unique array
-// with integer work only, so no schedule can change it:
+// 3.2; "Zhipu AI / GLM", section 9.3; "GLM-5 Notes", Replay). The result here
+// is unique by definition -- the first k of the stable descending sort, ties
+// to the lower key index -- and every step below computes a quantity that is
+// itself unique (a count, a threshold, a rank among distinct words) with
+// integer arithmetic only. No step depends on the order in which threads or
+// atomics happen to run.
 //
-//  1. each score becomes a 32-bit order-preserving key (-0 folded onto +0);
-//  2. radix select over the keys' range [min, max]: each pass histograms the
-//     keys that can still hold the k-th largest into <= 2048 bins (integer
-//     LDS atomics, 4 copies per bin so equal keys in one wave spread over
-//     banks), a block-wide suffix scan finds the bin that holds it, and the
-//     range narrows to that bin; <= 3 passes reach the threshold key T, the
-//     count `above` of keys > T, and how many keys equal T;
-//  3. winners: every key > T, plus the lowest-index `k - above` keys equal to
-//     T (index-order ranks from wave ballots; skipped when all of them fit);
-//  4. the <= 2048 winners, as 64-bit (key, ~index) words, are sorted
-//     descending by a bitonic network in LDS and written out as indices.
-//
-// One workgroup of 1024 threads per row. Rows of up to 32K scores stay in
-// registers between passes; longer rows are re-read from global memory
-// (they were just written by the indexer and sit in L2/MALL).
+// One 512-thread workgroup per row. Scores become 32-bit order-preserving
+// keys (-0 folded onto +0). A row of up to 32K keys stays in registers,
+// loaded as coalesced float4 sweeps (index = sweep*2048 + 4*thread + slot);
+// longer rows are re-read from L2 on every pass.
+//  1. pivot: a fixed sample (every SS-th index) is histogrammed over its
+//     range; the pivot is the lower edge of the bin holding the
+//     (ceil(k/SS)+24)-th largest sample, so ~1.2k keys clear it;
+//  2. candidates: keys >= pivot are compacted into LDS (positions from a
+//     block prefix sum) as unique 64-bit words (key << 32 | ~index), whose
+//     descending order is exactly the stable order (score desc, index asc);
+//  3. the candidates are sorted and the first k written out: bucket passes
+//     on 12-bit adaptive digits of (max - word), buckets of at most 32 words
+//     ranked by counting, denser buckets (those that reach below rank k)
+//     split again from their exact word range (a work list, up to three
+//     more levels), and a bitonic network for whatever is left;
+//  fallback, when fewer than k or more than 4096 keys clear the pivot (heavy
+//     ties, skewed rows): radix select over the whole row finds the k-th key
+//     T, the kept keys equal to T are the `need` smallest indices (the same
+//     select on complemented indices), and the k winners are sorted as above.
+// Histogram bins are found with a two-level (64 x 64) search that needs
+// wave-level DPP scans only.
+#include <type_traits>
+#include <utility>
+
 #include "dsa_common.hpp"
 #include "dsa_internal.hpp"
 
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWavesPerBlock = kThreads / 64;
-constexpr int kTile = 4 * kThreads;  // elements per coalesced sweep (float4 per thread)
-constexpr int kBins = 2048;
-constexpr int kCopies = 4;
-constexpr int kMaxTiles = 256;       // rows of up to 2^20 scores
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTile = 4 * kThreads;  // one coalesced sweep
+constexpr int kBins = 4096;          // 12-bit digits (64 groups of 64)
+constexpr int kCap = 4096;           // candidate capacity
+constexpr int kSmall = 32;           // rank-by-counting limit
+constexpr int kMaxWork = 16;         // dense buckets split per level
+constexpr int kFullBins = 1024;      // whole-row histogram: 10-bit digits
+constexpr int kFullCopies = 8;       // ... spread over lane & 7
 
-struct TopkShared {
-  uint32_t hist[kBins * kCopies];
-  unsigned long long comp[kMaxTopk];
-  uint32_t tie_cnt[kMaxTiles * kWavesPerBlock];
-  uint32_t red[2 * kWavesPerBlock];
-  uint32_t sel_bin, sel_above, sel_cnt;
-  uint32_t wcount;
+struct __attribute__((aligned(16))) TopkShared {
+  uint32_t bins[kBins];              // histogram counts / bucket starts
+  uint32_t fill[kBins];              // bucket fill counters
+  uint32_t cnt[kBins];               // bucket counts
+  uint32_t coarse[64];
+  unsigned long long wa[kCap];       // candidate / winner words, sort ping-pong
+  union {
+    unsigned long long wb[kCap];
+    uint32_t full[kFullBins * kFullCopies];  // whole-row histogram (fallback select)
+  } u;
+  union {
+    uint32_t samp[4096];
+    unsigned long long net[kCap];    // bitonic scratch
+  } v;
+  uint32_t red[2 * kWaves];
+  uint32_t misc[16];
+  uint32_t work[2][6 * kMaxWork];    // dense buckets: offset, length, max (2 words), min (2 words)
 };
+
+template <int... Is, typename F>
+__device__ __forceinline__ void unroll_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// f(integral_constant<int, I>) for I = 0 .. N-1 (compile-time register indices)
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---- block primitives (uniform control flow; each ends with a barrier) -----------
+
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32_t& total) {
+  const uint32_t x = wave_incl_scan(v);
+  if (lane_id() == 63) red[wave_id()] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = red[w];
+    base += w < wave_id() ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
+  const uint32_t m = wave_max(v);
+  if (lane_id() == 0) red[wave_id()] = m;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) r = max(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ uint32_t block_min(uint32_t v, uint32_t* red) {
+  const uint32_t m = wave_min(v);
+  if (lane_id() == 0) red[wave_id()] = m;
+  __syncthreads();
+  uint32_t r = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) r = min(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// (min, max) of a value over the block with a single exchange.
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* red) {
+  const uint32_t a = wave_min(mn), b = wave_max(mx);
+  if (lane_id() == 0) {
+    red[wave_id()] = a;
+    red[kWaves + wave_id()] = b;
+  }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mn = min(mn, red[w]);
+    mx = max(mx, red[kWaves + w]);
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void clear_bins(uint32_t* a, int n) {
+  for (int i = 4 * threadIdx.x; i < n; i += 4 * kThreads) *reinterpret_cast<uint4*>(a + i) = uint4{0u, 0u, 0u, 0u};
+}
+
+// Bin b of sh.bins[0..kBins) (zero past the used range) such that the
+// counts of the bins above b sum to `above` < target <= above + count(b).
+__device__ __forceinline__ void find_crossing(TopkShared& sh, uint32_t target, uint32_t& b, uint32_t& above,
+                                              uint32_t& cnt) {
+  const int lane = lane_id(), wave = wave_id();
+  {
+    const int g = 8 * wave + (lane >> 3);  // group of 64 bins
+    const int b0 = 64 * g + 8 * (lane & 7);
+    const uint4 x = *reinterpret_cast<const uint4*>(sh.bins + b0);
+    const uint4 y = *reinterpret_cast<const uint4*>(sh.bins + b0 + 4);
+    const uint32_t s = octet_sum(x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w);
+    if ((lane & 7) == 0) sh.coarse[g] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t c = sh.coarse[lane];
+    const uint32_t incl = wave_incl_scan(c);
+    const uint32_t above_g = lane_value(incl, 63) - incl;  // in groups above this one
+    const unsigned long long hit = __ballot(c != 0u && above_g < target && above_g + c >= target);
+    int g = __ffsll(static_cast<long long>(hit)) - 1;
+    g = g < 0 ? 0 : g;
+    const uint32_t base = lane_value(above_g, g);
+    const uint32_t f = sh.bins[64 * g + lane];
+    const uint32_t incl2 = wave_incl_scan(f);
+    const uint32_t above_f = base + lane_value(incl2, 63) - incl2;
+    const unsigned long long hit2 = __ballot(f != 0u && above_f < target && above_f + f >= target);
+    int fl = __ffsll(static_cast<long long>(hit2)) - 1;
+    fl = fl < 0 ? 0 : fl;
+    if (lane == fl) {
+      sh.misc[0] = 64 * g + lane;
+      sh.misc[1] = above_f;
+      sh.misc[2] = f;
+    }
+  }
+  __syncthreads();
+  b = sh.misc[0];
+  above = sh.misc[1];
+  cnt = sh.misc[2];
+}
+
+// Digits of width 2^shift over [lo, hi]: at most 2^bits bins.
+template <typename U>
+__device__ __forceinline__ void digit_plan(U lo, U hi, int bits, int& shift, int& nb) {
+  const U width = hi - lo;
+  int nbits = 0;
+  if constexpr (sizeof(U) == 8) nbits = width ? 64 - __clzll(static_cast<long long>(width)) : 0;
+  else nbits = width ? 32 - __clz(static_cast<int>(width)) : 0;
+  shift = nbits > bits ? nbits - bits : 0;
+  nb = int(width >> shift) + 1;
+}
+
+__device__ __forceinline__ void narrow(uint32_t& lo, uint32_t& hi, uint32_t b, int shift) {
+  const unsigned long long nlo = static_cast<unsigned long long>(lo) + (static_cast<unsigned long long>(b) << shift);
+  const unsigned long long nhi = nlo + ((1ull << shift) - 1ull);
+  lo = static_cast<uint32_t>(nlo);
+  hi = nhi < hi ? static_cast<uint32_t>(nhi) : hi;
+}
+
+// k-th largest of the visited values, all in [lo, hi] (count of them =
+// count); visit(f) calls f(value) for this thread's values. Returns the
+// threshold T, how many values equal to T are within the top `target`
+// (need) and how many values equal T (eq_total). Values are expected to be
+// spread (few collisions per histogram bin).
+template <typename Visit>
+__device__ __forceinline__ void select_small(TopkShared& sh, Visit&& visit, uint32_t lo, uint32_t hi,
+                                             uint32_t target, uint32_t count, uint32_t& T, uint32_t& need,
+                                             uint32_t& eq_total) {
+  eq_total = count;
+  for (int pass = 0; pass < 4 && lo < hi; ++pass) {  // 12-bit digits: <= 3 passes
+    int shift, nb;
+    digit_plan(lo, hi, 12, shift, nb);
+    clear_bins(sh.bins, kBins);
+    __syncthreads();
+    visit([&](uint32_t v) {
+      if (v >= lo && v <= hi) atomicAdd(&sh.bins[(v - lo) >> shift], 1u);
+    });
+    __syncthreads();
+    uint32_t b, above, cnt;
+    find_crossing(sh, target, b, above, cnt);
+    target -= above;
+    eq_total = cnt;
+    narrow(lo, hi, b, shift);
+    __syncthreads();  // bins and misc are rewritten by the next pass
+  }
+  T = lo;
+  need = target;
+}
+
+// The same select over a whole row, whose values may collide heavily (tie
+// classes): a 10-bit histogram with 8 copies per bin, reduced into sh.bins.
+template <typename Visit>
+__device__ __forceinline__ void select_full(TopkShared& sh, Visit&& visit, uint32_t lo, uint32_t hi,
+                                            uint32_t target, uint32_t count, uint32_t& T, uint32_t& need,
+                                            uint32_t& eq_total) {
+  const int lane = lane_id();
+  eq_total = count;
+  for (int pass = 0; pass < 5 && lo < hi; ++pass) {  // 10-bit digits: <= 4 passes
+    int shift, nb;
+    digit_plan(lo, hi, 10, shift, nb);
+    clear_bins(sh.u.full, kFullBins * kFullCopies);
+    clear_bins(sh.bins, kBins);
+    __syncthreads();
+    visit([&](uint32_t v) {
+      if (v >= lo && v <= hi) atomicAdd(&sh.u.full[((v - lo) >> shift) * kFullCopies + (lane & 7)], 1u);
+    });
+    __syncthreads();
+    for (int i = threadIdx.x; i < kFullBins; i += kThreads) {
+      const uint4 x = *reinterpret_cast<const uint4*>(sh.u.full + i * kFullCopies);
+      const uint4 y = *reinterpret_cast<const uint4*>(sh.u.full + i * kFullCopies + 4);
+      sh.bins[i] = x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w;
+    }
+    __syncthreads();
+    uint32_t b, above, cnt;
+    find_crossing(sh, target, b, above, cnt);
+    target -= above;
+    eq_total = cnt;
+    narrow(lo, hi, b, shift);
+    __syncthreads();
+  }
+  T = lo;
+  need = target;
+}
+
+// A score row as keys. EPT > 0: this thread's EPT keys in registers
+// (index = (e/4)*kTile + 4*t + e%4; keys past the row end are 0, below every
+// real key). EPT == 0: each pass re-reads the row from global memory.
+template <int EPT>
+struct Row {
+  uint32_t key[EPT > 0 ? EPT : 1];
+  const float* src;
+  int n;
+
+  __device__ __forceinline__ void load(const float* row, int len) {
+    src = row;
+    n = len;
+    if constexpr (EPT > 0) {
+      unroll<EPT / 4>([&](auto ss) {
+        constexpr int s = decltype(ss)::value;
+        const int i0 = s * kTile + 4 * int(threadIdx.x);
+        const float4 v = i0 < n ? *reinterpret_cast<const float4*>(row + i0) : float4{0.f, 0.f, 0.f, 0.f};
+        key[4 * s + 0] = i0 + 0 < n ? order_key(v.x) : 0u;
+        key[4 * s + 1] = i0 + 1 < n ? order_key(v.y) : 0u;
+        key[4 * s + 2] = i0 + 2 < n ? order_key(v.z) : 0u;
+        key[4 * s + 3] = i0 + 3 < n ? order_key(v.w) : 0u;
+      });
+    }
+  }
+
+  // f(index / SS, key) for this thread's elements whose index is a multiple
+  // of SS (a power of two >= 16) and below n.
+  template <typename F>
+  __device__ __forceinline__ void sample(int SS, F&& f) const {
+    if constexpr (EPT > 0) {
+      // index = s*kTile + 4t + q is a multiple of 16 iff q == 0 and t % 4 == 0
+      if ((threadIdx.x & 3) == 0 && SS == 16) {
+        unroll<EPT / 4>([&](auto ss) {
+          constexpr int s = decltype(ss)::value;
+          const int idx = s * kTile + 4 * int(threadIdx.x);
+          if (idx < n) f(idx >> 4, key[4 * s]);
+        });
+      }
+    } else {
+      const int lg = __ffs(SS) - 1;
+      for (int i0 = 4 * int(threadIdx.x); i0 < n; i0 += kTile) {
+        if ((i0 & (SS - 1)) == 0) f(i0 >> lg, order_key(src[i0]));
+      }
+    }
+  }
+
+  // f(index, key) for every element of this thread, padding (key 0) included.
+  template <typename F>
+  __device__ __forceinline__ void each(F&& f) const {
+    if constexpr (EPT > 0) {
+      unroll<EPT>([&](auto ee) {
+        constexpr int e = decltype(ee)::value;
+        f((e >> 2) * kTile + 4 * int(threadIdx.x) + (e & 3), key[e]);
+      });
+    } else {
+      for (int i0 = 4 * int(threadIdx.x); i0 < n; i0 += kTile) {
+        const float4 v = *reinterpret_cast<const float4*>(src + i0);
+        f(i0 + 0, order_key(v.x));
+        f(i0 + 1, i0 + 1 < n ? order_key(v.y) : 0u);
+        f(i0 + 2, i0 + 2 < n ? order_key(v.z) : 0u);
+        f(i0 + 3, i0 + 3 < n ? order_key(v.w) : 0u);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ unsigned long long word(uint32_t key, int idx) {
+  return (static_cast<unsigned long long>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx));
+}
+__device__ __forceinline__ int32_t word_idx(unsigned long long w) {
+  return static_cast<int32_t>(~static_cast<uint32_t>(w & 0xFFFFFFFFull));
+}
+
+// Winners: keys > T, and keys == T with complemented index >= I (the `need`
+// smallest indices; I = 0 keeps every key equal to T). each(f) visits
+// (index, key) of this thread's elements. Writes the words to sh.wa.
+template <typename Each>
+__device__ __forceinline__ void collect_winners(TopkShared& sh, Each&& each, uint32_t T, uint32_t I) {
+  uint32_t c = 0;
+  each([&](int idx, uint32_t key) { c += key > T || (key == T && ~static_cast<uint32_t>(idx) >= I); });
+  uint32_t tot;
+  uint32_t pos = block_scan(c, sh.red, tot);
+  each([&](int idx, uint32_t key) {
+    if (key > T || (key == T && ~static_cast<uint32_t>(idx) >= I)) {
+      if (pos < kMaxTopk) sh.wa[pos] = word(key, idx);
+      ++pos;
+    }
+  });
+  __syncthreads();
+}
+
+// Among the keys equal to T, the `need` smallest indices are those whose
+// complemented index is >= the returned threshold.
+template <typename Each>
+__device__ __forceinline__ uint32_t tie_threshold(TopkShared& sh, Each&& each, uint32_t T, uint32_t need,
+                                                  uint32_t eq_total, int n) {
+  uint32_t I, need2, eq2;
+  auto visit = [&](auto&& f) {
+    each([&](int idx, uint32_t key) {
+      if (key == T) f(~static_cast<uint32_t>(idx));
+    });
+  };
+  select_small(sh, visit, ~static_cast<uint32_t>(n - 1), 0xFFFFFFFFu, need, eq_total, I, need2, eq2);
+  return I;
+}
+
+// ---- sorting distinct 64-bit words (descending) ----------------------------------
+
+// Bucket the distinct words src[off .. off+m), all within [mn, mx], on 12
+// bits of (mx - word) into dst[off ..]; rank every bucket of <= kSmall words
+// by counting and write the indices of ranks < limit to out[rank]; append
+// denser buckets that start below `limit` to the work list wl (count in
+// sh.misc[6]) with their exact word range. Each thread handles the fixed
+// slots i = t + 512*j (j < 8) and issues every stage for all of them at once,
+// so the LDS round trips of different slots overlap.
+__device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long long* src, unsigned long long* dst,
+                                            int off, int m, unsigned long long mx, unsigned long long mn,
+                                            int limit, int32_t* out, uint32_t* wl) {
+  constexpr int J = kCap / kThreads;
+  const int t = threadIdx.x;
+  int shift, nb;
+  digit_plan(mn, mx, 12, shift, nb);
+  for (int i = 4 * t; i < nb; i += 4 * kThreads) {
+    *reinterpret_cast<uint4*>(sh.cnt + i) = uint4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(sh.fill + i) = uint4{0u, 0u, 0u, 0u};
+  }
+  unsigned long long w[J];
+  uint32_t bk[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = t + j * kThreads;
+    w[j] = i < m ? src[off + i] : 0ull;
+    bk[j] = uint32_t((mx - w[j]) >> shift);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (t + j * kThreads < m) atomicAdd(&sh.cnt[bk[j]], 1u);
+  __syncthreads();
+  // bucket starts: each thread owns 8 consecutive buckets
+  const int b0 = 8 * t;
+  uint32_t c[8], s = 0;
+  if (b0 < nb) {
+    const uint4 x = *reinterpret_cast<const uint4*>(sh.cnt + b0);
+    const uint4 y = *reinterpret_cast<const uint4*>(sh.cnt + b0 + 4);
+    c[0] = x.x; c[1] = x.y; c[2] = x.z; c[3] = x.w; c[4] = y.x; c[5] = y.y; c[6] = y.z; c[7] = y.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c[j] = b0 + j < nb ? c[j] : 0u;
+    s += c[j];
+  }
+  uint32_t tot;
+  uint32_t run = block_scan(s, sh.red, tot);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (b0 + j < nb) sh.bins[b0 + j] = run;
+    if (c[j] > kSmall && off + int(run) < limit) {
+      const uint32_t slot = atomicAdd(&sh.misc[6], 1u);
+      if (slot < kMaxWork) {
+        const unsigned long long bmx = mx - (static_cast<unsigned long long>(b0 + j) << shift);
+        const unsigned long long span = (1ull << shift) - 1ull;
+        const unsigned long long bmn = bmx - mn > span ? bmx - span : mn;
+        uint32_t* e = wl + 6 * slot;
+        e[0] = off + run;
+        e[1] = c[j];
+        e[2] = uint32_t(bmx >> 32);
+        e[3] = uint32_t(bmx);
+        e[4] = uint32_t(bmn >> 32);
+        e[5] = uint32_t(bmn);
+      }
+    }
+    run += c[j];
+  }
+  __syncthreads();
+  uint32_t start[J], cb[J], slot[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    start[j] = sh.bins[bk[j]];
+    cb[j] = sh.cnt[bk[j]];
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) slot[j] = t + j * kThreads < m ? atomicAdd(&sh.fill[bk[j]], 1u) : 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (t + j * kThreads < m) dst[off + start[j] + slot[j]] = w[j];
+  __syncthreads();
+  // rank inside small buckets: count the larger words of the bucket
+  uint32_t rank[J], most = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const bool live = t + j * kThreads < m && cb[j] <= kSmall && off + int(start[j]) < limit;
+    cb[j] = live ? cb[j] : 0u;
+    rank[j] = 0u;
+    most = max(most, cb[j]);
+  }
+  for (uint32_t q = 0; q < most; ++q) {
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (q < cb[j]) rank[j] += dst[off + start[j] + q] > w[j];
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (cb[j] && off + int(start[j] + rank[j]) < limit) out[off + start[j] + rank[j]] = word_idx(w[j]);
+  __syncthreads();
+}
+
+// Bitonic network (descending) on src[off .. off+m), m <= kCap; writes the
+// indices of ranks < limit.
+__device__ __forceinline__ void bitonic_segment(TopkShared& sh, const unsigned long long* src, int off, int m,
+                                                int limit, int32_t* out) {
+  const int t = threadIdx.x;
+  int P = 1;
+  while (P < m) P <<= 1;
+  for (int i = t; i < P; i += kThreads) sh.v.net[i] = i < m ? src[off + i] : 0ull;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = t; i < P / 2; i += kThreads) {
+        const int l = 2 * i - (i & (stride - 1));
+        const int h = l + stride;
+        const unsigned long long a = sh.v.net[l], b = sh.v.net[h];
+        if (((l & size) == 0) ? (a < b) : (a > b)) {
+          sh.v.net[l] = b;
+          sh.v.net[h] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = t; i < m; i += kThreads)
+    if (off + i < limit) out[off + i] = word_idx(sh.v.net[i]);
+  __syncthreads();
+}
+
+// Sort the m distinct words in sh.wa (all within [mn, mx]) descending and
+// write the indices of the first `limit` to out.
+__device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long long mx, unsigned long long mn,
+                                           int limit, int32_t* out) {
+  if (threadIdx.x == 0) {
+    uint32_t* e = sh.work[0];
+    e[0] = 0u;
+    e[1] = uint32_t(m);
+    e[2] = uint32_t(mx >> 32);
+    e[3] = uint32_t(mx);
+    e[4] = uint32_t(mn >> 32);
+    e[5] = uint32_t(mn);
+  }
+  const unsigned long long* src = sh.wa;
+  unsigned long long* dst = sh.u.wb;
+  int cur = 0, nitems = 1;
+  for (int level = 0; level < 4; ++level) {
+    if (threadIdx.x == 0) sh.misc[6] = 0u;
+    __syncthreads();
+    if (level == 3) {  // still dense after three splits: sorting network
+      for (int i = 0; i < nitems; ++i)
+        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), limit, out);
+      return;
+    }
+    for (int i = 0; i < nitems; ++i) {
+      const uint32_t* e = sh.work[cur] + 6 * i;
+      const unsigned long long emx = (static_cast<unsigned long long>(e[2]) << 32) | e[3];
+      const unsigned long long emn = (static_cast<unsigned long long>(e[4]) << 32) | e[5];
+      bucket_pass(sh, src, dst, int(e[0]), int(e[1]), emx, emn, limit, out, sh.work[cur ^ 1]);
+    }
+    const int next = int(sh.misc[6]);
+    if (next > kMaxWork) {  // more dense buckets than the list holds: redo these segments
+      for (int i = 0; i < nitems; ++i)
+        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), limit, out);
+      return;
+    }
+    if (next == 0) return;
+    nitems = next;
+    cur ^= 1;
+    const unsigned long long* tmp = src;
+    src = dst;
+    dst = const_cast<unsigned long long*>(tmp);
+    __syncthreads();
+  }
+}
 
 __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
   const int q = a.q_pos ? a.q_pos[r] : a.seq_len[r] - 1;
@@ -53,268 +559,103 @@ __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
   return n;
 }
 
-__device__ __forceinline__ unsigned long long pack(uint32_t key, int idx) {
-  return (static_cast<unsigned long long>(key) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx));
-}
-
-// Element e of thread t in the register layout: sweep e/4, float4 slot e%4.
-__device__ __forceinline__ int elem_index(int e, int t) {
-  return (e >> 2) * kTile + 4 * t + (e & 3);
-}
-
-template <int EPT>
-struct Row {
-  // EPT > 0: the row lives in registers; EPT == 0: streamed from global.
-  uint32_t key[EPT > 0 ? EPT : 1];
-  const float* src;
-  int n;
-
-  __device__ void load(const float* row, int len) {
-    src = row;
-    n = len;
-    if constexpr (EPT > 0) {
-#pragma unroll
-      for (int e = 0; e < EPT; e += 4) {
-        const int i0 = elem_index(e, threadIdx.x);
-        float4 v = i0 < n ? *reinterpret_cast<const float4*>(row + i0) : float4{0.f, 0.f, 0.f, 0.f};
-        key[e] = order_key(v.x);
-        key[e + 1] = order_key(v.y);
-        key[e + 2] = order_key(v.z);
-        key[e + 3] = order_key(v.w);
-      }
-    }
-  }
-
-  // f(sweep, slot, index, key) for every element of this thread with index < n.
-  template <typename F>
-  __device__ void visit(F&& f) const {
-    if constexpr (EPT > 0) {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int i = elem_index(e, threadIdx.x);
-        if (i < n) f(e >> 2, e & 3, i, key[e]);
-      }
-    } else {
-      for (int i0 = 4 * threadIdx.x, sw = 0; i0 < n; i0 += kTile, ++sw) {
-        const float4 v = *reinterpret_cast<const float4*>(src + i0);
-        const float x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (i0 + j < n) f(sw, j, i0 + j, order_key(x[j]));
-      }
-    }
-  }
-
-  // eq[j] = (element at index sw*kTile + 4*t + j exists and has key T).
-  __device__ void sweep_eq(int sw, uint32_t T, bool (&eq)[4]) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) eq[j] = false;
-    if constexpr (EPT > 0) {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e)
-        if ((e >> 2) == sw) eq[e & 3] = elem_index(e, threadIdx.x) < n && key[e] == T;
-    } else {
-      const int i0 = sw * kTile + 4 * threadIdx.x;
-      if (i0 < n) {
-        const float4 v = *reinterpret_cast<const float4*>(src + i0);
-        const float x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) eq[j] = i0 + j < n && order_key(x[j]) == T;
-      }
-    }
-  }
-};
-
-__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 64)));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 64)));
-  return v;
-}
-
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   __shared__ TopkShared sh;
   const int r = blockIdx.x;
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
   const int n = row_len(a, r);
   const int k = a.k;
   const int k_eff = n < k ? n : k;
   int32_t* out = a.idx + int64_t(r) * k;
+  for (int j = k_eff + t; j < k; j += kThreads) out[j] = -1;
 
   Row<EPT> row;
   row.load(a.scores + int64_t(r) * a.ld, n);
-  if (t == 0) sh.wcount = 0;
+  auto each_row = [&](auto&& f) { row.each(f); };
 
-  if (n <= k) {
-    __syncthreads();
-    row.visit([&](int, int, int i, uint32_t key) {
-      const uint32_t p = atomicAdd(&sh.wcount, 1u);
-      if (p < kMaxTopk) sh.comp[p] = pack(key, i);
+  if (n <= k) {  // every key is a winner: sort them all
+    uint32_t c = 0, lo = 0xFFFFFFFFu, hi = 0u;
+    row.each([&](int idx, uint32_t key) {
+      if (idx < n) {
+        ++c;
+        lo = min(lo, key);
+        hi = max(hi, key);
+      }
     });
-  } else {
-    // ---- range of the keys -------------------------------------------------
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    row.visit([&](int, int, int, uint32_t key) {
+    block_minmax(lo, hi, sh.red);
+    uint32_t tot;
+    uint32_t pos = block_scan(c, sh.red, tot);
+    row.each([&](int idx, uint32_t key) {
+      if (idx < n) sh.wa[pos++] = word(key, idx);
+    });
+    __syncthreads();
+    sort_words(sh, n, (static_cast<unsigned long long>(hi) << 32) | 0xFFFFFFFFull,
+               static_cast<unsigned long long>(lo) << 32, n, out);
+    return;
+  }
+
+  // ---- 1. pivot from the fixed sample ------------------------------------------------
+  int SS = 16;
+  while ((n + SS - 1) / SS > 4096) SS <<= 1;
+  const int ns = (n + SS - 1) / SS;
+  uint32_t smin = 0xFFFFFFFFu, smax = 0u;
+  row.sample(SS, [&](int i, uint32_t key) {  // i = index / SS
+    sh.v.samp[i] = key;
+    smin = min(smin, key);
+    smax = max(smax, key);
+  });
+  block_minmax(smin, smax, sh.red);
+  uint32_t target_s = uint32_t((k + SS - 1) / SS + 24);
+  if (target_s > uint32_t(ns)) target_s = uint32_t(ns);
+  uint32_t pivot = smin;
+  if (smin < smax) {
+    int shift, nb;
+    digit_plan(smin, smax, 12, shift, nb);
+    clear_bins(sh.bins, kBins);
+    __syncthreads();
+    for (int i = t; i < ns; i += kThreads) atomicAdd(&sh.bins[(sh.v.samp[i] - smin) >> shift], 1u);
+    __syncthreads();
+    uint32_t b, above, cnt;
+    find_crossing(sh, target_s, b, above, cnt);
+    pivot = smin + (b << shift);
+  }
+
+  // ---- 2. candidates >= pivot ---------------------------------------------------------
+  uint32_t c = 0, cmax = 0;
+  row.each([&](int, uint32_t key) {
+    c += key >= pivot;
+    cmax = max(cmax, key);
+  });
+  uint32_t C;
+  uint32_t pos = block_scan(c, sh.red, C);
+  if (C >= uint32_t(k) && C <= uint32_t(kCap)) {
+    row.each([&](int idx, uint32_t key) {
+      if (key >= pivot) sh.wa[pos++] = word(key, idx);
+    });
+    cmax = block_max(cmax, sh.red);  // (its barrier publishes the candidates)
+    // ---- 3. the k largest candidate words, in order -----------------------------------
+    sort_words(sh, int(C), (static_cast<unsigned long long>(cmax) << 32) | 0xFFFFFFFFull,
+               static_cast<unsigned long long>(pivot) << 32, k, out);
+    return;
+  }
+
+  // ---- fallback: exact select over the whole row, then sort the k winners ----------------
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  row.each([&](int idx, uint32_t key) {
+    if (idx < n) {
       lo = min(lo, key);
       hi = max(hi, key);
-    });
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-    if (lane == 0) {
-      sh.red[wave] = lo;
-      sh.red[kWavesPerBlock + wave] = hi;
     }
-    __syncthreads();
-    lo = 0xFFFFFFFFu;
-    hi = 0u;
-#pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-      lo = min(lo, sh.red[w]);
-      hi = max(hi, sh.red[kWavesPerBlock + w]);
-    }
-
-    // ---- radix select: narrow [lo, hi] to the k-th largest key ---------------
-    uint32_t target = uint32_t(k), eq_total = uint32_t(n);
-    // Each pass leaves a range of width < 2^(bits-11): three passes always
-    // suffice; the cap makes termination independent of the data.
-    for (int pass = 0; pass < 4 && lo < hi; ++pass) {
-      const uint32_t width = hi - lo;
-      const int nbits = 32 - __clz(width);
-      const int shift = nbits > 11 ? nbits - 11 : 0;
-      const int nb = int(width >> shift) + 1;
-      for (int i = t; i < nb * kCopies; i += kThreads) sh.hist[i] = 0u;
-      __syncthreads();
-      row.visit([&](int, int, int, uint32_t key) {
-        if (key >= lo && key <= hi) atomicAdd(&sh.hist[((key - lo) >> shift) * kCopies + (lane & (kCopies - 1))], 1u);
-      });
-      __syncthreads();
-      // Thread t owns bins 2t (lower) and 2t+1 (upper). Suffix scan from the top bin.
-      uint32_t c[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int bin = 2 * t + j;
-        uint32_t s = 0;
-        if (bin < nb) {
-#pragma unroll
-          for (int cpy = 0; cpy < kCopies; ++cpy) s += sh.hist[bin * kCopies + cpy];
-        }
-        c[j] = s;
-      }
-      const uint32_t tsum = c[0] + c[1];
-      uint32_t incl = tsum;  // suffix sum over lanes >= lane within the wave
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = static_cast<uint32_t>(__shfl_down(static_cast<int>(incl), off, 64));
-        if (lane + off < 64) incl += y;
-      }
-      if (lane == 0) sh.red[wave] = incl;  // wave total
-      __syncthreads();
-      uint32_t excl = incl - tsum;
-      for (int w = wave + 1; w < kWavesPerBlock; ++w) excl += sh.red[w];
-      // excl = number of keys in bins above this thread's two bins.
-      if (c[1] && excl < target && excl + c[1] >= target) {
-        sh.sel_bin = 2 * t + 1;
-        sh.sel_above = excl;
-        sh.sel_cnt = c[1];
-      } else if (c[0] && excl + c[1] < target && excl + c[1] + c[0] >= target) {
-        sh.sel_bin = 2 * t;
-        sh.sel_above = excl + c[1];
-        sh.sel_cnt = c[0];
-      }
-      __syncthreads();
-      const uint32_t bsel = sh.sel_bin;
-      target -= sh.sel_above;
-      eq_total = sh.sel_cnt;
-      const unsigned long long nlo = static_cast<unsigned long long>(lo) + (static_cast<unsigned long long>(bsel) << shift);
-      const unsigned long long nhi = nlo + ((1ull << shift) - 1ull);
-      lo = static_cast<uint32_t>(nlo);
-      hi = nhi < hi ? static_cast<uint32_t>(nhi) : hi;
-      __syncthreads();  // sel_* and red are rewritten by the next pass
-    }
-    const uint32_t T = lo;
-    const uint32_t need = target;  // keys equal to T that are selected
-
-    // ---- collect the winners -------------------------------------------------
-    const bool take_all_ties = need == eq_total;
-    row.visit([&](int, int, int i, uint32_t key) {
-      if (key > T || (take_all_ties && key == T)) {
-        const uint32_t p = atomicAdd(&sh.wcount, 1u);
-        if (p < kMaxTopk) sh.comp[p] = pack(key, i);
-      }
-    });
-    if (!take_all_ties) {
-      // Rank of each T-valued key in index order: index = sweep*kTile + 4*t + slot,
-      // so order is (sweep, wave, lane, slot). Count per (sweep, wave) first.
-      const int sweeps = (n + kTile - 1) / kTile;
-      for (int i = t; i < sweeps * kWavesPerBlock; i += kThreads) sh.tie_cnt[i] = 0u;
-      __syncthreads();
-      row.visit([&](int sw, int, int, uint32_t key) {
-        if (key == T) atomicAdd(&sh.tie_cnt[sw * kWavesPerBlock + wave], 1u);
-      });
-      __syncthreads();
-      if (t == 0) {  // exclusive prefix in (sweep, wave) order; at most 4096 entries
-        uint32_t run = 0;
-        for (int i = 0; i < sweeps * kWavesPerBlock; ++i) {
-          const uint32_t c = sh.tie_cnt[i];
-          sh.tie_cnt[i] = run;
-          run += c;
-        }
-      }
-      __syncthreads();
-      // Within a (sweep, wave): lanes below this one, then this lane's lower slots.
-      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      for (int sw = 0; sw * kTile < n; ++sw) {
-        const int i0 = sw * kTile + 4 * t;
-        bool eq[4];
-        row.sweep_eq(sw, T, eq);
-        // T-valued keys of lower lanes in this (sweep, wave), via per-slot ballots
-        uint32_t before = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) before += __popcll(__ballot(eq[j]) & below);
-        uint32_t rank = sh.tie_cnt[sw * kWavesPerBlock + wave] + before;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (eq[j]) {
-            if (rank < need) {
-              const uint32_t p = atomicAdd(&sh.wcount, 1u);
-              if (p < kMaxTopk) sh.comp[p] = pack(T, i0 + j);
-            }
-            ++rank;
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- sort the k_eff winners: bitonic, descending on (key, ~index) ------------
-  int P = 1;
-  while (P < k_eff) P <<= 1;
-  for (int i = k_eff + t; i < P; i += kThreads) sh.comp[i] = 0ull;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < P / 2; i += kThreads) {
-        const int l = 2 * i - (i & (stride - 1));
-        const int h = l + stride;
-        const unsigned long long x = sh.comp[l], y = sh.comp[h];
-        const bool desc = (l & size) == 0;
-        if (desc ? (x < y) : (x > y)) {
-          sh.comp[l] = y;
-          sh.comp[h] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int j = t; j < k; j += kThreads)
-    out[j] = j < k_eff ? static_cast<int32_t>(~static_cast<uint32_t>(sh.comp[j] & 0xFFFFFFFFull)) : -1;
+  });
+  block_minmax(lo, hi, sh.red);
+  uint32_t T, need, eq_total, I = 0u;
+  auto visit_keys = [&](auto&& f) { row.each([&](int, uint32_t key) { f(key); }); };
+  select_full(sh, visit_keys, lo, hi, uint32_t(k), uint32_t(n), T, need, eq_total);
+  if (need < eq_total) I = tie_threshold(sh, each_row, T, need, eq_total, n);
+  collect_winners(sh, each_row, T, I);
+  sort_words(sh, k, (static_cast<unsigned long long>(hi) << 32) | 0xFFFFFFFFull,
+             static_cast<unsigned long long>(T) << 32, k, out);
 }
 
 }  // namespace
@@ -322,10 +663,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
   dim3 grid(unsigned(a.R));
-  if (a.max_n <= 4 * kThreads) topk_kernel<4><<<grid, kThreads, 0, stream>>>(a);
-  else if (a.max_n <= 16 * kThreads) topk_kernel<16><<<grid, kThreads, 0, stream>>>(a);
-  else if (a.max_n <= 32 * kThreads) topk_kernel<32><<<grid, kThreads, 0, stream>>>(a);
-  else topk_kernel<0><<<grid, kThreads, 0, stream>>>(a);
+  if (a.max_n <= 4 * kTile) topk_kernel<16><<<grid, kThreads, 0, stream>>>(a);
+  else if (a.max_n <= 8 * kTile) topk_kernel<32><<<grid, kThreads, 0, stream>>>(a);
+  else if (a.max_n <= 16 * kTile) topk_kernel<64><<<grid, kThreads, 0, stream>>>(a);
+  else topk_kernel<0><<<grid, kThreads, 0, stream>>>(a);  // longer rows: streamed from L2
   return hipGetLastError();
 }
 

@@ -52,6 +52,18 @@ def _score_rows(kind, n, rng):
     if kind == "wide":  # magnitudes over the whole fp32 range, both signs, denormals
         e = rng.uniform(-140, 120, n)
         return (np.sign(rng.standard_normal(n)) * np.exp2(e)).astype(np.float32)
+    if kind == "twoclass":  # two tie classes far apart straddle k
+        v = np.ones(n, np.float32)
+        v[rng.choice(n, 1000, replace=False)] = 100.0
+        return v
+    if kind == "outlier":  # one huge score above a tight cluster
+        v = (1.0 + rng.standard_normal(n) * 1e-3).astype(np.float32)
+        v[rng.integers(n)] = 1e30
+        return v
+    if kind == "steps":  # tie classes of 64 consecutive keys
+        return (np.arange(n) // 64).astype(np.float32)
+    if kind == "fineties":  # N(0,1) rounded to 1/1024: moderate ties everywhere
+        return (np.round(rng.standard_normal(n) * 1024) / 1024).astype(np.float32)
     raise KeyError(kind)
 
 
@@ -85,6 +97,11 @@ TOPK_CASES = [
     ("relu", [32768], 2048),
     ("increasing", [32768, 2100], 2048),
     ("wide", [32768, 3000, 80000], 2048),
+    ("twoclass", [32768, 5000, 70000], 2048),
+    ("outlier", [32768, 9000, 66000], 2048),
+    ("steps", [32768, 4000, 100000], 2048),
+    ("fineties", [32768, 65536, 2100], 2048),
+    ("normal", [2049, 2050, 2100, 2500], 2048),
 ]
 
 
