@@ -40,9 +40,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
 struct AttnPlan {
   int splits;           // key splits per query row
-  int keys_per_split;   // multiple of 32
-  int head_blocks;      // ceil(H / 64)
-  int waves;            // waves per workgroup (16 heads each)
+  int keys_per_split;   // multiple of 64
+  int head_groups;      // ceil(H / 16): one workgroup per (query, head group, split)
   size_t ws_bytes;      // partial-result workspace (0 when splits == 1)
 };
 AttnPlan plan_attention(int R, int H, int k);

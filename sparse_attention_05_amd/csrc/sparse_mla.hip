@@ -9,28 +9,30 @@
 // decoding, and the plan to serve MLA in MQA form; section 3.2: attention is
 // computed sparsely on the retrieved subset).
 //
-// Decomposition. A workgroup (4 waves) owns (query r, a range of selected
-// positions, up to 64 heads); each wave owns 16 heads for all 512 value
-// dims. Per chunk of KC selected keys (32 for bf16, 16 for fp32):
-//  * gather: every latent row is read from HBM once per workgroup with
-//    16-byte loads (a wave covers 1 KiB of one row per instruction) and
-//    written to LDS twice: key-major (for q.c, contraction over dims) and
-//    value-major (for p.c, contraction over keys). The value-major copy comes
-//    from a 4x8 register transpose and uses an XOR-swizzled slot layout that
-//    keeps both its writes and its MFMA operand reads free of LDS bank
-//    conflicts. The loads of chunk c+1 are issued before chunk c is
-//    computed, into the other LDS buffer;
-//  * q.c on MFMA: S^T[key][head] = C[KC x 576] . Q^T[576 x 16], the query
-//    fragments stay in registers for the whole range;
-//  * online softmax in registers (exp2 domain; the row sums add the same
-//    bf16-rounded p that enters the MFMA, so numerator and denominator agree);
-//  * p.c on MFMA: O^T[v][head] += C^T[512 x KC] . P^T[KC x 16], P^T taken
-//    straight from the q.c accumulators (the K-slot order is chosen to
-//    match), O^T in 128 accumulator registers per lane.
+// Decomposition. A workgroup of 4 waves owns (query r, 16 heads, a range of
+// selected positions). The range is walked in chunks of 64 keys:
+//  * gather: the 64 latent rows go from HBM straight into LDS with 16-byte
+//    direct-to-LDS loads (no register staging). Rows are stored key-major,
+//    1152 bytes each, with the 16-byte chunks of row r XOR-permuted inside
+//    aligned groups of 8 by f(r) = 2(r mod 4) + (r/4 mod 2); this keeps both
+//    operand reads below free of LDS bank conflicts. Wave w loads exactly
+//    rows 16w..16w+15, the rows of its own q.c tile;
+//  * q.c on MFMA, split over the waves by key: wave w forms
+//    S^T[16 keys][16 heads] = C[16 x 576] . Q^T, the query fragments staying
+//    in registers for the whole range;
+//  * online softmax (exp2 domain) with the chunk maximum exchanged through
+//    LDS, so all waves apply the same running maximum; P^T goes to LDS in
+//    bf16 (the row sums add the same rounded p that enters the MFMA);
+//  * p.c on MFMA, split over the waves by value dimension: wave w forms
+//    O^T[128w..128w+127][16 heads] += C^T . P^T over all 64 keys, its value
+//    operand read from the key-major rows with the transposing LDS read
+//    (ds_read_b64_tr_b16), so no second, value-major copy is needed.
 // When a row's keys are split over several workgroups, each writes the
 // unnormalised O, its max and its sum; the combine kernel merges the splits
 // in ascending split order. The split plan depends only on (R, H, k) and the
 // device, so the same indices always give the same bits (index replay).
+// The workgroups sharing (query, key range) are placed on one XCD, so three
+// of every four gathers of a latent row hit that XCD's L2.
 #include "dsa_common.hpp"
 #include "dsa_internal.hpp"
 
@@ -39,336 +41,291 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 256;   // 4 waves
+constexpr int kGroupHeads = 16;     // heads per workgroup
+constexpr int kChunkKeys = 64;      // keys per LDS buffer, 16 per wave
+constexpr int kPRow = kChunkKeys + 4;  // padded row of the P^T staging array
 
 template <bool F32>
 struct AttnCfg {
-  static constexpr int KC = F32 ? 16 : 32;               // keys per chunk
-  static constexpr int ESZ = F32 ? 4 : 2;                // bytes per element
-  static constexpr int EPC = 16 / ESZ;                   // elements per 16-byte chunk
-  static constexpr int CK_STRIDE = kLatentDim + EPC;     // elements per key row (keeps 16-B alignment)
-  static constexpr int CV_STRIDE = F32 ? KC + 4 : KC;    // elements per value-dim row
-  static constexpr int CK_ELEMS = KC * CK_STRIDE;
-  static constexpr int CV_ELEMS = kValueDim * CV_STRIDE;
-  static constexpr int BUF_BYTES = (CK_ELEMS + CV_ELEMS) * ESZ;
-  static constexpr int NBUF = F32 ? 1 : 2;
-  static constexpr int TILES = KC / 16;                  // 16-key MFMA tiles per chunk
-  static constexpr int BLOCK_KEYS_SHIFT = F32 ? 7 : 6;   // block item -> (key quad, dim chunk)
-  static constexpr int ROPE_SHIFT = F32 ? 4 : 3;         // rope item -> (key, chunk)
-  static constexpr int ROPE_CHUNK0 = kValueDim / EPC;    // first 16-byte chunk of the RoPE part
+  static constexpr int ESZ = F32 ? 4 : 2;                    // bytes per element
+  static constexpr int ROW_BYTES = kLatentDim * ESZ;         // one latent row
+  static constexpr int ROW_CHUNKS = ROW_BYTES / 16;          // 16-byte chunks per row (multiple of 8)
+  static constexpr int BUF_BYTES = kChunkKeys * ROW_BYTES;
+  static constexpr int NBUF = F32 ? 1 : 2;                   // LDS buffers (147,456 bytes either way)
+  static constexpr int WAVE_LOADS = 16 * ROW_CHUNKS / 64;    // 1 KiB direct loads per wave per chunk
 };
+static_assert(AttnCfg<false>::ROW_CHUNKS % 8 == 0 && AttnCfg<true>::ROW_CHUNKS % 8 == 0, "swizzle groups");
 
-// Element offset of (value dim v, key column c, c % 4 == 0) in the
-// value-major copy. bf16 rows are 64 bytes = eight 8-byte slots of 4 keys,
-// slot c/4 stored at (c/4) ^ phi(v) with phi(v) = ((v >> 1) ^ (v >> 4)) & 7:
-// the MFMA operand reads (16 consecutive rows, one slot each) and the
-// transposed writes (rows 8 apart, alternating parity) both land on 16
-// distinct 8-byte slots of every 128-byte bank window.
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Chunk permutation of key row r (see the header comment).
+__device__ __forceinline__ int row_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Wave `wave` starts the gather of its 16 rows of chunk c: keys
+// j_beg + 64c + 16*wave + (0..15), whose raw indices the wave left in
+// s_idx[64c + 16*wave + i] (-1 past the range). Rows of missing keys (idx < 0,
+// outside the cache) are zero-filled. Returns the 16-bit mask of present keys
+// (bit i: row 16*wave + i of the chunk).
 template <bool F32>
-__device__ __forceinline__ int cv_off(int v, int c) {
+__device__ __forceinline__ uint32_t issue_chunk(const AttnArgs& a, int64_t base, const int* s_idx, int c,
+                                                char* buf, int wave, int lane) {
   using Cfg = AttnCfg<F32>;
-  if constexpr (F32) return v * Cfg::CV_STRIDE + c;
-  else return v * Cfg::CV_STRIDE + 4 * ((c >> 2) ^ (((v >> 1) ^ (v >> 4)) & 7));
+  int64_t src = -1;
+  if (lane < 16) {
+    const int s = s_idx[kChunkKeys * c + 16 * wave + lane];
+    const int64_t row = base + s;
+    if (s >= 0 && base >= 0 && row < a.cache_rows) src = row * Cfg::ROW_BYTES;
+  }
+  const uint32_t ok = uint32_t(__ballot(src >= 0)) & 0xFFFFu;
+  const uint32_t src_lo = uint32_t(uint64_t(src)), src_hi = uint32_t(uint64_t(src) >> 32);
+  const char* lat = static_cast<const char*>(a.latent);
+  char* wbuf = buf + 16 * wave * Cfg::ROW_BYTES;
+#pragma unroll
+  for (int m = 0; m < Cfg::WAVE_LOADS; ++m) {
+    // the 64 chunks of this load span rows rA (lanes < cut) and rA + 1
+    const int rA = (64 * m) / Cfg::ROW_CHUNKS;
+    const int cut = Cfg::ROW_CHUNKS * (rA + 1) - 64 * m;
+    const int rB = rA + 1 < 16 ? rA + 1 : 15;
+    const bool inA = lane < cut;
+    const int rl = inA ? rA : rA + 1;
+    const int pc = 64 * m + lane - Cfg::ROW_CHUNKS * rl;  // physical chunk in the row
+    const int lc = pc ^ row_swz(rl);                      // logical chunk it holds
+    const uint32_t loA = __builtin_amdgcn_readlane(src_lo, rA), loB = __builtin_amdgcn_readlane(src_lo, rB);
+    const uint32_t hiA = __builtin_amdgcn_readlane(src_hi, rA), hiB = __builtin_amdgcn_readlane(src_hi, rB);
+    const int64_t so = int64_t((uint64_t(inA ? hiA : hiB) << 32) | (inA ? loA : loB));
+    if ((ok >> rl) & 1u)
+      __builtin_amdgcn_global_load_lds(lat + so + 16 * lc, (lds_ptr)(wbuf + 1024 * m), 16, 0, 0);
+  }
+  if (ok != 0xFFFFu) {
+    for (int q = lane; q < 16 * Cfg::ROW_CHUNKS; q += 64)
+      if (!((ok >> (q / Cfg::ROW_CHUNKS)) & 1u)) *reinterpret_cast<uint4*>(wbuf + 16 * q) = uint4{0u, 0u, 0u, 0u};
+  }
+  return ok;
 }
 
 template <bool F32>
 using QFrag = typename std::conditional<F32, f32x8, bf16x8>::type;
 
-// Gathered data of one chunk held by one thread between the load and the
-// LDS write: two 4-key x 16-byte transpose blocks and one RoPE chunk.
-struct Stage {
-  uint4 blk[2][4];
-  uint4 rope;
-  int ok_rope;
-};
-
-template <bool F32>
-__device__ __forceinline__ void gather(Stage& st, const AttnArgs& a, int r, int64_t base, int j0, int j_end) {
-  using Cfg = AttnCfg<F32>;
-  const int t = threadIdx.x;
-  const char* lat = static_cast<const char*>(a.latent);
-  auto row_of = [&](int key, bool& ok) -> int64_t {
-    const int j = j0 + key;
-    const int s = j < j_end ? a.idx[int64_t(r) * a.k + j] : -1;
-    const int64_t row = base + s;
-    ok = s >= 0 && base >= 0 && row < a.cache_rows;
-    return ok ? row : 0;
-  };
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int item = t + h * kAttnThreads;  // 0..511
-    const int kq = item >> Cfg::BLOCK_KEYS_SHIFT;
-    const int dc = item & ((1 << Cfg::BLOCK_KEYS_SHIFT) - 1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bool ok;
-      const int64_t row = row_of(4 * kq + q, ok);
-      st.blk[h][q] = ok ? *reinterpret_cast<const uint4*>(lat + row * (kLatentDim * Cfg::ESZ) + 16 * dc)
-                        : uint4{0u, 0u, 0u, 0u};
-    }
-  }
-  {
-    const int it = t;  // rope item 0..255
-    const int key = it >> Cfg::ROPE_SHIFT;
-    const int ch = Cfg::ROPE_CHUNK0 + (it & ((1 << Cfg::ROPE_SHIFT) - 1));
-    bool ok;
-    const int64_t row = row_of(key, ok);
-    st.rope = ok ? *reinterpret_cast<const uint4*>(lat + row * (kLatentDim * Cfg::ESZ) + 16 * ch)
-                 : uint4{0u, 0u, 0u, 0u};
-    st.ok_rope = ok;
-  }
-}
-
-template <bool F32>
-__device__ __forceinline__ void stage_to_lds(const Stage& st, char* buf, int* valid) {
-  using Cfg = AttnCfg<F32>;
-  const int t = threadIdx.x;
-  char* ck = buf;
-  char* cv = buf + Cfg::CK_ELEMS * Cfg::ESZ;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int item = t + h * kAttnThreads;
-    const int kq = item >> Cfg::BLOCK_KEYS_SHIFT;
-    const int dc = item & ((1 << Cfg::BLOCK_KEYS_SHIFT) - 1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<uint4*>(ck + ((4 * kq + q) * Cfg::CK_STRIDE + Cfg::EPC * dc) * Cfg::ESZ) = st.blk[h][q];
-    if constexpr (F32) {
-      // 4 keys x 4 dims -> 4 value rows of 4 keys
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.blk[h][0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.blk[h][1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.blk[h][2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.blk[h][3]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<uint4*>(cv + cv_off<F32>(4 * dc + e, 4 * kq) * 4) = uint4{w0[e], w1[e], w2[e], w3[e]};
-    } else {
-      // 4 keys x 8 dims -> 8 value rows of 4 keys (two bf16 per word)
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.blk[h][0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.blk[h][1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.blk[h][2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.blk[h][3]);
-      // Step s writes row 8*dc + (s ^ odd): lanes of odd dc take the other row
-      // of each pair, so neighbouring lanes write rows of different parity.
-      const int odd = dc & 1;
-#pragma unroll
-      for (int sp = 0; sp < 8; sp += 2) {
-        const int wi = sp >> 1;
-        const uint32_t lo_e = (w0[wi] & 0xFFFFu) | (w1[wi] << 16);
-        const uint32_t hi_e = (w2[wi] & 0xFFFFu) | (w3[wi] << 16);
-        const uint32_t lo_o = (w0[wi] >> 16) | (w1[wi] & 0xFFFF0000u);
-        const uint32_t hi_o = (w2[wi] >> 16) | (w3[wi] & 0xFFFF0000u);
-        const int e0 = sp + odd, e1 = sp + (odd ^ 1);
-        *reinterpret_cast<uint2*>(cv + cv_off<F32>(8 * dc + e0, 4 * kq) * 2) =
-            odd ? uint2{lo_o, hi_o} : uint2{lo_e, hi_e};
-        *reinterpret_cast<uint2*>(cv + cv_off<F32>(8 * dc + e1, 4 * kq) * 2) =
-            odd ? uint2{lo_e, hi_e} : uint2{lo_o, hi_o};
-      }
-    }
-  }
-  {
-    const int it = t;
-    const int key = it >> Cfg::ROPE_SHIFT;
-    const int sub = it & ((1 << Cfg::ROPE_SHIFT) - 1);
-    *reinterpret_cast<uint4*>(ck + (key * Cfg::CK_STRIDE + Cfg::EPC * (Cfg::ROPE_CHUNK0 + sub)) * Cfg::ESZ) = st.rope;
-    if (sub == 0) valid[key] = st.ok_rope;
-  }
-}
-
 template <bool F32>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, int splits, int kps) {
   using Cfg = AttnCfg<F32>;
-  constexpr int KC = Cfg::KC;
-  // chunk buffers, reused by the epilogue for O as [64 heads][512] floats
-  constexpr int kOutBytes = 64 * (kValueDim + 4) * 4;
-  constexpr int kSmem = Cfg::NBUF * Cfg::BUF_BYTES > kOutBytes ? Cfg::NBUF * Cfg::BUF_BYTES : kOutBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
-  __shared__ int s_valid[Cfg::NBUF][KC];
+  using PT = typename std::conditional<F32, float, __bf16>::type;
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::NBUF * Cfg::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) PT s_p[kGroupHeads * kPRow];  // P^T as [head][key]
+  __shared__ float s_max[4][kGroupHeads];
+  __shared__ float s_l[4][kGroupHeads];
+  __shared__ int s_idx[kMaxTopk];  // raw indices of the range; wave w owns entries 64c + 16w + (0..15)
 
-  const int split = blockIdx.x % splits;
-  const int r = blockIdx.x / splits;
-  const int hb = blockIdx.y;
+  const int HG = (a.H + kGroupHeads - 1) / kGroupHeads;
+  const int pairs = a.R * splits;
+  int pair, hg;
+  {
+    const int u = blockIdx.x;
+    if ((pairs & 7) == 0) {  // workgroup u runs on XCD u mod 8: keep a pair's head groups together
+      const int local = u >> 3;
+      pair = (local / HG) * 8 + (u & 7);
+      hg = local % HG;
+    } else {
+      pair = u / HG;
+      hg = u % HG;
+    }
+  }
+  const int r = pair / splits, split = pair % splits;
   const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // scalar: LDS bases of direct loads must be
+  const int lane = t & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int h0 = hb * 64 + wave * 16;
-  const bool has_heads = h0 < a.H;
+  const int h = hg * kGroupHeads + col;  // this lane's head (MFMA column)
 
   int b = a.q_seq ? a.q_seq[r] : r;
   b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
   const int64_t base = a.row_off[b];
   const int j_beg = split * kps;
   const int j_end = (j_beg + kps < a.k) ? j_beg + kps : a.k;
-  const int nchunks = j_end > j_beg ? (j_end - j_beg + KC - 1) / KC : 0;
+  const int nchunks = j_end > j_beg ? (j_end - j_beg + kChunkKeys - 1) / kChunkKeys : 0;
 
-  Stage st;
-  if (nchunks > 0) gather<F32>(st, a, r, base, j_beg, j_end);
+  // Query fragments (B operand of q.c): head h, dims 32*ks + 8*grp .. +8.
+  // This wave's indices for every chunk, fetched once (one wait) before the
+  // query loads, so that no later wait on them also waits for other loads.
+  for (int q = lane; q < 16 * nchunks; q += 64) {
+    const int e = kChunkKeys * (q >> 4) + 16 * wave + (q & 15);
+    const int j = j_beg + e;
+    s_idx[e] = j < j_end ? a.idx[int64_t(r) * a.k + j] : -1;
+  }
 
-  // Query fragments (B operand of q.c): head h0 + col, dims 32*ks + 8*grp .. +8.
+  // Heads past H (last group) load head H-1 and are zeroed.
   QFrag<F32> qf[18];
   {
-    const int h = h0 + col;
+    const bool hv = h < a.H;
+    const int64_t qoff = (int64_t(r) * a.H + (hv ? h : a.H - 1)) * kLatentDim + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      if (h < a.H) {
-        const int64_t off = (int64_t(r) * a.H + h) * kLatentDim + 32 * ks + 8 * grp;
-        if constexpr (F32) {
-          const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + off);
-          const float4 x = p[0], y = p[1];
-          qf[ks] = f32x8{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
-        } else {
-          qf[ks] = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) + off);
-        }
+      if constexpr (F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qoff + 32 * ks);
+        const float4 x = p[0], y = p[1];
+        qf[ks] = hv ? f32x8{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}} : f32x8{{0, 0, 0, 0, 0, 0, 0, 0}};
       } else {
-        if constexpr (F32) qf[ks] = f32x8{{0, 0, 0, 0, 0, 0, 0, 0}};
-        else qf[ks] = bf16x8{};
+        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qoff + 32 * ks);
+        qf[ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
       }
     }
   }
 
-  f32x4 acc_o[32];
+  uint32_t ok[Cfg::NBUF];
 #pragma unroll
-  for (int mv = 0; mv < 32; ++mv) acc_o[mv] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max (log2 domain) of this lane's head
+  for (int i = 0; i < Cfg::NBUF; ++i)
+    ok[i] = i < nchunks ? issue_chunk<F32>(a, base, s_idx, i, smem + i * Cfg::BUF_BYTES, wave, lane) : 0u;
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int vt = 0; vt < 8; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max (log2 domain) of head h, equal in all waves
   float l_part = 0.f;       // this lane's share of the running sum
   const float scale2 = a.scale * kLog2e;
 
   for (int c = 0; c < nchunks; ++c) {
     const int bi = Cfg::NBUF == 2 ? (c & 1) : 0;
     char* buf = smem + bi * Cfg::BUF_BYTES;
-    if (Cfg::NBUF == 1 && c > 0) __syncthreads();  // single buffer: previous chunk consumed
-    stage_to_lds<F32>(st, buf, s_valid[bi]);
-    if (Cfg::NBUF == 2 && c + 1 < nchunks) gather<F32>(st, a, r, base, j_beg + (c + 1) * KC, j_end);
-    __syncthreads();  // this chunk is in LDS; the other buffer is free for the next write
-    if (Cfg::NBUF == 1 && c + 1 < nchunks) gather<F32>(st, a, r, base, j_beg + (c + 1) * KC, j_end);
+    if (Cfg::NBUF == 1 && c > 0) {
+      __syncthreads();  // every wave is done with the previous chunk
+      ok[0] = issue_chunk<F32>(a, base, s_idx, c, buf, wave, lane);
+    }
+    const uint32_t okc = ok[bi];
 
-    if (has_heads) {
-      const char* ck = buf;
-      const char* cv = buf + Cfg::CK_ELEMS * Cfg::ESZ;
-      // ---- logits: S^T[key][head] = C . Q^T ------------------------------------
-      // Four independent accumulator chains per tile (K-steps ks mod 4), summed
-      // in a fixed order, so the matrix cores are not serialised on one chain.
-      f32x4 sacc[Cfg::TILES];
+    // ---- logits of this wave's 16 keys: S^T = C[16 x 576] . Q^T ----------------------
+    f32x4 sacc;
+    {
+      const char* rp = buf + (16 * wave + col) * Cfg::ROW_BYTES;
+      const int sw = row_swz(col);
+      f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int mt = 0; mt < Cfg::TILES; ++mt) {
-        f32x4 part[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) part[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const char* rowp = ck + ((16 * mt + col) * Cfg::CK_STRIDE + 8 * grp) * Cfg::ESZ;
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          if constexpr (F32) {
-            const float4* p = reinterpret_cast<const float4*>(rowp + 32 * ks * 4);
-            const float4 x = p[0], y = p[1];
-            const f32x8 af{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
-            part[ks & 3] = mfma_k32(af, qf[ks], part[ks & 3]);
-          } else {
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(rowp + 32 * ks * 2);
-            part[ks & 3] = mfma_k32(af, qf[ks], part[ks & 3]);
-          }
-        }
-        sacc[mt] = (part[0] + part[1]) + (part[2] + part[3]);
-      }
-
-      // ---- online softmax -------------------------------------------------------
-      float x[Cfg::TILES][4];
-      float cmax = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < Cfg::TILES; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * mt + 4 * grp + i;
-          x[mt][i] = s_valid[bi][key] ? sacc[mt][i] * scale2 : -INFINITY;
-          cmax = fmaxf(cmax, x[mt][i]);
-        }
-      cmax = fmaxf(cmax, wave_shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, wave_shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);
-      if (m_new != -INFINITY) {  // wave-uniform: validity is per key, shared by heads
-        const float alpha = exp2f(m_run - m_new);
-        float p[Cfg::TILES][4];
-        float psum = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < Cfg::TILES; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float pv = exp2f(x[mt][i] - m_new);
-            if constexpr (!F32) pv = static_cast<float>(static_cast<__bf16>(pv));
-            p[mt][i] = pv;
-            psum += pv;
-          }
-        l_part = l_part * alpha + psum;
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-          for (int mv = 0; mv < 32; ++mv) acc_o[mv] *= alpha;
-        }
-        m_run = m_new;
-
-        // ---- O^T += C^T . P^T --------------------------------------------------------
+      for (int ks = 0; ks < 18; ++ks) {
         if constexpr (F32) {
-#pragma unroll
-          for (int mv = 0; mv < 32; ++mv) {
-            const float4 cvv = *reinterpret_cast<const float4*>(cv + cv_off<F32>(16 * mv + col, 4 * grp) * 4);
-            acc_o[mv] = __builtin_amdgcn_mfma_f32_16x16x4f32(cvv.x, p[0][0], acc_o[mv], 0, 0, 0);
-            acc_o[mv] = __builtin_amdgcn_mfma_f32_16x16x4f32(cvv.y, p[0][1], acc_o[mv], 0, 0, 0);
-            acc_o[mv] = __builtin_amdgcn_mfma_f32_16x16x4f32(cvv.z, p[0][2], acc_o[mv], 0, 0, 0);
-            acc_o[mv] = __builtin_amdgcn_mfma_f32_16x16x4f32(cvv.w, p[0][3], acc_o[mv], 0, 0, 0);
-          }
+          const int c0 = 8 * ks + 2 * grp;
+          const float4 x = *reinterpret_cast<const float4*>(rp + 16 * (c0 ^ sw));
+          const float4 y = *reinterpret_cast<const float4*>(rp + 16 * ((c0 + 1) ^ sw));
+          const f32x8 af{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
+          part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
         } else {
-          // K-slot 8*grp + i <-> key 4*grp + i (i < 4) and 16 + 4*grp + (i - 4) (i >= 4)
-          const bf16x8 pf{static_cast<__bf16>(p[0][0]), static_cast<__bf16>(p[0][1]),
-                          static_cast<__bf16>(p[0][2]), static_cast<__bf16>(p[0][3]),
-                          static_cast<__bf16>(p[1][0]), static_cast<__bf16>(p[1][1]),
-                          static_cast<__bf16>(p[1][2]), static_cast<__bf16>(p[1][3])};
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(rp + 16 * ((4 * ks + grp) ^ sw));
+          part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
+        }
+      }
+      sacc = part[0] + part[1];
+    }
+
+    // ---- chunk maximum per head over the 4 waves ----------------------------------------
+    float x[4];
+    float mx = -INFINITY;
 #pragma unroll
-          for (int mv = 0; mv < 32; ++mv) {
-            const int v = 16 * mv + col;
-            const uint2 lo = *reinterpret_cast<const uint2*>(cv + cv_off<F32>(v, 4 * grp) * 2);
-            const uint2 hi = *reinterpret_cast<const uint2*>(cv + cv_off<F32>(v, 16 + 4 * grp) * 2);
-            const bf16x8 af = __builtin_bit_cast(bf16x8, uint4{lo.x, lo.y, hi.x, hi.y});
-            acc_o[mv] = mfma_k32(af, pf, acc_o[mv]);
-          }
+    for (int i = 0; i < 4; ++i) {
+      x[i] = ((okc >> (4 * grp + i)) & 1u) ? sacc[i] * scale2 : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    if (grp == 0) s_max[wave][col] = mx;
+    __syncthreads();  // maxima visible; every wave is done with chunk c-1 and has its rows of chunk c
+    const float cmax = fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col]));
+    if (Cfg::NBUF == 2 && c + 1 < nchunks && c >= 1)
+      ok[bi ^ 1] = issue_chunk<F32>(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
+
+    const float m_new = fmaxf(m_run, cmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no key seen yet: p = alpha = 0
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+    PT pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = exp2f(x[i] - m_use);
+      pv[i] = static_cast<PT>(e);
+      psum += static_cast<float>(pv[i]);
+    }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int vt = 0; vt < 8; ++vt) acc[vt] *= alpha;
+    }
+    PT* prow = s_p + col * kPRow + 16 * wave + 4 * grp;
+    if constexpr (F32) {
+      *reinterpret_cast<float4*>(prow) = float4{pv[0], pv[1], pv[2], pv[3]};
+    } else {
+      const uint32_t w0 = uint32_t(__builtin_bit_cast(uint16_t, pv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[1])) << 16);
+      const uint32_t w1 = uint32_t(__builtin_bit_cast(uint16_t, pv[2])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[3])) << 16);
+      *reinterpret_cast<uint2*>(prow) = uint2{w0, w1};
+    }
+    __syncthreads();  // P^T of all 64 keys in LDS
+
+    // ---- O^T[128*wave + 16*vt + (0..15)][head] += C^T . P^T over the 64 keys -------------
+    if constexpr (F32) {
+#pragma unroll
+      for (int kq = 0; kq < kChunkKeys / 4; ++kq) {
+        const int row = 4 * kq + grp;
+        const float pf = s_p[col * kPRow + row];
+        const char* rp = buf + row * Cfg::ROW_BYTES;
+        const int sw = row_swz(row);
+#pragma unroll
+        for (int vt = 0; vt < 8; ++vt) {
+          const int v = 128 * wave + 16 * vt + col;
+          const float cv = *reinterpret_cast<const float*>(rp + 16 * ((v >> 2) ^ sw) + 4 * (v & 3));
+          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cv, pf, acc[vt], 0, 0, 0);
+        }
+      }
+    } else {
+      // K-slot 8*grp + i <-> key kb + 4*grp + i (i < 4) and kb + 16 + 4*grp + (i - 4).
+      // Transposing read: lane s of each 16-lane group names 4 values of row
+      // kb + 4*grp + s/4 (value dims v0 + 4*(s%4) ..), and receives value dim
+      // v0 + s of rows kb + 4*grp + 0..3.
+      const int tr_row = 4 * grp + (col >> 2);
+      const int tr_sw = ((col >> 2) << 1) | (grp & 1);  // row_swz of every row this lane names
+#pragma unroll
+      for (int kb = 0; kb < kChunkKeys; kb += 32) {
+        const PT* pp = s_p + col * kPRow + kb + 4 * grp;
+        const uint2 plo = *reinterpret_cast<const uint2*>(pp);
+        const uint2 phi = *reinterpret_cast<const uint2*>(pp + 16);
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
+        const char* rp = buf + (kb + tr_row) * Cfg::ROW_BYTES + 8 * (col & 1);
+#pragma unroll
+        for (int vt = 0; vt < 8; ++vt) {
+          const int lc = 16 * wave + 2 * vt + ((col >> 1) & 1);
+          const char* p0 = rp + 16 * (lc ^ tr_sw);
+          const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(lds_ptr)p0);
+          const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + 16 * Cfg::ROW_BYTES));
+          const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[vt] = mfma_k32(af, pf, acc[vt]);
         }
       }
     }
   }
 
-  // ---- epilogue: finish the row sums, stage O in LDS as [head][512], then
-  // write whole 2-KiB head rows with contiguous 16-byte stores ----------------
-  float l_tot = l_part + wave_shfl_xor(l_part, 16);
-  l_tot += wave_shfl_xor(l_tot, 32);
-  const bool final_out = splits == 1;
-  __syncthreads();  // every wave is done with the chunk buffers
-  // 4 waves x 16 heads x (512 + 4) floats: the 16-byte pad per head row
-  // spreads the 16 heads of a store over the LDS banks
-  constexpr int kORow = kValueDim + 4;
-  float* o_lds = reinterpret_cast<float*>(smem);
-  if (has_heads) {
-    const float inv = final_out ? (l_tot > 0.f ? 1.f / l_tot : 0.f) : 1.f;
-    float* orow = o_lds + (wave * 16 + col) * kORow;
-#pragma unroll
-    for (int mv = 0; mv < 32; ++mv)
-      *reinterpret_cast<float4*>(orow + 16 * mv + 4 * grp) =
-          float4{acc_o[mv][0] * inv, acc_o[mv][1] * inv, acc_o[mv][2] * inv, acc_o[mv][3] * inv};
-    const int h = h0 + col;
-    if (h < a.H && grp == 0) {
-      const int64_t rh = int64_t(r) * a.H + h;
-      if (final_out) {
-        if (a.lse) a.lse[rh] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-      } else {
-        float* ml = static_cast<float*>(a.ws) + int64_t(a.R) * splits * a.H * kValueDim;
-        const int64_t slot = (int64_t(r) * splits + split) * a.H + h;
-        *reinterpret_cast<float2*>(ml + 2 * slot) = float2{m_run, l_tot};
-      }
-    }
-  }
+  // ---- epilogue: row sums over the lanes and waves, then O rows as float4 ----------------
+  float l_w = l_part + wave_shfl_xor(l_part, 16);
+  l_w += wave_shfl_xor(l_w, 32);
+  if (grp == 0) s_l[wave][col] = l_w;
   __syncthreads();
-  const int hcount = (a.H - hb * 64) < 64 ? (a.H - hb * 64) : 64;  // heads of this block
-  float* dst = final_out ? a.out + (int64_t(r) * a.H + hb * 64) * kValueDim
-                         : static_cast<float*>(a.ws) + ((int64_t(r) * splits + split) * a.H + hb * 64) * kValueDim;
-  for (int i = t; i < hcount * (kValueDim / 4); i += kAttnThreads) {
-    const int hh = i / (kValueDim / 4), v4 = i % (kValueDim / 4);
-    reinterpret_cast<float4*>(dst)[i] = *reinterpret_cast<const float4*>(o_lds + hh * kORow + 4 * v4);
+  const float L = ((s_l[0][col] + s_l[1][col]) + s_l[2][col]) + s_l[3][col];
+  if (h >= a.H) return;
+  const int64_t rh = int64_t(r) * a.H + h;
+  const bool final_out = splits == 1;
+  const float inv = final_out ? (L > 0.f ? 1.f / L : 0.f) : 1.f;
+  float* dst = final_out ? a.out + rh * kValueDim
+                         : static_cast<float*>(a.ws) + ((int64_t(r) * splits + split) * a.H + h) * kValueDim;
+#pragma unroll
+  for (int vt = 0; vt < 8; ++vt)
+    *reinterpret_cast<float4*>(dst + 128 * wave + 16 * vt + 4 * grp) =
+        float4{acc[vt][0] * inv, acc[vt][1] * inv, acc[vt][2] * inv, acc[vt][3] * inv};
+  if (wave == 0 && grp == 0) {
+    if (final_out) {
+      if (a.lse) a.lse[rh] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      float* ml = static_cast<float*>(a.ws) + int64_t(a.R) * splits * a.H * kValueDim;
+      const int64_t slot = (int64_t(r) * splits + split) * a.H + h;
+      *reinterpret_cast<float2*>(ml + 2 * slot) = float2{m_run, L};
+    }
   }
 }
 
@@ -447,18 +404,16 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int splits) {
 
 AttnPlan plan_attention(int R, int H, int k) {
   AttnPlan p{};
-  p.head_blocks = (H + 63) / 64;
-  p.waves = 4;
-  const int base = (R > 0 ? R : 1) * p.head_blocks;
-  const int target = device_cu_count();  // one 4-wave workgroup fills a CU
+  p.head_groups = (H + kGroupHeads - 1) / kGroupHeads;
+  const int base = (R > 0 ? R : 1) * p.head_groups;
+  const int target = device_cu_count();  // one workgroup (147 KiB of LDS) per CU
   int splits = (target + base - 1) / base;
-  const int min_keys = 64;  // at least two chunks, so loads overlap compute
-  int max_splits = (k + min_keys - 1) / min_keys;
+  int max_splits = (k + kChunkKeys - 1) / kChunkKeys;
   if (max_splits > 64) max_splits = 64;  // the combine holds one split per lane
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int kps = (k + splits - 1) / splits;
-  kps = ((kps + 31) / 32) * 32;
+  kps = ((kps + kChunkKeys - 1) / kChunkKeys) * kChunkKeys;
   splits = (k + kps - 1) / kps;
   p.splits = splits;
   p.keys_per_split = kps;
@@ -469,7 +424,7 @@ AttnPlan plan_attention(int R, int H, int k) {
 
 hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
-  dim3 grid(unsigned(a.R) * unsigned(plan.splits), unsigned(plan.head_blocks));
+  const dim3 grid(unsigned(a.R) * unsigned(plan.splits) * unsigned(plan.head_groups));
   if (a.dtype == kF32) sparse_mla_kernel<true><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
   else sparse_mla_kernel<false><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
   hipError_t e = hipGetLastError();
