@@ -11,15 +11,20 @@
 // because 64 flop/B at 8 TB/s is 512 TFLOP/s, three times the fp32 vector peak.
 //
 // Work split: one wave owns `keys_per_wave` consecutive keys of one query
-// and walks them 64 at a time (4 MFMA column tiles of 16 keys). The query's
-// head tile(s) stay in registers as the A operand (heads on M); each lane
-// loads the B operand straight from HBM: key n = lane % 16, 8 consecutive
-// dims per K-step, 16-byte loads. The next 64 keys are loaded while the
-// current ones are multiplied. Epilogue per lane: ReLU, multiply by the head
-// weight, sum over the lane's 16 heads; a 3-shuffle butterfly then leaves
-// lane l with the full score of key s0 + l, so the 64 scores go out as one
-// coalesced 256-byte store. Every sum has a fixed order: the scores are
-// bitwise reproducible.
+// and walks them in groups of 64 (4 MFMA column tiles of 16 keys); the
+// launch gives each CU one 4-wave workgroup and spreads all keys over the
+// CUs once. Key rows go from HBM straight into the wave's LDS stage buffers
+// with 16-byte direct-to-LDS loads, all stages issued up front (after the
+// small query loads) so that the whole working set is in flight at once;
+// each group is multiplied as soon as its own loads have landed, while the
+// later ones are still arriving, and a consumed stage is refilled with the
+// group NS places ahead. The query's head tile(s) stay in registers as
+// the A operand (heads on M), the B operand is read from LDS (key n =
+// lane % 16, 8 consecutive dims per K-step). Epilogue per lane: ReLU,
+// multiply by the head weight, sum over the lane's 16 heads; a 3-shuffle
+// butterfly then leaves lane l with the full score of key s0 + l, so the 64
+// scores go out as one coalesced 256-byte store. Every sum has a fixed order:
+// the scores are bitwise reproducible.
 #include "dsa_common.hpp"
 #include "dsa_internal.hpp"
 
@@ -69,47 +74,128 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 c) {
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-template <int QK>
-struct KeyRaw {
-  uint4 v[QK == 0 ? 2 : 1];  // fp32: 32 B, bf16: 16 B, fp8: low 8 B used
+// Keys of a group sit in LDS as rows of DI elements, the 16-byte chunks of
+// row k permuted (XOR) by k mod 8 (k mod 4 for 4-chunk rows): the B-operand
+// reads of 8 (16) consecutive keys at one chunk offset then fall on distinct
+// banks.
+template <int QK, int DI>
+struct KeyCfg {
+  static constexpr int ESZ = QK == 0 ? 4 : (QK == 1 ? 2 : 1);  // bytes per key element
+  static constexpr int ROW = DI * ESZ;                        // bytes per key row
+  static constexpr int CPR = ROW / 16;                        // 16-byte chunks per row
+  static constexpr int SWZ = CPR < 8 ? CPR - 1 : 7;
+  static constexpr int GK = 64;                               // keys per group
+  static constexpr int GBYTES = GK * ROW;
+  static constexpr int LOADS = GBYTES / 1024;                 // 1 KiB direct loads per group
+  static constexpr int NS = GBYTES >= 32768 ? 1 : (32768 / GBYTES > 4 ? 4 : 32768 / GBYTES);  // stages
 };
 
-template <int QK>
-__device__ __forceinline__ void load_key(KeyRaw<QK>& k, const void* keys, int64_t elem_off) {
-  if constexpr (QK == 0) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(keys) + elem_off);
-    k.v[0] = p[0];
-    k.v[1] = p[1];
-  } else if constexpr (QK == 1) {
-    k.v[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(keys) + elem_off);
-  } else {
-    uint2 c = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(keys) + elem_off);
-    k.v[0] = uint4{c.x, c.y, 0u, 0u};
+// One 16-byte direct-to-LDS load per lane: lane l's bytes land at LDS byte
+// address lds + 16*l (lds wave-uniform). Issued from inline assembly so the
+// compiler, which cannot tell which LDS bytes such a load writes, does not
+// add a wait for every outstanding load before each LDS read; the kernel
+// waits itself, per group, with exact vmcnt counts. M0 is saved and restored.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// 4-byte variant: lane l's word lands at LDS byte address lds + 4*l.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(min(N, 63)): a smaller count only waits longer.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N < 63 ? N : 63) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p)));
+}
+
+// Start the direct-to-LDS load of keys s0 .. s0+63 (those below s_end) into
+// stage buffer `dst`. All earlier LDS reads of the wave are complete first
+// (the buffer may be a stage that was just consumed).
+template <int QK, int DI>
+__device__ __forceinline__ void load_group(const IndexArgs& a, int64_t base, int64_t s0, int64_t s_end, char* dst,
+                                           int lane) {
+  using C = KeyCfg<QK, DI>;
+  const char* keys = static_cast<const char*>(a.keys);
+  const uint32_t to = lds_addr(dst);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int m = 0; m < C::LOADS; ++m) {
+    const int pch = 64 * m + lane;      // physical chunk index in the group
+    const int row = pch / C::CPR;
+    const int lc = (pch % C::CPR) ^ (row & C::SWZ);
+    const int64_t key = s0 + row < s_end ? base + s0 + row : base;  // rows past the range re-read row 0
+    dma16(keys + key * C::ROW + 16 * lc, to + 1024 * m);
   }
 }
 
-template <int QK>
-__device__ __forceinline__ typename Frag<QK>::type key_frag(const KeyRaw<QK>& k) {
+// Wait until at most `ahead` key groups of direct loads are outstanding
+// (0 <= ahead <= 4; every group is LOADS instructions).
+template <int LOADS>
+__device__ __forceinline__ void wait_groups(int ahead) {
+  if (ahead >= 4) wait_vmcnt<4 * LOADS>();
+  else if (ahead == 3) wait_vmcnt<3 * LOADS>();
+  else if (ahead == 2) wait_vmcnt<2 * LOADS>();
+  else if (ahead == 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
+}
+
+// B operand of K-step ks for key row `row` of a stage: dims 32*ks + 8*grp .. +8.
+template <int QK, int DI>
+__device__ __forceinline__ typename Frag<QK>::type key_frag(const char* stage, int row, int grp, int ks) {
+  using C = KeyCfg<QK, DI>;
+  const char* rp = stage + row * C::ROW;
+  const int sw = row & C::SWZ;
   typename Frag<QK>::type f;
   if constexpr (QK == 0) {
-    const uint32_t* u = reinterpret_cast<const uint32_t*>(&k.v[0]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f.v[j] = __uint_as_float(u[j]);
+    const int c0 = 8 * ks + 2 * grp;
+    const float4 x = *reinterpret_cast<const float4*>(rp + 16 * (c0 ^ sw));
+    const float4 y = *reinterpret_cast<const float4*>(rp + 16 * ((c0 + 1) ^ sw));
+    f = f32x8{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
   } else if constexpr (QK == 1) {
-    f = __builtin_bit_cast(bf16x8, k.v[0]);
+    f = *reinterpret_cast<const bf16x8*>(rp + 16 * ((4 * ks + grp) ^ sw));
   } else {
-    f = fp8x8_to_bf16(uint2{k.v[0].x, k.v[0].y});
+    const uint2 c = *reinterpret_cast<const uint2*>(rp + 16 * ((2 * ks + (grp >> 1)) ^ sw) + 8 * (grp & 1));
+    f = fp8x8_to_bf16(c);
   }
   return f;
 }
 
 template <int QK, int MT, int DI>
 __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, int keys_per_wave) {
-  constexpr int NKS = DI / 32;  // K-steps of 32 dims
+  using C = KeyCfg<QK, DI>;
+  constexpr int NKS = DI / 32;       // K-steps of 32 dims
+  constexpr bool kQLds = QK != 0;    // bf16 query and weights staged through LDS
+  constexpr int QCPR = DI / 8;       // 16-byte chunks per bf16 query row
   using F = typename Frag<QK>::type;
+  __shared__ __attribute__((aligned(1024))) char smem[kWaves][C::NS][C::GBYTES];
+  __shared__ __attribute__((aligned(16))) char s_q[kQLds ? 64 * DI * 2 : 16];
+  __shared__ __attribute__((aligned(16))) float s_w[64];
 
   const int r = blockIdx.x;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;  // MFMA column: key within a 16-key tile
   const int grp = lane >> 4;  // K-slot group / C-row group
@@ -122,54 +208,77 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
   if (base < 0 || base >= a.cache_rows) n = 0;
   else if (n > a.cache_rows - base) n = a.cache_rows - base;
 
-  const int64_t s_beg = (int64_t(blockIdx.y) * kWaves + wave) * keys_per_wave;
+  const int64_t wg_beg = int64_t(blockIdx.y) * kWaves * keys_per_wave;
+  if (wg_beg >= n) return;  // the whole workgroup has no key
+  const int64_t s_beg = wg_beg + int64_t(wave) * keys_per_wave;
   const int64_t s_end = s_beg + keys_per_wave < n ? s_beg + keys_per_wave : n;
-  if (s_beg >= s_end) return;
+  const int groups = s_beg < s_end ? int((s_end - s_beg + 63) / 64) : 0;
 
-  // Issue the first key group before the query loads so both are in flight.
-  KeyRaw<QK> cur[4][NKS];
-  auto load_group = [&](KeyRaw<QK> (&dst)[4][NKS], int64_t s0) {
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int64_t s = s0 + 16 * blk + col;
-      const bool ok = s < s_end;
-      const int64_t off = (base + (ok ? s : 0)) * DI + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (ok) load_key<QK>(dst[blk][ks], a.keys, off + 32 * ks);
-        else {
-#pragma unroll
-          for (int j = 0; j < (QK == 0 ? 2 : 1); ++j) dst[blk][ks].v[j] = uint4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-  };
-  load_group(cur, s_beg);
-
-  // A operand: head 16*mt + col, dims 32*ks + 8*grp .. +8. Padded heads are zero.
   F qa[MT][NKS];
   float wr[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = 16 * mt + col;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (h < a.H_I) load_q<QK>(qa[mt][ks], a.q, (int64_t(r) * a.H_I + h) * DI + 32 * ks + 8 * grp);
-      else zero(qa[mt][ks]);
+  int issued = 0;
+  if constexpr (kQLds) {
+    // Query rows (H_I x DI bf16, chunks of row h XOR-permuted by h mod 8) and
+    // the H_I weights go to LDS by direct loads, shared by the 4 waves; the
+    // rows and weights of padded heads are zeroed.
+    const int qchunks = a.H_I * QCPR;
+    const char* qsrc = static_cast<const char*>(a.q) + int64_t(r) * a.H_I * (DI * 2);
+    const uint32_t qlds = lds_addr(s_q);
+    for (int m = wave; 64 * m < qchunks; m += kWaves) {
+      const int pch = 64 * m + lane;
+      const int h = pch / QCPR;
+      const int lc = (pch % QCPR) ^ (h & 7);
+      const char* src = qsrc + int64_t(h) * (DI * 2) + 16 * lc;
+      if (pch < qchunks) dma16(src, qlds + 1024 * m);
     }
+    if (wave == 0 && lane < a.H_I) dma4(a.w + int64_t(r) * a.H_I + lane, lds_addr(s_w));
+    for (int i = threadIdx.x + qchunks; i < 16 * MT * QCPR; i += kWaves * 64)
+      *reinterpret_cast<uint4*>(s_q + 16 * i) = uint4{0u, 0u, 0u, 0u};
+    if (threadIdx.x >= a.H_I && threadIdx.x < 16 * MT) s_w[threadIdx.x] = 0.f;
+    // then all key stages, so the whole working set is in flight
+    for (; issued < C::NS && issued < groups; ++issued)
+      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], lane);
+    wait_groups<C::LOADS>(issued);  // this wave's query and weight loads have landed
+    __syncthreads();
+    // A operand: head 16*mt + col, dims 32*ks + 8*grp .. +8
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hw = 16 * mt + 4 * grp + i;  // C row held by this lane
-      wr[mt][i] = hw < a.H_I ? a.w[int64_t(r) * a.H_I + hw] : 0.f;
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = 16 * mt + col;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qa[mt][ks] = *reinterpret_cast<const bf16x8*>(s_q + h * (DI * 2) + 16 * ((4 * ks + grp) ^ (h & 7)));
+      const float4 w4 = *reinterpret_cast<const float4*>(s_w + 16 * mt + 4 * grp);
+      wr[mt][0] = w4.x;
+      wr[mt][1] = w4.y;
+      wr[mt][2] = w4.z;
+      wr[mt][3] = w4.w;
     }
+  } else {
+    if (groups == 0) return;
+    // fp32: query fragments and weights straight into registers
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = 16 * mt + col;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (h < a.H_I) load_q<QK>(qa[mt][ks], a.q, (int64_t(r) * a.H_I + h) * DI + 32 * ks + 8 * grp);
+        else zero(qa[mt][ks]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hw = 16 * mt + 4 * grp + i;  // C row held by this lane
+        wr[mt][i] = hw < a.H_I ? a.w[int64_t(r) * a.H_I + hw] : 0.f;
+      }
+    }
+    for (; issued < C::NS && issued < groups; ++issued)
+      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], lane);
   }
 
   float* out = a.scores + int64_t(r) * a.ld;
-  for (int64_t s0 = s_beg; s0 < s_end; s0 += 64) {
-    KeyRaw<QK> nxt[4][NKS];
-    const bool more = s0 + 64 < s_end;
-    if (more) load_group(nxt, s0 + 64);
-
+  for (int g = 0; g < groups; ++g) {
+    const int64_t s0 = s_beg + 64 * g;
+    const char* stage = smem[wave][g % C::NS];
+    wait_groups<C::LOADS>(issued - 1 - g);  // group g has landed
     float part[4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
@@ -178,7 +287,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const F kb = key_frag<QK>(cur[blk][ks]);
+        const F kb = key_frag<QK, DI>(stage, 16 * blk + col, grp, ks);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_k32(qa[mt][ks], kb, acc[mt]);
       }
@@ -202,6 +311,11 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
       }
       part[blk] = p;
     }
+    // this stage is consumed: refill it with group g + NS
+    if (issued < groups) {
+      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][g % C::NS], lane);
+      ++issued;
+    }
 
     // Butterfly reduce-scatter over the 4 lane groups of each column:
     // afterwards lane l holds the score of key s0 + l.
@@ -222,53 +336,46 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
       }
       out[s] = v;
     }
-
-    if (more) {
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) cur[blk][ks] = nxt[blk][ks];
-    }
   }
 }
 
 template <int QK, int MT, int DI>
-hipError_t launch_t(const IndexArgs& a, int kpw, hipStream_t stream) {
+hipError_t launch_t(const IndexArgs& a, hipStream_t stream) {
+  // One 4-wave workgroup per CU (the stage buffers take most of the LDS);
+  // keys per wave: a multiple of 64 that spreads all keys over the CUs once.
+  const int64_t total = int64_t(a.R) * a.max_n;
+  const int64_t waves = int64_t(device_cu_count()) * kWaves;
+  int64_t kpw = (total + waves - 1) / waves;
+  kpw = ((kpw + 63) / 64) * 64;
+  if (kpw < 64) kpw = 64;
+  if (kpw > (int64_t(1) << 20)) kpw = int64_t(1) << 20;
   const int64_t per_wg = int64_t(kWaves) * kpw;
   const unsigned chunks = unsigned((a.max_n + per_wg - 1) / per_wg);
   dim3 grid(unsigned(a.R), chunks);
-  index_scores_kernel<QK, MT, DI><<<grid, kWaves * 64, 0, stream>>>(a, kpw);
+  index_scores_kernel<QK, MT, DI><<<grid, kWaves * 64, 0, stream>>>(a, int(kpw));
   return hipGetLastError();
 }
 
 template <int QK, int MT>
-hipError_t launch_d(const IndexArgs& a, int kpw, hipStream_t stream) {
-  return a.D_I == 64 ? launch_t<QK, MT, 64>(a, kpw, stream) : launch_t<QK, MT, 128>(a, kpw, stream);
+hipError_t launch_d(const IndexArgs& a, hipStream_t stream) {
+  return a.D_I == 64 ? launch_t<QK, MT, 64>(a, stream) : launch_t<QK, MT, 128>(a, stream);
 }
 
 template <int QK>
-hipError_t launch_m(const IndexArgs& a, int kpw, hipStream_t stream) {
-  if (a.H_I <= 16) return launch_d<QK, 1>(a, kpw, stream);
-  if (a.H_I <= 32) return launch_d<QK, 2>(a, kpw, stream);
-  return launch_d<QK, 4>(a, kpw, stream);
+hipError_t launch_m(const IndexArgs& a, hipStream_t stream) {
+  if (a.H_I <= 16) return launch_d<QK, 1>(a, stream);
+  if (a.H_I <= 32) return launch_d<QK, 2>(a, stream);
+  return launch_d<QK, 4>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
-  // Keys per wave: enough waves to cover the chip several times over, at
-  // least one 64-key group each.
-  const int64_t total = int64_t(a.R) * a.max_n;
-  const int64_t target_waves = int64_t(device_cu_count()) * 16;
-  int64_t kpw = (total + target_waves - 1) / target_waves;
-  kpw = ((kpw + 63) / 64) * 64;
-  if (kpw < 64) kpw = 64;
-  if (kpw > 1024) kpw = 1024;
   const int mode = a.q_dtype == kF32 ? 0 : (a.k_dtype == kFP8 ? 2 : 1);
-  if (mode == 0) return launch_m<0>(a, int(kpw), stream);
-  if (mode == 1) return launch_m<1>(a, int(kpw), stream);
-  return launch_m<2>(a, int(kpw), stream);
+  if (mode == 0) return launch_m<0>(a, stream);
+  if (mode == 1) return launch_m<1>(a, stream);
+  return launch_m<2>(a, stream);
 }
 
 }  // namespace dsa
