@@ -55,10 +55,28 @@ dsa_status check_attn_args(const void* q_abs, int dtype, const void* latent, int
   return DSA_OK;
 }
 
+// Fused-decode workspace, in order: scores [B, ld] fp32, indices [B, k],
+// attention partials, score sample [B, ld_sample] fp32, split top-k
+// candidates and state (each part 256-byte aligned).
+struct DecodeLayout {
+  int64_t ld, ld_sample;
+  size_t scores, idx, attn, sample, topk, total;
+};
+DecodeLayout decode_layout(int B, int max_len, int k, int H) {
+  DecodeLayout L{};
+  L.ld = (int64_t(max_len) + 3) / 4 * 4;
+  L.ld_sample = ((int64_t(max_len) + 15) / 16 + 3) / 4 * 4;
+  L.scores = 0;
+  L.idx = L.scores + align256(size_t(B) * L.ld * sizeof(float));
+  L.attn = L.idx + align256(size_t(B) * k * sizeof(int32_t));
+  L.sample = L.attn + align256(plan_attention(B, H, k).ws_bytes);
+  L.topk = L.sample + align256(size_t(B) * L.ld_sample * sizeof(float));
+  L.total = L.topk + align256(topk_split_ws_bytes(B));
+  return L;
+}
+
 size_t decode_ws_bytes(int B, int max_len, int k, int H) {
-  const int64_t ld = (int64_t(max_len) + 3) / 4 * 4;
-  return align256(size_t(B) * ld * sizeof(float)) + align256(size_t(B) * k * sizeof(int32_t)) +
-         plan_attention(B, H, k).ws_bytes;
+  return decode_layout(B, max_len, k, H).total;
 }
 
 }  // namespace
@@ -94,23 +112,30 @@ dsa_status dsa_index_scores(const void* q_idx, int32_t q_dtype, const float* hea
   if (ld_scores < max_n || (ld_scores & 3)) return DSA_ERR_SHAPE;
   if (!aligned16(scores)) return DSA_ERR_ALIGN;
   IndexArgs a{q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, q_seq, q_pos, nullptr,
-              R, H_I, D_I, max_n, scores, ld_scores};
+              R, H_I, D_I, max_n, scores, ld_scores, nullptr, 0, nullptr};
   hipError_t e = launch_index_scores(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : hip_fail(e);
 }
 
 dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t R, int32_t max_n,
                     int32_t k, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!scores || !q_pos || !idx_out) return DSA_ERR_NULL;
   if (R < 0 || max_n < 1) return DSA_ERR_SHAPE;
   if (max_n > kMaxTopkRow) return DSA_ERR_UNSUPPORTED;
   if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
   if (ld_scores < max_n || (ld_scores & 3)) return DSA_ERR_SHAPE;
   if (!aligned16(scores)) return DSA_ERR_ALIGN;
-  TopkArgs a{scores, ld_scores, q_pos, nullptr, R, max_n, k, idx_out};
-  hipError_t e = launch_topk(a, static_cast<hipStream_t>(stream));
+  TopkArgs a{scores, ld_scores, q_pos, nullptr, R, max_n, k, idx_out, nullptr, 0, nullptr, nullptr};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // With a large enough workspace, few long rows are split over workgroups.
+  if (workspace && topk_use_split(R, max_n) && ws_bytes >= topk_split_ws_bytes(R)) {
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSA_ERR_ALIGN;
+    a.cand = static_cast<unsigned long long*>(workspace);
+    a.state = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + size_t(R) * 4096 * sizeof(unsigned long long));
+    hipError_t e = launch_topk_clear(a.state, R, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  hipError_t e = launch_topk(a, s);
   return e == hipSuccess ? DSA_OK : hip_fail(e);
 }
 
@@ -148,18 +173,24 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSA_ERR_ALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t ld = (int64_t(max_len) + 3) / 4 * 4;
+  const DecodeLayout L = decode_layout(B, max_len, k, H);
   char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws);
-  int32_t* idx = reinterpret_cast<int32_t*>(ws + align256(size_t(B) * ld * sizeof(float)));
-  void* attn_ws = ws + align256(size_t(B) * ld * sizeof(float)) + align256(size_t(B) * k * sizeof(int32_t));
-  if (idx_out) idx = idx_out;
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  void* attn_ws = ws + L.attn;
+  float* sample = reinterpret_cast<float*>(ws + L.sample);
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws + L.topk);
+  uint32_t* tstate = reinterpret_cast<uint32_t*>(ws + L.topk + size_t(B) * 4096 * sizeof(unsigned long long));
+  const bool split = topk_use_split(B, max_len);
 
+  // the indexer also writes the score sample and clears the top-k state
   IndexArgs ia{q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, nullptr, nullptr,
-               seq_len, B, H_I, D_I, max_len, scores, ld};
+               seq_len, B, H_I, D_I, max_len, scores, L.ld, split ? sample : nullptr, L.ld_sample,
+               split ? tstate : nullptr};
   hipError_t e = launch_index_scores(ia, s);
   if (e != hipSuccess) return hip_fail(e);
-  TopkArgs ta{scores, ld, nullptr, seq_len, B, max_len, k, idx};
+  TopkArgs ta{scores, L.ld, nullptr, seq_len, B, max_len, k, idx, split ? sample : nullptr, L.ld_sample,
+              split ? tstate : nullptr, split ? cand : nullptr};
   e = launch_topk(ta, s);
   if (e != hipSuccess) return hip_fail(e);
   const AttnPlan plan = plan_attention(B, H, k);
@@ -171,6 +202,8 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
 size_t dsa_workspace_size(int32_t entry, int32_t rows, int32_t max_len, int32_t k, int32_t H) {
   if (rows < 0 || k < 1 || H < 1) return 0;
   switch (entry) {
+    case DSA_ENTRY_TOPK:
+      return topk_use_split(rows, max_len) ? topk_split_ws_bytes(rows) : 0;
     case DSA_ENTRY_SPARSE_MLA:
       return plan_attention(rows, H, k).ws_bytes;
     case DSA_ENTRY_DECODE:

@@ -25,6 +25,9 @@ struct IndexArgs {
   int R, H_I, D_I, max_n;
   float* scores;
   int64_t ld;
+  float* sample;          // NULL, or receives sample[r * ld_sample + i] = scores[r, 16 i]
+  int64_t ld_sample;
+  uint32_t* topk_state;   // NULL, or [R][4] words set to zero (split top-k state)
 };
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 
@@ -35,8 +38,17 @@ struct TopkArgs {
   const int32_t* seq_len;
   int R, max_n, k;
   int32_t* idx;
+  // Split selection (several workgroups per row), used when state and cand
+  // are given and the rows are few and long:
+  const float* sample;        // NULL, or sample[r * ld_sample + i] = scores[r, 16 i]
+  int64_t ld_sample;
+  uint32_t* state;            // [R][4], zero at launch; left zero
+  unsigned long long* cand;   // [R][4096] candidate words
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+bool topk_use_split(int R, int max_n);
+size_t topk_split_ws_bytes(int R);  // cand, then state
+hipError_t launch_topk_clear(uint32_t* state, int R, hipStream_t stream);
 
 struct AttnPlan {
   int splits;           // key splits per query row

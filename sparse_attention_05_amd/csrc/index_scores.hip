@@ -199,6 +199,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;  // MFMA column: key within a 16-key tile
   const int grp = lane >> 4;  // K-slot group / C-row group
+  if (a.topk_state && blockIdx.y == 0 && threadIdx.x < 4) a.topk_state[4 * r + threadIdx.x] = 0u;
 
   int b = a.q_seq ? a.q_seq[r] : r;
   b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
@@ -335,6 +336,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
         if (!(sc < 0.f)) v *= sc;
       }
       out[s] = v;
+      if (a.sample && (s & 15) == 0) a.sample[int64_t(r) * a.ld_sample + (s >> 4)] = v;
     }
   }
 }

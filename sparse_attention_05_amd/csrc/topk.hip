@@ -559,6 +559,51 @@ __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
   return n;
 }
 
+// Pivot from the sample sh.v.samp[0..ns) (every SS-th key of the row, range
+// [smin, smax]): the lower edge of the 12-bit histogram bin that holds the
+// (ceil(k/SS)+24)-th largest sample, so that about k + 24*SS keys clear it.
+__device__ __forceinline__ uint32_t sample_pivot(TopkShared& sh, int ns, int SS, int k, uint32_t smin, uint32_t smax) {
+  uint32_t target_s = uint32_t((k + SS - 1) / SS + 24);
+  if (target_s > uint32_t(ns)) target_s = uint32_t(ns);
+  uint32_t pivot = smin;
+  if (smin < smax) {
+    int shift, nb;
+    digit_plan(smin, smax, 12, shift, nb);
+    clear_bins(sh.bins, kBins);
+    __syncthreads();
+    for (int i = int(threadIdx.x); i < ns; i += kThreads) atomicAdd(&sh.bins[(sh.v.samp[i] - smin) >> shift], 1u);
+    __syncthreads();
+    uint32_t b, above, cnt;
+    find_crossing(sh, target_s, b, above, cnt);
+    pivot = smin + (b << shift);
+  }
+  return pivot;
+}
+
+// Exact selection over a whole row held by `row` (any EPT), for rows whose
+// pivot did not yield k..kCap candidates: radix select finds the k-th key T,
+// the kept keys equal to T are the `need` smallest indices, and the k winners
+// are sorted.
+template <int EPT>
+__device__ __forceinline__ void select_exact(TopkShared& sh, const Row<EPT>& row, int n, int k, int32_t* out) {
+  auto each_row = [&](auto&& f) { row.each(f); };
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  row.each([&](int idx, uint32_t key) {
+    if (idx < n) {
+      lo = min(lo, key);
+      hi = max(hi, key);
+    }
+  });
+  block_minmax(lo, hi, sh.red);
+  uint32_t T, need, eq_total, I = 0u;
+  auto visit_keys = [&](auto&& f) { row.each([&](int, uint32_t key) { f(key); }); };
+  select_full(sh, visit_keys, lo, hi, uint32_t(k), uint32_t(n), T, need, eq_total);
+  if (need < eq_total) I = tie_threshold(sh, each_row, T, need, eq_total, n);
+  collect_winners(sh, each_row, T, I);
+  sort_words(sh, k, (static_cast<unsigned long long>(hi) << 32) | 0xFFFFFFFFull,
+             static_cast<unsigned long long>(T) << 32, k, out);
+}
+
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   __shared__ TopkShared sh;
@@ -606,20 +651,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     smax = max(smax, key);
   });
   block_minmax(smin, smax, sh.red);
-  uint32_t target_s = uint32_t((k + SS - 1) / SS + 24);
-  if (target_s > uint32_t(ns)) target_s = uint32_t(ns);
-  uint32_t pivot = smin;
-  if (smin < smax) {
-    int shift, nb;
-    digit_plan(smin, smax, 12, shift, nb);
-    clear_bins(sh.bins, kBins);
-    __syncthreads();
-    for (int i = t; i < ns; i += kThreads) atomicAdd(&sh.bins[(sh.v.samp[i] - smin) >> shift], 1u);
-    __syncthreads();
-    uint32_t b, above, cnt;
-    find_crossing(sh, target_s, b, above, cnt);
-    pivot = smin + (b << shift);
-  }
+  const uint32_t pivot = sample_pivot(sh, ns, SS, k, smin, smax);
 
   // ---- 2. candidates >= pivot ---------------------------------------------------------
   uint32_t c = 0, cmax = 0;
@@ -641,27 +673,151 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   }
 
   // ---- fallback: exact select over the whole row, then sort the k winners ----------------
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  row.each([&](int idx, uint32_t key) {
-    if (idx < n) {
-      lo = min(lo, key);
-      hi = max(hi, key);
+  select_exact(sh, row, n, k, out);
+}
+
+// Split selection for few long rows: the row is cut into slices of kTile
+// keys, one workgroup each. Every workgroup derives the same pivot from the
+// row's sample, appends its slice's candidates (keys >= pivot, as words) to
+// the row's candidate array at an offset claimed with one atomic add, and
+// counts itself in; the last workgroup of the row to arrive sorts the
+// candidates (or runs the exact selection over the whole row when fewer than
+// k or more than kCap keys cleared the pivot) and clears the row's state for
+// the next launch. The candidate set is fixed by the pivot, so the order in
+// which slices append does not change the result.
+__global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a, int slices) {
+  __shared__ TopkShared sh;
+  const int r = blockIdx.x / slices, g = blockIdx.x % slices;
+  const int t = threadIdx.x;
+  const int n = row_len(a, r);
+  const int k = a.k;
+  const float* row = a.scores + int64_t(r) * a.ld;
+  uint32_t* st = a.state + 4 * r;  // count, arrivals, max candidate key, ~min candidate key
+  unsigned long long* cand = a.cand + int64_t(r) * kCap;
+
+  // ---- pivot (identical in every slice of the row; 0 when every key wins) ----------------
+  uint32_t pivot = 0u;
+  if (n > k) {
+    int SS = 16;
+    while ((n + SS - 1) / SS > 4096) SS <<= 1;
+    const int ns = (n + SS - 1) / SS;
+    uint32_t smin = 0xFFFFFFFFu, smax = 0u;
+    for (int i = t; i < ns; i += kThreads) {
+      const float v = a.sample ? a.sample[int64_t(r) * a.ld_sample + int64_t(i) * (SS / 16)] : row[int64_t(i) * SS];
+      const uint32_t key = order_key(v);
+      sh.v.samp[i] = key;
+      smin = min(smin, key);
+      smax = max(smax, key);
     }
-  });
-  block_minmax(lo, hi, sh.red);
-  uint32_t T, need, eq_total, I = 0u;
-  auto visit_keys = [&](auto&& f) { row.each([&](int, uint32_t key) { f(key); }); };
-  select_full(sh, visit_keys, lo, hi, uint32_t(k), uint32_t(n), T, need, eq_total);
-  if (need < eq_total) I = tie_threshold(sh, each_row, T, need, eq_total, n);
-  collect_winners(sh, each_row, T, I);
-  sort_words(sh, k, (static_cast<unsigned long long>(hi) << 32) | 0xFFFFFFFFull,
-             static_cast<unsigned long long>(T) << 32, k, out);
+    block_minmax(smin, smax, sh.red);
+    pivot = sample_pivot(sh, ns, SS, k, smin, smax);
+  }
+
+  // ---- this slice's candidates -----------------------------------------------------------
+  const int i0 = g * kTile + 4 * t;
+  uint32_t key[4];
+  {
+    const float4 v = i0 < n ? *reinterpret_cast<const float4*>(row + i0) : float4{0.f, 0.f, 0.f, 0.f};
+    key[0] = order_key(v.x);
+    key[1] = order_key(v.y);
+    key[2] = order_key(v.z);
+    key[3] = order_key(v.w);
+  }
+  uint32_t c = 0, kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (i0 + e < n && key[e] >= pivot) {
+      ++c;
+      kmax = max(kmax, key[e]);
+      kmin = min(kmin, key[e]);
+    }
+  }
+  uint32_t total;
+  uint32_t pos = block_scan(c, sh.red, total);
+  block_minmax(kmin, kmax, sh.red);
+  // Cross-workgroup traffic uses device-coherent accesses (relaxed atomics at
+  // agent scope: performed or written through past the per-XCD L2s) instead
+  // of fences, which would write back whole L2 caches.
+  if (t == 0) {
+    sh.misc[0] = total ? __hip_atomic_fetch_add(&st[0], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    if (total) {
+      __hip_atomic_fetch_max(&st[2], kmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_max(&st[3], ~kmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  const uint32_t at = sh.misc[0];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (i0 + e < n && key[e] >= pivot) {
+      if (at + pos < uint32_t(kCap))
+        __hip_atomic_store(&cand[at + pos], word(key[e], i0 + e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ++pos;
+    }
+  }
+
+  // ---- arrival: the last slice of the row finishes it -------------------------------------
+  // Every thread's candidate stores have completed before the slice counts
+  // itself in (vmcnt covers stores), so the last slice sees all of them.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (t == 0) sh.misc[1] = __hip_atomic_fetch_add(&st[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sh.misc[1] != uint32_t(slices - 1)) return;
+  if (t == 0) {
+    sh.misc[2] = __hip_atomic_load(&st[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.misc[3] = __hip_atomic_load(&st[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.misc[4] = ~__hip_atomic_load(&st[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const uint32_t C = sh.misc[2], cmax = sh.misc[3], cmin = sh.misc[4];
+  if (t < 4) __hip_atomic_store(&st[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
+
+  const int k_eff = n < k ? n : k;
+  int32_t* out = a.idx + int64_t(r) * k;
+  for (int j = k_eff + t; j < k; j += kThreads) out[j] = -1;
+  if (n == 0) return;
+  if (n <= k || (C >= uint32_t(k) && C <= uint32_t(kCap))) {
+    for (int j = t; j < int(C); j += kThreads)
+      sh.wa[j] = __hip_atomic_load(&cand[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    sort_words(sh, int(C), (static_cast<unsigned long long>(cmax) << 32) | 0xFFFFFFFFull,
+               static_cast<unsigned long long>(cmin) << 32, k_eff, out);
+    return;
+  }
+  Row<0> full;
+  full.load(row, n);
+  select_exact(sh, full, n, k, out);
+}
+
+__global__ void topk_clear_kernel(uint32_t* state, int words) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < words) state[i] = 0u;
 }
 
 }  // namespace
 
+bool topk_use_split(int R, int max_n) {
+  return max_n > 4 * kTile && R <= device_cu_count() / 2;
+}
+
+size_t topk_split_ws_bytes(int R) {
+  return size_t(R) * kCap * sizeof(unsigned long long) + size_t(R) * 4 * sizeof(uint32_t);
+}
+
+hipError_t launch_topk_clear(uint32_t* state, int R, hipStream_t stream) {
+  const int words = 4 * R;
+  if (words > 0) topk_clear_kernel<<<dim3(unsigned((words + 255) / 256)), 256, 0, stream>>>(state, words);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
+  if (a.state && a.cand && topk_use_split(a.R, a.max_n)) {
+    const int slices = (a.max_n + kTile - 1) / kTile;
+    topk_split_kernel<<<dim3(unsigned(a.R) * unsigned(slices)), kThreads, 0, stream>>>(a, slices);
+    return hipGetLastError();
+  }
   dim3 grid(unsigned(a.R));
   if (a.max_n <= 4 * kTile) topk_kernel<16><<<grid, kThreads, 0, stream>>>(a);
   else if (a.max_n <= 8 * kTile) topk_kernel<32><<<grid, kThreads, 0, stream>>>(a);

@@ -130,13 +130,21 @@ def dsa_index_scores(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Ten
 
 
 def dsa_topk(scores: torch.Tensor, q_pos: torch.Tensor, max_n: int, k: int, *,
-             idx_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Deterministic top-k indices [R, k] (int32, rank order, -1 padded)."""
+             idx_out: Optional[torch.Tensor] = None, workspace=None, stream=None) -> torch.Tensor:
+    """Deterministic top-k indices [R, k] (int32, rank order, -1 padded).
+
+    workspace: None allocates what the library asks for (few long rows are
+    then split over several workgroups); False passes none (one workgroup
+    per row); a uint8 tensor is used as given."""
     R = scores.shape[0]
     if idx_out is None:
         idx_out = torch.empty((R, k), dtype=torch.int32, device=scores.device)
-    st = lib.dsa_topk(_ptr(scores), scores.shape[1], _ptr(q_pos), R, max_n, k, _ptr(idx_out), None, 0,
-                      _stream(stream))
+    if workspace is False:
+        workspace = None
+    else:
+        workspace = _workspace(dsa_workspace_size(DSA_ENTRY_TOPK, R, max_n, k, 1), workspace, scores.device)
+    st = lib.dsa_topk(_ptr(scores), scores.shape[1], _ptr(q_pos), R, max_n, k, _ptr(idx_out), _ptr(workspace),
+                      0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "dsa_topk")
     return idx_out
 

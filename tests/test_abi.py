@@ -119,4 +119,9 @@ def test_decode_rejects_small_workspace(dsa):
 def test_workspace_sizes_are_aligned(dsa):
     for rows, k, H in [(1, 64, 8), (4, 2048, 64), (16, 2048, 64), (8192, 2048, 64)]:
         assert dsa.dsa_workspace_size(dsa.DSA_ENTRY_SPARSE_MLA, rows, 0, k, H) % 256 == 0
-    assert dsa.dsa_workspace_size(dsa.DSA_ENTRY_TOPK, 4, 32768, 2048, 64) == 0
+    # top-k: few long rows get a split-selection workspace (candidates + state),
+    # short rows or many rows need none
+    need = dsa.dsa_workspace_size(dsa.DSA_ENTRY_TOPK, 4, 32768, 2048, 64)
+    assert need >= 4 * 4096 * 8 + 4 * 16
+    assert dsa.dsa_workspace_size(dsa.DSA_ENTRY_TOPK, 4, 8192, 2048, 64) == 0
+    assert dsa.dsa_workspace_size(dsa.DSA_ENTRY_TOPK, 4096, 32768, 2048, 64) == 0

@@ -67,7 +67,7 @@ def _score_rows(kind, n, rng):
     raise KeyError(kind)
 
 
-def _run_topk(dsa, rows, k):
+def _run_topk(dsa, rows, k, split=True):
     import torch
     R = len(rows)
     max_n = max(len(x) for x in rows)
@@ -79,7 +79,7 @@ def _run_topk(dsa, rows, k):
     s_d = torch.from_numpy(S).cuda()
     q_d = torch.from_numpy(q_pos).cuda()
     idx = torch.randint(-7, 1 << 30, (R, k), dtype=torch.int32, device="cuda")
-    dsa.dsa_topk(s_d, q_d, max_n, k, idx_out=idx)
+    dsa.dsa_topk(s_d, q_d, max_n, k, idx_out=idx, workspace=None if split else False)
     return idx.cpu().numpy()
 
 
@@ -105,12 +105,15 @@ TOPK_CASES = [
 ]
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["ws", "nows"])
 @pytest.mark.parametrize("kind,lens,k", TOPK_CASES, ids=[f"{c[0]}-{len(c[1])}rows-k{c[2]}" for c in TOPK_CASES])
-def test_topk_matches_oracle_on_identical_scores(dsa, kind, lens, k):
+def test_topk_matches_oracle_on_identical_scores(dsa, kind, lens, k, split):
+    """With a workspace, rows longer than 8192 go through the split selection
+    (slices, shared pivot, last slice sorts); without, one workgroup per row."""
     rng = np.random.default_rng(zlib.crc32(repr((kind, lens, k)).encode()))
     rows = [_score_rows(kind, n, rng) for n in lens]
-    _say("topk", kind, lens, k)
-    got = _run_topk(dsa, rows, k)
+    _say("topk", kind, lens, k, "split" if split else "single")
+    got = _run_topk(dsa, rows, k, split)
     for r, x in enumerate(rows):
         want = O.topk_row(x, k)
         assert np.array_equal(got[r], want), f"row {r} (n={len(x)}): first diff at {np.argmax(got[r] != want)}"
