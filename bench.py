@@ -76,6 +76,76 @@ def pmc_traffic(kernel_src: str, workload: str):
         return None
 
 
+COPY_BYTES = 256 << 20      # calibration copy for the HBM byte counters
+PMC_LAUNCHES = 20
+
+
+def pmc_pass(workload: str):
+    """Workload for the two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE):
+    an elementwise negation over COPY_BYTES (reads and writes exactly that many
+    bytes) and PMC_LAUNCHES indexer launches on rotating input sets."""
+    import torch
+    from sparse_attention_05_amd import dsa, inputs
+    torch.cuda.set_device(0)
+    p = inputs.workload(workload, seed=0)
+    max_len = int(p.seq_len.max())
+    n_sets = max(2, math.ceil(2 * MALL_BYTES / step_bytes(p)))
+    sets = [inputs.to_torch(p, "cuda") for _ in range(n_sets)]
+    # calibration: an elementwise kernel that reads and writes exactly COPY_BYTES
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    scores = torch.empty((p.B, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda")
+    for i in range(PMC_LAUNCHES):
+        d = sets[i % n_sets]
+        dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, max_len, k_scale=d.k_scale,
+                             scores=scores)
+    torch.cuda.synchronize()
+    log(f"bench: pmc pass done ({PMC_LAUNCHES} indexer launches, 3 passes over {COPY_BYTES >> 20} MiB)")
+
+
+def ingest_pmc(workload: str, fetch_csv: str, write_csv: str):
+    """Turn the two counter CSVs of pmc_pass into profiles/index_scores_<workload>_traffic.json:
+    per-launch HBM bytes of the indexer, each counter scaled by bytes/counter of the copy."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            key = (row["Kernel_Name"], row["Dispatch_Id"])
+            vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+        idx = [v for (k, _), v in vals.items() if "index_scores" in k]
+        cpy = [v for (k, _), v in vals.items() if "neg_kernel" in k]
+        return idx, cpy
+
+    fi, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    wi, wc = per_kernel(write_csv, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024.0
+    f_fetch = kib / statistics.median(fc)
+    f_write = kib / statistics.median(wc)
+    from sparse_attention_05_amd import inputs
+    p = inputs.workload(workload, seed=0)
+    rec = {
+        "workload": workload,
+        "kernel_sha256": hashlib.sha256(open(os.path.join(ROOT, "sparse_attention_05_amd", "csrc",
+                                                          "index_scores.hip"), "rb").read()).hexdigest(),
+        "fetch_kib_per_launch": statistics.median(fi), "write_kib_per_launch": statistics.median(wi),
+        "copy_fetch_kib": statistics.median(fc), "copy_write_kib": statistics.median(wc),
+        "fetch_scale": f_fetch, "write_scale": f_write,
+        "bytes_per_launch": 1024.0 * (statistics.median(fi) * f_fetch + statistics.median(wi) * f_write),
+        "algorithmic_bytes_per_launch": indexer_bytes(p),
+        "launches": len(fi),
+    }
+    out = os.path.join(ROOT, "profiles", f"index_scores_{workload}_traffic.json")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(p, budget_s: float):
     from oracle import dsa_oracle as O
     try:
@@ -105,13 +175,22 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input copies cycled through (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true", help="run the counter workload (under rocprofv3 --pmc)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the indexer traffic record from two counter runs")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.workload, *args.ingest_pmc)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
               "supported. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.pmc_pass:
+        pmc_pass(args.workload)
+        return
     import numpy as np
     import torch
     from sparse_attention_05_amd import dsa, inputs
