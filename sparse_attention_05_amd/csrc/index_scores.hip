@@ -348,6 +348,8 @@ hipError_t launch_t(const IndexArgs& a, hipStream_t stream) {
   const int64_t total = int64_t(a.R) * a.max_n;
   const int64_t waves = int64_t(device_cu_count()) * kWaves;
   int64_t kpw = (total + waves - 1) / waves;
+  const int64_t quarter = (int64_t(a.max_n) + kWaves - 1) / kWaves;  // keep all 4 waves of a row busy
+  if (kpw > quarter) kpw = quarter;
   kpw = ((kpw + 63) / 64) * 64;
   if (kpw < 64) kpw = 64;
   if (kpw > (int64_t(1) << 20)) kpw = int64_t(1) << 20;

@@ -19,6 +19,7 @@ reproducible on its own and on any machine.
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Optional, Sequence
 
@@ -103,9 +104,15 @@ class DSAProblem:
 # --------------------------------------------------------------------------
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (nearest, ties to even); return the bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    """Round finite float32 values to bfloat16 (nearest, ties to even); return
+    the bits. In 32-bit arithmetic: a finite value's bits plus 0x8000 stay
+    below 2**32."""
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    u += r
+    u >>= 16
     return u.astype(np.uint16)
 
 
@@ -132,16 +139,38 @@ def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
 
 
 def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0,
-                 chunk: int = 1 << 24) -> np.ndarray:
-    """N(0, std^2) samples stored as bf16 bits, generated in bounded chunks."""
+                 chunk: int = 1 << 22) -> np.ndarray:
+    """N(0, std^2) samples stored as bf16 bits (nearest, ties to even).
+
+    Chunk i of ``chunk`` values is drawn from the stream's bit generator
+    jumped i times, so the chunks are independent and can be generated on
+    several threads with a result that does not depend on the thread count.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
     total = int(np.prod(shape))
     out = np.empty(total, dtype=np.uint16)
-    for lo in range(0, total, chunk):
-        hi = min(total, lo + chunk)
-        v = rng.standard_normal(hi - lo, dtype=np.float32)
+    base = rng.bit_generator
+
+    def fill(i):
+        lo, hi = i * chunk, min(total, (i + 1) * chunk)
+        v = np.random.Generator(base.jumped(i + 1)).standard_normal(hi - lo, dtype=np.float32)
         if std != 1.0:
             v *= np.float32(std)
-        out[lo:hi] = f32_to_bf16_bits(v)
+        u = v.view(np.uint32)
+        r = u >> 16
+        r &= 1
+        r += 0x7FFF
+        u += r                                   # finite values: no 32-bit overflow
+        out[lo:hi] = u.view(np.uint16)[1::2]     # high halves (little-endian)
+
+    n_chunks = (total + chunk - 1) // chunk
+    if n_chunks <= 1:
+        for i in range(n_chunks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(n_chunks)))
     return out.reshape(shape)
 
 
