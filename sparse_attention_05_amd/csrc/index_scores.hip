@@ -64,6 +64,11 @@ __device__ __forceinline__ void load_q(typename Frag<QK>::type& f, const void* b
   }
 }
 
+// max(x, 0) in one instruction (v_med3_f32 clamps to [0, +inf]).
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_amdgcn_fmed3f(x, 0.f, __builtin_inff());
+}
+
 // OCP e4m3 -> bf16 is exact (3 mantissa bits fit in 7, every e4m3 exponent
 // fits bf16's range); v_cvt_scalef32_pk_bf16_fp8 converts two codes per call.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 c) {
@@ -75,15 +80,18 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 c) {
 }
 
 // Keys of a group sit in LDS as rows of DI elements, the 16-byte chunks of
-// row k permuted (XOR) by k mod 8 (k mod 4 for 4-chunk rows): the B-operand
-// reads of 8 (16) consecutive keys at one chunk offset then fall on distinct
-// banks.
-template <int QK, int DI>
+// row k permuted (XOR) by k mod 8 or k mod 16 (by k mod CPR for shorter
+// rows): the B-operand reads of 8 (16) consecutive keys at one chunk offset
+// then fall on distinct banks.
+template <int QK, int DI, bool WIDE = false>
 struct KeyCfg {
   static constexpr int ESZ = QK == 0 ? 4 : (QK == 1 ? 2 : 1);  // bytes per key element
   static constexpr int ROW = DI * ESZ;                        // bytes per key row
   static constexpr int CPR = ROW / 16;                        // 16-byte chunks per row
-  static constexpr int SWZ = CPR < 8 ? CPR - 1 : 7;
+  // WIDE: 4-bit permutation (conflict-free 16-lane reads; the prefill kernel,
+  // bound by LDS); otherwise 3 bits, which keeps each 8-lane part of a direct
+  // load inside one 128-byte line (the decode kernel, bound by HBM).
+  static constexpr int SWZ = WIDE ? (CPR < 16 ? CPR - 1 : 15) : (CPR < 8 ? CPR - 1 : 7);
   static constexpr int GK = 64;                               // keys per group
   static constexpr int GBYTES = GK * ROW;
   static constexpr int LOADS = GBYTES / 1024;                 // 1 KiB direct loads per group
@@ -163,9 +171,9 @@ __device__ __forceinline__ void wait_groups(int ahead) {
 }
 
 // B operand of K-step ks for key row `row` of a stage: dims 32*ks + 8*grp .. +8.
-template <int QK, int DI>
+template <int QK, int DI, bool WIDE = false>
 __device__ __forceinline__ typename Frag<QK>::type key_frag(const char* stage, int row, int grp, int ks) {
-  using C = KeyCfg<QK, DI>;
+  using C = KeyCfg<QK, DI, WIDE>;
   const char* rp = stage + row * C::ROW;
   const int sw = row & C::SWZ;
   typename Frag<QK>::type f;
@@ -341,6 +349,204 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
   }
 }
 
+// ---- prefill: many queries of one sequence ----------------------------------------
+// A workgroup of kPfWaves waves owns kPfWaves x kPfQpw consecutive query
+// rows of a single sequence; every wave keeps its kPfQpw queries in
+// registers (one wave per SIMD, so each has the whole register file) and all
+// waves share one ring of kPfStages key groups in LDS. A key row read from L2
+// feeds 8 queries x H_I heads of MFMA work (the decode kernel feeds one), and
+// each key fragment read from LDS feeds kPfQpw x MT MFMAs. The keys of a
+// group are loaded by all waves together (direct loads); groups go in pairs
+// per barrier, and the second group's fragments are read while the first
+// group's epilogue runs. Workgroups run from the last rows (longest key ranges) to the
+// first, so the short ones fill the tail. bf16 query and keys.
+constexpr int kPfWaves = 8;
+constexpr int kPfQpw = 1;
+constexpr int kPfRows = kPfWaves * kPfQpw;
+constexpr int kPfStages = 8;  // even: groups go in pairs
+
+template <int MT, int DI>
+__global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(IndexArgs a) {
+  using C = KeyCfg<1, DI, true>;
+  constexpr int NKS = DI / 32;
+  constexpr int LPW = C::LOADS / kPfWaves;  // direct loads per wave per group
+  static_assert(C::LOADS % kPfWaves == 0, "group loads split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char ring[kPfStages][C::GBYTES];
+
+  const int blk = int(gridDim.x) - 1 - int(blockIdx.x);
+  const int r0 = blk * kPfRows;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+
+  const int64_t base = a.row_off[0];
+  const bool base_ok = base >= 0 && base < a.cache_rows;
+  auto row_n = [&](int rr) -> int64_t {
+    int64_t n = int64_t(a.q_pos[rr]) + 1;
+    if (n > a.max_n) n = a.max_n;
+    if (n > a.cache_rows - base) n = a.cache_rows - base;
+    return base_ok && n > 0 ? n : 0;
+  };
+  int64_t n_q[kPfQpw];
+#pragma unroll
+  for (int q = 0; q < kPfQpw; ++q) {
+    const int rr = r0 + wave * kPfQpw + q;
+    n_q[q] = rr < a.R ? row_n(rr) : 0;
+  }
+  int64_t n_wg = 0;
+  for (int i = 0; i < kPfRows && r0 + i < a.R; ++i) {
+    const int64_t ni = row_n(r0 + i);
+    n_wg = ni > n_wg ? ni : n_wg;
+  }
+  const int groups = int((n_wg + 63) / 64);
+
+  // query fragments and weights of this wave's rows (zero for padded heads or
+  // missing rows), waited for here and re-defined through an empty asm, so
+  // that no later use waits on them behind the key loads
+  bf16x8 qa[kPfQpw][MT][NKS];
+  float wr[kPfQpw][MT][4];
+#pragma unroll
+  for (int q = 0; q < kPfQpw; ++q) {
+    const int rr = r0 + wave * kPfQpw + q;
+    const bool rv = rr < a.R;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = 16 * mt + col;
+      const bool hv = rv && h < a.H_I;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int64_t off = (int64_t(hv ? rr : 0) * a.H_I + (hv ? h : 0)) * DI + 32 * ks + 8 * grp;
+        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+        qa[q][mt][ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hw = 16 * mt + 4 * grp + i;
+        const bool wv = rv && hw < a.H_I;
+        const float x = a.w[int64_t(wv ? rr : 0) * a.H_I + (wv ? hw : 0)];
+        wr[q][mt][i] = wv ? x : 0.f;
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int q = 0; q < kPfQpw; ++q)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint4 u = __builtin_bit_cast(uint4, qa[q][mt][ks]);
+        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+        qa[q][mt][ks] = __builtin_bit_cast(bf16x8, u);
+      }
+      asm volatile("" : "+v"(wr[q][mt][0]), "+v"(wr[q][mt][1]), "+v"(wr[q][mt][2]), "+v"(wr[q][mt][3]));
+    }
+
+  const char* keys = static_cast<const char*>(a.keys);
+  auto issue = [&](int g) {
+    const uint32_t to = lds_addr(ring[g % kPfStages]);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int m = wave * LPW + j;
+      const int pch = 64 * m + lane;
+      const int row = pch / C::CPR;
+      const int lc = (pch % C::CPR) ^ (row & C::SWZ);
+      const int64_t s = int64_t(g) * 64 + row;
+      const int64_t key = base + (s < n_wg ? s : 0);  // rows past the range re-read row 0
+      dma16(keys + key * C::ROW + 16 * lc, to + 1024 * m);
+    }
+  };
+  int issued = 0;
+  for (; issued < kPfStages - 2 && issued < groups; ++issued) issue(issued);
+
+  auto load_frags = [&](int g, bf16x8 (&kb)[4][NKS]) {
+    const char* stage = ring[g % kPfStages];
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) kb[b4][ks] = key_frag<1, DI, true>(stage, 16 * b4 + col, grp, ks);
+  };
+  // scores of group g for this wave's queries from fragments kb; the
+  // fragments of group `next` (if >= 0) are read into kb once the MFMAs have
+  // consumed it, so their LDS latency overlaps this group's epilogue
+  auto finish = [&](int g, bf16x8 (&kb)[4][NKS], int next) {
+    const int64_t s0 = int64_t(g) * 64;
+    f32x4 acc[kPfQpw][4][MT];
+#pragma unroll
+    for (int q = 0; q < kPfQpw; ++q)
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[q][b4][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one round per K-step of independent MFMAs; the scheduling fences keep
+    // the compiler from regrouping them into dependent chains
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < kPfQpw; ++q)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[q][b4][mt] = mfma_k32(qa[q][mt][ks], kb[b4][ks], acc[q][b4][mt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (next >= 0) load_frags(next, kb);
+#pragma unroll
+    for (int q = 0; q < kPfQpw; ++q) {
+      float part[4];
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        float pm[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          pm[mt] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pm[mt] += wr[q][mt][i] * relu(acc[q][b4][mt][i]);
+        }
+        float pp = pm[0];
+#pragma unroll
+        for (int mt = 1; mt < MT; ++mt) pp += pm[mt];
+        part[b4] = pp;
+      }
+      const bool hi5 = lane & 32, hi4 = lane & 16;
+      const float x0 = wave_shfl_xor(hi5 ? part[0] : part[2], 32);
+      const float x1 = wave_shfl_xor(hi5 ? part[1] : part[3], 32);
+      const float k0 = (hi5 ? part[2] : part[0]) + x0;
+      const float k1 = (hi5 ? part[3] : part[1]) + x1;
+      const float rv = wave_shfl_xor(hi4 ? k0 : k1, 16);
+      const float v = (hi4 ? k1 : k0) + rv;
+      const int rr = r0 + wave * kPfQpw + q;
+      const int64_t s = s0 + lane;
+      if (s < n_q[q]) a.scores[int64_t(rr) * a.ld + s] = v;
+    }
+  };
+  const int64_t n_max_w = n_q[0] > n_q[kPfQpw - 1] ? n_q[0] : n_q[kPfQpw - 1];
+  for (int g = 0; g < groups; g += 2) {
+    // this wave's parts of groups g and g + 1 have landed
+    wait_groups<LPW>(issued - (g + 2 < groups ? g + 2 : groups));
+    __syncthreads();  // every part has; every wave is done with groups g - 2 and g - 1
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int j = 0; j < 2 && issued < groups; ++j, ++issued) issue(issued);  // refill their stages
+    const bool two = g + 1 < groups && int64_t(g + 1) * 64 < n_max_w;
+    if (int64_t(g) * 64 >= n_max_w) continue;  // nothing of this wave's rows here
+    bf16x8 kb[4][NKS];
+    load_frags(g, kb);
+    finish(g, kb, -1);
+    if (two) {
+      load_frags(g + 1, kb);
+      finish(g + 1, kb, -1);
+    }
+  }
+}
+
+template <int MT, int DI>
+hipError_t launch_prefill(const IndexArgs& a, hipStream_t stream) {
+  const unsigned blocks = unsigned((a.R + kPfRows - 1) / kPfRows);
+  index_scores_prefill_kernel<MT, DI><<<dim3(blocks), kPfWaves * 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 template <int QK, int MT, int DI>
 hipError_t launch_t(const IndexArgs& a, hipStream_t stream) {
   // One 4-wave workgroup per CU (the stage buffers take most of the LDS);
@@ -377,6 +583,12 @@ hipError_t launch_m(const IndexArgs& a, hipStream_t stream) {
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
   const int mode = a.q_dtype == kF32 ? 0 : (a.k_dtype == kFP8 ? 2 : 1);
+  // many bf16 queries of one sequence (causal prefill form): key tiles shared by 8 queries
+  if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && !a.sample && !a.topk_state) {
+    if (a.H_I <= 16) return a.D_I == 64 ? launch_prefill<1, 64>(a, stream) : launch_prefill<1, 128>(a, stream);
+    if (a.H_I <= 32) return a.D_I == 64 ? launch_prefill<2, 64>(a, stream) : launch_prefill<2, 128>(a, stream);
+    return a.D_I == 64 ? launch_prefill<4, 64>(a, stream) : launch_prefill<4, 128>(a, stream);
+  }
   if (mode == 0) return launch_m<0>(a, stream);
   if (mode == 1) return launch_m<1>(a, stream);
   return launch_m<2>(a, stream);

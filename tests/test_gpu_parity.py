@@ -331,3 +331,31 @@ def test_fused_decode_repeatable_and_replayable(dsa):
     rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale)
     assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
     C.assert_attn_close(out, ref_o, lse, ref_l)
+
+
+# ------------------------------------------------------------------------------
+# causal prefill form (one sequence, a query per position)
+# ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H_I,D_I", [(777, 64, 128), (300, 32, 64), (100, 16, 128), (40, 64, 64)])
+def test_prefill_form_scores_topk_attention(dsa, T, H_I, D_I):
+    """Every row's scores within the bound of the oracle (this form runs the
+    multi-query indexer: 8 rows per workgroup sharing the key tiles), top-k
+    equal to the stable order of those scores, attention on a few rows."""
+    import torch
+    p = inputs.prefill_config(T, seed=3, H_I=H_I, D_I=D_I, k=64)
+    d = inputs.to_torch(p)
+    s_d = dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, T, q_seq=d.q_seq)
+    idx_d = dsa.dsa_topk(s_d, d.q_pos, T, p.k)
+    scores, idx = s_d.cpu().numpy(), idx_d.cpu().numpy()
+    ref_rows = O.index_scores(p)
+    for r in range(p.R):
+        n = r + 1
+        ref = ref_rows[r].astype(np.float64)
+        bound = C.score_bound(p, r, np.arange(n), ref)
+        assert not (np.abs(scores[r, :n] - ref) > bound).any(), f"row {r}"
+        assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k)), f"row {r}"
+    rows = [0, 1, T // 2, T - 1]
+    out, lse = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx_d, p.scale, q_seq=d.q_seq)
+    ref_o, ref_l = O.sparse_mla(p, idx[rows], rows=rows)
+    C.assert_attn_close(out.cpu().numpy()[rows], ref_o, lse.cpu().numpy()[rows], ref_l)
