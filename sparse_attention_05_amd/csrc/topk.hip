@@ -82,6 +82,12 @@ __device__ __forceinline__ void unroll(F&& f) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// Barrier that orders LDS accesses only (no wait for outstanding global
+// stores, unlike __syncthreads, whose workgroup release waits for them).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---- block primitives (uniform control flow; each ends with a barrier) -----------
 
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32_t& total) {
@@ -451,8 +457,12 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
     start[j] = sh.bins[bk[j]];
     cb[j] = sh.cnt[bk[j]];
   }
+  // Slots past m count on a spare word of their own (the bitonic scratch,
+  // unused here), so every slot's atomic and load below is unconditional:
+  // the LDS round trips of all slots of a thread are in flight together.
+  uint32_t* spare = reinterpret_cast<uint32_t*>(sh.v.net) + t;
 #pragma unroll
-  for (int j = 0; j < J; ++j) slot[j] = t + j * kThreads < m ? atomicAdd(&sh.fill[bk[j]], 1u) : 0u;
+  for (int j = 0; j < J; ++j) slot[j] = atomicAdd(t + j * kThreads < m ? &sh.fill[bk[j]] : spare, 1u);
 #pragma unroll
   for (int j = 0; j < J; ++j)
     if (t + j * kThreads < m) dst[off + start[j] + slot[j]] = w[j];
@@ -463,18 +473,21 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
   for (int j = 0; j < J; ++j) {
     const bool live = t + j * kThreads < m && cb[j] <= kSmall && off + int(start[j]) < limit;
     cb[j] = live ? cb[j] : 0u;
+    start[j] = live ? start[j] : 0u;
     rank[j] = 0u;
     most = max(most, cb[j]);
   }
   for (uint32_t q = 0; q < most; ++q) {
+    unsigned long long x[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j)
-      if (q < cb[j]) rank[j] += dst[off + start[j] + q] > w[j];
+    for (int j = 0; j < J; ++j) x[j] = dst[off + start[j] + (q < cb[j] ? q : 0u)];
+#pragma unroll
+    for (int j = 0; j < J; ++j) rank[j] += (q < cb[j]) & (x[j] > w[j]);
   }
 #pragma unroll
   for (int j = 0; j < J; ++j)
     if (cb[j] && off + int(start[j] + rank[j]) < limit) out[off + start[j] + rank[j]] = word_idx(w[j]);
-  __syncthreads();
+  lds_barrier();  // orders the LDS use only; the index stores need not complete here
 }
 
 // Bitonic network (descending) on src[off .. off+m), m <= kCap; writes the
@@ -695,6 +708,10 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a, int sl
   uint32_t* st = a.state + 4 * r;  // count, arrivals, max candidate key, ~min candidate key
   unsigned long long* cand = a.cand + int64_t(r) * kCap;
 
+  // this slice's scores, loaded first so the load overlaps the pivot
+  const int i0 = g * kTile + 4 * t;
+  const float4 sv = i0 < n ? *reinterpret_cast<const float4*>(row + i0) : float4{0.f, 0.f, 0.f, 0.f};
+
   // ---- pivot (identical in every slice of the row; 0 when every key wins) ----------------
   uint32_t pivot = 0u;
   if (n > k) {
@@ -714,15 +731,11 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a, int sl
   }
 
   // ---- this slice's candidates -----------------------------------------------------------
-  const int i0 = g * kTile + 4 * t;
   uint32_t key[4];
-  {
-    const float4 v = i0 < n ? *reinterpret_cast<const float4*>(row + i0) : float4{0.f, 0.f, 0.f, 0.f};
-    key[0] = order_key(v.x);
-    key[1] = order_key(v.y);
-    key[2] = order_key(v.z);
-    key[3] = order_key(v.w);
-  }
+  key[0] = order_key(sv.x);
+  key[1] = order_key(sv.y);
+  key[2] = order_key(sv.z);
+  key[3] = order_key(sv.w);
   uint32_t c = 0, kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
