@@ -350,20 +350,65 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
 }
 
 // ---- prefill: many queries of one sequence ----------------------------------------
-// A workgroup of kPfWaves waves owns kPfWaves x kPfQpw consecutive query
-// rows of a single sequence; every wave keeps its kPfQpw queries in
-// registers (one wave per SIMD, so each has the whole register file) and all
-// waves share one ring of kPfStages key groups in LDS. A key row read from L2
-// feeds 8 queries x H_I heads of MFMA work (the decode kernel feeds one), and
-// each key fragment read from LDS feeds kPfQpw x MT MFMAs. The keys of a
-// group are loaded by all waves together (direct loads); groups go in pairs
-// per barrier, and the second group's fragments are read while the first
-// group's epilogue runs. Workgroups run from the last rows (longest key ranges) to the
-// first, so the short ones fill the tail. bf16 query and keys.
+// A workgroup of kPfWaves waves (two per SIMD) takes kPfWaves consecutive
+// query rows of one sequence, one row per wave; the waves share a ring of
+// kPfStages key groups in LDS, which they fill together with direct loads,
+// one group per barrier. A key row read from L2 feeds kPfWaves queries x H_I
+// heads of MFMA work (the decode kernel feeds one). Within a group each wave
+// works tile by tile (16 keys): while the matrix core multiplies tile b, the
+// wave runs tile b-1's epilogue (ReLU, head weights, head sum) on the VALU
+// and then refills tile b-1's fragment registers with the next group's keys,
+// so neither the epilogue nor the LDS reads leave the matrix core idle; the
+// scheduler is told to interleave the streams. Workgroups run from the last
+// rows (longest key ranges) to the first, so the short ones fill the tail.
+// bf16 query and keys.
 constexpr int kPfWaves = 8;
-constexpr int kPfQpw = 1;
-constexpr int kPfRows = kPfWaves * kPfQpw;
-constexpr int kPfStages = 8;  // even: groups go in pairs
+constexpr int kPfRows = kPfWaves;
+constexpr int kPfStages = 8;
+
+// ReLU on the bit pattern: a float with the sign bit set is a negative int32,
+// so an integer max with 0 sends it to +0.0 (one VALU op; the float min/max
+// forms cost a NaN-quieting op on top).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// s_waitcnt vmcnt(A * LPW) for the largest A <= ahead (A <= 8).
+template <int LPW, int A = 8>
+__device__ __forceinline__ void wait_ahead(int ahead) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= A) wait_vmcnt<A * LPW>();
+    else wait_ahead<LPW, A - 1>(ahead);
+  }
+}
+
+// Lane 16*r + n holds p[t] = the part of 16-lane row r for key 16*t + n;
+// returns, in lane 16*t + n, the sum over the 4 rows of p[t]. The 32-lane
+// swap leaves rows {0+2, 1+3} sums of p[0], p[2] (and of p[1], p[3]) side by
+// side; the 16-lane swap pairs those up. Three lane swaps on the VALU, no
+// LDS round trip; the sum order is (r0 + r2) + (r1 + r3).
+__device__ __forceinline__ float rows_transpose_sum(const float (&p)[4]) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+  const float x = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // rows: p0 r0+r2, p0 r1+r3, p2 .., p2 ..
+  const float y = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // rows: p1 r0+r2, p1 r1+r3, p3 .., p3 ..
+  const auto sxy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(sxy[0]) + __uint_as_float(sxy[1]);
+}
+
+// s_waitcnt vmcnt(min(n, A)): at most n vector memory operations of this
+// wave still outstanding (they complete in issue order).
+template <int A>
+__device__ __forceinline__ void wait_ops(int n) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= A) wait_vmcnt<A>();
+    else wait_ops<A - 1>(n);
+  }
+}
 
 template <int MT, int DI>
 __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(IndexArgs a) {
@@ -371,6 +416,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   constexpr int NKS = DI / 32;
   constexpr int LPW = C::LOADS / kPfWaves;  // direct loads per wave per group
   static_assert(C::LOADS % kPfWaves == 0, "group loads split evenly over the waves");
+  static_assert(kPfStages >= 2 && kPfStages <= 9, "wait_ahead covers up to 8 groups in flight");
   __shared__ __attribute__((aligned(1024))) char ring[kPfStages][C::GBYTES];
 
   const int blk = int(gridDim.x) - 1 - int(blockIdx.x);
@@ -387,60 +433,16 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     if (n > a.cache_rows - base) n = a.cache_rows - base;
     return base_ok && n > 0 ? n : 0;
   };
-  int64_t n_q[kPfQpw];
-#pragma unroll
-  for (int q = 0; q < kPfQpw; ++q) {
-    const int rr = r0 + wave * kPfQpw + q;
-    n_q[q] = rr < a.R ? row_n(rr) : 0;
-  }
+  const int rr = r0 + wave;
+  const bool rv = rr < a.R;
+  const int64_t n_w = rv ? row_n(rr) : 0;
   int64_t n_wg = 0;
   for (int i = 0; i < kPfRows && r0 + i < a.R; ++i) {
     const int64_t ni = row_n(r0 + i);
     n_wg = ni > n_wg ? ni : n_wg;
   }
   const int groups = int((n_wg + 63) / 64);
-
-  // query fragments and weights of this wave's rows (zero for padded heads or
-  // missing rows), waited for here and re-defined through an empty asm, so
-  // that no later use waits on them behind the key loads
-  bf16x8 qa[kPfQpw][MT][NKS];
-  float wr[kPfQpw][MT][4];
-#pragma unroll
-  for (int q = 0; q < kPfQpw; ++q) {
-    const int rr = r0 + wave * kPfQpw + q;
-    const bool rv = rr < a.R;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int h = 16 * mt + col;
-      const bool hv = rv && h < a.H_I;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int64_t off = (int64_t(hv ? rr : 0) * a.H_I + (hv ? h : 0)) * DI + 32 * ks + 8 * grp;
-        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
-        qa[q][mt][ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hw = 16 * mt + 4 * grp + i;
-        const bool wv = rv && hw < a.H_I;
-        const float x = a.w[int64_t(wv ? rr : 0) * a.H_I + (wv ? hw : 0)];
-        wr[q][mt][i] = wv ? x : 0.f;
-      }
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int q = 0; q < kPfQpw; ++q)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        uint4 u = __builtin_bit_cast(uint4, qa[q][mt][ks]);
-        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-        qa[q][mt][ks] = __builtin_bit_cast(bf16x8, u);
-      }
-      asm volatile("" : "+v"(wr[q][mt][0]), "+v"(wr[q][mt][1]), "+v"(wr[q][mt][2]), "+v"(wr[q][mt][3]));
-    }
+  if (groups == 0) return;  // the same for every wave of the workgroup
 
   const char* keys = static_cast<const char*>(a.keys);
   auto issue = [&](int g) {
@@ -457,86 +459,118 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     }
   };
   int issued = 0;
-  for (; issued < kPfStages - 2 && issued < groups; ++issued) issue(issued);
+  for (; issued < kPfStages && issued < groups; ++issued) issue(issued);
 
-  auto load_frags = [&](int g, bf16x8 (&kb)[4][NKS]) {
-    const char* stage = ring[g % kPfStages];
+  // query fragments and weights of this wave's row (zero for padded heads or
+  // a missing row), loaded behind the first key groups and waited for with
+  // them, then re-defined through an empty asm, so that no later use waits
+  // on them behind the key loads
+  bf16x8 qa[MT][NKS];
+  float wr[MT][4];
 #pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kb[b4][ks] = key_frag<1, DI, true>(stage, 16 * b4 + col, grp, ks);
-  };
-  // scores of group g for this wave's queries from fragments kb; the
-  // fragments of group `next` (if >= 0) are read into kb once the MFMAs have
-  // consumed it, so their LDS latency overlaps this group's epilogue
-  auto finish = [&](int g, bf16x8 (&kb)[4][NKS], int next) {
-    const int64_t s0 = int64_t(g) * 64;
-    f32x4 acc[kPfQpw][4][MT];
-#pragma unroll
-    for (int q = 0; q < kPfQpw; ++q)
-#pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[q][b4][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // one round per K-step of independent MFMAs; the scheduling fences keep
-    // the compiler from regrouping them into dependent chains
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = 16 * mt + col;
+    const bool hv = rv && h < a.H_I;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
+      const int64_t off = (int64_t(hv ? rr : 0) * a.H_I + (hv ? h : 0)) * DI + 32 * ks + 8 * grp;
+      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+      qa[mt][ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hw = 16 * mt + 4 * grp + i;
+      const bool wv = rv && hw < a.H_I;
+      const float x = a.w[int64_t(wv ? rr : 0) * a.H_I + (wv ? hw : 0)];
+      wr[mt][i] = wv ? x : 0.f;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 u = __builtin_bit_cast(uint4, qa[mt][ks]);
+      asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+      qa[mt][ks] = __builtin_bit_cast(bf16x8, u);
+    }
+    asm volatile("" : "+v"(wr[mt][0]), "+v"(wr[mt][1]), "+v"(wr[mt][2]), "+v"(wr[mt][3]));
+  }
+
+
+  // fragments of tile b4 (keys 16*b4 .. +16) of group g (a stage past the
+  // last group holds stale keys: reading it is harmless, its products are
+  // never stored)
+  auto tile_frags = [&](int g, int b4, bf16x8 (&kt)[NKS]) {
+    const char* stage = ring[g % kPfStages];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kt[ks] = key_frag<1, DI, true>(stage, 16 * b4 + col, grp, ks);
+  };
+  // ReLU, head weight and the sum over the lane's 4 heads of each of the MT
+  // head tiles: this lane's part of the score of key 16*b4 + n
+  auto tile_epi = [&](const f32x4 (&c)[MT]) -> float {
+    float pm[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      pm[mt] = wr[mt][0] * relu_bits(c[mt][0]);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) pm[mt] += wr[mt][i] * relu_bits(c[mt][i]);
+    }
+    float pp = pm[0];
+#pragma unroll
+    for (int mt = 1; mt < MT; ++mt) pp += pm[mt];
+    return pp;
+  };
+
+  // this wave's score row as a buffer of n_w floats: stores past it are dropped
+  const __amdgpu_buffer_rsrc_t srow =
+      __builtin_amdgcn_make_buffer_rsrc(a.scores + int64_t(rv ? rr : 0) * a.ld, 0, int(n_w * 4), 0x00020000);
+
+  bf16x8 kb[4][NKS];
+  f32x4 acc[4][MT];
+  // the prologue waited for every load: group 0 has landed for every wave
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int b4 = 0; b4 < 4; ++b4) tile_frags(0, b4, kb[b4]);
+
+  for (int g = 0; g < groups; ++g) {
+    // own parts of group g+1 landed: behind them are the direct loads of
+    // the later groups and one score store per group since (every group's
+    // store is issued, its out-of-range lanes dropped by the buffer bounds)
+    if (g + 1 < groups) wait_ops<LPW * (kPfStages - 2) + kPfStages - 1>(
+        LPW * (issued - (g + 2)) + (g < kPfStages - 1 ? g : kPfStages - 1));
+    // every part of g+1 has landed; every wave's reads of group g are done,
+    // so its stage takes group g + kPfStages
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (issued < groups) {
+      issue(issued);
+      ++issued;
+    }
+    float part[4];
+#pragma unroll
+    for (int b4 = 0; b4 < 4; ++b4) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < kPfQpw; ++q)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4)
+        for (int mt = 0; mt < MT; ++mt)
+          acc[b4][mt] = mfma_k32(qa[mt][ks], kb[b4][ks], ks ? acc[b4][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
+      if (b4 > 0) part[b4 - 1] = tile_epi(acc[b4 - 1]);
+      tile_frags(g + 1, b4, kb[b4]);
+      // each MFMA followed by two VALU ops of the previous tile's epilogue;
+      // the next group's fragment reads after the tile's last MFMA
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[q][b4][mt] = mfma_k32(qa[q][mt][ks], kb[b4][ks], acc[q][b4][mt]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (next >= 0) load_frags(next, kb);
-#pragma unroll
-    for (int q = 0; q < kPfQpw; ++q) {
-      float part[4];
-#pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        float pm[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          pm[mt] = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pm[mt] += wr[q][mt][i] * relu(acc[q][b4][mt][i]);
-        }
-        float pp = pm[0];
-#pragma unroll
-        for (int mt = 1; mt < MT; ++mt) pp += pm[mt];
-        part[b4] = pp;
+      for (int i = 0; i < MT * NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       }
-      const bool hi5 = lane & 32, hi4 = lane & 16;
-      const float x0 = wave_shfl_xor(hi5 ? part[0] : part[2], 32);
-      const float x1 = wave_shfl_xor(hi5 ? part[1] : part[3], 32);
-      const float k0 = (hi5 ? part[2] : part[0]) + x0;
-      const float k1 = (hi5 ? part[3] : part[1]) + x1;
-      const float rv = wave_shfl_xor(hi4 ? k0 : k1, 16);
-      const float v = (hi4 ? k1 : k0) + rv;
-      const int rr = r0 + wave * kPfQpw + q;
-      const int64_t s = s0 + lane;
-      if (s < n_q[q]) a.scores[int64_t(rr) * a.ld + s] = v;
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  const int64_t n_max_w = n_q[0] > n_q[kPfQpw - 1] ? n_q[0] : n_q[kPfQpw - 1];
-  for (int g = 0; g < groups; g += 2) {
-    // this wave's parts of groups g and g + 1 have landed
-    wait_groups<LPW>(issued - (g + 2 < groups ? g + 2 : groups));
-    __syncthreads();  // every part has; every wave is done with groups g - 2 and g - 1
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    for (int j = 0; j < 2 && issued < groups; ++j, ++issued) issue(issued);  // refill their stages
-    const bool two = g + 1 < groups && int64_t(g + 1) * 64 < n_max_w;
-    if (int64_t(g) * 64 >= n_max_w) continue;  // nothing of this wave's rows here
-    bf16x8 kb[4][NKS];
-    load_frags(g, kb);
-    finish(g, kb, -1);
-    if (two) {
-      load_frags(g + 1, kb);
-      finish(g + 1, kb, -1);
-    }
+    part[3] = tile_epi(acc[3]);
+    const float v = rows_transpose_sum(part);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, (g * 64 + lane) * 4, 0, 0);
   }
 }
 
@@ -584,7 +618,9 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
   const int mode = a.q_dtype == kF32 ? 0 : (a.k_dtype == kFP8 ? 2 : 1);
   // many bf16 queries of one sequence (causal prefill form): key tiles shared by 8 queries
-  if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && !a.sample && !a.topk_state) {
+  // (a score row is addressed with 32-bit byte offsets there)
+  if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 28) && !a.sample &&
+      !a.topk_state) {
     if (a.H_I <= 16) return a.D_I == 64 ? launch_prefill<1, 64>(a, stream) : launch_prefill<1, 128>(a, stream);
     if (a.H_I <= 32) return a.D_I == 64 ? launch_prefill<2, 64>(a, stream) : launch_prefill<2, 128>(a, stream);
     return a.D_I == 64 ? launch_prefill<4, 64>(a, stream) : launch_prefill<4, 128>(a, stream);
