@@ -128,6 +128,21 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
       : "memory");
 }
 
+// 16-byte direct-to-LDS load through a buffer resource: lane l reads the
+// 16 bytes at byte offset `off` of the buffer (zeros past its end) into LDS
+// byte address lds + 16*l.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(r), "s"(lds)
+      : "memory");
+}
+
 // s_waitcnt vmcnt(min(N, 63)): a smaller count only waits longer.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -364,7 +379,9 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
 // bf16 query and keys.
 constexpr int kPfWaves = 8;
 constexpr int kPfRows = kPfWaves;
-constexpr int kPfStages = 8;
+constexpr int kPfKeys = 128;  // keys per group (one barrier each)
+constexpr int kPfTiles = kPfKeys / 16;
+constexpr int kPfStages = 4;
 
 // ReLU on the bit pattern: a float with the sign bit set is a negative int32,
 // so an integer max with 0 sends it to +0.0 (one VALU op; the float min/max
@@ -414,10 +431,11 @@ template <int MT, int DI>
 __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(IndexArgs a) {
   using C = KeyCfg<1, DI, true>;
   constexpr int NKS = DI / 32;
-  constexpr int LPW = C::LOADS / kPfWaves;  // direct loads per wave per group
-  static_assert(C::LOADS % kPfWaves == 0, "group loads split evenly over the waves");
-  static_assert(kPfStages >= 2 && kPfStages <= 9, "wait_ahead covers up to 8 groups in flight");
-  __shared__ __attribute__((aligned(1024))) char ring[kPfStages][C::GBYTES];
+  constexpr int GB = kPfKeys * C::ROW;      // bytes per group
+  constexpr int LPW = GB / 1024 / kPfWaves;  // direct loads per wave per group
+  static_assert((GB / 1024) % kPfWaves == 0, "group loads split evenly over the waves");
+  static_assert(kPfStages >= 3, "a group lands while the one before it is multiplied");
+  __shared__ __attribute__((aligned(1024))) char ring[kPfStages][GB];
 
   const int blk = int(gridDim.x) - 1 - int(blockIdx.x);
   const int r0 = blk * kPfRows;
@@ -441,22 +459,29 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     const int64_t ni = row_n(r0 + i);
     n_wg = ni > n_wg ? ni : n_wg;
   }
-  const int groups = int((n_wg + 63) / 64);
+  const int groups = int((n_wg + kPfKeys - 1) / kPfKeys);
   if (groups == 0) return;  // the same for every wave of the workgroup
 
-  const char* keys = static_cast<const char*>(a.keys);
+  // Group g is the buffer of key rows 128*g .. n_wg-1 (rows past the range
+  // read as zeros); this lane's byte offset in it for each of the wave's
+  // loads is the same in every group.
+  const char* keys = static_cast<const char*>(a.keys) + base * C::ROW;
+  uint32_t src_off[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int m = wave * LPW + j;
+    const int pch = 64 * m + lane;
+    const int row = pch / C::CPR;
+    const int lc = (pch % C::CPR) ^ (row & C::SWZ);
+    src_off[j] = uint32_t(row * C::ROW + 16 * lc);
+  }
   auto issue = [&](int g) {
     const uint32_t to = lds_addr(ring[g % kPfStages]);
+    const int64_t s0 = int64_t(g) * kPfKeys;
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(keys + s0 * C::ROW), 0, int((n_wg - s0) * C::ROW), 0x00020000);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int m = wave * LPW + j;
-      const int pch = 64 * m + lane;
-      const int row = pch / C::CPR;
-      const int lc = (pch % C::CPR) ^ (row & C::SWZ);
-      const int64_t s = int64_t(g) * 64 + row;
-      const int64_t key = base + (s < n_wg ? s : 0);  // rows past the range re-read row 0
-      dma16(keys + key * C::ROW + 16 * lc, to + 1024 * m);
-    }
+    for (int j = 0; j < LPW; ++j) dma16_buf(src, src_off[j], to + 1024 * (wave * LPW + j));
   };
   int issued = 0;
   for (; issued < kPfStages && issued < groups; ++issued) issue(issued);
@@ -498,16 +523,16 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   }
 
 
-  // fragments of tile b4 (keys 16*b4 .. +16) of group g (a stage past the
-  // last group holds stale keys: reading it is harmless, its products are
-  // never stored)
-  auto tile_frags = [&](int g, int b4, bf16x8 (&kt)[NKS]) {
+  // fragments of tile t (keys 16*t .. +16) of group g (a stage past the last
+  // group holds stale keys: reading it is harmless, its products are never
+  // stored)
+  auto tile_frags = [&](int g, int t, bf16x8 (&kt)[NKS]) {
     const char* stage = ring[g % kPfStages];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kt[ks] = key_frag<1, DI, true>(stage, 16 * b4 + col, grp, ks);
+    for (int ks = 0; ks < NKS; ++ks) kt[ks] = key_frag<1, DI, true>(stage, 16 * t + col, grp, ks);
   };
   // ReLU, head weight and the sum over the lane's 4 heads of each of the MT
-  // head tiles: this lane's part of the score of key 16*b4 + n
+  // head tiles: this lane's part of the score of key 16*t + n
   auto tile_epi = [&](const f32x4 (&c)[MT]) -> float {
     float pm[MT];
 #pragma unroll
@@ -526,39 +551,43 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   const __amdgpu_buffer_rsrc_t srow =
       __builtin_amdgcn_make_buffer_rsrc(a.scores + int64_t(rv ? rr : 0) * a.ld, 0, int(n_w * 4), 0x00020000);
 
-  bf16x8 kb[4][NKS];
-  f32x4 acc[4][MT];
+  // two fragment tiles and two accumulator tiles: tile t is multiplied from
+  // kb[t&1] into acc[t&1] while tile t-1's epilogue runs from acc[(t-1)&1]
+  // and tile t+1's fragments are read into kb[(t+1)&1]
+  bf16x8 kb[2][NKS];
+  f32x4 acc[2][MT];
   // the prologue waited for every load: group 0 has landed for every wave
   asm volatile("s_barrier" ::: "memory");
-#pragma unroll
-  for (int b4 = 0; b4 < 4; ++b4) tile_frags(0, b4, kb[b4]);
+  tile_frags(0, 0, kb[0]);
 
   for (int g = 0; g < groups; ++g) {
-    // own parts of group g+1 landed: behind them are the direct loads of
-    // the later groups and one score store per group since (every group's
-    // store is issued, its out-of-range lanes dropped by the buffer bounds)
-    if (g + 1 < groups) wait_ops<LPW * (kPfStages - 2) + kPfStages - 1>(
-        LPW * (issued - (g + 2)) + (g < kPfStages - 1 ? g : kPfStages - 1));
-    // every part of g+1 has landed; every wave's reads of group g are done,
-    // so its stage takes group g + kPfStages
+    // own parts of group g+1 landed (its first tile is read during this
+    // group's last one): behind them are the direct loads of the later
+    // groups and two score stores per group since
+    if (g + 1 < groups) wait_ops<LPW * (kPfStages - 2) + 2 * (kPfStages - 1)>(
+        LPW * (issued - (g + 2)) + 2 * (g < kPfStages - 2 ? g : kPfStages - 2));
+    // every part of g+1 has landed; every wave is done with group g-1, so
+    // its stage takes group g-1 + kPfStages
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (issued < groups) {
+    if (g >= 1 && issued < groups) {
       issue(issued);
       ++issued;
     }
-    float part[4];
+    float part[kPfTiles];
 #pragma unroll
-    for (int b4 = 0; b4 < 4; ++b4) {
+    for (int t = 0; t < kPfTiles; ++t) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          acc[b4][mt] = mfma_k32(qa[mt][ks], kb[b4][ks], ks ? acc[b4][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
-      if (b4 > 0) part[b4 - 1] = tile_epi(acc[b4 - 1]);
-      tile_frags(g + 1, b4, kb[b4]);
-      // each MFMA followed by two VALU ops of the previous tile's epilogue;
-      // the next group's fragment reads after the tile's last MFMA
+          acc[t & 1][mt] =
+              mfma_k32(qa[mt][ks], kb[t & 1][ks], ks ? acc[t & 1][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
+      if (t > 0) part[t - 1] = tile_epi(acc[(t - 1) & 1]);
+      if (t + 1 < kPfTiles) tile_frags(g, t + 1, kb[(t + 1) & 1]);
+      else tile_frags(g + 1, 0, kb[(t + 1) & 1]);
+      // each MFMA followed by VALU work of the previous tile's epilogue;
+      // the fragment reads after the tile's MFMAs
 #pragma unroll
       for (int i = 0; i < MT * NKS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -568,9 +597,14 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
       __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    part[3] = tile_epi(acc[3]);
-    const float v = rows_transpose_sum(part);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, (g * 64 + lane) * 4, 0, 0);
+    part[kPfTiles - 1] = tile_epi(acc[(kPfTiles - 1) & 1]);
+#pragma unroll
+    for (int h = 0; h < kPfTiles / 4; ++h) {
+      const float p4[4] = {part[4 * h], part[4 * h + 1], part[4 * h + 2], part[4 * h + 3]};
+      const float v = rows_transpose_sum(p4);
+      // non-temporal: the scores are read by the next kernel, not this one
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, (g * kPfKeys + 64 * h + lane) * 4, 0, 2);
+    }
   }
 }
 
@@ -618,8 +652,8 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
   const int mode = a.q_dtype == kF32 ? 0 : (a.k_dtype == kFP8 ? 2 : 1);
   // many bf16 queries of one sequence (causal prefill form): key tiles shared by 8 queries
-  // (a score row is addressed with 32-bit byte offsets there)
-  if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 28) && !a.sample &&
+  // (key and score rows are addressed with 32-bit byte offsets there)
+  if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 22) && !a.sample &&
       !a.topk_state) {
     if (a.H_I <= 16) return a.D_I == 64 ? launch_prefill<1, 64>(a, stream) : launch_prefill<1, 128>(a, stream);
     if (a.H_I <= 32) return a.D_I == 64 ? launch_prefill<2, 64>(a, stream) : launch_prefill<2, 128>(a, stream);

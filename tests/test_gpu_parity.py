@@ -345,7 +345,9 @@ def test_prefill_form_scores_topk_attention(dsa, T, H_I, D_I):
     import torch
     p = inputs.prefill_config(T, seed=3, H_I=H_I, D_I=D_I, k=64)
     d = inputs.to_torch(p)
-    s_d = dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, T, q_seq=d.q_seq)
+    sentinel = -12345.5
+    s_d = torch.full((T, (T + 3) // 4 * 4), sentinel, dtype=torch.float32, device="cuda")
+    dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, T, q_seq=d.q_seq, scores=s_d)
     idx_d = dsa.dsa_topk(s_d, d.q_pos, T, p.k)
     scores, idx = s_d.cpu().numpy(), idx_d.cpu().numpy()
     ref_rows = O.index_scores(p)
@@ -354,6 +356,7 @@ def test_prefill_form_scores_topk_attention(dsa, T, H_I, D_I):
         ref = ref_rows[r].astype(np.float64)
         bound = C.score_bound(p, r, np.arange(n), ref)
         assert not (np.abs(scores[r, :n] - ref) > bound).any(), f"row {r}"
+        assert (scores[r, n:] == sentinel).all(), f"row {r}: entries past q_pos written"
         assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k)), f"row {r}"
     rows = [0, 1, T // 2, T - 1]
     out, lse = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx_d, p.scale, q_seq=d.q_seq)
