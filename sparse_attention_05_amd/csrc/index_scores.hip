@@ -206,6 +206,39 @@ __device__ __forceinline__ typename Frag<QK>::type key_frag(const char* stage, i
   return f;
 }
 
+// ReLU on the bit pattern: a float with the sign bit set is a negative int32,
+// so an integer max with 0 sends it to +0.0 (one VALU op; the float min/max
+// forms cost a NaN-quieting op on top).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// Lane 16*r + n holds p[t] = the part of 16-lane row r for key 16*t + n;
+// returns, in lane 16*t + n, the sum over the 4 rows of p[t]. The 32-lane
+// swap leaves rows {0+2, 1+3} sums of p[0], p[2] (and of p[1], p[3]) side by
+// side; the 16-lane swap pairs those up. Three lane swaps on the VALU, no
+// LDS round trip; the sum order is (r0 + r2) + (r1 + r3).
+__device__ __forceinline__ float rows_transpose_sum(const float (&p)[4]) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+  const float x = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // rows: p0 r0+r2, p0 r1+r3, p2 .., p2 ..
+  const float y = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // rows: p1 r0+r2, p1 r1+r3, p3 .., p3 ..
+  const auto sxy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(sxy[0]) + __uint_as_float(sxy[1]);
+}
+
+// s_waitcnt vmcnt(min(n, A)): at most n vector memory operations of this
+// wave still outstanding (they complete in issue order).
+template <int A>
+__device__ __forceinline__ void wait_ops(int n) {
+  if constexpr (A == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= A) wait_vmcnt<A>();
+    else wait_ops<A - 1>(n);
+  }
+}
+
 template <int QK, int MT, int DI>
 __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, int keys_per_wave) {
   using C = KeyCfg<QK, DI>;
@@ -298,6 +331,58 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
       load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], lane);
   }
 
+  if constexpr (QK == 1) {
+    // bf16 keys: the score (and sample) stores are branch-free buffer
+    // stores (lanes past this wave's range are dropped by the bounds), one
+    // per group each, so the wait for a group can count them exactly instead
+    // of also waiting for the stores issued after its loads.
+    const bool smp = a.sample != nullptr;
+    const int spg = smp ? 2 : 1;  // stores per group
+    const __amdgpu_buffer_rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc(
+        a.scores + int64_t(r) * a.ld + s_beg, 0, int((s_end - s_beg) * 4), 0x00020000);
+    const int64_t smp0 = s_beg >> 4;  // s_beg is a multiple of 64
+    const int nsmp = smp && s_beg < s_end ? int((s_end - 1) / 16 - smp0 + 1) : 0;
+    const __amdgpu_buffer_rsrc_t ssmp = __builtin_amdgcn_make_buffer_rsrc(
+        smp ? a.sample + int64_t(r) * a.ld_sample + smp0 : a.scores, 0, nsmp * 4, 0x00020000);
+    for (int g = 0; g < groups; ++g) {
+      const int64_t s0 = s_beg + 64 * g;
+      const char* stage = smem[wave][g % C::NS];
+      // behind group g's loads: those of the later groups and the stores of
+      // the groups computed since it was issued
+      const int behind = C::LOADS * (issued - 1 - g) + spg * (g < C::NS ? g : C::NS);
+      float part[4];
+      wait_ops<C::LOADS * (C::NS - 1) + 2 * C::NS>(behind);  // group g landed
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        f32x4 acc[MT];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const F kb = key_frag<QK, DI>(stage, 16 * blk + col, grp, ks);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_k32(qa[mt][ks], kb, ks ? acc[mt] : f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        float p = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p += wr[mt][i] * relu_bits(acc[mt][i]);
+        part[blk] = p;
+      }
+      // this stage is consumed: refill it with group g + NS
+      if (issued < groups) {
+        load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][g % C::NS], lane);
+        ++issued;
+      }
+      const float v = rows_transpose_sum(part);
+      const int64_t s = s0 + lane;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, int(s - s_beg) * 4, 0, 0);
+      if (smp)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ssmp,
+                                              (s & 15) ? -16 : int((s >> 4) - smp0) * 4, 0, 0);
+    }
+    return;
+  }
+
   float* out = a.scores + int64_t(r) * a.ld;
   for (int g = 0; g < groups; ++g) {
     const int64_t s0 = s_beg + 64 * g;
@@ -383,12 +468,6 @@ constexpr int kPfKeys = 128;  // keys per group (one barrier each)
 constexpr int kPfTiles = kPfKeys / 16;
 constexpr int kPfStages = 4;
 
-// ReLU on the bit pattern: a float with the sign bit set is a negative int32,
-// so an integer max with 0 sends it to +0.0 (one VALU op; the float min/max
-// forms cost a NaN-quieting op on top).
-__device__ __forceinline__ float relu_bits(float x) {
-  return __int_as_float(max(__float_as_int(x), 0));
-}
 
 // s_waitcnt vmcnt(A * LPW) for the largest A <= ahead (A <= 8).
 template <int LPW, int A = 8>
@@ -401,31 +480,7 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
   }
 }
 
-// Lane 16*r + n holds p[t] = the part of 16-lane row r for key 16*t + n;
-// returns, in lane 16*t + n, the sum over the 4 rows of p[t]. The 32-lane
-// swap leaves rows {0+2, 1+3} sums of p[0], p[2] (and of p[1], p[3]) side by
-// side; the 16-lane swap pairs those up. Three lane swaps on the VALU, no
-// LDS round trip; the sum order is (r0 + r2) + (r1 + r3).
-__device__ __forceinline__ float rows_transpose_sum(const float (&p)[4]) {
-  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
-  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
-  const float x = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);  // rows: p0 r0+r2, p0 r1+r3, p2 .., p2 ..
-  const float y = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);  // rows: p1 r0+r2, p1 r1+r3, p3 .., p3 ..
-  const auto sxy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(sxy[0]) + __uint_as_float(sxy[1]);
-}
 
-// s_waitcnt vmcnt(min(n, A)): at most n vector memory operations of this
-// wave still outstanding (they complete in issue order).
-template <int A>
-__device__ __forceinline__ void wait_ops(int n) {
-  if constexpr (A == 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (n >= A) wait_vmcnt<A>();
-    else wait_ops<A - 1>(n);
-  }
-}
 
 template <int MT, int DI>
 __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(IndexArgs a) {
