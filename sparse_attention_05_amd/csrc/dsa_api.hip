@@ -57,7 +57,7 @@ dsa_status check_attn_args(const void* q_abs, int dtype, const void* latent, int
 
 // Fused-decode workspace, in order: scores [B, ld] fp32, indices [B, k],
 // attention partials, score sample [B, ld_sample] fp32, split top-k
-// candidates and state (each part 256-byte aligned).
+// candidates and counts (each part 256-byte aligned).
 struct DecodeLayout {
   int64_t ld, ld_sample;
   size_t scores, idx, attn, sample, topk, total;
@@ -71,7 +71,7 @@ DecodeLayout decode_layout(int B, int max_len, int k, int H) {
   L.attn = L.idx + align256(size_t(B) * k * sizeof(int32_t));
   L.sample = L.attn + align256(plan_attention(B, H, k).ws_bytes);
   L.topk = L.sample + align256(size_t(B) * L.ld_sample * sizeof(float));
-  L.total = L.topk + align256(topk_split_ws_bytes(B));
+  L.total = L.topk + align256(topk_split_ws_bytes(B, max_len));
   return L;
 }
 
@@ -112,7 +112,7 @@ dsa_status dsa_index_scores(const void* q_idx, int32_t q_dtype, const float* hea
   if (ld_scores < max_n || (ld_scores & 3)) return DSA_ERR_SHAPE;
   if (!aligned16(scores)) return DSA_ERR_ALIGN;
   IndexArgs a{q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, q_seq, q_pos, nullptr,
-              R, H_I, D_I, max_n, scores, ld_scores, nullptr, 0, nullptr};
+              R, H_I, D_I, max_n, scores, ld_scores, nullptr, 0};
   hipError_t e = launch_index_scores(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : hip_fail(e);
 }
@@ -128,12 +128,9 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos
   TopkArgs a{scores, ld_scores, q_pos, nullptr, R, max_n, k, idx_out, nullptr, 0, nullptr, nullptr};
   hipStream_t s = static_cast<hipStream_t>(stream);
   // With a large enough workspace, few long rows are split over workgroups.
-  if (workspace && topk_use_split(R, max_n) && ws_bytes >= topk_split_ws_bytes(R)) {
+  if (workspace && topk_use_split(R, max_n) && ws_bytes >= topk_split_ws_bytes(R, max_n)) {
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSA_ERR_ALIGN;
-    a.cand = static_cast<unsigned long long*>(workspace);
-    a.state = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + size_t(R) * 4096 * sizeof(unsigned long long));
-    hipError_t e = launch_topk_clear(a.state, R, s);
-    if (e != hipSuccess) return hip_fail(e);
+    topk_split_carve(workspace, R, max_n, a);
   }
   hipError_t e = launch_topk(a, s);
   return e == hipSuccess ? DSA_OK : hip_fail(e);
@@ -179,18 +176,16 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
   void* attn_ws = ws + L.attn;
   float* sample = reinterpret_cast<float*>(ws + L.sample);
-  unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws + L.topk);
-  uint32_t* tstate = reinterpret_cast<uint32_t*>(ws + L.topk + size_t(B) * 4096 * sizeof(unsigned long long));
   const bool split = topk_use_split(B, max_len);
 
-  // the indexer also writes the score sample and clears the top-k state
+  // the indexer also writes the score sample the split top-k takes its pivot from
   IndexArgs ia{q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, nullptr, nullptr,
-               seq_len, B, H_I, D_I, max_len, scores, L.ld, split ? sample : nullptr, L.ld_sample,
-               split ? tstate : nullptr};
+               seq_len, B, H_I, D_I, max_len, scores, L.ld, split ? sample : nullptr, L.ld_sample};
   hipError_t e = launch_index_scores(ia, s);
   if (e != hipSuccess) return hip_fail(e);
   TopkArgs ta{scores, L.ld, nullptr, seq_len, B, max_len, k, idx, split ? sample : nullptr, L.ld_sample,
-              split ? tstate : nullptr, split ? cand : nullptr};
+              nullptr, nullptr};
+  if (split) topk_split_carve(ws + L.topk, B, max_len, ta);
   e = launch_topk(ta, s);
   if (e != hipSuccess) return hip_fail(e);
   const AttnPlan plan = plan_attention(B, H, k);
@@ -203,7 +198,7 @@ size_t dsa_workspace_size(int32_t entry, int32_t rows, int32_t max_len, int32_t 
   if (rows < 0 || k < 1 || H < 1) return 0;
   switch (entry) {
     case DSA_ENTRY_TOPK:
-      return topk_use_split(rows, max_len) ? topk_split_ws_bytes(rows) : 0;
+      return topk_use_split(rows, max_len) ? topk_split_ws_bytes(rows, max_len) : 0;
     case DSA_ENTRY_SPARSE_MLA:
       return plan_attention(rows, H, k).ws_bytes;
     case DSA_ENTRY_DECODE:

@@ -27,7 +27,6 @@ struct IndexArgs {
   int64_t ld;
   float* sample;          // NULL, or receives sample[r * ld_sample + i] = scores[r, 16 i]
   int64_t ld_sample;
-  uint32_t* topk_state;   // NULL, or [R][4] words set to zero (split top-k state)
 };
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 
@@ -42,13 +41,13 @@ struct TopkArgs {
   // are given and the rows are few and long:
   const float* sample;        // NULL, or sample[r * ld_sample + i] = scores[r, 16 i]
   int64_t ld_sample;
-  uint32_t* state;            // [R][4], zero at launch; left zero
-  unsigned long long* cand;   // [R][4096] candidate words
+  uint32_t* state;            // [R][slices] candidate counts (written, then read, by each launch)
+  unsigned long long* cand;   // [R][slices][2048] candidate words
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 bool topk_use_split(int R, int max_n);
-size_t topk_split_ws_bytes(int R);  // cand, then state
-hipError_t launch_topk_clear(uint32_t* state, int R, hipStream_t stream);
+size_t topk_split_ws_bytes(int R, int max_n);
+void topk_split_carve(void* ws, int R, int max_n, TopkArgs& a);  // sets a.cand, a.state
 
 struct AttnPlan {
   int splits;           // key splits per query row

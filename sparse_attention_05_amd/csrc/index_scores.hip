@@ -255,7 +255,6 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;  // MFMA column: key within a 16-key tile
   const int grp = lane >> 4;  // K-slot group / C-row group
-  if (a.topk_state && blockIdx.y == 0 && threadIdx.x < 4) a.topk_state[4 * r + threadIdx.x] = 0u;
 
   int b = a.q_seq ? a.q_seq[r] : r;
   b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
@@ -708,8 +707,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   const int mode = a.q_dtype == kF32 ? 0 : (a.k_dtype == kFP8 ? 2 : 1);
   // many bf16 queries of one sequence (causal prefill form): key tiles shared by 8 queries
   // (key and score rows are addressed with 32-bit byte offsets there)
-  if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 22) && !a.sample &&
-      !a.topk_state) {
+  if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 22) && !a.sample) {
     if (a.H_I <= 16) return a.D_I == 64 ? launch_prefill<1, 64>(a, stream) : launch_prefill<1, 128>(a, stream);
     if (a.H_I <= 32) return a.D_I == 64 ? launch_prefill<2, 64>(a, stream) : launch_prefill<2, 128>(a, stream);
     return a.D_I == 64 ? launch_prefill<4, 64>(a, stream) : launch_prefill<4, 128>(a, stream);

@@ -382,15 +382,16 @@ __device__ __forceinline__ uint32_t tie_threshold(TopkShared& sh, Each&& each, u
 // ---- sorting distinct 64-bit words (descending) ----------------------------------
 
 // Bucket the distinct words src[off .. off+m), all within [mn, mx], on 12
-// bits of (mx - word) into dst[off ..]; rank every bucket of <= kSmall words
-// by counting and write the indices of ranks < limit to out[rank]; append
-// denser buckets that start below `limit` to the work list wl (count in
-// sh.misc[6]) with their exact word range. Each thread handles the fixed
+// bits of (mx - word); only buckets whose ranks meet the window [lo, hi) go on:
+// their words are placed in dst[off ..], every such bucket of <= kSmall words
+// is ranked by counting and the indices of its ranks within the window are
+// written to out[rank]; denser ones are appended to the work list wl (count
+// in sh.misc[6]) with their exact word range. Each thread handles the fixed
 // slots i = t + 512*j (j < 8) and issues every stage for all of them at once,
 // so the LDS round trips of different slots overlap.
 __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long long* src, unsigned long long* dst,
-                                            int off, int m, unsigned long long mx, unsigned long long mn,
-                                            int limit, int32_t* out, uint32_t* wl) {
+                                            int off, int m, unsigned long long mx, unsigned long long mn, int lo,
+                                            int hi, int32_t* out, uint32_t* wl) {
   constexpr int J = kCap / kThreads;
   const int t = threadIdx.x;
   int shift, nb;
@@ -433,7 +434,7 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (b0 + j < nb) sh.bins[b0 + j] = run;
-    if (c[j] > kSmall && off + int(run) < limit) {
+    if (c[j] > kSmall && off + int(run) < hi && off + int(run + c[j]) > lo) {
       const uint32_t slot = atomicAdd(&sh.misc[6], 1u);
       if (slot < kMaxWork) {
         const unsigned long long bmx = mx - (static_cast<unsigned long long>(b0 + j) << shift);
@@ -452,48 +453,68 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
   }
   __syncthreads();
   uint32_t start[J], cb[J], slot[J];
+  bool keep[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     start[j] = sh.bins[bk[j]];
     cb[j] = sh.cnt[bk[j]];
+    keep[j] = t + j * kThreads < m && off + int(start[j]) < hi && off + int(start[j] + cb[j]) > lo;
   }
-  // Slots past m count on a spare word of their own (the bitonic scratch,
-  // unused here), so every slot's atomic and load below is unconditional:
-  // the LDS round trips of all slots of a thread are in flight together.
+  // Slots that are not placed count on a spare word of their own (the
+  // bitonic scratch, unused here), so every slot's atomic and load below is
+  // unconditional: the LDS round trips of all slots of a thread are in
+  // flight together.
   uint32_t* spare = reinterpret_cast<uint32_t*>(sh.v.net) + t;
 #pragma unroll
-  for (int j = 0; j < J; ++j) slot[j] = atomicAdd(t + j * kThreads < m ? &sh.fill[bk[j]] : spare, 1u);
+  for (int j = 0; j < J; ++j) slot[j] = atomicAdd(keep[j] ? &sh.fill[bk[j]] : spare, 1u);
 #pragma unroll
   for (int j = 0; j < J; ++j)
-    if (t + j * kThreads < m) dst[off + start[j] + slot[j]] = w[j];
+    if (keep[j]) dst[off + start[j] + slot[j]] = w[j];
   __syncthreads();
-  // rank inside small buckets: count the larger words of the bucket
-  uint32_t rank[J], most = 0;
+  // rank inside small buckets: count the larger words of the bucket. The
+  // elements placed in a small bucket are first listed (word in the bitonic
+  // scratch, bucket start and size in sh.bins, free now), so that each is
+  // ranked by one thread in eight-wide batches of LDS reads, whatever slot
+  // it came from.
+  uint32_t nl = 0;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const bool live = t + j * kThreads < m && cb[j] <= kSmall && off + int(start[j]) < limit;
-    cb[j] = live ? cb[j] : 0u;
-    start[j] = live ? start[j] : 0u;
-    rank[j] = 0u;
-    most = max(most, cb[j]);
+    cb[j] = keep[j] && cb[j] <= kSmall ? cb[j] : 0u;
+    nl += cb[j] != 0u;
   }
-  for (uint32_t q = 0; q < most; ++q) {
-    unsigned long long x[J];
+  uint32_t n_live;
+  uint32_t lp = block_scan(nl, sh.red, n_live);
 #pragma unroll
-    for (int j = 0; j < J; ++j) x[j] = dst[off + start[j] + (q < cb[j] ? q : 0u)];
-#pragma unroll
-    for (int j = 0; j < J; ++j) rank[j] += (q < cb[j]) & (x[j] > w[j]);
+  for (int j = 0; j < J; ++j) {
+    if (cb[j]) {
+      sh.v.net[lp] = w[j];
+      sh.bins[lp] = uint32_t(off + int(start[j])) | (cb[j] << 16);
+      ++lp;
+    }
   }
+  __syncthreads();
+  for (uint32_t e = t; e < n_live; e += kThreads) {
+    const unsigned long long we = sh.v.net[e];
+    const uint32_t sc = sh.bins[e];
+    const uint32_t b0 = sc & 0xFFFFu, c = sc >> 16;
+    uint32_t rk = 0;
+    for (uint32_t q0 = 0; q0 < c; q0 += 8) {
+      unsigned long long y[8];
 #pragma unroll
-  for (int j = 0; j < J; ++j)
-    if (cb[j] && off + int(start[j] + rank[j]) < limit) out[off + start[j] + rank[j]] = word_idx(w[j]);
+      for (int u = 0; u < 8; ++u) y[u] = dst[b0 + (q0 + u < c ? q0 + u : 0u)];  // past the bucket: not counted
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rk += (q0 + u < c) & (y[u] > we);
+    }
+    const int at = int(b0 + rk);
+    if (at >= lo && at < hi) out[at] = word_idx(we);
+  }
   lds_barrier();  // orders the LDS use only; the index stores need not complete here
 }
 
 // Bitonic network (descending) on src[off .. off+m), m <= kCap; writes the
-// indices of ranks < limit.
+// indices of the ranks in [lo, hi).
 __device__ __forceinline__ void bitonic_segment(TopkShared& sh, const unsigned long long* src, int off, int m,
-                                                int limit, int32_t* out) {
+                                                int lo, int hi, int32_t* out) {
   const int t = threadIdx.x;
   int P = 1;
   while (P < m) P <<= 1;
@@ -514,14 +535,14 @@ __device__ __forceinline__ void bitonic_segment(TopkShared& sh, const unsigned l
     }
   }
   for (int i = t; i < m; i += kThreads)
-    if (off + i < limit) out[off + i] = word_idx(sh.v.net[i]);
+    if (off + i >= lo && off + i < hi) out[off + i] = word_idx(sh.v.net[i]);
   __syncthreads();
 }
 
 // Sort the m distinct words in sh.wa (all within [mn, mx]) descending and
-// write the indices of the first `limit` to out.
+// write the indices of the ranks in [lo, hi) to out[rank].
 __device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long long mx, unsigned long long mn,
-                                           int limit, int32_t* out) {
+                                           int lo, int hi, int32_t* out) {
   if (threadIdx.x == 0) {
     uint32_t* e = sh.work[0];
     e[0] = 0u;
@@ -539,19 +560,19 @@ __device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long 
     __syncthreads();
     if (level == 3) {  // still dense after three splits: sorting network
       for (int i = 0; i < nitems; ++i)
-        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), limit, out);
+        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), lo, hi, out);
       return;
     }
     for (int i = 0; i < nitems; ++i) {
       const uint32_t* e = sh.work[cur] + 6 * i;
       const unsigned long long emx = (static_cast<unsigned long long>(e[2]) << 32) | e[3];
       const unsigned long long emn = (static_cast<unsigned long long>(e[4]) << 32) | e[5];
-      bucket_pass(sh, src, dst, int(e[0]), int(e[1]), emx, emn, limit, out, sh.work[cur ^ 1]);
+      bucket_pass(sh, src, dst, int(e[0]), int(e[1]), emx, emn, lo, hi, out, sh.work[cur ^ 1]);
     }
     const int next = int(sh.misc[6]);
     if (next > kMaxWork) {  // more dense buckets than the list holds: redo these segments
       for (int i = 0; i < nitems; ++i)
-        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), limit, out);
+        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), lo, hi, out);
       return;
     }
     if (next == 0) return;
@@ -614,7 +635,7 @@ __device__ __forceinline__ void select_exact(TopkShared& sh, const Row<EPT>& row
   if (need < eq_total) I = tie_threshold(sh, each_row, T, need, eq_total, n);
   collect_winners(sh, each_row, T, I);
   sort_words(sh, k, (static_cast<unsigned long long>(hi) << 32) | 0xFFFFFFFFull,
-             static_cast<unsigned long long>(T) << 32, k, out);
+             static_cast<unsigned long long>(T) << 32, 0, k, out);
 }
 
 template <int EPT>
@@ -649,7 +670,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     });
     __syncthreads();
     sort_words(sh, n, (static_cast<unsigned long long>(hi) << 32) | 0xFFFFFFFFull,
-               static_cast<unsigned long long>(lo) << 32, n, out);
+               static_cast<unsigned long long>(lo) << 32, 0, n, out);
     return;
   }
 
@@ -681,7 +702,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     cmax = block_max(cmax, sh.red);  // (its barrier publishes the candidates)
     // ---- 3. the k largest candidate words, in order -----------------------------------
     sort_words(sh, int(C), (static_cast<unsigned long long>(cmax) << 32) | 0xFFFFFFFFull,
-               static_cast<unsigned long long>(pivot) << 32, k, out);
+               static_cast<unsigned long long>(pivot) << 32, 0, k, out);
     return;
   }
 
@@ -689,24 +710,28 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   select_exact(sh, row, n, k, out);
 }
 
-// Split selection for few long rows: the row is cut into slices of kTile
-// keys, one workgroup each. Every workgroup derives the same pivot from the
-// row's sample, appends its slice's candidates (keys >= pivot, as words) to
-// the row's candidate array at an offset claimed with one atomic add, and
-// counts itself in; the last workgroup of the row to arrive sorts the
-// candidates (or runs the exact selection over the whole row when fewer than
-// k or more than kCap keys cleared the pivot) and clears the row's state for
-// the next launch. The candidate set is fixed by the pivot, so the order in
-// which slices append does not change the result.
-__global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a, int slices) {
+// Split selection for few long rows, in two launches.
+//  topk_cand_kernel: the row is cut into slices of kTile keys, one workgroup
+//    each; every workgroup derives the same pivot from the row's sample and
+//    writes its slice's candidates (keys >= pivot, as words, in index order)
+//    and their count to the slice's own region of the workspace.
+//  topk_window_kernel: one workgroup per 128 output ranks of a row gathers
+//    the row's candidates, buckets them and ranks only the buckets that meet
+//    its window (or, when fewer than k or more than kCap keys cleared the
+//    pivot, the first workgroup of the row runs the exact selection over the
+//    whole row).
+// The candidate set is fixed by the pivot and every rank is unique, so the
+// result does not depend on how the work is spread.
+constexpr int kWindow = 128;  // output ranks per workgroup of the second launch
+
+__global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int slices) {
   __shared__ TopkShared sh;
   const int r = blockIdx.x / slices, g = blockIdx.x % slices;
   const int t = threadIdx.x;
   const int n = row_len(a, r);
   const int k = a.k;
   const float* row = a.scores + int64_t(r) * a.ld;
-  uint32_t* st = a.state + 4 * r;  // count, arrivals, max candidate key, ~min candidate key
-  unsigned long long* cand = a.cand + int64_t(r) * kCap;
+  unsigned long long* cand = a.cand + (int64_t(r) * slices + g) * kTile;
 
   // this slice's scores, loaded first so the load overlaps the pivot
   const int i0 = g * kTile + 4 * t;
@@ -730,82 +755,98 @@ __global__ __launch_bounds__(kThreads) void topk_split_kernel(TopkArgs a, int sl
     pivot = sample_pivot(sh, ns, SS, k, smin, smax);
   }
 
-  // ---- this slice's candidates -----------------------------------------------------------
+  // ---- this slice's candidates, compacted in index order ---------------------------------
   uint32_t key[4];
   key[0] = order_key(sv.x);
   key[1] = order_key(sv.y);
   key[2] = order_key(sv.z);
   key[3] = order_key(sv.w);
-  uint32_t c = 0, kmax = 0u, kmin = 0xFFFFFFFFu;
+  uint32_t c = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (i0 + e < n && key[e] >= pivot) {
-      ++c;
-      kmax = max(kmax, key[e]);
-      kmin = min(kmin, key[e]);
-    }
-  }
+  for (int e = 0; e < 4; ++e) c += i0 + e < n && key[e] >= pivot;
   uint32_t total;
   uint32_t pos = block_scan(c, sh.red, total);
-  block_minmax(kmin, kmax, sh.red);
-  // Cross-workgroup traffic uses device-coherent accesses (relaxed atomics at
-  // agent scope: performed or written through past the per-XCD L2s) instead
-  // of fences, which would write back whole L2 caches.
-  if (t == 0) {
-    sh.misc[0] = total ? __hip_atomic_fetch_add(&st[0], total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-    if (total) {
-      __hip_atomic_fetch_max(&st[2], kmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_max(&st[3], ~kmin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();
-  const uint32_t at = sh.misc[0];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (i0 + e < n && key[e] >= pivot) {
-      if (at + pos < uint32_t(kCap))
-        __hip_atomic_store(&cand[at + pos], word(key[e], i0 + e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      cand[pos] = word(key[e], i0 + e);
       ++pos;
     }
   }
-
-  // ---- arrival: the last slice of the row finishes it -------------------------------------
-  // Every thread's candidate stores have completed before the slice counts
-  // itself in (vmcnt covers stores), so the last slice sees all of them.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (t == 0) sh.misc[1] = __hip_atomic_fetch_add(&st[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (sh.misc[1] != uint32_t(slices - 1)) return;
-  if (t == 0) {
-    sh.misc[2] = __hip_atomic_load(&st[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.misc[3] = __hip_atomic_load(&st[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.misc[4] = ~__hip_atomic_load(&st[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  const uint32_t C = sh.misc[2], cmax = sh.misc[3], cmin = sh.misc[4];
-  if (t < 4) __hip_atomic_store(&st[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
-
-  const int k_eff = n < k ? n : k;
-  int32_t* out = a.idx + int64_t(r) * k;
-  for (int j = k_eff + t; j < k; j += kThreads) out[j] = -1;
-  if (n == 0) return;
-  if (n <= k || (C >= uint32_t(k) && C <= uint32_t(kCap))) {
-    for (int j = t; j < int(C); j += kThreads)
-      sh.wa[j] = __hip_atomic_load(&cand[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    sort_words(sh, int(C), (static_cast<unsigned long long>(cmax) << 32) | 0xFFFFFFFFull,
-               static_cast<unsigned long long>(cmin) << 32, k_eff, out);
-    return;
-  }
-  Row<0> full;
-  full.load(row, n);
-  select_exact(sh, full, n, k, out);
+  if (t == 0) a.state[int64_t(r) * slices + g] = total;
 }
 
-__global__ void topk_clear_kernel(uint32_t* state, int words) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < words) state[i] = 0u;
+__global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int slices, int windows) {
+  __shared__ TopkShared sh;
+  const int r = blockIdx.x / windows, w = blockIdx.x % windows;
+  const int t = threadIdx.x;
+  const int n = row_len(a, r);
+  const int k = a.k;
+  const int k_eff = n < k ? n : k;
+  int32_t* out = a.idx + int64_t(r) * k;
+  if (w == 0)
+    for (int j = k_eff + t; j < k; j += kThreads) out[j] = -1;
+  const int lo = w * kWindow, hi = lo + kWindow < k_eff ? lo + kWindow : k_eff;
+  if (lo >= hi) return;
+
+  // Slice counts (slices <= kThreads) and, in the same round trip, the first
+  // words of every slice's region: thread t reads words j*tps + t%tps of
+  // slice t/tps (tps threads per slice), which covers the typical count.
+  const unsigned long long* cand = a.cand + int64_t(r) * slices * kTile;
+  const uint32_t cnt = t < slices ? a.state[int64_t(r) * slices + t] : 0u;
+  constexpr int J = kCap / kThreads;
+  int tps = kThreads;
+  while (tps > 1 && tps * slices > kThreads) tps >>= 1;
+  const int sg = t / tps, sl = t % tps;
+  unsigned long long x[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) x[j] = sg < slices ? cand[int64_t(sg) * kTile + j * tps + sl] : 0ull;
+  uint32_t C;
+  const uint32_t at = block_scan(cnt, sh.red, C);
+  if (C < uint32_t(k_eff) || C > uint32_t(kCap)) {
+    if (w != 0) return;  // one workgroup runs the exact selection of the row
+    Row<0> full;
+    full.load(a.scores + int64_t(r) * a.ld, n);
+    select_exact(sh, full, n, k, out);
+    return;
+  }
+  if (t < slices) {
+    sh.bins[t] = at;
+    sh.cnt[t] = cnt;
+  }
+  __syncthreads();
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  bool rest = false;  // this slice holds more words than were read ahead
+  if (sg < slices) {
+    const int m = int(sh.cnt[sg]), o = int(sh.bins[sg]);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int i = j * tps + sl;
+      if (i < m) {
+        sh.wa[o + i] = x[j];
+        const uint32_t kx = uint32_t(x[j] >> 32);
+        kmin = min(kmin, kx);
+        kmax = max(kmax, kx);
+      }
+    }
+    rest = m > J * tps;
+  }
+  // the rest of the longer slices (rows with skewed candidates)
+  if (__syncthreads_or(rest)) {
+    for (int g = 0; g < slices; ++g) {
+      const int m = int(sh.cnt[g]), o = int(sh.bins[g]);
+      for (int i = J * tps + t; i < m; i += kThreads) {
+        const unsigned long long y = cand[int64_t(g) * kTile + i];
+        sh.wa[o + i] = y;
+        const uint32_t ky = uint32_t(y >> 32);
+        kmin = min(kmin, ky);
+        kmax = max(kmax, ky);
+      }
+    }
+  }
+  block_minmax(kmin, kmax, sh.red);  // (its barriers publish the gathered words)
+  sort_words(sh, int(C), (static_cast<unsigned long long>(kmax) << 32) | 0xFFFFFFFFull,
+             static_cast<unsigned long long>(kmin) << 32, lo, hi, out);
 }
 
 }  // namespace
@@ -814,21 +855,26 @@ bool topk_use_split(int R, int max_n) {
   return max_n > 4 * kTile && R <= device_cu_count() / 2;
 }
 
-size_t topk_split_ws_bytes(int R) {
-  return size_t(R) * kCap * sizeof(unsigned long long) + size_t(R) * 4 * sizeof(uint32_t);
+// Split workspace: the candidate words [R][slices][kTile], then the slice
+// counts [R][slices].
+size_t topk_split_ws_bytes(int R, int max_n) {
+  const size_t slices = size_t((max_n + kTile - 1) / kTile);
+  return size_t(R) * slices * kTile * sizeof(unsigned long long) + size_t(R) * slices * sizeof(uint32_t);
 }
 
-hipError_t launch_topk_clear(uint32_t* state, int R, hipStream_t stream) {
-  const int words = 4 * R;
-  if (words > 0) topk_clear_kernel<<<dim3(unsigned((words + 255) / 256)), 256, 0, stream>>>(state, words);
-  return hipGetLastError();
+void topk_split_carve(void* ws, int R, int max_n, TopkArgs& a) {
+  const size_t slices = size_t((max_n + kTile - 1) / kTile);
+  a.cand = static_cast<unsigned long long*>(ws);
+  a.state = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + size_t(R) * slices * kTile * sizeof(unsigned long long));
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
   if (a.state && a.cand && topk_use_split(a.R, a.max_n)) {
-    const int slices = (a.max_n + kTile - 1) / kTile;
-    topk_split_kernel<<<dim3(unsigned(a.R) * unsigned(slices)), kThreads, 0, stream>>>(a, slices);
+    const int slices = (a.max_n + kTile - 1) / kTile;  // <= kThreads for rows up to 2^20 keys
+    const int windows = (a.k + kWindow - 1) / kWindow;
+    topk_cand_kernel<<<dim3(unsigned(a.R) * unsigned(slices)), kThreads, 0, stream>>>(a, slices);
+    topk_window_kernel<<<dim3(unsigned(a.R) * unsigned(windows)), kThreads, 0, stream>>>(a, slices, windows);
     return hipGetLastError();
   }
   dim3 grid(unsigned(a.R));
