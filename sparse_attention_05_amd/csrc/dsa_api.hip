@@ -185,11 +185,16 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
   if (e != hipSuccess) return hip_fail(e);
   TopkArgs ta{scores, L.ld, nullptr, seq_len, B, max_len, k, idx, split ? sample : nullptr, L.ld_sample,
               nullptr, nullptr};
+  const AttnPlan plan = plan_attention(B, H, k);
+  AttnArgs aa{q_abs, act_dtype, latent, cache_rows, row_off, B, nullptr, idx, k, B, H, scale, out, lse, attn_ws};
+  if (split && act_dtype == DSA_BF16) {  // few long rows: selection fused with the attention
+    topk_split_carve(ws + L.topk, B, max_len, ta);
+    e = launch_topk_attn(ta, aa, plan, s);
+    return e == hipSuccess ? DSA_OK : hip_fail(e);
+  }
   if (split) topk_split_carve(ws + L.topk, B, max_len, ta);
   e = launch_topk(ta, s);
   if (e != hipSuccess) return hip_fail(e);
-  const AttnPlan plan = plan_attention(B, H, k);
-  AttnArgs aa{q_abs, act_dtype, latent, cache_rows, row_off, B, nullptr, idx, k, B, H, scale, out, lse, attn_ws};
   e = launch_sparse_mla(aa, plan, s);
   return e == hipSuccess ? DSA_OK : hip_fail(e);
 }

@@ -72,7 +72,12 @@ struct AttnArgs {
   float* lse;
   void* ws;
 };
-hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
+hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);  // + combine
+hipError_t launch_attn_combine(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
+// Split selection fused with the attention (rows few and long, ta.state and
+// ta.cand set, bf16 attention operands): candidates, then selection +
+// attention per (row, split, head group), then the combine.
+hipError_t launch_topk_attn(const TopkArgs& ta, const AttnArgs& aa, const AttnPlan& plan, hipStream_t stream);
 
 int device_cu_count();
 

@@ -33,120 +33,30 @@
 // device, so the same indices always give the same bits (index replay).
 // The workgroups sharing (query, key range) are placed on one XCD, so three
 // of every four gathers of a latent row hit that XCD's L2.
-#include "dsa_common.hpp"
-#include "dsa_internal.hpp"
+#include "attn_core.hpp"
 
 namespace dsa {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kAttnThreads = 256;   // 4 waves
-constexpr int kGroupHeads = 16;     // heads per workgroup
-constexpr int kChunkKeys = 64;      // keys per LDS buffer, 16 per wave
-constexpr int kPRow = kChunkKeys + 4;  // padded row of the P^T staging array
-
-template <bool F32>
-struct AttnCfg {
-  static constexpr int ESZ = F32 ? 4 : 2;                    // bytes per element
-  static constexpr int ROW_BYTES = kLatentDim * ESZ;         // one latent row
-  static constexpr int ROW_CHUNKS = ROW_BYTES / 16;          // 16-byte chunks per row (multiple of 8)
-  static constexpr int BUF_BYTES = kChunkKeys * ROW_BYTES;
-  static constexpr int NBUF = F32 ? 1 : 2;                   // LDS buffers (147,456 bytes either way)
-  static constexpr int WAVE_LOADS = 16 * ROW_CHUNKS / 64;    // 1 KiB direct loads per wave per chunk
-};
-static_assert(AttnCfg<false>::ROW_CHUNKS % 8 == 0 && AttnCfg<true>::ROW_CHUNKS % 8 == 0, "swizzle groups");
-
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// Chunk permutation of key row r (see the header comment).
-__device__ __forceinline__ int row_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
-// Wave `wave` starts the gather of its 16 rows of chunk c: keys
-// j_beg + 64c + 16*wave + (0..15), whose raw indices the wave left in
-// s_idx[64c + 16*wave + i] (-1 past the range). Rows of missing keys (idx < 0,
-// outside the cache) are zero-filled. Returns the 16-bit mask of present keys
-// (bit i: row 16*wave + i of the chunk).
-template <bool F32>
-__device__ __forceinline__ uint32_t issue_chunk(const AttnArgs& a, int64_t base, const int* s_idx, int c,
-                                                char* buf, int wave, int lane) {
-  using Cfg = AttnCfg<F32>;
-  int64_t src = -1;
-  if (lane < 16) {
-    const int s = s_idx[kChunkKeys * c + 16 * wave + lane];
-    const int64_t row = base + s;
-    if (s >= 0 && base >= 0 && row < a.cache_rows) src = row * Cfg::ROW_BYTES;
-  }
-  const uint32_t ok = uint32_t(__ballot(src >= 0)) & 0xFFFFu;
-  const uint32_t src_lo = uint32_t(uint64_t(src)), src_hi = uint32_t(uint64_t(src) >> 32);
-  const char* lat = static_cast<const char*>(a.latent);
-  char* wbuf = buf + 16 * wave * Cfg::ROW_BYTES;
-#pragma unroll
-  for (int m = 0; m < Cfg::WAVE_LOADS; ++m) {
-    // the 64 chunks of this load span rows rA (lanes < cut) and rA + 1
-    const int rA = (64 * m) / Cfg::ROW_CHUNKS;
-    const int cut = Cfg::ROW_CHUNKS * (rA + 1) - 64 * m;
-    const int rB = rA + 1 < 16 ? rA + 1 : 15;
-    const bool inA = lane < cut;
-    const int rl = inA ? rA : rA + 1;
-    const int pc = 64 * m + lane - Cfg::ROW_CHUNKS * rl;  // physical chunk in the row
-    const int lc = pc ^ row_swz(rl);                      // logical chunk it holds
-    const uint32_t loA = __builtin_amdgcn_readlane(src_lo, rA), loB = __builtin_amdgcn_readlane(src_lo, rB);
-    const uint32_t hiA = __builtin_amdgcn_readlane(src_hi, rA), hiB = __builtin_amdgcn_readlane(src_hi, rB);
-    const int64_t so = int64_t((uint64_t(inA ? hiA : hiB) << 32) | (inA ? loA : loB));
-    if ((ok >> rl) & 1u)
-      __builtin_amdgcn_global_load_lds(lat + so + 16 * lc, (lds_ptr)(wbuf + 1024 * m), 16, 0, 0);
-  }
-  if (ok != 0xFFFFu) {
-    for (int q = lane; q < 16 * Cfg::ROW_CHUNKS; q += 64)
-      if (!((ok >> (q / Cfg::ROW_CHUNKS)) & 1u)) *reinterpret_cast<uint4*>(wbuf + 16 * q) = uint4{0u, 0u, 0u, 0u};
-  }
-  return ok;
-}
-
-template <bool F32>
-using QFrag = typename std::conditional<F32, f32x8, bf16x8>::type;
+using namespace attn;
 
 template <bool F32>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, int splits, int kps) {
-  using Cfg = AttnCfg<F32>;
-  using PT = typename std::conditional<F32, float, __bf16>::type;
-  __shared__ __attribute__((aligned(1024))) char smem[Cfg::NBUF * Cfg::BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) PT s_p[kGroupHeads * kPRow];  // P^T as [head][key]
-  __shared__ float s_max[4][kGroupHeads];
-  __shared__ float s_l[4][kGroupHeads];
+  __shared__ Smem<F32> sm;
   __shared__ int s_idx[kMaxTopk];  // raw indices of the range; wave w owns entries 64c + 16w + (0..15)
-
   const int HG = (a.H + kGroupHeads - 1) / kGroupHeads;
-  const int pairs = a.R * splits;
-  int pair, hg;
-  {
-    const int u = blockIdx.x;
-    if ((pairs & 7) == 0) {  // workgroup u runs on XCD u mod 8: keep a pair's head groups together
-      const int local = u >> 3;
-      pair = (local / HG) * 8 + (u & 7);
-      hg = local % HG;
-    } else {
-      pair = u / HG;
-      hg = u % HG;
-    }
-  }
-  const int r = pair / splits, split = pair % splits;
+  int r, split, hg;
+  map_block(blockIdx.x, a.R, splits, HG, r, split, hg);
   const int t = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // scalar: LDS bases of direct loads must be
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int h = hg * kGroupHeads + col;  // this lane's head (MFMA column)
-
-  int b = a.q_seq ? a.q_seq[r] : r;
-  b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
-  const int64_t base = a.row_off[b];
   const int j_beg = split * kps;
   const int j_end = (j_beg + kps < a.k) ? j_beg + kps : a.k;
   const int nchunks = j_end > j_beg ? (j_end - j_beg + kChunkKeys - 1) / kChunkKeys : 0;
 
-  // Query fragments (B operand of q.c): head h, dims 32*ks + 8*grp .. +8.
+  const int64_t base = seq_base(a, r);
   // This wave's indices for every chunk, fetched once (one wait) before the
   // query loads, so that no later wait on them also waits for other loads.
   for (int q = lane; q < 16 * nchunks; q += 64) {
@@ -154,187 +64,17 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, in
     const int j = j_beg + e;
     s_idx[e] = j < j_end ? a.idx[int64_t(r) * a.k + j] : -1;
   }
-
-  // Heads past H (last group) load head H-1 and are zeroed.
   QFrag<F32> qf[18];
-  {
-    const bool hv = h < a.H;
-    const int64_t qoff = (int64_t(r) * a.H + (hv ? h : a.H - 1)) * kLatentDim + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      if constexpr (F32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + qoff + 32 * ks);
-        const float4 x = p[0], y = p[1];
-        qf[ks] = hv ? f32x8{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}} : f32x8{{0, 0, 0, 0, 0, 0, 0, 0}};
-      } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qoff + 32 * ks);
-        qf[ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
-      }
-    }
-  }
-
-  uint32_t ok[Cfg::NBUF];
-#pragma unroll
-  for (int i = 0; i < Cfg::NBUF; ++i)
-    ok[i] = i < nchunks ? issue_chunk<F32>(a, base, s_idx, i, smem + i * Cfg::BUF_BYTES, wave, lane) : 0u;
-
-  f32x4 acc[8];
-#pragma unroll
-  for (int vt = 0; vt < 8; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max (log2 domain) of head h, equal in all waves
-  float l_part = 0.f;       // this lane's share of the running sum
-  const float scale2 = a.scale * kLog2e;
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int bi = Cfg::NBUF == 2 ? (c & 1) : 0;
-    char* buf = smem + bi * Cfg::BUF_BYTES;
-    if (Cfg::NBUF == 1 && c > 0) {
-      __syncthreads();  // every wave is done with the previous chunk
-      ok[0] = issue_chunk<F32>(a, base, s_idx, c, buf, wave, lane);
-    }
-    const uint32_t okc = ok[bi];
-
-    // ---- logits of this wave's 16 keys: S^T = C[16 x 576] . Q^T ----------------------
-    f32x4 sacc;
-    {
-      const char* rp = buf + (16 * wave + col) * Cfg::ROW_BYTES;
-      const int sw = row_swz(col);
-      f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        if constexpr (F32) {
-          const int c0 = 8 * ks + 2 * grp;
-          const float4 x = *reinterpret_cast<const float4*>(rp + 16 * (c0 ^ sw));
-          const float4 y = *reinterpret_cast<const float4*>(rp + 16 * ((c0 + 1) ^ sw));
-          const f32x8 af{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
-          part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
-        } else {
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(rp + 16 * ((4 * ks + grp) ^ sw));
-          part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
-        }
-      }
-      sacc = part[0] + part[1];
-    }
-
-    // ---- chunk maximum per head over the 4 waves ----------------------------------------
-    float x[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = ((okc >> (4 * grp + i)) & 1u) ? sacc[i] * scale2 : -INFINITY;
-      mx = fmaxf(mx, x[i]);
-    }
-    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    if (grp == 0) s_max[wave][col] = mx;
-    __syncthreads();  // maxima visible; every wave is done with chunk c-1 and has its rows of chunk c
-    const float cmax = fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col]));
-    if (Cfg::NBUF == 2 && c + 1 < nchunks && c >= 1)
-      ok[bi ^ 1] = issue_chunk<F32>(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
-
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no key seen yet: p = alpha = 0
-    const float alpha = exp2f(m_run - m_use);
-    float psum = 0.f;
-    PT pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = exp2f(x[i] - m_use);
-      pv[i] = static_cast<PT>(e);
-      psum += static_cast<float>(pv[i]);
-    }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int vt = 0; vt < 8; ++vt) acc[vt] *= alpha;
-    }
-    PT* prow = s_p + col * kPRow + 16 * wave + 4 * grp;
-    if constexpr (F32) {
-      *reinterpret_cast<float4*>(prow) = float4{pv[0], pv[1], pv[2], pv[3]};
-    } else {
-      const uint32_t w0 = uint32_t(__builtin_bit_cast(uint16_t, pv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[1])) << 16);
-      const uint32_t w1 = uint32_t(__builtin_bit_cast(uint16_t, pv[2])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[3])) << 16);
-      *reinterpret_cast<uint2*>(prow) = uint2{w0, w1};
-    }
-    __syncthreads();  // P^T of all 64 keys in LDS
-
-    // ---- O^T[128*wave + 16*vt + (0..15)][head] += C^T . P^T over the 64 keys -------------
-    if constexpr (F32) {
-#pragma unroll
-      for (int kq = 0; kq < kChunkKeys / 4; ++kq) {
-        const int row = 4 * kq + grp;
-        const float pf = s_p[col * kPRow + row];
-        const char* rp = buf + row * Cfg::ROW_BYTES;
-        const int sw = row_swz(row);
-#pragma unroll
-        for (int vt = 0; vt < 8; ++vt) {
-          const int v = 128 * wave + 16 * vt + col;
-          const float cv = *reinterpret_cast<const float*>(rp + 16 * ((v >> 2) ^ sw) + 4 * (v & 3));
-          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cv, pf, acc[vt], 0, 0, 0);
-        }
-      }
-    } else {
-      // K-slot 8*grp + i <-> key kb + 4*grp + i (i < 4) and kb + 16 + 4*grp + (i - 4).
-      // Transposing read: lane s of each 16-lane group names 4 values of row
-      // kb + 4*grp + s/4 (value dims v0 + 4*(s%4) ..), and receives value dim
-      // v0 + s of rows kb + 4*grp + 0..3.
-      const int tr_row = 4 * grp + (col >> 2);
-      const int tr_sw = ((col >> 2) << 1) | (grp & 1);  // row_swz of every row this lane names
-#pragma unroll
-      for (int kb = 0; kb < kChunkKeys; kb += 32) {
-        const PT* pp = s_p + col * kPRow + kb + 4 * grp;
-        const uint2 plo = *reinterpret_cast<const uint2*>(pp);
-        const uint2 phi = *reinterpret_cast<const uint2*>(pp + 16);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
-        const char* rp = buf + (kb + tr_row) * Cfg::ROW_BYTES + 8 * (col & 1);
-#pragma unroll
-        for (int vt = 0; vt < 8; ++vt) {
-          const int lc = 16 * wave + 2 * vt + ((col >> 1) & 1);
-          const char* p0 = rp + 16 * (lc ^ tr_sw);
-          const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(lds_ptr)p0);
-          const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + 16 * Cfg::ROW_BYTES));
-          const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[vt] = mfma_k32(af, pf, acc[vt]);
-        }
-      }
-    }
-  }
-
-  // ---- epilogue: row sums over the lanes and waves, then O rows as float4 ----------------
-  float l_w = l_part + wave_shfl_xor(l_part, 16);
-  l_w += wave_shfl_xor(l_w, 32);
-  if (grp == 0) s_l[wave][col] = l_w;
-  __syncthreads();
-  const float L = ((s_l[0][col] + s_l[1][col]) + s_l[2][col]) + s_l[3][col];
-  if (h >= a.H) return;
-  const int64_t rh = int64_t(r) * a.H + h;
-  const bool final_out = splits == 1;
-  const float inv = final_out ? (L > 0.f ? 1.f / L : 0.f) : 1.f;
-  float* dst = final_out ? a.out + rh * kValueDim
-                         : static_cast<float*>(a.ws) + ((int64_t(r) * splits + split) * a.H + h) * kValueDim;
-#pragma unroll
-  for (int vt = 0; vt < 8; ++vt)
-    *reinterpret_cast<float4*>(dst + 128 * wave + 16 * vt + 4 * grp) =
-        float4{acc[vt][0] * inv, acc[vt][1] * inv, acc[vt][2] * inv, acc[vt][3] * inv};
-  if (wave == 0 && grp == 0) {
-    if (final_out) {
-      if (a.lse) a.lse[rh] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
-    } else {
-      float* ml = static_cast<float*>(a.ws) + int64_t(a.R) * splits * a.H * kValueDim;
-      const int64_t slot = (int64_t(r) * splits + split) * a.H + h;
-      *reinterpret_cast<float2*>(ml + 2 * slot) = float2{m_run, L};
-    }
-  }
+  load_q<F32>(a, r, h, grp, qf);
+  attend<F32>(a, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, sm);
 }
 
 // Merge key splits: O = sum_s e_s O_s / sum_s e_s l_s, e_s = 2^(m_s - max m),
-// splits with an empty sum skipped. P = ceil(splits / 16) adjacent lanes share
-// one output float4, each lane loading and summing its <= 16 splits (all loads
-// issued together), then the P partial sums are added in lane order. Every
-// order is fixed, so the result is bitwise reproducible.
-template <int P>
+// splits with an empty sum skipped. P adjacent lanes share one output float4,
+// each lane loading and summing its SPL consecutive splits (all loads issued
+// together), then the P partial sums are added in lane order. Every order is
+// fixed, so the result is bitwise reproducible.
+template <int P, int SPL>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int splits) {
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t o4 = gid / P;            // output float4 index over [R, H, 128]
@@ -346,11 +86,11 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int splits) {
   const int r = int(rh / a.H), h = int(rh % a.H);
   const float* ws = static_cast<const float*>(a.ws);
   const float* ml = ws + int64_t(a.R) * splits * a.H * kValueDim;
-  const int s0 = part * 16;
-  float4 o[16];
-  float2 w[16];
+  const int s0 = part * SPL;
+  float4 o[SPL];
+  float2 w[SPL];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < SPL; ++i) {
     const int s = s0 + i;
     if (live && s < splits) {
       const int64_t slot = (int64_t(r) * splits + s) * a.H + h;
@@ -363,14 +103,14 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int splits) {
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < SPL; ++i)
     if (w[i].y > 0.f) M = fmaxf(M, w[i].x);
 #pragma unroll
   for (int d = 1; d < P; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
   float L = 0.f;
   float4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < SPL; ++i) {
     if (w[i].y > 0.f) {
       const float e = exp2f(w[i].x - M);
       L += e * w[i].y;
@@ -402,6 +142,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int splits) {
 
 }  // namespace
 
+using attn::kChunkKeys;
+using attn::kGroupHeads;
+
 AttnPlan plan_attention(int R, int H, int k) {
   AttnPlan p{};
   p.head_groups = (H + kGroupHeads - 1) / kGroupHeads;
@@ -409,7 +152,7 @@ AttnPlan plan_attention(int R, int H, int k) {
   const int target = device_cu_count();  // one workgroup (147 KiB of LDS) per CU
   int splits = (target + base - 1) / base;
   int max_splits = (k + kChunkKeys - 1) / kChunkKeys;
-  if (max_splits > 64) max_splits = 64;  // the combine holds one split per lane
+  if (max_splits > 64) max_splits = 64;  // the combine covers up to 16 lanes x 4 splits
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int kps = (k + splits - 1) / splits;
@@ -428,13 +171,21 @@ hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_
   if (a.dtype == kF32) sparse_mla_kernel<true><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
   else sparse_mla_kernel<false><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.splits == 1) return e;
-  const int P = plan.splits <= 16 ? 1 : (plan.splits <= 32 ? 2 : 4);
+  if (e != hipSuccess) return e;
+  return launch_attn_combine(a, plan, stream);
+}
+
+hipError_t launch_attn_combine(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
+  if (a.R == 0 || plan.splits == 1) return hipSuccess;
+  // 4 splits per lane: up to 16 lanes per output float4 (splits <= 64)
+  const int P = plan.splits <= 4 ? 1 : plan.splits <= 8 ? 2 : plan.splits <= 16 ? 4 : plan.splits <= 32 ? 8 : 16;
   const int64_t threads = int64_t(a.R) * a.H * (kValueDim / 4) * P;
   const dim3 cgrid(unsigned((threads + 255) / 256));
-  if (P == 1) combine_kernel<1><<<cgrid, 256, 0, stream>>>(a, plan.splits);
-  else if (P == 2) combine_kernel<2><<<cgrid, 256, 0, stream>>>(a, plan.splits);
-  else combine_kernel<4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
+  if (P == 1) combine_kernel<1, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
+  else if (P == 2) combine_kernel<2, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
+  else if (P == 4) combine_kernel<4, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
+  else if (P == 8) combine_kernel<8, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
+  else combine_kernel<16, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "attn_core.hpp"
 #include "dsa_common.hpp"
 #include "dsa_internal.hpp"
 
@@ -391,7 +392,7 @@ __device__ __forceinline__ uint32_t tie_threshold(TopkShared& sh, Each&& each, u
 // so the LDS round trips of different slots overlap.
 __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long long* src, unsigned long long* dst,
                                             int off, int m, unsigned long long mx, unsigned long long mn, int lo,
-                                            int hi, int32_t* out, uint32_t* wl) {
+                                            int hi, int32_t* out, int obase, uint32_t* wl) {
   constexpr int J = kCap / kThreads;
   const int t = threadIdx.x;
   int shift, nb;
@@ -506,15 +507,15 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
       for (int u = 0; u < 8; ++u) rk += (q0 + u < c) & (y[u] > we);
     }
     const int at = int(b0 + rk);
-    if (at >= lo && at < hi) out[at] = word_idx(we);
+    if (at >= lo && at < hi) out[at - obase] = word_idx(we);
   }
   lds_barrier();  // orders the LDS use only; the index stores need not complete here
 }
 
 // Bitonic network (descending) on src[off .. off+m), m <= kCap; writes the
-// indices of the ranks in [lo, hi).
+// indices of the ranks in [lo, hi) (rank q to out[q - obase]).
 __device__ __forceinline__ void bitonic_segment(TopkShared& sh, const unsigned long long* src, int off, int m,
-                                                int lo, int hi, int32_t* out) {
+                                                int lo, int hi, int32_t* out, int obase) {
   const int t = threadIdx.x;
   int P = 1;
   while (P < m) P <<= 1;
@@ -535,14 +536,14 @@ __device__ __forceinline__ void bitonic_segment(TopkShared& sh, const unsigned l
     }
   }
   for (int i = t; i < m; i += kThreads)
-    if (off + i >= lo && off + i < hi) out[off + i] = word_idx(sh.v.net[i]);
+    if (off + i >= lo && off + i < hi) out[off + i - obase] = word_idx(sh.v.net[i]);
   __syncthreads();
 }
 
 // Sort the m distinct words in sh.wa (all within [mn, mx]) descending and
-// write the indices of the ranks in [lo, hi) to out[rank].
+// write the indices of the ranks q in [lo, hi) to out[q - obase].
 __device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long long mx, unsigned long long mn,
-                                           int lo, int hi, int32_t* out) {
+                                           int lo, int hi, int32_t* out, int obase = 0) {
   if (threadIdx.x == 0) {
     uint32_t* e = sh.work[0];
     e[0] = 0u;
@@ -560,19 +561,19 @@ __device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long 
     __syncthreads();
     if (level == 3) {  // still dense after three splits: sorting network
       for (int i = 0; i < nitems; ++i)
-        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), lo, hi, out);
+        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), lo, hi, out, obase);
       return;
     }
     for (int i = 0; i < nitems; ++i) {
       const uint32_t* e = sh.work[cur] + 6 * i;
       const unsigned long long emx = (static_cast<unsigned long long>(e[2]) << 32) | e[3];
       const unsigned long long emn = (static_cast<unsigned long long>(e[4]) << 32) | e[5];
-      bucket_pass(sh, src, dst, int(e[0]), int(e[1]), emx, emn, lo, hi, out, sh.work[cur ^ 1]);
+      bucket_pass(sh, src, dst, int(e[0]), int(e[1]), emx, emn, lo, hi, out, obase, sh.work[cur ^ 1]);
     }
     const int next = int(sh.misc[6]);
     if (next > kMaxWork) {  // more dense buckets than the list holds: redo these segments
       for (int i = 0; i < nitems; ++i)
-        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), lo, hi, out);
+        bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), lo, hi, out, obase);
       return;
     }
     if (next == 0) return;
@@ -617,25 +618,26 @@ __device__ __forceinline__ uint32_t sample_pivot(TopkShared& sh, int ns, int SS,
 // Exact selection over a whole row held by `row` (any EPT), for rows whose
 // pivot did not yield k..kCap candidates: radix select finds the k-th key T,
 // the kept keys equal to T are the `need` smallest indices, and the k winners
-// are sorted.
+// are sorted; ranks q in [lo, hi) go to out[q - obase].
 template <int EPT>
-__device__ __forceinline__ void select_exact(TopkShared& sh, const Row<EPT>& row, int n, int k, int32_t* out) {
+__device__ __forceinline__ void select_exact(TopkShared& sh, const Row<EPT>& row, int n, int k, int32_t* out,
+                                             int lo = 0, int hi = kMaxTopk, int obase = 0) {
   auto each_row = [&](auto&& f) { row.each(f); };
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  uint32_t lo_key = 0xFFFFFFFFu, hi_key = 0u;
   row.each([&](int idx, uint32_t key) {
     if (idx < n) {
-      lo = min(lo, key);
-      hi = max(hi, key);
+      lo_key = min(lo_key, key);
+      hi_key = max(hi_key, key);
     }
   });
-  block_minmax(lo, hi, sh.red);
+  block_minmax(lo_key, hi_key, sh.red);
   uint32_t T, need, eq_total, I = 0u;
   auto visit_keys = [&](auto&& f) { row.each([&](int, uint32_t key) { f(key); }); };
-  select_full(sh, visit_keys, lo, hi, uint32_t(k), uint32_t(n), T, need, eq_total);
+  select_full(sh, visit_keys, lo_key, hi_key, uint32_t(k), uint32_t(n), T, need, eq_total);
   if (need < eq_total) I = tie_threshold(sh, each_row, T, need, eq_total, n);
   collect_winners(sh, each_row, T, I);
-  sort_words(sh, k, (static_cast<unsigned long long>(hi) << 32) | 0xFFFFFFFFull,
-             static_cast<unsigned long long>(T) << 32, 0, k, out);
+  sort_words(sh, k, (static_cast<unsigned long long>(hi_key) << 32) | 0xFFFFFFFFull,
+             static_cast<unsigned long long>(T) << 32, lo, hi < k ? hi : k, out, obase);
 }
 
 template <int EPT>
@@ -776,19 +778,14 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
   if (t == 0) a.state[int64_t(r) * slices + g] = total;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int slices, int windows) {
-  __shared__ TopkShared sh;
-  const int r = blockIdx.x / windows, w = blockIdx.x % windows;
+// Ranks [lo, hi) of row r (hi <= min(n, k)) from the candidates of the
+// slices, indices to out[rank - obase]; when fewer than k or more than kCap
+// keys cleared the pivot, the exact selection over the whole row instead.
+__device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a, int r, int slices, int n, int lo,
+                                              int hi, int32_t* out, int obase) {
   const int t = threadIdx.x;
-  const int n = row_len(a, r);
   const int k = a.k;
   const int k_eff = n < k ? n : k;
-  int32_t* out = a.idx + int64_t(r) * k;
-  if (w == 0)
-    for (int j = k_eff + t; j < k; j += kThreads) out[j] = -1;
-  const int lo = w * kWindow, hi = lo + kWindow < k_eff ? lo + kWindow : k_eff;
-  if (lo >= hi) return;
-
   // Slice counts (slices <= kThreads) and, in the same round trip, the first
   // words of every slice's region: thread t reads words j*tps + t%tps of
   // slice t/tps (tps threads per slice), which covers the typical count.
@@ -804,10 +801,9 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int s
   uint32_t C;
   const uint32_t at = block_scan(cnt, sh.red, C);
   if (C < uint32_t(k_eff) || C > uint32_t(kCap)) {
-    if (w != 0) return;  // one workgroup runs the exact selection of the row
     Row<0> full;
     full.load(a.scores + int64_t(r) * a.ld, n);
-    select_exact(sh, full, n, k, out);
+    select_exact(sh, full, n, k, out, lo, hi, obase);
     return;
   }
   if (t < slices) {
@@ -846,8 +842,69 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int s
   }
   block_minmax(kmin, kmax, sh.red);  // (its barriers publish the gathered words)
   sort_words(sh, int(C), (static_cast<unsigned long long>(kmax) << 32) | 0xFFFFFFFFull,
-             static_cast<unsigned long long>(kmin) << 32, lo, hi, out);
+             static_cast<unsigned long long>(kmin) << 32, lo, hi, out, obase);
 }
+
+__global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int slices, int windows) {
+  __shared__ TopkShared sh;
+  const int r = blockIdx.x / windows, w = blockIdx.x % windows;
+  const int t = threadIdx.x;
+  const int n = row_len(a, r);
+  const int k = a.k;
+  const int k_eff = n < k ? n : k;
+  int32_t* out = a.idx + int64_t(r) * k;
+  if (w == 0)
+    for (int j = k_eff + t; j < k; j += kThreads) out[j] = -1;
+  const int lo = w * kWindow, hi = lo + kWindow < k_eff ? lo + kWindow : k_eff;
+  if (lo >= hi) return;
+  window_select(sh, a, r, slices, n, lo, hi, out, 0);
+}
+
+// Decode with selection and attention fused: the workgroup of (query r, key
+// split, head group) first selects the split's ranks [j_beg, j_end) exactly as
+// topk_window_kernel does (8 waves), into LDS and (head group 0) the index
+// output, then its waves 0..3 run the same attention core as the attention
+// kernel over those keys. Same split plan and same core: the same bits as
+// selection followed by the attention kernel on the recorded indices.
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnArgs aa, int slices, int splits,
+                                                             int kps) {
+  __shared__ union Shared {
+    TopkShared sel;
+    attn::Smem<F32> att;
+  } u;
+  __shared__ int s_idx[kMaxTopk];
+  const int HG = (aa.H + attn::kGroupHeads - 1) / attn::kGroupHeads;
+  int r, split, hg;
+  attn::map_block(blockIdx.x, aa.R, splits, HG, r, split, hg);
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t base = attn::seq_base(aa, r);
+  const int n = row_len(ta, r);
+  const int k = ta.k;
+  const int k_eff = n < k ? n : k;
+  const int j_beg = split * kps;
+  const int j_end = j_beg + kps < k ? j_beg + kps : k;
+  // ranks past k_eff, and the attention's chunk tail past j_end, stay -1
+  const int span = (j_end - j_beg + attn::kChunkKeys - 1) / attn::kChunkKeys * attn::kChunkKeys;
+  for (int i = t; i < span; i += kThreads) s_idx[i] = -1;
+  __syncthreads();
+  const int hi = j_end < k_eff ? j_end : k_eff;
+  if (j_beg < hi) window_select(u.sel, ta, r, slices, n, j_beg, hi, s_idx, j_beg);
+  __syncthreads();  // the split's indices are in LDS; the selection's LDS is free
+  if (hg == 0)
+    for (int i = t; i < j_end - j_beg; i += kThreads) ta.idx[int64_t(r) * k + j_beg + i] = s_idx[i];
+  if (wave >= 4) return;  // barriers below count the four attention waves only
+  // the query fragments now (a barrier waits for every outstanding load, so
+  // loaded earlier they would hold up the selection); they land while the
+  // first rows are gathered
+  attn::QFrag<F32> qf[18];
+  attn::load_q<F32>(aa, r, hg * attn::kGroupHeads + col, grp, qf);
+  attn::attend<F32>(aa, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, u.att);
+}
+
 
 }  // namespace
 
@@ -866,6 +923,17 @@ void topk_split_carve(void* ws, int R, int max_n, TopkArgs& a) {
   const size_t slices = size_t((max_n + kTile - 1) / kTile);
   a.cand = static_cast<unsigned long long*>(ws);
   a.state = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + size_t(R) * slices * kTile * sizeof(unsigned long long));
+}
+
+hipError_t launch_topk_attn(const TopkArgs& ta, const AttnArgs& aa, const AttnPlan& plan, hipStream_t stream) {
+  if (ta.R == 0) return hipSuccess;
+  const int slices = (ta.max_n + kTile - 1) / kTile;  // <= kThreads for rows up to 2^20 keys
+  topk_cand_kernel<<<dim3(unsigned(ta.R) * unsigned(slices)), kThreads, 0, stream>>>(ta, slices);
+  const dim3 grid(unsigned(aa.R) * unsigned(plan.splits) * unsigned(plan.head_groups));
+  topk_attn_kernel<false><<<grid, kThreads, 0, stream>>>(ta, aa, slices, plan.splits, plan.keys_per_split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn_combine(aa, plan, stream);
 }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {

@@ -333,6 +333,31 @@ def test_fused_decode_repeatable_and_replayable(dsa):
     C.assert_attn_close(out, ref_o, lse, ref_l)
 
 
+@pytest.mark.parametrize("lens,k", [([12000, 9000, 20000], 2048), ([30000], 1000),
+                                    ([9000, 16385, 12000, 10000, 9001], 512)])
+def test_fused_split_decode_matches_pipeline_and_replay(dsa, lens, k):
+    """Contexts past 8K take the split selection fused with the attention
+    (selection of each split's ranks, then attention over them, in one
+    workgroup): the same bits as the three entry points and as replaying the
+    recorded indices; k = 1000 leaves a partial last chunk."""
+    import torch
+    p = inputs.decode_config(lens, seed=11, k=k)
+    d = inputs.to_torch(p)
+    out, lse, idx = _fused(dsa, p, d)
+    scores, idx2, out2, lse2 = _pipeline(dsa, p)
+    assert np.array_equal(idx, idx2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    C.assert_index_invariants(idx, p.q_pos, p.k)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k)), f"row {r}"
+    rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale)
+    assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
+    rows = [0, p.R - 1]
+    ref_o, ref_l = O.sparse_mla(p, idx[rows], rows=rows)
+    C.assert_attn_close(out[rows], ref_o, lse[rows], ref_l)
+
+
 # ------------------------------------------------------------------------------
 # causal prefill form (one sequence, a query per position)
 # ------------------------------------------------------------------------------
