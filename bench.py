@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DSA decode tokens/s @32K ctx, k=2048; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFS = 2500.0  # dense bf16
 MALL_BYTES = 256 << 20
 
 
@@ -156,14 +157,91 @@ def cpu_baseline(p, budget_s: float):
     rows = 0
     t0 = time.perf_counter()
     while True:
-        O.dsa_forward(p, rows=[rows % p.R])
+        # decode: the rows in turn; prefill: positions spread over the sequence
+        r = rows % p.R if p.is_decode() else (rows * 2654435761) % p.R
+        O.dsa_forward(p, rows=[r])
         rows += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    what = (f"decode rows of the same workload (full indexer over {int(p.seq_len[0])} keys" if p.is_decode()
+            else f"query rows at spread positions of the same {int(p.R)}-token prefill (causal indexer")
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} decode rows of the same workload (full indexer over "
-                      f"{int(p.seq_len[0])} keys, stable-sort top-k, fp64 attention), {dt:.1f} s"}
+            "sample": f"{rows} {what}, stable-sort top-k, fp64 attention), {dt:.1f} s"}
+
+
+def prefill_flops(p):
+    """Algorithmic FLOPs of the causal indexer (2*H_I*D_I per query-key pair,
+    keys 0..t for query t) and of the sparse attention (2*H*(576+512) per
+    selected key, min(k, t+1) keys for query t)."""
+    T = int(p.R)
+    pairs = T * (T + 1) // 2
+    sel = sum(min(p.k, t + 1) for t in range(T))
+    return pairs * 2 * p.H_I * p.D_I, sel * 2 * p.H * (576 + 512)
+
+
+def prefill_bench(args, p):
+    """One step = the causal prefill pass of one sequence through the three
+    entry points (indexer scores for every query, top-k, sparse attention);
+    the roofline line is the indexer's, bound by the matrix cores."""
+    import torch
+    from sparse_attention_05_amd import dsa, inputs
+    d = inputs.to_torch(p, "cuda")
+    T = int(p.R)
+    ld = (T + 3) // 4 * 4
+    scores = torch.empty((T, ld), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, p.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, p.H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((T, p.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(dsa.dsa_workspace_size(dsa.DSA_ENTRY_SPARSE_MLA, T, 0, p.k, p.H), 256), dtype=torch.uint8,
+                     device="cuda")
+
+    def index():
+        dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, T, q_seq=d.q_seq, scores=scores)
+
+    def step():
+        index()
+        dsa.dsa_topk(scores, d.q_pos, T, p.k, idx_out=idx)
+        dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx, p.scale, q_seq=d.q_seq, out=out, lse=lse,
+                                workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    start.record()
+    for _ in range(args.steps):
+        index()
+    end.record()
+    torch.cuda.synchronize()
+    idx_us = start.elapsed_time(end) * 1e3 / args.steps
+    fl_idx, fl_att = prefill_flops(p)
+    achieved = fl_idx / (idx_us * 1e-6) / 1e12
+    log(f"bench: prefill {ms_step:.3f} ms/pass, indexer {idx_us:.1f} us = {achieved:.0f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        cpu = cpu_baseline(p, args.cpu_seconds)
+    rec = {
+        "metric": "DSA causal prefill tokens/s (one 8,192-token sequence, k=2048); indexer MFMA TFLOP/s vs peak",
+        "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": 1, "context": T, "k": p.k, "indexer_heads": p.H_I,
+                   "indexer_dim": p.D_I, "mla_heads": p.H, "latent_dim": 576},
+        "attention_tflops": fl_att / (ms_step * 1e-3) / 1e12,
+        "roofline": {"kernel": "index_scores_prefill", "bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFS, "traffic": None,
+                     "flops_per_launch": fl_idx, "us_per_launch": idx_us},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def main():
@@ -199,7 +277,8 @@ def main():
     log(f"bench: generating {args.workload}")
     p = inputs.workload(args.workload, seed=0)
     if not p.is_decode():
-        raise SystemExit("bench.py times decode workloads")
+        prefill_bench(args, p)
+        return
     max_len = int(p.seq_len.max())
     sb = step_bytes(p)
     n_sets = args.sets or max(2, math.ceil(2 * MALL_BYTES / sb))

@@ -54,6 +54,7 @@ struct AttnPlan {
   int keys_per_split;   // multiple of 64
   int head_groups;      // ceil(H / 16): one workgroup per (query, head group, split)
   size_t ws_bytes;      // partial-result workspace (0 when splits == 1)
+  bool wide;            // many queries, H <= 64, one split: bf16 runs one workgroup per query for all heads
 };
 AttnPlan plan_attention(int R, int H, int k);
 

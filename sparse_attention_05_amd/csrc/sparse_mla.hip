@@ -69,6 +69,321 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, in
   attend<F32>(a, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, sm);
 }
 
+// ---- many queries: one workgroup per query for all (<= 64) heads ---------------------
+// With a workgroup per (query, 16 heads) every selected latent row would be
+// gathered once per head group; here the 4 waves of one workgroup share each
+// gathered chunk of 64 rows among all 64 heads, so a row is read once per
+// query. Per chunk:
+//  * q.c split by head: wave w forms S^T for heads 16w .. 16w+15 over the 64
+//    keys (its query fragments stay in registers), so each head's maximum
+//    and sum stay within one wave; the maxima go through LDS to the p.c;
+//  * P^T (bf16) is written into the rope part (bytes 1024..1151) of the
+//    chunk's rows, free once q.c is done: head h's 64 probabilities go to
+//    row h, so no extra LDS is needed;
+//  * p.c split by value dimension as in the 16-head kernel: wave w forms
+//    O^T[128w .. 128w+127][all heads], each transposed value fragment feeding
+//    the 4 head tiles.
+// Rows go from HBM to LDS with direct loads issued from inline assembly and
+// waited for exactly, so the gather of chunk c+1 overlaps chunk c. Chunks
+// past the last selected position are skipped (they would add exactly 0).
+constexpr int kWideHeads = 64;
+
+// 16-byte direct-to-LDS load: lane l's 16 bytes land at LDS byte lds + 16*l.
+__device__ __forceinline__ void wide_dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// Wave `wave` starts the gather of rows 16*wave .. +15 of chunk c (keys
+// j_beg + 64c + ...; raw indices in s_idx) into buf; missing rows are
+// zero-filled. Returns the 16-bit mask of present rows.
+__device__ __forceinline__ uint32_t wide_issue(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
+                                               int wave, int lane) {
+  using Cfg = AttnCfg<false>;
+  int64_t src = -1;
+  if (lane < 16) {
+    const int s = s_idx[kChunkKeys * c + 16 * wave + lane];
+    const int64_t row = base + s;
+    if (s >= 0 && base >= 0 && row < a.cache_rows) src = row * Cfg::ROW_BYTES;
+  }
+  const uint32_t ok = uint32_t(__ballot(src >= 0)) & 0xFFFFu;
+  const uint32_t src_lo = uint32_t(uint64_t(src)), src_hi = uint32_t(uint64_t(src) >> 32);
+  const char* lat = static_cast<const char*>(a.latent);
+  char* wbuf = buf + 16 * wave * Cfg::ROW_BYTES;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)wbuf)));
+#pragma unroll
+  for (int m = 0; m < Cfg::WAVE_LOADS; ++m) {
+    const int rA = (64 * m) / Cfg::ROW_CHUNKS;
+    const int cut = Cfg::ROW_CHUNKS * (rA + 1) - 64 * m;
+    const int rB = rA + 1 < 16 ? rA + 1 : 15;
+    const bool inA = lane < cut;
+    const int rl = inA ? rA : rA + 1;
+    const int pc = 64 * m + lane - Cfg::ROW_CHUNKS * rl;
+    const int lc = pc ^ row_swz(rl);
+    const uint32_t loA = __builtin_amdgcn_readlane(src_lo, rA), loB = __builtin_amdgcn_readlane(src_lo, rB);
+    const uint32_t hiA = __builtin_amdgcn_readlane(src_hi, rA), hiB = __builtin_amdgcn_readlane(src_hi, rB);
+    int64_t so = int64_t((uint64_t(inA ? hiA : hiB) << 32) | (inA ? loA : loB));
+    // a missing row reads row 0 of the cache (always present), its LDS row
+    // is zero-filled below once the loads have landed
+    so = ((ok >> rl) & 1u) ? so : 0;
+    wide_dma16(lat + so + 16 * lc, lds0 + 1024 * m);
+  }
+  return ok;
+}
+
+__global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs a, int kps) {
+  using Cfg = AttnCfg<false>;
+  constexpr int WL = Cfg::WAVE_LOADS;  // direct loads per wave per chunk
+  __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::BUF_BYTES];
+  __shared__ int s_idx[kMaxTopk];
+  __shared__ float s_max[kWideHeads];
+  __shared__ float s_l[kWideHeads];
+  __shared__ uint32_t s_ok[2][4];
+  __shared__ int s_last[4];
+  const int r = int(gridDim.x) - 1 - int(blockIdx.x);  // later queries (more keys) first
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t base = seq_base(a, r);
+  const int j_end = kps < a.k ? kps : a.k;  // one split: keys 0 .. j_end-1
+
+  // the range's indices; the last selected position bounds the chunks walked
+  int last = -1;
+  for (int e = t; e < j_end; e += kAttnThreads) {
+    const int v = a.idx[int64_t(r) * a.k + e];
+    s_idx[e] = v;
+    last = v >= 0 ? e : last;
+  }
+  const int span = (j_end + kChunkKeys - 1) / kChunkKeys * kChunkKeys;
+  for (int e = j_end + t; e < span; e += kAttnThreads) s_idx[e] = -1;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) last = max(last, __shfl_xor(last, d, 64));
+  if (lane == 0) s_last[wave] = last;
+
+  // query fragments of this wave's q.c head 16*wave + col (zero past H)
+  bf16x8 qf[18];
+  {
+    const int h = 16 * wave + col;
+    const bool hv = h < a.H;
+    const int64_t qoff = (int64_t(r) * a.H + (hv ? h : 0)) * kLatentDim + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qoff + 32 * ks);
+      qf[ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
+    }
+  }
+  // every load above has landed; the fragments are re-defined through an
+  // empty asm, so that no wait for them is placed inside the chunk loop
+  // (where it would also wait for the next chunk's rows), and placed in
+  // accumulation registers (an MFMA reads its B operand from there too),
+  // which leaves the vector registers to the LDS fragments read ahead
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    uint4 u = __builtin_bit_cast(uint4, qf[ks]);
+    asm volatile("" : "+a"(u.x), "+a"(u.y), "+a"(u.z), "+a"(u.w));
+    qf[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+  __syncthreads();
+  const int nchunks = (max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])) + kChunkKeys) / kChunkKeys;
+
+  uint32_t okw[2] = {0u, 0u};
+  int issued = 0;
+  for (; issued < 2 && issued < nchunks; ++issued)
+    okw[issued] = wide_issue(a, base, s_idx, issued, smem + issued * Cfg::BUF_BYTES, wave, lane);
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int vt = 0; vt < 8; ++vt)
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[vt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mq = -INFINITY;  // running max of the q.c head 16*wave + col
+  float lq = 0.f;        // this lane's share of its running sum
+  float mo[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // of the p.c heads 16ht + col
+  const float scale2 = a.scale * kLog2e;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int bi = c & 1;
+    char* buf = smem + bi * Cfg::BUF_BYTES;
+    // this wave's rows of chunk c have landed (chunk c+1's loads may still
+    // be in flight); rows of missing keys are zeroed; then every wave's are
+    if (issued > c + 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (okw[bi] != 0xFFFFu) {
+      char* wbuf = buf + 16 * wave * Cfg::ROW_BYTES;
+      for (int q = lane; q < 16 * Cfg::ROW_CHUNKS; q += 64)
+        if (!((okw[bi] >> (q / Cfg::ROW_CHUNKS)) & 1u)) *reinterpret_cast<uint4*>(wbuf + 16 * q) = uint4{0u, 0u, 0u, 0u};
+    }
+    if (lane == 0) s_ok[bi][wave] = okw[bi];
+    __syncthreads();
+
+    // ---- q.c: S^T for keys 16kt + (0..15), heads 16*wave + (0..15) --------------------
+    // (the key fragments of K-step ks+1 are read while the MFMAs of ks run:
+    // one wave per SIMD has no other wave to hide the LDS latency)
+    f32x4 sc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const char* rows[4];
+      int sws[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        rows[kt] = buf + (16 * kt + col) * Cfg::ROW_BYTES;
+        sws[kt] = row_swz(16 * kt + col);
+      }
+      bf16x8 fa[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) fa[0][kt] = *reinterpret_cast<const bf16x8*>(rows[kt] + 16 * (grp ^ sws[kt]));
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        if (ks + 1 < 18) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            fa[(ks + 1) & 1][kt] =
+                *reinterpret_cast<const bf16x8*>(rows[kt] + 16 * ((4 * (ks + 1) + grp) ^ sws[kt]));
+        }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sc[kt] = mfma_k32(fa[ks & 1][kt], qf[ks], sc[kt]);
+        if (ks + 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+    }
+    // logits (log2 domain), -inf for missing keys; the head's maximum over the chunk
+    float x[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint32_t okt = s_ok[bi][kt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[kt][i] = ((okt >> (4 * grp + i)) & 1u) ? sc[kt][i] * scale2 : -INFINITY;
+        mx = fmaxf(mx, x[kt][i]);
+      }
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    if (grp == 0) s_max[16 * wave + col] = mx;
+    __syncthreads();  // maxima visible; every wave is done with q.c of chunk c (its rope parts are free)
+    // the next chunk's rows go into the other buffer (every wave is done with chunk c-1)
+    if (issued == c + 1 && issued < nchunks) {
+      okw[bi ^ 1] = wide_issue(a, base, s_idx, issued, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
+      ++issued;
+    }
+
+    // ---- softmax of this wave's heads: P^T into the rope part of row h -----------------
+    {
+      const int h = 16 * wave + col;
+      const float m_new = fmaxf(mq, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(mq - m_use);
+      float psum = 0.f;
+      char* prow = buf + h * Cfg::ROW_BYTES + 8 * (grp & 1);
+      const int hs = row_swz(h);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        __bf16 pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = static_cast<__bf16>(exp2f(x[kt][i] - m_use));
+          psum += static_cast<float>(pv[i]);
+        }
+        // keys 16kt + 4grp .. +3: rope chunk 64 + (2kt + grp/2), swizzled in its group
+        const int ch = 64 + ((2 * kt + (grp >> 1)) ^ hs);
+        const uint32_t w0 = uint32_t(__builtin_bit_cast(uint16_t, pv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[1])) << 16);
+        const uint32_t w1 = uint32_t(__builtin_bit_cast(uint16_t, pv[2])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[3])) << 16);
+        *reinterpret_cast<uint2*>(prow + 16 * ch) = uint2{w0, w1};
+      }
+      lq = lq * alpha + psum;
+      mq = m_new;
+    }
+    // rescale of the p.c accumulators by the same per-head alpha
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      const float cmax = s_max[16 * ht + col];
+      const float m_new = fmaxf(mo[ht], cmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(mo[ht] - m_use);
+      mo[ht] = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int vt = 0; vt < 8; ++vt) acc[vt][ht] *= alpha;
+      }
+    }
+    __syncthreads();  // P^T of all heads in LDS
+
+    // ---- O^T[128*wave + 16*vt + (0..15)][16*ht + (0..15)] += C^T . P^T ---------------
+    {
+      const int tr_row = 4 * grp + (col >> 2);
+      const int tr_sw = ((col >> 2) << 1) | (grp & 1);
+      // P^T of head 16ht + col for both K-steps: keys kb + 4grp .. +3 and kb + 16 + 4grp .. +3
+      bf16x8 pf[2][4];
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+          const int h = 16 * ht + col, kb = 32 * kq;
+          const char* prow = buf + h * Cfg::ROW_BYTES + 8 * (grp & 1);
+          const int hs = row_swz(h);
+          const uint2 plo = *reinterpret_cast<const uint2*>(prow + 16 * (64 + ((kb / 8 + (grp >> 1)) ^ hs)));
+          const uint2 phi = *reinterpret_cast<const uint2*>(prow + 16 * (64 + ((kb / 8 + 2 + (grp >> 1)) ^ hs)));
+          pf[kq][ht] = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
+        }
+      // transposed value fragment of step q = (kq, vt), read one step ahead
+      auto vfrag = [&](int q) -> bf16x8 {
+        const int kq = q >> 3, vt = q & 7;
+        const char* rp = buf + (32 * kq + tr_row) * Cfg::ROW_BYTES + 8 * (col & 1);
+        const int lc = 16 * wave + 2 * vt + ((col >> 1) & 1);
+        const char* p0 = rp + 16 * (lc ^ tr_sw);
+        const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(lds_ptr)p0);
+        const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + 16 * Cfg::ROW_BYTES));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vf[2];
+      vf[0] = vfrag(0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (q + 1 < 16) vf[(q + 1) & 1] = vfrag(q + 1);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) acc[q & 7][ht] = mfma_k32(vf[q & 1], pf[q >> 3][ht], acc[q & 7][ht]);
+        if (q + 1 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: row sums of each head, then O rows ----------------------------------------
+  {
+    float l = lq + wave_shfl_xor(lq, 16);
+    l += wave_shfl_xor(l, 32);
+    if (grp == 0) s_l[16 * wave + col] = l;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int h = 16 * ht + col;
+    if (h >= a.H) continue;
+    const float L = s_l[h];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const int64_t rh = int64_t(r) * a.H + h;
+    float* dst = a.out + rh * kValueDim;
+#pragma unroll
+    for (int vt = 0; vt < 8; ++vt)
+      *reinterpret_cast<float4*>(dst + 128 * wave + 16 * vt + 4 * grp) =
+          float4{acc[vt][ht][0] * inv, acc[vt][ht][1] * inv, acc[vt][ht][2] * inv, acc[vt][ht][3] * inv};
+    if (wave == 0 && grp == 0 && a.lse) a.lse[rh] = L > 0.f ? (mo[ht] + __log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
 // Merge key splits: O = sum_s e_s O_s / sum_s e_s l_s, e_s = 2^(m_s - max m),
 // splits with an empty sum skipped. P adjacent lanes share one output float4,
 // each lane loading and summing its SPL consecutive splits (all loads issued
@@ -160,6 +475,9 @@ AttnPlan plan_attention(int R, int H, int k) {
   splits = (k + kps - 1) / kps;
   p.splits = splits;
   p.keys_per_split = kps;
+  // many queries (two workgroups per CU even at one split): one workgroup per
+  // query for all heads (bf16)
+  p.wide = H <= kWideHeads && int64_t(R) * p.head_groups >= 2 * int64_t(target) && splits == 1;
   p.ws_bytes = splits > 1 ? size_t(R) * splits * H * (kValueDim + 2) * sizeof(float) : 0;
   p.ws_bytes = (p.ws_bytes + 255) / 256 * 256;
   return p;
@@ -167,6 +485,10 @@ AttnPlan plan_attention(int R, int H, int k) {
 
 hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
+  if (plan.wide && a.dtype != kF32) {
+    sparse_mla_wide_kernel<<<dim3(unsigned(a.R)), kAttnThreads, 0, stream>>>(a, plan.keys_per_split);
+    return hipGetLastError();
+  }
   const dim3 grid(unsigned(a.R) * unsigned(plan.splits) * unsigned(plan.head_groups));
   if (a.dtype == kF32) sparse_mla_kernel<true><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
   else sparse_mla_kernel<false><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
