@@ -101,47 +101,48 @@ __device__ __forceinline__ void wide_dma16(const void* src, uint32_t lds) {
       : "memory");
 }
 
-// Wave `wave` starts the gather of rows 16*wave .. +15 of chunk c (keys
-// j_beg + 64c + ...; raw indices in s_idx) into buf; missing rows are
-// zero-filled. Returns the 16-bit mask of present rows.
-__device__ __forceinline__ uint32_t wide_issue(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
-                                               int wave, int lane) {
+// LDS layout of a chunk (64 rows x 72 chunks of 16 bytes): wave w's rows
+// 16w .. 16w+15 form a block of 18,432 bytes in which chunk c of row p sits
+// at 1024*(c/4) + 64*p + 16*(c%4). The direct load m of a wave then covers
+// chunks 4m .. 4m+3 of all 16 rows: lane l always reads row l/4 (at 16-byte
+// offset 4m + l%4), so a gather needs one address per lane.
+constexpr int kWideBlock = 16 * 1152;
+__device__ __forceinline__ int wide_off(int row, int c) {
+  return kWideBlock * (row >> 4) + 1024 * (c >> 2) + 64 * (row & 15) + 16 * (c & 3);
+}
+
+// The gather of rows 16*wave .. +15 of chunk c (raw indices in s_idx) into
+// buf: this lane's source row (a missing row reads cache row 0 and is
+// zero-filled once it has landed), the LDS base of the wave's block and the
+// 16-bit mask of present rows; load m (0..17) is then wide_dma16(src + 64m,
+// lds + 1024m).
+struct WideGather {
+  const char* src;
+  uint32_t lds;
+  uint32_t mask;
+};
+__device__ __forceinline__ WideGather wide_gather(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
+                                                  int wave, int lane) {
   using Cfg = AttnCfg<false>;
-  int64_t src = -1;
-  if (lane < 16) {
-    const int s = s_idx[kChunkKeys * c + 16 * wave + lane];
-    const int64_t row = base + s;
-    if (s >= 0 && base >= 0 && row < a.cache_rows) src = row * Cfg::ROW_BYTES;
-  }
-  const uint32_t ok = uint32_t(__ballot(src >= 0)) & 0xFFFFu;
-  const uint32_t src_lo = uint32_t(uint64_t(src)), src_hi = uint32_t(uint64_t(src) >> 32);
-  const char* lat = static_cast<const char*>(a.latent);
-  char* wbuf = buf + 16 * wave * Cfg::ROW_BYTES;
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)wbuf)));
+  const int s = s_idx[kChunkKeys * c + 16 * wave + (lane >> 2)];
+  const int64_t row = base + s;
+  const bool ok = s >= 0 && base >= 0 && row < a.cache_rows;
+  const unsigned long long okm = __ballot(ok && (lane & 3) == 0);  // bit 4i: row i
+  uint32_t mask = 0;
 #pragma unroll
-  for (int m = 0; m < Cfg::WAVE_LOADS; ++m) {
-    const int rA = (64 * m) / Cfg::ROW_CHUNKS;
-    const int cut = Cfg::ROW_CHUNKS * (rA + 1) - 64 * m;
-    const int rB = rA + 1 < 16 ? rA + 1 : 15;
-    const bool inA = lane < cut;
-    const int rl = inA ? rA : rA + 1;
-    const int pc = 64 * m + lane - Cfg::ROW_CHUNKS * rl;
-    const int lc = pc ^ row_swz(rl);
-    const uint32_t loA = __builtin_amdgcn_readlane(src_lo, rA), loB = __builtin_amdgcn_readlane(src_lo, rB);
-    const uint32_t hiA = __builtin_amdgcn_readlane(src_hi, rA), hiB = __builtin_amdgcn_readlane(src_hi, rB);
-    int64_t so = int64_t((uint64_t(inA ? hiA : hiB) << 32) | (inA ? loA : loB));
-    // a missing row reads row 0 of the cache (always present), its LDS row
-    // is zero-filled below once the loads have landed
-    so = ((ok >> rl) & 1u) ? so : 0;
-    wide_dma16(lat + so + 16 * lc, lds0 + 1024 * m);
-  }
-  return ok;
+  for (int i = 0; i < 16; ++i) mask |= uint32_t((okm >> (4 * i)) & 1ull) << i;
+  WideGather g;
+  g.src = static_cast<const char*>(a.latent) + (ok ? row : 0) * Cfg::ROW_BYTES + 16 * (lane & 3);
+  g.lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(buf + kWideBlock * wave))));
+  g.mask = mask;
+  return g;
 }
 
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs a, int kps) {
   using Cfg = AttnCfg<false>;
   constexpr int WL = Cfg::WAVE_LOADS;  // direct loads per wave per chunk
+  static_assert(WL == 18, "one direct load of the next chunk per K-step of q.c");
   __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::BUF_BYTES];
   __shared__ int s_idx[kMaxTopk];
   __shared__ float s_max[kWideHeads];
@@ -196,10 +197,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
   __syncthreads();
   const int nchunks = (max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])) + kChunkKeys) / kChunkKeys;
 
+  // chunk 0 now; chunk c+1 is issued during the q.c of chunk c, one direct
+  // load per K-step, once every wave is done with the buffer (chunk c-1's)
   uint32_t okw[2] = {0u, 0u};
-  int issued = 0;
-  for (; issued < 2 && issued < nchunks; ++issued)
-    okw[issued] = wide_issue(a, base, s_idx, issued, smem + issued * Cfg::BUF_BYTES, wave, lane);
+  if (nchunks > 0) {
+    const WideGather g = wide_gather(a, base, s_idx, 0, smem, wave, lane);
+#pragma unroll
+    for (int m = 0; m < WL; ++m) wide_dma16(g.src + 64 * m, g.lds + 1024 * m);
+    okw[0] = g.mask;
+  }
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -214,17 +220,20 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
   for (int c = 0; c < nchunks; ++c) {
     const int bi = c & 1;
     char* buf = smem + bi * Cfg::BUF_BYTES;
-    // this wave's rows of chunk c have landed (chunk c+1's loads may still
-    // be in flight); rows of missing keys are zeroed; then every wave's are
-    if (issued > c + 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(WL) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this wave's rows of chunk c have landed (nothing else is in flight);
+    // rows of missing keys are zeroed; then every wave's are
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (okw[bi] != 0xFFFFu) {
-      char* wbuf = buf + 16 * wave * Cfg::ROW_BYTES;
-      for (int q = lane; q < 16 * Cfg::ROW_CHUNKS; q += 64)
-        if (!((okw[bi] >> (q / Cfg::ROW_CHUNKS)) & 1u)) *reinterpret_cast<uint4*>(wbuf + 16 * q) = uint4{0u, 0u, 0u, 0u};
+      for (int q = lane; q < 16 * Cfg::ROW_CHUNKS; q += 64) {
+        const int rr = q / Cfg::ROW_CHUNKS, cc = q % Cfg::ROW_CHUNKS;
+        if (!((okw[bi] >> rr) & 1u)) *reinterpret_cast<uint4*>(buf + wide_off(16 * wave + rr, cc)) = uint4{0u, 0u, 0u, 0u};
+      }
     }
     if (lane == 0) s_ok[bi][wave] = okw[bi];
     __syncthreads();
+    const bool more = c + 1 < nchunks;
+    WideGather gn{nullptr, 0u, 0u};
+    if (more) gn = wide_gather(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
 
     // ---- q.c: S^T for keys 16kt + (0..15), heads 16*wave + (0..15) --------------------
     // (the key fragments of K-step ks+1 are read while the MFMAs of ks run:
@@ -233,26 +242,22 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      const char* rows[4];
-      int sws[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        rows[kt] = buf + (16 * kt + col) * Cfg::ROW_BYTES;
-        sws[kt] = row_swz(16 * kt + col);
-      }
+      // key row 16kt + col, dims 32ks + 8grp .. +8: chunk 4ks + grp, one contiguous KiB per read
+      const char* fbase = buf + 64 * col + 16 * grp;
       bf16x8 fa[2][4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) fa[0][kt] = *reinterpret_cast<const bf16x8*>(rows[kt] + 16 * (grp ^ sws[kt]));
+      for (int kt = 0; kt < 4; ++kt) fa[0][kt] = *reinterpret_cast<const bf16x8*>(fbase + kWideBlock * kt);
+      __builtin_amdgcn_sched_barrier(0);  // the pattern below starts with the reads of K-step 1
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
         if (ks + 1 < 18) {
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
-            fa[(ks + 1) & 1][kt] =
-                *reinterpret_cast<const bf16x8*>(rows[kt] + 16 * ((4 * (ks + 1) + grp) ^ sws[kt]));
+            fa[(ks + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(fbase + kWideBlock * kt + 1024 * (ks + 1));
         }
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) sc[kt] = mfma_k32(fa[ks & 1][kt], qf[ks], sc[kt]);
+        if (more) wide_dma16(gn.src + 64 * ks, gn.lds + 1024 * ks);  // load ks of chunk c+1
         if (ks + 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
@@ -273,11 +278,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
     if (grp == 0) s_max[16 * wave + col] = mx;
     __syncthreads();  // maxima visible; every wave is done with q.c of chunk c (its rope parts are free)
-    // the next chunk's rows go into the other buffer (every wave is done with chunk c-1)
-    if (issued == c + 1 && issued < nchunks) {
-      okw[bi ^ 1] = wide_issue(a, base, s_idx, issued, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
-      ++issued;
-    }
+    okw[bi ^ 1] = gn.mask;
 
     // ---- softmax of this wave's heads: P^T into the rope part of row h -----------------
     {
@@ -286,8 +287,6 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = exp2f(mq - m_use);
       float psum = 0.f;
-      char* prow = buf + h * Cfg::ROW_BYTES + 8 * (grp & 1);
-      const int hs = row_swz(h);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         __bf16 pv[4];
@@ -296,11 +295,11 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
           pv[i] = static_cast<__bf16>(exp2f(x[kt][i] - m_use));
           psum += static_cast<float>(pv[i]);
         }
-        // keys 16kt + 4grp .. +3: rope chunk 64 + (2kt + grp/2), swizzled in its group
-        const int ch = 64 + ((2 * kt + (grp >> 1)) ^ hs);
+        // keys 16kt + 4grp .. +3 of head h: rope chunk 64 + 2kt + grp/2 of row h, half grp&1
+        const int ch = 64 + 2 * kt + (grp >> 1);
         const uint32_t w0 = uint32_t(__builtin_bit_cast(uint16_t, pv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[1])) << 16);
         const uint32_t w1 = uint32_t(__builtin_bit_cast(uint16_t, pv[2])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[3])) << 16);
-        *reinterpret_cast<uint2*>(prow + 16 * ch) = uint2{w0, w1};
+        *reinterpret_cast<uint2*>(buf + wide_off(h, ch) + 8 * (grp & 1)) = uint2{w0, w1};
       }
       lq = lq * alpha + psum;
       mq = m_new;
@@ -323,7 +322,6 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
     // ---- O^T[128*wave + 16*vt + (0..15)][16*ht + (0..15)] += C^T . P^T ---------------
     {
       const int tr_row = 4 * grp + (col >> 2);
-      const int tr_sw = ((col >> 2) << 1) | (grp & 1);
       // P^T of head 16ht + col for both K-steps: keys kb + 4grp .. +3 and kb + 16 + 4grp .. +3
       bf16x8 pf[2][4];
 #pragma unroll
@@ -331,25 +329,25 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
           const int h = 16 * ht + col, kb = 32 * kq;
-          const char* prow = buf + h * Cfg::ROW_BYTES + 8 * (grp & 1);
-          const int hs = row_swz(h);
-          const uint2 plo = *reinterpret_cast<const uint2*>(prow + 16 * (64 + ((kb / 8 + (grp >> 1)) ^ hs)));
-          const uint2 phi = *reinterpret_cast<const uint2*>(prow + 16 * (64 + ((kb / 8 + 2 + (grp >> 1)) ^ hs)));
+          const uint2 plo = *reinterpret_cast<const uint2*>(buf + wide_off(h, 64 + kb / 8 + (grp >> 1)) + 8 * (grp & 1));
+          const uint2 phi = *reinterpret_cast<const uint2*>(buf + wide_off(h, 64 + kb / 8 + 2 + (grp >> 1)) + 8 * (grp & 1));
           pf[kq][ht] = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
         }
       // transposed value fragment of step q = (kq, vt), read one step ahead
+      // lane (col, grp) names key row 32kq + tr_row (+16 for the second
+      // read), value dims 128*wave + 16vt + 4(col%4) .. +3: chunk
+      // 16*wave + 2vt + (col%4)/2, half (col%4)&1
       auto vfrag = [&](int q) -> bf16x8 {
         const int kq = q >> 3, vt = q & 7;
-        const char* rp = buf + (32 * kq + tr_row) * Cfg::ROW_BYTES + 8 * (col & 1);
-        const int lc = 16 * wave + 2 * vt + ((col >> 1) & 1);
-        const char* p0 = rp + 16 * (lc ^ tr_sw);
+        const char* p0 = buf + wide_off(32 * kq + tr_row, 16 * wave + 2 * vt + ((col & 3) >> 1)) + 8 * (col & 1);
         const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(lds_ptr)p0);
         const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + 16 * Cfg::ROW_BYTES));
+            (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + kWideBlock));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8 vf[2];
       vf[0] = vfrag(0);
+      __builtin_amdgcn_sched_barrier(0);  // the pattern below starts with the reads of step 1
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         if (q + 1 < 16) vf[(q + 1) & 1] = vfrag(q + 1);
