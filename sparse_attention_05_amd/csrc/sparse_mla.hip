@@ -139,6 +139,16 @@ __device__ __forceinline__ WideGather wide_gather(const AttnArgs& a, int64_t bas
   return g;
 }
 
+// Reference maximum of a head's running softmax (log2 domain) after a chunk
+// whose maximum is cmax: it moves (and the output accumulators are rescaled)
+// only when cmax exceeds it by more than 8, so probabilities stay <= 2^8
+// (exact in bf16's range, summed in fp32) and the 128-register rescale is
+// rare. The softmax stays exact: sums and outputs use the same reference,
+// the LSE adds it back.
+__device__ __forceinline__ float wide_ref_max(float m_run, float cmax) {
+  return (m_run == -INFINITY || cmax > m_run + 8.f) ? fmaxf(m_run, cmax) : m_run;
+}
+
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs a, int kps) {
   using Cfg = AttnCfg<false>;
   constexpr int WL = Cfg::WAVE_LOADS;  // direct loads per wave per chunk
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
     // ---- softmax of this wave's heads: P^T into the rope part of row h -----------------
     {
       const int h = 16 * wave + col;
-      const float m_new = fmaxf(mq, mx);
+      const float m_new = wide_ref_max(mq, mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = exp2f(mq - m_use);
       float psum = 0.f;
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
       const float cmax = s_max[16 * ht + col];
-      const float m_new = fmaxf(mo[ht], cmax);
+      const float m_new = wide_ref_max(mo[ht], cmax);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = exp2f(mo[ht] - m_use);
       mo[ht] = m_new;

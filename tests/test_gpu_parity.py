@@ -249,6 +249,27 @@ def test_attention_holes_and_empty_rows(dsa):
     C.assert_attn_close(out[:3], ref[:3], lse[:3], lse_ref[:3])
 
 
+@pytest.mark.parametrize("std,k", [(1.0, 512), (30.0, 512), (3.0, 200)])
+def test_attention_many_queries_matches_oracle(dsa, std, k):
+    """Enough queries for the one-workgroup-per-query (all heads) kernel:
+    several 64-key chunks, holes anywhere, one empty row, a peaked softmax
+    (q_abs std 30) and a key count that leaves a partial last chunk."""
+    p = inputs.decode_config([600] * 160, seed=12, H=64, k=k, q_abs_std=std)
+    rng = np.random.default_rng(int(std * 10) + k)
+    idx = np.full((p.R, k), -1, np.int32)
+    for r in range(p.R):
+        idx[r] = rng.choice(600, size=k, replace=False)
+    idx[rng.random(idx.shape) < 0.2] = -1      # holes anywhere
+    idx[5] = -1                                # a row with no valid key
+    idx[7, k // 2:] = -1                       # a row whose selection stops half way
+    out, lse = _gpu_attn(dsa, p, idx)
+    rows = [0, 5, 7, 80, p.R - 1]
+    ref, lse_ref = O.sparse_mla(p, idx[rows], rows=rows)
+    assert (out[5] == 0).all() and np.isneginf(lse[5]).all()
+    keep = [0, 2, 3, 4]
+    C.assert_attn_close(out[rows][keep], ref[keep], lse[rows][keep], lse_ref[keep])
+
+
 # ------------------------------------------------------------------------------
 # whole path
 # ------------------------------------------------------------------------------
