@@ -312,6 +312,34 @@ def main():
     tok_s = p.B / (ms_step * 1e-3)
     log(f"bench: {ms_step * 1e3:.2f} us/step, {tok_s:,.0f} tokens/s (wall {wall:.3f} s)")
 
+    # ---- the same steps captured in a HIP graph (launch gaps vs kernel time) -------------
+    graph_ms, graph_same = None, None
+    try:
+        ref = [tuple(x.clone() for x in c()) for c in calls]
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        reps = max(1, args.steps // n_sets)
+        g.replay()
+        torch.cuda.synchronize()
+        graph_same = all(torch.equal(a, b) for c, r in zip(calls, ref) for a, b in zip((c.out, c.lse, c.idx), r))
+        start.record()
+        for _ in range(reps):
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        graph_ms = start.elapsed_time(end) / (reps * n_sets)
+        g.replay()
+        torch.cuda.synchronize()
+        graph_same = graph_same and all(
+            torch.equal(a, b) for c, r in zip(calls, ref) for a, b in zip((c.out, c.lse, c.idx), r))
+        del g
+        log(f"bench: graph-captured {graph_ms * 1e3:.2f} us/step (replays equal to eager: {graph_same})")
+    except Exception as e:  # capture unsupported here: report it, keep the eager numbers
+        log(f"bench: graph capture failed: {e}")
+
     # ---- the dominant kernel alone: K back-to-back indexer launches ----------------------
     scores = [torch.empty((p.B, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
     for i in range(min(args.warmup, n_sets)):
@@ -345,6 +373,7 @@ def main():
                    "indexer_heads": p.H_I, "indexer_dim": p.D_I, "indexer_keys": p.key_dtype,
                    "mla_heads": p.H, "latent_dim": 576, "input_sets": n_sets},
         "step_hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
+        "graph_ms_per_step": graph_ms, "graph_replays_equal_eager": graph_same,
         "step_algorithmic_bytes": sb,
         "deterministic": deterministic,
         "roofline": {"kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
