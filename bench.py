@@ -340,6 +340,35 @@ def main():
     except Exception as e:  # capture unsupported here: report it, keep the eager numbers
         log(f"bench: graph capture failed: {e}")
 
+    # ---- cross-layer index reuse: a block of 4 layers shares one selection -------------
+    # Layer 0 runs the fused step (indexer, top-k, attention) and records its
+    # indices; layers 1..3 run only the sparse attention over those indices,
+    # each with its own queries and latent cache (another input set's).
+    share_layers = 4
+    outs = [(torch.empty_like(calls[0].out), torch.empty_like(calls[0].lse)) for _ in range(share_layers - 1)]
+    aws = torch.empty(max(dsa.dsa_workspace_size(dsa.DSA_ENTRY_SPARSE_MLA, p.B, 0, p.k, p.H), 256),
+                      dtype=torch.uint8, device="cuda")
+
+    def block(i):
+        c = calls[i % n_sets]
+        c()
+        for l in range(1, share_layers):
+            d = sets[(i + l) % n_sets]
+            dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, c.idx, p.scale, out=outs[l - 1][0],
+                                    lse=outs[l - 1][1], workspace=aws)
+
+    for i in range(min(args.warmup, n_sets)):
+        block(i)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        block(i)
+    end.record()
+    torch.cuda.synchronize()
+    block_ms = start.elapsed_time(end) / args.steps
+    log(f"bench: index-shared block of {share_layers} layers {block_ms * 1e3:.2f} us "
+        f"(vs {share_layers} fused steps {share_layers * ms_step * 1e3:.2f} us)")
+
     # ---- the dominant kernel alone: K back-to-back indexer launches ----------------------
     scores = [torch.empty((p.B, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
     for i in range(min(args.warmup, n_sets)):
@@ -374,6 +403,9 @@ def main():
                    "mla_heads": p.H, "latent_dim": 576, "input_sets": n_sets},
         "step_hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
         "graph_ms_per_step": graph_ms, "graph_replays_equal_eager": graph_same,
+        "index_share": {"layers": share_layers, "ms_per_block": block_ms,
+                        "tokens_per_s_per_block": p.B / (block_ms * 1e-3),
+                        "speedup_vs_independent_layers": share_layers * ms_step / block_ms},
         "step_algorithmic_bytes": sb,
         "deterministic": deterministic,
         "roofline": {"kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
