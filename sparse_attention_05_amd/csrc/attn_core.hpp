@@ -195,18 +195,32 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
       const char* rp = buf + (16 * wave + col) * Cfg::ROW_BYTES;
       const int sw = row_swz(col);
       f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if constexpr (F32) {
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        if constexpr (F32) {
+        for (int ks = 0; ks < 18; ++ks) {
           const int c0 = 8 * ks + 2 * grp;
           const float4 x = *reinterpret_cast<const float4*>(rp + 16 * (c0 ^ sw));
           const float4 y = *reinterpret_cast<const float4*>(rp + 16 * ((c0 + 1) ^ sw));
           const f32x8 af{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
           part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
-        } else {
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(rp + 16 * ((4 * ks + grp) ^ sw));
-          part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
         }
+      } else {
+        // key fragments read four K-steps ahead of their MFMA (a wave has its
+        // SIMD to itself here: nothing else hides the LDS latency)
+        constexpr int D = 4;
+        bf16x8 fr[D];
+#pragma unroll
+        for (int i = 0; i < D; ++i) fr[i] = *reinterpret_cast<const bf16x8*>(rp + 16 * ((4 * i + grp) ^ sw));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          const bf16x8 af = fr[ks % D];
+          if (ks + D < 18) fr[ks % D] = *reinterpret_cast<const bf16x8*>(rp + 16 * ((4 * (ks + D) + grp) ^ sw));
+          part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
+          if (ks + D < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
       sacc = part[0] + part[1];
     }
@@ -276,24 +290,39 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
       // v0 + s of rows kb + 4*grp + 0..3.
       const int tr_row = 4 * grp + (col >> 2);
       const int tr_sw = ((col >> 2) << 1) | (grp & 1);  // row_swz of every row this lane names
+      bf16x8 pf[2];
 #pragma unroll
-      for (int kb = 0; kb < kChunkKeys; kb += 32) {
-        const PT* pp = s_p + col * kPRow + kb + 4 * grp;
+      for (int kq = 0; kq < 2; ++kq) {
+        const PT* pp = s_p + col * kPRow + 32 * kq + 4 * grp;
         const uint2 plo = *reinterpret_cast<const uint2*>(pp);
         const uint2 phi = *reinterpret_cast<const uint2*>(pp + 16);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
-        const char* rp = buf + (kb + tr_row) * Cfg::ROW_BYTES + 8 * (col & 1);
-#pragma unroll
-        for (int vt = 0; vt < 8; ++vt) {
-          const int lc = 16 * wave + 2 * vt + ((col >> 1) & 1);
-          const char* p0 = rp + 16 * (lc ^ tr_sw);
-          const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(lds_ptr)p0);
-          const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + 16 * Cfg::ROW_BYTES));
-          const bf16x8 af = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[vt] = mfma_k32(af, pf, acc[vt]);
-        }
+        pf[kq] = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
       }
+      // value fragment of step q = (kb = 32*(q/8), vt = q%8), read three steps ahead
+      auto vfrag = [&](int q) -> bf16x8 {
+        const int kb = 32 * (q >> 3), vt = q & 7;
+        const char* rp = buf + (kb + tr_row) * Cfg::ROW_BYTES + 8 * (col & 1);
+        const int lc = 16 * wave + 2 * vt + ((col >> 1) & 1);
+        const char* p0 = rp + 16 * (lc ^ tr_sw);
+        const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(lds_ptr)p0);
+        const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + 16 * Cfg::ROW_BYTES));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int D = 3;
+      bf16x8 vr[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) vr[i] = vfrag(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const bf16x8 af = vr[q % D];
+        if (q + D < 16) vr[q % D] = vfrag(q + D);
+        acc[q & 7] = mfma_k32(af, pf[q >> 3], acc[q & 7]);
+        if (q + D < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
