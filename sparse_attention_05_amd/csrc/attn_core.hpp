@@ -39,17 +39,49 @@ static_assert(AttnCfg<false>::ROW_CHUNKS % 8 == 0 && AttnCfg<true>::ROW_CHUNKS %
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// 16-byte direct-to-LDS load issued from inline assembly: lane l's 16 bytes
+// land at LDS byte lds + 16*l (lds wave-uniform). The compiler does not see
+// these loads, so it adds no waits for them: every use waits explicitly
+// (vm_wait_all), and it never holds an LDS read of one buffer behind the
+// loads into another.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// Wait until every vector memory operation of this wave has completed.
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p))));
+}
+
 // Chunk permutation of key row r (see the header comment).
 __device__ __forceinline__ int row_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
-// Wave `wave` starts the gather of its 16 rows of chunk c: keys
+// The gather of wave `wave`'s 16 rows of chunk c: keys
 // j_beg + 64c + 16*wave + (0..15), whose raw indices the wave left in
-// s_idx[64c + 16*wave + i] (-1 past the range). Rows of missing keys (idx < 0,
-// outside the cache) are zero-filled. Returns the 16-bit mask of present keys
-// (bit i: row 16*wave + i of the chunk).
+// s_idx[64c + 16*wave + i] (-1 past the range). gather_plan reads the indices
+// and zero-fills the rows of missing keys (idx < 0, outside the cache);
+// gather_load(m) then issues the wave's direct load m (0 .. WAVE_LOADS-1),
+// so the loads of a chunk can be spread over other work.
+struct Gather {
+  uint32_t src_lo, src_hi;  // lanes < 16: byte offset in the cache of row i (-1: missing)
+  uint32_t ok;              // 16-bit mask of present rows (bit i: row 16*wave + i of the chunk)
+  char* wbuf;               // the wave's block of the buffer
+};
+
 template <bool F32>
-__device__ __forceinline__ uint32_t issue_chunk(const AttnArgs& a, int64_t base, const int* s_idx, int c,
-                                                char* buf, int wave, int lane) {
+__device__ __forceinline__ Gather gather_plan(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
+                                              int wave, int lane) {
   using Cfg = AttnCfg<F32>;
   int64_t src = -1;
   if (lane < 16) {
@@ -57,31 +89,127 @@ __device__ __forceinline__ uint32_t issue_chunk(const AttnArgs& a, int64_t base,
     const int64_t row = base + s;
     if (s >= 0 && base >= 0 && row < a.cache_rows) src = row * Cfg::ROW_BYTES;
   }
-  const uint32_t ok = uint32_t(__ballot(src >= 0)) & 0xFFFFu;
-  const uint32_t src_lo = uint32_t(uint64_t(src)), src_hi = uint32_t(uint64_t(src) >> 32);
-  const char* lat = static_cast<const char*>(a.latent);
-  char* wbuf = buf + 16 * wave * Cfg::ROW_BYTES;
-#pragma unroll
-  for (int m = 0; m < Cfg::WAVE_LOADS; ++m) {
-    // the 64 chunks of this load span rows rA (lanes < cut) and rA + 1
-    const int rA = (64 * m) / Cfg::ROW_CHUNKS;
-    const int cut = Cfg::ROW_CHUNKS * (rA + 1) - 64 * m;
-    const int rB = rA + 1 < 16 ? rA + 1 : 15;
-    const bool inA = lane < cut;
-    const int rl = inA ? rA : rA + 1;
-    const int pc = 64 * m + lane - Cfg::ROW_CHUNKS * rl;  // physical chunk in the row
-    const int lc = pc ^ row_swz(rl);                      // logical chunk it holds
-    const uint32_t loA = __builtin_amdgcn_readlane(src_lo, rA), loB = __builtin_amdgcn_readlane(src_lo, rB);
-    const uint32_t hiA = __builtin_amdgcn_readlane(src_hi, rA), hiB = __builtin_amdgcn_readlane(src_hi, rB);
-    const int64_t so = int64_t((uint64_t(inA ? hiA : hiB) << 32) | (inA ? loA : loB));
-    if ((ok >> rl) & 1u)
-      __builtin_amdgcn_global_load_lds(lat + so + 16 * lc, (lds_ptr)(wbuf + 1024 * m), 16, 0, 0);
-  }
-  if (ok != 0xFFFFu) {
+  Gather g;
+  g.ok = uint32_t(__ballot(src >= 0)) & 0xFFFFu;
+  g.src_lo = uint32_t(uint64_t(src));
+  g.src_hi = uint32_t(uint64_t(src) >> 32);
+  g.wbuf = buf + 16 * wave * Cfg::ROW_BYTES;
+  if (g.ok != 0xFFFFu) {
     for (int q = lane; q < 16 * Cfg::ROW_CHUNKS; q += 64)
-      if (!((ok >> (q / Cfg::ROW_CHUNKS)) & 1u)) *reinterpret_cast<uint4*>(wbuf + 16 * q) = uint4{0u, 0u, 0u, 0u};
+      if (!((g.ok >> (q / Cfg::ROW_CHUNKS)) & 1u)) *reinterpret_cast<uint4*>(g.wbuf + 16 * q) = uint4{0u, 0u, 0u, 0u};
   }
-  return ok;
+  return g;
+}
+
+// Direct load m of a planned gather: the 64 16-byte pieces of rows rA (lanes
+// < cut) and rA + 1, each landing at its permuted place in the row (the
+// compiler's builtin, which the compiler waits for itself).
+template <bool F32>
+__device__ __forceinline__ void gather_load(const AttnArgs& a, const Gather& g, int m, int lane) {
+  using Cfg = AttnCfg<F32>;
+  const int rA = (64 * m) / Cfg::ROW_CHUNKS;
+  const int cut = Cfg::ROW_CHUNKS * (rA + 1) - 64 * m;
+  const int rB = rA + 1 < 16 ? rA + 1 : 15;
+  const bool inA = lane < cut;
+  const int rl = inA ? rA : rA + 1;
+  const int pc = 64 * m + lane - Cfg::ROW_CHUNKS * rl;  // physical chunk in the row
+  const int lc = pc ^ row_swz(rl);                      // logical chunk it holds
+  const uint32_t loA = __builtin_amdgcn_readlane(g.src_lo, rA), loB = __builtin_amdgcn_readlane(g.src_lo, rB);
+  const uint32_t hiA = __builtin_amdgcn_readlane(g.src_hi, rA), hiB = __builtin_amdgcn_readlane(g.src_hi, rB);
+  const int64_t so = int64_t((uint64_t(inA ? hiA : hiB) << 32) | (inA ? loA : loB));
+  const char* src = static_cast<const char*>(a.latent) + so + 16 * lc;
+  if ((g.ok >> rl) & 1u) __builtin_amdgcn_global_load_lds(src, (lds_ptr)(g.wbuf + 1024 * m), 16, 0, 0);
+}
+
+// bf16 chunks use the block layout instead: wave w's rows 16w .. 16w+15 form
+// a block of 18,432 bytes in which 16-byte piece p of row i sits at
+// 1024*(p/4) + 64*i + 16*(p%4) (blk_off). Lane l then always loads row
+// 16w + l/4, pieces 4m + l%4 for m = 0 .. 17: load m is the lane's row
+// pointer plus 64m into the block at 1024m, so the 18 loads of a chunk can be
+// spread over other work at the cost of one 64-bit add each.
+constexpr int kBlock = 16 * 1152;
+__device__ __forceinline__ int blk_off(int row, int p) {
+  return kBlock * (row >> 4) + 1024 * (p >> 2) + 64 * (row & 15) + 16 * (p & 3);
+}
+
+struct BGather {
+  const char* src;  // this lane's row + 16*(lane%4) (row 0 when missing: not loaded)
+  uint32_t lds;     // LDS address of the wave's block
+  bool live;        // this lane's row is present
+  uint32_t ok;      // 16-bit mask of present rows
+};
+
+__device__ __forceinline__ BGather bgather_plan(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
+                                                int wave, int lane) {
+  const int s = s_idx[kChunkKeys * c + 16 * wave + (lane >> 2)];
+  const int64_t row = base + s;
+  BGather g;
+  g.live = s >= 0 && base >= 0 && row < a.cache_rows;
+  const unsigned long long okm = __ballot(g.live && (lane & 3) == 0);  // bit 4i: row i
+  uint32_t ok = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ok |= uint32_t((okm >> (4 * i)) & 1ull) << i;
+  g.ok = ok;
+  g.src = static_cast<const char*>(a.latent) + (g.live ? row : 0) * 1152 + 16 * (lane & 3);
+  char* blk = buf + kBlock * wave;
+  g.lds = lds_addr(blk);
+  if (!g.live) {
+#pragma unroll
+    for (int m = 0; m < 18; ++m) *reinterpret_cast<uint4*>(blk + 1024 * m + 16 * lane) = uint4{0u, 0u, 0u, 0u};
+  }
+  return g;
+}
+
+__device__ __forceinline__ void bgather_load(const BGather& g, int m) {
+  const char* p = g.src;
+  asm volatile("" : "+v"(p));  // the address is formed here, not hoisted into 18 live pairs
+  if (g.live) dma16(p + 64 * m, g.lds + 1024 * m);
+}
+
+__device__ __forceinline__ uint32_t bgather_all(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
+                                                int wave, int lane) {
+  const BGather g = bgather_plan(a, base, s_idx, c, buf, wave, lane);
+#pragma unroll
+  for (int m = 0; m < 18; ++m) bgather_load(g, m);
+  return g.ok;
+}
+
+// The whole gather of chunk c at once; returns the mask of present rows.
+template <bool F32>
+__device__ __forceinline__ uint32_t issue_chunk(const AttnArgs& a, int64_t base, const int* s_idx, int c,
+                                                char* buf, int wave, int lane) {
+  const Gather g = gather_plan<F32>(a, base, s_idx, c, buf, wave, lane);
+#pragma unroll
+  for (int m = 0; m < AttnCfg<F32>::WAVE_LOADS; ++m) gather_load<F32>(a, g, m, lane);
+  return g.ok;
+}
+
+// bf16 logits of this wave's 16 keys of the chunk: S^T = C[16 x 576] . Q^T.
+// Lane (col, grp) reads piece 4ks + grp of row col of the wave's block (at
+// blk + 64*col + 16*grp + 1024*ks: each K-step reads 1 KiB contiguously),
+// four K-steps ahead of its MFMA (a wave has its SIMD to itself: nothing
+// else hides the LDS latency). LOADS: direct load ks of the next chunk's
+// gather rides on K-step ks, so those loads go out while this chunk is
+// computed.
+template <bool LOADS>
+__device__ __forceinline__ f32x4 qc_bf16(const char* rp, const bf16x8 (&qf)[18], const BGather& gn) {
+  f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  constexpr int D = 4;
+  bf16x8 fr[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) fr[i] = *reinterpret_cast<const bf16x8*>(rp + 1024 * i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    const bf16x8 af = fr[ks % D];
+    if (ks + D < 18) fr[ks % D] = *reinterpret_cast<const bf16x8*>(rp + 1024 * (ks + D));
+    part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
+    if constexpr (LOADS) bgather_load(gn, ks);
+    if (ks + D < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return part[0] + part[1];
 }
 
 template <bool F32>
@@ -89,6 +217,34 @@ using QFrag = typename std::conditional<F32, f32x8, bf16x8>::type;
 
 template <bool F32>
 using PType = typename std::conditional<F32, float, __bf16>::type;
+
+// bf16: the 16 heads' query rows staged once per workgroup in LDS (at dst,
+// row h at 16-byte piece kQPitch*h: the pitch of 73 pieces makes the
+// fragment reads conflict-free), 18 KiB of loads per workgroup instead of
+// every wave loading all of them. All lanes load: pad slots and heads past H
+// read the query's first piece, which nothing reads back.
+constexpr int kQPitch = 73;
+__device__ __forceinline__ void stage_q(const AttnArgs& a, int r, int hg, char* dst, int wave, int lane) {
+  const char* q = static_cast<const char*>(a.q);
+  const uint32_t d = lds_addr(dst);
+  for (int m = wave; 64 * m < kGroupHeads * kQPitch; m += 4) {
+    const int s = 64 * m + lane;
+    const int h = s / kQPitch, j = s - kQPitch * h;
+    const int hh = hg * kGroupHeads + h;
+    const bool v = h < kGroupHeads && j < kLatentDim / 8 && hh < a.H;
+    dma16(v ? q + ((int64_t(r) * a.H + hh) * kLatentDim + 8 * j) * 2 : q, d + 1024 * m);
+  }
+}
+
+// This lane's query fragments (head hg*16 + col, dims 32*ks + 8*grp .. +8)
+// from the staged rows; heads past H are zero.
+__device__ __forceinline__ void read_q(const char* src, bool hv, int col, int grp, bf16x8 (&qf)[18]) {
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks) {
+    const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * (kQPitch * col + 4 * ks + grp));
+    qf[ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
+  }
+}
 
 // LDS of one workgroup's attention.
 template <bool F32>
@@ -153,7 +309,7 @@ __device__ __forceinline__ int64_t seq_base(const AttnArgs& a, int r) {
 // output (splits == 1) or the split's unnormalised output, maximum and sum.
 template <bool F32>
 __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int splits, int hg, int j_beg,
-                                       int j_end, int64_t base, const int* s_idx, const QFrag<F32> (&qf)[18],
+                                       int j_end, int64_t base, const int* s_idx, QFrag<F32> (&qf)[18],
                                        Smem<F32>& sm) {
   using Cfg = AttnCfg<F32>;
   using PT = PType<F32>;
@@ -169,9 +325,19 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
   const int nchunks = j_end > j_beg ? (j_end - j_beg + kChunkKeys - 1) / kChunkKeys : 0;
 
   uint32_t ok[Cfg::NBUF];
-#pragma unroll
-  for (int i = 0; i < Cfg::NBUF; ++i)
-    ok[i] = i < nchunks ? issue_chunk<F32>(a, base, s_idx, i, smem + i * Cfg::BUF_BYTES, wave, lane) : 0u;
+  if constexpr (F32) {
+    ok[0] = nchunks > 0 ? issue_chunk<F32>(a, base, s_idx, 0, smem, wave, lane) : 0u;
+  } else if (nchunks > 0) {
+    // chunk 0 and the staged query (in buffer 1) in one round trip, then the
+    // query fragments into registers; chunk 1's loads go out during chunk
+    // 0's q.c
+    ok[0] = bgather_all(a, base, s_idx, 0, smem, wave, lane);
+    stage_q(a, r, hg, smem + Cfg::BUF_BYTES, wave, lane);
+    vm_wait_all();
+    __syncthreads();
+    read_q(smem + Cfg::BUF_BYTES, h < a.H, col, grp, qf);
+    __syncthreads();  // every wave has its fragments: buffer 1 is free
+  }
 
   f32x4 acc[8];
 #pragma unroll
@@ -187,15 +353,18 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
       __syncthreads();  // every wave is done with the previous chunk
       ok[0] = issue_chunk<F32>(a, base, s_idx, c, buf, wave, lane);
     }
+    if constexpr (!F32) {
+      if (c > 0) vm_wait_all();  // this wave's rows of chunk c (the only loads in flight) have landed
+    }
     const uint32_t okc = ok[bi];
 
     // ---- logits of this wave's 16 keys: S^T = C[16 x 576] . Q^T ----------------------
     f32x4 sacc;
     {
-      const char* rp = buf + (16 * wave + col) * Cfg::ROW_BYTES;
-      const int sw = row_swz(col);
-      f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       if constexpr (F32) {
+        const char* rp = buf + (16 * wave + col) * Cfg::ROW_BYTES;
+        const int sw = row_swz(col);
+        f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) {
           const int c0 = 8 * ks + 2 * grp;
@@ -204,25 +373,17 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
           const f32x8 af{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
           part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
         }
+        sacc = part[0] + part[1];
       } else {
-        // key fragments read four K-steps ahead of their MFMA (a wave has its
-        // SIMD to itself here: nothing else hides the LDS latency)
-        constexpr int D = 4;
-        bf16x8 fr[D];
-#pragma unroll
-        for (int i = 0; i < D; ++i) fr[i] = *reinterpret_cast<const bf16x8*>(rp + 16 * ((4 * i + grp) ^ sw));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          const bf16x8 af = fr[ks % D];
-          if (ks + D < 18) fr[ks % D] = *reinterpret_cast<const bf16x8*>(rp + 16 * ((4 * (ks + D) + grp) ^ sw));
-          part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
-          if (ks + D < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        const char* rp = buf + kBlock * wave + 64 * col + 16 * grp;
+        if (c == 0 && nchunks > 1) {  // buffer 1 is free since the query was read
+          const BGather gn = bgather_plan(a, base, s_idx, 1, smem + Cfg::BUF_BYTES, wave, lane);
+          ok[1] = gn.ok;
+          sacc = qc_bf16<true>(rp, qf, gn);
+        } else {
+          sacc = qc_bf16<false>(rp, qf, BGather{});
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-      sacc = part[0] + part[1];
     }
 
     // ---- chunk maximum per head over the 4 waves ----------------------------------------
@@ -238,8 +399,14 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
     if (grp == 0) s_max[wave][col] = mx;
     __syncthreads();  // maxima visible; every wave is done with chunk c-1 and has its rows of chunk c
     const float cmax = fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col]));
-    if (Cfg::NBUF == 2 && c + 1 < nchunks && c >= 1)
-      ok[bi ^ 1] = issue_chunk<F32>(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
+    // chunks 2, 3, ...: buffer bi^1 is free once every wave is past the
+    // barrier above; the next chunk's loads go out during this chunk's p.c
+    const bool pc_loads = !F32 && c + 1 < nchunks && c >= 1;
+    BGather gn{};
+    if (pc_loads) {
+      gn = bgather_plan(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
+      ok[bi ^ 1] = gn.ok;
+    }
 
     const float m_new = fmaxf(m_run, cmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no key seen yet: p = alpha = 0
@@ -289,7 +456,6 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
       // kb + 4*grp + s/4 (value dims v0 + 4*(s%4) ..), and receives value dim
       // v0 + s of rows kb + 4*grp + 0..3.
       const int tr_row = 4 * grp + (col >> 2);
-      const int tr_sw = ((col >> 2) << 1) | (grp & 1);  // row_swz of every row this lane names
       bf16x8 pf[2];
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
@@ -298,31 +464,45 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
         const uint2 phi = *reinterpret_cast<const uint2*>(pp + 16);
         pf[kq] = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
       }
-      // value fragment of step q = (kb = 32*(q/8), vt = q%8), read three steps ahead
+      // value fragment of step q = (kb = 32*(q/8), vt = q%8), read three
+      // steps ahead: lane (col, grp) names row kb + tr_row (and, 16 rows on,
+      // the next block), value dims 128*wave + 16vt + 4(col%4) .. +3, that is
+      // piece 16*wave + 2vt + (col%4)/2, half (col%4)&1
       auto vfrag = [&](int q) -> bf16x8 {
         const int kb = 32 * (q >> 3), vt = q & 7;
-        const char* rp = buf + (kb + tr_row) * Cfg::ROW_BYTES + 8 * (col & 1);
-        const int lc = 16 * wave + 2 * vt + ((col >> 1) & 1);
-        const char* p0 = rp + 16 * (lc ^ tr_sw);
+        const char* p0 = buf + blk_off(kb + tr_row, 16 * wave + 2 * vt + ((col >> 1) & 1)) + 8 * (col & 1);
         const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(lds_ptr)p0);
         const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + 16 * Cfg::ROW_BYTES));
+            (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + kBlock));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      constexpr int D = 3;
-      bf16x8 vr[D];
+      // LOADS: direct load q of the next chunk rides on step q (and the
+      // last two after the loop)
+      auto pc = [&](auto loads) {
+        constexpr bool LOADS = decltype(loads)::value;
+        constexpr int D = 3;
+        bf16x8 vr[D];
 #pragma unroll
-      for (int i = 0; i < D; ++i) vr[i] = vfrag(i);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < D; ++i) vr[i] = vfrag(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const bf16x8 af = vr[q % D];
-        if (q + D < 16) vr[q % D] = vfrag(q + D);
-        acc[q & 7] = mfma_k32(af, pf[q >> 3], acc[q & 7]);
-        if (q + D < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 16; ++q) {
+          const bf16x8 af = vr[q % D];
+          if (q + D < 16) vr[q % D] = vfrag(q + D);
+          acc[q & 7] = mfma_k32(af, pf[q >> 3], acc[q & 7]);
+          if constexpr (LOADS) bgather_load(gn, q);
+          if (q + D < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LOADS) {
+          static_assert(Cfg::WAVE_LOADS == 18, "two loads left after the 16 steps");
+          bgather_load(gn, 16);
+          bgather_load(gn, 17);
+        }
+      };
+      if (pc_loads) pc(std::true_type{});
+      else pc(std::false_type{});
     }
   }
 

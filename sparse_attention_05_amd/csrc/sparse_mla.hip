@@ -64,8 +64,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, in
     const int j = j_beg + e;
     s_idx[e] = j < j_end ? a.idx[int64_t(r) * a.k + j] : -1;
   }
-  QFrag<F32> qf[18];
-  load_q<F32>(a, r, h, grp, qf);
+  QFrag<F32> qf[18];  // bf16: staged and read by attend itself
+  if constexpr (F32) load_q<F32>(a, r, h, grp, qf);
   attend<F32>(a, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, sm);
 }
 
@@ -88,19 +88,6 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, in
 // past the last selected position are skipped (they would add exactly 0).
 constexpr int kWideHeads = 64;
 
-// 16-byte direct-to-LDS load: lane l's 16 bytes land at LDS byte lds + 16*l.
-__device__ __forceinline__ void wide_dma16(const void* src, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds)
-      : "memory");
-}
-
 // LDS layout of a chunk (64 rows x 72 chunks of 16 bytes): wave w's rows
 // 16w .. 16w+15 form a block of 18,432 bytes in which chunk c of row p sits
 // at 1024*(c/4) + 64*p + 16*(c%4). The direct load m of a wave then covers
@@ -114,7 +101,7 @@ __device__ __forceinline__ int wide_off(int row, int c) {
 // The gather of rows 16*wave .. +15 of chunk c (raw indices in s_idx) into
 // buf: this lane's source row (a missing row reads cache row 0 and is
 // zero-filled once it has landed), the LDS base of the wave's block and the
-// 16-bit mask of present rows; load m (0..17) is then wide_dma16(src + 64m,
+// 16-bit mask of present rows; load m (0..17) is then dma16(src + 64m,
 // lds + 1024m).
 struct WideGather {
   const char* src;
@@ -213,7 +200,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
   if (nchunks > 0) {
     const WideGather g = wide_gather(a, base, s_idx, 0, smem, wave, lane);
 #pragma unroll
-    for (int m = 0; m < WL; ++m) wide_dma16(g.src + 64 * m, g.lds + 1024 * m);
+    for (int m = 0; m < WL; ++m) dma16(g.src + 64 * m, g.lds + 1024 * m);
     okw[0] = g.mask;
   }
 
@@ -267,7 +254,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
         }
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) sc[kt] = mfma_k32(fa[ks & 1][kt], qf[ks], sc[kt]);
-        if (more) wide_dma16(gn.src + 64 * ks, gn.lds + 1024 * ks);  // load ks of chunk c+1
+        if (more) dma16(gn.src + 64 * ks, gn.lds + 1024 * ks);  // load ks of chunk c+1
         if (ks + 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }

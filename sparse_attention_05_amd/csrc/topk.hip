@@ -83,10 +83,26 @@ __device__ __forceinline__ void unroll(F&& f) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-// Barrier that orders LDS accesses only (no wait for outstanding global
-// stores, unlike __syncthreads, whose workgroup release waits for them).
+// Barrier that orders LDS accesses only. __syncthreads also waits for every
+// outstanding global load and store of the wave (its workgroup fence waits
+// on the whole vector-memory count), which would hold a barrier up behind
+// loads issued early for later use. No thread here reads global memory that
+// another thread of its workgroup wrote, and loads into registers are waited
+// for where they are used, so ordering the LDS is all the selection needs.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// true in every thread when `p` holds in any thread (uniform control flow)
+__device__ __forceinline__ bool block_any(bool p, uint32_t* red) {
+  const bool w = __ballot(p) != 0ull;
+  if (lane_id() == 0) red[wave_id()] = w ? 1u : 0u;
+  lds_barrier();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) r |= red[i];
+  lds_barrier();
+  return r != 0u;
 }
 
 // ---- block primitives (uniform control flow; each ends with a barrier) -----------
@@ -94,7 +110,7 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32_t& total) {
   const uint32_t x = wave_incl_scan(v);
   if (lane_id() == 63) red[wave_id()] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
@@ -102,7 +118,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
     base += w < wave_id() ? c : 0u;
     tot += c;
   }
-  __syncthreads();
+  lds_barrier();
   total = tot;
   return base + x - v;
 }
@@ -110,22 +126,22 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   const uint32_t m = wave_max(v);
   if (lane_id() == 0) red[wave_id()] = m;
-  __syncthreads();
+  lds_barrier();
   uint32_t r = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) r = max(r, red[w]);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
 __device__ __forceinline__ uint32_t block_min(uint32_t v, uint32_t* red) {
   const uint32_t m = wave_min(v);
   if (lane_id() == 0) red[wave_id()] = m;
-  __syncthreads();
+  lds_barrier();
   uint32_t r = 0xFFFFFFFFu;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) r = min(r, red[w]);
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -136,7 +152,7 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_
     red[wave_id()] = a;
     red[kWaves + wave_id()] = b;
   }
-  __syncthreads();
+  lds_barrier();
   mn = 0xFFFFFFFFu;
   mx = 0u;
 #pragma unroll
@@ -144,7 +160,7 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_
     mn = min(mn, red[w]);
     mx = max(mx, red[kWaves + w]);
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 __device__ __forceinline__ void clear_bins(uint32_t* a, int n) {
@@ -164,7 +180,7 @@ __device__ __forceinline__ void find_crossing(TopkShared& sh, uint32_t target, u
     const uint32_t s = octet_sum(x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w);
     if ((lane & 7) == 0) sh.coarse[g] = s;
   }
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
     const uint32_t c = sh.coarse[lane];
     const uint32_t incl = wave_incl_scan(c);
@@ -185,7 +201,7 @@ __device__ __forceinline__ void find_crossing(TopkShared& sh, uint32_t target, u
       sh.misc[2] = f;
     }
   }
-  __syncthreads();
+  lds_barrier();
   b = sh.misc[0];
   above = sh.misc[1];
   cnt = sh.misc[2];
@@ -223,17 +239,17 @@ __device__ __forceinline__ void select_small(TopkShared& sh, Visit&& visit, uint
     int shift, nb;
     digit_plan(lo, hi, 12, shift, nb);
     clear_bins(sh.bins, kBins);
-    __syncthreads();
+    lds_barrier();
     visit([&](uint32_t v) {
       if (v >= lo && v <= hi) atomicAdd(&sh.bins[(v - lo) >> shift], 1u);
     });
-    __syncthreads();
+    lds_barrier();
     uint32_t b, above, cnt;
     find_crossing(sh, target, b, above, cnt);
     target -= above;
     eq_total = cnt;
     narrow(lo, hi, b, shift);
-    __syncthreads();  // bins and misc are rewritten by the next pass
+    lds_barrier();  // bins and misc are rewritten by the next pass
   }
   T = lo;
   need = target;
@@ -252,23 +268,23 @@ __device__ __forceinline__ void select_full(TopkShared& sh, Visit&& visit, uint3
     digit_plan(lo, hi, 10, shift, nb);
     clear_bins(sh.u.full, kFullBins * kFullCopies);
     clear_bins(sh.bins, kBins);
-    __syncthreads();
+    lds_barrier();
     visit([&](uint32_t v) {
       if (v >= lo && v <= hi) atomicAdd(&sh.u.full[((v - lo) >> shift) * kFullCopies + (lane & 7)], 1u);
     });
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < kFullBins; i += kThreads) {
       const uint4 x = *reinterpret_cast<const uint4*>(sh.u.full + i * kFullCopies);
       const uint4 y = *reinterpret_cast<const uint4*>(sh.u.full + i * kFullCopies + 4);
       sh.bins[i] = x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w;
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t b, above, cnt;
     find_crossing(sh, target, b, above, cnt);
     target -= above;
     eq_total = cnt;
     narrow(lo, hi, b, shift);
-    __syncthreads();
+    lds_barrier();
   }
   T = lo;
   need = target;
@@ -362,7 +378,7 @@ __device__ __forceinline__ void collect_winners(TopkShared& sh, Each&& each, uin
       ++pos;
     }
   });
-  __syncthreads();
+  lds_barrier();
 }
 
 // Among the keys equal to T, the `need` smallest indices are those whose
@@ -409,11 +425,11 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
     w[j] = i < m ? src[off + i] : 0ull;
     bk[j] = uint32_t((mx - w[j]) >> shift);
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int j = 0; j < J; ++j)
     if (t + j * kThreads < m) atomicAdd(&sh.cnt[bk[j]], 1u);
-  __syncthreads();
+  lds_barrier();
   // bucket starts: each thread owns 8 consecutive buckets
   const int b0 = 8 * t;
   uint32_t c[8], s = 0;
@@ -452,7 +468,7 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
     }
     run += c[j];
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t start[J], cb[J], slot[J];
   bool keep[J];
 #pragma unroll
@@ -471,7 +487,7 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
 #pragma unroll
   for (int j = 0; j < J; ++j)
     if (keep[j]) dst[off + start[j] + slot[j]] = w[j];
-  __syncthreads();
+  lds_barrier();
   // rank inside small buckets: count the larger words of the bucket. The
   // elements placed in a small bucket are first listed (word in the bitonic
   // scratch, bucket start and size in sh.bins, free now), so that each is
@@ -493,7 +509,7 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
       ++lp;
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (uint32_t e = t; e < n_live; e += kThreads) {
     const unsigned long long we = sh.v.net[e];
     const uint32_t sc = sh.bins[e];
@@ -520,7 +536,7 @@ __device__ __forceinline__ void bitonic_segment(TopkShared& sh, const unsigned l
   int P = 1;
   while (P < m) P <<= 1;
   for (int i = t; i < P; i += kThreads) sh.v.net[i] = i < m ? src[off + i] : 0ull;
-  __syncthreads();
+  lds_barrier();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = t; i < P / 2; i += kThreads) {
@@ -532,12 +548,12 @@ __device__ __forceinline__ void bitonic_segment(TopkShared& sh, const unsigned l
           sh.v.net[h] = a;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
   for (int i = t; i < m; i += kThreads)
     if (off + i >= lo && off + i < hi) out[off + i - obase] = word_idx(sh.v.net[i]);
-  __syncthreads();
+  lds_barrier();
 }
 
 // Sort the m distinct words in sh.wa (all within [mn, mx]) descending and
@@ -558,7 +574,7 @@ __device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long 
   int cur = 0, nitems = 1;
   for (int level = 0; level < 4; ++level) {
     if (threadIdx.x == 0) sh.misc[6] = 0u;
-    __syncthreads();
+    lds_barrier();
     if (level == 3) {  // still dense after three splits: sorting network
       for (int i = 0; i < nitems; ++i)
         bitonic_segment(sh, src, int(sh.work[cur][6 * i]), int(sh.work[cur][6 * i + 1]), lo, hi, out, obase);
@@ -582,7 +598,7 @@ __device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long 
     const unsigned long long* tmp = src;
     src = dst;
     dst = const_cast<unsigned long long*>(tmp);
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -605,9 +621,9 @@ __device__ __forceinline__ uint32_t sample_pivot(TopkShared& sh, int ns, int SS,
     int shift, nb;
     digit_plan(smin, smax, 12, shift, nb);
     clear_bins(sh.bins, kBins);
-    __syncthreads();
+    lds_barrier();
     for (int i = int(threadIdx.x); i < ns; i += kThreads) atomicAdd(&sh.bins[(sh.v.samp[i] - smin) >> shift], 1u);
-    __syncthreads();
+    lds_barrier();
     uint32_t b, above, cnt;
     find_crossing(sh, target_s, b, above, cnt);
     pivot = smin + (b << shift);
@@ -670,7 +686,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     row.each([&](int idx, uint32_t key) {
       if (idx < n) sh.wa[pos++] = word(key, idx);
     });
-    __syncthreads();
+    lds_barrier();
     sort_words(sh, n, (static_cast<unsigned long long>(hi) << 32) | 0xFFFFFFFFull,
                static_cast<unsigned long long>(lo) << 32, 0, n, out);
     return;
@@ -745,13 +761,28 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
     int SS = 16;
     while ((n + SS - 1) / SS > 4096) SS <<= 1;
     const int ns = (n + SS - 1) / SS;
+    // every sample load is issued before the first wait (indexes past ns
+    // re-read the last sample and are not used)
+    const float* src = a.sample ? a.sample + int64_t(r) * a.ld_sample : row;
+    const int64_t stride = a.sample ? SS / 16 : SS;
+    constexpr int PT = 4096 / kThreads;
+    float sv_[PT];
+#pragma unroll
+    for (int j = 0; j < PT / 2; ++j) sv_[j] = src[int64_t(min(t + kThreads * j, ns - 1)) * stride];
+    if (ns > kThreads * (PT / 2)) {
+#pragma unroll
+      for (int j = PT / 2; j < PT; ++j) sv_[j] = src[int64_t(min(t + kThreads * j, ns - 1)) * stride];
+    }
     uint32_t smin = 0xFFFFFFFFu, smax = 0u;
-    for (int i = t; i < ns; i += kThreads) {
-      const float v = a.sample ? a.sample[int64_t(r) * a.ld_sample + int64_t(i) * (SS / 16)] : row[int64_t(i) * SS];
-      const uint32_t key = order_key(v);
-      sh.v.samp[i] = key;
-      smin = min(smin, key);
-      smax = max(smax, key);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = t + kThreads * j;
+      if (i < ns) {
+        const uint32_t key = order_key(sv_[j]);
+        sh.v.samp[i] = key;
+        smin = min(smin, key);
+        smax = max(smax, key);
+      }
     }
     block_minmax(smin, smax, sh.red);
     pivot = sample_pivot(sh, ns, SS, k, smin, smax);
@@ -781,23 +812,42 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
 // Ranks [lo, hi) of row r (hi <= min(n, k)) from the candidates of the
 // slices, indices to out[rank - obase]; when fewer than k or more than kCap
 // keys cleared the pivot, the exact selection over the whole row instead.
+// Slice counts (slices <= kThreads) and, in the same round trip, the first
+// words of every slice's region: thread t reads words j*tps + t%tps of slice
+// t/tps (tps threads per slice), which covers the typical count. Issued apart
+// from the selection so that a caller can start them before other work.
+struct WindowLoads {
+  uint32_t cnt;
+  unsigned long long x[kCap / kThreads];
+};
+
+__device__ __forceinline__ int window_tps(int slices) {
+  int tps = kThreads;
+  while (tps > 1 && tps * slices > kThreads) tps >>= 1;
+  return tps;
+}
+
+__device__ __forceinline__ void window_loads(const TopkArgs& a, int r, int slices, WindowLoads& L) {
+  const int t = threadIdx.x;
+  const unsigned long long* cand = a.cand + int64_t(r) * slices * kTile;
+  L.cnt = t < slices ? a.state[int64_t(r) * slices + t] : 0u;
+  const int tps = window_tps(slices);
+  const int sg = t / tps, sl = t % tps;
+#pragma unroll
+  for (int j = 0; j < kCap / kThreads; ++j) L.x[j] = sg < slices ? cand[int64_t(sg) * kTile + j * tps + sl] : 0ull;
+}
+
 __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a, int r, int slices, int n, int lo,
-                                              int hi, int32_t* out, int obase) {
+                                              int hi, int32_t* out, int obase, const WindowLoads& L) {
   const int t = threadIdx.x;
   const int k = a.k;
   const int k_eff = n < k ? n : k;
-  // Slice counts (slices <= kThreads) and, in the same round trip, the first
-  // words of every slice's region: thread t reads words j*tps + t%tps of
-  // slice t/tps (tps threads per slice), which covers the typical count.
   const unsigned long long* cand = a.cand + int64_t(r) * slices * kTile;
-  const uint32_t cnt = t < slices ? a.state[int64_t(r) * slices + t] : 0u;
+  const uint32_t cnt = L.cnt;
   constexpr int J = kCap / kThreads;
-  int tps = kThreads;
-  while (tps > 1 && tps * slices > kThreads) tps >>= 1;
+  const int tps = window_tps(slices);
   const int sg = t / tps, sl = t % tps;
-  unsigned long long x[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) x[j] = sg < slices ? cand[int64_t(sg) * kTile + j * tps + sl] : 0ull;
+  const unsigned long long* x = L.x;
   uint32_t C;
   const uint32_t at = block_scan(cnt, sh.red, C);
   if (C < uint32_t(k_eff) || C > uint32_t(kCap)) {
@@ -810,7 +860,7 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
     sh.bins[t] = at;
     sh.cnt[t] = cnt;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   bool rest = false;  // this slice holds more words than were read ahead
   if (sg < slices) {
@@ -828,7 +878,7 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
     rest = m > J * tps;
   }
   // the rest of the longer slices (rows with skewed candidates)
-  if (__syncthreads_or(rest)) {
+  if (block_any(rest, sh.red)) {
     for (int g = 0; g < slices; ++g) {
       const int m = int(sh.cnt[g]), o = int(sh.bins[g]);
       for (int i = J * tps + t; i < m; i += kThreads) {
@@ -857,7 +907,9 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int s
     for (int j = k_eff + t; j < k; j += kThreads) out[j] = -1;
   const int lo = w * kWindow, hi = lo + kWindow < k_eff ? lo + kWindow : k_eff;
   if (lo >= hi) return;
-  window_select(sh, a, r, slices, n, lo, hi, out, 0);
+  WindowLoads L;
+  window_loads(a, r, slices, L);
+  window_select(sh, a, r, slices, n, lo, hi, out, 0, L);
 }
 
 // Decode with selection and attention fused: the workgroup of (query r, key
@@ -881,6 +933,10 @@ __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnAr
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int col = lane & 15, grp = lane >> 4;
+  // The selection's global loads go out first, in one round trip: the
+  // candidate counts and words, the row's length and first cache row.
+  WindowLoads L;
+  window_loads(ta, r, slices, L);
   const int64_t base = attn::seq_base(aa, r);
   const int n = row_len(ta, r);
   const int k = ta.k;
@@ -890,18 +946,15 @@ __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnAr
   // ranks past k_eff, and the attention's chunk tail past j_end, stay -1
   const int span = (j_end - j_beg + attn::kChunkKeys - 1) / attn::kChunkKeys * attn::kChunkKeys;
   for (int i = t; i < span; i += kThreads) s_idx[i] = -1;
-  __syncthreads();
+  lds_barrier();
   const int hi = j_end < k_eff ? j_end : k_eff;
-  if (j_beg < hi) window_select(u.sel, ta, r, slices, n, j_beg, hi, s_idx, j_beg);
-  __syncthreads();  // the split's indices are in LDS; the selection's LDS is free
+  if (j_beg < hi) window_select(u.sel, ta, r, slices, n, j_beg, hi, s_idx, j_beg, L);
+  lds_barrier();  // the split's indices are in LDS; the selection's LDS is free
   if (hg == 0)
     for (int i = t; i < j_end - j_beg; i += kThreads) ta.idx[int64_t(r) * k + j_beg + i] = s_idx[i];
   if (wave >= 4) return;  // barriers below count the four attention waves only
-  // the query fragments now (a barrier waits for every outstanding load, so
-  // loaded earlier they would hold up the selection); they land while the
-  // first rows are gathered
-  attn::QFrag<F32> qf[18];
-  attn::load_q<F32>(aa, r, hg * attn::kGroupHeads + col, grp, qf);
+  attn::QFrag<F32> qf[18];  // bf16: staged and read by attend itself
+  if constexpr (F32) attn::load_q<F32>(aa, r, hg * attn::kGroupHeads + col, grp, qf);
   attn::attend<F32>(aa, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, u.att);
 }
 
