@@ -65,7 +65,7 @@ struct __attribute__((aligned(16))) TopkShared {
     uint32_t samp[4096];
     unsigned long long net[kCap];    // bitonic scratch
   } v;
-  uint32_t red[2 * kWaves];
+  uint32_t red[4 * kWaves];
   uint32_t misc[16];
   uint32_t work[2][6 * kMaxWork];    // dense buckets: offset, length, max (2 words), min (2 words)
 };
@@ -120,6 +120,28 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* red, uint32
   }
   lds_barrier();
   total = tot;
+  return base + x - v;
+}
+
+// block_scan of v and, in the same exchange, the maximum of u over the block
+__device__ __forceinline__ uint32_t block_scan_max(uint32_t v, uint32_t u, uint32_t* red, uint32_t& total,
+                                                   uint32_t& umax) {
+  const uint32_t x = wave_incl_scan(v);
+  const uint32_t m = wave_max(u);
+  if (lane_id() == 63) red[wave_id()] = x;
+  if (lane_id() == 0) red[kWaves + wave_id()] = m;
+  lds_barrier();
+  uint32_t base = 0, tot = 0, mm = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = red[w];
+    base += w < wave_id() ? c : 0u;
+    tot += c;
+    mm = max(mm, red[kWaves + w]);
+  }
+  lds_barrier();
+  total = tot;
+  umax = mm;
   return base + x - v;
 }
 
@@ -406,10 +428,18 @@ __device__ __forceinline__ uint32_t tie_threshold(TopkShared& sh, Each&& each, u
 // in sh.misc[6]) with their exact word range. Each thread handles the fixed
 // slots i = t + 512*j (j < 8) and issues every stage for all of them at once,
 // so the LDS round trips of different slots overlap.
+constexpr int kJ = kCap / kThreads;  // words per thread in a bucket pass
+
+__device__ __forceinline__ void bucket_finish(TopkShared& sh, const unsigned long long (&w)[kJ],
+                                              const uint32_t (&bk)[kJ], const bool (&valid)[kJ],
+                                              unsigned long long* dst, int off, unsigned long long mx,
+                                              unsigned long long mn, int shift, int nb, int lo, int hi, int32_t* out,
+                                              int obase, uint32_t* wl);
+
 __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long long* src, unsigned long long* dst,
                                             int off, int m, unsigned long long mx, unsigned long long mn, int lo,
                                             int hi, int32_t* out, int obase, uint32_t* wl) {
-  constexpr int J = kCap / kThreads;
+  constexpr int J = kJ;
   const int t = threadIdx.x;
   int shift, nb;
   digit_plan(mn, mx, 12, shift, nb);
@@ -419,17 +449,34 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
   }
   unsigned long long w[J];
   uint32_t bk[J];
+  bool valid[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int i = t + j * kThreads;
-    w[j] = i < m ? src[off + i] : 0ull;
+    valid[j] = i < m;
+    w[j] = valid[j] ? src[off + i] : 0ull;
     bk[j] = uint32_t((mx - w[j]) >> shift);
   }
   lds_barrier();
 #pragma unroll
   for (int j = 0; j < J; ++j)
-    if (t + j * kThreads < m) atomicAdd(&sh.cnt[bk[j]], 1u);
+    if (valid[j]) atomicAdd(&sh.cnt[bk[j]], 1u);
   lds_barrier();
+  bucket_finish(sh, w, bk, valid, dst, off, mx, mn, shift, nb, lo, hi, out, obase, wl);
+}
+
+// The rest of a bucket pass once sh.cnt holds the complete bucket counts of
+// the words w[j] (valid[j]; bucket bk[j] = (mx - w) >> shift, nb buckets,
+// sh.fill zero): bucket starts, the dense buckets that meet [lo, hi) listed
+// in wl (count in sh.misc[6]), the words of those buckets placed into
+// dst[off + ...], and the small ones ranked by counting.
+__device__ __forceinline__ void bucket_finish(TopkShared& sh, const unsigned long long (&w)[kJ],
+                                              const uint32_t (&bk)[kJ], const bool (&valid)[kJ],
+                                              unsigned long long* dst, int off, unsigned long long mx,
+                                              unsigned long long mn, int shift, int nb, int lo, int hi, int32_t* out,
+                                              int obase, uint32_t* wl) {
+  constexpr int J = kJ;
+  const int t = threadIdx.x;
   // bucket starts: each thread owns 8 consecutive buckets
   const int b0 = 8 * t;
   uint32_t c[8], s = 0;
@@ -475,7 +522,7 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
   for (int j = 0; j < J; ++j) {
     start[j] = sh.bins[bk[j]];
     cb[j] = sh.cnt[bk[j]];
-    keep[j] = t + j * kThreads < m && off + int(start[j]) < hi && off + int(start[j] + cb[j]) > lo;
+    keep[j] = valid[j] && off + int(start[j]) < hi && off + int(start[j] + cb[j]) > lo;
   }
   // Slots that are not placed count on a spare word of their own (the
   // bitonic scratch, unused here), so every slot's atomic and load below is
@@ -556,6 +603,10 @@ __device__ __forceinline__ void bitonic_segment(TopkShared& sh, const unsigned l
   lds_barrier();
 }
 
+__device__ __forceinline__ void sort_levels(TopkShared& sh, const unsigned long long* src, unsigned long long* dst,
+                                            int cur, int nitems, int level0, int lo, int hi, int32_t* out,
+                                            int obase);
+
 // Sort the m distinct words in sh.wa (all within [mn, mx]) descending and
 // write the indices of the ranks q in [lo, hi) to out[q - obase].
 __device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long long mx, unsigned long long mn,
@@ -569,10 +620,15 @@ __device__ __forceinline__ void sort_words(TopkShared& sh, int m, unsigned long 
     e[4] = uint32_t(mn >> 32);
     e[5] = uint32_t(mn);
   }
-  const unsigned long long* src = sh.wa;
-  unsigned long long* dst = sh.u.wb;
-  int cur = 0, nitems = 1;
-  for (int level = 0; level < 4; ++level) {
+  sort_levels(sh, sh.wa, sh.u.wb, 0, 1, 0, lo, hi, out, obase);
+}
+
+// The passes of sort_words from `level` on: nitems segments listed in
+// sh.work[cur] (offset, length, max, min), their words in src.
+__device__ __forceinline__ void sort_levels(TopkShared& sh, const unsigned long long* src, unsigned long long* dst,
+                                            int cur, int nitems, int level0, int lo, int hi, int32_t* out,
+                                            int obase) {
+  for (int level = level0; level < 4; ++level) {
     if (threadIdx.x == 0) sh.misc[6] = 0u;
     lds_barrier();
     if (level == 3) {  // still dense after three splits: sorting network
@@ -794,11 +850,15 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
   key[1] = order_key(sv.y);
   key[2] = order_key(sv.z);
   key[3] = order_key(sv.w);
-  uint32_t c = 0;
+  uint32_t c = 0, cm = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) c += i0 + e < n && key[e] >= pivot;
-  uint32_t total;
-  uint32_t pos = block_scan(c, sh.red, total);
+  for (int e = 0; e < 4; ++e) {
+    const bool in = i0 + e < n && key[e] >= pivot;
+    c += in;
+    cm = in ? max(cm, key[e]) : cm;
+  }
+  uint32_t total, cmax;
+  uint32_t pos = block_scan_max(c, cm, sh.red, total, cmax);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (i0 + e < n && key[e] >= pivot) {
@@ -806,7 +866,8 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
       ++pos;
     }
   }
-  if (t == 0) a.state[int64_t(r) * slices + g] = total;
+  if (t == 0)
+    reinterpret_cast<uint4*>(a.state)[int64_t(r) * slices + g] = uint4{total, cmax, pivot, 0u};
 }
 
 // Ranks [lo, hi) of row r (hi <= min(n, k)) from the candidates of the
@@ -817,7 +878,8 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
 // t/tps (tps threads per slice), which covers the typical count. Issued apart
 // from the selection so that a caller can start them before other work.
 struct WindowLoads {
-  uint32_t cnt;
+  uint4 st;   // slice t's (count, largest candidate key, pivot, 0), t < slices
+  uint32_t own;  // the count of the slice whose words this thread holds
   unsigned long long x[kCap / kThreads];
 };
 
@@ -830,35 +892,30 @@ __device__ __forceinline__ int window_tps(int slices) {
 __device__ __forceinline__ void window_loads(const TopkArgs& a, int r, int slices, WindowLoads& L) {
   const int t = threadIdx.x;
   const unsigned long long* cand = a.cand + int64_t(r) * slices * kTile;
-  L.cnt = t < slices ? a.state[int64_t(r) * slices + t] : 0u;
+  const uint4* st = reinterpret_cast<const uint4*>(a.state) + int64_t(r) * slices;
+  L.st = t < slices ? st[t] : uint4{0u, 0u, 0u, 0u};
   const int tps = window_tps(slices);
   const int sg = t / tps, sl = t % tps;
+  L.own = sg < slices ? st[sg].x : 0u;
 #pragma unroll
   for (int j = 0; j < kCap / kThreads; ++j) L.x[j] = sg < slices ? cand[int64_t(sg) * kTile + j * tps + sl] : 0ull;
 }
 
-__device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a, int r, int slices, int n, int lo,
-                                              int hi, int32_t* out, int obase, const WindowLoads& L) {
+// The candidates gathered into sh.wa in slice order (offset `at` of slice t
+// from the scan of the counts) and sorted there: the general form, for rows
+// whose slices hold more words than were read ahead, or whose window meets
+// more dense buckets than one pass lists.
+__device__ __forceinline__ void window_gather_sort(TopkShared& sh, const TopkArgs& a, int r, int slices, uint32_t C,
+                                                   uint32_t at, int lo, int hi, int32_t* out, int obase,
+                                                   const WindowLoads& L) {
   const int t = threadIdx.x;
-  const int k = a.k;
-  const int k_eff = n < k ? n : k;
+  constexpr int J = kJ;
   const unsigned long long* cand = a.cand + int64_t(r) * slices * kTile;
-  const uint32_t cnt = L.cnt;
-  constexpr int J = kCap / kThreads;
   const int tps = window_tps(slices);
   const int sg = t / tps, sl = t % tps;
-  const unsigned long long* x = L.x;
-  uint32_t C;
-  const uint32_t at = block_scan(cnt, sh.red, C);
-  if (C < uint32_t(k_eff) || C > uint32_t(kCap)) {
-    Row<0> full;
-    full.load(a.scores + int64_t(r) * a.ld, n);
-    select_exact(sh, full, n, k, out, lo, hi, obase);
-    return;
-  }
   if (t < slices) {
     sh.bins[t] = at;
-    sh.cnt[t] = cnt;
+    sh.cnt[t] = L.st.x;
   }
   lds_barrier();
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -869,8 +926,8 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
     for (int j = 0; j < J; ++j) {
       const int i = j * tps + sl;
       if (i < m) {
-        sh.wa[o + i] = x[j];
-        const uint32_t kx = uint32_t(x[j] >> 32);
+        sh.wa[o + i] = L.x[j];
+        const uint32_t kx = uint32_t(L.x[j] >> 32);
         kmin = min(kmin, kx);
         kmax = max(kmax, kx);
       }
@@ -893,6 +950,86 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
   block_minmax(kmin, kmax, sh.red);  // (its barriers publish the gathered words)
   sort_words(sh, int(C), (static_cast<unsigned long long>(kmax) << 32) | 0xFFFFFFFFull,
              static_cast<unsigned long long>(kmin) << 32, lo, hi, out, obase);
+}
+
+// Ranks [lo, hi) of row r (hi <= min(n, k)) from the candidates of the
+// slices, indices to out[rank - obase]; when fewer than k or more than kCap
+// keys cleared the pivot, the exact selection over the whole row instead.
+// Usually the read-ahead words already are all of them: then the first
+// bucket pass works on them in registers, on digits of the range [pivot,
+// largest candidate] that the candidate kernel recorded, with no gather
+// into LDS and no range reduction; later passes, if any, as in sort_words.
+__device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a, int r, int slices, int n, int lo,
+                                              int hi, int32_t* out, int obase, const WindowLoads& L) {
+  const int t = threadIdx.x;
+  const int k = a.k;
+  const int k_eff = n < k ? n : k;
+  constexpr int J = kJ;
+  const int tps = window_tps(slices);
+  const int sg = t / tps, sl = t % tps;
+  // the first pass's bins, cleared before the exchange below orders them
+  // before its histogram
+  for (int i = 4 * t; i < kBins; i += 4 * kThreads) {
+    *reinterpret_cast<uint4*>(sh.cnt + i) = uint4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<uint4*>(sh.fill + i) = uint4{0u, 0u, 0u, 0u};
+  }
+  if (t == 0) sh.misc[6] = 0u;
+  // one exchange: slice offsets and the total (scan of the counts), the
+  // largest candidate key, the longest slice, the pivot
+  const uint32_t cnt = L.st.x;
+  const uint32_t xs = wave_incl_scan(cnt);
+  {
+    const uint32_t wm = wave_max(L.st.y), wc = wave_max(cnt);
+    if (lane_id() == 63) sh.red[wave_id()] = xs;
+    if (lane_id() == 0) {
+      sh.red[kWaves + wave_id()] = wm;
+      sh.red[2 * kWaves + wave_id()] = wc;
+    }
+    if (t == 0) sh.red[3 * kWaves] = L.st.z;
+    lds_barrier();
+  }
+  uint32_t C = 0, base = 0, kmax = 0, longest = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t c = sh.red[w];
+    base += w < wave_id() ? c : 0u;
+    C += c;
+    kmax = max(kmax, sh.red[kWaves + w]);
+    longest = max(longest, sh.red[2 * kWaves + w]);
+  }
+  const uint32_t pivot = sh.red[3 * kWaves];
+  const uint32_t at = base + xs - cnt;  // slice t's offset in the gathered order
+  if (C < uint32_t(k_eff) || C > uint32_t(kCap)) {
+    Row<0> full;
+    full.load(a.scores + int64_t(r) * a.ld, n);
+    select_exact(sh, full, n, k, out, lo, hi, obase);
+    return;
+  }
+  if (longest > uint32_t(J * tps)) {
+    window_gather_sort(sh, a, r, slices, C, at, lo, hi, out, obase, L);
+    return;
+  }
+  const unsigned long long mx = (static_cast<unsigned long long>(kmax) << 32) | 0xFFFFFFFFull;
+  const unsigned long long mn = static_cast<unsigned long long>(pivot) << 32;
+  int shift, nb;
+  digit_plan(mn, mx, 12, shift, nb);
+  uint32_t bk[J];
+  bool valid[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    valid[j] = sg < slices && uint32_t(j * tps + sl) < L.own;
+    bk[j] = uint32_t((mx - L.x[j]) >> shift);
+    if (valid[j]) atomicAdd(&sh.cnt[bk[j]], 1u);
+  }
+  lds_barrier();
+  bucket_finish(sh, L.x, bk, valid, sh.u.wb, 0, mx, mn, shift, nb, lo, hi, out, obase, sh.work[1]);
+  const int next = int(sh.misc[6]);
+  if (next == 0) return;
+  if (next > kMaxWork) {
+    window_gather_sort(sh, a, r, slices, C, at, lo, hi, out, obase, L);
+    return;
+  }
+  sort_levels(sh, sh.u.wb, sh.wa, 1, next, 1, lo, hi, out, obase);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int slices, int windows) {
@@ -969,7 +1106,7 @@ bool topk_use_split(int R, int max_n) {
 // counts [R][slices].
 size_t topk_split_ws_bytes(int R, int max_n) {
   const size_t slices = size_t((max_n + kTile - 1) / kTile);
-  return size_t(R) * slices * kTile * sizeof(unsigned long long) + size_t(R) * slices * sizeof(uint32_t);
+  return size_t(R) * slices * kTile * sizeof(unsigned long long) + size_t(R) * slices * sizeof(uint4);
 }
 
 void topk_split_carve(void* ws, int R, int max_n, TopkArgs& a) {

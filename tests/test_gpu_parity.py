@@ -379,6 +379,25 @@ def test_fused_split_decode_matches_pipeline_and_replay(dsa, lens, k):
     C.assert_attn_close(out[rows], ref_o, lse[rows], ref_l)
 
 
+def test_fused_split_decode_whole_window_with_tie_classes(dsa):
+    """64 queries over 8,200 keys: one attention split per query, so each
+    fused workgroup selects all 2,048 ranks itself. Keys drawn from 100
+    prototypes make about 100 score classes of ~80 keys each, so a window
+    meets more dense buckets than one bucket pass lists and the selection
+    takes its general form (candidates gathered, then sorted). Indices equal
+    the stable order of the scores; the fused step equals the entry points."""
+    p = inputs.decode_config([8200] * 64, seed=12, tie_levels=100, k=2048)
+    d = inputs.to_torch(p)
+    out, lse, idx = _fused(dsa, p, d)
+    scores, idx2, out2, lse2 = _pipeline(dsa, p)
+    assert np.array_equal(idx, idx2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    C.assert_index_invariants(idx, p.q_pos, p.k)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k)), f"row {r}"
+
+
 # ------------------------------------------------------------------------------
 # causal prefill form (one sequence, a query per position)
 # ------------------------------------------------------------------------------
