@@ -95,6 +95,7 @@ struct KeyCfg {
   static constexpr int GK = 64;                               // keys per group
   static constexpr int GBYTES = GK * ROW;
   static constexpr int LOADS = GBYTES / 1024;                 // 1 KiB direct loads per group
+  static constexpr int GLOADS = LOADS + (QK == 2 ? 1 : 0);     // + the row scales (fp8)
   static constexpr int NS = GBYTES >= 32768 ? 1 : (32768 / GBYTES > 4 ? 4 : 32768 / GBYTES);  // stages
 };
 
@@ -143,6 +144,21 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off
       : "memory");
 }
 
+// 2-byte direct-to-LDS load through a buffer resource: lane l reads the
+// 16-bit value at byte offset `off` (zero past the buffer's end) and writes
+// it, zero-extended, to the 32-bit LDS word lds + 4*l.
+__device__ __forceinline__ void dma2_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "buffer_load_ushort %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(r), "s"(lds)
+      : "memory");
+}
+
 // s_waitcnt vmcnt(min(N, 63)): a smaller count only waits longer.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -155,11 +171,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Start the direct-to-LDS load of keys s0 .. s0+63 (those below s_end) into
-// stage buffer `dst`. All earlier LDS reads of the wave are complete first
-// (the buffer may be a stage that was just consumed).
+// stage buffer `dst`; fp8 keys: then their row scales (bf16 bits), key s0+l
+// into the 32-bit word sc_dst + 4*l (zero past s_end). All earlier LDS reads
+// of the wave are complete first (the buffers may be a stage that was just
+// consumed). GLOADS loads in all.
 template <int QK, int DI>
 __device__ __forceinline__ void load_group(const IndexArgs& a, int64_t base, int64_t s0, int64_t s_end, char* dst,
-                                           int lane) {
+                                           uint32_t* sc_dst, int lane) {
   using C = KeyCfg<QK, DI>;
   const char* keys = static_cast<const char*>(a.keys);
   const uint32_t to = lds_addr(dst);
@@ -171,6 +189,11 @@ __device__ __forceinline__ void load_group(const IndexArgs& a, int64_t base, int
     const int lc = (pch % C::CPR) ^ (row & C::SWZ);
     const int64_t key = s0 + row < s_end ? base + s0 + row : base;  // rows past the range re-read row 0
     dma16(keys + key * C::ROW + 16 * lc, to + 1024 * m);
+  }
+  if constexpr (QK == 2) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.k_scale + base), 0, int(2 * s_end), 0x00020000);
+    dma2_buf(rs, uint32_t(2 * (s0 + lane)), lds_addr(sc_dst));
   }
 }
 
@@ -249,6 +272,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
   __shared__ __attribute__((aligned(1024))) char smem[kWaves][C::NS][C::GBYTES];
   __shared__ __attribute__((aligned(16))) char s_q[kQLds ? 64 * DI * 2 : 16];
   __shared__ __attribute__((aligned(16))) float s_w[64];
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[kWaves][C::NS][QK == 2 ? 64 : 1];  // fp8 row scales
 
   const int r = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -293,8 +317,8 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
     if (threadIdx.x >= a.H_I && threadIdx.x < 16 * MT) s_w[threadIdx.x] = 0.f;
     // then all key stages, so the whole working set is in flight
     for (; issued < C::NS && issued < groups; ++issued)
-      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], lane);
-    wait_groups<C::LOADS>(issued);  // this wave's query and weight loads have landed
+      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], s_sc[wave][issued], lane);
+    wait_groups<C::GLOADS>(issued);  // this wave's query and weight loads have landed
     __syncthreads();
     // A operand: head 16*mt + col, dims 32*ks + 8*grp .. +8
 #pragma unroll
@@ -327,14 +351,14 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
       }
     }
     for (; issued < C::NS && issued < groups; ++issued)
-      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], lane);
+      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], s_sc[wave][issued], lane);
   }
 
-  if constexpr (QK == 1) {
-    // bf16 keys: the score (and sample) stores are branch-free buffer
-    // stores (lanes past this wave's range are dropped by the bounds), one
-    // per group each, so the wait for a group can count them exactly instead
-    // of also waiting for the stores issued after its loads.
+  if constexpr (QK != 0) {
+    // bf16 and fp8 keys: the score (and sample) stores are branch-free
+    // buffer stores (lanes past this wave's range are dropped by the
+    // bounds), one per group each, so the wait for a group can count them
+    // exactly instead of also waiting for the stores issued after its loads.
     const bool smp = a.sample != nullptr;
     const int spg = smp ? 2 : 1;  // stores per group
     const __amdgpu_buffer_rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc(
@@ -348,9 +372,19 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
       const char* stage = smem[wave][g % C::NS];
       // behind group g's loads: those of the later groups and the stores of
       // the groups computed since it was issued
-      const int behind = C::LOADS * (issued - 1 - g) + spg * (g < C::NS ? g : C::NS);
+      const int behind = C::GLOADS * (issued - 1 - g) + spg * (g < C::NS ? g : C::NS);
       float part[4];
-      wait_ops<C::LOADS * (C::NS - 1) + 2 * C::NS>(behind);  // group g landed
+      wait_ops<C::GLOADS * (C::NS - 1) + 2 * C::NS>(behind);  // group g landed
+      // fp8: the row scale of the key in this lane's MFMA column for each
+      // block, and of key s0 + lane (read before the stage is refilled)
+      float scb[4] = {1.f, 1.f, 1.f, 1.f};
+      uint32_t scl = 0u;
+      if constexpr (QK == 2) {
+        const uint32_t* scs = s_sc[wave][g % C::NS];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) scb[blk] = bf16_bits_to_f32(scs[16 * blk + col]);
+        scl = scs[lane];
+      }
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         f32x4 acc[MT];
@@ -361,18 +395,31 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
           for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_k32(qa[mt][ks], kb, ks ? acc[mt] : f32x4{0.f, 0.f, 0.f, 0.f});
         }
         float p = 0.f;
+        if (QK == 2 && scb[blk] < 0.f) {
+          // relu(sc*z) with a negative row scale: scale each dot first
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p += wr[mt][i] * relu_bits(acc[mt][i]);
+            for (int i = 0; i < 4; ++i) p += wr[mt][i] * relu_bits(scb[blk] * acc[mt][i]);
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p += wr[mt][i] * relu_bits(acc[mt][i]);
+        }
         part[blk] = p;
       }
       // this stage is consumed: refill it with group g + NS
       if (issued < groups) {
-        load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][g % C::NS], lane);
+        load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][g % C::NS], s_sc[wave][g % C::NS], lane);
         ++issued;
       }
-      const float v = rows_transpose_sum(part);
+      float v = rows_transpose_sum(part);
+      if constexpr (QK == 2) {
+        // non-negative row scale: relu(sc*z) = sc*relu(z), applied once per key
+        const float sc = bf16_bits_to_f32(scl);
+        if (!(sc < 0.f)) v *= sc;
+      }
       const int64_t s = s0 + lane;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, int(s - s_beg) * 4, 0, 0);
       if (smp)
@@ -421,7 +468,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
     }
     // this stage is consumed: refill it with group g + NS
     if (issued < groups) {
-      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][g % C::NS], lane);
+      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][g % C::NS], s_sc[wave][g % C::NS], lane);
       ++issued;
     }
 

@@ -46,6 +46,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 4 * kThreads;  // one coalesced sweep
 constexpr int kBins = 4096;          // 12-bit digits (64 groups of 64)
 constexpr int kCap = 4096;           // candidate capacity
+constexpr int kMaxSamples = 16384;   // score samples behind a split pivot
 constexpr int kSmall = 32;           // rank-by-counting limit
 constexpr int kMaxWork = 16;         // dense buckets split per level
 constexpr int kFullBins = 1024;      // whole-row histogram: 10-bit digits
@@ -812,36 +813,77 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
   const float4 sv = i0 < n ? *reinterpret_cast<const float4*>(row + i0) : float4{0.f, 0.f, 0.f, 0.f};
 
   // ---- pivot (identical in every slice of the row; 0 when every key wins) ----------------
+  // From the indexer's every-16th-score sample (every SS-th score, up to
+  // kMaxSamples of them, held in registers): the t-th largest sample, t
+  // chosen so that the count of keys above it, about t*SS with a standard
+  // deviation of about sqrt(t)*SS, falls below k only 4 deviations down;
+  // the pivot is the lower edge of the 12-bit bin holding it, refined by a
+  // second 12-bit histogram inside that bin when the bin holds more than a
+  // few samples past t (wide bins: a heavy tail stretches the range).
   uint32_t pivot = 0u;
   if (n > k) {
     int SS = 16;
-    while ((n + SS - 1) / SS > 4096) SS <<= 1;
+    while ((n + SS - 1) / SS > kMaxSamples) SS <<= 1;
     const int ns = (n + SS - 1) / SS;
     // every sample load is issued before the first wait (indexes past ns
     // re-read the last sample and are not used)
     const float* src = a.sample ? a.sample + int64_t(r) * a.ld_sample : row;
     const int64_t stride = a.sample ? SS / 16 : SS;
-    constexpr int PT = 4096 / kThreads;
-    float sv_[PT];
+    constexpr int PT = kMaxSamples / kThreads;
+    constexpr int PQ = PT / 4;
+    uint32_t key[PT];
 #pragma unroll
-    for (int j = 0; j < PT / 2; ++j) sv_[j] = src[int64_t(min(t + kThreads * j, ns - 1)) * stride];
-    if (ns > kThreads * (PT / 2)) {
+    for (int q = 0; q < 4; ++q) {
+      if (q == 0 || ns > kThreads * PQ * q) {
 #pragma unroll
-      for (int j = PT / 2; j < PT; ++j) sv_[j] = src[int64_t(min(t + kThreads * j, ns - 1)) * stride];
+        for (int j = PQ * q; j < PQ * (q + 1); ++j)
+          key[j] = __float_as_uint(src[int64_t(min(t + kThreads * j, ns - 1)) * stride]);
+      }
     }
     uint32_t smin = 0xFFFFFFFFu, smax = 0u;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
-      const int i = t + kThreads * j;
-      if (i < ns) {
-        const uint32_t key = order_key(sv_[j]);
-        sh.v.samp[i] = key;
-        smin = min(smin, key);
-        smax = max(smax, key);
+      key[j] = order_key(__uint_as_float(key[j]));
+      if (t + kThreads * j < ns) {
+        smin = min(smin, key[j]);
+        smax = max(smax, key[j]);
       }
     }
     block_minmax(smin, smax, sh.red);
-    pivot = sample_pivot(sh, ns, SS, k, smin, smax);
+    const float kq = float(k) / float(SS);
+    const float rt = 2.f + sqrtf(4.f + kq);
+    uint32_t ts = uint32_t(ceilf(rt * rt));
+    if (ts > uint32_t(ns)) ts = uint32_t(ns);
+    pivot = smin;
+    if (smin < smax) {
+      int shift, nb;
+      digit_plan(smin, smax, 12, shift, nb);
+      clear_bins(sh.bins, kBins);
+      lds_barrier();
+#pragma unroll
+      for (int j = 0; j < PT; ++j)
+        if (t + kThreads * j < ns) atomicAdd(&sh.bins[(key[j] - smin) >> shift], 1u);
+      lds_barrier();
+      uint32_t b, above, cnt;
+      find_crossing(sh, ts, b, above, cnt);
+      const uint32_t lo1 = smin + (b << shift);
+      pivot = lo1;
+      if (shift > 0 && above + cnt > ts + 8) {
+        const unsigned long long top = static_cast<unsigned long long>(lo1) + ((1ull << shift) - 1ull);
+        const uint32_t hi1 = top < smax ? static_cast<uint32_t>(top) : smax;
+        int shift2, nb2;
+        digit_plan(lo1, hi1, 12, shift2, nb2);
+        clear_bins(sh.bins, kBins);  // (find_crossing's last barrier ended its reads)
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < PT; ++j)
+          if (t + kThreads * j < ns && key[j] >= lo1 && key[j] <= hi1) atomicAdd(&sh.bins[(key[j] - lo1) >> shift2], 1u);
+        lds_barrier();
+        uint32_t b2, above2, cnt2;
+        find_crossing(sh, ts - above, b2, above2, cnt2);
+        pivot = lo1 + (b2 << shift2);
+      }
+    }
   }
 
   // ---- this slice's candidates, compacted in index order ---------------------------------
