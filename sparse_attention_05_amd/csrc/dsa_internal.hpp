@@ -41,8 +41,9 @@ struct TopkArgs {
   // are given and the rows are few and long:
   const float* sample;        // NULL, or sample[r * ld_sample + i] = scores[r, 16 i]
   int64_t ld_sample;
-  uint32_t* state;            // [R][slices] candidate counts (written, then read, by each launch)
-  unsigned long long* cand;   // [R][slices][2048] candidate words
+  uint32_t* state;            // [R][slices] uint4: candidate count, largest candidate key, pivot, 0
+  unsigned long long* cand;   // [R][slices][slice_tiles * 2048] candidate words
+  int slice_tiles;            // 2048-key tiles per slice (set with cand and state)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 bool topk_use_split(int R, int max_n);

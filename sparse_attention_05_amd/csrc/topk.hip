@@ -46,7 +46,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 4 * kThreads;  // one coalesced sweep
 constexpr int kBins = 4096;          // 12-bit digits (64 groups of 64)
 constexpr int kCap = 4096;           // candidate capacity
-constexpr int kMaxSamples = 16384;   // score samples behind a split pivot
+constexpr int kMaxSamples = 8192;    // score samples behind a pivot
+constexpr int kMaxSliceTiles = 8;    // tiles of kTile keys per slice of a split row
 constexpr int kSmall = 32;           // rank-by-counting limit
 constexpr int kMaxWork = 16;         // dense buckets split per level
 constexpr int kFullBins = 1024;      // whole-row histogram: 10-bit digits
@@ -63,7 +64,7 @@ struct __attribute__((aligned(16))) TopkShared {
     uint32_t full[kFullBins * kFullCopies];  // whole-row histogram (fallback select)
   } u;
   union {
-    uint32_t samp[4096];
+    uint32_t samp[kMaxSamples];      // score sample keys (split pivot)
     unsigned long long net[kCap];    // bitonic scratch
   } v;
   uint32_t red[4 * kWaves];
@@ -668,24 +669,42 @@ __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
 }
 
 // Pivot from the sample sh.v.samp[0..ns) (every SS-th key of the row, range
-// [smin, smax]): the lower edge of the 12-bit histogram bin that holds the
-// (ceil(k/SS)+24)-th largest sample, so that about k + 24*SS keys clear it.
+// [smin, smax]). The t-th largest sample is taken, t chosen so that the count
+// of keys above it (about t*SS, with a standard deviation of about
+// sqrt(t)*SS) falls below k only 3 deviations down; the pivot is the lower
+// edge of the 12-bit bin holding it, refined by a second 12-bit histogram
+// inside that bin when the bin holds more than a few samples past t (a heavy
+// tail stretches the range and widens the bins).
 __device__ __forceinline__ uint32_t sample_pivot(TopkShared& sh, int ns, int SS, int k, uint32_t smin, uint32_t smax) {
-  uint32_t target_s = uint32_t((k + SS - 1) / SS + 24);
-  if (target_s > uint32_t(ns)) target_s = uint32_t(ns);
-  uint32_t pivot = smin;
-  if (smin < smax) {
-    int shift, nb;
-    digit_plan(smin, smax, 12, shift, nb);
-    clear_bins(sh.bins, kBins);
-    lds_barrier();
-    for (int i = int(threadIdx.x); i < ns; i += kThreads) atomicAdd(&sh.bins[(sh.v.samp[i] - smin) >> shift], 1u);
-    lds_barrier();
-    uint32_t b, above, cnt;
-    find_crossing(sh, target_s, b, above, cnt);
-    pivot = smin + (b << shift);
+  const float kq = float(k) / float(SS);
+  const float rt = 1.5f + sqrtf(2.25f + kq);
+  uint32_t ts = uint32_t(ceilf(rt * rt));
+  if (ts > uint32_t(ns)) ts = uint32_t(ns);
+  if (!(smin < smax)) return smin;
+  int shift, nb;
+  digit_plan(smin, smax, 12, shift, nb);
+  clear_bins(sh.bins, kBins);
+  lds_barrier();
+  for (int i = int(threadIdx.x); i < ns; i += kThreads) atomicAdd(&sh.bins[(sh.v.samp[i] - smin) >> shift], 1u);
+  lds_barrier();
+  uint32_t b, above, cnt;
+  find_crossing(sh, ts, b, above, cnt);
+  const uint32_t lo1 = smin + (b << shift);
+  if (shift == 0 || above + cnt <= ts + 8) return lo1;
+  const unsigned long long top = static_cast<unsigned long long>(lo1) + ((1ull << shift) - 1ull);
+  const uint32_t hi1 = top < smax ? static_cast<uint32_t>(top) : smax;
+  int shift2, nb2;
+  digit_plan(lo1, hi1, 12, shift2, nb2);
+  clear_bins(sh.bins, kBins);  // (find_crossing's last barrier ended its reads)
+  lds_barrier();
+  for (int i = int(threadIdx.x); i < ns; i += kThreads) {
+    const uint32_t x = sh.v.samp[i];
+    if (x >= lo1 && x <= hi1) atomicAdd(&sh.bins[(x - lo1) >> shift2], 1u);
   }
-  return pivot;
+  lds_barrier();
+  uint32_t b2, above2, cnt2;
+  find_crossing(sh, ts - above, b2, above2, cnt2);
+  return lo1 + (b2 << shift2);
 }
 
 // Exact selection over a whole row held by `row` (any EPT), for rows whose
@@ -751,7 +770,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 
   // ---- 1. pivot from the fixed sample ------------------------------------------------
   int SS = 16;
-  while ((n + SS - 1) / SS > 4096) SS <<= 1;
+  while ((n + SS - 1) / SS > kMaxSamples) SS <<= 1;
   const int ns = (n + SS - 1) / SS;
   uint32_t smin = 0xFFFFFFFFu, smax = 0u;
   row.sample(SS, [&](int i, uint32_t key) {  // i = index / SS
@@ -799,6 +818,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 // result does not depend on how the work is spread.
 constexpr int kWindow = 128;  // output ranks per workgroup of the second launch
 
+template <int T>
 __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int slices) {
   __shared__ TopkShared sh;
   const int r = blockIdx.x / slices, g = blockIdx.x % slices;
@@ -806,106 +826,84 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
   const int n = row_len(a, r);
   const int k = a.k;
   const float* row = a.scores + int64_t(r) * a.ld;
-  unsigned long long* cand = a.cand + (int64_t(r) * slices + g) * kTile;
+  unsigned long long* cand = a.cand + (int64_t(r) * slices + g) * (int64_t(T) * kTile);
 
-  // this slice's scores, loaded first so the load overlaps the pivot
-  const int i0 = g * kTile + 4 * t;
-  const float4 sv = i0 < n ? *reinterpret_cast<const float4*>(row + i0) : float4{0.f, 0.f, 0.f, 0.f};
+  // this slice's scores (T tiles of kTile keys), loaded first so the loads
+  // overlap the pivot
+  float4 sv[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const int i0 = (g * T + j) * kTile + 4 * t;
+    sv[j] = i0 < n ? *reinterpret_cast<const float4*>(row + i0) : float4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---- pivot (identical in every slice of the row; 0 when every key wins) ----------------
-  // From the indexer's every-16th-score sample (every SS-th score, up to
-  // kMaxSamples of them, held in registers): the t-th largest sample, t
-  // chosen so that the count of keys above it, about t*SS with a standard
-  // deviation of about sqrt(t)*SS, falls below k only 4 deviations down;
-  // the pivot is the lower edge of the 12-bit bin holding it, refined by a
-  // second 12-bit histogram inside that bin when the bin holds more than a
-  // few samples past t (wide bins: a heavy tail stretches the range).
+  // from the indexer's every-16th-score sample (every SS-th score, at most
+  // kMaxSamples), staged in LDS
   uint32_t pivot = 0u;
   if (n > k) {
     int SS = 16;
     while ((n + SS - 1) / SS > kMaxSamples) SS <<= 1;
     const int ns = (n + SS - 1) / SS;
     // every sample load is issued before the first wait (indexes past ns
-    // re-read the last sample and are not used)
+    // re-read the last sample and are not used), in batches of 2048 samples
     const float* src = a.sample ? a.sample + int64_t(r) * a.ld_sample : row;
     const int64_t stride = a.sample ? SS / 16 : SS;
     constexpr int PT = kMaxSamples / kThreads;
-    constexpr int PQ = PT / 4;
-    uint32_t key[PT];
+    constexpr int PQ = 4;
+    float sv_[PT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < PT / PQ; ++q) {
       if (q == 0 || ns > kThreads * PQ * q) {
 #pragma unroll
-        for (int j = PQ * q; j < PQ * (q + 1); ++j)
-          key[j] = __float_as_uint(src[int64_t(min(t + kThreads * j, ns - 1)) * stride]);
+        for (int j = PQ * q; j < PQ * (q + 1); ++j) sv_[j] = src[int64_t(min(t + kThreads * j, ns - 1)) * stride];
       }
     }
     uint32_t smin = 0xFFFFFFFFu, smax = 0u;
 #pragma unroll
-    for (int j = 0; j < PT; ++j) {
-      key[j] = order_key(__uint_as_float(key[j]));
-      if (t + kThreads * j < ns) {
-        smin = min(smin, key[j]);
-        smax = max(smax, key[j]);
+    for (int q = 0; q < PT / PQ; ++q) {
+      if (q == 0 || ns > kThreads * PQ * q) {
+#pragma unroll
+        for (int j = PQ * q; j < PQ * (q + 1); ++j) {
+          const int i = t + kThreads * j;
+          if (i < ns) {
+            const uint32_t key = order_key(sv_[j]);
+            sh.v.samp[i] = key;
+            smin = min(smin, key);
+            smax = max(smax, key);
+          }
+        }
       }
     }
     block_minmax(smin, smax, sh.red);
-    const float kq = float(k) / float(SS);
-    const float rt = 2.f + sqrtf(4.f + kq);
-    uint32_t ts = uint32_t(ceilf(rt * rt));
-    if (ts > uint32_t(ns)) ts = uint32_t(ns);
-    pivot = smin;
-    if (smin < smax) {
-      int shift, nb;
-      digit_plan(smin, smax, 12, shift, nb);
-      clear_bins(sh.bins, kBins);
-      lds_barrier();
-#pragma unroll
-      for (int j = 0; j < PT; ++j)
-        if (t + kThreads * j < ns) atomicAdd(&sh.bins[(key[j] - smin) >> shift], 1u);
-      lds_barrier();
-      uint32_t b, above, cnt;
-      find_crossing(sh, ts, b, above, cnt);
-      const uint32_t lo1 = smin + (b << shift);
-      pivot = lo1;
-      if (shift > 0 && above + cnt > ts + 8) {
-        const unsigned long long top = static_cast<unsigned long long>(lo1) + ((1ull << shift) - 1ull);
-        const uint32_t hi1 = top < smax ? static_cast<uint32_t>(top) : smax;
-        int shift2, nb2;
-        digit_plan(lo1, hi1, 12, shift2, nb2);
-        clear_bins(sh.bins, kBins);  // (find_crossing's last barrier ended its reads)
-        lds_barrier();
-#pragma unroll
-        for (int j = 0; j < PT; ++j)
-          if (t + kThreads * j < ns && key[j] >= lo1 && key[j] <= hi1) atomicAdd(&sh.bins[(key[j] - lo1) >> shift2], 1u);
-        lds_barrier();
-        uint32_t b2, above2, cnt2;
-        find_crossing(sh, ts - above, b2, above2, cnt2);
-        pivot = lo1 + (b2 << shift2);
-      }
-    }
+    pivot = sample_pivot(sh, ns, SS, k, smin, smax);
   }
 
-  // ---- this slice's candidates, compacted in index order ---------------------------------
-  uint32_t key[4];
-  key[0] = order_key(sv.x);
-  key[1] = order_key(sv.y);
-  key[2] = order_key(sv.z);
-  key[3] = order_key(sv.w);
+  // ---- this slice's candidates, compacted (thread order, then tile order) -------------------
   uint32_t c = 0, cm = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bool in = i0 + e < n && key[e] >= pivot;
-    c += in;
-    cm = in ? max(cm, key[e]) : cm;
+  for (int j = 0; j < T; ++j) {
+    const int i0 = (g * T + j) * kTile + 4 * t;
+    const uint32_t key[4] = {order_key(sv[j].x), order_key(sv[j].y), order_key(sv[j].z), order_key(sv[j].w)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = i0 + e < n && key[e] >= pivot;
+      c += in;
+      cm = in ? max(cm, key[e]) : cm;
+    }
   }
   uint32_t total, cmax;
   uint32_t pos = block_scan_max(c, cm, sh.red, total, cmax);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (i0 + e < n && key[e] >= pivot) {
-      cand[pos] = word(key[e], i0 + e);
-      ++pos;
+  for (int j = 0; j < T; ++j) {
+    const int i0 = (g * T + j) * kTile + 4 * t;
+    const uint32_t key[4] = {order_key(sv[j].x), order_key(sv[j].y), order_key(sv[j].z), order_key(sv[j].w)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i0 + e < n && key[e] >= pivot) {
+        cand[pos] = word(key[e], i0 + e);
+        ++pos;
+      }
     }
   }
   if (t == 0)
@@ -933,14 +931,15 @@ __device__ __forceinline__ int window_tps(int slices) {
 
 __device__ __forceinline__ void window_loads(const TopkArgs& a, int r, int slices, WindowLoads& L) {
   const int t = threadIdx.x;
-  const unsigned long long* cand = a.cand + int64_t(r) * slices * kTile;
+  const int64_t stride = int64_t(a.slice_tiles) * kTile;  // words per slice region
+  const unsigned long long* cand = a.cand + int64_t(r) * slices * stride;
   const uint4* st = reinterpret_cast<const uint4*>(a.state) + int64_t(r) * slices;
   L.st = t < slices ? st[t] : uint4{0u, 0u, 0u, 0u};
   const int tps = window_tps(slices);
   const int sg = t / tps, sl = t % tps;
   L.own = sg < slices ? st[sg].x : 0u;
 #pragma unroll
-  for (int j = 0; j < kCap / kThreads; ++j) L.x[j] = sg < slices ? cand[int64_t(sg) * kTile + j * tps + sl] : 0ull;
+  for (int j = 0; j < kCap / kThreads; ++j) L.x[j] = sg < slices ? cand[sg * stride + j * tps + sl] : 0ull;
 }
 
 // The candidates gathered into sh.wa in slice order (offset `at` of slice t
@@ -948,11 +947,12 @@ __device__ __forceinline__ void window_loads(const TopkArgs& a, int r, int slice
 // whose slices hold more words than were read ahead, or whose window meets
 // more dense buckets than one pass lists.
 __device__ __forceinline__ void window_gather_sort(TopkShared& sh, const TopkArgs& a, int r, int slices, uint32_t C,
-                                                   uint32_t at, int lo, int hi, int32_t* out, int obase,
-                                                   const WindowLoads& L) {
+                                                   uint32_t at, uint32_t longest, int lo, int hi, int32_t* out,
+                                                   int obase, const WindowLoads& L) {
   const int t = threadIdx.x;
   constexpr int J = kJ;
-  const unsigned long long* cand = a.cand + int64_t(r) * slices * kTile;
+  const int64_t stride = int64_t(a.slice_tiles) * kTile;
+  const unsigned long long* cand = a.cand + int64_t(r) * slices * stride;
   const int tps = window_tps(slices);
   const int sg = t / tps, sl = t % tps;
   if (t < slices) {
@@ -961,29 +961,32 @@ __device__ __forceinline__ void window_gather_sort(TopkShared& sh, const TopkArg
   }
   lds_barrier();
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  bool rest = false;  // this slice holds more words than were read ahead
-  if (sg < slices) {
-    const int m = int(sh.cnt[sg]), o = int(sh.bins[sg]);
+  const int m = sg < slices ? int(sh.cnt[sg]) : 0, o = sg < slices ? int(sh.bins[sg]) : 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = j * tps + sl;
+    if (i < m) {
+      sh.wa[o + i] = L.x[j];
+      const uint32_t kx = uint32_t(L.x[j] >> 32);
+      kmin = min(kmin, kx);
+      kmax = max(kmax, kx);
+    }
+  }
+  // the rest of the longer slices (rows with skewed candidates), J*tps more
+  // words of every slice per round, all of a round's loads in flight at once
+  for (int b0 = J * tps; b0 < int(longest); b0 += J * tps) {
+    unsigned long long y[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int i = j * tps + sl;
-      if (i < m) {
-        sh.wa[o + i] = L.x[j];
-        const uint32_t kx = uint32_t(L.x[j] >> 32);
-        kmin = min(kmin, kx);
-        kmax = max(kmax, kx);
-      }
+      const int i = b0 + j * tps + sl;
+      y[j] = i < m ? cand[sg * stride + i] : 0ull;
     }
-    rest = m > J * tps;
-  }
-  // the rest of the longer slices (rows with skewed candidates)
-  if (block_any(rest, sh.red)) {
-    for (int g = 0; g < slices; ++g) {
-      const int m = int(sh.cnt[g]), o = int(sh.bins[g]);
-      for (int i = J * tps + t; i < m; i += kThreads) {
-        const unsigned long long y = cand[int64_t(g) * kTile + i];
-        sh.wa[o + i] = y;
-        const uint32_t ky = uint32_t(y >> 32);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int i = b0 + j * tps + sl;
+      if (i < m) {
+        sh.wa[o + i] = y[j];
+        const uint32_t ky = uint32_t(y[j] >> 32);
         kmin = min(kmin, ky);
         kmax = max(kmax, ky);
       }
@@ -1048,7 +1051,7 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
     return;
   }
   if (longest > uint32_t(J * tps)) {
-    window_gather_sort(sh, a, r, slices, C, at, lo, hi, out, obase, L);
+    window_gather_sort(sh, a, r, slices, C, at, longest, lo, hi, out, obase, L);
     return;
   }
   const unsigned long long mx = (static_cast<unsigned long long>(kmax) << 32) | 0xFFFFFFFFull;
@@ -1068,7 +1071,7 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
   const int next = int(sh.misc[6]);
   if (next == 0) return;
   if (next > kMaxWork) {
-    window_gather_sort(sh, a, r, slices, C, at, lo, hi, out, obase, L);
+    window_gather_sort(sh, a, r, slices, C, at, longest, lo, hi, out, obase, L);
     return;
   }
   sort_levels(sh, sh.u.wb, sh.wa, 1, next, 1, lo, hi, out, obase);
@@ -1144,23 +1147,49 @@ bool topk_use_split(int R, int max_n) {
   return max_n > 4 * kTile && R <= device_cu_count() / 2;
 }
 
-// Split workspace: the candidate words [R][slices][kTile], then the slice
-// counts [R][slices].
+// Tiles of kTile keys per slice: the fewest (a power of two up to
+// kMaxSliceTiles) that keep the candidate launch to one workgroup per CU, so
+// long rows do not queue several rounds of workgroups that each recompute
+// the pivot.
+static int split_tiles(int R, int max_n) {
+  int T = 1;
+  while (T < kMaxSliceTiles && int64_t(R) * ((max_n + kTile * T - 1) / (kTile * T)) > device_cu_count()) T *= 2;
+  return T;
+}
+
+static int split_slices(int max_n, int T) { return (max_n + kTile * T - 1) / (kTile * T); }
+
+static void launch_cand(const TopkArgs& a, int slices, hipStream_t stream) {
+  const dim3 grid(unsigned(a.R) * unsigned(slices));
+  switch (a.slice_tiles) {
+    case 1: topk_cand_kernel<1><<<grid, kThreads, 0, stream>>>(a, slices); break;
+    case 2: topk_cand_kernel<2><<<grid, kThreads, 0, stream>>>(a, slices); break;
+    case 4: topk_cand_kernel<4><<<grid, kThreads, 0, stream>>>(a, slices); break;
+    default: topk_cand_kernel<kMaxSliceTiles><<<grid, kThreads, 0, stream>>>(a, slices); break;
+  }
+}
+
+// Split workspace: the candidate words [R][slices][T * kTile], then the
+// slice records [R][slices] (uint4).
 size_t topk_split_ws_bytes(int R, int max_n) {
-  const size_t slices = size_t((max_n + kTile - 1) / kTile);
-  return size_t(R) * slices * kTile * sizeof(unsigned long long) + size_t(R) * slices * sizeof(uint4);
+  const int T = split_tiles(R, max_n);
+  const size_t slices = size_t(split_slices(max_n, T));
+  return size_t(R) * slices * T * kTile * sizeof(unsigned long long) + size_t(R) * slices * sizeof(uint4);
 }
 
 void topk_split_carve(void* ws, int R, int max_n, TopkArgs& a) {
-  const size_t slices = size_t((max_n + kTile - 1) / kTile);
+  const int T = split_tiles(R, max_n);
+  const size_t slices = size_t(split_slices(max_n, T));
+  a.slice_tiles = T;
   a.cand = static_cast<unsigned long long*>(ws);
-  a.state = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + size_t(R) * slices * kTile * sizeof(unsigned long long));
+  a.state = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) +
+                                        size_t(R) * slices * T * kTile * sizeof(unsigned long long));
 }
 
 hipError_t launch_topk_attn(const TopkArgs& ta, const AttnArgs& aa, const AttnPlan& plan, hipStream_t stream) {
   if (ta.R == 0) return hipSuccess;
-  const int slices = (ta.max_n + kTile - 1) / kTile;  // <= kThreads for rows up to 2^20 keys
-  topk_cand_kernel<<<dim3(unsigned(ta.R) * unsigned(slices)), kThreads, 0, stream>>>(ta, slices);
+  const int slices = split_slices(ta.max_n, ta.slice_tiles);  // <= kThreads for rows up to 2^23 keys
+  launch_cand(ta, slices, stream);
   const dim3 grid(unsigned(aa.R) * unsigned(plan.splits) * unsigned(plan.head_groups));
   topk_attn_kernel<false><<<grid, kThreads, 0, stream>>>(ta, aa, slices, plan.splits, plan.keys_per_split);
   hipError_t e = hipGetLastError();
@@ -1171,9 +1200,9 @@ hipError_t launch_topk_attn(const TopkArgs& ta, const AttnArgs& aa, const AttnPl
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
   if (a.state && a.cand && topk_use_split(a.R, a.max_n)) {
-    const int slices = (a.max_n + kTile - 1) / kTile;  // <= kThreads for rows up to 2^20 keys
+    const int slices = split_slices(a.max_n, a.slice_tiles);  // <= kThreads for rows up to 2^23 keys
     const int windows = (a.k + kWindow - 1) / kWindow;
-    topk_cand_kernel<<<dim3(unsigned(a.R) * unsigned(slices)), kThreads, 0, stream>>>(a, slices);
+    launch_cand(a, slices, stream);
     topk_window_kernel<<<dim3(unsigned(a.R) * unsigned(windows)), kThreads, 0, stream>>>(a, slices, windows);
     return hipGetLastError();
   }
