@@ -10,10 +10,10 @@
 // kernel is a key stream bound by HBM; it still needs the matrix cores,
 // because 64 flop/B at 8 TB/s is 512 TFLOP/s, three times the fp32 vector peak.
 //
-// Work split: one wave owns `keys_per_wave` consecutive keys of one query
-// and walks them in groups of 64 (4 MFMA column tiles of 16 keys); the
-// launch gives each CU one 4-wave workgroup and spreads all keys over the
-// CUs once. Key rows go from HBM straight into the wave's LDS stage buffers
+// Work split: one wave owns consecutive keys of one query and walks them in
+// groups of 64 (4 MFMA column tiles of 16 keys); the launch gives each CU one
+// 4-wave workgroup and spreads all keys over the CUs once (up to 64 queries:
+// shares of the CUs in proportion to the rows' actual lengths). Key rows go from HBM straight into the wave's LDS stage buffers
 // with 16-byte direct-to-LDS loads, all stages issued up front (after the
 // small query loads) so that the whole working set is in flight at once;
 // each group is multiplied as soon as its own loads have landed, while the
@@ -262,6 +262,57 @@ __device__ __forceinline__ void wait_ops(int n) {
   }
 }
 
+// Keys of query r: cache rows base .. base+n-1 of its sequence.
+__device__ __forceinline__ void query_range(const IndexArgs& a, int r, int64_t& base, int64_t& n) {
+  int b = a.q_seq ? a.q_seq[r] : r;
+  b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
+  const int qpos = a.q_pos ? a.q_pos[r] : a.seq_len[b] - 1;
+  n = qpos + 1 < a.max_n ? qpos + 1 : a.max_n;
+  if (n < 0) n = 0;
+  base = a.row_off[b];
+  if (base < 0 || base >= a.cache_rows) n = 0;
+  else if (n > a.cache_rows - base) n = a.cache_rows - base;
+}
+
+// Balanced form (R <= 64, a 1-D grid of G >= R workgroups): every wave works
+// out the same split from all the rows' lengths (lane r: row r), with no
+// barrier. Row r gets 1 + floor((G - R) * n_r / N) workgroups (N = sum n_r),
+// consecutive in the grid, and its keys in equal multiples of 64 per wave;
+// returns this workgroup's row, the row's base and length, the first key of
+// the workgroup and the keys per wave (workgroups past the shares get n = 0).
+__device__ __forceinline__ void balanced_split(const IndexArgs& a, int w, int G, int& r, int64_t& base, int64_t& n,
+                                               int64_t& wg_beg, int64_t& kpw) {
+  // a workgroup past every row's share keeps these: no key, nothing loaded
+  r = 0;
+  base = 0;
+  n = 0;
+  wg_beg = 0;
+  kpw = 64;
+  const int lane = threadIdx.x & 63;
+  int64_t bl = 0, nl = 0;
+  if (lane < a.R) query_range(a, lane, bl, nl);
+  // N as a float-free sum: lengths are below 2^31, R <= 64
+  unsigned long long tot = nl;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) tot += __shfl_xor(tot, d, 64);
+  uint32_t share = 0;
+  if (lane < a.R)
+    share = 1u + (tot ? uint32_t((unsigned long long)(G - a.R) * (unsigned long long)nl / tot) : 0u);
+  const uint32_t incl = wave_incl_scan(share);
+  const unsigned long long hit = __ballot(lane < a.R && uint32_t(w) < incl && uint32_t(w) >= incl - share);
+  if (hit == 0ull) return;
+  r = __ffsll(static_cast<long long>(hit)) - 1;
+  const uint32_t sh_r = __builtin_amdgcn_readlane(share, r);
+  const uint32_t first = __builtin_amdgcn_readlane(incl, r) - sh_r;
+  base = (int64_t(__builtin_amdgcn_readlane(uint32_t(uint64_t(bl) >> 32), r)) << 32) |
+         __builtin_amdgcn_readlane(uint32_t(bl), r);
+  n = __builtin_amdgcn_readlane(uint32_t(nl), r);
+  const int64_t per = (n + int64_t(sh_r) * kWaves - 1) / (int64_t(sh_r) * kWaves);
+  kpw = (per + 63) / 64 * 64;
+  if (kpw < 64) kpw = 64;
+  wg_beg = int64_t(w - int(first)) * kWaves * kpw;
+}
+
 template <int QK, int MT, int DI>
 __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, int keys_per_wave) {
   using C = KeyCfg<QK, DI>;
@@ -274,24 +325,28 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
   __shared__ __attribute__((aligned(16))) float s_w[64];
   __shared__ __attribute__((aligned(16))) uint32_t s_sc[kWaves][C::NS][QK == 2 ? 64 : 1];  // fp8 row scales
 
-  const int r = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;  // MFMA column: key within a 16-key tile
   const int grp = lane >> 4;  // K-slot group / C-row group
 
-  int b = a.q_seq ? a.q_seq[r] : r;
-  b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
-  const int qpos = a.q_pos ? a.q_pos[r] : a.seq_len[b] - 1;
-  int64_t n = qpos + 1 < a.max_n ? qpos + 1 : a.max_n;
-  const int64_t base = a.row_off[b];
-  if (base < 0 || base >= a.cache_rows) n = 0;
-  else if (n > a.cache_rows - base) n = a.cache_rows - base;
-
-  const int64_t wg_beg = int64_t(blockIdx.y) * kWaves * keys_per_wave;
+  // keys_per_wave > 0: query blockIdx.x, chunk blockIdx.y of that many keys
+  // per wave; 0: the balanced split over a 1-D grid
+  int r;
+  int64_t base, n, wg_beg, kpw64;
+  if (keys_per_wave > 0) {
+    r = blockIdx.x;
+    query_range(a, r, base, n);
+    kpw64 = keys_per_wave;
+    wg_beg = int64_t(blockIdx.y) * kWaves * kpw64;
+  } else {
+    balanced_split(a, blockIdx.x, gridDim.x, r, base, n, wg_beg, kpw64);
+  }
+  r = __builtin_amdgcn_readfirstlane(r);
   if (wg_beg >= n) return;  // the whole workgroup has no key
-  const int64_t s_beg = wg_beg + int64_t(wave) * keys_per_wave;
-  const int64_t s_end = s_beg + keys_per_wave < n ? s_beg + keys_per_wave : n;
+  const int keys_per_wave_r = int(kpw64);
+  const int64_t s_beg = wg_beg + int64_t(wave) * keys_per_wave_r;
+  const int64_t s_end = s_beg + keys_per_wave_r < n ? s_beg + keys_per_wave_r : n;
   const int groups = s_beg < s_end ? int((s_end - s_beg + 63) / 64) : 0;
 
   F qa[MT][NKS];
@@ -718,8 +773,16 @@ hipError_t launch_prefill(const IndexArgs& a, hipStream_t stream) {
 
 template <int QK, int MT, int DI>
 hipError_t launch_t(const IndexArgs& a, hipStream_t stream) {
-  // One 4-wave workgroup per CU (the stage buffers take most of the LDS);
-  // keys per wave: a multiple of 64 that spreads all keys over the CUs once.
+  // One 4-wave workgroup per CU (the stage buffers take most of the LDS).
+  // Up to 64 queries: the balanced split, which shares the CUs out by the
+  // rows' actual lengths (read on the device), so rows shorter than max_n
+  // leave no CU idle.
+  if (a.R <= 64) {
+    index_scores_kernel<QK, MT, DI><<<dim3(unsigned(device_cu_count())), kWaves * 64, 0, stream>>>(a, 0);
+    return hipGetLastError();
+  }
+  // Otherwise keys per wave: a multiple of 64 that spreads all keys over the
+  // CUs once, and a grid of (query, chunk).
   const int64_t total = int64_t(a.R) * a.max_n;
   const int64_t waves = int64_t(device_cu_count()) * kWaves;
   int64_t kpw = (total + waves - 1) / waves;
