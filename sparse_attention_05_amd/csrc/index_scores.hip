@@ -276,10 +276,12 @@ __device__ __forceinline__ void query_range(const IndexArgs& a, int r, int64_t& 
 
 // Balanced form (R <= 64, a 1-D grid of G >= R workgroups): every wave works
 // out the same split from all the rows' lengths (lane r: row r), with no
-// barrier. Row r gets 1 + floor((G - R) * n_r / N) workgroups (N = sum n_r),
-// consecutive in the grid, and its keys in equal multiples of 64 per wave;
-// returns this workgroup's row, the row's base and length, the first key of
-// the workgroup and the keys per wave (workgroups past the shares get n = 0).
+// barrier. Row r gets 1 + floor((G - R) * u_r / U) workgroups, u_r its
+// length in units of 1024 keys (rounded up) and U their sum (32-bit integer
+// arithmetic: the shares add up to at most G), consecutive in the grid, and
+// its keys in equal multiples of 64 per wave; returns this workgroup's row,
+// the row's base and length, the first key of the workgroup and the keys per
+// wave (a workgroup past the shares gets n = 0).
 __device__ __forceinline__ void balanced_split(const IndexArgs& a, int w, int G, int& r, int64_t& base, int64_t& n,
                                                int64_t& wg_beg, int64_t& kpw) {
   // a workgroup past every row's share keeps these: no key, nothing loaded
@@ -291,13 +293,15 @@ __device__ __forceinline__ void balanced_split(const IndexArgs& a, int w, int G,
   const int lane = threadIdx.x & 63;
   int64_t bl = 0, nl = 0;
   if (lane < a.R) query_range(a, lane, bl, nl);
-  // N as a float-free sum: lengths are below 2^31, R <= 64
-  unsigned long long tot = nl;
+  const uint32_t ul = uint32_t((nl + 1023) >> 10);  // < 2^22
+  uint32_t tot = ul;                                // < 2^28
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) tot += __shfl_xor(tot, d, 64);
   uint32_t share = 0;
-  if (lane < a.R)
-    share = 1u + (tot ? uint32_t((unsigned long long)(G - a.R) * (unsigned long long)nl / tot) : 0u);
+  if (lane < a.R) {
+    // (G - R) * ul < 2^10 * 2^22: 32 bits
+    share = 1u + (tot ? uint32_t(G - a.R) * ul / tot : 0u);
+  }
   const uint32_t incl = wave_incl_scan(share);
   const unsigned long long hit = __ballot(lane < a.R && uint32_t(w) < incl && uint32_t(w) >= incl - share);
   if (hit == 0ull) return;
@@ -306,10 +310,10 @@ __device__ __forceinline__ void balanced_split(const IndexArgs& a, int w, int G,
   const uint32_t first = __builtin_amdgcn_readlane(incl, r) - sh_r;
   base = (int64_t(__builtin_amdgcn_readlane(uint32_t(uint64_t(bl) >> 32), r)) << 32) |
          __builtin_amdgcn_readlane(uint32_t(bl), r);
-  n = __builtin_amdgcn_readlane(uint32_t(nl), r);
-  const int64_t per = (n + int64_t(sh_r) * kWaves - 1) / (int64_t(sh_r) * kWaves);
-  kpw = (per + 63) / 64 * 64;
-  if (kpw < 64) kpw = 64;
+  const uint32_t n32 = __builtin_amdgcn_readlane(uint32_t(nl), r);
+  n = n32;
+  const uint32_t per = (n32 + sh_r * kWaves - 1) / (sh_r * kWaves);
+  kpw = per < 64 ? 64 : int64_t((per + 63) / 64 * 64);
   wg_beg = int64_t(w - int(first)) * kWaves * kpw;
 }
 
