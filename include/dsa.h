@@ -193,6 +193,25 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
  */
 size_t dsa_workspace_size(int32_t entry, int32_t rows, int32_t max_len, int32_t k, int32_t H);
 
+/*
+ * dsa_check_indices -- debug validator of index arrays: the structure the
+ * top-k guarantees ("GLM-5 Notes", Replay: indices must be reproducible;
+ * the entries are positions of selected keys), checked without the scores.
+ * For query r with n = q_pos[r] + 1 and k_eff = min(k, n), an entry counts
+ * as bad when, among the first k_eff, it lies outside [0, n) or repeats an
+ * earlier valid one (each repeat counts once), or, past k_eff, it is not -1
+ * (q_pos[r] < 0: every entry must be -1).
+ * The count is ADDED to *n_bad (a device int32 the caller zeroes first; no
+ * memset is enqueued, so the call may be captured in a graph).
+ *
+ *   idx   [R, k] int32 (device);  q_pos [R] int32 (device);  k in 1 .. DSA_MAX_TOPK
+ *   n_bad device int32, accumulated with one atomic add per row with a bad entry
+ * Enqueued on `stream`; returns DSA_ERR_NULL / DSA_ERR_SHAPE /
+ * DSA_ERR_UNSUPPORTED for bad arguments before any launch.
+ */
+dsa_status dsa_check_indices(const int32_t* idx, const int32_t* q_pos, int32_t R, int32_t k,
+                             int32_t* n_bad, void* stream);
+
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int32_t status);
 

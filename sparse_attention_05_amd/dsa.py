@@ -34,6 +34,7 @@ SIGNATURES = {
     "dsa_decode_fused": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I64, _P, _P, _I32, _I32, _I32, _I32,
                                 _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
     "dsa_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "dsa_check_indices": (_I32, [_P, _P, _I32, _I32, _P, _P]),
     "dsa_status_string": (ctypes.c_char_p, [_I32]),
     "dsa_last_error": (ctypes.c_char_p, []),
 }
@@ -170,6 +171,19 @@ def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, row_off: torc
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "dsa_sparse_mla_attn")
     return out, lse
+
+
+def dsa_check_indices(idx: torch.Tensor, q_pos: torch.Tensor, *, n_bad: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Count of structurally bad entries of idx [R, k] (out of [0, q_pos+1),
+    repeated, or bad -1 padding), ADDED to n_bad (a zeroed int32 device
+    scalar is allocated when none is passed); returns n_bad."""
+    R, k = idx.shape
+    if n_bad is None:
+        n_bad = torch.zeros(1, dtype=torch.int32, device=idx.device)
+    st = lib.dsa_check_indices(_ptr(idx), _ptr(q_pos), R, k, _ptr(n_bad), _stream(stream))
+    _check(st, "dsa_check_indices")
+    return n_bad
 
 
 class DecodeCall:

@@ -116,6 +116,16 @@ def test_decode_rejects_small_workspace(dsa):
     assert st == dsa.DSA_ERR_DTYPE
 
 
+def test_check_indices_rejects(dsa):
+    lib = dsa.lib
+    assert lib.dsa_check_indices(A, A, 4, 2048, None, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_check_indices(None, A, 4, 2048, A, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_check_indices(A, A, -1, 2048, A, None) == dsa.DSA_ERR_SHAPE
+    assert lib.dsa_check_indices(A, A, 4, 0, A, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_check_indices(A, A, 4, 2049, A, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_check_indices(None, None, 0, 64, A, None) == dsa.DSA_OK  # nothing to check
+
+
 def test_workspace_sizes_are_aligned(dsa):
     for rows, k, H in [(1, 64, 8), (4, 2048, 64), (16, 2048, 64), (8192, 2048, 64)]:
         assert dsa.dsa_workspace_size(dsa.DSA_ENTRY_SPARSE_MLA, rows, 0, k, H) % 256 == 0

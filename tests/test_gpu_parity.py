@@ -398,6 +398,51 @@ def test_fused_split_decode_whole_window_with_tie_classes(dsa):
         assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k)), f"row {r}"
 
 
+def _bad_entries(idx, q_pos):
+    """numpy count of what dsa_check_indices counts (test-side restatement of
+    the structure a top-k index array must have)."""
+    bad = 0
+    R, k = idx.shape
+    for r in range(R):
+        n = int(q_pos[r]) + 1
+        ke = max(0, min(k, n))
+        head = idx[r, :ke]
+        ok = (head >= 0) & (head < n)
+        bad += int((~ok).sum())
+        vals = np.sort(head[ok])
+        bad += int((vals[1:] == vals[:-1]).sum())
+        bad += int((idx[r, ke:] != -1).sum())
+    return bad
+
+
+def test_check_indices_counts_planted_faults(dsa):
+    """The validator finds nothing in a real fused-decode index array, and
+    counts exactly the entries planted wrong: out of range, repeated, wrong
+    padding, a negative position, a row with no candidates."""
+    import torch
+    p = inputs.decode_config([3000, 2049, 700, 5000], seed=13, k=2048)
+    d = inputs.to_torch(p)
+    _, _, idx = _fused(dsa, p, d)
+    q_pos = torch.from_numpy(p.q_pos.astype(np.int32)).cuda()
+    assert int(dsa.dsa_check_indices(torch.from_numpy(idx).cuda(), q_pos).item()) == 0
+    bad = idx.copy()
+    bad[0, 5] = bad[0, 9]            # repeat
+    bad[0, 10] = 3000                # out of range (n = 3000)
+    bad[1, 0] = -3                   # negative
+    bad[2, 700] = 7                  # padding that is not -1
+    bad[2, 701] = 8
+    bad[3, 100] = bad[3, 101] = bad[3, 102]  # two repeats of one value
+    want = _bad_entries(bad, p.q_pos)
+    assert want == 7
+    got = dsa.dsa_check_indices(torch.from_numpy(bad).cuda(), q_pos)
+    assert int(got.item()) == want
+    # accumulation across calls, and q_pos < 0 (every entry must be -1)
+    neg = torch.full((1, 64), -1, dtype=torch.int32, device="cuda")
+    neg[0, 3] = 0
+    acc = dsa.dsa_check_indices(neg, torch.tensor([-1], dtype=torch.int32, device="cuda"), n_bad=got)
+    assert int(acc.item()) == want + 1
+
+
 # ------------------------------------------------------------------------------
 # causal prefill form (one sequence, a query per position)
 # ------------------------------------------------------------------------------
