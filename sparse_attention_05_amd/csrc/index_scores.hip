@@ -96,7 +96,9 @@ struct KeyCfg {
   static constexpr int GBYTES = GK * ROW;
   static constexpr int LOADS = GBYTES / 1024;                 // 1 KiB direct loads per group
   static constexpr int GLOADS = LOADS + (QK == 2 ? 1 : 0);     // + the row scales (fp8)
-  static constexpr int NS = GBYTES >= 32768 ? 1 : (32768 / GBYTES > 4 ? 4 : 32768 / GBYTES);  // stages
+  static constexpr int W = QK == 0 ? 4 : 8;                    // waves per workgroup (decode form)
+  static constexpr int WBUDGET = 131072 / W;                    // stage bytes per wave
+  static constexpr int NS = GBYTES >= WBUDGET ? 1 : (WBUDGET / GBYTES > 4 ? 4 : WBUDGET / GBYTES);  // stages
 };
 
 // One 16-byte direct-to-LDS load per lane: lane l's bytes land at LDS byte
@@ -282,8 +284,8 @@ __device__ __forceinline__ void query_range(const IndexArgs& a, int r, int64_t& 
 // its keys in equal multiples of 64 per wave; returns this workgroup's row,
 // the row's base and length, the first key of the workgroup and the keys per
 // wave (a workgroup past the shares gets n = 0).
-__device__ __forceinline__ void balanced_split(const IndexArgs& a, int w, int G, int& r, int64_t& base, int64_t& n,
-                                               int64_t& wg_beg, int64_t& kpw) {
+__device__ __forceinline__ void balanced_split(const IndexArgs& a, int w, int G, int waves, int& r, int64_t& base,
+                                               int64_t& n, int64_t& wg_beg, int64_t& kpw) {
   // a workgroup past every row's share keeps these: no key, nothing loaded
   r = 0;
   base = 0;
@@ -312,14 +314,15 @@ __device__ __forceinline__ void balanced_split(const IndexArgs& a, int w, int G,
          __builtin_amdgcn_readlane(uint32_t(bl), r);
   const uint32_t n32 = __builtin_amdgcn_readlane(uint32_t(nl), r);
   n = n32;
-  const uint32_t per = (n32 + sh_r * kWaves - 1) / (sh_r * kWaves);
+  const uint32_t per = (n32 + sh_r * waves - 1) / (sh_r * waves);
   kpw = per < 64 ? 64 : int64_t((per + 63) / 64 * 64);
-  wg_beg = int64_t(w - int(first)) * kWaves * kpw;
+  wg_beg = int64_t(w - int(first)) * waves * kpw;
 }
 
 template <int QK, int MT, int DI>
-__global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, int keys_per_wave) {
+__global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(IndexArgs a, int keys_per_wave) {
   using C = KeyCfg<QK, DI>;
+  constexpr int kWaves = C::W;
   constexpr int NKS = DI / 32;       // K-steps of 32 dims
   constexpr bool kQLds = QK != 0;    // bf16 query and weights staged through LDS
   constexpr int QCPR = DI / 8;       // 16-byte chunks per bf16 query row
@@ -344,7 +347,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_scores_kernel(IndexArgs a, 
     kpw64 = keys_per_wave;
     wg_beg = int64_t(blockIdx.y) * kWaves * kpw64;
   } else {
-    balanced_split(a, blockIdx.x, gridDim.x, r, base, n, wg_beg, kpw64);
+    balanced_split(a, blockIdx.x, gridDim.x, kWaves, r, base, n, wg_beg, kpw64);
   }
   r = __builtin_amdgcn_readfirstlane(r);
   if (wg_beg >= n) return;  // the whole workgroup has no key
@@ -777,6 +780,7 @@ hipError_t launch_prefill(const IndexArgs& a, hipStream_t stream) {
 
 template <int QK, int MT, int DI>
 hipError_t launch_t(const IndexArgs& a, hipStream_t stream) {
+  constexpr int kWaves = KeyCfg<QK, DI>::W;
   // One 4-wave workgroup per CU (the stage buffers take most of the LDS).
   // Up to 64 queries: the balanced split, which shares the CUs out by the
   // rows' actual lengths (read on the device), so rows shorter than max_n
