@@ -48,6 +48,7 @@ constexpr int kBins = 4096;          // 12-bit digits (64 groups of 64)
 constexpr int kCap = 4096;           // candidate capacity
 constexpr int kMaxSamples = 8192;    // score samples behind a pivot
 constexpr int kMaxSliceTiles = 8;    // tiles of kTile keys per slice of a split row
+constexpr int kBatch = 8;            // streamed tiles in flight per pass over a long row
 constexpr int kSmall = 32;           // rank-by-counting limit
 constexpr int kMaxWork = 16;         // dense buckets split per level
 constexpr int kFullBins = 1024;      // whole-row histogram: 10-bit digits
@@ -353,9 +354,21 @@ struct Row {
         });
       }
     } else {
+      // every SS-th index: the thread's indexes 4t + j*kTile that are
+      // multiples of SS, kBatch loads in flight at a time
       const int lg = __ffs(SS) - 1;
-      for (int i0 = 4 * int(threadIdx.x); i0 < n; i0 += kTile) {
-        if ((i0 & (SS - 1)) == 0) f(i0 >> lg, order_key(src[i0]));
+      for (int b0 = 4 * int(threadIdx.x); b0 < n; b0 += kTile * kBatch) {
+        float x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i0 = b0 + u * kTile;
+          x[u] = i0 < n && (i0 & (SS - 1)) == 0 ? src[i0] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i0 = b0 + u * kTile;
+          if (i0 < n && (i0 & (SS - 1)) == 0) f(i0 >> lg, order_key(x[u]));
+        }
       }
     }
   }
@@ -369,12 +382,24 @@ struct Row {
         f((e >> 2) * kTile + 4 * int(threadIdx.x) + (e & 3), key[e]);
       });
     } else {
-      for (int i0 = 4 * int(threadIdx.x); i0 < n; i0 += kTile) {
-        const float4 v = *reinterpret_cast<const float4*>(src + i0);
-        f(i0 + 0, order_key(v.x));
-        f(i0 + 1, i0 + 1 < n ? order_key(v.y) : 0u);
-        f(i0 + 2, i0 + 2 < n ? order_key(v.z) : 0u);
-        f(i0 + 3, i0 + 3 < n ? order_key(v.w) : 0u);
+      // streamed from memory, kBatch tiles' loads in flight before any is used
+      for (int b0 = 4 * int(threadIdx.x); b0 < n; b0 += kTile * kBatch) {
+        float4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i0 = b0 + u * kTile;
+          v[u] = i0 < n ? *reinterpret_cast<const float4*>(src + i0) : float4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i0 = b0 + u * kTile;
+          if (i0 < n) {
+            f(i0 + 0, order_key(v[u].x));
+            f(i0 + 1, i0 + 1 < n ? order_key(v[u].y) : 0u);
+            f(i0 + 2, i0 + 2 < n ? order_key(v[u].z) : 0u);
+            f(i0 + 3, i0 + 3 < n ? order_key(v[u].w) : 0u);
+          }
+        }
       }
     }
   }
