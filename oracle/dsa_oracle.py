@@ -43,6 +43,12 @@ score, because the top-k ranks the float32 scores the API emits):
        O[r, h, :] = sum_j softmax(l)_j * C[idx_j, :512]
        LSE[r, h] = log sum_j exp(l_j)
 
+   The latent cache may also be stored in FP8 ("Zhipu AI / GLM", section
+   11.4, lists an FP8 KV cache among GLM-5's rollout measures; the pages fix
+   no scale granularity): the reading here is one float32 scale per cached
+   token, C[s, :] = e4m3(code[s, :]) * scale[s], dequantised before any
+   arithmetic, so the attention above is unchanged.
+
 The pages print no worked numbers for any of these stages; the tests pin
 this module to closed forms, brute force on tiny inputs, library routines
 (torch scaled_dot_product_attention for the dense case, torch's fp8 and
@@ -179,12 +185,29 @@ def sparse_mla_row(q_abs_r: np.ndarray, rows: np.ndarray, scale: float):
     return out, lse
 
 
+def latent_dtype(prob) -> str:
+    """Storage dtype of the latent cache (the activation dtype unless set)."""
+    return getattr(prob, "latent_dtype", None) or prob.act_dtype
+
+
+def latent_rows(prob, cache_rows: np.ndarray) -> np.ndarray:
+    """Latent rows (float64) at the absolute cache positions ``cache_rows``;
+    fp8 rows are e4m3(code) * float32(row scale)."""
+    cache_rows = np.asarray(cache_rows, dtype=np.int64)
+    dt = latent_dtype(prob)
+    c = decode(prob.latent[cache_rows], dt)
+    if dt == "fp8_e4m3":
+        sc = np.asarray(prob.latent_scale, dtype=np.float32)[cache_rows].astype(np.float64)
+        c = c * sc[:, None]
+    return c
+
+
 def selected_rows(prob, r: int, idx_row: np.ndarray) -> np.ndarray:
     """Latent rows (float64) of the keys named by idx_row (entries < 0 skipped)."""
     b = int(prob.q_seq[r])
     sel = np.asarray(idx_row)
     sel = sel[sel >= 0].astype(np.int64)
-    return decode(prob.latent[int(prob.row_off[b]) + sel], prob.act_dtype)
+    return latent_rows(prob, int(prob.row_off[b]) + sel)
 
 
 def sparse_mla(prob, idx: np.ndarray, rows=None):

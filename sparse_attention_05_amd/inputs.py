@@ -39,7 +39,8 @@ class DSAProblem:
 
     Indexer: ``q_idx`` [R, H_I, D_I], ``head_w`` [R, H_I] fp32, ``k_idx``
     [rows, D_I] (+ ``k_scale`` [rows] bf16 bits when the keys are fp8).
-    Attention: ``q_abs`` [R, H, 576], ``latent`` [rows, 576].
+    Attention: ``q_abs`` [R, H, 576], ``latent`` [rows, 576] (+ ``latent_scale``
+    [rows] float32 when the latent rows are fp8).
     Sequence b owns cache rows ``row_off[b] .. row_off[b]+seq_len[b]-1``;
     query r belongs to sequence ``q_seq[r]`` at position ``q_pos[r]`` and its
     candidates are keys 0..q_pos[r] of that sequence.
@@ -61,9 +62,16 @@ class DSAProblem:
     q_pos: np.ndarray
     k: int
     scale: float
-    act_dtype: str  # dtype of q_idx, q_abs and latent
+    act_dtype: str  # dtype of q_idx, q_abs (and latent unless latent_dtype is set)
     key_dtype: str  # dtype of k_idx
     meta: dict = field(default_factory=dict)
+    latent_dtype: Optional[str] = None          # "fp8_e4m3": latent stored as codes ...
+    latent_scale: Optional[np.ndarray] = None   # ... with one float32 scale per cache row
+
+    @property
+    def kv_dtype(self) -> str:
+        """Storage dtype of the latent cache."""
+        return self.latent_dtype or self.act_dtype
 
     @property
     def R(self) -> int:
@@ -174,6 +182,41 @@ def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0,
     return out.reshape(shape)
 
 
+def _normal_e4m3_rows(rng: np.random.Generator, rows: int, dim: int, std: float = 1.0,
+                      chunk_rows: int = 1 << 13):
+    """N(0, std^2) rows [rows, dim] stored as OCP E4M3FN codes with one
+    float32 scale per row, scale = (row max |x|) / 448 (1 for an all-zero
+    row), code = nearest e4m3 of x / scale (clipped to +-448).
+
+    Block i of ``chunk_rows`` rows comes from the stream's bit generator
+    jumped i + 1 times, as in _normal_bf16.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    codes = np.empty((rows, dim), dtype=np.uint8)
+    scales = np.empty(rows, dtype=np.float32)
+    base = rng.bit_generator
+
+    def fill(i):
+        lo, hi = i * chunk_rows, min(rows, (i + 1) * chunk_rows)
+        v = np.random.Generator(base.jumped(i + 1)).standard_normal((hi - lo, dim), dtype=np.float32)
+        if std != 1.0:
+            v *= np.float32(std)
+        mx = np.abs(v).max(axis=1)
+        sc = np.where(mx > 0, mx / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        scales[lo:hi] = sc
+        codes[lo:hi] = f32_to_e4m3_codes(np.clip(v / sc[:, None], -448.0, 448.0))
+
+    n_chunks = (rows + chunk_rows - 1) // chunk_rows
+    if n_chunks <= 1:
+        for i in range(n_chunks):
+            fill(i)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(n_chunks)))
+    return codes, scales
+
+
 def _streams(seed: int):
     children = np.random.SeedSequence(seed).spawn(len(_STREAMS))
     return {name: np.random.Generator(np.random.PCG64(c)) for name, c in zip(_STREAMS, children)}
@@ -229,7 +272,7 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
                   H: int = 64, k: int = 2048, key_dtype: str = "bf16",
                   boost_frac: float = 0.0, boost_sigma: float = 4.0,
                   tie_levels: int = 0, latent_std: float = 0.1, q_abs_std: float = 1.0,
-                  name: str = "decode") -> DSAProblem:
+                  latent_dtype: str = "bf16", name: str = "decode") -> DSAProblem:
     """Decode batch: one new query per sequence at its last position.
 
     * indexer queries N(0,1) bf16, head weights U(0,1) fp32, keys N(0,1);
@@ -246,7 +289,8 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
       ``tie_levels`` values, all exact in fp32, so large tie classes straddle
       the k-th rank;
     * absorbed queries N(0, q_abs_std^2) bf16, latent rows N(0, latent_std^2)
-      bf16.
+      bf16, or with ``latent_dtype="fp8_e4m3"`` e4m3 codes with a float32
+      per-row scale (row max |x| / 448).
     """
     st = _streams(seed)
     B = len(seq_lens)
@@ -297,7 +341,13 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
                 raise ValueError(f"unknown key dtype {key_dtype}")
 
     q_abs = _normal_bf16(st["q_abs"], (B, H, LATENT_DIM), std=q_abs_std)
-    latent = _normal_bf16(st["latent"], (rows, LATENT_DIM), std=latent_std)
+    latent_scale = None
+    if latent_dtype == "bf16":
+        latent = _normal_bf16(st["latent"], (rows, LATENT_DIM), std=latent_std)
+    elif latent_dtype == "fp8_e4m3":
+        latent, latent_scale = _normal_e4m3_rows(st["latent"], rows, LATENT_DIM, std=latent_std)
+    else:
+        raise ValueError(f"unknown latent dtype {latent_dtype}")
     seq_len = np.asarray(seq_lens, np.int32)
     return DSAProblem(
         name=name, q_idx=q_idx, head_w=head_w, k_idx=k_store, k_scale=k_scale,
@@ -305,6 +355,7 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
         q_seq=np.arange(B, dtype=np.int32), q_pos=seq_len - 1,
         k=k, scale=1.0 / math.sqrt(192.0), act_dtype="bf16", key_dtype=key_dtype,
         meta={"seed": seed, "boost_frac": boost_frac, "tie_levels": tie_levels},
+        latent_dtype=None if latent_dtype == "bf16" else latent_dtype, latent_scale=latent_scale,
     )
 
 
@@ -356,6 +407,11 @@ def workload(name: str, seed: int = 0) -> DSAProblem:
     if name == "decode-128k-fp8":
         return decode_config([131072] * 7 + [200000], seed=seed, key_dtype="fp8_e4m3",
                              boost_frac=0.02, name=name)
+    if name == "decode-32k-fp8kv":
+        return decode_config([32768] * 4, seed=seed, latent_dtype="fp8_e4m3", name=name)
+    if name == "decode-128k-fp8kv":
+        return decode_config([131072] * 7 + [200000], seed=seed, key_dtype="fp8_e4m3",
+                             boost_frac=0.02, latent_dtype="fp8_e4m3", name=name)
     if name == "ties-64k":
         return decode_config([65536] * 16, seed=seed, tie_levels=8, name=name)
     if name == "prefill-8k":
@@ -383,7 +439,8 @@ def to_torch(prob: DSAProblem, device="cuda"):
         q_idx=t(prob.q_idx, prob.act_dtype), head_w=t(prob.head_w, "f32"),
         k_idx=t(prob.k_idx, prob.key_dtype),
         k_scale=None if prob.k_scale is None else t(prob.k_scale.view(np.int16), None),
-        q_abs=t(prob.q_abs, prob.act_dtype), latent=t(prob.latent, prob.act_dtype),
+        q_abs=t(prob.q_abs, prob.act_dtype), latent=t(prob.latent, prob.kv_dtype),
+        latent_scale=None if prob.latent_scale is None else t(prob.latent_scale, "f32"),
         row_off=t(prob.row_off.astype(np.int64), None), seq_len=t(prob.seq_len.astype(np.int32), None),
         q_seq=t(prob.q_seq.astype(np.int32), None), q_pos=t(prob.q_pos.astype(np.int32), None),
     )

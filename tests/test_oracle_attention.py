@@ -111,3 +111,72 @@ def test_negative_indices_are_skipped():
     q = O.decode(p.q_abs, "f32")
     ref = _sdpa(q[0], lat[[5, 100, 7]], p.scale)
     np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-14)
+
+
+# ---- FP8 (e4m3) latent rows with one float32 scale per row ----------------------------------
+
+def _fp8_problem(codes, row_scale, q, scale, idx_rows):
+    """A one-sequence problem whose latent cache holds e4m3 codes; q [R, H, 576]."""
+    import types
+    n = codes.shape[0]
+    return types.SimpleNamespace(
+        q_abs=np.asarray(q, np.float32), act_dtype="f32", latent=np.asarray(codes, np.uint8),
+        latent_dtype="fp8_e4m3", latent_scale=np.asarray(row_scale, np.float32),
+        row_off=np.zeros(1, np.int64), q_seq=np.zeros(q.shape[0], np.int32), scale=scale,
+        R=q.shape[0]), np.asarray(idx_rows, np.int32)
+
+
+def _torch_e4m3(codes):
+    """Independent decoder: torch's float8_e4m3fn view, widened to float64."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def test_fp8_latent_golden_hand_case():
+    g = json.load(open(os.path.join(GOLDEN, "attention_fp8_hand.json")))
+    q = np.zeros((1, 1, 576), np.float32)
+    for d, v in g["q_sparse"].items():
+        q[0, 0, int(d)] = v
+    codes = np.zeros((len(g["codes_sparse"]), 576), np.uint8)
+    for j, r in enumerate(g["codes_sparse"]):
+        for d, v in r.items():
+            codes[j, int(d)] = v
+    prob, idx = _fp8_problem(codes, g["row_scale"], q, g["scale"], [[0, 1]])
+    out, lse = O.sparse_mla(prob, idx)
+    want = np.zeros(512)
+    for d, v in g["out_sparse"].items():
+        want[int(d)] = v
+    # q was stored as float32: ln 3 carries float32 rounding into the weights
+    np.testing.assert_allclose(out[0, 0], want, rtol=1e-7, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], g["lse"], rtol=1e-7)
+
+
+def test_fp8_latent_single_key_is_its_scaled_row():
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 256, size=(5, 576)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x30      # no NaN codes
+    sc = np.array([0.5, 3.0, 1e-3, 7.25, 1.0], np.float32)
+    q = rng.standard_normal((3, 576)).astype(np.float32)
+    rows64 = _torch_e4m3(codes) * sc.astype(np.float64)[:, None]
+    for s in range(5):
+        prob, idx = _fp8_problem(codes, sc, q[None], 0.5, [[s, -1, -1]])
+        out, lse = O.sparse_mla(prob, idx)
+        np.testing.assert_array_equal(out[0], np.broadcast_to(rows64[s, :512], (3, 512)))
+        np.testing.assert_allclose(lse[0], 0.5 * (q.astype(np.float64) @ rows64[s]), rtol=1e-13)
+
+
+def test_fp8_latent_equals_bf16_when_rows_are_exact():
+    """Power-of-two row scales keep every dequantised value exact in bf16: the
+    fp8 problem then equals the bf16 problem holding those values."""
+    p8 = inputs.decode_config([300, 70], seed=5, H=16, k=64, latent_dtype="fp8_e4m3")
+    p8.latent_scale = np.exp2(np.round(np.log2(p8.latent_scale))).astype(np.float32)
+    vals = (_torch_e4m3(p8.latent) * p8.latent_scale.astype(np.float64)[:, None]).astype(np.float32)
+    bits = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), vals)
+    import dataclasses
+    pb = dataclasses.replace(p8, latent=bits, latent_dtype=None, latent_scale=None)
+    _, idx, out8, lse8 = O.dsa_forward(p8)
+    _, idxb, outb, lseb = O.dsa_forward(pb)
+    np.testing.assert_array_equal(idx, idxb)
+    np.testing.assert_allclose(out8, outb, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse8, lseb, rtol=0, atol=1e-13)

@@ -66,6 +66,28 @@ def _fp8_no_scale(prob, b, n):
     return O.decode(prob.k_idx[lo:lo + n], prob.key_dtype)
 
 
+def _fp8_latent_no_scale(prob, cache_rows):
+    return O.decode(prob.latent[np.asarray(cache_rows, np.int64)], O.latent_dtype(prob))
+
+
+def _fp8_latent_scale_of_next_row(prob, cache_rows):
+    cache_rows = np.asarray(cache_rows, np.int64)
+    sc = np.asarray(prob.latent_scale, np.float64)
+    nxt = np.minimum(cache_rows + 1, sc.shape[0] - 1)
+    nxt = np.where(nxt == cache_rows, np.maximum(cache_rows - 1, 0), nxt)
+    return O.decode(prob.latent[cache_rows], O.latent_dtype(prob)) * sc[nxt][:, None]
+
+
+def _fp8_latent_scaled_keys_only(prob, cache_rows):
+    rows = _orig_latent_rows(prob, cache_rows)
+    raw = O.decode(prob.latent[np.asarray(cache_rows, np.int64)], O.latent_dtype(prob))
+    rows[:, :512] = raw[:, :512]
+    return rows
+
+
+_orig_latent_rows = O.latent_rows
+
+
 CASES = [
     ("index_scores_row", _no_relu, [TI.test_relu_zeroes_negative_dots, TI.test_golden_hand_case]),
     ("index_scores_row", _w_reversed, [TI.test_head_weights_follow_their_head]),
@@ -76,6 +98,12 @@ CASES = [
     ("sparse_mla_row", _value_from_rope_end, [TA.test_single_key_gives_its_value_rows, TA.test_golden_hand_case]),
     ("sparse_mla_row", _no_scale, [TA.test_dense_equals_sdpa_when_k_covers_context]),
     ("sparse_mla_row", _latent_only_logits, [TA.test_golden_hand_case]),
+    ("latent_rows", _fp8_latent_no_scale, [TA.test_fp8_latent_golden_hand_case,
+                                           TA.test_fp8_latent_single_key_is_its_scaled_row]),
+    ("latent_rows", _fp8_latent_scale_of_next_row, [TA.test_fp8_latent_golden_hand_case,
+                                                    TA.test_fp8_latent_single_key_is_its_scaled_row]),
+    ("latent_rows", _fp8_latent_scaled_keys_only, [TA.test_fp8_latent_golden_hand_case,
+                                                   TA.test_fp8_latent_single_key_is_its_scaled_row]),
 ]
 
 

@@ -89,3 +89,18 @@ def test_prefill_subset_rows_match_full_rows():
     assert np.array_equal(sub.q_idx, full.q_idx[[0, 150, 299]])
     assert np.array_equal(sub.q_abs, full.q_abs[[0, 150, 299]])
     assert np.array_equal(sub.k_idx, full.k_idx)
+
+
+def test_fp8_latent_rows_round_trip():
+    p = inputs.decode_config([600, 300], seed=3, H_I=16, H=16, k=64, latent_dtype="fp8_e4m3")
+    assert p.latent.dtype == np.uint8 and p.latent.shape == (900, 576)
+    assert p.latent_scale.dtype == np.float32 and (p.latent_scale > 0).all()
+    c = O.latent_rows(p, np.arange(900))
+    assert np.isfinite(c).all()
+    mx = np.abs(c).max(axis=1)
+    # scale = rowmax / 448: the largest entry of every row lands on code 448 (within rounding)
+    np.testing.assert_allclose(mx, 448.0 * p.latent_scale.astype(np.float64), rtol=1e-6)
+    # N(0, 0.1^2) draws, 3 significant bits: the spread survives quantisation
+    assert 0.08 < float(c.std()) < 0.12
+    again = inputs.decode_config([600, 300], seed=3, H_I=16, H=16, k=64, latent_dtype="fp8_e4m3")
+    assert np.array_equal(p.latent, again.latent) and np.array_equal(p.latent_scale, again.latent_scale)
