@@ -37,6 +37,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def latent_row_bytes(p) -> int:
+    """Bytes of one gathered latent row: 576 elements (+4 B row scale for fp8)."""
+    esz = {"bf16": 2, "f32": 4, "fp8_e4m3": 1}
+    return 576 * esz[p.kv_dtype] + (4 if p.kv_dtype == "fp8_e4m3" else 0)
+
+
+def attention_bytes(p) -> int:
+    """Algorithmic bytes of one attention launch over k_eff keys per query:
+    the selected latent rows, the indices, the queries and the outputs."""
+    esz = {"bf16": 2, "f32": 4}
+    k_eff = sum(min(p.k, int(x)) for x in p.seq_len.astype(int))
+    return (k_eff * latent_row_bytes(p) + p.B * p.k * 4 + p.B * p.H * 576 * esz[p.act_dtype]
+            + p.B * p.H * (512 + 1) * 4)
+
+
 def step_bytes(p) -> int:
     """Algorithmic HBM bytes of one decode step: every candidate indexer key,
     every selected latent row, the queries, weights and the outputs."""
@@ -44,7 +59,7 @@ def step_bytes(p) -> int:
     n = p.seq_len.astype(int)
     keys = int(n.sum()) * p.D_I * esz[p.key_dtype] + (int(n.sum()) * 2 if p.key_dtype == "fp8_e4m3" else 0)
     k_eff = [min(p.k, int(x)) for x in n]
-    gather = sum(k_eff) * 576 * esz[p.act_dtype]
+    gather = sum(k_eff) * latent_row_bytes(p)
     small = (p.B * p.H_I * p.D_I * esz[p.act_dtype] + p.B * p.H_I * 4 + p.B * p.H * 576 * esz[p.act_dtype]
              + p.B * p.H * 512 * 4 + p.B * p.H * 4 + p.B * p.k * 4)
     return keys + gather + small
@@ -286,7 +301,7 @@ def main():
     sets = [base] + [type(base)(**{k: (v.clone() if v is not None else None) for k, v in vars(base).items()})
                      for _ in range(n_sets - 1)]
     calls = [dsa.DecodeCall(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len, max_len,
-                            p.k, p.scale, k_scale=d.k_scale) for d in sets]
+                            p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale) for d in sets]
     log(f"bench: {n_sets} input sets of {sb / 1e6:.1f} MB algorithmic traffic per step")
 
     # determinism check on set 0 (not timed)
@@ -354,8 +369,8 @@ def main():
         c()
         for l in range(1, share_layers):
             d = sets[(i + l) % n_sets]
-            dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, c.idx, p.scale, out=outs[l - 1][0],
-                                    lse=outs[l - 1][1], workspace=aws)
+            dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, c.idx, p.scale, latent_scale=d.latent_scale,
+                                    out=outs[l - 1][0], lse=outs[l - 1][1], workspace=aws)
 
     for i in range(min(args.warmup, n_sets)):
         block(i)
@@ -368,6 +383,24 @@ def main():
     block_ms = start.elapsed_time(end) / args.steps
     log(f"bench: index-shared block of {share_layers} layers {block_ms * 1e3:.2f} us "
         f"(vs {share_layers} fused steps {share_layers * ms_step * 1e3:.2f} us)")
+
+    # ---- the attention alone over recorded indices: K back-to-back launches --------------
+    def attn(i):
+        d = sets[i % n_sets]
+        dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, calls[i % n_sets].idx, p.scale,
+                                latent_scale=d.latent_scale, out=outs[0][0], lse=outs[0][1], workspace=aws)
+
+    for i in range(min(args.warmup, n_sets)):
+        attn(i)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        attn(i)
+    end.record()
+    torch.cuda.synchronize()
+    attn_us = start.elapsed_time(end) * 1e3 / args.steps
+    ab = attention_bytes(p)
+    log(f"bench: attention {attn_us:.2f} us/launch, {ab / (attn_us * 1e-6) / 1e9:,.0f} GB/s algorithmic")
 
     # ---- the dominant kernel alone: K back-to-back indexer launches ----------------------
     scores = [torch.empty((p.B, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
@@ -400,8 +433,10 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if p.act_dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": args.workload, "batch": p.B, "context": max_len, "k": p.k,
                    "indexer_heads": p.H_I, "indexer_dim": p.D_I, "indexer_keys": p.key_dtype,
-                   "mla_heads": p.H, "latent_dim": 576, "input_sets": n_sets},
+                   "mla_heads": p.H, "latent_dim": 576, "latent": p.kv_dtype, "input_sets": n_sets},
         "step_hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
+        "attention": {"us_per_launch": attn_us, "bytes_per_launch": ab,
+                      "gbps": ab / (attn_us * 1e-6) / 1e9},
         "graph_ms_per_step": graph_ms, "graph_replays_equal_eager": graph_same,
         "index_share": {"layers": share_layers, "ms_per_block": block_ms,
                         "tokens_per_s_per_block": p.B / (block_ms * 1e-3),

@@ -146,14 +146,20 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos
  * the same indices give bitwise identical outputs (index replay: "GLM-5
  * Notes", Replay; "GLM-5: from Vibe Coding...", section 3.2).
  *
- *   q_abs    [R, H, 576]  dtype DSA_BF16 or DSA_F32 (latent has the same dtype)
- *   latent   [cache_rows, 576], 16-B aligned
+ *   q_abs    [R, H, 576]  dtype DSA_BF16 or DSA_F32
+ *   latent   [cache_rows, 576], 16-B aligned, latent_dtype = dtype, or
+ *            DSA_FP8_E4M3 with dtype DSA_BF16: OCP e4m3 codes (576 bytes per
+ *            row) dequantised as code * latent_scale[row] (an FP8 KV cache,
+ *            "Zhipu AI / GLM", section 11.4; one float32 scale per row is
+ *            this library's reading). latent_scale [cache_rows] fp32, 4-B
+ *            aligned, required for fp8 and ignored otherwise.
  *   idx      [R, k] int32;  k in 1 .. DSA_MAX_TOPK;  H in 1 .. 128
  *   out      [R, H, 512] fp32;  lse [R, H] fp32 or NULL
  *   workspace: dsa_workspace_size(DSA_ENTRY_SPARSE_MLA, R, 0, k, H) bytes
  * A row with no valid index gets out = 0 and lse = -inf.
  */
 dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* latent,
+                               int32_t latent_dtype, const float* latent_scale,
                                int64_t cache_rows, const int64_t* row_off, int32_t B,
                                const int32_t* q_seq, const int32_t* idx, int32_t k,
                                int32_t R, int32_t H, float scale, float* out, float* lse,
@@ -170,7 +176,8 @@ dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* lat
  *
  *   q_idx [B, H_I, D_I], head_w [B, H_I], k_idx/k_scale as in dsa_index_scores
  *   q_abs [B, H, 576], latent [cache_rows, 576]: act_dtype (DSA_BF16 or
- *   DSA_F32) is the dtype of q_idx, q_abs and latent; k_dtype as in
+ *   DSA_F32) is the dtype of q_idx and q_abs; latent_dtype and
+ *   latent_scale as in dsa_sparse_mla_attn; k_dtype as in
  *   dsa_index_scores.
  *   seq_len [B] int32 (1 <= seq_len[b] <= max_len), row_off [B] int64
  *   out [B, H, 512] fp32, lse [B, H] or NULL, idx_out [B, k] int32 or NULL
@@ -178,7 +185,8 @@ dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* lat
  */
 dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* k_idx,
                             int32_t k_dtype, const uint16_t* k_scale, const void* q_abs,
-                            const void* latent, int32_t act_dtype, int64_t cache_rows,
+                            const void* latent, int32_t act_dtype, int32_t latent_dtype,
+                            const float* latent_scale, int64_t cache_rows,
                             const int64_t* row_off, const int32_t* seq_len, int32_t B,
                             int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k,
                             float scale, float* out, float* lse, int32_t* idx_out,

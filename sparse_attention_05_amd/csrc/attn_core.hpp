@@ -303,6 +303,38 @@ __device__ __forceinline__ int64_t seq_base(const AttnArgs& a, int r) {
   return a.row_off[b];
 }
 
+// Epilogue of a workgroup: the row sums over the lanes and waves, then the
+// normalised output rows as float4 (splits == 1) or the split's unnormalised
+// output, its maximum and its sum.
+__device__ __forceinline__ void write_result(const AttnArgs& a, int r, int split, int splits, int h, int wave,
+                                             int col, int grp, const f32x4 (&acc)[8], float m_run, float l_part,
+                                             float (*s_l)[kGroupHeads]) {
+  float l_w = l_part + wave_shfl_xor(l_part, 16);
+  l_w += wave_shfl_xor(l_w, 32);
+  if (grp == 0) s_l[wave][col] = l_w;
+  __syncthreads();
+  const float L = ((s_l[0][col] + s_l[1][col]) + s_l[2][col]) + s_l[3][col];
+  if (h >= a.H) return;
+  const int64_t rh = int64_t(r) * a.H + h;
+  const bool final_out = splits == 1;
+  const float inv = final_out ? (L > 0.f ? 1.f / L : 0.f) : 1.f;
+  float* dst = final_out ? a.out + rh * kValueDim
+                         : static_cast<float*>(a.ws) + ((int64_t(r) * splits + split) * a.H + h) * kValueDim;
+#pragma unroll
+  for (int vt = 0; vt < 8; ++vt)
+    *reinterpret_cast<float4*>(dst + 128 * wave + 16 * vt + 4 * grp) =
+        float4{acc[vt][0] * inv, acc[vt][1] * inv, acc[vt][2] * inv, acc[vt][3] * inv};
+  if (wave == 0 && grp == 0) {
+    if (final_out) {
+      if (a.lse) a.lse[rh] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      float* ml = static_cast<float*>(a.ws) + int64_t(a.R) * splits * a.H * kValueDim;
+      const int64_t slot = (int64_t(r) * splits + split) * a.H + h;
+      *reinterpret_cast<float2*>(ml + 2 * slot) = float2{m_run, L};
+    }
+  }
+}
+
 // The chunk loop and the epilogue over keys j_beg .. j_end-1 of query r, for
 // waves 0..3 of the workgroup; s_idx[j - j_beg] holds the raw index of key j
 // (-1: none), base the sequence's first cache row. Writes the normalised
@@ -506,31 +538,280 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
     }
   }
 
-  // ---- epilogue: row sums over the lanes and waves, then O rows as float4 ----------------
-  float l_w = l_part + wave_shfl_xor(l_part, 16);
-  l_w += wave_shfl_xor(l_w, 32);
-  if (grp == 0) s_l[wave][col] = l_w;
-  __syncthreads();
-  const float L = ((s_l[0][col] + s_l[1][col]) + s_l[2][col]) + s_l[3][col];
-  if (h >= a.H) return;
-  const int64_t rh = int64_t(r) * a.H + h;
-  const bool final_out = splits == 1;
-  const float inv = final_out ? (L > 0.f ? 1.f / L : 0.f) : 1.f;
-  float* dst = final_out ? a.out + rh * kValueDim
-                         : static_cast<float*>(a.ws) + ((int64_t(r) * splits + split) * a.H + h) * kValueDim;
+  write_result(a, r, split, splits, h, wave, col, grp, acc, m_run, l_part, s_l);
+}
+
+
+// ---- FP8 latent rows: e4m3 codes with one float32 scale per cache row ----------------------
+// C[s, :] = e4m3(code[s, :]) * scale[s]. The codes convert exactly to bf16
+// (every e4m3 value is a bf16 value), so q.c and p.c run on the same bf16
+// MFMA; the row scale stays outside the products: it multiplies key j's
+// logit (l_j = scale * s_j * (q . code_j)) and its softmax weight before the
+// p.c (O = sum_j (p_j s_j) code_j / sum_j p_j).
+// A chunk of 64 rows takes 36,864 bytes: wave w's rows 16w .. 16w+15 form a
+// block of 9,216 bytes in which 16-byte piece p (0..35) of row i sits at
+// 1024*(p/4) + 64*i + 16*(p%4) (blk8_off). Lane l loads row 16w + l/4, pieces
+// 4m + l%4 for m = 0..8, and the scale of row 16w + l%16 into the wave's
+// 64-word scale slot (four copies of its 16 scales), so a chunk is ten direct
+// loads per wave.
+// q.c: lane (col, grp) reads piece 4kk + grp of key row col (16 codes, one
+// contiguous KiB per read over the wave) and feeds K-steps 2kk and 2kk+1 with
+// its two halves; the query fragments use the same dims per K-slot.
+// p.c: the value operand comes from the key-major rows through the
+// transposing byte read (ds_read_b64_tr_b8: lane n of a 16-lane group names 8
+// bytes of row n/2, and receives byte n of the group's 8 rows), converted to
+// bf16 in registers.
+constexpr int kBlock8 = 16 * kLatentDim;
+constexpr int kBuf8 = 4 * kBlock8;
+constexpr int kLoads8 = kLatentDim / 64;   // 1-KiB row loads per wave per chunk (then one for the scales)
+constexpr int kPRow8 = kChunkKeys + 8;     // P^T row (bf16): 144 bytes, 16-byte aligned reads
+static_assert(kGroupHeads * kQPitch * 16 <= kBuf8, "the staged query fits one fp8 buffer");
+
+__device__ __forceinline__ int blk8_off(int row, int p) {
+  return kBlock8 * (row >> 4) + 1024 * (p >> 2) + 64 * (row & 15) + 16 * (p & 3);
+}
+
+// 4-byte direct-to-LDS load (lane l's word lands at lds + 4*l), waited for
+// like dma16.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+struct Smem8 {
+  char buf[2 * kBuf8] __attribute__((aligned(1024)));
+  float sc[2][4][64] __attribute__((aligned(16)));  // [buffer][wave]: scales of the wave's 16 keys, 4 copies
+  __bf16 s_p[kGroupHeads * kPRow8] __attribute__((aligned(16)));  // P^T as [head][key], scaled
+  float s_max[4][kGroupHeads];
+  float s_l[4][kGroupHeads];
+};
+
+struct BGather8 {
+  const char* src;    // this lane's row + 16*(lane%4) (row 0 when missing: not loaded)
+  const float* ssrc;  // scale of row 16w + lane%16 (row 0 when missing)
+  uint32_t lds;       // LDS address of the wave's block
+  uint32_t slds;      // LDS address of the wave's scale slot
+  bool live;          // this lane's row is present
+  uint32_t ok;        // 16-bit mask of present rows
+};
+
+__device__ __forceinline__ BGather8 bgather8_plan(const AttnArgs& a, int64_t base, const int* s_idx, int c,
+                                                  char* buf, float* sc, int wave, int lane) {
+  const int* si = s_idx + kChunkKeys * c + 16 * wave;
+  const int s = si[lane >> 2];
+  const int64_t row = base + s;
+  BGather8 g;
+  g.live = s >= 0 && base >= 0 && row < a.cache_rows;
+  const unsigned long long okm = __ballot(g.live && (lane & 3) == 0);  // bit 4i: row i
+  uint32_t ok = 0;
 #pragma unroll
-  for (int vt = 0; vt < 8; ++vt)
-    *reinterpret_cast<float4*>(dst + 128 * wave + 16 * vt + 4 * grp) =
-        float4{acc[vt][0] * inv, acc[vt][1] * inv, acc[vt][2] * inv, acc[vt][3] * inv};
-  if (wave == 0 && grp == 0) {
-    if (final_out) {
-      if (a.lse) a.lse[rh] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
-    } else {
-      float* ml = static_cast<float*>(a.ws) + int64_t(a.R) * splits * a.H * kValueDim;
-      const int64_t slot = (int64_t(r) * splits + split) * a.H + h;
-      *reinterpret_cast<float2*>(ml + 2 * slot) = float2{m_run, L};
-    }
+  for (int i = 0; i < 16; ++i) ok |= uint32_t((okm >> (4 * i)) & 1ull) << i;
+  g.ok = ok;
+  g.src = static_cast<const char*>(a.latent) + (g.live ? row : 0) * kLatentDim + 16 * (lane & 3);
+  const int s2 = si[lane & 15];
+  const int64_t row2 = base + s2;
+  const bool live2 = s2 >= 0 && base >= 0 && row2 < a.cache_rows;
+  g.ssrc = a.latent_scale + (live2 ? row2 : 0);
+  char* blk = buf + kBlock8 * wave;
+  g.lds = lds_addr(blk);
+  g.slds = lds_addr(sc + 64 * wave);
+  if (!g.live) {
+#pragma unroll
+    for (int m = 0; m < kLoads8; ++m) *reinterpret_cast<uint4*>(blk + 1024 * m + 16 * lane) = uint4{0u, 0u, 0u, 0u};
   }
+  return g;
+}
+
+// Direct load m (0 .. kLoads8) of a planned fp8 gather; the last one is the scales.
+__device__ __forceinline__ void bgather8_load(const BGather8& g, int m) {
+  if (m < kLoads8) {
+    const char* p = g.src;
+    asm volatile("" : "+v"(p));  // the address is formed here, not hoisted
+    if (g.live) dma16(p + 64 * m, g.lds + 1024 * m);
+  } else {
+    dma4(g.ssrc, g.slds);
+  }
+}
+
+// Query fragments for the fp8 K-slot order: K-step 2kk + hf of lane (col,
+// grp) holds dims 64kk + 16grp + 8hf .. +8 (staged piece 8kk + 2grp + hf).
+__device__ __forceinline__ void read_q8(const char* src, bool hv, int col, int grp, bf16x8 (&qf)[18]) {
+#pragma unroll
+  for (int kk = 0; kk < 9; ++kk)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * (kQPitch * col + 8 * kk + 2 * grp + hf));
+      qf[2 * kk + hf] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
+    }
+}
+
+// fp8 logits of this wave's 16 keys, before the row scales: S^T = code[16 x 576] . Q^T.
+// LOADS: direct load kk of the next chunk's gather rides on piece kk (the
+// scale load after the loop).
+template <bool LOADS>
+__device__ __forceinline__ f32x4 qc_fp8(const char* rp, const bf16x8 (&qf)[18], const BGather8& gn) {
+  f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  constexpr int D = 3;
+  uint4 fr[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) fr[i] = *reinterpret_cast<const uint4*>(rp + 1024 * i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < kLoads8; ++kk) {
+    const uint4 x = fr[kk % D];
+    if (kk + D < kLoads8) fr[kk % D] = *reinterpret_cast<const uint4*>(rp + 1024 * (kk + D));
+    part[0] = mfma_k32(fp8x8_to_bf16(uint2{x.x, x.y}), qf[2 * kk], part[0]);
+    part[1] = mfma_k32(fp8x8_to_bf16(uint2{x.z, x.w}), qf[2 * kk + 1], part[1]);
+    if constexpr (LOADS) bgather8_load(gn, kk);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LOADS) bgather8_load(gn, kLoads8);
+  return part[0] + part[1];
+}
+
+// attend() for fp8 latent rows (bf16 queries); same decomposition, split
+// order and epilogue.
+__device__ __forceinline__ void attend8(const AttnArgs& a, int r, int split, int splits, int hg, int j_beg,
+                                       int j_end, int64_t base, const int* s_idx, Smem8& sm) {
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int h = hg * kGroupHeads + col;
+  const int nchunks = j_end > j_beg ? (j_end - j_beg + kChunkKeys - 1) / kChunkKeys : 0;
+
+  bf16x8 qf[18];
+  uint32_t ok[2] = {0u, 0u};
+  if (nchunks > 0) {
+    // chunk 0 and the staged query (in buffer 1) in one round trip
+    const BGather8 g = bgather8_plan(a, base, s_idx, 0, sm.buf, &sm.sc[0][0][0], wave, lane);
+#pragma unroll
+    for (int m = 0; m <= kLoads8; ++m) bgather8_load(g, m);
+    ok[0] = g.ok;
+    stage_q(a, r, hg, sm.buf + kBuf8, wave, lane);
+    vm_wait_all();
+    __syncthreads();
+    read_q8(sm.buf + kBuf8, h < a.H, col, grp, qf);
+    __syncthreads();  // every wave has its fragments: buffer 1 is free
+  }
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int vt = 0; vt < 8; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+  const float scale2 = a.scale * kLog2e;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int bi = c & 1;
+    char* buf = sm.buf + bi * kBuf8;
+    if (c > 0) vm_wait_all();  // this wave's rows and scales of chunk c have landed
+    const uint32_t okc = ok[bi];
+
+    // ---- logits of this wave's 16 keys --------------------------------------------------
+    const char* rp = buf + kBlock8 * wave + 64 * col + 16 * grp;
+    f32x4 sacc;
+    if (c == 0 && nchunks > 1) {  // buffer 1 is free since the query was read
+      const BGather8 gn = bgather8_plan(a, base, s_idx, 1, sm.buf + kBuf8, &sm.sc[1][0][0], wave, lane);
+      ok[1] = gn.ok;
+      sacc = qc_fp8<true>(rp, qf, gn);
+    } else {
+      sacc = qc_fp8<false>(rp, qf, BGather8{});
+    }
+    const float4 s4 = *reinterpret_cast<const float4*>(&sm.sc[bi][wave][4 * grp]);  // keys 4grp + i
+    float sk[4] = {s4.x, s4.y, s4.z, s4.w};
+    float x[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool live = (okc >> (4 * grp + i)) & 1u;
+      sk[i] = live ? sk[i] : 0.f;
+      x[i] = live ? (sacc[i] * sk[i]) * scale2 : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    if (grp == 0) sm.s_max[wave][col] = mx;
+    __syncthreads();  // maxima visible; every wave is done with chunk c-1 and has its rows of chunk c
+    const float cmax = fmaxf(fmaxf(sm.s_max[0][col], sm.s_max[1][col]), fmaxf(sm.s_max[2][col], sm.s_max[3][col]));
+    const bool pc_loads = c + 1 < nchunks && c >= 1;
+    BGather8 gn{};
+    if (pc_loads) {
+      gn = bgather8_plan(a, base, s_idx, c + 1, sm.buf + (bi ^ 1) * kBuf8, &sm.sc[bi ^ 1][0][0], wave, lane);
+      ok[bi ^ 1] = gn.ok;
+    }
+
+    const float m_new = fmaxf(m_run, cmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+    __bf16 pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = exp2f(x[i] - m_use);
+      psum += e;
+      pv[i] = static_cast<__bf16>(e * sk[i]);
+    }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int vt = 0; vt < 8; ++vt) acc[vt] *= alpha;
+    }
+    {
+      __bf16* prow = sm.s_p + col * kPRow8 + 16 * wave + 4 * grp;
+      const uint32_t w0 = uint32_t(__builtin_bit_cast(uint16_t, pv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[1])) << 16);
+      const uint32_t w1 = uint32_t(__builtin_bit_cast(uint16_t, pv[2])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[3])) << 16);
+      *reinterpret_cast<uint2*>(prow) = uint2{w0, w1};
+    }
+    __syncthreads();  // P^T of all 64 keys in LDS
+
+    // ---- O^T[128*wave + 16*vt + (0..15)][head] += code^T . (P s)^T over the 64 keys ------
+    // K-slot 8*grp + i <-> key 32*kq + 8*grp + i.
+    bf16x8 pf[2];
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq)
+      pf[kq] = *reinterpret_cast<const bf16x8*>(sm.s_p + col * kPRow8 + 32 * kq + 8 * grp);
+    // value fragment of step q = (kq = q/8, vt = q%8): lane (col, grp) names 8
+    // bytes of row 32kq + 8grp + col/2, value dims 128*wave + 16vt + 8(col%2) ..,
+    // that is piece 8*wave + vt, half col%2
+    auto vfrag = [&](int q) -> bf16x8 {
+      const int kq = q >> 3, vt = q & 7;
+      const char* p0 = buf + blk8_off(32 * kq + 8 * grp + (col >> 1), 8 * wave + vt) + 8 * (col & 1);
+      typedef int v2i __attribute__((ext_vector_type(2)));
+      const v2i w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(lds_ptr)p0);
+      return fp8x8_to_bf16(uint2{uint32_t(w.x), uint32_t(w.y)});
+    };
+    auto pc = [&](auto loads) {
+      constexpr bool LOADS = decltype(loads)::value;
+      constexpr int D = 3;
+      bf16x8 vr[D];
+#pragma unroll
+      for (int i = 0; i < D; ++i) vr[i] = vfrag(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const bf16x8 af = vr[q % D];
+        if (q + D < 16) vr[q % D] = vfrag(q + D);
+        acc[q & 7] = mfma_k32(af, pf[q >> 3], acc[q & 7]);
+        if constexpr (LOADS) {
+          if (q <= kLoads8) bgather8_load(gn, q);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (pc_loads) pc(std::true_type{});
+    else pc(std::false_type{});
+  }
+
+  write_result(a, r, split, splits, h, wave, col, grp, acc, m_run, l_part, sm.s_l);
 }
 
 }  // namespace attn

@@ -43,11 +43,25 @@ dsa_status check_index_args(const void* q, int q_dtype, const float* w, const vo
   return DSA_OK;
 }
 
-dsa_status check_attn_args(const void* q_abs, int dtype, const void* latent, int64_t cache_rows,
-                           const int64_t* row_off, int B, const int32_t* idx, int k, int R, int H,
-                           const float* out) {
+// The latent cache is stored in the activation dtype, or as fp8 codes with a
+// float32 row scale next to bf16 queries.
+dsa_status check_latent(int dtype, int latent_dtype, const float* latent_scale) {
+  if (latent_dtype == DSA_FP8_E4M3) {
+    if (dtype != DSA_BF16) return DSA_ERR_DTYPE;
+    if (!latent_scale) return DSA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(latent_scale) & 3u) return DSA_ERR_ALIGN;
+    return DSA_OK;
+  }
+  return latent_dtype == dtype ? DSA_OK : DSA_ERR_DTYPE;
+}
+
+dsa_status check_attn_args(const void* q_abs, int dtype, const void* latent, int latent_dtype,
+                           const float* latent_scale, int64_t cache_rows, const int64_t* row_off, int B,
+                           const int32_t* idx, int k, int R, int H, const float* out) {
   if (!q_abs || !latent || !row_off || !idx || !out) return DSA_ERR_NULL;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  const dsa_status lt = check_latent(dtype, latent_dtype, latent_scale);
+  if (lt != DSA_OK) return lt;
   if (R < 0 || B < 1 || cache_rows < 1) return DSA_ERR_SHAPE;
   if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
   if (H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
@@ -136,24 +150,27 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos
   return e == hipSuccess ? DSA_OK : hip_fail(e);
 }
 
-dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* latent, int64_t cache_rows,
-                               const int64_t* row_off, int32_t B, const int32_t* q_seq, const int32_t* idx,
-                               int32_t k, int32_t R, int32_t H, float scale, float* out, float* lse,
-                               void* workspace, size_t ws_bytes, void* stream) {
-  dsa_status st = check_attn_args(q_abs, dtype, latent, cache_rows, row_off, B, idx, k, R, H, out);
+dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* latent, int32_t latent_dtype,
+                               const float* latent_scale, int64_t cache_rows, const int64_t* row_off, int32_t B,
+                               const int32_t* q_seq, const int32_t* idx, int32_t k, int32_t R, int32_t H,
+                               float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  dsa_status st = check_attn_args(q_abs, dtype, latent, latent_dtype, latent_scale, cache_rows, row_off, B, idx,
+                                  k, R, H, out);
   if (st != DSA_OK) return st;
   if (!q_seq && R != B) return DSA_ERR_SHAPE;
   const AttnPlan plan = plan_attention(R, H, k);
   if (plan.ws_bytes && (!workspace || ws_bytes < plan.ws_bytes)) return DSA_ERR_WORKSPACE;
   if (plan.ws_bytes && !aligned16(workspace)) return DSA_ERR_ALIGN;
-  AttnArgs a{q_abs, dtype, latent, cache_rows, row_off, B, q_seq, idx, k, R, H, scale, out, lse, workspace};
+  AttnArgs a{q_abs, dtype, latent, latent_dtype, latent_scale, cache_rows, row_off, B, q_seq, idx, k, R, H,
+             scale, out, lse, workspace};
   hipError_t e = launch_sparse_mla(a, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : hip_fail(e);
 }
 
 dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* k_idx, int32_t k_dtype,
                             const uint16_t* k_scale, const void* q_abs, const void* latent, int32_t act_dtype,
-                            int64_t cache_rows, const int64_t* row_off, const int32_t* seq_len, int32_t B,
+                            int32_t latent_dtype, const float* latent_scale, int64_t cache_rows, const int64_t* row_off, const int32_t* seq_len, int32_t B,
                             int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k, float scale,
                             float* out, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
                             void* stream) {
@@ -162,6 +179,8 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
   if (st != DSA_OK) return st;
   if (!seq_len || !q_abs || !latent || !out) return DSA_ERR_NULL;
   if (act_dtype != DSA_F32 && act_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  st = check_latent(act_dtype, latent_dtype, latent_scale);
+  if (st != DSA_OK) return st;
   if (max_len > kMaxTopkRow) return DSA_ERR_UNSUPPORTED;
   if (k < 1 || k > DSA_MAX_TOPK || H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
   if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
@@ -186,7 +205,8 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
   TopkArgs ta{scores, L.ld, nullptr, seq_len, B, max_len, k, idx, split ? sample : nullptr, L.ld_sample,
               nullptr, nullptr};
   const AttnPlan plan = plan_attention(B, H, k);
-  AttnArgs aa{q_abs, act_dtype, latent, cache_rows, row_off, B, nullptr, idx, k, B, H, scale, out, lse, attn_ws};
+  AttnArgs aa{q_abs, act_dtype, latent, latent_dtype, latent_scale, cache_rows, row_off, B, nullptr, idx, k, B,
+              H, scale, out, lse, attn_ws};
   if (split && act_dtype == DSA_BF16) {  // few long rows: selection fused with the attention
     topk_split_carve(ws + L.topk, B, max_len, ta);
     e = launch_topk_attn(ta, aa, plan, s);

@@ -42,6 +42,16 @@ __device__ __forceinline__ f32x4 mfma_k32(const f32x8& a, const f32x8& b, f32x4 
   return c;
 }
 
+// OCP e4m3 -> bf16 is exact (3 mantissa bits fit in 7, every e4m3 exponent
+// fits bf16's range); v_cvt_scalef32_pk_bf16_fp8 converts two codes per call.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 c) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -63,6 +63,8 @@ struct AttnArgs {
   const void* q;
   int dtype;
   const void* latent;
+  int latent_dtype;            // dtype, or kFP8 (e4m3 codes) with bf16 queries
+  const float* latent_scale;   // fp8 latent: one scale per cache row
   int64_t cache_rows;
   const int64_t* row_off;
   int B;

@@ -69,16 +69,6 @@ __device__ __forceinline__ float relu(float x) {
   return __builtin_amdgcn_fmed3f(x, 0.f, __builtin_inff());
 }
 
-// OCP e4m3 -> bf16 is exact (3 mantissa bits fit in 7, every e4m3 exponent
-// fits bf16's range); v_cvt_scalef32_pk_bf16_fp8 converts two codes per call.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 c) {
-  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false);
-  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true);
-  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false);
-  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true);
-  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
 // Keys of a group sit in LDS as rows of DI elements, the 16-byte chunks of
 // row k permuted (XOR) by k mod 8 or k mod 16 (by k mod CPR for shorter
 // rows): the B-operand reads of 8 (16) consecutive keys at one chunk offset

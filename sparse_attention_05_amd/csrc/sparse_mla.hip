@@ -40,9 +40,12 @@ namespace {
 
 using namespace attn;
 
-template <bool F32>
+// M: kF32 (fp32 queries and rows), kBF16, or kFP8 (bf16 queries, e4m3 rows
+// with a row scale).
+template <int M>
 __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, int splits, int kps) {
-  __shared__ Smem<F32> sm;
+  constexpr bool F32 = M == kF32;
+  __shared__ typename std::conditional<M == kFP8, Smem8, Smem<F32>>::type sm;
   __shared__ int s_idx[kMaxTopk];  // raw indices of the range; wave w owns entries 64c + 16w + (0..15)
   const int HG = (a.H + kGroupHeads - 1) / kGroupHeads;
   int r, split, hg;
@@ -64,9 +67,13 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, in
     const int j = j_beg + e;
     s_idx[e] = j < j_end ? a.idx[int64_t(r) * a.k + j] : -1;
   }
-  QFrag<F32> qf[18];  // bf16: staged and read by attend itself
-  if constexpr (F32) load_q<F32>(a, r, h, grp, qf);
-  attend<F32>(a, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, sm);
+  if constexpr (M == kFP8) {
+    attend8(a, r, split, splits, hg, j_beg, j_end, base, s_idx, sm);
+  } else {
+    QFrag<F32> qf[18];  // bf16: staged and read by attend itself
+    if constexpr (F32) load_q<F32>(a, r, h, grp, qf);
+    attend<F32>(a, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, sm);
+  }
 }
 
 // ---- many queries: one workgroup per query for all (<= 64) heads ---------------------
@@ -480,13 +487,14 @@ AttnPlan plan_attention(int R, int H, int k) {
 
 hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
-  if (plan.wide && a.dtype != kF32) {
+  if (plan.wide && a.dtype == kBF16 && a.latent_dtype == kBF16) {
     sparse_mla_wide_kernel<<<dim3(unsigned(a.R)), kAttnThreads, 0, stream>>>(a, plan.keys_per_split);
     return hipGetLastError();
   }
   const dim3 grid(unsigned(a.R) * unsigned(plan.splits) * unsigned(plan.head_groups));
-  if (a.dtype == kF32) sparse_mla_kernel<true><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
-  else sparse_mla_kernel<false><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
+  if (a.latent_dtype == kFP8) sparse_mla_kernel<kFP8><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
+  else if (a.dtype == kF32) sparse_mla_kernel<kF32><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
+  else sparse_mla_kernel<kBF16><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_attn_combine(a, plan, stream);

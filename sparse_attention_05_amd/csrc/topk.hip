@@ -1125,12 +1125,13 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int s
 // output, then its waves 0..3 run the same attention core as the attention
 // kernel over those keys. Same split plan and same core: the same bits as
 // selection followed by the attention kernel on the recorded indices.
-template <bool F32>
+// M: kBF16 (bf16 latent rows) or kFP8 (e4m3 rows with a row scale).
+template <int M>
 __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnArgs aa, int slices, int splits,
                                                              int kps) {
   __shared__ union Shared {
     TopkShared sel;
-    attn::Smem<F32> att;
+    typename std::conditional<M == kFP8, attn::Smem8, attn::Smem<false>>::type att;
   } u;
   __shared__ int s_idx[kMaxTopk];
   const int HG = (aa.H + attn::kGroupHeads - 1) / attn::kGroupHeads;
@@ -1138,8 +1139,6 @@ __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnAr
   attn::map_block(blockIdx.x, aa.R, splits, HG, r, split, hg);
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int lane = t & 63;
-  const int col = lane & 15, grp = lane >> 4;
   // The selection's global loads go out first, in one round trip: the
   // candidate counts and words, the row's length and first cache row.
   WindowLoads L;
@@ -1160,9 +1159,12 @@ __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnAr
   if (hg == 0)
     for (int i = t; i < j_end - j_beg; i += kThreads) ta.idx[int64_t(r) * k + j_beg + i] = s_idx[i];
   if (wave >= 4) return;  // barriers below count the four attention waves only
-  attn::QFrag<F32> qf[18];  // bf16: staged and read by attend itself
-  if constexpr (F32) attn::load_q<F32>(aa, r, hg * attn::kGroupHeads + col, grp, qf);
-  attn::attend<F32>(aa, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, u.att);
+  if constexpr (M == kFP8) {
+    attn::attend8(aa, r, split, splits, hg, j_beg, j_end, base, s_idx, u.att);
+  } else {
+    bf16x8 qf[18];  // staged and read by attend itself
+    attn::attend<false>(aa, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, u.att);
+  }
 }
 
 
@@ -1216,7 +1218,8 @@ hipError_t launch_topk_attn(const TopkArgs& ta, const AttnArgs& aa, const AttnPl
   const int slices = split_slices(ta.max_n, ta.slice_tiles);  // <= kThreads for rows up to 2^23 keys
   launch_cand(ta, slices, stream);
   const dim3 grid(unsigned(aa.R) * unsigned(plan.splits) * unsigned(plan.head_groups));
-  topk_attn_kernel<false><<<grid, kThreads, 0, stream>>>(ta, aa, slices, plan.splits, plan.keys_per_split);
+  if (aa.latent_dtype == kFP8) topk_attn_kernel<kFP8><<<grid, kThreads, 0, stream>>>(ta, aa, slices, plan.splits, plan.keys_per_split);
+  else topk_attn_kernel<kBF16><<<grid, kThreads, 0, stream>>>(ta, aa, slices, plan.splits, plan.keys_per_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_attn_combine(aa, plan, stream);

@@ -29,10 +29,10 @@ SIGNATURES = {
     "dsa_index_scores": (_I32, [_P, _I32, _P, _P, _I32, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                 _P, _I64, _P]),
     "dsa_topk": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
-    "dsa_sparse_mla_attn": (_I32, [_P, _I32, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _F32, _P, _P,
-                                   _P, _SZ, _P]),
-    "dsa_decode_fused": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I64, _P, _P, _I32, _I32, _I32, _I32,
-                                _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
+    "dsa_sparse_mla_attn": (_I32, [_P, _I32, _P, _I32, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _F32,
+                                   _P, _P, _P, _SZ, _P]),
+    "dsa_decode_fused": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _I32, _I32, _I32,
+                                _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
     "dsa_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "dsa_check_indices": (_I32, [_P, _P, _I32, _I32, _P, _P]),
     "dsa_status_string": (ctypes.c_char_p, [_I32]),
@@ -151,11 +151,13 @@ def dsa_topk(scores: torch.Tensor, q_pos: torch.Tensor, max_n: int, k: int, *,
 
 
 def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, row_off: torch.Tensor,
-                        idx: torch.Tensor, scale: float, *, q_seq: Optional[torch.Tensor] = None,
+                        idx: torch.Tensor, scale: float, *, latent_scale: Optional[torch.Tensor] = None,
+                        q_seq: Optional[torch.Tensor] = None,
                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                         want_lse: bool = True, workspace: Optional[torch.Tensor] = None,
                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Sparse absorbed MLA: (out [R, H, 512] fp32, lse [R, H] fp32)."""
+    """Sparse absorbed MLA: (out [R, H, 512] fp32, lse [R, H] fp32). A uint8
+    (or float8_e4m3fn) latent holds e4m3 codes scaled by latent_scale [rows]."""
     R, H, _ = q_abs.shape
     k = idx.shape[1]
     dev = q_abs.device
@@ -166,7 +168,8 @@ def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, row_off: torc
     nbytes = dsa_workspace_size(DSA_ENTRY_SPARSE_MLA, R, 0, k, H)
     workspace = _workspace(nbytes, workspace, dev)
     st = lib.dsa_sparse_mla_attn(
-        _ptr(q_abs), _dtype_code(q_abs), _ptr(latent), latent.shape[0], _ptr(row_off), row_off.numel(),
+        _ptr(q_abs), _dtype_code(q_abs), _ptr(latent), _dtype_code(latent), _ptr(latent_scale), latent.shape[0],
+        _ptr(row_off), row_off.numel(),
         _ptr(q_seq), _ptr(idx), k, R, H, float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "dsa_sparse_mla_attn")
@@ -192,8 +195,8 @@ class DecodeCall:
     allocation. Used where per-step host overhead matters."""
 
     def __init__(self, q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
-                 scale: float, *, k_scale=None, out=None, lse=None, idx_out=None, want_lse=True,
-                 record_idx=True, workspace=None):
+                 scale: float, *, k_scale=None, latent_scale=None, out=None, lse=None, idx_out=None,
+                 want_lse=True, record_idx=True, workspace=None):
         B, H_I, D_I = q_idx.shape
         H = q_abs.shape[1]
         dev = q_idx.device
@@ -203,12 +206,13 @@ class DecodeCall:
             torch.empty((B, k), dtype=torch.int32, device=dev)
         nbytes = dsa_workspace_size(DSA_ENTRY_DECODE, B, max_len, k, H)
         self.workspace = _workspace(nbytes, workspace, dev)
-        if _dtype_code(q_idx) != _dtype_code(q_abs) or _dtype_code(q_abs) != _dtype_code(latent):
-            raise TypeError("q_idx, q_abs and latent must share one dtype")
-        self._keep = (q_idx, head_w, k_idx, k_scale, q_abs, latent, row_off, seq_len)
+        if _dtype_code(q_idx) != _dtype_code(q_abs):
+            raise TypeError("q_idx and q_abs must share one dtype")
+        self._keep = (q_idx, head_w, k_idx, k_scale, q_abs, latent, latent_scale, row_off, seq_len)
         self._args = (
             _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _dtype_code(k_idx), _ptr(k_scale), _ptr(q_abs), _ptr(latent),
-            _dtype_code(q_abs), k_idx.shape[0], _ptr(row_off), _ptr(seq_len), B, max_len, H_I, D_I, H, k,
+            _dtype_code(q_abs), _dtype_code(latent), _ptr(latent_scale), k_idx.shape[0], _ptr(row_off),
+            _ptr(seq_len), B, max_len, H_I, D_I, H, k,
             float(scale), _ptr(self.out), _ptr(self.lse), _ptr(self.idx), _ptr(self.workspace),
             self.workspace.numel() * self.workspace.element_size())
 
@@ -219,10 +223,10 @@ class DecodeCall:
 
 
 def dsa_decode_fused(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
-                     scale: float, *, k_scale=None, out=None, lse=None, idx_out=None, want_lse=True,
-                     record_idx=True, workspace=None, stream=None):
+                     scale: float, *, k_scale=None, latent_scale=None, out=None, lse=None, idx_out=None,
+                     want_lse=True, record_idx=True, workspace=None, stream=None):
     """One decode step; returns (out [B,H,512], lse [B,H] or None, idx [B,k] or None)."""
     call = DecodeCall(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len, k, scale,
-                      k_scale=k_scale, out=out, lse=lse, idx_out=idx_out, want_lse=want_lse,
-                      record_idx=record_idx, workspace=workspace)
+                      k_scale=k_scale, latent_scale=latent_scale, out=out, lse=lse, idx_out=idx_out,
+                      want_lse=want_lse, record_idx=record_idx, workspace=workspace)
     return call(stream)

@@ -89,13 +89,18 @@ def test_topk_rejects(dsa):
 def test_sparse_mla_rejects(dsa):
     lib = dsa.lib
     def call(**kw):
-        a = dict(q=A, dt=1, lat=A, rows=100, off=A, B=4, qseq=None, idx=A, k=2048, R=4, H=64, out=A, ws=None, wsb=0)
+        a = dict(q=A, dt=1, lat=A, ldt=1, lsc=None, rows=100, off=A, B=4, qseq=None, idx=A, k=2048, R=4, H=64,
+                 out=A, ws=None, wsb=0)
         a.update(kw)
-        return lib.dsa_sparse_mla_attn(a["q"], a["dt"], a["lat"], a["rows"], a["off"], a["B"], a["qseq"],
-                                       a["idx"], a["k"], a["R"], a["H"], 0.1, a["out"], None, a["ws"],
+        return lib.dsa_sparse_mla_attn(a["q"], a["dt"], a["lat"], a["ldt"], a["lsc"], a["rows"], a["off"], a["B"],
+                                       a["qseq"], a["idx"], a["k"], a["R"], a["H"], 0.1, a["out"], None, a["ws"],
                                        a["wsb"], None)
     assert call(idx=None) == dsa.DSA_ERR_NULL
-    assert call(dt=2) == dsa.DSA_ERR_DTYPE
+    assert call(dt=2, ldt=2) == dsa.DSA_ERR_DTYPE
+    assert call(ldt=0) == dsa.DSA_ERR_DTYPE                  # latent dtype differs, not fp8
+    assert call(ldt=2) == dsa.DSA_ERR_NULL                   # fp8 latent without its row scales
+    assert call(dt=0, ldt=2, lsc=A) == dsa.DSA_ERR_DTYPE     # fp8 latent needs bf16 queries
+    assert call(ldt=2, lsc=A + 2) == dsa.DSA_ERR_ALIGN
     assert call(k=4096) == dsa.DSA_ERR_UNSUPPORTED
     assert call(H=129) == dsa.DSA_ERR_UNSUPPORTED
     assert call(lat=MIS) == dsa.DSA_ERR_ALIGN
@@ -108,10 +113,16 @@ def test_decode_rejects_small_workspace(dsa):
     lib = dsa.lib
     need = dsa.dsa_workspace_size(dsa.DSA_ENTRY_DECODE, 4, 32768, 2048, 64)
     assert need % 256 == 0 and need >= 4 * 32768 * 4 + 4 * 2048 * 4
-    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
                               0.07, A, None, None, A, need - 1, None)
     assert st == dsa.DSA_ERR_WORKSPACE
-    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 2, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 2, A, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
+                              0.07, A, None, None, A, need - 1, None)
+    assert st == dsa.DSA_ERR_WORKSPACE                       # fp8 latent accepted up to the workspace
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 2, None, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
+                              0.07, A, None, None, A, need, None)
+    assert st == dsa.DSA_ERR_NULL
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 2, 2, A, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
                               0.07, A, None, None, A, need, None)
     assert st == dsa.DSA_ERR_DTYPE
 

@@ -34,7 +34,7 @@ def _say(*a):
 
 def _decode_call(dsa, p, d):
     return dsa.DecodeCall(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len,
-                          int(p.seq_len.max()), p.k, p.scale, k_scale=d.k_scale)
+                          int(p.seq_len.max()), p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale)
 
 
 def _run(call):
@@ -83,6 +83,18 @@ def test_decode_32k_fullsize(dsa):
 def test_decode_128k_fp8_fullsize(dsa):
     """Batch 8: 7 x 131,072 + 1 x 200,000, fp8 keys with per-row scales, 2% boosted keys."""
     _check_decode(dsa, inputs.workload("decode-128k-fp8"))
+
+
+@pytest.mark.parametrize("name", ["decode-32k-fp8kv", "decode-128k-fp8kv"])
+def test_decode_fp8_latent_fullsize(dsa, name):
+    """The two decode workloads with the latent cache in fp8 (e4m3 codes, one
+    float32 scale per row), replayed bitwise through the attention entry."""
+    import torch
+    p = inputs.workload(name)
+    d, out, lse, idx = _check_decode(dsa, p)
+    rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale,
+                                           latent_scale=d.latent_scale)
+    assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
 
 
 def test_ties_64k_replay_fullsize(dsa):

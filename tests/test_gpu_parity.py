@@ -217,7 +217,8 @@ def _gpu_attn(dsa, prob, idx, d=None):
     idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
     out = torch.full((prob.R, prob.H, 512), float("nan"), dtype=torch.float32, device="cuda")
     lse = torch.full((prob.R, prob.H), float("nan"), dtype=torch.float32, device="cuda")
-    dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx_d, prob.scale, q_seq=d.q_seq, out=out, lse=lse)
+    dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx_d, prob.scale, latent_scale=d.latent_scale,
+                            q_seq=d.q_seq, out=out, lse=lse)
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
@@ -281,7 +282,8 @@ def _pipeline(dsa, p):
     s_d = torch.from_numpy(scores).cuda()
     idx = torch.full((p.R, p.k), 12345, dtype=torch.int32, device="cuda")
     dsa.dsa_topk(s_d, d.q_pos, p.max_n, p.k, idx_out=idx)
-    out, lse = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx, p.scale, q_seq=d.q_seq)
+    out, lse = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx, p.scale, latent_scale=d.latent_scale,
+                                       q_seq=d.q_seq)
     return scores, idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
 
 
@@ -312,8 +314,8 @@ def _fused(dsa, p, d, ws=None):
     lse = torch.full((p.B, p.H), float("nan"), dtype=torch.float32, device="cuda")
     idx = torch.full((p.B, p.k), 777, dtype=torch.int32, device="cuda")
     dsa.dsa_decode_fused(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len,
-                         int(p.seq_len.max()), p.k, p.scale, k_scale=d.k_scale, out=out, lse=lse,
-                         idx_out=idx, workspace=ws)
+                         int(p.seq_len.max()), p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale,
+                         out=out, lse=lse, idx_out=idx, workspace=ws)
     return out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy()
 
 
@@ -472,3 +474,77 @@ def test_prefill_form_scores_topk_attention(dsa, T, H_I, D_I):
     out, lse = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx_d, p.scale, q_seq=d.q_seq)
     ref_o, ref_l = O.sparse_mla(p, idx[rows], rows=rows)
     C.assert_attn_close(out.cpu().numpy()[rows], ref_o, lse.cpu().numpy()[rows], ref_l)
+
+
+# ------------------------------------------------------------------------------
+# FP8 latent cache (e4m3 codes, one float32 scale per row)
+# ------------------------------------------------------------------------------
+
+def _fp8_attn_problem(lens, seed, H, k, std=1.0, scale_spread=0.0):
+    p = inputs.decode_config(lens, seed=seed, H=H, k=k, q_abs_std=std, latent_dtype="fp8_e4m3")
+    if scale_spread:
+        rng = np.random.default_rng(seed)
+        p.latent_scale = (p.latent_scale * 10.0 ** rng.uniform(-scale_spread, scale_spread,
+                                                               p.latent_scale.shape)).astype(np.float32)
+    return p
+
+
+@pytest.mark.parametrize("H,k,std,spread", [(64, 2048, 1.0, 0.0), (64, 2048, 30.0, 0.0), (8, 64, 1.0, 0.0),
+                                            (72, 256, 1.0, 0.0), (16, 1, 1.0, 0.0), (64, 100, 1.0, 0.0),
+                                            (64, 2048, 1.0, 1.0)])
+def test_attention_fp8_latent_matches_oracle(dsa, H, k, std, spread):
+    """fp8 rows: ragged tails, partial chunks, H not a multiple of 16, a
+    peaked softmax, and row scales spread over two decades either way."""
+    p = _fp8_attn_problem([3000, 2500, 4096], 16, H, k, std, spread)
+    rng = np.random.default_rng(H * 5 + k)
+    idx = np.full((p.R, k), -1, np.int32)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        m = min(k, n) if r != 1 else min(k, n) // 2 + (k == 1)
+        idx[r, :m] = rng.choice(n, size=m, replace=False)
+    _say("fp8 attention", H, k, std, spread)
+    out, lse = _gpu_attn(dsa, p, idx)
+    ref, lse_ref = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref, lse, lse_ref)
+
+
+def test_attention_fp8_latent_holes_empty_rows_and_many_queries(dsa):
+    p = _fp8_attn_problem([600] * 160, 17, 64, 512)
+    rng = np.random.default_rng(3)
+    idx = np.stack([rng.choice(600, size=512, replace=False) for _ in range(p.R)]).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.2] = -1
+    idx[5] = -1
+    idx[7, 256:] = -1
+    idx[9, :] = 123                            # one key repeated: every entry counts
+    out, lse = _gpu_attn(dsa, p, idx)
+    rows = [0, 5, 7, 9, 80, p.R - 1]
+    ref, lse_ref = O.sparse_mla(p, idx[rows], rows=rows)
+    assert (out[5] == 0).all() and np.isneginf(lse[5]).all()
+    keep = [0, 2, 3, 4, 5]
+    C.assert_attn_close(out[rows][keep], ref[keep], lse[rows][keep], lse_ref[keep])
+
+
+@pytest.mark.parametrize("lens,k", [([4096, 3000, 2049, 1500, 7001], 2048), ([12000, 9000, 20000], 2048),
+                                    ([9000, 16385, 12000, 10000, 9001], 512)])
+def test_fused_decode_fp8_latent_matches_pipeline_replay_and_oracle(dsa, lens, k):
+    """Short contexts take selection then the attention kernel; past 8K the
+    selection is fused with the attention: both give the bits of the three
+    entry points and of replaying the recorded indices."""
+    import torch
+    p = inputs.decode_config(lens, seed=18, k=k, latent_dtype="fp8_e4m3")
+    d = inputs.to_torch(p)
+    out, lse, idx = _fused(dsa, p, d)
+    out_b, lse_b, idx_b = _fused(dsa, p, d)
+    assert np.array_equal(out, out_b) and np.array_equal(lse, lse_b) and np.array_equal(idx, idx_b)
+    scores, idx2, out2, lse2 = _pipeline(dsa, p)
+    assert np.array_equal(idx, idx2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    C.assert_index_invariants(idx, p.q_pos, p.k)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k)), f"row {r}"
+    rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale,
+                                           latent_scale=d.latent_scale)
+    assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
+    ref_o, ref_l = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l)
