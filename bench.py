@@ -47,21 +47,22 @@ def attention_bytes(p) -> int:
     """Algorithmic bytes of one attention launch over k_eff keys per query:
     the selected latent rows, the indices, the queries and the outputs."""
     esz = {"bf16": 2, "f32": 4}
-    k_eff = sum(min(p.k, int(x)) for x in p.seq_len.astype(int))
-    return (k_eff * latent_row_bytes(p) + p.B * p.k * 4 + p.B * p.H * 576 * esz[p.act_dtype]
-            + p.B * p.H * (512 + 1) * 4)
+    k_eff = sum(min(p.k, int(x) + 1) for x in p.q_pos.astype(int))
+    return (k_eff * latent_row_bytes(p) + p.R * p.k * 4 + p.R * p.H * 576 * esz[p.act_dtype]
+            + p.R * p.H * (512 + 1) * 4)
 
 
 def step_bytes(p) -> int:
-    """Algorithmic HBM bytes of one decode step: every candidate indexer key,
-    every selected latent row, the queries, weights and the outputs."""
+    """Algorithmic HBM bytes of one decode step: every candidate indexer key
+    (once, however many of the sequence's new tokens score it), every
+    selected latent row, the queries, weights and the outputs."""
     esz = {"bf16": 2, "f32": 4, "fp8_e4m3": 1}
     n = p.seq_len.astype(int)
     keys = int(n.sum()) * p.D_I * esz[p.key_dtype] + (int(n.sum()) * 2 if p.key_dtype == "fp8_e4m3" else 0)
-    k_eff = [min(p.k, int(x)) for x in n]
+    k_eff = [min(p.k, int(x) + 1) for x in p.q_pos.astype(int)]
     gather = sum(k_eff) * latent_row_bytes(p)
-    small = (p.B * p.H_I * p.D_I * esz[p.act_dtype] + p.B * p.H_I * 4 + p.B * p.H * 576 * esz[p.act_dtype]
-             + p.B * p.H * 512 * 4 + p.B * p.H * 4 + p.B * p.k * 4)
+    small = (p.R * p.H_I * p.D_I * esz[p.act_dtype] + p.R * p.H_I * 4 + p.R * p.H * 576 * esz[p.act_dtype]
+             + p.R * p.H * 512 * 4 + p.R * p.H * 4 + p.R * p.k * 4)
     return keys + gather + small
 
 
@@ -71,9 +72,9 @@ def indexer_bytes(p) -> int:
     query its H_I x D_I query and H_I weights."""
     esz = {"bf16": 2, "f32": 4, "fp8_e4m3": 1}
     n = int(p.seq_len.astype(int).sum())
-    per_key = p.D_I * esz[p.key_dtype] + (2 if p.key_dtype == "fp8_e4m3" else 0) + 4
+    per_key = p.D_I * esz[p.key_dtype] + (2 if p.key_dtype == "fp8_e4m3" else 0) + 4 * p.tokens_per_seq
     per_query = p.H_I * p.D_I * esz[p.act_dtype] + p.H_I * 4
-    return n * per_key + p.B * per_query
+    return n * per_key + p.R * per_query
 
 
 def pmc_traffic(kernel_src: str, workload: str):
@@ -220,6 +221,12 @@ def prefill_bench(args, p):
         dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx, p.scale, q_seq=d.q_seq, out=out, lse=lse,
                                 workspace=ws)
 
+    # the clocks ramp over the first second or so of load: warm up for a
+    # fixed time, then the W warmup steps
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < args.prewarm_s:
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -267,6 +274,7 @@ def main():
     ap.add_argument("--workload", default="decode-32k")
     ap.add_argument("--sets", type=int, default=0, help="input copies cycled through (0: auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--prewarm-s", type=float, default=1.5, help="prefill: seconds of untimed passes first")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true", help="run the counter workload (under rocprofv3 --pmc)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -300,8 +308,10 @@ def main():
     base = inputs.to_torch(p, "cuda")
     sets = [base] + [type(base)(**{k: (v.clone() if v is not None else None) for k, v in vars(base).items()})
                      for _ in range(n_sets - 1)]
+    m = p.tokens_per_seq
     calls = [dsa.DecodeCall(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len, max_len,
-                            p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale) for d in sets]
+                            p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale, q_per_seq=m)
+             for d in sets]
     log(f"bench: {n_sets} input sets of {sb / 1e6:.1f} MB algorithmic traffic per step")
 
     # determinism check on set 0 (not timed)
@@ -324,7 +334,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
-    tok_s = p.B / (ms_step * 1e-3)
+    tok_s = p.R / (ms_step * 1e-3)
     log(f"bench: {ms_step * 1e3:.2f} us/step, {tok_s:,.0f} tokens/s (wall {wall:.3f} s)")
 
     # ---- the same steps captured in a HIP graph (launch gaps vs kernel time) -------------
@@ -361,7 +371,7 @@ def main():
     # each with its own queries and latent cache (another input set's).
     share_layers = 4
     outs = [(torch.empty_like(calls[0].out), torch.empty_like(calls[0].lse)) for _ in range(share_layers - 1)]
-    aws = torch.empty(max(dsa.dsa_workspace_size(dsa.DSA_ENTRY_SPARSE_MLA, p.B, 0, p.k, p.H), 256),
+    aws = torch.empty(max(dsa.dsa_workspace_size(dsa.DSA_ENTRY_SPARSE_MLA, p.R, 0, p.k, p.H), 256),
                       dtype=torch.uint8, device="cuda")
 
     def block(i):
@@ -370,7 +380,8 @@ def main():
         for l in range(1, share_layers):
             d = sets[(i + l) % n_sets]
             dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, c.idx, p.scale, latent_scale=d.latent_scale,
-                                    out=outs[l - 1][0], lse=outs[l - 1][1], workspace=aws)
+                                    q_seq=d.q_seq if m > 1 else None, out=outs[l - 1][0], lse=outs[l - 1][1],
+                                    workspace=aws)
 
     for i in range(min(args.warmup, n_sets)):
         block(i)
@@ -388,7 +399,8 @@ def main():
     def attn(i):
         d = sets[i % n_sets]
         dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, calls[i % n_sets].idx, p.scale,
-                                latent_scale=d.latent_scale, out=outs[0][0], lse=outs[0][1], workspace=aws)
+                                latent_scale=d.latent_scale, q_seq=d.q_seq if m > 1 else None, out=outs[0][0],
+                                lse=outs[0][1], workspace=aws)
 
     for i in range(min(args.warmup, n_sets)):
         attn(i)
@@ -403,23 +415,31 @@ def main():
     log(f"bench: attention {attn_us:.2f} us/launch, {ab / (attn_us * 1e-6) / 1e9:,.0f} GB/s algorithmic")
 
     # ---- the dominant kernel alone: K back-to-back indexer launches ----------------------
-    scores = [torch.empty((p.B, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
+    # (several tokens per sequence: the decode-form entry, which runs the fused step's indexer)
+    scores = [torch.empty((p.R, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
+
+    def index(i):
+        d = sets[i % n_sets]
+        if m > 1:
+            dsa.dsa_index_scores_decode(d.q_idx, d.head_w, d.k_idx, d.row_off, d.seq_len, max_len, q_per_seq=m,
+                                        k_scale=d.k_scale, scores=scores[i % n_sets])
+        else:
+            dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, max_len, k_scale=d.k_scale,
+                                 scores=scores[i % n_sets])
+
     for i in range(min(args.warmup, n_sets)):
-        d = sets[i]
-        dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, max_len, k_scale=d.k_scale,
-                             scores=scores[i])
+        index(i)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        d = sets[i % n_sets]
-        dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, max_len, k_scale=d.k_scale,
-                             scores=scores[i % n_sets])
+        index(i)
     end.record()
     torch.cuda.synchronize()
     idx_us = start.elapsed_time(end) * 1e3 / args.steps
     ib = indexer_bytes(p)
     achieved = ib / (idx_us * 1e-6) / 1e9
-    log(f"bench: indexer {idx_us:.2f} us/launch, {achieved:,.0f} GB/s algorithmic")
+    idx_tflops = 2.0 * p.H_I * p.D_I * sum(int(x) + 1 for x in p.q_pos.astype(int)) / (idx_us * 1e-6) / 1e12
+    log(f"bench: indexer {idx_us:.2f} us/launch, {achieved:,.0f} GB/s algorithmic, {idx_tflops:.0f} TFLOP/s")
 
     traffic = pmc_traffic(os.path.join(ROOT, "sparse_attention_05_amd", "csrc", "index_scores.hip"), args.workload)
     cpu = None
@@ -433,19 +453,20 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if p.act_dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": args.workload, "batch": p.B, "context": max_len, "k": p.k,
                    "indexer_heads": p.H_I, "indexer_dim": p.D_I, "indexer_keys": p.key_dtype,
-                   "mla_heads": p.H, "latent_dim": 576, "latent": p.kv_dtype, "input_sets": n_sets},
+                   "mla_heads": p.H, "latent_dim": 576, "latent": p.kv_dtype, "tokens_per_seq": m,
+                   "input_sets": n_sets},
         "step_hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
         "attention": {"us_per_launch": attn_us, "bytes_per_launch": ab,
                       "gbps": ab / (attn_us * 1e-6) / 1e9},
         "graph_ms_per_step": graph_ms, "graph_replays_equal_eager": graph_same,
         "index_share": {"layers": share_layers, "ms_per_block": block_ms,
-                        "tokens_per_s_per_block": p.B / (block_ms * 1e-3),
+                        "tokens_per_s_per_block": p.R / (block_ms * 1e-3),
                         "speedup_vs_independent_layers": share_layers * ms_step / block_ms},
         "step_algorithmic_bytes": sb,
         "deterministic": deterministic,
         "roofline": {"kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "bytes_per_launch": ib, "us_per_launch": idx_us},
+                     "bytes_per_launch": ib, "us_per_launch": idx_us, "tflops": idx_tflops},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -65,6 +65,8 @@ typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype;
 #define DSA_VALUE_DIM 512
 /* Largest k this library selects (the pages use k = 2048 throughout). */
 #define DSA_MAX_TOPK 2048
+/* Most new tokens per sequence in one dsa_decode_fused step. */
+#define DSA_MAX_TOKENS_PER_SEQ 8
 
 /* Entry ids for dsa_workspace_size. */
 #define DSA_ENTRY_INDEX_SCORES 0
@@ -103,6 +105,28 @@ dsa_status dsa_index_scores(const void* q_idx, int32_t q_dtype, const float* hea
                             const int32_t* q_seq, const int32_t* q_pos, int32_t R,
                             int32_t H_I, int32_t D_I, int32_t max_n,
                             float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * dsa_index_scores_decode -- the indexer of dsa_decode_fused on its own: the
+ * scores of B sequences with q_per_seq new tokens each, row r = b *
+ * q_per_seq + i at position seq_len[b] - q_per_seq + i (the tokens' keys
+ * already appended), as dsa_index_scores computes them for those rows. With
+ * bf16 keys and q_per_seq >= 2 each key row is read once for all of a
+ * sequence's tokens (the multi-token step of dsa_decode_fused).
+ *
+ *   q_idx [R, H_I, D_I], head_w [R, H_I], R = B * q_per_seq;
+ *   q_per_seq in 1 .. DSA_MAX_TOKENS_PER_SEQ
+ *   seq_len [B] int32 (q_per_seq <= seq_len[b] <= max_len), row_off [B] int64
+ *   scores [R, ld_scores] fp32, ld_scores >= max_len, % 4 == 0, 16-B aligned;
+ *   entries past a row's position are left untouched
+ * Other arguments, dtypes and errors as in dsa_index_scores.
+ */
+dsa_status dsa_index_scores_decode(const void* q_idx, int32_t q_dtype, const float* head_w,
+                                   const void* k_idx, int32_t k_dtype, const uint16_t* k_scale,
+                                   int64_t cache_rows, const int64_t* row_off,
+                                   const int32_t* seq_len, int32_t B, int32_t q_per_seq,
+                                   int32_t H_I, int32_t D_I, int32_t max_len, float* scores,
+                                   int64_t ld_scores, void* stream);
 
 /*
  * dsa_topk -- deterministic top-k over each score row.
@@ -167,34 +191,42 @@ dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* lat
 
 /*
  * dsa_decode_fused -- one decode step: indexer -> top-k -> sparse MLA for B
- * sequences with one new query each (q_pos[b] = seq_len[b] - 1, the new
- * token's key and latent row already appended). Enqueues the same kernels
- * as the three entry points above, with the scores (and the indices when
- * idx_out is NULL) kept in the workspace; the attention split plan equals
- * dsa_sparse_mla_attn's, so replaying the recorded idx_out through
- * dsa_sparse_mla_attn reproduces out and lse bitwise.
+ * sequences with q_per_seq new tokens each, their keys and latent rows
+ * already appended. Query row r = b * q_per_seq + i is token i of sequence b,
+ * at position seq_len[b] - q_per_seq + i, and selects its own top-k over its
+ * own causal range. q_per_seq = 1 is plain decode; 2 .. 8 serves the tokens
+ * of a multi-token (MTP / speculative) step ("GLM-5: from Vibe Coding...",
+ * section 2.1: multi-token prediction with shared parameters, 4 speculative
+ * steps; "Zhipu AI / GLM", section 11.1: MTP steps share top-k indices and
+ * the KV cache). With bf16 keys the indexer reads each key row once for all
+ * of a sequence's new tokens. Enqueues the same kernels as the three entry
+ * points above, with the scores (and the indices when idx_out is NULL) kept
+ * in the workspace; the attention split plan equals dsa_sparse_mla_attn's,
+ * so replaying the recorded idx_out through dsa_sparse_mla_attn (q_seq[r] =
+ * r / q_per_seq) reproduces out and lse bitwise.
  *
- *   q_idx [B, H_I, D_I], head_w [B, H_I], k_idx/k_scale as in dsa_index_scores
- *   q_abs [B, H, 576], latent [cache_rows, 576]: act_dtype (DSA_BF16 or
+ *   R = B * q_per_seq;  q_per_seq in 1 .. DSA_MAX_TOKENS_PER_SEQ
+ *   q_idx [R, H_I, D_I], head_w [R, H_I], k_idx/k_scale as in dsa_index_scores
+ *   q_abs [R, H, 576], latent [cache_rows, 576]: act_dtype (DSA_BF16 or
  *   DSA_F32) is the dtype of q_idx and q_abs; latent_dtype and
  *   latent_scale as in dsa_sparse_mla_attn; k_dtype as in
  *   dsa_index_scores.
- *   seq_len [B] int32 (1 <= seq_len[b] <= max_len), row_off [B] int64
- *   out [B, H, 512] fp32, lse [B, H] or NULL, idx_out [B, k] int32 or NULL
- *   workspace: dsa_workspace_size(DSA_ENTRY_DECODE, B, max_len, k, H) bytes
+ *   seq_len [B] int32 (q_per_seq <= seq_len[b] <= max_len), row_off [B] int64
+ *   out [R, H, 512] fp32, lse [R, H] or NULL, idx_out [R, k] int32 or NULL
+ *   workspace: dsa_workspace_size(DSA_ENTRY_DECODE, R, max_len, k, H) bytes
  */
 dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* k_idx,
                             int32_t k_dtype, const uint16_t* k_scale, const void* q_abs,
                             const void* latent, int32_t act_dtype, int32_t latent_dtype,
                             const float* latent_scale, int64_t cache_rows,
                             const int64_t* row_off, const int32_t* seq_len, int32_t B,
-                            int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k,
+                            int32_t q_per_seq, int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k,
                             float scale, float* out, float* lse, int32_t* idx_out,
                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * dsa_workspace_size -- bytes of workspace an entry point needs.
- * entry: one of DSA_ENTRY_*; rows = R (or B for DSA_ENTRY_DECODE);
+ * entry: one of DSA_ENTRY_*; rows = R (B * q_per_seq for DSA_ENTRY_DECODE);
  * max_len = longest sequence (decode) or max_n (top-k); k; H = MLA heads.
  * Returns 0 when the entry needs none; the result is a multiple of 256.
  * It queries the current device (the split plan depends on its CU count).

@@ -298,7 +298,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int r, int h, int grp,
 // First cache row of query r's sequence (load it before the query fragments:
 // waits are in issue order).
 __device__ __forceinline__ int64_t seq_base(const AttnArgs& a, int r) {
-  int b = a.q_seq ? a.q_seq[r] : r;
+  int b = a.q_seq ? a.q_seq[r] : r / a.qps;
   b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
   return a.row_off[b];
 }

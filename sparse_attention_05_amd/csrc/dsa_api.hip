@@ -131,6 +131,27 @@ dsa_status dsa_index_scores(const void* q_idx, int32_t q_dtype, const float* hea
   return e == hipSuccess ? DSA_OK : hip_fail(e);
 }
 
+dsa_status dsa_index_scores_decode(const void* q_idx, int32_t q_dtype, const float* head_w, const void* k_idx,
+                                   int32_t k_dtype, const uint16_t* k_scale, int64_t cache_rows,
+                                   const int64_t* row_off, const int32_t* seq_len, int32_t B, int32_t q_per_seq,
+                                   int32_t H_I, int32_t D_I, int32_t max_len, float* scores, int64_t ld_scores,
+                                   void* stream) {
+  if (q_per_seq < 1 || q_per_seq > DSA_MAX_TOKENS_PER_SEQ) return DSA_ERR_UNSUPPORTED;
+  if (B < 1 || int64_t(B) * q_per_seq > (int64_t(1) << 24)) return DSA_ERR_SHAPE;
+  const int R = B * q_per_seq;
+  dsa_status st = check_index_args(q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, R,
+                                   H_I, D_I, max_len);
+  if (st != DSA_OK) return st;
+  if (!seq_len || !scores) return DSA_ERR_NULL;
+  if (ld_scores < max_len || (ld_scores & 3)) return DSA_ERR_SHAPE;
+  if (!aligned16(scores)) return DSA_ERR_ALIGN;
+  IndexArgs a{q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, nullptr, nullptr, seq_len,
+              R, H_I, D_I, max_len, scores, ld_scores, nullptr, 0};
+  a.qps = q_per_seq;
+  hipError_t e = launch_index_scores(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : hip_fail(e);
+}
+
 dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos, int32_t R, int32_t max_n,
                     int32_t k, int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
   if (!scores || !q_pos || !idx_out) return DSA_ERR_NULL;
@@ -170,11 +191,15 @@ dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* lat
 
 dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* k_idx, int32_t k_dtype,
                             const uint16_t* k_scale, const void* q_abs, const void* latent, int32_t act_dtype,
-                            int32_t latent_dtype, const float* latent_scale, int64_t cache_rows, const int64_t* row_off, const int32_t* seq_len, int32_t B,
+                            int32_t latent_dtype, const float* latent_scale, int64_t cache_rows,
+                            const int64_t* row_off, const int32_t* seq_len, int32_t B, int32_t q_per_seq,
                             int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k, float scale,
                             float* out, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
                             void* stream) {
-  dsa_status st = check_index_args(q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, B,
+  if (q_per_seq < 1 || q_per_seq > DSA_MAX_TOKENS_PER_SEQ) return DSA_ERR_UNSUPPORTED;
+  if (B < 1 || int64_t(B) * q_per_seq > (int64_t(1) << 24)) return DSA_ERR_SHAPE;
+  const int R = B * q_per_seq;  // query rows: q_per_seq per sequence, sequence-major
+  dsa_status st = check_index_args(q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, R,
                                    H_I, D_I, max_len);
   if (st != DSA_OK) return st;
   if (!seq_len || !q_abs || !latent || !out) return DSA_ERR_NULL;
@@ -184,35 +209,38 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
   if (max_len > kMaxTopkRow) return DSA_ERR_UNSUPPORTED;
   if (k < 1 || k > DSA_MAX_TOPK || H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
   if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
-  const size_t need = decode_ws_bytes(B, max_len, k, H);
+  const size_t need = decode_ws_bytes(R, max_len, k, H);
   if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSA_ERR_ALIGN;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const DecodeLayout L = decode_layout(B, max_len, k, H);
+  const DecodeLayout L = decode_layout(R, max_len, k, H);
   char* ws = static_cast<char*>(workspace);
   float* scores = reinterpret_cast<float*>(ws + L.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
   void* attn_ws = ws + L.attn;
   float* sample = reinterpret_cast<float*>(ws + L.sample);
-  const bool split = topk_use_split(B, max_len);
+  const bool split = topk_use_split(R, max_len);
 
   // the indexer also writes the score sample the split top-k takes its pivot from
   IndexArgs ia{q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, nullptr, nullptr,
-               seq_len, B, H_I, D_I, max_len, scores, L.ld, split ? sample : nullptr, L.ld_sample};
+               seq_len, R, H_I, D_I, max_len, scores, L.ld, split ? sample : nullptr, L.ld_sample};
+  ia.qps = q_per_seq;
   hipError_t e = launch_index_scores(ia, s);
   if (e != hipSuccess) return hip_fail(e);
-  TopkArgs ta{scores, L.ld, nullptr, seq_len, B, max_len, k, idx, split ? sample : nullptr, L.ld_sample,
+  TopkArgs ta{scores, L.ld, nullptr, seq_len, R, max_len, k, idx, split ? sample : nullptr, L.ld_sample,
               nullptr, nullptr};
-  const AttnPlan plan = plan_attention(B, H, k);
-  AttnArgs aa{q_abs, act_dtype, latent, latent_dtype, latent_scale, cache_rows, row_off, B, nullptr, idx, k, B,
+  ta.qps = q_per_seq;
+  const AttnPlan plan = plan_attention(R, H, k);
+  AttnArgs aa{q_abs, act_dtype, latent, latent_dtype, latent_scale, cache_rows, row_off, B, nullptr, idx, k, R,
               H, scale, out, lse, attn_ws};
+  aa.qps = q_per_seq;
   if (split && act_dtype == DSA_BF16) {  // few long rows: selection fused with the attention
-    topk_split_carve(ws + L.topk, B, max_len, ta);
+    topk_split_carve(ws + L.topk, R, max_len, ta);
     e = launch_topk_attn(ta, aa, plan, s);
     return e == hipSuccess ? DSA_OK : hip_fail(e);
   }
-  if (split) topk_split_carve(ws + L.topk, B, max_len, ta);
+  if (split) topk_split_carve(ws + L.topk, R, max_len, ta);
   e = launch_topk(ta, s);
   if (e != hipSuccess) return hip_fail(e);
   e = launch_sparse_mla(aa, plan, s);

@@ -27,6 +27,8 @@ struct IndexArgs {
   int64_t ld;
   float* sample;          // NULL, or receives sample[r * ld_sample + i] = scores[r, 16 i]
   int64_t ld_sample;
+  int qps = 1;            // decode form (q_seq, q_pos NULL): row r is query r % qps of sequence r / qps,
+                          // at position seq_len - qps + r % qps
 };
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 
@@ -44,6 +46,7 @@ struct TopkArgs {
   uint32_t* state;            // [R][slices] uint4: candidate count, largest candidate key, pivot, 0
   unsigned long long* cand;   // [R][slices][slice_tiles * 2048] candidate words
   int slice_tiles;            // 2048-key tiles per slice (set with cand and state)
+  int qps = 1;                // decode form (q_pos NULL): queries per sequence, as in IndexArgs
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 bool topk_use_split(int R, int max_n);
@@ -75,6 +78,7 @@ struct AttnArgs {
   float* out;
   float* lse;
   void* ws;
+  int qps = 1;  // q_seq NULL: row r belongs to sequence r / qps
 };
 hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);  // + combine
 hipError_t launch_attn_combine(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);

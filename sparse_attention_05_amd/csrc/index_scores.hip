@@ -256,9 +256,9 @@ __device__ __forceinline__ void wait_ops(int n) {
 
 // Keys of query r: cache rows base .. base+n-1 of its sequence.
 __device__ __forceinline__ void query_range(const IndexArgs& a, int r, int64_t& base, int64_t& n) {
-  int b = a.q_seq ? a.q_seq[r] : r;
+  int b = a.q_seq ? a.q_seq[r] : r / a.qps;
   b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
-  const int qpos = a.q_pos ? a.q_pos[r] : a.seq_len[b] - 1;
+  const int qpos = a.q_pos ? a.q_pos[r] : a.seq_len[b] - a.qps + r % a.qps;
   n = qpos + 1 < a.max_n ? qpos + 1 : a.max_n;
   if (n < 0) n = 0;
   base = a.row_off[b];
@@ -580,45 +580,86 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 
 
 
-template <int MT, int DI>
-__global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(IndexArgs a) {
+// kPfWaves waves share a ring of key groups; QW query rows of one sequence
+// per workgroup, each row's tiles split over kPfWaves / QW waves (QW = 8:
+// one wave per row, all 8 tiles of a group; QW = 4: two waves per row, 4
+// tiles each).
+// SLICED false (prefill form: B = 1, q_pos given, QW = 8): workgroup
+// blockIdx.x takes rows 8*blk .. +7, counted from the last, and keys 0 ..
+// the end of its longest row.
+// SLICED true (decode form with qps <= QW new tokens per sequence):
+// workgroup (blockIdx.x, blockIdx.y) takes the qps rows of sequence
+// blockIdx.y and its keys kps*blockIdx.x .. +kps-1, so each key row is read
+// once for all of them; rows past qps are idle. With QW = 4 the query rows
+// and head weights go to LDS once per workgroup (through ring stages 2-3,
+// while key groups 0-1 load) instead of every wave loading its row.
+// Scores (and the score sample, when asked) are stored up to each row's end.
+template <int MT, int DI, int QW, bool SLICED>
+__global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(IndexArgs a, int kps) {
   using C = KeyCfg<1, DI, true>;
+  constexpr int RW = kPfWaves;
   constexpr int NKS = DI / 32;
   constexpr int GB = kPfKeys * C::ROW;      // bytes per group
-  constexpr int LPW = GB / 1024 / kPfWaves;  // direct loads per wave per group
-  static_assert((GB / 1024) % kPfWaves == 0, "group loads split evenly over the waves");
+  constexpr int LPW = GB / 1024 / RW;       // direct loads per wave per group
+  constexpr int TPW = kPfTiles * QW / RW;   // tiles per wave per group
+  constexpr bool QLDS = SLICED && QW == 4;  // query rows staged in LDS
+  constexpr int QCPR = DI / 8;              // 16-byte chunks per query row
+  constexpr int QB = 16 * MT * DI * 2;      // staged bytes per query (heads padded to 16*MT)
+  static_assert((GB / 1024) % RW == 0, "group loads split evenly over the waves");
   static_assert(kPfStages >= 3, "a group lands while the one before it is multiplied");
+  static_assert(TPW % 4 == 0, "a wave's tiles of a group form whole 64-key score stores");
+  static_assert(!QLDS || QW * QB <= 2 * GB, "the staged queries fit two ring stages");
   __shared__ __attribute__((aligned(1024))) char ring[kPfStages][GB];
+  __shared__ __attribute__((aligned(16))) float s_w[QLDS ? QW : 1][64];
 
-  const int blk = int(gridDim.x) - 1 - int(blockIdx.x);
-  const int r0 = blk * kPfRows;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
+  const int qrow = wave % QW;                  // this wave's query row in the workgroup
+  const int tb = (wave / QW) * TPW;            // its first tile of each group
 
-  const int64_t base = a.row_off[0];
+  int r0, nrows, b;
+  int64_t k_beg, k_lim;
+  if constexpr (!SLICED) {
+    const int blk = int(gridDim.x) - 1 - int(blockIdx.x);
+    r0 = blk * QW;
+    nrows = a.R - r0 < QW ? a.R - r0 : QW;
+    b = 0;
+    k_beg = 0;
+    k_lim = a.max_n;
+  } else {
+    b = blockIdx.y;
+    r0 = b * a.qps;
+    nrows = a.qps < QW ? a.qps : QW;
+    k_beg = int64_t(blockIdx.x) * kps;
+    k_lim = k_beg + kps;
+  }
+  const int64_t base = a.row_off[b];
   const bool base_ok = base >= 0 && base < a.cache_rows;
-  auto row_n = [&](int rr) -> int64_t {
-    int64_t n = int64_t(a.q_pos[rr]) + 1;
+  auto row_n = [&](int i) -> int64_t {
+    const int rr = r0 + i;
+    int64_t n = (a.q_pos ? int64_t(a.q_pos[rr]) : int64_t(a.seq_len[b]) - a.qps + i) + 1;
     if (n > a.max_n) n = a.max_n;
     if (n > a.cache_rows - base) n = a.cache_rows - base;
     return base_ok && n > 0 ? n : 0;
   };
-  const int rr = r0 + wave;
-  const bool rv = rr < a.R;
-  const int64_t n_w = rv ? row_n(rr) : 0;
+  const int rr = r0 + qrow;
+  const bool rv = qrow < nrows;
+  const int64_t n_w = rv ? row_n(qrow) : 0;
   int64_t n_wg = 0;
-  for (int i = 0; i < kPfRows && r0 + i < a.R; ++i) {
-    const int64_t ni = row_n(r0 + i);
+  for (int i = 0; i < nrows; ++i) {
+    const int64_t ni = row_n(i);
     n_wg = ni > n_wg ? ni : n_wg;
   }
-  const int groups = int((n_wg + kPfKeys - 1) / kPfKeys);
+  const int64_t k_end = n_wg < k_lim ? n_wg : k_lim;
+  const int groups = k_end > k_beg ? int((k_end - k_beg + kPfKeys - 1) / kPfKeys) : 0;
   if (groups == 0) return;  // the same for every wave of the workgroup
 
-  // Group g is the buffer of key rows 128*g .. n_wg-1 (rows past the range
-  // read as zeros); this lane's byte offset in it for each of the wave's
-  // loads is the same in every group.
-  const char* keys = static_cast<const char*>(a.keys) + base * C::ROW;
+  // Group g is the buffer of key rows k_beg + 128*g .. k_end-1 (rows past
+  // the range read as zeros); this lane's byte offset in it for each of the
+  // wave's loads is the same in every group.
+  const char* keys = static_cast<const char*>(a.keys) + (base + k_beg) * C::ROW;
+  const int64_t span = k_end - k_beg;
   uint32_t src_off[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
@@ -632,38 +673,78 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     const uint32_t to = lds_addr(ring[g % kPfStages]);
     const int64_t s0 = int64_t(g) * kPfKeys;
     const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(keys + s0 * C::ROW), 0, int((n_wg - s0) * C::ROW), 0x00020000);
+        const_cast<char*>(keys + s0 * C::ROW), 0, int((span - s0) * C::ROW), 0x00020000);
 #pragma unroll
     for (int j = 0; j < LPW; ++j) dma16_buf(src, src_off[j], to + 1024 * (wave * LPW + j));
   };
-  int issued = 0;
-  for (; issued < kPfStages && issued < groups; ++issued) issue(issued);
 
-  // query fragments and weights of this wave's row (zero for padded heads or
-  // a missing row), loaded behind the first key groups and waited for with
-  // them, then re-defined through an empty asm, so that no later use waits
-  // on them behind the key loads
   bf16x8 qa[MT][NKS];
   float wr[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = 16 * mt + col;
-    const bool hv = rv && h < a.H_I;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int64_t off = (int64_t(hv ? rr : 0) * a.H_I + (hv ? h : 0)) * DI + 32 * ks + 8 * grp;
-      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
-      qa[mt][ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
+  int issued = 0;
+  if constexpr (QLDS) {
+    // query rows (chunks of head h XOR-permuted by h mod 8; heads past H_I
+    // and idle rows zeroed) and head weights into LDS, ahead of key groups
+    // 0-1; once every wave's part has landed the fragments go to registers
+    // and stages 2-3 take key groups 2-3
+    char* qst = ring[2];
+    const uint32_t qlds = lds_addr(qst);
+    for (int m = wave; 64 * m < QW * 16 * MT * QCPR; m += RW) {
+      const int pch = 64 * m + lane;
+      const int q = pch / (16 * MT * QCPR);
+      const int h = (pch / QCPR) % (16 * MT);
+      const int lc = (pch % QCPR) ^ (h & 7);
+      if (q < nrows && h < a.H_I)
+        dma16(static_cast<const char*>(a.q) + (int64_t(r0 + q) * a.H_I + h) * (DI * 2) + 16 * lc, qlds + 1024 * m);
+      else
+        *reinterpret_cast<uint4*>(qst + 16 * pch) = uint4{0u, 0u, 0u, 0u};
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hw = 16 * mt + 4 * grp + i;
-      const bool wv = rv && hw < a.H_I;
-      const float x = a.w[int64_t(wv ? rr : 0) * a.H_I + (wv ? hw : 0)];
-      wr[mt][i] = wv ? x : 0.f;
+    if (wave < QW) {
+      if (wave < nrows && lane < a.H_I) dma4(a.w + int64_t(r0 + wave) * a.H_I + lane, lds_addr(s_w[wave]));
+      else s_w[wave][lane] = 0.f;
     }
+    for (; issued < 2 && issued < groups; ++issued) issue(issued);
+    wait_ops<2 * LPW>(LPW * issued);  // this wave's query and weight loads have landed
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = 16 * mt + col;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qst + qrow * QB + h * (DI * 2) + 16 * ((4 * ks + grp) ^ (h & 7)));
+      const float4 w4 = *reinterpret_cast<const float4*>(&s_w[qrow][16 * mt + 4 * grp]);
+      wr[mt][0] = w4.x;
+      wr[mt][1] = w4.y;
+      wr[mt][2] = w4.z;
+      wr[mt][3] = w4.w;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stages 2-3 are free
+    for (; issued < kPfStages && issued < groups; ++issued) issue(issued);
+  } else {
+    for (; issued < kPfStages && issued < groups; ++issued) issue(issued);
+    // query fragments and weights of this wave's row (zero for padded heads
+    // or a missing row), loaded behind the first key groups and waited for
+    // with them, then re-defined through an empty asm, so that no later use
+    // waits on them behind the key loads
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int h = 16 * mt + col;
+      const bool hv = rv && h < a.H_I;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int64_t off = (int64_t(hv ? rr : 0) * a.H_I + (hv ? h : 0)) * DI + 32 * ks + 8 * grp;
+        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+        qa[mt][ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hw = 16 * mt + 4 * grp + i;
+        const bool wv = rv && hw < a.H_I;
+        const float x = a.w[int64_t(wv ? rr : 0) * a.H_I + (wv ? hw : 0)];
+        wr[mt][i] = wv ? x : 0.f;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -674,7 +755,6 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     }
     asm volatile("" : "+v"(wr[mt][0]), "+v"(wr[mt][1]), "+v"(wr[mt][2]), "+v"(wr[mt][3]));
   }
-
 
   // fragments of tile t (keys 16*t .. +16) of group g (a stage past the last
   // group holds stale keys: reading it is harmless, its products are never
@@ -700,25 +780,34 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     return pp;
   };
 
-  // this wave's score row as a buffer of n_w floats: stores past it are dropped
-  const __amdgpu_buffer_rsrc_t srow =
-      __builtin_amdgcn_make_buffer_rsrc(a.scores + int64_t(rv ? rr : 0) * a.ld, 0, int(n_w * 4), 0x00020000);
+  // this wave's score row from key k_beg, as a buffer that ends at the row's
+  // end: stores past it are dropped; likewise its score sample (every 16th
+  // key; k_beg is a multiple of 128)
+  const int64_t own = n_w > k_beg ? n_w - k_beg : 0;
+  const __amdgpu_buffer_rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc(
+      a.scores + int64_t(rv ? rr : 0) * a.ld + k_beg, 0, int(own * 4), 0x00020000);
+  const bool smp = SLICED && a.sample != nullptr;
+  const int spg = smp ? 2 * (TPW / 4) : TPW / 4;  // stores per group
+  const __amdgpu_buffer_rsrc_t ssmp = __builtin_amdgcn_make_buffer_rsrc(
+      smp ? a.sample + int64_t(rv ? rr : 0) * a.ld_sample + (k_beg >> 4) : a.scores, 0,
+      smp ? int((own + 15) / 16 * 4) : 0, 0x00020000);
 
   // two fragment tiles and two accumulator tiles: tile t is multiplied from
   // kb[t&1] into acc[t&1] while tile t-1's epilogue runs from acc[(t-1)&1]
   // and tile t+1's fragments are read into kb[(t+1)&1]
   bf16x8 kb[2][NKS];
   f32x4 acc[2][MT];
-  // the prologue waited for every load: group 0 has landed for every wave
+  // group 0 has landed for every wave (behind it: the later groups' loads)
+  wait_ops<LPW * (kPfStages - 1)>(LPW * (issued - 1));
   asm volatile("s_barrier" ::: "memory");
-  tile_frags(0, 0, kb[0]);
+  tile_frags(0, tb, kb[0]);
 
   for (int g = 0; g < groups; ++g) {
     // own parts of group g+1 landed (its first tile is read during this
     // group's last one): behind them are the direct loads of the later
-    // groups and two score stores per group since
-    if (g + 1 < groups) wait_ops<LPW * (kPfStages - 2) + 2 * (kPfStages - 1)>(
-        LPW * (issued - (g + 2)) + 2 * (g < kPfStages - 2 ? g : kPfStages - 2));
+    // groups and spg score stores per group since
+    if (g + 1 < groups) wait_ops<LPW * (kPfStages - 2) + kPfTiles / 2 * (kPfStages - 1)>(
+        LPW * (issued - (g + 2)) + spg * (g < kPfStages - 2 ? g : kPfStages - 2));
     // every part of g+1 has landed; every wave is done with group g-1, so
     // its stage takes group g-1 + kPfStages
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -726,9 +815,9 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
       issue(issued);
       ++issued;
     }
-    float part[kPfTiles];
+    float part[TPW];
 #pragma unroll
-    for (int t = 0; t < kPfTiles; ++t) {
+    for (int t = 0; t < TPW; ++t) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
@@ -737,8 +826,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
           acc[t & 1][mt] =
               mfma_k32(qa[mt][ks], kb[t & 1][ks], ks ? acc[t & 1][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
       if (t > 0) part[t - 1] = tile_epi(acc[(t - 1) & 1]);
-      if (t + 1 < kPfTiles) tile_frags(g, t + 1, kb[(t + 1) & 1]);
-      else tile_frags(g + 1, 0, kb[(t + 1) & 1]);
+      if (t + 1 < TPW) tile_frags(g, tb + t + 1, kb[(t + 1) & 1]);
+      else tile_frags(g + 1, tb, kb[(t + 1) & 1]);
       // each MFMA followed by VALU work of the previous tile's epilogue;
       // the fragment reads after the tile's MFMAs
 #pragma unroll
@@ -750,13 +839,17 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
       __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    part[kPfTiles - 1] = tile_epi(acc[(kPfTiles - 1) & 1]);
+    part[TPW - 1] = tile_epi(acc[(TPW - 1) & 1]);
 #pragma unroll
-    for (int h = 0; h < kPfTiles / 4; ++h) {
+    for (int h = 0; h < TPW / 4; ++h) {
       const float p4[4] = {part[4 * h], part[4 * h + 1], part[4 * h + 2], part[4 * h + 3]};
       const float v = rows_transpose_sum(p4);
       // non-temporal: the scores are read by the next kernel, not this one
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, (g * kPfKeys + 64 * h + lane) * 4, 0, 2);
+      const int key = g * kPfKeys + 16 * tb + 64 * h + lane;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, key * 4, 0, 2);
+      if constexpr (SLICED) {
+        if (smp) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ssmp, (key & 15) ? -16 : (key >> 4) * 4, 0, 2);
+      }
     }
   }
 }
@@ -764,7 +857,22 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
 template <int MT, int DI>
 hipError_t launch_prefill(const IndexArgs& a, hipStream_t stream) {
   const unsigned blocks = unsigned((a.R + kPfRows - 1) / kPfRows);
-  index_scores_prefill_kernel<MT, DI><<<dim3(blocks), kPfWaves * 64, 0, stream>>>(a);
+  index_scores_prefill_kernel<MT, DI, kPfRows, false><<<dim3(blocks), kPfWaves * 64, 0, stream>>>(a, 0);
+  return hipGetLastError();
+}
+
+// Decode form with 2..8 new tokens per sequence: a workgroup per (key slice,
+// sequence), the slices sized so that the grid covers the CUs about once.
+template <int MT, int DI>
+hipError_t launch_multi_token(const IndexArgs& a, hipStream_t stream) {
+  const int cus = device_cu_count();
+  const int per_seq = (cus + a.B - 1) / a.B;
+  int64_t kps = (int64_t(a.max_n) + per_seq - 1) / per_seq;
+  kps = (kps + kPfKeys - 1) / kPfKeys * kPfKeys;
+  const unsigned slices = unsigned((a.max_n + kps - 1) / kps);
+  const dim3 grid(slices, unsigned(a.B));
+  if (a.qps <= 4) index_scores_prefill_kernel<MT, DI, 4, true><<<grid, kPfWaves * 64, 0, stream>>>(a, int(kps));
+  else index_scores_prefill_kernel<MT, DI, 8, true><<<grid, kPfWaves * 64, 0, stream>>>(a, int(kps));
   return hipGetLastError();
 }
 
@@ -815,6 +923,12 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   const int mode = a.q_dtype == kF32 ? 0 : (a.k_dtype == kFP8 ? 2 : 1);
   // many bf16 queries of one sequence (causal prefill form): key tiles shared by 8 queries
   // (key and score rows are addressed with 32-bit byte offsets there)
+  // several new bf16 tokens per sequence (decode form): each key row read once for all of them
+  if (mode == 1 && !a.q_seq && !a.q_pos && a.qps >= 2 && a.qps <= kPfWaves && a.max_n <= (int64_t(1) << 22)) {
+    if (a.H_I <= 16) return a.D_I == 64 ? launch_multi_token<1, 64>(a, stream) : launch_multi_token<1, 128>(a, stream);
+    if (a.H_I <= 32) return a.D_I == 64 ? launch_multi_token<2, 64>(a, stream) : launch_multi_token<2, 128>(a, stream);
+    return a.D_I == 64 ? launch_multi_token<4, 64>(a, stream) : launch_multi_token<4, 128>(a, stream);
+  }
   if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 22) && !a.sample) {
     if (a.H_I <= 16) return a.D_I == 64 ? launch_prefill<1, 64>(a, stream) : launch_prefill<1, 128>(a, stream);
     if (a.H_I <= 32) return a.D_I == 64 ? launch_prefill<2, 64>(a, stream) : launch_prefill<2, 128>(a, stream);

@@ -686,7 +686,7 @@ __device__ __forceinline__ void sort_levels(TopkShared& sh, const unsigned long 
 }
 
 __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
-  const int q = a.q_pos ? a.q_pos[r] : a.seq_len[r] - 1;
+  const int q = a.q_pos ? a.q_pos[r] : a.seq_len[r / a.qps] - a.qps + r % a.qps;
   int n = q + 1;
   if (n > a.max_n) n = a.max_n;
   if (n < 0) n = 0;

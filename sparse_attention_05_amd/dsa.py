@@ -21,18 +21,20 @@ DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_DTYPE, DSA_ERR_ALIGN, DSA_ERR_WORKS
     DSA_ERR_UNSUPPORTED, DSA_ERR_HIP = range(8)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_ENTRY_INDEX_SCORES, DSA_ENTRY_TOPK, DSA_ENTRY_SPARSE_MLA, DSA_ENTRY_DECODE = 0, 1, 2, 3
-DSA_LATENT_DIM, DSA_VALUE_DIM, DSA_MAX_TOPK = 576, 512, 2048
+DSA_LATENT_DIM, DSA_VALUE_DIM, DSA_MAX_TOPK, DSA_MAX_TOKENS_PER_SEQ = 576, 512, 2048, 8
 
 # C signatures, in the order of include/dsa.h.
 _P, _I32, _I64, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "dsa_index_scores": (_I32, [_P, _I32, _P, _P, _I32, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                 _P, _I64, _P]),
+    "dsa_index_scores_decode": (_I32, [_P, _I32, _P, _P, _I32, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                       _P, _I64, _P]),
     "dsa_topk": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "dsa_sparse_mla_attn": (_I32, [_P, _I32, _P, _I32, _P, _I64, _P, _I32, _P, _P, _I32, _I32, _I32, _F32,
                                    _P, _P, _P, _SZ, _P]),
     "dsa_decode_fused": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _I32, _I32, _I32,
-                                _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
+                                _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
     "dsa_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "dsa_check_indices": (_I32, [_P, _P, _I32, _I32, _P, _P]),
     "dsa_status_string": (ctypes.c_char_p, [_I32]),
@@ -130,6 +132,24 @@ def dsa_index_scores(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Ten
     return scores
 
 
+def dsa_index_scores_decode(q_idx: torch.Tensor, head_w: torch.Tensor, k_idx: torch.Tensor,
+                            row_off: torch.Tensor, seq_len: torch.Tensor, max_len: int, *, q_per_seq: int = 1,
+                            k_scale: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Decode-form indexer scores [R, ld] (fp32), R = B * q_per_seq rows,
+    row b * q_per_seq + i at position seq_len[b] - q_per_seq + i."""
+    R, H_I, D_I = q_idx.shape
+    B = seq_len.numel()
+    if scores is None:
+        scores = torch.empty((R, (max_len + 3) // 4 * 4), dtype=torch.float32, device=q_idx.device)
+    st = lib.dsa_index_scores_decode(
+        _ptr(q_idx), _dtype_code(q_idx), _ptr(head_w), _ptr(k_idx), _dtype_code(k_idx), _ptr(k_scale),
+        k_idx.shape[0], _ptr(row_off), _ptr(seq_len), B, q_per_seq, H_I, D_I, max_len, _ptr(scores),
+        scores.shape[1], _stream(stream))
+    _check(st, "dsa_index_scores_decode")
+    return scores
+
+
 def dsa_topk(scores: torch.Tensor, q_pos: torch.Tensor, max_n: int, k: int, *,
              idx_out: Optional[torch.Tensor] = None, workspace=None, stream=None) -> torch.Tensor:
     """Deterministic top-k indices [R, k] (int32, rank order, -1 padded).
@@ -195,16 +215,19 @@ class DecodeCall:
     allocation. Used where per-step host overhead matters."""
 
     def __init__(self, q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
-                 scale: float, *, k_scale=None, latent_scale=None, out=None, lse=None, idx_out=None,
-                 want_lse=True, record_idx=True, workspace=None):
-        B, H_I, D_I = q_idx.shape
+                 scale: float, *, k_scale=None, latent_scale=None, q_per_seq: int = 1, out=None, lse=None,
+                 idx_out=None, want_lse=True, record_idx=True, workspace=None):
+        R, H_I, D_I = q_idx.shape
+        B = seq_len.numel()
+        if R != B * q_per_seq:
+            raise ValueError(f"q_idx has {R} rows; {B} sequences x {q_per_seq} tokens expected")
         H = q_abs.shape[1]
         dev = q_idx.device
-        self.out = out if out is not None else torch.empty((B, H, DSA_VALUE_DIM), dtype=torch.float32, device=dev)
-        self.lse = lse if lse is not None or not want_lse else torch.empty((B, H), dtype=torch.float32, device=dev)
+        self.out = out if out is not None else torch.empty((R, H, DSA_VALUE_DIM), dtype=torch.float32, device=dev)
+        self.lse = lse if lse is not None or not want_lse else torch.empty((R, H), dtype=torch.float32, device=dev)
         self.idx = idx_out if idx_out is not None or not record_idx else \
-            torch.empty((B, k), dtype=torch.int32, device=dev)
-        nbytes = dsa_workspace_size(DSA_ENTRY_DECODE, B, max_len, k, H)
+            torch.empty((R, k), dtype=torch.int32, device=dev)
+        nbytes = dsa_workspace_size(DSA_ENTRY_DECODE, R, max_len, k, H)
         self.workspace = _workspace(nbytes, workspace, dev)
         if _dtype_code(q_idx) != _dtype_code(q_abs):
             raise TypeError("q_idx and q_abs must share one dtype")
@@ -212,7 +235,7 @@ class DecodeCall:
         self._args = (
             _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _dtype_code(k_idx), _ptr(k_scale), _ptr(q_abs), _ptr(latent),
             _dtype_code(q_abs), _dtype_code(latent), _ptr(latent_scale), k_idx.shape[0], _ptr(row_off),
-            _ptr(seq_len), B, max_len, H_I, D_I, H, k,
+            _ptr(seq_len), B, q_per_seq, max_len, H_I, D_I, H, k,
             float(scale), _ptr(self.out), _ptr(self.lse), _ptr(self.idx), _ptr(self.workspace),
             self.workspace.numel() * self.workspace.element_size())
 
@@ -223,10 +246,11 @@ class DecodeCall:
 
 
 def dsa_decode_fused(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
-                     scale: float, *, k_scale=None, latent_scale=None, out=None, lse=None, idx_out=None,
-                     want_lse=True, record_idx=True, workspace=None, stream=None):
-    """One decode step; returns (out [B,H,512], lse [B,H] or None, idx [B,k] or None)."""
+                     scale: float, *, k_scale=None, latent_scale=None, q_per_seq: int = 1, out=None, lse=None,
+                     idx_out=None, want_lse=True, record_idx=True, workspace=None, stream=None):
+    """One decode step for q_per_seq new tokens per sequence (R = B * q_per_seq
+    rows, sequence-major); returns (out [R,H,512], lse [R,H] or None, idx [R,k] or None)."""
     call = DecodeCall(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len, k, scale,
-                      k_scale=k_scale, latent_scale=latent_scale, out=out, lse=lse, idx_out=idx_out,
-                      want_lse=want_lse, record_idx=record_idx, workspace=workspace)
+                      k_scale=k_scale, latent_scale=latent_scale, q_per_seq=q_per_seq, out=out, lse=lse,
+                      idx_out=idx_out, want_lse=want_lse, record_idx=record_idx, workspace=workspace)
     return call(stream)

@@ -101,10 +101,16 @@ class DSAProblem:
     def max_n(self) -> int:
         return int(self.q_pos.max()) + 1
 
+    @property
+    def tokens_per_seq(self) -> int:
+        return int(self.meta.get("tokens_per_seq", 1))
+
     def is_decode(self) -> bool:
-        """One query per sequence, at its last position."""
-        return (self.R == self.B and np.array_equal(self.q_seq, np.arange(self.B))
-                and np.array_equal(self.q_pos, self.seq_len - 1))
+        """tokens_per_seq queries per sequence (sequence-major), at its last positions."""
+        m = self.tokens_per_seq
+        i = np.arange(self.R) % m
+        return (self.R == self.B * m and np.array_equal(self.q_seq, np.arange(self.R) // m)
+                and np.array_equal(self.q_pos, np.repeat(self.seq_len, m) - m + i))
 
 
 # --------------------------------------------------------------------------
@@ -272,8 +278,10 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
                   H: int = 64, k: int = 2048, key_dtype: str = "bf16",
                   boost_frac: float = 0.0, boost_sigma: float = 4.0,
                   tie_levels: int = 0, latent_std: float = 0.1, q_abs_std: float = 1.0,
-                  latent_dtype: str = "bf16", name: str = "decode") -> DSAProblem:
-    """Decode batch: one new query per sequence at its last position.
+                  latent_dtype: str = "bf16", tokens_per_seq: int = 1,
+                  name: str = "decode") -> DSAProblem:
+    """Decode batch: ``tokens_per_seq`` new queries per sequence at its last
+    positions (query row b * tokens_per_seq + i at seq_len[b] - tokens_per_seq + i).
 
     * indexer queries N(0,1) bf16, head weights U(0,1) fp32, keys N(0,1);
     * ``key_dtype="fp8_e4m3"`` stores keys as OCP E4M3FN codes with a per-row
@@ -294,13 +302,15 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
     """
     st = _streams(seed)
     B = len(seq_lens)
+    m = int(tokens_per_seq)
+    R = B * m
     seq_lens = [int(s) for s in seq_lens]
     rows = int(sum(seq_lens))
     row_off = _offsets(seq_lens)
 
     if tie_levels:
-        q_f = st["q_idx"].integers(-4, 4, size=(B, H_I, D_I)).astype(np.float32)
-        head_w = (st["head_w"].integers(1, 9, size=(B, H_I)) / 8.0).astype(np.float32)
+        q_f = st["q_idx"].integers(-4, 4, size=(R, H_I, D_I)).astype(np.float32)
+        head_w = (st["head_w"].integers(1, 9, size=(R, H_I)) / 8.0).astype(np.float32)
         protos = st["proto"].integers(-4, 4, size=(tie_levels, D_I)).astype(np.float32)
         choice = st["k_idx"].integers(0, tie_levels, size=rows)
         k_f = protos[choice]
@@ -310,18 +320,18 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
         if key_dtype != "bf16":
             raise ValueError("tie-class inputs are stored as bf16")
     else:
-        q_idx = _normal_bf16(st["q_idx"], (B, H_I, D_I))
-        head_w = st["head_w"].random((B, H_I), dtype=np.float32)
+        q_idx = _normal_bf16(st["q_idx"], (R, H_I, D_I))
+        head_w = st["head_w"].random((R, H_I), dtype=np.float32)
         k_scale = None
         if key_dtype == "bf16" and not boost_frac:
             k_store = _normal_bf16(st["k_idx"], (rows, D_I))
         else:
             k_f = st["k_idx"].standard_normal((rows, D_I), dtype=np.float32)
             if boost_frac:
-                q_vals = (q_idx.astype(np.uint32) << 16).view(np.float32).reshape(B, H_I, D_I)
+                q_vals = (q_idx.astype(np.uint32) << 16).view(np.float32).reshape(B, m * H_I, D_I)
                 rb = st["boost"]
                 for b in range(B):
-                    mean_q = q_vals[b].mean(axis=0)
+                    mean_q = q_vals[b].mean(axis=0)     # over the heads of the sequence's queries
                     u = mean_q / np.linalg.norm(mean_q)
                     per_head = q_vals[b] @ u            # dot of each head's query with u
                     amp = boost_sigma * math.sqrt(D_I) / float(per_head.mean())
@@ -340,7 +350,7 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
             else:
                 raise ValueError(f"unknown key dtype {key_dtype}")
 
-    q_abs = _normal_bf16(st["q_abs"], (B, H, LATENT_DIM), std=q_abs_std)
+    q_abs = _normal_bf16(st["q_abs"], (R, H, LATENT_DIM), std=q_abs_std)
     latent_scale = None
     if latent_dtype == "bf16":
         latent = _normal_bf16(st["latent"], (rows, LATENT_DIM), std=latent_std)
@@ -352,9 +362,10 @@ def decode_config(seq_lens: Sequence[int], seed: int = 0, H_I: int = 64, D_I: in
     return DSAProblem(
         name=name, q_idx=q_idx, head_w=head_w, k_idx=k_store, k_scale=k_scale,
         q_abs=q_abs, latent=latent, row_off=row_off, seq_len=seq_len,
-        q_seq=np.arange(B, dtype=np.int32), q_pos=seq_len - 1,
+        q_seq=np.arange(R, dtype=np.int32) // m,
+        q_pos=(np.repeat(seq_len, m) - m + np.arange(R) % m).astype(np.int32),
         k=k, scale=1.0 / math.sqrt(192.0), act_dtype="bf16", key_dtype=key_dtype,
-        meta={"seed": seed, "boost_frac": boost_frac, "tie_levels": tie_levels},
+        meta={"seed": seed, "boost_frac": boost_frac, "tie_levels": tie_levels, "tokens_per_seq": m},
         latent_dtype=None if latent_dtype == "bf16" else latent_dtype, latent_scale=latent_scale,
     )
 
@@ -412,6 +423,8 @@ def workload(name: str, seed: int = 0) -> DSAProblem:
     if name == "decode-128k-fp8kv":
         return decode_config([131072] * 7 + [200000], seed=seed, key_dtype="fp8_e4m3",
                              boost_frac=0.02, latent_dtype="fp8_e4m3", name=name)
+    if name == "decode-32k-mtp4":
+        return decode_config([32768] * 4, seed=seed, tokens_per_seq=4, name=name)
     if name == "ties-64k":
         return decode_config([65536] * 16, seed=seed, tie_levels=8, name=name)
     if name == "prefill-8k":

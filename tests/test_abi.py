@@ -28,7 +28,8 @@ def dsa():
 
 def test_header_lists_the_entry_points():
     fns = header_functions()
-    for name in ("dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_decode_fused",
+    for name in ("dsa_index_scores", "dsa_index_scores_decode", "dsa_topk", "dsa_sparse_mla_attn",
+                 "dsa_decode_fused",
                  "dsa_workspace_size", "dsa_status_string", "dsa_last_error"):
         assert name in fns
 
@@ -76,6 +77,23 @@ def test_index_scores_rejects(dsa):
     assert _index(lib, max_n=0) == dsa.DSA_ERR_SHAPE
 
 
+def test_index_scores_decode_rejects(dsa):
+    lib = dsa.lib
+    def call(**kw):
+        a = dict(q=A, qdt=1, w=A, keys=A, kdt=1, ksc=None, rows=4 * 32768, off=A, sl=A, B=4, m=4, HI=64, DI=128,
+                 ml=32768, sc=A, ld=32768)
+        a.update(kw)
+        return lib.dsa_index_scores_decode(a["q"], a["qdt"], a["w"], a["keys"], a["kdt"], a["ksc"], a["rows"],
+                                           a["off"], a["sl"], a["B"], a["m"], a["HI"], a["DI"], a["ml"], a["sc"],
+                                           a["ld"], None)
+    assert call(sl=None) == dsa.DSA_ERR_NULL
+    assert call(m=0) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(m=9) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(ld=32766) == dsa.DSA_ERR_SHAPE
+    assert call(kdt=2) == dsa.DSA_ERR_NULL         # fp8 keys without their row scales
+    assert call(sc=MIS) == dsa.DSA_ERR_ALIGN
+
+
 def test_topk_rejects(dsa):
     lib = dsa.lib
     assert lib.dsa_topk(None, 128, A, 1, 100, 64, A, None, 0, None) == dsa.DSA_ERR_NULL
@@ -113,18 +131,28 @@ def test_decode_rejects_small_workspace(dsa):
     lib = dsa.lib
     need = dsa.dsa_workspace_size(dsa.DSA_ENTRY_DECODE, 4, 32768, 2048, 64)
     assert need % 256 == 0 and need >= 4 * 32768 * 4 + 4 * 2048 * 4
-    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, A, A, 4, 1, 32768, 64, 128, 64, 2048,
                               0.07, A, None, None, A, need - 1, None)
     assert st == dsa.DSA_ERR_WORKSPACE
-    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 2, A, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 2, A, 4 * 32768, A, A, 4, 1, 32768, 64, 128, 64, 2048,
                               0.07, A, None, None, A, need - 1, None)
     assert st == dsa.DSA_ERR_WORKSPACE                       # fp8 latent accepted up to the workspace
-    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 2, None, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 2, None, 4 * 32768, A, A, 4, 1, 32768, 64, 128, 64, 2048,
                               0.07, A, None, None, A, need, None)
     assert st == dsa.DSA_ERR_NULL
-    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 2, 2, A, 4 * 32768, A, A, 4, 32768, 64, 128, 64, 2048,
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 2, 2, A, 4 * 32768, A, A, 4, 1, 32768, 64, 128, 64, 2048,
                               0.07, A, None, None, A, need, None)
     assert st == dsa.DSA_ERR_DTYPE
+    # several new tokens per sequence: the workspace is sized by rows = B * q_per_seq
+    need4 = dsa.dsa_workspace_size(dsa.DSA_ENTRY_DECODE, 16, 32768, 2048, 64)
+    assert need4 > need
+    st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, A, A, 4, 4, 32768, 64, 128, 64,
+                              2048, 0.07, A, None, None, A, need, None)
+    assert st == dsa.DSA_ERR_WORKSPACE
+    for bad in (0, 9):
+        st = lib.dsa_decode_fused(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, A, A, 4, bad, 32768, 64, 128,
+                                  64, 2048, 0.07, A, None, None, A, need4, None)
+        assert st == dsa.DSA_ERR_UNSUPPORTED
 
 
 def test_check_indices_rejects(dsa):

@@ -34,7 +34,8 @@ def _say(*a):
 
 def _decode_call(dsa, p, d):
     return dsa.DecodeCall(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len,
-                          int(p.seq_len.max()), p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale)
+                          int(p.seq_len.max()), p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale,
+                          q_per_seq=p.tokens_per_seq)
 
 
 def _run(call):
@@ -45,8 +46,9 @@ def _run(call):
 
 
 def _scores(dsa, p, d):
-    s = dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, int(p.seq_len.max()),
-                             k_scale=d.k_scale)
+    """Scores from the decode-form indexer entry, the fused step's own indexer."""
+    s = dsa.dsa_index_scores_decode(d.q_idx, d.head_w, d.k_idx, d.row_off, d.seq_len, int(p.seq_len.max()),
+                                    q_per_seq=p.tokens_per_seq, k_scale=d.k_scale)
     return s.cpu().numpy()
 
 
@@ -94,6 +96,18 @@ def test_decode_fp8_latent_fullsize(dsa, name):
     d, out, lse, idx = _check_decode(dsa, p)
     rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale,
                                            latent_scale=d.latent_scale)
+    assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
+
+
+def test_decode_32k_multi_token_fullsize(dsa):
+    """Batch 4 x 32,768 with 4 new tokens per sequence (16 query rows), each
+    selecting its own top-k; an index replay through the attention entry is
+    bitwise equal."""
+    import torch
+    p = inputs.workload("decode-32k-mtp4")
+    d, out, lse, idx = _check_decode(dsa, p)
+    rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale,
+                                           q_seq=d.q_seq)
     assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
 
 

@@ -548,3 +548,82 @@ def test_fused_decode_fp8_latent_matches_pipeline_replay_and_oracle(dsa, lens, k
     assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
     ref_o, ref_l = O.sparse_mla(p, idx)
     C.assert_attn_close(out, ref_o, lse, ref_l)
+
+
+# ------------------------------------------------------------------------------
+# multi-token decode: several new tokens per sequence in one fused step
+# ------------------------------------------------------------------------------
+
+def _fused_multi(dsa, p, d):
+    """The fused step for p.tokens_per_seq tokens per sequence; also returns
+    the scores it left in its workspace (region 0: [R, ld] fp32)."""
+    import torch
+    m = p.tokens_per_seq
+    max_len = int(p.seq_len.max())
+    nbytes = dsa.dsa_workspace_size(dsa.DSA_ENTRY_DECODE, p.R, max_len, p.k, p.H)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((p.R, p.H, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((p.R, p.H), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((p.R, p.k), 777, dtype=torch.int32, device="cuda")
+    dsa.dsa_decode_fused(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len, max_len, p.k,
+                         p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale, q_per_seq=m, out=out, lse=lse,
+                         idx_out=idx, workspace=ws)
+    torch.cuda.synchronize()
+    ld = (max_len + 3) // 4 * 4
+    scores = ws[:p.R * ld * 4].view(torch.float32).reshape(p.R, ld).cpu().numpy().copy()
+    return out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), scores
+
+
+@pytest.mark.parametrize("m,lens,key_dtype,latent_dtype", [
+    (4, [4096, 3000, 2049, 700], "bf16", "bf16"),          # selection, then the attention kernel
+    (4, [12000, 9000, 20000], "bf16", "bf16"),              # selection fused with the attention
+    (2, [9000, 16385, 12000], "bf16", "fp8_e4m3"),
+    (3, [5000, 8200, 4], "bf16", "bf16"),                   # idle wave; a sequence of 4 tokens
+    (8, [10000, 2500], "bf16", "bf16"),                     # eight waves, one per token
+    (4, [9000, 3000], "fp8_e4m3", "bf16"),                  # fp8 keys: one key stream per row
+])
+def test_fused_multi_token_decode(dsa, m, lens, key_dtype, latent_dtype):
+    """Each token selects its own top-k over its own causal range: indices equal
+    the stable order of the step's own scores, scores within the bound of the
+    oracle, attention within tolerance, two runs and an index replay bitwise
+    equal."""
+    import torch
+    p = inputs.decode_config(lens, seed=21 + m, k=2048, key_dtype=key_dtype, latent_dtype=latent_dtype,
+                             boost_frac=0.02 if key_dtype == "fp8_e4m3" else 0.0, tokens_per_seq=m)
+    d = inputs.to_torch(p)
+    out, lse, idx, scores = _fused_multi(dsa, p, d)
+    out2, lse2, idx2, _ = _fused_multi(dsa, p, d)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2) and np.array_equal(idx, idx2)
+    C.assert_index_invariants(idx, p.q_pos, p.k)
+    swaps = 0
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k)), f"row {r}"
+        ref, bound = C.assert_scores_close(p, r, scores[r])
+        swaps += C.near_tie_swaps(idx[r], O.topk_row(ref.astype(np.float32), p.k), ref, bound)
+    _say(f"multi-token m={m}: near-tie swaps {swaps}")
+    # the decode-form indexer entry runs the step's indexer: the same scores
+    alone = dsa.dsa_index_scores_decode(d.q_idx, d.head_w, d.k_idx, d.row_off, d.seq_len, int(p.seq_len.max()),
+                                        q_per_seq=m, k_scale=d.k_scale).cpu().numpy()
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(alone[r, :n], scores[r, :n]), f"row {r}"
+    rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale,
+                                           latent_scale=d.latent_scale, q_seq=d.q_seq)
+    assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
+    ref_o, ref_l = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l)
+
+
+def test_fused_multi_token_exact_scores_end_to_end(dsa):
+    """Tie-class inputs (every score exact in fp32): the shared-key-stream
+    scores equal the oracle's bit for bit and the indices end to end."""
+    p = inputs.decode_config([9000, 6000, 12000], seed=31, k=2048, tie_levels=8, tokens_per_seq=4)
+    d = inputs.to_torch(p)
+    out, lse, idx, scores = _fused_multi(dsa, p, d)
+    ref_scores, ref_idx, ref_o, ref_l = O.dsa_forward(p)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(scores[r, :n], ref_scores[r]), f"row {r}"
+    assert np.array_equal(idx, ref_idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l)
