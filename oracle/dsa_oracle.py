@@ -49,6 +49,10 @@ score, because the top-k ranks the float32 scores the API emits):
    token, C[s, :] = e4m3(code[s, :]) * scale[s], dequantised before any
    arithmetic, so the attention above is unchanged.
 
+4. Context-parallel merges (key-range shards): the global top-k from the
+   shards' local (score, key) lists, and the log-sum-exp merge of the
+   shards' partial attentions (see the end of this module).
+
 The pages print no worked numbers for any of these stages; the tests pin
 this module to closed forms, brute force on tiny inputs, library routines
 (torch scaled_dot_product_attention for the dense case, torch's fp8 and
@@ -235,3 +239,48 @@ def dsa_forward(prob, rows=None):
     idx = topk(scores, prob.k)
     out, lse = sparse_mla(prob, idx, rows)
     return scores, idx, out, lse
+
+
+# --------------------------------------------------------------------------
+# context parallelism: key-range shards, merged exactly
+# --------------------------------------------------------------------------
+# "GLM-5: from Vibe Coding to Agentic Engineering", section 2.4.2, splits
+# long sequences over context-parallel groups. The reading here: shard p
+# holds keys [lo_p, hi_p) of every sequence, selects its local top-k, and a
+# merge of the shards' (score, key) lists gives the global selection; each
+# shard then attends over the global winners it holds, and a log-sum-exp
+# merge of the shards' (O, LSE) gives the output.
+
+def topk_merge(pair_scores: np.ndarray, pair_idx: np.ndarray, k: int) -> np.ndarray:
+    """Global top-k of P shards' candidate lists [P, m] (float32 scores,
+    global key indices, -1 = empty): the first k of the union stably sorted
+    by score descending, ties to the lower key. Pads with -1."""
+    s = np.asarray(pair_scores, dtype=np.float32).reshape(-1)
+    i = np.asarray(pair_idx, dtype=np.int64).reshape(-1)
+    keep = i >= 0
+    s, i = s[keep].astype(np.float64), i[keep]
+    order = np.lexsort((i, -s))                 # primary: score desc; then key asc
+    out = np.full(k, -1, dtype=np.int32)
+    n = min(k, order.size)
+    out[:n] = i[order[:n]]
+    return out
+
+
+def attn_merge(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge P partial attentions over disjoint key sets: o_parts [P, H, 512]
+    (each normalised over its own keys), lse_parts [P, H] (natural log,
+    -inf = no key). O = sum_p exp(LSE_p - LSE) O_p, LSE = log sum_p exp(LSE_p)."""
+    o = np.asarray(o_parts, dtype=np.float64)
+    l = np.asarray(lse_parts, dtype=np.float64)
+    H = l.shape[1]
+    out = np.zeros(o.shape[1:])
+    lse = np.full(H, -np.inf)
+    for h in range(H):
+        fin = np.isfinite(l[:, h])
+        if not fin.any():
+            continue
+        m = l[fin, h].max()
+        w = np.exp(l[fin, h] - m)
+        lse[h] = m + np.log(w.sum())
+        out[h] = (w[:, None] * o[fin, h]).sum(axis=0) / w.sum()
+    return out, lse

@@ -8,6 +8,7 @@ from oracle import dsa_oracle as O
 import test_oracle_attention as TA
 import test_oracle_indexer as TI
 import test_oracle_topk as TT
+import test_oracle_cp as TC
 
 
 def _no_relu(q, w, keys):
@@ -88,6 +89,26 @@ def _fp8_latent_scaled_keys_only(prob, cache_rows):
 _orig_latent_rows = O.latent_rows
 
 
+def _merge_ties_high_first(pair_scores, pair_idx, k):
+    s = np.asarray(pair_scores, np.float32).reshape(-1)
+    i = np.asarray(pair_idx, np.int64).reshape(-1)
+    keep = i >= 0
+    s, i = s[keep].astype(np.float64), i[keep]
+    order = np.lexsort((-i, -s))
+    out = np.full(k, -1, np.int32)
+    out[:min(k, order.size)] = i[order[:k]]
+    return out
+
+
+def _merge_unweighted(o_parts, lse_parts):
+    o = np.asarray(o_parts, np.float64)
+    l = np.asarray(lse_parts, np.float64)
+    fin = np.isfinite(l)
+    out = np.where(fin[:, :, None], o, 0).sum(axis=0) / np.maximum(fin.sum(axis=0), 1)[:, None]
+    m = np.where(fin, l, -np.inf).max(axis=0)
+    return out, m + np.log(np.where(fin, np.exp(l - m), 0).sum(axis=0))
+
+
 CASES = [
     ("index_scores_row", _no_relu, [TI.test_relu_zeroes_negative_dots, TI.test_golden_hand_case]),
     ("index_scores_row", _w_reversed, [TI.test_head_weights_follow_their_head]),
@@ -98,6 +119,9 @@ CASES = [
     ("sparse_mla_row", _value_from_rope_end, [TA.test_single_key_gives_its_value_rows, TA.test_golden_hand_case]),
     ("sparse_mla_row", _no_scale, [TA.test_dense_equals_sdpa_when_k_covers_context]),
     ("sparse_mla_row", _latent_only_logits, [TA.test_golden_hand_case]),
+    ("topk_merge", _merge_ties_high_first, [TC.test_merge_closed_forms]),
+    ("attn_merge", _merge_unweighted, [TC.test_attention_merge_equals_whole_attention,
+                                       TC.test_attention_merge_closed_forms]),
     ("latent_rows", _fp8_latent_no_scale, [TA.test_fp8_latent_golden_hand_case,
                                            TA.test_fp8_latent_single_key_is_its_scaled_row]),
     ("latent_rows", _fp8_latent_scale_of_next_row, [TA.test_fp8_latent_golden_hand_case,
