@@ -186,6 +186,54 @@ def cpu_baseline(p, budget_s: float):
             "sample": f"{rows} {what}, stable-sort top-k, fp64 attention), {dt:.1f} s"}
 
 
+def context_parallel(dsa, p, d, call, steps, P=4):
+    """Key-range shards rehearsed on one device: each shard scores its keys and
+    selects locally; timed are the merges that would follow the exchanges
+    (the selection from the shards' candidate lists, the output from their
+    partial attentions)."""
+    import torch
+    max_len = int(p.seq_len.max())
+    edges = [int(x) // 64 * 64 for x in torch.linspace(0, max_len, P + 1).tolist()]
+    edges[-1] = max_len
+    q_pos = d.q_pos.long()
+    ps, pi, shards = [], [], []
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        off = (d.row_off + lo).contiguous()
+        qp = (torch.minimum(q_pos, torch.full_like(q_pos, hi - 1)) - lo).to(torch.int32).contiguous()
+        sc = dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, off, qp, hi - lo, k_scale=d.k_scale)
+        a, b = dsa.dsa_topk_pairs(sc, dsa.dsa_topk(sc, qp, hi - lo, p.k), lo)
+        ps.append(a)
+        pi.append(b)
+        shards.append((lo, hi, off))
+    ps, pi = torch.stack(ps).contiguous(), torch.stack(pi).contiguous()
+    idx = dsa.dsa_topk_merge(ps, pi)
+    o_parts, l_parts = [], []
+    for lo, hi, off in shards:
+        o, l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, off, dsa.dsa_shard_indices(idx, lo, hi), p.scale,
+                                       latent_scale=d.latent_scale)
+        o_parts.append(o)
+        l_parts.append(l)
+    o_parts, l_parts = torch.stack(o_parts).contiguous(), torch.stack(l_parts).contiguous()
+    out, lse = dsa.dsa_attn_merge(o_parts, l_parts)
+    _, _, idx1 = call()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(idx, idx1))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("topk_merge_us", lambda: dsa.dsa_topk_merge(ps, pi, idx_out=idx)),
+                     ("attn_merge_us", lambda: dsa.dsa_attn_merge(o_parts, l_parts, out=out, lse=lse))):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        res[name] = start.elapsed_time(end) * 1e3 / steps
+    return {"shards": P, **res, "merged_equals_unsharded": same}
+
+
 def prefill_flops(p):
     """Algorithmic FLOPs of the causal indexer (2*H_I*D_I per query-key pair,
     keys 0..t for query t) and of the sparse attention (2*H*(576+512) per
@@ -414,6 +462,13 @@ def main():
     ab = attention_bytes(p)
     log(f"bench: attention {attn_us:.2f} us/launch, {ab / (attn_us * 1e-6) / 1e9:,.0f} GB/s algorithmic")
 
+    # ---- context parallelism rehearsed with 4 key-range shards: the merges ----------------
+    cp = None
+    if m == 1:
+        cp = context_parallel(dsa, p, sets[0], calls[0], args.steps)
+        log(f"bench: 4-shard top-k merge {cp['topk_merge_us']:.2f} us, output merge {cp['attn_merge_us']:.2f} us "
+            f"(merged selection equals the unsharded one: {cp['merged_equals_unsharded']})")
+
     # ---- the dominant kernel alone: K back-to-back indexer launches ----------------------
     # (several tokens per sequence: the decode-form entry, which runs the fused step's indexer)
     scores = [torch.empty((p.R, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
@@ -462,6 +517,7 @@ def main():
         "index_share": {"layers": share_layers, "ms_per_block": block_ms,
                         "tokens_per_s_per_block": p.R / (block_ms * 1e-3),
                         "speedup_vs_independent_layers": share_layers * ms_step / block_ms},
+        "context_parallel": cp,
         "step_algorithmic_bytes": sb,
         "deterministic": deterministic,
         "roofline": {"kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -225,6 +225,51 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Context parallelism over key ranges ("GLM-5: from Vibe Coding...", section
+ * 2.4.2: long sequences split over context-parallel groups). Shard p holds
+ * keys [lo_p, hi_p) of every sequence; it scores them (dsa_index_scores over
+ * its cache rows, positions shifted by -lo_p), selects a local top-k
+ * (dsa_topk) and turns it into a candidate list (dsa_topk_pairs); the
+ * gathered lists [P, R, k] merge into the global top-k (dsa_topk_merge),
+ * equal to the unsharded selection because the order (score descending,
+ * lower key first) is total and the shards' keys are disjoint. Each shard
+ * then attends over the global winners it holds (dsa_shard_indices, then
+ * dsa_sparse_mla_attn) and the partial outputs merge by their log-sum-exp
+ * in shard order (dsa_attn_merge), deterministic for a fixed P. On one
+ * device the shards are views of one cache. All four only enqueue work on
+ * `stream`; arguments are checked on the host.
+ */
+
+/* pair_score[r, j] = scores[r, idx[r, j]], pair_idx[r, j] = idx[r, j] +
+ * key_offset (the shard's lo), -inf / -1 where idx[r, j] = -1.
+ * scores [R, ld_scores] fp32; idx, pair_idx [R, k] int32; pair_score [R, k]. */
+dsa_status dsa_topk_pairs(const float* scores, int64_t ld_scores, const int32_t* idx,
+                          int32_t R, int32_t k, int32_t key_offset, float* pair_score,
+                          int32_t* pair_idx, void* stream);
+
+/* idx_out[r, :] = the first k of the union of the P lists pair_*[p, r, :]
+ * (each in rank order with its -1 entries last, as dsa_topk_pairs leaves
+ * them, keys disjoint across lists) in the order score descending, lower key
+ * first; -1 past the candidates. pair_score [P, R, k] fp32, pair_idx
+ * [P, R, k] int32; P in 1 .. 8 with P * k <= 16384 (else
+ * DSA_ERR_UNSUPPORTED). Lists that break these rules give unspecified
+ * indices (never an access outside the arrays). */
+dsa_status dsa_topk_merge(const float* pair_score, const int32_t* pair_idx, int32_t P,
+                          int32_t R, int32_t k, int32_t* idx_out, void* stream);
+
+/* idx_local[r, j] = idx[r, j] - lo where lo <= idx[r, j] < hi, else -1:
+ * the global winners a shard holds, in its own key numbering. [R, k] int32. */
+dsa_status dsa_shard_indices(const int32_t* idx, int32_t R, int32_t k, int32_t lo, int32_t hi,
+                             int32_t* idx_local, void* stream);
+
+/* out[r, h] = sum_p exp(lse_p - LSE) o_p[r, h], lse[r, h] = LSE = log sum_p
+ * exp(lse_p), summed in shard order; shards with lse -inf add nothing, and a
+ * row with none gets out = 0, lse = -inf. o_parts [P, R, H, 512] fp32 and out
+ * [R, H, 512] 16-B aligned; lse_parts [P, R, H]; lse [R, H] or NULL. */
+dsa_status dsa_attn_merge(const float* o_parts, const float* lse_parts, int32_t P, int32_t R,
+                          int32_t H, float* out, float* lse, void* stream);
+
+/*
  * dsa_workspace_size -- bytes of workspace an entry point needs.
  * entry: one of DSA_ENTRY_*; rows = R (B * q_per_seq for DSA_ENTRY_DECODE);
  * max_len = longest sequence (decode) or max_n (top-k); k; H = MLA heads.

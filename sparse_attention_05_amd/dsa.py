@@ -35,6 +35,10 @@ SIGNATURES = {
                                    _P, _P, _P, _SZ, _P]),
     "dsa_decode_fused": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _I32, _I32, _I32,
                                 _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
+    "dsa_topk_pairs": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _P]),
+    "dsa_topk_merge": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P]),
+    "dsa_shard_indices": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P]),
+    "dsa_attn_merge": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "dsa_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "dsa_check_indices": (_I32, [_P, _P, _I32, _I32, _P, _P]),
     "dsa_status_string": (ctypes.c_char_p, [_I32]),
@@ -207,6 +211,52 @@ def dsa_check_indices(idx: torch.Tensor, q_pos: torch.Tensor, *, n_bad: Optional
     st = lib.dsa_check_indices(_ptr(idx), _ptr(q_pos), R, k, _ptr(n_bad), _stream(stream))
     _check(st, "dsa_check_indices")
     return n_bad
+
+
+def dsa_topk_pairs(scores: torch.Tensor, idx: torch.Tensor, key_offset: int, *, pair_score=None, pair_idx=None,
+                   stream=None):
+    """A shard's candidate list: (scores at idx, idx + key_offset), -inf / -1 for -1."""
+    R, k = idx.shape
+    if pair_score is None:
+        pair_score = torch.empty((R, k), dtype=torch.float32, device=idx.device)
+    if pair_idx is None:
+        pair_idx = torch.empty((R, k), dtype=torch.int32, device=idx.device)
+    st = lib.dsa_topk_pairs(_ptr(scores), scores.shape[1], _ptr(idx), R, k, int(key_offset), _ptr(pair_score),
+                            _ptr(pair_idx), _stream(stream))
+    _check(st, "dsa_topk_pairs")
+    return pair_score, pair_idx
+
+
+def dsa_topk_merge(pair_score: torch.Tensor, pair_idx: torch.Tensor, *, idx_out=None, stream=None) -> torch.Tensor:
+    """Global top-k [R, k] from P shards' candidate lists [P, R, k]."""
+    P, R, k = pair_idx.shape
+    if idx_out is None:
+        idx_out = torch.empty((R, k), dtype=torch.int32, device=pair_idx.device)
+    st = lib.dsa_topk_merge(_ptr(pair_score), _ptr(pair_idx), P, R, k, _ptr(idx_out), _stream(stream))
+    _check(st, "dsa_topk_merge")
+    return idx_out
+
+
+def dsa_shard_indices(idx: torch.Tensor, lo: int, hi: int, *, idx_local=None, stream=None) -> torch.Tensor:
+    """Entries of idx in [lo, hi) shifted by -lo, others -1."""
+    R, k = idx.shape
+    if idx_local is None:
+        idx_local = torch.empty_like(idx)
+    st = lib.dsa_shard_indices(_ptr(idx), R, k, int(lo), int(hi), _ptr(idx_local), _stream(stream))
+    _check(st, "dsa_shard_indices")
+    return idx_local
+
+
+def dsa_attn_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, out=None, lse=None, stream=None):
+    """Log-sum-exp merge of P partial attentions [P, R, H, 512] / [P, R, H]."""
+    P, R, H, _ = o_parts.shape
+    if out is None:
+        out = torch.empty((R, H, DSA_VALUE_DIM), dtype=torch.float32, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((R, H), dtype=torch.float32, device=o_parts.device)
+    st = lib.dsa_attn_merge(_ptr(o_parts), _ptr(lse_parts), P, R, H, _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "dsa_attn_merge")
+    return out, lse
 
 
 class DecodeCall:

@@ -627,3 +627,93 @@ def test_fused_multi_token_exact_scores_end_to_end(dsa):
         assert np.array_equal(scores[r, :n], ref_scores[r]), f"row {r}"
     assert np.array_equal(idx, ref_idx)
     C.assert_attn_close(out, ref_o, lse, ref_l)
+
+
+# ------------------------------------------------------------------------------
+# context parallelism over key ranges, rehearsed with P shards on one device
+# ------------------------------------------------------------------------------
+
+def _cp_step(dsa, p, d, P):
+    """Each shard scores its own keys, selects locally and lists its candidates;
+    the merged lists give the selection; each shard attends over the winners
+    it holds; the partial outputs are merged."""
+    import torch
+    max_len = int(p.seq_len.max())
+    edges = [int(x) // 64 * 64 for x in np.linspace(0, max_len, P + 1)]
+    edges[-1] = max_len
+    q_pos = d.q_pos.long()
+    ps, pi, shards = [], [], []
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        off = (d.row_off + lo).contiguous()
+        qp = (torch.minimum(q_pos, torch.full_like(q_pos, hi - 1)) - lo).to(torch.int32).contiguous()
+        sc = dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, off, qp, hi - lo, k_scale=d.k_scale)
+        loc = dsa.dsa_topk(sc, qp, hi - lo, p.k)
+        a, b = dsa.dsa_topk_pairs(sc, loc, lo)
+        ps.append(a)
+        pi.append(b)
+        shards.append((lo, hi, off))
+    ps = torch.stack(ps).contiguous()
+    pi = torch.stack(pi).contiguous()
+    idx = dsa.dsa_topk_merge(ps, pi)
+    o_parts, l_parts = [], []
+    for lo, hi, off in shards:
+        loc = dsa.dsa_shard_indices(idx, lo, hi)
+        o, l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, off, loc, p.scale, latent_scale=d.latent_scale,
+                                       q_seq=d.q_seq)
+        o_parts.append(o)
+        l_parts.append(l)
+    o_parts = torch.stack(o_parts).contiguous()
+    l_parts = torch.stack(l_parts).contiguous()
+    out, lse = dsa.dsa_attn_merge(o_parts, l_parts)
+    torch.cuda.synchronize()
+    return (ps.cpu().numpy(), pi.cpu().numpy(), idx.cpu().numpy(), o_parts.cpu().numpy(), l_parts.cpu().numpy(),
+            out.cpu().numpy(), lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("P,lens,tie_levels", [(2, [9000, 5000], 0), (4, [32768, 20000, 6000], 0),
+                                               (8, [16385, 12000, 900], 8), (3, [7000, 700], 0)])
+def test_context_parallel_rehearsal(dsa, P, lens, tie_levels):
+    """The merged selection equals the unsharded top-k bit for bit (and the
+    oracle's merge of the same lists); the merged output equals the oracle's
+    merge of the same partial outputs and the attention over the selection
+    within the attention tolerances; two runs are bitwise equal."""
+    import torch
+    p = inputs.decode_config(lens, seed=41 + P, k=2048, tie_levels=tie_levels)
+    d = inputs.to_torch(p)
+    max_len = int(p.seq_len.max())
+    ps, pi, idx, o_parts, l_parts, out, lse = _cp_step(dsa, p, d, P)
+    full = dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, max_len, k_scale=d.k_scale)
+    idx_full = dsa.dsa_topk(full, d.q_pos, max_len, p.k).cpu().numpy()
+    assert np.array_equal(idx, idx_full)
+    for r in range(p.R):
+        assert np.array_equal(idx[r], O.topk_merge(ps[:, r], pi[:, r], p.k)), f"row {r}"
+    C.assert_index_invariants(idx, p.q_pos, p.k)
+    for r in range(p.R):
+        ref_o, ref_l = O.attn_merge(o_parts[:, r], l_parts[:, r])
+        C.assert_attn_close(out[r:r + 1], ref_o[None], lse[r:r + 1], ref_l[None], fp32=True)
+    ref_o, ref_l = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l)
+    again = _cp_step(dsa, p, d, P)
+    assert np.array_equal(again[2], idx) and np.array_equal(again[5], out) and np.array_equal(again[6], lse)
+
+
+def test_topk_merge_matches_oracle_on_random_lists(dsa):
+    """Lists of every length up to k, ties across lists, signed zeros."""
+    import torch
+    rng = np.random.default_rng(3)
+    P, R, k = 5, 6, 512
+    ps = np.full((P, R, k), -np.inf, np.float32)
+    pi = np.full((P, R, k), -1, np.int32)
+    for r in range(R):
+        keys = rng.permutation(P * 4000)[:P * k]
+        for q in range(P):
+            m = int(rng.integers(0, k + 1)) if r % 2 else k
+            s = (rng.integers(-3, 4, m) / 2.0).astype(np.float32)
+            s[s == 0] = np.where(rng.random((s == 0).sum()) < 0.5, np.float32(0.0), np.float32(-0.0))
+            kk = keys[q * k:q * k + m]
+            order = np.lexsort((kk, -s.astype(np.float64)))
+            ps[q, r, :m] = s[order]
+            pi[q, r, :m] = kk[order]
+    got = dsa.dsa_topk_merge(torch.from_numpy(ps).cuda(), torch.from_numpy(pi).cuda()).cpu().numpy()
+    for r in range(R):
+        assert np.array_equal(got[r], O.topk_merge(ps[:, r], pi[:, r], k)), f"row {r}"
