@@ -49,6 +49,9 @@ score, because the top-k ranks the float32 scores the API emits):
    token, C[s, :] = e4m3(code[s, :]) * scale[s], dequantised before any
    arithmetic, so the attention above is unchanged.
 
+The caches may be paged: a block table maps each sequence's positions to
+pages of a shared pool (cache_rows_of); the values are unchanged.
+
 4. Context-parallel merges (key-range shards): the global top-k from the
    shards' local (score, key) lists, and the log-sum-exp merge of the
    shards' partial attentions (see the end of this module).
@@ -105,12 +108,24 @@ def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def cache_rows_of(prob, b: int, pos: np.ndarray) -> np.ndarray:
+    """Cache rows holding positions ``pos`` of sequence b: row_off[b] + pos, or
+    through the block table when the cache is paged (position s sits in page
+    table[b, s // page_size] at row s % page_size of that page)."""
+    pos = np.asarray(pos, dtype=np.int64)
+    table = getattr(prob, "block_table", None)
+    if table is None:
+        return int(prob.row_off[b]) + pos
+    ps = int(prob.page_size)
+    return np.asarray(table, dtype=np.int64)[b][pos // ps] * ps + pos % ps
+
+
 def indexer_keys(prob, b: int, n: int) -> np.ndarray:
     """Keys 0..n-1 of sequence b as float64 (dequantised if fp8)."""
-    lo = int(prob.row_off[b])
-    k = decode(prob.k_idx[lo:lo + n], prob.key_dtype)
+    rows = cache_rows_of(prob, b, np.arange(n))
+    k = decode(prob.k_idx[rows], prob.key_dtype)
     if prob.key_dtype == "fp8_e4m3":
-        k = k * bf16_to_f64(prob.k_scale[lo:lo + n])[:, None]
+        k = k * bf16_to_f64(prob.k_scale[rows])[:, None]
     return k
 
 
@@ -211,7 +226,7 @@ def selected_rows(prob, r: int, idx_row: np.ndarray) -> np.ndarray:
     b = int(prob.q_seq[r])
     sel = np.asarray(idx_row)
     sel = sel[sel >= 0].astype(np.int64)
-    return latent_rows(prob, int(prob.row_off[b]) + sel)
+    return latent_rows(prob, cache_rows_of(prob, b, sel))
 
 
 def sparse_mla(prob, idx: np.ndarray, rows=None):

@@ -67,6 +67,8 @@ class DSAProblem:
     meta: dict = field(default_factory=dict)
     latent_dtype: Optional[str] = None          # "fp8_e4m3": latent stored as codes ...
     latent_scale: Optional[np.ndarray] = None   # ... with one float32 scale per cache row
+    block_table: Optional[np.ndarray] = None    # paged cache: [B, max_pages] page ids ...
+    page_size: int = 0                          # ... of page_size rows; row_off unused
 
     @property
     def kv_dtype(self) -> str:
@@ -425,11 +427,50 @@ def workload(name: str, seed: int = 0) -> DSAProblem:
                              boost_frac=0.02, latent_dtype="fp8_e4m3", name=name)
     if name == "decode-32k-mtp4":
         return decode_config([32768] * 4, seed=seed, tokens_per_seq=4, name=name)
+    if name == "decode-32k-paged":
+        return paged_view(decode_config([32768] * 4, seed=seed, name="decode-32k"), page_size=64, seed=seed)
     if name == "ties-64k":
         return decode_config([65536] * 16, seed=seed, tie_levels=8, name=name)
     if name == "prefill-8k":
         return prefill_config(8192, seed=seed, name=name)
     raise KeyError(name)
+
+
+def paged_view(prob: DSAProblem, page_size: int = 64, seed: int = 0, spare_pages: int = 3) -> DSAProblem:
+    """The same problem with its caches in a paged pool: every sequence's rows
+    cut into pages of ``page_size`` rows, the pages placed at seeded random
+    slots of a pool with ``spare_pages`` extra pages (filled with other rows),
+    and a block table [B, max_pages] naming each sequence's pages in order
+    (unused table entries point at slot 0). Storage only: the rows are moved,
+    not changed."""
+    import dataclasses
+
+    rng = np.random.default_rng(seed)
+    B = prob.B
+    pages = [(int(n) + page_size - 1) // page_size for n in prob.seq_len]
+    total = sum(pages) + spare_pages
+    slots = rng.permutation(total)
+    max_pages = max(pages)
+    table = np.zeros((B, max_pages), np.int32)
+    src_rows = rng.integers(0, prob.cache_rows, total * page_size)   # spare and tail rows: other rows
+    nxt = 0
+    for b in range(B):
+        for j in range(pages[b]):
+            slot = int(slots[nxt])
+            nxt += 1
+            table[b, j] = slot
+            lo = int(prob.row_off[b]) + j * page_size
+            cnt = min(page_size, int(prob.seq_len[b]) - j * page_size)
+            src_rows[slot * page_size:slot * page_size + cnt] = np.arange(lo, lo + cnt)
+
+    def move(arr):
+        return None if arr is None else np.ascontiguousarray(arr[src_rows])
+
+    return dataclasses.replace(
+        prob, name=prob.name + f"-paged{page_size}", k_idx=move(prob.k_idx), k_scale=move(prob.k_scale),
+        latent=move(prob.latent), latent_scale=move(prob.latent_scale),
+        row_off=np.zeros(B, np.int64), block_table=table, page_size=page_size,
+        meta={**prob.meta, "paged_from": prob.name})
 
 
 def to_torch(prob: DSAProblem, device="cuda"):
@@ -456,4 +497,5 @@ def to_torch(prob: DSAProblem, device="cuda"):
         latent_scale=None if prob.latent_scale is None else t(prob.latent_scale, "f32"),
         row_off=t(prob.row_off.astype(np.int64), None), seq_len=t(prob.seq_len.astype(np.int32), None),
         q_seq=t(prob.q_seq.astype(np.int32), None), q_pos=t(prob.q_pos.astype(np.int32), None),
+        block_table=None if prob.block_table is None else t(prob.block_table.astype(np.int32), None),
     )

@@ -174,3 +174,15 @@ def test_workspace_sizes_are_aligned(dsa):
     assert need >= 4 * 4096 * 8 + 4 * 16
     assert dsa.dsa_workspace_size(dsa.DSA_ENTRY_TOPK, 4, 8192, 2048, 64) == 0
     assert dsa.dsa_workspace_size(dsa.DSA_ENTRY_TOPK, 4096, 32768, 2048, 64) == 0
+
+
+def test_context_parallel_entries_reject(dsa):
+    lib = dsa.lib
+    assert lib.dsa_topk_pairs(None, 8, A, 1, 4, 0, A, A, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_topk_pairs(A, 8, A, 1, 4, -1, A, A, None) == dsa.DSA_ERR_SHAPE
+    assert lib.dsa_topk_merge(A, A, 9, 1, 4, A, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk_merge(A, A, 0, 1, 4, A, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk_merge(A, A, 2, 1, 0, A, None) == dsa.DSA_ERR_SHAPE
+    assert lib.dsa_shard_indices(A, 1, 4, 5, 3, A, None) == dsa.DSA_ERR_SHAPE
+    assert lib.dsa_attn_merge(A, A, 9, 1, 4, A, None, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_attn_merge(MIS, A, 2, 1, 4, A, None, None) == dsa.DSA_ERR_ALIGN

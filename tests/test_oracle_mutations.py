@@ -9,6 +9,7 @@ import test_oracle_attention as TA
 import test_oracle_indexer as TI
 import test_oracle_topk as TT
 import test_oracle_cp as TC
+import test_oracle_pipeline as TPL
 
 
 def _no_relu(q, w, keys):
@@ -100,6 +101,14 @@ def _merge_ties_high_first(pair_scores, pair_idx, k):
     return out
 
 
+def _page_row_without_page_base(prob, b, pos):
+    pos = np.asarray(pos, np.int64)
+    if getattr(prob, "block_table", None) is None:
+        return int(prob.row_off[b]) + pos
+    ps = int(prob.page_size)
+    return np.asarray(prob.block_table, np.int64)[b][pos // ps] + pos % ps
+
+
 def _merge_unweighted(o_parts, lse_parts):
     o = np.asarray(o_parts, np.float64)
     l = np.asarray(lse_parts, np.float64)
@@ -119,6 +128,8 @@ CASES = [
     ("sparse_mla_row", _value_from_rope_end, [TA.test_single_key_gives_its_value_rows, TA.test_golden_hand_case]),
     ("sparse_mla_row", _no_scale, [TA.test_dense_equals_sdpa_when_k_covers_context]),
     ("sparse_mla_row", _latent_only_logits, [TA.test_golden_hand_case]),
+    ("cache_rows_of", _page_row_without_page_base, [TPL.test_paged_cache_rows_hand_case,
+                                                     lambda: TPL.test_paged_view_moves_rows_only(64)]),
     ("topk_merge", _merge_ties_high_first, [TC.test_merge_closed_forms]),
     ("attn_merge", _merge_unweighted, [TC.test_attention_merge_equals_whole_attention,
                                        TC.test_attention_merge_closed_forms]),

@@ -1,5 +1,6 @@
 """Whole-path pins of the oracle and checks of the seeded input generators."""
 import numpy as np
+import pytest
 import torch
 
 from oracle import dsa_oracle as O
@@ -104,3 +105,27 @@ def test_fp8_latent_rows_round_trip():
     assert 0.08 < float(c.std()) < 0.12
     again = inputs.decode_config([600, 300], seed=3, H_I=16, H=16, k=64, latent_dtype="fp8_e4m3")
     assert np.array_equal(p.latent, again.latent) and np.array_equal(p.latent_scale, again.latent_scale)
+
+
+def test_paged_cache_rows_hand_case():
+    """Two sequences in pages of 2 rows: sequence 0 in pages 3, 0; sequence 1 in page 2."""
+    import types
+    p = types.SimpleNamespace(block_table=np.array([[3, 0], [2, 0]], np.int32), page_size=2,
+                              row_off=np.zeros(2, np.int64))
+    assert O.cache_rows_of(p, 0, np.arange(4)).tolist() == [6, 7, 0, 1]
+    assert O.cache_rows_of(p, 1, np.arange(2)).tolist() == [4, 5]
+
+
+@pytest.mark.parametrize("page", [64, 128])
+def test_paged_view_moves_rows_only(page):
+    """The oracle's whole path is unchanged when the caches are paged."""
+    p = inputs.decode_config([700, 300, 129], seed=9, H_I=16, H=16, k=64, key_dtype="fp8_e4m3",
+                             latent_dtype="fp8_e4m3", tokens_per_seq=2)
+    q = inputs.paged_view(p, page_size=page, seed=1)
+    assert q.block_table.shape == (3, (700 + page - 1) // page)
+    assert len(set(q.block_table[q.block_table > 0].ravel().tolist())) == (q.block_table > 0).sum()
+    s1, i1, o1, l1 = O.dsa_forward(p)
+    s2, i2, o2, l2 = O.dsa_forward(q)
+    for a, b in zip(s1, s2):
+        assert np.array_equal(a, b)
+    assert np.array_equal(i1, i2) and np.array_equal(o1, o2) and np.array_equal(l1, l2)
