@@ -357,8 +357,10 @@ def main():
     sets = [base] + [type(base)(**{k: (v.clone() if v is not None else None) for k, v in vars(base).items()})
                      for _ in range(n_sets - 1)]
     m = p.tokens_per_seq
+    paged = p.block_table is not None
     calls = [dsa.DecodeCall(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len, max_len,
-                            p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale, q_per_seq=m)
+                            p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale, q_per_seq=m,
+                            block_table=d.block_table, page_size=p.page_size)
              for d in sets]
     log(f"bench: {n_sets} input sets of {sb / 1e6:.1f} MB algorithmic traffic per step")
 
@@ -428,7 +430,8 @@ def main():
         for l in range(1, share_layers):
             d = sets[(i + l) % n_sets]
             dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, c.idx, p.scale, latent_scale=d.latent_scale,
-                                    q_seq=d.q_seq if m > 1 else None, out=outs[l - 1][0], lse=outs[l - 1][1],
+                                    q_seq=d.q_seq if m > 1 else None, block_table=d.block_table,
+                                    page_size=p.page_size, out=outs[l - 1][0], lse=outs[l - 1][1],
                                     workspace=aws)
 
     for i in range(min(args.warmup, n_sets)):
@@ -447,7 +450,8 @@ def main():
     def attn(i):
         d = sets[i % n_sets]
         dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, calls[i % n_sets].idx, p.scale,
-                                latent_scale=d.latent_scale, q_seq=d.q_seq if m > 1 else None, out=outs[0][0],
+                                latent_scale=d.latent_scale, q_seq=d.q_seq if m > 1 else None,
+                                block_table=d.block_table, page_size=p.page_size, out=outs[0][0],
                                 lse=outs[0][1], workspace=aws)
 
     for i in range(min(args.warmup, n_sets)):
@@ -464,13 +468,14 @@ def main():
 
     # ---- context parallelism rehearsed with 4 key-range shards: the merges ----------------
     cp = None
-    if m == 1:
+    if m == 1 and not paged:
         cp = context_parallel(dsa, p, sets[0], calls[0], args.steps)
         log(f"bench: 4-shard top-k merge {cp['topk_merge_us']:.2f} us, output merge {cp['attn_merge_us']:.2f} us "
             f"(merged selection equals the unsharded one: {cp['merged_equals_unsharded']})")
 
     # ---- the dominant kernel alone: K back-to-back indexer launches ----------------------
-    # (several tokens per sequence: the decode-form entry, which runs the fused step's indexer)
+    # (several tokens per sequence: the decode-form entry, which runs the fused step's
+    # indexer; a paged cache has no standalone indexer entry: no roofline line)
     scores = [torch.empty((p.R, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
 
     def index(i):
@@ -482,21 +487,27 @@ def main():
             dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, max_len, k_scale=d.k_scale,
                                  scores=scores[i % n_sets])
 
-    for i in range(min(args.warmup, n_sets)):
-        index(i)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        index(i)
-    end.record()
-    torch.cuda.synchronize()
-    idx_us = start.elapsed_time(end) * 1e3 / args.steps
-    ib = indexer_bytes(p)
-    achieved = ib / (idx_us * 1e-6) / 1e9
-    idx_tflops = 2.0 * p.H_I * p.D_I * sum(int(x) + 1 for x in p.q_pos.astype(int)) / (idx_us * 1e-6) / 1e12
-    log(f"bench: indexer {idx_us:.2f} us/launch, {achieved:,.0f} GB/s algorithmic, {idx_tflops:.0f} TFLOP/s")
+    roofline = None
+    if not paged:
+        for i in range(min(args.warmup, n_sets)):
+            index(i)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.steps):
+            index(i)
+        end.record()
+        torch.cuda.synchronize()
+        idx_us = start.elapsed_time(end) * 1e3 / args.steps
+        ib = indexer_bytes(p)
+        achieved = ib / (idx_us * 1e-6) / 1e9
+        idx_tflops = 2.0 * p.H_I * p.D_I * sum(int(x) + 1 for x in p.q_pos.astype(int)) / (idx_us * 1e-6) / 1e12
+        log(f"bench: indexer {idx_us:.2f} us/launch, {achieved:,.0f} GB/s algorithmic, {idx_tflops:.0f} TFLOP/s")
 
-    traffic = pmc_traffic(os.path.join(ROOT, "sparse_attention_05_amd", "csrc", "index_scores.hip"), args.workload)
+        traffic = pmc_traffic(os.path.join(ROOT, "sparse_attention_05_amd", "csrc", "index_scores.hip"),
+                              args.workload)
+        roofline = {"kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                    "bytes_per_launch": ib, "us_per_launch": idx_us, "tflops": idx_tflops}
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
@@ -509,6 +520,7 @@ def main():
         "config": {"workload": args.workload, "batch": p.B, "context": max_len, "k": p.k,
                    "indexer_heads": p.H_I, "indexer_dim": p.D_I, "indexer_keys": p.key_dtype,
                    "mla_heads": p.H, "latent_dim": 576, "latent": p.kv_dtype, "tokens_per_seq": m,
+                   "page_size": p.page_size or None,
                    "input_sets": n_sets},
         "step_hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
         "attention": {"us_per_launch": attn_us, "bytes_per_launch": ab,
@@ -520,9 +532,7 @@ def main():
         "context_parallel": cp,
         "step_algorithmic_bytes": sb,
         "deterministic": deterministic,
-        "roofline": {"kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "bytes_per_launch": ib, "us_per_launch": idx_us, "tflops": idx_tflops},
+        "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

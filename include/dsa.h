@@ -225,6 +225,42 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Paged caches (the serving-engine layout: a pool of fixed-size pages and a
+ * block table per sequence). Same computation and outputs as
+ * dsa_sparse_mla_attn / dsa_decode_fused, with row_off replaced by:
+ *   block_table [B, max_pages] int32: position s of sequence b is row
+ *               s % page_size of page block_table[b][s / page_size], i.e.
+ *               cache row block_table[b][s / page_size] * page_size +
+ *               s % page_size of the indexer keys, their fp8 scales, the
+ *               latent rows and their fp8 scales alike;
+ *   page_size   a power of two in 64 .. 2^20 (DSA_ERR_UNSUPPORTED otherwise),
+ *               cache_rows >= page_size; page ids outside the pool
+ *               [0, cache_rows / page_size) are clamped into it;
+ *   max_pages   >= 1; for the decode step max_pages * page_size >= max_len.
+ * The computation per key does not depend on where the key is stored, so a
+ * paged step gives the bits of the same step on a contiguous cache.
+ * Several new tokens per sequence run with one key stream per token.
+ */
+dsa_status dsa_sparse_mla_attn_paged(const void* q_abs, int32_t dtype, const void* latent,
+                                     int32_t latent_dtype, const float* latent_scale,
+                                     int64_t cache_rows, const int32_t* block_table,
+                                     int32_t max_pages, int32_t page_size, int32_t B,
+                                     const int32_t* q_seq, const int32_t* idx, int32_t k,
+                                     int32_t R, int32_t H, float scale, float* out, float* lse,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
+dsa_status dsa_decode_fused_paged(const void* q_idx, const float* head_w, const void* k_idx,
+                                  int32_t k_dtype, const uint16_t* k_scale, const void* q_abs,
+                                  const void* latent, int32_t act_dtype, int32_t latent_dtype,
+                                  const float* latent_scale, int64_t cache_rows,
+                                  const int32_t* block_table, int32_t max_pages,
+                                  int32_t page_size, const int32_t* seq_len, int32_t B,
+                                  int32_t q_per_seq, int32_t max_len, int32_t H_I, int32_t D_I,
+                                  int32_t H, int32_t k, float scale, float* out, float* lse,
+                                  int32_t* idx_out, void* workspace, size_t ws_bytes,
+                                  void* stream);
+
+/*
  * Context parallelism over key ranges ("GLM-5: from Vibe Coding...", section
  * 2.4.2: long sequences split over context-parallel groups). Shard p holds
  * keys [lo_p, hi_p) of every sequence; it scores them (dsa_index_scores over
@@ -264,8 +300,8 @@ dsa_status dsa_shard_indices(const int32_t* idx, int32_t R, int32_t k, int32_t l
 
 /* out[r, h] = sum_p exp(lse_p - LSE) o_p[r, h], lse[r, h] = LSE = log sum_p
  * exp(lse_p), summed in shard order; shards with lse -inf add nothing, and a
- * row with none gets out = 0, lse = -inf. o_parts [P, R, H, 512] fp32 and out
- * [R, H, 512] 16-B aligned; lse_parts [P, R, H]; lse [R, H] or NULL. */
+ * row with none gets out = 0, lse = -inf. P in 1 .. 8. o_parts [P, R, H, 512]
+ * fp32 and out [R, H, 512] 16-B aligned; lse_parts [P, R, H]; lse [R, H] or NULL. */
 dsa_status dsa_attn_merge(const float* o_parts, const float* lse_parts, int32_t P, int32_t R,
                           int32_t H, float* out, float* lse, void* stream);
 

@@ -67,6 +67,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Chunk permutation of key row r (see the header comment).
 __device__ __forceinline__ int row_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
+// Cache row of selected position s of the sequence `base` names (its first
+// row; paged caches: its index, the row then being row s mod page of page
+// table[base][s / page], the page id clamped into the pool); false for a
+// missing key (s < 0 or outside the cache or the block table).
+__device__ __forceinline__ bool attn_row(const AttnArgs& a, int64_t base, int s, int64_t& row) {
+  row = 0;
+  if (s < 0 || base < 0) return false;
+  if (a.table) {
+    const int pi = s >> a.page_shift;
+    if (pi >= a.max_pages) return false;
+    int pg = a.table[base * a.max_pages + pi];
+    const int npages = int(a.cache_rows >> a.page_shift);
+    pg = pg < 0 ? 0 : (pg >= npages ? npages - 1 : pg);
+    row = (int64_t(pg) << a.page_shift) + (s & ((1 << a.page_shift) - 1));
+    return true;
+  }
+  if (base + s >= a.cache_rows) return false;
+  row = base + s;
+  return true;
+}
+
 // The gather of wave `wave`'s 16 rows of chunk c: keys
 // j_beg + 64c + 16*wave + (0..15), whose raw indices the wave left in
 // s_idx[64c + 16*wave + i] (-1 past the range). gather_plan reads the indices
@@ -85,9 +106,8 @@ __device__ __forceinline__ Gather gather_plan(const AttnArgs& a, int64_t base, c
   using Cfg = AttnCfg<F32>;
   int64_t src = -1;
   if (lane < 16) {
-    const int s = s_idx[kChunkKeys * c + 16 * wave + lane];
-    const int64_t row = base + s;
-    if (s >= 0 && base >= 0 && row < a.cache_rows) src = row * Cfg::ROW_BYTES;
+    int64_t row;
+    if (attn_row(a, base, s_idx[kChunkKeys * c + 16 * wave + lane], row)) src = row * Cfg::ROW_BYTES;
   }
   Gather g;
   g.ok = uint32_t(__ballot(src >= 0)) & 0xFFFFu;
@@ -141,16 +161,15 @@ struct BGather {
 
 __device__ __forceinline__ BGather bgather_plan(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
                                                 int wave, int lane) {
-  const int s = s_idx[kChunkKeys * c + 16 * wave + (lane >> 2)];
-  const int64_t row = base + s;
+  int64_t row;
   BGather g;
-  g.live = s >= 0 && base >= 0 && row < a.cache_rows;
+  g.live = attn_row(a, base, s_idx[kChunkKeys * c + 16 * wave + (lane >> 2)], row);
   const unsigned long long okm = __ballot(g.live && (lane & 3) == 0);  // bit 4i: row i
   uint32_t ok = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ok |= uint32_t((okm >> (4 * i)) & 1ull) << i;
   g.ok = ok;
-  g.src = static_cast<const char*>(a.latent) + (g.live ? row : 0) * 1152 + 16 * (lane & 3);
+  g.src = static_cast<const char*>(a.latent) + row * 1152 + 16 * (lane & 3);
   char* blk = buf + kBlock * wave;
   g.lds = lds_addr(blk);
   if (!g.live) {
@@ -295,12 +314,12 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int r, int h, int grp,
 
 }
 
-// First cache row of query r's sequence (load it before the query fragments:
-// waits are in issue order).
+// First cache row of query r's sequence, or (paged caches) the sequence's
+// index (load it before the query fragments: waits are in issue order).
 __device__ __forceinline__ int64_t seq_base(const AttnArgs& a, int r) {
   int b = a.q_seq ? a.q_seq[r] : r / a.qps;
   b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
-  return a.row_off[b];
+  return a.table ? int64_t(b) : a.row_off[b];
 }
 
 // Epilogue of a workgroup: the row sums over the lanes and waves, then the
@@ -605,20 +624,18 @@ struct BGather8 {
 __device__ __forceinline__ BGather8 bgather8_plan(const AttnArgs& a, int64_t base, const int* s_idx, int c,
                                                   char* buf, float* sc, int wave, int lane) {
   const int* si = s_idx + kChunkKeys * c + 16 * wave;
-  const int s = si[lane >> 2];
-  const int64_t row = base + s;
+  int64_t row;
   BGather8 g;
-  g.live = s >= 0 && base >= 0 && row < a.cache_rows;
+  g.live = attn_row(a, base, si[lane >> 2], row);
   const unsigned long long okm = __ballot(g.live && (lane & 3) == 0);  // bit 4i: row i
   uint32_t ok = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) ok |= uint32_t((okm >> (4 * i)) & 1ull) << i;
   g.ok = ok;
-  g.src = static_cast<const char*>(a.latent) + (g.live ? row : 0) * kLatentDim + 16 * (lane & 3);
-  const int s2 = si[lane & 15];
-  const int64_t row2 = base + s2;
-  const bool live2 = s2 >= 0 && base >= 0 && row2 < a.cache_rows;
-  g.ssrc = a.latent_scale + (live2 ? row2 : 0);
+  g.src = static_cast<const char*>(a.latent) + row * kLatentDim + 16 * (lane & 3);
+  int64_t row2;
+  attn_row(a, base, si[lane & 15], row2);  // row 0 when missing
+  g.ssrc = a.latent_scale + row2;
   char* blk = buf + kBlock8 * wave;
   g.lds = lds_addr(blk);
   g.slds = lds_addr(sc + 64 * wave);

@@ -17,6 +17,7 @@ namespace {
 
 constexpr int kMergeThreads = 512;
 constexpr int kMergeMaxWords = 16384;  // P * k words of 8 bytes in LDS
+constexpr int kMaxShards = 8;
 
 // pair_score[r, j] = scores[r, idx[r, j]], pair_idx[r, j] = idx[r, j] + offset
 // (-inf and -1 where idx is -1).
@@ -44,12 +45,26 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float* 
   const int part = blockIdx.x % parts;
   const int m = P * k;
   int valid = 0;
-  for (int e = threadIdx.x; e < m; e += kMergeThreads) {
-    const int p = e / k;
-    const int64_t g = (int64_t(p) * R + r) * k + (e - p * k);
-    const int i = pi[g];
-    w[e] = i >= 0 ? (static_cast<unsigned long long>(order_key(ps[g])) << 32) | static_cast<uint32_t>(~i) : 0ull;
-    valid += i >= 0;
+  // the words, 8 per thread per batch with all their loads in flight
+  for (int e0 = 0; e0 < m; e0 += 8 * kMergeThreads) {
+    int iv[8];
+    float sv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * kMergeThreads + threadIdx.x;
+      const int p = e / k;
+      const int64_t g = (int64_t(p) * R + r) * k + (e - p * k);
+      iv[u] = e < m ? pi[g] : -1;
+      sv[u] = e < m ? ps[g] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * kMergeThreads + threadIdx.x;
+      if (e < m)
+        w[e] = iv[u] >= 0 ? (static_cast<unsigned long long>(order_key(sv[u])) << 32) | static_cast<uint32_t>(~iv[u])
+                          : 0ull;
+      valid += iv[u] >= 0;
+    }
   }
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) valid += __shfl_xor(valid, d, 64);
@@ -114,21 +129,30 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* o_parts, c
   const int64_t rh = gid / (kValueDim / 4);
   const int v4 = int(gid % (kValueDim / 4));
   const int64_t RH = int64_t(R) * H;
+  // all shards' values loaded together (P <= kMaxShards), then summed in shard order
+  float l[kMaxShards];
+  float4 o[kMaxShards];
+#pragma unroll
+  for (int p = 0; p < kMaxShards; ++p) {
+    l[p] = p < P ? lse_parts[p * RH + rh] : -INFINITY;
+    o[p] = p < P ? reinterpret_cast<const float4*>(o_parts + (p * RH + rh) * kValueDim)[v4]
+                 : float4{0.f, 0.f, 0.f, 0.f};
+  }
   float M = -INFINITY;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, lse_parts[p * RH + rh]);
+#pragma unroll
+  for (int p = 0; p < kMaxShards; ++p) M = fmaxf(M, l[p]);
   float L = 0.f;
   float4 acc{0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
-    for (int p = 0; p < P; ++p) {
-      const float l = lse_parts[p * RH + rh];
-      if (l == -INFINITY) continue;
-      const float wgt = expf(l - M);
-      const float4 o = reinterpret_cast<const float4*>(o_parts + (p * RH + rh) * kValueDim)[v4];
+#pragma unroll
+    for (int p = 0; p < kMaxShards; ++p) {
+      if (l[p] == -INFINITY) continue;
+      const float wgt = expf(l[p] - M);
       L += wgt;
-      acc.x += wgt * o.x;
-      acc.y += wgt * o.y;
-      acc.z += wgt * o.z;
-      acc.w += wgt * o.w;
+      acc.x += wgt * o[p].x;
+      acc.y += wgt * o[p].y;
+      acc.z += wgt * o[p].z;
+      acc.w += wgt * o[p].w;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -162,7 +186,7 @@ dsa_status dsa_topk_merge(const float* pair_score, const int32_t* pair_idx, int3
                           int32_t* idx_out, void* stream) {
   if (!pair_score || !pair_idx || !idx_out) return DSA_ERR_NULL;
   if (R < 0 || k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_SHAPE;
-  if (P < 1 || P > 8 || P * k > kMergeMaxWords) return DSA_ERR_UNSUPPORTED;
+  if (P < 1 || P > kMaxShards || P * k > kMergeMaxWords) return DSA_ERR_UNSUPPORTED;
   if (R == 0) return DSA_OK;
   // enough workgroups per row to cover the CUs, each ranking at least 512 candidates
   const int cus = device_cu_count();
@@ -189,7 +213,8 @@ dsa_status dsa_shard_indices(const int32_t* idx, int32_t R, int32_t k, int32_t l
 dsa_status dsa_attn_merge(const float* o_parts, const float* lse_parts, int32_t P, int32_t R, int32_t H, float* out,
                           float* lse, void* stream) {
   if (!o_parts || !lse_parts || !out) return DSA_ERR_NULL;
-  if (P < 1 || R < 0 || H < 1) return DSA_ERR_SHAPE;
+  if (R < 0 || H < 1) return DSA_ERR_SHAPE;
+  if (P < 1 || P > kMaxShards) return DSA_ERR_UNSUPPORTED;
   if (!aligned(o_parts, 16) || !aligned(out, 16)) return DSA_ERR_ALIGN;
   const int64_t threads = int64_t(R) * H * (kValueDim / 4);
   if (threads == 0) return DSA_OK;

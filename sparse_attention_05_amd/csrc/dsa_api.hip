@@ -28,9 +28,9 @@ size_t align256(size_t x) {
 constexpr int kMaxTopkRow = 1 << 20;  // longest score row the top-k accepts
 
 dsa_status check_index_args(const void* q, int q_dtype, const float* w, const void* keys, int k_dtype,
-                            const uint16_t* k_scale, int64_t cache_rows, const int64_t* row_off, int B,
-                            int R, int H_I, int D_I, int max_n) {
-  if (!q || !w || !keys || !row_off) return DSA_ERR_NULL;
+                            const uint16_t* k_scale, int64_t cache_rows, int B, int R, int H_I, int D_I,
+                            int max_n) {
+  if (!q || !w || !keys) return DSA_ERR_NULL;
   if (k_dtype == DSA_FP8_E4M3 && !k_scale) return DSA_ERR_NULL;
   if (R < 0 || B < 1 || cache_rows < 1 || max_n < 1) return DSA_ERR_SHAPE;
   if (H_I < 1 || H_I > 64) return DSA_ERR_UNSUPPORTED;
@@ -56,9 +56,9 @@ dsa_status check_latent(int dtype, int latent_dtype, const float* latent_scale) 
 }
 
 dsa_status check_attn_args(const void* q_abs, int dtype, const void* latent, int latent_dtype,
-                           const float* latent_scale, int64_t cache_rows, const int64_t* row_off, int B,
-                           const int32_t* idx, int k, int R, int H, const float* out) {
-  if (!q_abs || !latent || !row_off || !idx || !out) return DSA_ERR_NULL;
+                           const float* latent_scale, int64_t cache_rows, int B, const int32_t* idx, int k, int R,
+                           int H, const float* out) {
+  if (!q_abs || !latent || !idx || !out) return DSA_ERR_NULL;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return DSA_ERR_DTYPE;
   const dsa_status lt = check_latent(dtype, latent_dtype, latent_scale);
   if (lt != DSA_OK) return lt;
@@ -67,6 +67,38 @@ dsa_status check_attn_args(const void* q_abs, int dtype, const void* latent, int
   if (H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
   if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
   return DSA_OK;
+}
+
+// Where a sequence's cache rows are: consecutive from row_off[b], or in
+// pages of 2^page_shift rows named by the block table.
+struct CacheMap {
+  const int64_t* row_off;
+  const int32_t* table;
+  int max_pages;
+  int page_shift;
+};
+
+dsa_status check_cache_map(const CacheMap& m, int64_t cache_rows, int64_t max_len) {
+  if (!m.table) return m.row_off ? DSA_OK : DSA_ERR_NULL;
+  if (m.page_shift < 6 || m.page_shift > 20) return DSA_ERR_UNSUPPORTED;
+  if (m.max_pages < 1 || cache_rows < (int64_t(1) << m.page_shift)) return DSA_ERR_SHAPE;
+  if (max_len > (int64_t(m.max_pages) << m.page_shift)) return DSA_ERR_SHAPE;
+  return DSA_OK;
+}
+
+// log2 of a power-of-two page size, else -1.
+int page_shift_of(int32_t page_size) {
+  if (page_size < 1 || (page_size & (page_size - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < page_size) ++s;
+  return s;
+}
+
+template <typename Args>
+void set_map(Args& a, const CacheMap& m) {
+  a.table = m.table;
+  a.max_pages = m.max_pages;
+  a.page_shift = m.page_shift;
 }
 
 // Fused-decode workspace, in order: scores [B, ld] fp32, indices [B, k],
@@ -91,6 +123,88 @@ DecodeLayout decode_layout(int B, int max_len, int k, int H) {
 
 size_t decode_ws_bytes(int B, int max_len, int k, int H) {
   return decode_layout(B, max_len, k, H).total;
+}
+
+
+dsa_status decode_fused_impl(const void* q_idx, const float* head_w, const void* k_idx, int32_t k_dtype,
+                             const uint16_t* k_scale, const void* q_abs, const void* latent, int32_t act_dtype,
+                             int32_t latent_dtype, const float* latent_scale, int64_t cache_rows, const CacheMap& cm,
+                             const int32_t* seq_len, int32_t B, int32_t q_per_seq, int32_t max_len, int32_t H_I,
+                             int32_t D_I, int32_t H, int32_t k, float scale, float* out, float* lse,
+                             int32_t* idx_out, void* workspace, size_t ws_bytes, void* stream) {
+  if (q_per_seq < 1 || q_per_seq > DSA_MAX_TOKENS_PER_SEQ) return DSA_ERR_UNSUPPORTED;
+  if (B < 1 || int64_t(B) * q_per_seq > (int64_t(1) << 24)) return DSA_ERR_SHAPE;
+  const int R = B * q_per_seq;  // query rows: q_per_seq per sequence, sequence-major
+  dsa_status st = check_index_args(q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, B, R, H_I, D_I,
+                                   max_len);
+  if (st != DSA_OK) return st;
+  st = check_cache_map(cm, cache_rows, max_len);
+  if (st != DSA_OK) return st;
+  if (!seq_len || !q_abs || !latent || !out) return DSA_ERR_NULL;
+  if (act_dtype != DSA_F32 && act_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  st = check_latent(act_dtype, latent_dtype, latent_scale);
+  if (st != DSA_OK) return st;
+  if (max_len > kMaxTopkRow) return DSA_ERR_UNSUPPORTED;
+  if (k < 1 || k > DSA_MAX_TOPK || H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
+  if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
+  const size_t need = decode_ws_bytes(R, max_len, k, H);
+  if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSA_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DecodeLayout L = decode_layout(R, max_len, k, H);
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
+  void* attn_ws = ws + L.attn;
+  float* sample = reinterpret_cast<float*>(ws + L.sample);
+  const bool split = topk_use_split(R, max_len);
+
+  // the indexer also writes the score sample the split top-k takes its pivot from
+  IndexArgs ia{q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, cm.row_off, B, nullptr, nullptr,
+               seq_len, R, H_I, D_I, max_len, scores, L.ld, split ? sample : nullptr, L.ld_sample};
+  ia.qps = q_per_seq;
+  set_map(ia, cm);
+  hipError_t e = launch_index_scores(ia, s);
+  if (e != hipSuccess) return hip_fail(e);
+  TopkArgs ta{scores, L.ld, nullptr, seq_len, R, max_len, k, idx, split ? sample : nullptr, L.ld_sample,
+              nullptr, nullptr};
+  ta.qps = q_per_seq;
+  const AttnPlan plan = plan_attention(R, H, k);
+  AttnArgs aa{q_abs, act_dtype, latent, latent_dtype, latent_scale, cache_rows, cm.row_off, B, nullptr, idx, k,
+              R, H, scale, out, lse, attn_ws};
+  aa.qps = q_per_seq;
+  set_map(aa, cm);
+  if (split && act_dtype == DSA_BF16) {  // few long rows: selection fused with the attention
+    topk_split_carve(ws + L.topk, R, max_len, ta);
+    e = launch_topk_attn(ta, aa, plan, s);
+    return e == hipSuccess ? DSA_OK : hip_fail(e);
+  }
+  if (split) topk_split_carve(ws + L.topk, R, max_len, ta);
+  e = launch_topk(ta, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_sparse_mla(aa, plan, s);
+  return e == hipSuccess ? DSA_OK : hip_fail(e);
+}
+
+dsa_status sparse_mla_impl(const void* q_abs, int32_t dtype, const void* latent, int32_t latent_dtype,
+                           const float* latent_scale, int64_t cache_rows, const CacheMap& cm, int32_t B,
+                           const int32_t* q_seq, const int32_t* idx, int32_t k, int32_t R, int32_t H, float scale,
+                           float* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_attn_args(q_abs, dtype, latent, latent_dtype, latent_scale, cache_rows, B, idx, k, R, H,
+                                  out);
+  if (st != DSA_OK) return st;
+  st = check_cache_map(cm, cache_rows, 0);
+  if (st != DSA_OK) return st;
+  if (!q_seq && R != B) return DSA_ERR_SHAPE;
+  const AttnPlan plan = plan_attention(R, H, k);
+  if (plan.ws_bytes && (!workspace || ws_bytes < plan.ws_bytes)) return DSA_ERR_WORKSPACE;
+  if (plan.ws_bytes && !aligned16(workspace)) return DSA_ERR_ALIGN;
+  AttnArgs a{q_abs, dtype, latent, latent_dtype, latent_scale, cache_rows, cm.row_off, B, q_seq, idx, k, R, H,
+             scale, out, lse, workspace};
+  set_map(a, cm);
+  hipError_t e = launch_sparse_mla(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : hip_fail(e);
 }
 
 }  // namespace
@@ -118,10 +232,10 @@ dsa_status dsa_index_scores(const void* q_idx, int32_t q_dtype, const float* hea
                             const int64_t* row_off, int32_t B, const int32_t* q_seq, const int32_t* q_pos,
                             int32_t R, int32_t H_I, int32_t D_I, int32_t max_n, float* scores,
                             int64_t ld_scores, void* stream) {
-  dsa_status st = check_index_args(q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, R,
-                                   H_I, D_I, max_n);
+  dsa_status st = check_index_args(q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, B, R, H_I, D_I,
+                                   max_n);
   if (st != DSA_OK) return st;
-  if (!q_pos || !scores) return DSA_ERR_NULL;
+  if (!q_pos || !scores || !row_off) return DSA_ERR_NULL;
   if (!q_seq && R != B) return DSA_ERR_SHAPE;
   if (ld_scores < max_n || (ld_scores & 3)) return DSA_ERR_SHAPE;
   if (!aligned16(scores)) return DSA_ERR_ALIGN;
@@ -139,10 +253,10 @@ dsa_status dsa_index_scores_decode(const void* q_idx, int32_t q_dtype, const flo
   if (q_per_seq < 1 || q_per_seq > DSA_MAX_TOKENS_PER_SEQ) return DSA_ERR_UNSUPPORTED;
   if (B < 1 || int64_t(B) * q_per_seq > (int64_t(1) << 24)) return DSA_ERR_SHAPE;
   const int R = B * q_per_seq;
-  dsa_status st = check_index_args(q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, R,
-                                   H_I, D_I, max_len);
+  dsa_status st = check_index_args(q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, B, R, H_I, D_I,
+                                   max_len);
   if (st != DSA_OK) return st;
-  if (!seq_len || !scores) return DSA_ERR_NULL;
+  if (!seq_len || !scores || !row_off) return DSA_ERR_NULL;
   if (ld_scores < max_len || (ld_scores & 3)) return DSA_ERR_SHAPE;
   if (!aligned16(scores)) return DSA_ERR_ALIGN;
   IndexArgs a{q_idx, q_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, nullptr, nullptr, seq_len,
@@ -176,17 +290,21 @@ dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* lat
                                const int32_t* q_seq, const int32_t* idx, int32_t k, int32_t R, int32_t H,
                                float scale, float* out, float* lse, void* workspace, size_t ws_bytes,
                                void* stream) {
-  dsa_status st = check_attn_args(q_abs, dtype, latent, latent_dtype, latent_scale, cache_rows, row_off, B, idx,
-                                  k, R, H, out);
-  if (st != DSA_OK) return st;
-  if (!q_seq && R != B) return DSA_ERR_SHAPE;
-  const AttnPlan plan = plan_attention(R, H, k);
-  if (plan.ws_bytes && (!workspace || ws_bytes < plan.ws_bytes)) return DSA_ERR_WORKSPACE;
-  if (plan.ws_bytes && !aligned16(workspace)) return DSA_ERR_ALIGN;
-  AttnArgs a{q_abs, dtype, latent, latent_dtype, latent_scale, cache_rows, row_off, B, q_seq, idx, k, R, H,
-             scale, out, lse, workspace};
-  hipError_t e = launch_sparse_mla(a, plan, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? DSA_OK : hip_fail(e);
+  return sparse_mla_impl(q_abs, dtype, latent, latent_dtype, latent_scale, cache_rows, CacheMap{row_off, nullptr, 0, 0},
+                         B, q_seq, idx, k, R, H, scale, out, lse, workspace, ws_bytes, stream);
+}
+
+dsa_status dsa_sparse_mla_attn_paged(const void* q_abs, int32_t dtype, const void* latent, int32_t latent_dtype,
+                                     const float* latent_scale, int64_t cache_rows, const int32_t* block_table,
+                                     int32_t max_pages, int32_t page_size, int32_t B, const int32_t* q_seq,
+                                     const int32_t* idx, int32_t k, int32_t R, int32_t H, float scale, float* out,
+                                     float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (!block_table) return DSA_ERR_NULL;
+  const int sh = page_shift_of(page_size);
+  if (sh < 0) return DSA_ERR_UNSUPPORTED;
+  return sparse_mla_impl(q_abs, dtype, latent, latent_dtype, latent_scale, cache_rows,
+                         CacheMap{nullptr, block_table, max_pages, sh}, B, q_seq, idx, k, R, H, scale, out, lse,
+                         workspace, ws_bytes, stream);
 }
 
 dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* k_idx, int32_t k_dtype,
@@ -196,56 +314,28 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
                             int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k, float scale,
                             float* out, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
                             void* stream) {
-  if (q_per_seq < 1 || q_per_seq > DSA_MAX_TOKENS_PER_SEQ) return DSA_ERR_UNSUPPORTED;
-  if (B < 1 || int64_t(B) * q_per_seq > (int64_t(1) << 24)) return DSA_ERR_SHAPE;
-  const int R = B * q_per_seq;  // query rows: q_per_seq per sequence, sequence-major
-  dsa_status st = check_index_args(q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, R,
-                                   H_I, D_I, max_len);
-  if (st != DSA_OK) return st;
-  if (!seq_len || !q_abs || !latent || !out) return DSA_ERR_NULL;
-  if (act_dtype != DSA_F32 && act_dtype != DSA_BF16) return DSA_ERR_DTYPE;
-  st = check_latent(act_dtype, latent_dtype, latent_scale);
-  if (st != DSA_OK) return st;
-  if (max_len > kMaxTopkRow) return DSA_ERR_UNSUPPORTED;
-  if (k < 1 || k > DSA_MAX_TOPK || H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
-  if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
-  const size_t need = decode_ws_bytes(R, max_len, k, H);
-  if (!workspace || ws_bytes < need) return DSA_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSA_ERR_ALIGN;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const DecodeLayout L = decode_layout(R, max_len, k, H);
-  char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws + L.scores);
-  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + L.idx);
-  void* attn_ws = ws + L.attn;
-  float* sample = reinterpret_cast<float*>(ws + L.sample);
-  const bool split = topk_use_split(R, max_len);
-
-  // the indexer also writes the score sample the split top-k takes its pivot from
-  IndexArgs ia{q_idx, act_dtype, head_w, k_idx, k_dtype, k_scale, cache_rows, row_off, B, nullptr, nullptr,
-               seq_len, R, H_I, D_I, max_len, scores, L.ld, split ? sample : nullptr, L.ld_sample};
-  ia.qps = q_per_seq;
-  hipError_t e = launch_index_scores(ia, s);
-  if (e != hipSuccess) return hip_fail(e);
-  TopkArgs ta{scores, L.ld, nullptr, seq_len, R, max_len, k, idx, split ? sample : nullptr, L.ld_sample,
-              nullptr, nullptr};
-  ta.qps = q_per_seq;
-  const AttnPlan plan = plan_attention(R, H, k);
-  AttnArgs aa{q_abs, act_dtype, latent, latent_dtype, latent_scale, cache_rows, row_off, B, nullptr, idx, k, R,
-              H, scale, out, lse, attn_ws};
-  aa.qps = q_per_seq;
-  if (split && act_dtype == DSA_BF16) {  // few long rows: selection fused with the attention
-    topk_split_carve(ws + L.topk, R, max_len, ta);
-    e = launch_topk_attn(ta, aa, plan, s);
-    return e == hipSuccess ? DSA_OK : hip_fail(e);
-  }
-  if (split) topk_split_carve(ws + L.topk, R, max_len, ta);
-  e = launch_topk(ta, s);
-  if (e != hipSuccess) return hip_fail(e);
-  e = launch_sparse_mla(aa, plan, s);
-  return e == hipSuccess ? DSA_OK : hip_fail(e);
+  return decode_fused_impl(q_idx, head_w, k_idx, k_dtype, k_scale, q_abs, latent, act_dtype, latent_dtype,
+                           latent_scale, cache_rows, CacheMap{row_off, nullptr, 0, 0}, seq_len, B, q_per_seq,
+                           max_len, H_I, D_I, H, k, scale, out, lse, idx_out, workspace, ws_bytes, stream);
 }
+
+dsa_status dsa_decode_fused_paged(const void* q_idx, const float* head_w, const void* k_idx, int32_t k_dtype,
+                                  const uint16_t* k_scale, const void* q_abs, const void* latent,
+                                  int32_t act_dtype, int32_t latent_dtype, const float* latent_scale,
+                                  int64_t cache_rows, const int32_t* block_table, int32_t max_pages,
+                                  int32_t page_size, const int32_t* seq_len, int32_t B, int32_t q_per_seq,
+                                  int32_t max_len, int32_t H_I, int32_t D_I, int32_t H, int32_t k, float scale,
+                                  float* out, float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  if (!block_table) return DSA_ERR_NULL;
+  const int sh = page_shift_of(page_size);
+  if (sh < 0) return DSA_ERR_UNSUPPORTED;
+  return decode_fused_impl(q_idx, head_w, k_idx, k_dtype, k_scale, q_abs, latent, act_dtype, latent_dtype,
+                           latent_scale, cache_rows, CacheMap{nullptr, block_table, max_pages, sh}, seq_len, B,
+                           q_per_seq, max_len, H_I, D_I, H, k, scale, out, lse, idx_out, workspace, ws_bytes,
+                           stream);
+}
+
 
 size_t dsa_workspace_size(int32_t entry, int32_t rows, int32_t max_len, int32_t k, int32_t H) {
   if (rows < 0 || k < 1 || H < 1) return 0;

@@ -29,6 +29,9 @@ struct IndexArgs {
   int64_t ld_sample;
   int qps = 1;            // decode form (q_seq, q_pos NULL): row r is query r % qps of sequence r / qps,
                           // at position seq_len - qps + r % qps
+  const int32_t* table = nullptr;  // paged caches: [B, max_pages] page ids (row_off unused)
+  int max_pages = 0;
+  int page_shift = 0;              // log2 of the page size (>= 6)
 };
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 
@@ -79,6 +82,9 @@ struct AttnArgs {
   float* lse;
   void* ws;
   int qps = 1;  // q_seq NULL: row r belongs to sequence r / qps
+  const int32_t* table = nullptr;  // paged caches, as in IndexArgs
+  int max_pages = 0;
+  int page_shift = 0;
 };
 hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);  // + combine
 hipError_t launch_attn_combine(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);

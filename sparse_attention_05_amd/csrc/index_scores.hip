@@ -162,6 +162,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p)));
 }
 
+// Cache row of key s of the sequence `base` names: base + s, or (paged) row
+// s mod page of page table[base][s / page], the page id clamped into the pool.
+__device__ __forceinline__ int64_t key_row(const IndexArgs& a, int64_t base, int64_t s) {
+  if (!a.table) return base + s;
+  int pg = a.table[base * a.max_pages + (s >> a.page_shift)];
+  const int npages = int(a.cache_rows >> a.page_shift);
+  pg = pg < 0 ? 0 : (pg >= npages ? npages - 1 : pg);
+  return (int64_t(pg) << a.page_shift) + (s & ((int64_t(1) << a.page_shift) - 1));
+}
+
 // Start the direct-to-LDS load of keys s0 .. s0+63 (those below s_end) into
 // stage buffer `dst`; fp8 keys: then their row scales (bf16 bits), key s0+l
 // into the 32-bit word sc_dst + 4*l (zero past s_end). All earlier LDS reads
@@ -173,19 +183,21 @@ __device__ __forceinline__ void load_group(const IndexArgs& a, int64_t base, int
   using C = KeyCfg<QK, DI>;
   const char* keys = static_cast<const char*>(a.keys);
   const uint32_t to = lds_addr(dst);
+  // the group's 64 keys are consecutive cache rows (a page holds whole groups)
+  const int64_t g0 = key_row(a, base, s0);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
   for (int m = 0; m < C::LOADS; ++m) {
     const int pch = 64 * m + lane;      // physical chunk index in the group
     const int row = pch / C::CPR;
     const int lc = (pch % C::CPR) ^ (row & C::SWZ);
-    const int64_t key = s0 + row < s_end ? base + s0 + row : base;  // rows past the range re-read row 0
+    const int64_t key = s0 + row < s_end ? g0 + row : g0;  // rows past the range re-read the first
     dma16(keys + key * C::ROW + 16 * lc, to + 1024 * m);
   }
   if constexpr (QK == 2) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.k_scale + base), 0, int(2 * s_end), 0x00020000);
-    dma2_buf(rs, uint32_t(2 * (s0 + lane)), lds_addr(sc_dst));
+        const_cast<uint16_t*>(a.k_scale + g0), 0, int(2 * (s_end - s0)), 0x00020000);
+    dma2_buf(rs, uint32_t(2 * lane), lds_addr(sc_dst));
   }
 }
 
@@ -254,17 +266,25 @@ __device__ __forceinline__ void wait_ops(int n) {
   }
 }
 
-// Keys of query r: cache rows base .. base+n-1 of its sequence.
+// Keys 0 .. n-1 of query r's sequence; base is the sequence's first cache
+// row, or (paged caches) the sequence's index (see key_row).
 __device__ __forceinline__ void query_range(const IndexArgs& a, int r, int64_t& base, int64_t& n) {
   int b = a.q_seq ? a.q_seq[r] : r / a.qps;
   b = b < 0 ? 0 : (b >= a.B ? a.B - 1 : b);
   const int qpos = a.q_pos ? a.q_pos[r] : a.seq_len[b] - a.qps + r % a.qps;
   n = qpos + 1 < a.max_n ? qpos + 1 : a.max_n;
   if (n < 0) n = 0;
+  if (a.table) {
+    base = b;
+    const int64_t cap = int64_t(a.max_pages) << a.page_shift;
+    if (n > cap) n = cap;
+    return;
+  }
   base = a.row_off[b];
   if (base < 0 || base >= a.cache_rows) n = 0;
   else if (n > a.cache_rows - base) n = a.cache_rows - base;
 }
+
 
 // Balanced form (R <= 64, a 1-D grid of G >= R workgroups): every wave works
 // out the same split from all the rows' lengths (lane r: row r), with no
@@ -501,7 +521,7 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
       float sc = 1.f;
       if constexpr (QK == 2) {
         const int64_t s = s0 + 16 * blk + col;
-        sc = s < s_end ? bf16_bits_to_f32(a.k_scale[base + s]) : 1.f;
+        sc = s < s_end ? bf16_bits_to_f32(a.k_scale[key_row(a, base, s)]) : 1.f;
       }
       float p = 0.f;
       if (QK == 2 && sc < 0.f) {
@@ -538,7 +558,7 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
     if (s < s_end) {
       if constexpr (QK == 2) {
         // Non-negative row scale: relu(sc*z) = sc*relu(z), applied once per key.
-        const float sc = bf16_bits_to_f32(a.k_scale[base + s]);
+        const float sc = bf16_bits_to_f32(a.k_scale[key_row(a, base, s)]);
         if (!(sc < 0.f)) v *= sc;
       }
       out[s] = v;
@@ -924,12 +944,14 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   // many bf16 queries of one sequence (causal prefill form): key tiles shared by 8 queries
   // (key and score rows are addressed with 32-bit byte offsets there)
   // several new bf16 tokens per sequence (decode form): each key row read once for all of them
-  if (mode == 1 && !a.q_seq && !a.q_pos && a.qps >= 2 && a.qps <= kPfWaves && a.max_n <= (int64_t(1) << 22)) {
+  if (mode == 1 && !a.q_seq && !a.q_pos && !a.table && a.qps >= 2 && a.qps <= kPfWaves &&
+      a.max_n <= (int64_t(1) << 22)) {
     if (a.H_I <= 16) return a.D_I == 64 ? launch_multi_token<1, 64>(a, stream) : launch_multi_token<1, 128>(a, stream);
     if (a.H_I <= 32) return a.D_I == 64 ? launch_multi_token<2, 64>(a, stream) : launch_multi_token<2, 128>(a, stream);
     return a.D_I == 64 ? launch_multi_token<4, 64>(a, stream) : launch_multi_token<4, 128>(a, stream);
   }
-  if (mode == 1 && a.B == 1 && a.q_pos && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 22) && !a.sample) {
+  if (mode == 1 && a.B == 1 && a.q_pos && !a.table && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 22) &&
+      !a.sample) {
     if (a.H_I <= 16) return a.D_I == 64 ? launch_prefill<1, 64>(a, stream) : launch_prefill<1, 128>(a, stream);
     if (a.H_I <= 32) return a.D_I == 64 ? launch_prefill<2, 64>(a, stream) : launch_prefill<2, 128>(a, stream);
     return a.D_I == 64 ? launch_prefill<4, 64>(a, stream) : launch_prefill<4, 128>(a, stream);

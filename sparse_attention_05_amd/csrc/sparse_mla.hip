@@ -118,15 +118,14 @@ struct WideGather {
 __device__ __forceinline__ WideGather wide_gather(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
                                                   int wave, int lane) {
   using Cfg = AttnCfg<false>;
-  const int s = s_idx[kChunkKeys * c + 16 * wave + (lane >> 2)];
-  const int64_t row = base + s;
-  const bool ok = s >= 0 && base >= 0 && row < a.cache_rows;
+  int64_t row;
+  const bool ok = attn_row(a, base, s_idx[kChunkKeys * c + 16 * wave + (lane >> 2)], row);
   const unsigned long long okm = __ballot(ok && (lane & 3) == 0);  // bit 4i: row i
   uint32_t mask = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mask |= uint32_t((okm >> (4 * i)) & 1ull) << i;
   WideGather g;
-  g.src = static_cast<const char*>(a.latent) + (ok ? row : 0) * Cfg::ROW_BYTES + 16 * (lane & 3);
+  g.src = static_cast<const char*>(a.latent) + row * Cfg::ROW_BYTES + 16 * (lane & 3);
   g.lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(buf + kWideBlock * wave))));
   g.mask = mask;

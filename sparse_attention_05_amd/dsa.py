@@ -35,6 +35,10 @@ SIGNATURES = {
                                    _P, _P, _P, _SZ, _P]),
     "dsa_decode_fused": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _I32, _I32, _I32,
                                 _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
+    "dsa_sparse_mla_attn_paged": (_I32, [_P, _I32, _P, _I32, _P, _I64, _P, _I32, _I32, _I32, _P, _P, _I32, _I32,
+                                         _I32, _F32, _P, _P, _P, _SZ, _P]),
+    "dsa_decode_fused_paged": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _I32, _I32, _P,
+                                      _I32, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
     "dsa_topk_pairs": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _P]),
     "dsa_topk_merge": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P]),
     "dsa_shard_indices": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _P]),
@@ -174,14 +178,17 @@ def dsa_topk(scores: torch.Tensor, q_pos: torch.Tensor, max_n: int, k: int, *,
     return idx_out
 
 
-def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, row_off: torch.Tensor,
+def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, row_off: Optional[torch.Tensor],
                         idx: torch.Tensor, scale: float, *, latent_scale: Optional[torch.Tensor] = None,
-                        q_seq: Optional[torch.Tensor] = None,
+                        q_seq: Optional[torch.Tensor] = None, block_table: Optional[torch.Tensor] = None,
+                        page_size: int = 0,
                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                         want_lse: bool = True, workspace: Optional[torch.Tensor] = None,
                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Sparse absorbed MLA: (out [R, H, 512] fp32, lse [R, H] fp32). A uint8
-    (or float8_e4m3fn) latent holds e4m3 codes scaled by latent_scale [rows]."""
+    (or float8_e4m3fn) latent holds e4m3 codes scaled by latent_scale [rows].
+    With block_table [B, max_pages] (and page_size) the cache is paged and
+    row_off is ignored."""
     R, H, _ = q_abs.shape
     k = idx.shape[1]
     dev = q_abs.device
@@ -191,11 +198,20 @@ def dsa_sparse_mla_attn(q_abs: torch.Tensor, latent: torch.Tensor, row_off: torc
         lse = torch.empty((R, H), dtype=torch.float32, device=dev)
     nbytes = dsa_workspace_size(DSA_ENTRY_SPARSE_MLA, R, 0, k, H)
     workspace = _workspace(nbytes, workspace, dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if block_table is not None:
+        st = lib.dsa_sparse_mla_attn_paged(
+            _ptr(q_abs), _dtype_code(q_abs), _ptr(latent), _dtype_code(latent), _ptr(latent_scale),
+            latent.shape[0], _ptr(block_table), block_table.shape[1], int(page_size), block_table.shape[0],
+            _ptr(q_seq), _ptr(idx), k, R, H, float(scale), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
+            _stream(stream))
+        _check(st, "dsa_sparse_mla_attn_paged")
+        return out, lse
     st = lib.dsa_sparse_mla_attn(
         _ptr(q_abs), _dtype_code(q_abs), _ptr(latent), _dtype_code(latent), _ptr(latent_scale), latent.shape[0],
         _ptr(row_off), row_off.numel(),
-        _ptr(q_seq), _ptr(idx), k, R, H, float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+        _ptr(q_seq), _ptr(idx), k, R, H, float(scale), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
+        _stream(stream))
     _check(st, "dsa_sparse_mla_attn")
     return out, lse
 
@@ -265,8 +281,9 @@ class DecodeCall:
     allocation. Used where per-step host overhead matters."""
 
     def __init__(self, q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
-                 scale: float, *, k_scale=None, latent_scale=None, q_per_seq: int = 1, out=None, lse=None,
-                 idx_out=None, want_lse=True, record_idx=True, workspace=None):
+                 scale: float, *, k_scale=None, latent_scale=None, q_per_seq: int = 1, block_table=None,
+                 page_size: int = 0, out=None, lse=None, idx_out=None, want_lse=True, record_idx=True,
+                 workspace=None):
         R, H_I, D_I = q_idx.shape
         B = seq_len.numel()
         if R != B * q_per_seq:
@@ -281,26 +298,31 @@ class DecodeCall:
         self.workspace = _workspace(nbytes, workspace, dev)
         if _dtype_code(q_idx) != _dtype_code(q_abs):
             raise TypeError("q_idx and q_abs must share one dtype")
-        self._keep = (q_idx, head_w, k_idx, k_scale, q_abs, latent, latent_scale, row_off, seq_len)
+        self._keep = (q_idx, head_w, k_idx, k_scale, q_abs, latent, latent_scale, row_off, seq_len, block_table)
+        cache = ((_ptr(block_table), block_table.shape[1], int(page_size)) if block_table is not None
+                 else (_ptr(row_off),))
+        self._fn = lib.dsa_decode_fused_paged if block_table is not None else lib.dsa_decode_fused
         self._args = (
             _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _dtype_code(k_idx), _ptr(k_scale), _ptr(q_abs), _ptr(latent),
-            _dtype_code(q_abs), _dtype_code(latent), _ptr(latent_scale), k_idx.shape[0], _ptr(row_off),
+            _dtype_code(q_abs), _dtype_code(latent), _ptr(latent_scale), k_idx.shape[0], *cache,
             _ptr(seq_len), B, q_per_seq, max_len, H_I, D_I, H, k,
             float(scale), _ptr(self.out), _ptr(self.lse), _ptr(self.idx), _ptr(self.workspace),
             self.workspace.numel() * self.workspace.element_size())
 
     def __call__(self, stream=None):
-        st = lib.dsa_decode_fused(*self._args, _stream(stream))
+        st = self._fn(*self._args, _stream(stream))
         _check(st, "dsa_decode_fused")
         return self.out, self.lse, self.idx
 
 
 def dsa_decode_fused(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
-                     scale: float, *, k_scale=None, latent_scale=None, q_per_seq: int = 1, out=None, lse=None,
-                     idx_out=None, want_lse=True, record_idx=True, workspace=None, stream=None):
+                     scale: float, *, k_scale=None, latent_scale=None, q_per_seq: int = 1, block_table=None,
+                     page_size: int = 0, out=None, lse=None, idx_out=None, want_lse=True, record_idx=True,
+                     workspace=None, stream=None):
     """One decode step for q_per_seq new tokens per sequence (R = B * q_per_seq
     rows, sequence-major); returns (out [R,H,512], lse [R,H] or None, idx [R,k] or None)."""
     call = DecodeCall(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len, k, scale,
-                      k_scale=k_scale, latent_scale=latent_scale, q_per_seq=q_per_seq, out=out, lse=lse,
-                      idx_out=idx_out, want_lse=want_lse, record_idx=record_idx, workspace=workspace)
+                      k_scale=k_scale, latent_scale=latent_scale, q_per_seq=q_per_seq, block_table=block_table,
+                      page_size=page_size, out=out, lse=lse, idx_out=idx_out, want_lse=want_lse,
+                      record_idx=record_idx, workspace=workspace)
     return call(stream)

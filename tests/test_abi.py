@@ -186,3 +186,23 @@ def test_context_parallel_entries_reject(dsa):
     assert lib.dsa_shard_indices(A, 1, 4, 5, 3, A, None) == dsa.DSA_ERR_SHAPE
     assert lib.dsa_attn_merge(A, A, 9, 1, 4, A, None, None) == dsa.DSA_ERR_UNSUPPORTED
     assert lib.dsa_attn_merge(MIS, A, 2, 1, 4, A, None, None) == dsa.DSA_ERR_ALIGN
+
+
+def test_paged_entries_reject(dsa):
+    lib = dsa.lib
+    need = dsa.dsa_workspace_size(dsa.DSA_ENTRY_DECODE, 4, 32768, 2048, 64)
+
+    def fused(table=A, max_pages=512, page=64, ws=need):
+        return lib.dsa_decode_fused_paged(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, table, max_pages, page,
+                                          A, 4, 1, 32768, 64, 128, 64, 2048, 0.07, A, None, None, A, ws, None)
+    assert fused(table=None) == dsa.DSA_ERR_NULL
+    assert fused(page=96) == dsa.DSA_ERR_UNSUPPORTED       # not a power of two
+    assert fused(page=32) == dsa.DSA_ERR_UNSUPPORTED       # below one 64-key group
+    assert fused(max_pages=511) == dsa.DSA_ERR_SHAPE       # the table cannot hold max_len
+    assert fused(ws=need - 1) == dsa.DSA_ERR_WORKSPACE
+
+    def attn(table=A, page=64):
+        return lib.dsa_sparse_mla_attn_paged(A, 1, A, 1, None, 100000, table, 64, page, 4, None, A, 2048, 4, 64,
+                                             0.1, A, None, None, 0, None)
+    assert attn(table=None) == dsa.DSA_ERR_NULL
+    assert attn(page=100) == dsa.DSA_ERR_UNSUPPORTED

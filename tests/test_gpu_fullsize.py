@@ -35,7 +35,7 @@ def _say(*a):
 def _decode_call(dsa, p, d):
     return dsa.DecodeCall(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len,
                           int(p.seq_len.max()), p.k, p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale,
-                          q_per_seq=p.tokens_per_seq)
+                          q_per_seq=p.tokens_per_seq, block_table=d.block_table, page_size=p.page_size)
 
 
 def _run(call):
@@ -109,6 +109,19 @@ def test_decode_32k_multi_token_fullsize(dsa):
     rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale,
                                            q_seq=d.q_seq)
     assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
+
+
+def test_decode_32k_paged_fullsize(dsa):
+    """decode-32k in a pool of shuffled 64-row pages: the contiguous step's bits."""
+    p = inputs.workload("decode-32k-paged")
+    c = inputs.workload("decode-32k")
+    d = inputs.to_torch(p)
+    o, l, i = _run(_decode_call(dsa, p, d))
+    dc = inputs.to_torch(c)
+    oc, lc, ic = _run(_decode_call(dsa, c, dc))
+    assert np.array_equal(i, ic) and np.array_equal(o, oc) and np.array_equal(l, lc)
+    ref_o, ref_l = O.sparse_mla(p, i)
+    C.assert_attn_close(o, ref_o, l, ref_l)
 
 
 def test_ties_64k_replay_fullsize(dsa):

@@ -717,3 +717,57 @@ def test_topk_merge_matches_oracle_on_random_lists(dsa):
     got = dsa.dsa_topk_merge(torch.from_numpy(ps).cuda(), torch.from_numpy(pi).cuda()).cpu().numpy()
     for r in range(R):
         assert np.array_equal(got[r], O.topk_merge(ps[:, r], pi[:, r], k)), f"row {r}"
+
+
+# ------------------------------------------------------------------------------
+# paged caches: a block table over a shuffled page pool
+# ------------------------------------------------------------------------------
+
+def _decode_run(dsa, p, d):
+    import torch
+    max_len = int(p.seq_len.max())
+    call = dsa.DecodeCall(d.q_idx, d.head_w, d.k_idx, d.q_abs, d.latent, d.row_off, d.seq_len, max_len, p.k,
+                          p.scale, k_scale=d.k_scale, latent_scale=d.latent_scale, q_per_seq=p.tokens_per_seq,
+                          block_table=d.block_table, page_size=p.page_size)
+    o, l, i = call()
+    torch.cuda.synchronize()
+    return o.cpu().numpy().copy(), l.cpu().numpy().copy(), i.cpu().numpy().copy()
+
+
+@pytest.mark.parametrize("page,lens,key_dtype,latent_dtype", [
+    (64, [12000, 9000, 20000], "bf16", "bf16"),            # selection fused with the attention
+    (256, [4096, 3000, 700], "bf16", "bf16"),              # selection, then the attention kernel
+    (128, [9000, 16385], "fp8_e4m3", "fp8_e4m3"),
+    (64, [600] * 70, "bf16", "bf16"),                       # many rows
+])
+def test_paged_decode_equals_contiguous(dsa, page, lens, key_dtype, latent_dtype):
+    """Where a key is stored does not change its arithmetic: the paged step
+    gives the contiguous step's indices and outputs bit for bit, and so does
+    the paged attention entry replaying the indices."""
+    import torch
+    p = inputs.decode_config(lens, seed=51, k=2048, key_dtype=key_dtype, latent_dtype=latent_dtype,
+                             boost_frac=0.02 if key_dtype == "fp8_e4m3" else 0.0)
+    q = inputs.paged_view(p, page_size=page, seed=5)
+    o1, l1, i1 = _decode_run(dsa, p, inputs.to_torch(p))
+    dq = inputs.to_torch(q)
+    o2, l2, i2 = _decode_run(dsa, q, dq)
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    rep_o, rep_l = dsa.dsa_sparse_mla_attn(dq.q_abs, dq.latent, None, torch.from_numpy(i2).cuda(), q.scale,
+                                           latent_scale=dq.latent_scale, block_table=dq.block_table,
+                                           page_size=page)
+    assert np.array_equal(rep_o.cpu().numpy(), o2) and np.array_equal(rep_l.cpu().numpy(), l2)
+    rows = [0, q.R - 1]
+    ref_o, ref_l = O.sparse_mla(q, i2[rows], rows=rows)
+    C.assert_attn_close(o2[rows], ref_o, l2[rows], ref_l)
+
+
+def test_paged_multi_token_decode_matches_oracle(dsa):
+    """Several new tokens per sequence on a paged cache (one key stream per
+    token): indices equal the oracle's on tie-class inputs (exact scores)."""
+    p = inputs.decode_config([9000, 6000], seed=52, k=2048, tie_levels=8, tokens_per_seq=3)
+    q = inputs.paged_view(p, page_size=64, seed=6)
+    o, l, i = _decode_run(dsa, q, inputs.to_torch(q))
+    _, ref_idx, ref_o, ref_l = O.dsa_forward(q)
+    assert np.array_equal(i, ref_idx)
+    C.assert_attn_close(o, ref_o, l, ref_l)
