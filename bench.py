@@ -163,6 +163,25 @@ def ingest_pmc(workload: str, fetch_csv: str, write_csv: str):
     print(json.dumps(rec, indent=1))
 
 
+def copy_gbps(nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """Device-to-device copy of nbytes on this GPU: (read + written) bytes per second."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    secs = start.elapsed_time(end) * 1e-3 / reps
+    del src, dst
+    return 2 * nbytes / secs / 1e9
+
+
 def cpu_baseline(p, budget_s: float):
     from oracle import dsa_oracle as O
     try:
@@ -387,6 +406,17 @@ def main():
     tok_s = p.R / (ms_step * 1e-3)
     log(f"bench: {ms_step * 1e3:.2f} us/step, {tok_s:,.0f} tokens/s (wall {wall:.3f} s)")
 
+    # ---- per-step percentiles: an event after every step of a second timed run -------------
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        calls[i % n_sets]()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
+    pct = {"p10": per[len(per) // 10], "median": per[len(per) // 2], "p90": per[(9 * len(per)) // 10]}
+    log(f"bench: per-step us p10 {pct['p10']:.2f}, median {pct['median']:.2f}, p90 {pct['p90']:.2f}")
+
     # ---- the same steps captured in a HIP graph (launch gaps vs kernel time) -------------
     graph_ms, graph_same = None, None
     try:
@@ -505,9 +535,12 @@ def main():
 
         traffic = pmc_traffic(os.path.join(ROOT, "sparse_attention_05_amd", "csrc", "index_scores.hip"),
                               args.workload)
+        copy = copy_gbps()
+        log(f"bench: device copy {copy:,.0f} GB/s (read + write)")
         roofline = {"kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                    "bytes_per_launch": ib, "us_per_launch": idx_us, "tflops": idx_tflops}
+                    "bytes_per_launch": ib, "us_per_launch": idx_us, "tflops": idx_tflops,
+                    "copy_gbps_measured": copy, "frac_of_copy": achieved / copy}
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
@@ -522,6 +555,7 @@ def main():
                    "mla_heads": p.H, "latent_dim": 576, "latent": p.kv_dtype, "tokens_per_seq": m,
                    "page_size": p.page_size or None,
                    "input_sets": n_sets},
+        "step_us_percentiles": pct,
         "step_hbm_gbps": sb / (ms_step * 1e-3) / 1e9,
         "attention": {"us_per_launch": attn_us, "bytes_per_launch": ab,
                       "gbps": ab / (attn_us * 1e-6) / 1e9},
