@@ -771,3 +771,48 @@ def test_paged_multi_token_decode_matches_oracle(dsa):
     _, ref_idx, ref_o, ref_l = O.dsa_forward(q)
     assert np.array_equal(i, ref_idx)
     C.assert_attn_close(o, ref_o, l, ref_l)
+
+
+# ------------------------------------------------------------------------------
+# edge cases of the next rows
+# ------------------------------------------------------------------------------
+
+def test_edges_fp8_latent_128_heads(dsa):
+    p = _fp8_attn_problem([5000, 3000], 61, 128, 2048, std=3.0)
+    rng = np.random.default_rng(61)
+    idx = np.stack([rng.choice(int(p.q_pos[r]) + 1, 2048, replace=False) for r in range(p.R)]).astype(np.int32)
+    out, lse = _gpu_attn(dsa, p, idx)
+    ref, lse_ref = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref, lse, lse_ref)
+
+
+@pytest.mark.parametrize("m,k", [(5, 32), (2, 2048)])
+def test_edges_multi_token(dsa, m, k):
+    """Five tokens (the eight-wave shared ring), k below one chunk; two tokens."""
+    p = inputs.decode_config([9000, 600, 5], seed=62 + m, k=k, tie_levels=8, tokens_per_seq=m)
+    d = inputs.to_torch(p)
+    out, lse, idx, scores = _fused_multi(dsa, p, d)
+    ref_scores, ref_idx, ref_o, ref_l = O.dsa_forward(p)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        if n > 0:
+            assert np.array_equal(scores[r, :n], ref_scores[r]), f"row {r}"
+    assert np.array_equal(idx, ref_idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l)
+
+
+def test_edges_paged_large_pages(dsa):
+    p = inputs.decode_config([9000, 5000, 2100], seed=63, k=2048)
+    q = inputs.paged_view(p, page_size=1024, seed=7, spare_pages=1)
+    o1, l1, i1 = _decode_run(dsa, p, inputs.to_torch(p))
+    o2, l2, i2 = _decode_run(dsa, q, inputs.to_torch(q))
+    assert np.array_equal(i1, i2) and np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_edges_context_parallel_one_shard(dsa):
+    p = inputs.decode_config([9000, 3000], seed=64, k=2048)
+    d = inputs.to_torch(p)
+    ps, pi, idx, o_parts, l_parts, out, lse = _cp_step(dsa, p, d, 1)
+    full = dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, int(p.seq_len.max()))
+    assert np.array_equal(idx, dsa.dsa_topk(full, d.q_pos, int(p.seq_len.max()), p.k).cpu().numpy())
+    assert np.array_equal(out, o_parts[0]) and np.array_equal(lse, l_parts[0])   # one part: itself
