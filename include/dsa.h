@@ -14,7 +14,10 @@
  *   (q_seq == NULL means query r belongs to sequence r) at 0-based position
  *   q_pos[r]; its candidate keys are positions 0 .. q_pos[r] of that sequence
  *   (the query's own key included). Decode is R == B, q_seq == NULL,
- *   q_pos[b] = len_b - 1; causal prefill is B == 1, q_pos[r] = r.
+ *   q_pos[b] = len_b - 1 (or q_per_seq new tokens per sequence, R = B *
+ *   q_per_seq, in dsa_decode_fused); causal prefill is B == 1, q_pos[r] = r.
+ *   The *_paged entry points take a block table over a pool of fixed-size
+ *   pages instead of row_off.
  * Device metadata (row_off, q_seq, q_pos, seq_len, idx) is trusted: the
  *   preconditions q_pos[r] < max_n, 0 <= q_seq[r] < B and
  *   row_off[q_seq[r]] + q_pos[r] < cache_rows are not checked on the host.
@@ -32,8 +35,9 @@
  *
  * Citations name the pages that describe the method: "GLM-5: from Vibe
  * Coding to Agentic Engineering" (paper notes, sections 2.1, 2.1.1, 2.1.2,
- * 3.2), "Zhipu AI / GLM: From Blank Infilling to Compaction-Aware Agentic
- * RL" (sections 9.1, 9.3, 11.1) and "GLM-5 Notes" (DSA, Replay).
+ * 2.4.2, 3.2), "Zhipu AI / GLM: From Blank Infilling to Compaction-Aware
+ * Agentic RL" (sections 9.1, 9.3, 11.1, 11.4) and "GLM-5 Notes" (DSA,
+ * Replay).
  */
 #ifndef DSA_H
 #define DSA_H

@@ -6,6 +6,7 @@
 
 #include "dsa.h"
 #include "dsa_common.hpp"
+#include "dsa_internal.hpp"
 
 namespace dsa {
 namespace {
@@ -78,5 +79,5 @@ extern "C" dsa_status dsa_check_indices(const int32_t* idx, const int32_t* q_pos
   dsa::check_indices_kernel<<<dim3(unsigned(R)), dsa::kCheckThreads, 0, static_cast<hipStream_t>(stream)>>>(
       idx, q_pos, k, n_bad);
   const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+  return e == hipSuccess ? DSA_OK : static_cast<dsa_status>(dsa::record_hip_error(e));
 }

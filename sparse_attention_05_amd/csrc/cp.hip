@@ -162,7 +162,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* o_parts, c
 
 bool aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-dsa_status launched() { return hipGetLastError() == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+dsa_status launched() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DSA_OK : static_cast<dsa_status>(record_hip_error(e));
+}
 
 }  // namespace
 }  // namespace dsa

@@ -209,6 +209,10 @@ dsa_status sparse_mla_impl(const void* q_abs, int32_t dtype, const void* latent,
 
 }  // namespace
 
+int record_hip_error(hipError_t e) {
+  return hip_fail(e);
+}
+
 int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;

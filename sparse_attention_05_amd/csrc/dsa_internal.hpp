@@ -94,5 +94,7 @@ hipError_t launch_attn_combine(const AttnArgs& a, const AttnPlan& plan, hipStrea
 hipError_t launch_topk_attn(const TopkArgs& ta, const AttnArgs& aa, const AttnPlan& plan, hipStream_t stream);
 
 int device_cu_count();
+// Records a failed launch's text for dsa_last_error(); returns DSA_ERR_HIP's value.
+int record_hip_error(hipError_t e);
 
 }  // namespace dsa
