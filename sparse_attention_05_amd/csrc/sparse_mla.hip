@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
 // Merge key splits: O = sum_s e_s O_s / sum_s e_s l_s, e_s = 2^(m_s - max m),
 // splits with an empty sum skipped. P adjacent lanes share one output float4,
 // each lane loading and summing its SPL consecutive splits (all loads issued
-// together), then the P partial sums are added in lane order. Every order is
+// together), then the P partial sums are added in lane order (P * SPL >= splits). Every order is
 // fixed, so the result is bitwise reproducible.
 template <int P, int SPL>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int splits) {
@@ -501,15 +501,18 @@ hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_
 
 hipError_t launch_attn_combine(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   if (a.R == 0 || plan.splits == 1) return hipSuccess;
-  // 4 splits per lane: up to 16 lanes per output float4 (splits <= 64)
-  const int P = plan.splits <= 4 ? 1 : plan.splits <= 8 ? 2 : plan.splits <= 16 ? 4 : plan.splits <= 32 ? 8 : 16;
+  // P lanes per output float4, SPL splits per lane (splits <= 64), each
+  // lane's loads all in flight together; 9-16 splits run as 2 x 8, which
+  // measured faster than 4 x 4 and 1 x 16
+  const int s = plan.splits;
+  const int P = s <= 4 ? 1 : s <= 16 ? 2 : s <= 32 ? 8 : 16;
   const int64_t threads = int64_t(a.R) * a.H * (kValueDim / 4) * P;
   const dim3 cgrid(unsigned((threads + 255) / 256));
-  if (P == 1) combine_kernel<1, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
-  else if (P == 2) combine_kernel<2, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
-  else if (P == 4) combine_kernel<4, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
-  else if (P == 8) combine_kernel<8, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
-  else combine_kernel<16, 4><<<cgrid, 256, 0, stream>>>(a, plan.splits);
+  if (s <= 4) combine_kernel<1, 4><<<cgrid, 256, 0, stream>>>(a, s);
+  else if (s <= 8) combine_kernel<2, 4><<<cgrid, 256, 0, stream>>>(a, s);
+  else if (s <= 16) combine_kernel<2, 8><<<cgrid, 256, 0, stream>>>(a, s);
+  else if (s <= 32) combine_kernel<8, 4><<<cgrid, 256, 0, stream>>>(a, s);
+  else combine_kernel<16, 4><<<cgrid, 256, 0, stream>>>(a, s);
   return hipGetLastError();
 }
 
