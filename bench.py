@@ -201,8 +201,24 @@ def cpu_baseline(p, budget_s: float):
     dt = time.perf_counter() - t0
     what = (f"decode rows of the same workload (full indexer over {int(p.seq_len[0])} keys" if p.is_decode()
             else f"query rows at spread positions of the same {int(p.R)}-token prefill (causal indexer")
+    # the same oracle on one thread, over a shorter sample
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1, t1 = 0, time.perf_counter()
+            while True:
+                r = n1 % p.R if p.is_decode() else (n1 * 2654435761) % p.R
+                O.dsa_forward(p, rows=[r])
+                n1 += 1
+                if time.perf_counter() - t1 >= budget_s / 4:
+                    break
+            single = n1 / (time.perf_counter() - t1)
+    except Exception:
+        pass
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} {what}, stable-sort top-k, fp64 attention), {dt:.1f} s"}
+            "sample": f"{rows} {what}, stable-sort top-k, fp64 attention), {dt:.1f} s",
+            "single_thread_value": single}
 
 
 def context_parallel(dsa, p, d, call, steps, P=4):
