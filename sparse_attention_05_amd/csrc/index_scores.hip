@@ -614,13 +614,16 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 // and head weights go to LDS once per workgroup (through ring stages 2-3,
 // while key groups 0-1 load) instead of every wave loading its row.
 // Scores (and the score sample, when asked) are stored up to each row's end.
-template <int MT, int DI, int QW, bool SLICED>
+template <int QK, int MT, int DI, int QW, bool SLICED>
 __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(IndexArgs a, int kps) {
-  using C = KeyCfg<1, DI, true>;
+  using C = KeyCfg<QK, DI, true>;
+  using F = typename Frag<QK>::type;
+  static_assert(QK == 1 || (QK == 2 && SLICED), "fp8 keys: the multi-token decode form only");
   constexpr int RW = kPfWaves;
   constexpr int NKS = DI / 32;
   constexpr int GB = kPfKeys * C::ROW;      // bytes per group
-  constexpr int LPW = GB / 1024 / RW;       // direct loads per wave per group
+  constexpr int KL = GB / 1024 / RW;        // key loads per wave per group
+  constexpr int LPW = KL + (QK == 2 ? 1 : 0);  // + fp8: the row scales of 16 keys
   constexpr int TPW = kPfTiles * QW / RW;   // tiles per wave per group
   constexpr bool QLDS = SLICED && QW == 4;  // query rows staged in LDS
   constexpr int QCPR = DI / 8;              // 16-byte chunks per query row
@@ -628,9 +631,14 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   static_assert((GB / 1024) % RW == 0, "group loads split evenly over the waves");
   static_assert(kPfStages >= 3, "a group lands while the one before it is multiplied");
   static_assert(TPW % 4 == 0, "a wave's tiles of a group form whole 64-key score stores");
-  static_assert(!QLDS || QW * QB <= 2 * GB, "the staged queries fit two ring stages");
+  static_assert(!QLDS || QK != 1 || QW * QB <= 2 * GB, "the staged bf16 queries fit two ring stages");
   __shared__ __attribute__((aligned(1024))) char ring[kPfStages][GB];
   __shared__ __attribute__((aligned(16))) float s_w[QLDS ? QW : 1][64];
+  // fp8: row scales (bf16 bits, zero-extended words); wave w's dma2 fills
+  // words 64w .. 64w+63, the first 16 for keys 16w .. 16w+15 of the group
+  __shared__ __attribute__((aligned(16))) uint32_t s_ksc[QK == 2 ? kPfStages : 1][QK == 2 ? RW * 64 : 1];
+  // fp8 stages are too small to stage the queries in: a buffer of their own
+  __shared__ __attribute__((aligned(1024))) char s_qst[QLDS && QK == 2 ? QW * QB : 16];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -682,8 +690,8 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   const int64_t span = k_end - k_beg;
   uint32_t src_off[LPW];
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int m = wave * LPW + j;
+  for (int j = 0; j < KL; ++j) {
+    const int m = wave * KL + j;
     const int pch = 64 * m + lane;
     const int row = pch / C::CPR;
     const int lc = (pch % C::CPR) ^ (row & C::SWZ);
@@ -695,7 +703,15 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(keys + s0 * C::ROW), 0, int((span - s0) * C::ROW), 0x00020000);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) dma16_buf(src, src_off[j], to + 1024 * (wave * LPW + j));
+    for (int j = 0; j < KL; ++j) dma16_buf(src, src_off[j], to + 1024 * (wave * KL + j));
+    if constexpr (QK == 2) {
+      // scales of keys s0 + 16*wave .. +15 (zero past the range)
+      const int64_t first = s0 + 16 * wave;
+      const int64_t cnt = span - first < 16 ? (span - first > 0 ? span - first : 0) : 16;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(a.k_scale + base + k_beg + (cnt > 0 ? first : 0)), 0, int(2 * cnt), 0x00020000);
+      dma2_buf(rs, uint32_t(2 * lane), lds_addr(&s_ksc[g % kPfStages][64 * wave]));
+    }
   };
 
   bf16x8 qa[MT][NKS];
@@ -706,7 +722,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     // and idle rows zeroed) and head weights into LDS, ahead of key groups
     // 0-1; once every wave's part has landed the fragments go to registers
     // and stages 2-3 take key groups 2-3
-    char* qst = ring[2];
+    char* qst = QK == 1 ? ring[2] : s_qst;
     const uint32_t qlds = lds_addr(qst);
     for (int m = wave; 64 * m < QW * 16 * MT * QCPR; m += RW) {
       const int pch = 64 * m + lane;
@@ -779,20 +795,35 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   // fragments of tile t (keys 16*t .. +16) of group g (a stage past the last
   // group holds stale keys: reading it is harmless, its products are never
   // stored)
-  auto tile_frags = [&](int g, int t, bf16x8 (&kt)[NKS]) {
+  auto tile_frags = [&](int g, int t, F (&kt)[NKS]) {
     const char* stage = ring[g % kPfStages];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kt[ks] = key_frag<1, DI, true>(stage, 16 * t + col, grp, ks);
+    for (int ks = 0; ks < NKS; ++ks) kt[ks] = key_frag<QK, DI, true>(stage, 16 * t + col, grp, ks);
+  };
+  // fp8: row scale of key j of group g's stage
+  auto key_scale = [&](int g, int j) -> float {
+    return bf16_bits_to_f32(s_ksc[g % kPfStages][64 * (j >> 4) + (j & 15)]);
   };
   // ReLU, head weight and the sum over the lane's 4 heads of each of the MT
-  // head tiles: this lane's part of the score of key 16*t + n
-  auto tile_epi = [&](const f32x4 (&c)[MT]) -> float {
+  // head tiles: this lane's part of the score of key 16*t + n (fp8 with a
+  // negative row scale sc: relu(sc * dot) per head; a non-negative scale is
+  // applied to the summed score)
+  auto tile_epi = [&](const f32x4 (&c)[MT], float sc) -> float {
     float pm[MT];
+    if (QK == 2 && sc < 0.f) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      pm[mt] = wr[mt][0] * relu_bits(c[mt][0]);
+      for (int mt = 0; mt < MT; ++mt) {
+        pm[mt] = wr[mt][0] * relu_bits(sc * c[mt][0]);
 #pragma unroll
-      for (int i = 1; i < 4; ++i) pm[mt] += wr[mt][i] * relu_bits(c[mt][i]);
+        for (int i = 1; i < 4; ++i) pm[mt] += wr[mt][i] * relu_bits(sc * c[mt][i]);
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        pm[mt] = wr[mt][0] * relu_bits(c[mt][0]);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) pm[mt] += wr[mt][i] * relu_bits(c[mt][i]);
+      }
     }
     float pp = pm[0];
 #pragma unroll
@@ -815,7 +846,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   // two fragment tiles and two accumulator tiles: tile t is multiplied from
   // kb[t&1] into acc[t&1] while tile t-1's epilogue runs from acc[(t-1)&1]
   // and tile t+1's fragments are read into kb[(t+1)&1]
-  bf16x8 kb[2][NKS];
+  F kb[2][NKS];
   f32x4 acc[2][MT];
   // group 0 has landed for every wave (behind it: the later groups' loads)
   wait_ops<LPW * (kPfStages - 1)>(LPW * (issued - 1));
@@ -845,7 +876,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
         for (int mt = 0; mt < MT; ++mt)
           acc[t & 1][mt] =
               mfma_k32(qa[mt][ks], kb[t & 1][ks], ks ? acc[t & 1][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
-      if (t > 0) part[t - 1] = tile_epi(acc[(t - 1) & 1]);
+      if (t > 0) part[t - 1] = tile_epi(acc[(t - 1) & 1], QK == 2 ? key_scale(g, 16 * (tb + t - 1) + col) : 1.f);
       if (t + 1 < TPW) tile_frags(g, tb + t + 1, kb[(t + 1) & 1]);
       else tile_frags(g + 1, tb, kb[(t + 1) & 1]);
       // each MFMA followed by VALU work of the previous tile's epilogue;
@@ -859,11 +890,15 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
       __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    part[TPW - 1] = tile_epi(acc[(TPW - 1) & 1]);
+    part[TPW - 1] = tile_epi(acc[(TPW - 1) & 1], QK == 2 ? key_scale(g, 16 * (tb + TPW - 1) + col) : 1.f);
 #pragma unroll
     for (int h = 0; h < TPW / 4; ++h) {
       const float p4[4] = {part[4 * h], part[4 * h + 1], part[4 * h + 2], part[4 * h + 3]};
-      const float v = rows_transpose_sum(p4);
+      float v = rows_transpose_sum(p4);
+      if constexpr (QK == 2) {
+        const float sc = key_scale(g, 16 * tb + 64 * h + lane);
+        if (!(sc < 0.f)) v *= sc;
+      }
       // non-temporal: the scores are read by the next kernel, not this one
       const int key = g * kPfKeys + 16 * tb + 64 * h + lane;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, key * 4, 0, 2);
@@ -877,13 +912,13 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
 template <int MT, int DI>
 hipError_t launch_prefill(const IndexArgs& a, hipStream_t stream) {
   const unsigned blocks = unsigned((a.R + kPfRows - 1) / kPfRows);
-  index_scores_prefill_kernel<MT, DI, kPfRows, false><<<dim3(blocks), kPfWaves * 64, 0, stream>>>(a, 0);
+  index_scores_prefill_kernel<1, MT, DI, kPfRows, false><<<dim3(blocks), kPfWaves * 64, 0, stream>>>(a, 0);
   return hipGetLastError();
 }
 
 // Decode form with 2..8 new tokens per sequence: a workgroup per (key slice,
 // sequence), the slices sized so that the grid covers the CUs about once.
-template <int MT, int DI>
+template <int QK, int MT, int DI>
 hipError_t launch_multi_token(const IndexArgs& a, hipStream_t stream) {
   const int cus = device_cu_count();
   const int per_seq = (cus + a.B - 1) / a.B;
@@ -891,9 +926,16 @@ hipError_t launch_multi_token(const IndexArgs& a, hipStream_t stream) {
   kps = (kps + kPfKeys - 1) / kPfKeys * kPfKeys;
   const unsigned slices = unsigned((a.max_n + kps - 1) / kps);
   const dim3 grid(slices, unsigned(a.B));
-  if (a.qps <= 4) index_scores_prefill_kernel<MT, DI, 4, true><<<grid, kPfWaves * 64, 0, stream>>>(a, int(kps));
-  else index_scores_prefill_kernel<MT, DI, 8, true><<<grid, kPfWaves * 64, 0, stream>>>(a, int(kps));
+  if (a.qps <= 4) index_scores_prefill_kernel<QK, MT, DI, 4, true><<<grid, kPfWaves * 64, 0, stream>>>(a, int(kps));
+  else index_scores_prefill_kernel<QK, MT, DI, 8, true><<<grid, kPfWaves * 64, 0, stream>>>(a, int(kps));
   return hipGetLastError();
+}
+
+template <int QK>
+hipError_t launch_multi_token_m(const IndexArgs& a, hipStream_t stream) {
+  if (a.H_I <= 16) return a.D_I == 64 ? launch_multi_token<QK, 1, 64>(a, stream) : launch_multi_token<QK, 1, 128>(a, stream);
+  if (a.H_I <= 32) return a.D_I == 64 ? launch_multi_token<QK, 2, 64>(a, stream) : launch_multi_token<QK, 2, 128>(a, stream);
+  return a.D_I == 64 ? launch_multi_token<QK, 4, 64>(a, stream) : launch_multi_token<QK, 4, 128>(a, stream);
 }
 
 template <int QK, int MT, int DI>
@@ -943,13 +985,10 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream) {
   const int mode = a.q_dtype == kF32 ? 0 : (a.k_dtype == kFP8 ? 2 : 1);
   // many bf16 queries of one sequence (causal prefill form): key tiles shared by 8 queries
   // (key and score rows are addressed with 32-bit byte offsets there)
-  // several new bf16 tokens per sequence (decode form): each key row read once for all of them
-  if (mode == 1 && !a.q_seq && !a.q_pos && !a.table && a.qps >= 2 && a.qps <= kPfWaves &&
-      a.max_n <= (int64_t(1) << 22)) {
-    if (a.H_I <= 16) return a.D_I == 64 ? launch_multi_token<1, 64>(a, stream) : launch_multi_token<1, 128>(a, stream);
-    if (a.H_I <= 32) return a.D_I == 64 ? launch_multi_token<2, 64>(a, stream) : launch_multi_token<2, 128>(a, stream);
-    return a.D_I == 64 ? launch_multi_token<4, 64>(a, stream) : launch_multi_token<4, 128>(a, stream);
-  }
+  // several new tokens per sequence (decode form, bf16 or fp8 keys): each key row read once for all of them
+  if ((mode == 1 || mode == 2) && !a.q_seq && !a.q_pos && !a.table && a.qps >= 2 && a.qps <= kPfWaves &&
+      a.max_n <= (int64_t(1) << 22))
+    return mode == 1 ? launch_multi_token_m<1>(a, stream) : launch_multi_token_m<2>(a, stream);
   if (mode == 1 && a.B == 1 && a.q_pos && !a.table && a.R >= 4 * kPfRows && a.max_n <= (int64_t(1) << 22) &&
       !a.sample) {
     if (a.H_I <= 16) return a.D_I == 64 ? launch_prefill<1, 64>(a, stream) : launch_prefill<1, 128>(a, stream);

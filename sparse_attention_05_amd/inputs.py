@@ -427,6 +427,9 @@ def workload(name: str, seed: int = 0) -> DSAProblem:
                              boost_frac=0.02, latent_dtype="fp8_e4m3", name=name)
     if name == "decode-32k-mtp4":
         return decode_config([32768] * 4, seed=seed, tokens_per_seq=4, name=name)
+    if name == "decode-128k-fp8-mtp4":
+        return decode_config([131072] * 7 + [200000], seed=seed, key_dtype="fp8_e4m3", boost_frac=0.02,
+                             tokens_per_seq=4, name=name)
     if name == "decode-32k-paged":
         return paged_view(decode_config([32768] * 4, seed=seed, name="decode-32k"), page_size=64, seed=seed)
     if name == "ties-64k":

@@ -111,6 +111,12 @@ def test_decode_32k_multi_token_fullsize(dsa):
     assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
 
 
+def test_decode_128k_fp8_multi_token_fullsize(dsa):
+    """Batch 8 (7 x 131,072 + 200,000) with fp8 keys and 4 new tokens per
+    sequence (32 query rows): the shared key stream for fp8 keys at full size."""
+    _check_decode(dsa, inputs.workload("decode-128k-fp8-mtp4"))
+
+
 def test_decode_32k_paged_fullsize(dsa):
     """decode-32k in a pool of shuffled 64-row pages: the contiguous step's bits."""
     p = inputs.workload("decode-32k-paged")

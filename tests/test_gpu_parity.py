@@ -816,3 +816,24 @@ def test_edges_context_parallel_one_shard(dsa):
     full = dsa.dsa_index_scores(d.q_idx, d.head_w, d.k_idx, d.row_off, d.q_pos, int(p.seq_len.max()))
     assert np.array_equal(idx, dsa.dsa_topk(full, d.q_pos, int(p.seq_len.max()), p.k).cpu().numpy())
     assert np.array_equal(out, o_parts[0]) and np.array_equal(lse, l_parts[0])   # one part: itself
+
+
+@pytest.mark.parametrize("m", [4, 6])
+def test_multi_token_fp8_keys_with_negative_scales(dsa, m):
+    """fp8 keys in the shared-key-stream indexer, a tenth of the row scales
+    negated (relu(scale * dot) per head there): scores within the bound of the
+    oracle's, indices the stable order of the step's own scores."""
+    p = inputs.decode_config([9000, 5000, 300], seed=70 + m, k=2048, key_dtype="fp8_e4m3", boost_frac=0.02,
+                             tokens_per_seq=m)
+    rng = np.random.default_rng(m)
+    neg = rng.random(p.k_scale.shape[0]) < 0.1
+    p.k_scale = np.where(neg, p.k_scale | np.uint16(0x8000), p.k_scale).astype(np.uint16)
+    d = inputs.to_torch(p)
+    out, lse, idx, scores = _fused_multi(dsa, p, d)
+    C.assert_index_invariants(idx, p.q_pos, p.k)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        assert np.array_equal(idx[r], O.topk_row(scores[r, :n], p.k)), f"row {r}"
+        C.assert_scores_close(p, r, scores[r])
+    ref_o, ref_l = O.sparse_mla(p, idx)
+    C.assert_attn_close(out, ref_o, lse, ref_l)
