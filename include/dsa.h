@@ -229,6 +229,32 @@ dsa_status dsa_decode_fused(const void* q_idx, const float* head_w, const void* 
                             void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_decode_fused_noalloc -- dsa_decode_fused for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, kernels and bits,
+ * without workspace / ws_bytes. The workspace is a scratch array of the
+ * library, dsa_decode_noalloc_limit() bytes (64 MiB) per device, held from
+ * the first call on a device until the process ends; the call itself never
+ * allocates or frees. A step whose workspace (dsa_workspace_size(
+ * DSA_ENTRY_DECODE, ...)) exceeds the limit returns DSA_ERR_WORKSPACE
+ * (dsa_last_error() names both sizes) before anything is enqueued. Nothing in
+ * the scratch has to start at zero: every launch writes what it reads later.
+ * All calls on one device share its scratch, so calls that overlap on one
+ * GPU (concurrent streams, or several threads) race; serialise them.
+ */
+dsa_status dsa_decode_fused_noalloc(const void* q_idx, const float* head_w, const void* k_idx,
+                                    int32_t k_dtype, const uint16_t* k_scale, const void* q_abs,
+                                    const void* latent, int32_t act_dtype, int32_t latent_dtype,
+                                    const float* latent_scale, int64_t cache_rows,
+                                    const int64_t* row_off, const int32_t* seq_len, int32_t B,
+                                    int32_t q_per_seq, int32_t max_len, int32_t H_I, int32_t D_I,
+                                    int32_t H, int32_t k, float scale, float* out, float* lse,
+                                    int32_t* idx_out, void* stream);
+
+/* Bytes of scratch dsa_decode_fused_noalloc holds per device. */
+size_t dsa_decode_noalloc_limit(void);
+
+/*
  * Paged caches (the serving-engine layout: a pool of fixed-size pages and a
  * block table per sequence). Same computation and outputs as
  * dsa_sparse_mla_attn / dsa_decode_fused, with row_off replaced by:
@@ -340,7 +366,8 @@ dsa_status dsa_check_indices(const int32_t* idx, const int32_t* q_pos, int32_t R
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int32_t status);
 
-/* Text of the last DSA_ERR_HIP on the calling thread (static per thread). */
+/* Text of the last DSA_ERR_HIP on the calling thread, or of the last
+ * DSA_ERR_WORKSPACE of dsa_decode_fused_noalloc (static per thread). */
 const char* dsa_last_error(void);
 
 #ifdef __cplusplus

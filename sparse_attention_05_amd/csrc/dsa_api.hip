@@ -3,6 +3,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dsa.h"
 #include "dsa_common.hpp"
 #include "dsa_internal.hpp"
@@ -207,6 +209,35 @@ dsa_status sparse_mla_impl(const void* q_abs, int32_t dtype, const void* latent,
   return e == hipSuccess ? DSA_OK : hip_fail(e);
 }
 
+// ---- scratch of the no-allocation decode entry ---------------------------------
+// One file-scope device array per GPU, held until the process ends. In host
+// code `scratch` names a host-side stand-in, not device memory: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+dsa_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return DSA_ERR_ALIGN;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 
 int record_hip_error(hipError_t e) {
@@ -340,6 +371,36 @@ dsa_status dsa_decode_fused_paged(const void* q_idx, const float* head_w, const 
                            stream);
 }
 
+dsa_status dsa_decode_fused_noalloc(const void* q_idx, const float* head_w, const void* k_idx, int32_t k_dtype,
+                                    const uint16_t* k_scale, const void* q_abs, const void* latent,
+                                    int32_t act_dtype, int32_t latent_dtype, const float* latent_scale,
+                                    int64_t cache_rows, const int64_t* row_off, const int32_t* seq_len, int32_t B,
+                                    int32_t q_per_seq, int32_t max_len, int32_t H_I, int32_t D_I, int32_t H,
+                                    int32_t k, float scale, float* out, float* lse, int32_t* idx_out,
+                                    void* stream) {
+  // sizes the workspace formula cannot take are rejected by the checks in
+  // decode_fused_impl; the formula itself needs R >= 1, max_len >= 1, k, H >= 1
+  if (q_per_seq < 1 || q_per_seq > DSA_MAX_TOKENS_PER_SEQ) return DSA_ERR_UNSUPPORTED;
+  if (B < 1 || int64_t(B) * q_per_seq > (int64_t(1) << 24) || max_len < 1) return DSA_ERR_SHAPE;
+  if (max_len > kMaxTopkRow || k < 1 || k > DSA_MAX_TOPK || H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
+  const size_t need = decode_ws_bytes(B * q_per_seq, max_len, k, H);
+  if (need > kScratchBytes) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "dsa_decode_fused_noalloc: this step needs %zu bytes of scratch; the library holds %zu per device",
+             need, kScratchBytes);
+    return DSA_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  const dsa_status st = scratch_ptr(&ws);
+  if (st != DSA_OK) return st;
+  return decode_fused_impl(q_idx, head_w, k_idx, k_dtype, k_scale, q_abs, latent, act_dtype, latent_dtype,
+                           latent_scale, cache_rows, CacheMap{row_off, nullptr, 0, 0}, seq_len, B, q_per_seq,
+                           max_len, H_I, D_I, H, k, scale, out, lse, idx_out, ws, kScratchBytes, stream);
+}
+
+size_t dsa_decode_noalloc_limit(void) {
+  return kScratchBytes;
+}
 
 size_t dsa_workspace_size(int32_t entry, int32_t rows, int32_t max_len, int32_t k, int32_t H) {
   if (rows < 0 || k < 1 || H < 1) return 0;

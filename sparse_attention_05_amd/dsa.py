@@ -35,6 +35,9 @@ SIGNATURES = {
                                    _P, _P, _P, _SZ, _P]),
     "dsa_decode_fused": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _I32, _I32, _I32,
                                 _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P]),
+    "dsa_decode_fused_noalloc": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _P, _I32, _I32,
+                                        _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _P]),
+    "dsa_decode_noalloc_limit": (_SZ, []),
     "dsa_sparse_mla_attn_paged": (_I32, [_P, _I32, _P, _I32, _P, _I64, _P, _I32, _I32, _I32, _P, _P, _I32, _I32,
                                          _I32, _F32, _P, _P, _P, _SZ, _P]),
     "dsa_decode_fused_paged": (_I32, [_P, _P, _P, _I32, _P, _P, _P, _I32, _I32, _P, _I64, _P, _I32, _I32, _P,
@@ -313,6 +316,37 @@ class DecodeCall:
         st = self._fn(*self._args, _stream(stream))
         _check(st, "dsa_decode_fused")
         return self.out, self.lse, self.idx
+
+
+def dsa_decode_noalloc_limit() -> int:
+    return int(lib.dsa_decode_noalloc_limit())
+
+
+def dsa_decode_fused_noalloc(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,
+                             scale: float, *, k_scale=None, latent_scale=None, q_per_seq: int = 1,
+                             out=None, lse=None, idx_out=None, stream=None):
+    """dsa_decode_fused with the library's per-device scratch as workspace
+    (no device allocation by the library). out/lse/idx_out are allocated here
+    when not passed; pass them to keep the call allocation-free."""
+    R, H_I, D_I = q_idx.shape
+    B = seq_len.numel()
+    H = q_abs.shape[1]
+    dev = q_idx.device
+    if out is None:
+        out = torch.empty((R, H, DSA_VALUE_DIM), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    if idx_out is None:
+        idx_out = torch.empty((R, k), dtype=torch.int32, device=dev)
+    st = lib.dsa_decode_fused_noalloc(
+        _ptr(q_idx), _ptr(head_w), _ptr(k_idx), _dtype_code(k_idx), _ptr(k_scale), _ptr(q_abs), _ptr(latent),
+        _dtype_code(q_abs), _dtype_code(latent), _ptr(latent_scale), k_idx.shape[0], _ptr(row_off),
+        _ptr(seq_len), B, q_per_seq, max_len, H_I, D_I, H, k, float(scale), _ptr(out), _ptr(lse), _ptr(idx_out),
+        _stream(stream))
+    if st == DSA_ERR_WORKSPACE:
+        raise DSAError(st, "dsa_decode_fused_noalloc: " + (lib.dsa_last_error() or b"").decode())
+    _check(st, "dsa_decode_fused_noalloc")
+    return out, lse, idx_out
 
 
 def dsa_decode_fused(q_idx, head_w, k_idx, q_abs, latent, row_off, seq_len, max_len: int, k: int,

@@ -155,6 +155,31 @@ def test_decode_rejects_small_workspace(dsa):
         assert st == dsa.DSA_ERR_UNSUPPORTED
 
 
+def test_decode_noalloc_rejects_before_any_device_call(dsa):
+    """The no-allocation step refuses bad shapes and steps larger than its
+    per-device scratch on the host (no device call is made for these)."""
+    lib = dsa.lib
+    limit = dsa.dsa_decode_noalloc_limit()
+    assert limit == 64 << 20
+    # 16 rows of 2^20 keys need more workspace than the scratch holds
+    big = dsa.dsa_workspace_size(dsa.DSA_ENTRY_DECODE, 16, 1 << 20, 2048, 64)
+    assert big > limit
+    st = lib.dsa_decode_fused_noalloc(A, A, A, 1, None, A, A, 1, 1, None, 16 << 20, A, A, 16, 1, 1 << 20, 64, 128,
+                                      64, 2048, 0.07, A, None, None, None)
+    assert st == dsa.DSA_ERR_WORKSPACE
+    assert b"scratch" in lib.dsa_last_error()
+    for bad in (0, 9):
+        st = lib.dsa_decode_fused_noalloc(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, A, A, 4, bad, 32768, 64,
+                                          128, 64, 2048, 0.07, A, None, None, None)
+        assert st == dsa.DSA_ERR_UNSUPPORTED
+    st = lib.dsa_decode_fused_noalloc(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, A, A, 0, 1, 32768, 64, 128,
+                                      64, 2048, 0.07, A, None, None, None)
+    assert st == dsa.DSA_ERR_SHAPE
+    st = lib.dsa_decode_fused_noalloc(A, A, A, 1, None, A, A, 1, 1, None, 4 * 32768, A, A, 4, 1, 32768, 64, 128,
+                                      64, 4096, 0.07, A, None, None, None)
+    assert st == dsa.DSA_ERR_UNSUPPORTED
+
+
 def test_check_indices_rejects(dsa):
     lib = dsa.lib
     assert lib.dsa_check_indices(A, A, 4, 2048, None, None) == dsa.DSA_ERR_NULL
