@@ -181,7 +181,8 @@ dsa_status dsa_topk(const float* scores, int64_t ld_scores, const int32_t* q_pos
  *            "Zhipu AI / GLM", section 11.4; one float32 scale per row is
  *            this library's reading). latent_scale [cache_rows] fp32, 4-B
  *            aligned, required for fp8 and ignored otherwise.
- *   idx      [R, k] int32;  k in 1 .. DSA_MAX_TOPK;  H in 1 .. 128
+ *   idx      [R, k] int32;  k in 1 .. DSA_MAX_TOPK;  H in 1 .. 128;
+ *            cache_rows < 2^31 (larger caches: DSA_ERR_UNSUPPORTED)
  *   out      [R, H, 512] fp32;  lse [R, H] fp32 or NULL
  *   workspace: dsa_workspace_size(DSA_ENTRY_SPARSE_MLA, R, 0, k, H) bytes
  * A row with no valid index gets out = 0 and lse = -inf.

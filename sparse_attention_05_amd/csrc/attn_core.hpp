@@ -152,47 +152,6 @@ __device__ __forceinline__ int blk_off(int row, int p) {
   return kBlock * (row >> 4) + 1024 * (p >> 2) + 64 * (row & 15) + 16 * (p & 3);
 }
 
-struct BGather {
-  const char* src;  // this lane's row + 16*(lane%4) (row 0 when missing: not loaded)
-  uint32_t lds;     // LDS address of the wave's block
-  bool live;        // this lane's row is present
-  uint32_t ok;      // 16-bit mask of present rows
-};
-
-__device__ __forceinline__ BGather bgather_plan(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
-                                                int wave, int lane) {
-  int64_t row;
-  BGather g;
-  g.live = attn_row(a, base, s_idx[kChunkKeys * c + 16 * wave + (lane >> 2)], row);
-  const unsigned long long okm = __ballot(g.live && (lane & 3) == 0);  // bit 4i: row i
-  uint32_t ok = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) ok |= uint32_t((okm >> (4 * i)) & 1ull) << i;
-  g.ok = ok;
-  g.src = static_cast<const char*>(a.latent) + row * 1152 + 16 * (lane & 3);
-  char* blk = buf + kBlock * wave;
-  g.lds = lds_addr(blk);
-  if (!g.live) {
-#pragma unroll
-    for (int m = 0; m < 18; ++m) *reinterpret_cast<uint4*>(blk + 1024 * m + 16 * lane) = uint4{0u, 0u, 0u, 0u};
-  }
-  return g;
-}
-
-__device__ __forceinline__ void bgather_load(const BGather& g, int m) {
-  const char* p = g.src;
-  asm volatile("" : "+v"(p));  // the address is formed here, not hoisted into 18 live pairs
-  if (g.live) dma16(p + 64 * m, g.lds + 1024 * m);
-}
-
-__device__ __forceinline__ uint32_t bgather_all(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
-                                                int wave, int lane) {
-  const BGather g = bgather_plan(a, base, s_idx, c, buf, wave, lane);
-#pragma unroll
-  for (int m = 0; m < 18; ++m) bgather_load(g, m);
-  return g.ok;
-}
-
 // The whole gather of chunk c at once; returns the mask of present rows.
 template <bool F32>
 __device__ __forceinline__ uint32_t issue_chunk(const AttnArgs& a, int64_t base, const int* s_idx, int c,
@@ -206,12 +165,9 @@ __device__ __forceinline__ uint32_t issue_chunk(const AttnArgs& a, int64_t base,
 // bf16 logits of this wave's 16 keys of the chunk: S^T = C[16 x 576] . Q^T.
 // Lane (col, grp) reads piece 4ks + grp of row col of the wave's block (at
 // blk + 64*col + 16*grp + 1024*ks: each K-step reads 1 KiB contiguously),
-// four K-steps ahead of its MFMA (a wave has its SIMD to itself: nothing
-// else hides the LDS latency). LOADS: direct load ks of the next chunk's
-// gather rides on K-step ks, so those loads go out while this chunk is
-// computed.
-template <bool LOADS>
-__device__ __forceinline__ f32x4 qc_bf16(const char* rp, const bf16x8 (&qf)[18], const BGather& gn) {
+// four K-steps ahead of its MFMA (a compute wave has no other wave of its
+// role on its SIMD to hide the LDS latency).
+__device__ __forceinline__ f32x4 qc_bf16(const char* rp, const bf16x8 (&qf)[18]) {
   f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   constexpr int D = 4;
   bf16x8 fr[D];
@@ -223,7 +179,6 @@ __device__ __forceinline__ f32x4 qc_bf16(const char* rp, const bf16x8 (&qf)[18],
     const bf16x8 af = fr[ks % D];
     if (ks + D < 18) fr[ks % D] = *reinterpret_cast<const bf16x8*>(rp + 1024 * (ks + D));
     part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
-    if constexpr (LOADS) bgather_load(gn, ks);
     if (ks + D < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
@@ -272,6 +227,7 @@ struct Smem {
   PType<F32> s_p[kGroupHeads * kPRow] __attribute__((aligned(16)));  // P^T as [head][key]
   float s_max[4][kGroupHeads];
   float s_l[4][kGroupHeads];
+  uint32_t s_ok[2][4];  // bf16 gather: present rows of each 16-row block of the chunk in each buffer
 };
 
 // Workgroup u -> (query r, key split, head group). Workgroup u runs on XCD
@@ -354,41 +310,25 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, int r, int split
   }
 }
 
-// The chunk loop and the epilogue over keys j_beg .. j_end-1 of query r, for
-// waves 0..3 of the workgroup; s_idx[j - j_beg] holds the raw index of key j
-// (-1: none), base the sequence's first cache row. Writes the normalised
-// output (splits == 1) or the split's unnormalised output, maximum and sum.
-template <bool F32>
-__device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int splits, int hg, int j_beg,
-                                       int j_end, int64_t base, const int* s_idx, QFrag<F32> (&qf)[18],
-                                       Smem<F32>& sm) {
-  using Cfg = AttnCfg<F32>;
-  using PT = PType<F32>;
+// fp32 rows and queries: the chunk loop and the epilogue over keys j_beg ..
+// j_end-1 of query r, for a 4-wave workgroup; s_idx[j - j_beg] holds the raw
+// index of key j (-1: none), base the sequence's first cache row. One LDS
+// buffer: each chunk's rows are gathered (direct loads into the row-major
+// layout with the row_swz permutation), then q.c, softmax and p.c as in
+// attend_bf16 on the fp32 matrix cores. Writes the normalised output
+// (splits == 1) or the split's unnormalised output, maximum and sum.
+__device__ __forceinline__ void attend_f32(const AttnArgs& a, int r, int split, int splits, int hg, int j_beg,
+                                           int j_end, int64_t base, const int* s_idx, const f32x8 (&qf)[18],
+                                           Smem<true>& sm) {
+  using Cfg = AttnCfg<true>;
   char* smem = sm.buf;
-  PT* s_p = sm.s_p;
-  float (*s_max)[kGroupHeads] = sm.s_max;
-  float (*s_l)[kGroupHeads] = sm.s_l;
+  float* s_p = sm.s_p;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int h = hg * kGroupHeads + col;
   const int nchunks = j_end > j_beg ? (j_end - j_beg + kChunkKeys - 1) / kChunkKeys : 0;
-
-  uint32_t ok[Cfg::NBUF];
-  if constexpr (F32) {
-    ok[0] = nchunks > 0 ? issue_chunk<F32>(a, base, s_idx, 0, smem, wave, lane) : 0u;
-  } else if (nchunks > 0) {
-    // chunk 0 and the staged query (in buffer 1) in one round trip, then the
-    // query fragments into registers; chunk 1's loads go out during chunk
-    // 0's q.c
-    ok[0] = bgather_all(a, base, s_idx, 0, smem, wave, lane);
-    stage_q(a, r, hg, smem + Cfg::BUF_BYTES, wave, lane);
-    vm_wait_all();
-    __syncthreads();
-    read_q(smem + Cfg::BUF_BYTES, h < a.H, col, grp, qf);
-    __syncthreads();  // every wave has its fragments: buffer 1 is free
-  }
 
   f32x4 acc[8];
 #pragma unroll
@@ -398,43 +338,26 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
   const float scale2 = a.scale * kLog2e;
 
   for (int c = 0; c < nchunks; ++c) {
-    const int bi = Cfg::NBUF == 2 ? (c & 1) : 0;
-    char* buf = smem + bi * Cfg::BUF_BYTES;
-    if (Cfg::NBUF == 1 && c > 0) {
-      __syncthreads();  // every wave is done with the previous chunk
-      ok[0] = issue_chunk<F32>(a, base, s_idx, c, buf, wave, lane);
-    }
-    if constexpr (!F32) {
-      if (c > 0) vm_wait_all();  // this wave's rows of chunk c (the only loads in flight) have landed
-    }
-    const uint32_t okc = ok[bi];
+    char* buf = smem;
+    if (c > 0) __syncthreads();  // every wave is done with the previous chunk
+    const uint32_t okc = issue_chunk<true>(a, base, s_idx, c, buf, wave, lane);
+    vm_wait_all();
 
     // ---- logits of this wave's 16 keys: S^T = C[16 x 576] . Q^T ----------------------
     f32x4 sacc;
     {
-      if constexpr (F32) {
-        const char* rp = buf + (16 * wave + col) * Cfg::ROW_BYTES;
-        const int sw = row_swz(col);
-        f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      const char* rp = buf + (16 * wave + col) * Cfg::ROW_BYTES;
+      const int sw = row_swz(col);
+      f32x4 part[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-          const int c0 = 8 * ks + 2 * grp;
-          const float4 x = *reinterpret_cast<const float4*>(rp + 16 * (c0 ^ sw));
-          const float4 y = *reinterpret_cast<const float4*>(rp + 16 * ((c0 + 1) ^ sw));
-          const f32x8 af{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
-          part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
-        }
-        sacc = part[0] + part[1];
-      } else {
-        const char* rp = buf + kBlock * wave + 64 * col + 16 * grp;
-        if (c == 0 && nchunks > 1) {  // buffer 1 is free since the query was read
-          const BGather gn = bgather_plan(a, base, s_idx, 1, smem + Cfg::BUF_BYTES, wave, lane);
-          ok[1] = gn.ok;
-          sacc = qc_bf16<true>(rp, qf, gn);
-        } else {
-          sacc = qc_bf16<false>(rp, qf, BGather{});
-        }
+      for (int ks = 0; ks < 18; ++ks) {
+        const int c0 = 8 * ks + 2 * grp;
+        const float4 x = *reinterpret_cast<const float4*>(rp + 16 * (c0 ^ sw));
+        const float4 y = *reinterpret_cast<const float4*>(rp + 16 * ((c0 + 1) ^ sw));
+        const f32x8 af{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
+        part[ks & 1] = mfma_k32(af, qf[ks], part[ks & 1]);
       }
+      sacc = part[0] + part[1];
     }
 
     // ---- chunk maximum per head over the 4 waves ----------------------------------------
@@ -447,28 +370,19 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
     }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    if (grp == 0) s_max[wave][col] = mx;
-    __syncthreads();  // maxima visible; every wave is done with chunk c-1 and has its rows of chunk c
-    const float cmax = fmaxf(fmaxf(s_max[0][col], s_max[1][col]), fmaxf(s_max[2][col], s_max[3][col]));
-    // chunks 2, 3, ...: buffer bi^1 is free once every wave is past the
-    // barrier above; the next chunk's loads go out during this chunk's p.c
-    const bool pc_loads = !F32 && c + 1 < nchunks && c >= 1;
-    BGather gn{};
-    if (pc_loads) {
-      gn = bgather_plan(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
-      ok[bi ^ 1] = gn.ok;
-    }
+    if (grp == 0) sm.s_max[wave][col] = mx;
+    __syncthreads();  // maxima visible; every wave has its rows of chunk c
+    const float cmax = fmaxf(fmaxf(sm.s_max[0][col], sm.s_max[1][col]), fmaxf(sm.s_max[2][col], sm.s_max[3][col]));
 
     const float m_new = fmaxf(m_run, cmax);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no key seen yet: p = alpha = 0
     const float alpha = exp2f(m_run - m_use);
     float psum = 0.f;
-    PT pv[4];
+    float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float e = exp2f(x[i] - m_use);
-      pv[i] = static_cast<PT>(e);
-      psum += static_cast<float>(pv[i]);
+      pv[i] = exp2f(x[i] - m_use);
+      psum += pv[i];
     }
     l_part = l_part * alpha + psum;
     m_run = m_new;
@@ -476,49 +390,266 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
 #pragma unroll
       for (int vt = 0; vt < 8; ++vt) acc[vt] *= alpha;
     }
-    PT* prow = s_p + col * kPRow + 16 * wave + 4 * grp;
-    if constexpr (F32) {
-      *reinterpret_cast<float4*>(prow) = float4{pv[0], pv[1], pv[2], pv[3]};
-    } else {
+    *reinterpret_cast<float4*>(s_p + col * kPRow + 16 * wave + 4 * grp) = float4{pv[0], pv[1], pv[2], pv[3]};
+    __syncthreads();  // P^T of all 64 keys in LDS
+
+    // ---- O^T[128*wave + 16*vt + (0..15)][head] += C^T . P^T over the 64 keys -------------
+#pragma unroll
+    for (int kq = 0; kq < kChunkKeys / 4; ++kq) {
+      const int row = 4 * kq + grp;
+      const float pf = s_p[col * kPRow + row];
+      const char* rp = buf + row * Cfg::ROW_BYTES;
+      const int sw = row_swz(row);
+#pragma unroll
+      for (int vt = 0; vt < 8; ++vt) {
+        const int v = 128 * wave + 16 * vt + col;
+        const float cv = *reinterpret_cast<const float*>(rp + 16 * ((v >> 2) ^ sw) + 4 * (v & 3));
+        acc[vt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cv, pf, acc[vt], 0, 0, 0);
+      }
+    }
+  }
+
+  write_result(a, r, split, splits, h, wave, col, grp, acc, m_run, l_part, sm.s_l);
+}
+
+// ---- bf16 rows, gathered through registers ------------------------------------------------
+// The workgroup has 8 waves: waves 0..3 compute (the q.c / softmax / p.c of
+// attend, unchanged), waves 4..7 gather. Gather wave p brings rows 16p ..
+// 16p+15 of each 64-row chunk into registers: lane (i = lane/8, q = lane%8)
+// loads 16-byte piece q of every 128-byte line m (0..8) of rows 16p + i and
+// 16p + 8 + i, so eight lanes read one whole line (a 1152-byte row is nine
+// lines) -- twice the bytes per request of four lanes on 64-byte halves, and
+// measured about 1.5x the per-CU rate of direct-to-LDS loads. It then stores
+// the rows into the chunk buffer in the block layout (blk_off) that the
+// compute waves read. Two chunks are in flight in registers while two sit in
+// the LDS buffers, and the barriers between the roles order LDS only: a
+// plain workgroup barrier would also drain the gathers in flight.
+constexpr int kAttnWaves8 = 8;
+constexpr int kGatherLines = kLatentDim * 2 / 128;  // 128-byte lines per bf16 row (9)
+
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct RowRegs {
+  uint4 v[2][kGatherLines];
+  bool live[2];
+};
+
+// The range's raw indices s_idx[0 .. span) become cache rows (-1: missing
+// key), by all threads of the workgroup, every lookup in flight at once (a
+// paged cache reads its block table here, once per key, not in the gather).
+// Cache rows fit in 31 bits (the entry points refuse larger caches).
+template <int THREADS>
+__device__ __forceinline__ void rows_of_indices(const AttnArgs& a, int64_t base, int* s_idx, int span) {
+  constexpr int kPer = kMaxTopk / THREADS;
+  int64_t row[kPer];
+  bool ok[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = int(threadIdx.x) + u * THREADS;
+    ok[u] = e < span && attn_row(a, base, s_idx[e < span ? e : 0], row[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = int(threadIdx.x) + u * THREADS;
+    if (e < span) s_idx[e] = ok[u] ? int(row[u]) : -1;
+  }
+}
+
+// Issue the loads of gather wave p's rows of chunk c (cache rows in s_row,
+// -1 for a missing key, which reads row 0 and is stored as zeros).
+__device__ __forceinline__ void rows_issue(const AttnArgs& a, const int* s_row, int c, int p, int lane, RowRegs& rr) {
+  int row[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    row[g] = s_row[kChunkKeys * c + 16 * p + 8 * g + (lane >> 3)];
+    rr.live[g] = row[g] >= 0;
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.latent) +
+                                                      int64_t(rr.live[g] ? row[g] : 0) * 1152 + 16 * (lane & 7));
+#pragma unroll
+    for (int m = 0; m < kGatherLines; ++m) rr.v[g][m] = src[8 * m];
+  }
+}
+
+// The query rows of the workgroup's 16 heads (16 x 72 pieces of 16 bytes),
+// loaded by the gather waves into registers -- early, so that they land while
+// the indices are being found -- and staged once in LDS for the compute waves
+// (four compute waves loading them each would quadruple this traffic on the
+// CU's load path, which bounds the kernel). Piece e = 256u + 64p + lane of
+// gather wave p; heads past H read head H-1 (their columns are computed and
+// never written).
+constexpr int kQPieces = kGroupHeads * kLatentDim / 8;  // 1152
+struct QRegs {
+  bf16x8 v[5];  // a clang vector type: a HIP uint4 member is copied through private memory here
+};
+__device__ __forceinline__ void q_issue(const AttnArgs& a, int r, int hg, int p, int lane, QRegs& qr) {
+#pragma unroll
+  for (int u = 0; u < 5; ++u) {
+    const int e0 = 256 * u + 64 * p + lane;
+    const int e = e0 < kQPieces ? e0 : kQPieces - 1;  // past the rows: a piece that exists, not stored
+    const int h = e / 72, j = e - 72 * (e / 72);
+    const int hh = hg * kGroupHeads + h < a.H ? hg * kGroupHeads + h : a.H - 1;
+    qr.v[u] = *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(a.q) +
+                                               (int64_t(r) * a.H + hh) * kLatentDim + 8 * j);
+  }
+}
+// Row h at piece kQPitch*h of `dst` (the pitch makes the fragment reads conflict-free).
+__device__ __forceinline__ void q_store(const QRegs& qr, char* dst, int p, int lane) {
+#pragma unroll
+  for (int u = 0; u < 5; ++u) {
+    const int e = 256 * u + 64 * p + lane;
+    const int h = e / 72, j = e - 72 * (e / 72);
+    if (e < kQPieces) *reinterpret_cast<bf16x8*>(dst + 16 * (kQPitch * h + j)) = qr.v[u];
+  }
+}
+
+// Store gather wave p's rows into `buf` (rows of missing keys as zeros, so
+// that p.c adds exactly 0 for them) and return the 16-bit mask of present
+// rows. Piece 8m + q of row 16p + 8g + i goes to blk_off: per store, two
+// contiguous 512-byte runs.
+__device__ __forceinline__ uint32_t rows_store(const RowRegs& rr, char* buf, int p, int lane) {
+  const int i = lane >> 3, q = lane & 7;
+  char* dst = buf + kBlock * p + 1024 * (q >> 2) + 16 * (q & 3) + 64 * i;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int m = 0; m < kGatherLines; ++m)
+      *reinterpret_cast<uint4*>(dst + 2048 * m + 512 * g) = rr.live[g] ? rr.v[g][m] : uint4{0u, 0u, 0u, 0u};
+  const unsigned long long b0 = __ballot(rr.live[0] && q == 0), b1 = __ballot(rr.live[1] && q == 0);
+  uint32_t mask = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    mask |= (uint32_t((b0 >> (8 * k)) & 1ull) << k) | (uint32_t((b1 >> (8 * k)) & 1ull) << (8 + k));
+  return mask;
+}
+
+// attend() for bf16 rows with gather waves: the same split, arithmetic and
+// order of operations as attend<false>, hence the same bits. All 8 waves call
+// it; s_row holds the range's cache rows (rows_of_indices), filled by the
+// caller, and qr the gather waves' query pieces (q_issue). After a prologue
+// (chunk 0 and the query staged; the query read into the compute waves'
+// registers, which frees buffer 1), the two roles run separate loops with
+// the same barriers, per chunk c:
+//   compute: q.c(c) | B1 | softmax(c) | B2 | p.c(c)                    | B3
+//   gather :        | B1 |            | B2 | store c+1, issue c+3     | B3
+// (buffer c%2 holds chunk c; chunk c+1's buffer last held chunk c-1, whose
+// p.c ended before B1), so their registers never live at the same time.
+__device__ __forceinline__ void attend_bf16(const AttnArgs& a, int r, int split, int splits, int hg, int j_beg,
+                                            int j_end, const int* s_row, const QRegs& qr, Smem<false>& sm) {
+  using Cfg = AttnCfg<false>;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int nchunks = j_end > j_beg ? (j_end - j_beg + kChunkKeys - 1) / kChunkKeys : 0;
+
+  if (wave >= 4) {
+    // ---- gather waves: chunk j travels in register set j % 2 -----------------------------
+    const int p = wave - 4;
+    RowRegs rs[2];
+    if (nchunks > 0) {
+      rows_issue(a, s_row, 0, p, lane, rs[0]);
+      if (nchunks > 1) rows_issue(a, s_row, 1, p, lane, rs[1]);
+      q_store(qr, sm.buf + Cfg::BUF_BYTES, p, lane);
+      const uint32_t m0 = rows_store(rs[0], sm.buf, p, lane);
+      if (lane == 0) sm.s_ok[0][p] = m0;
+      if (nchunks > 2) rows_issue(a, s_row, 2, p, lane, rs[0]);
+    }
+    lds_sync();  // chunk 0 in buffer 0, the query staged in buffer 1
+    lds_sync();  // the compute waves have read the query: buffer 1 is free
+    auto step = [&](int c, auto next_c) {
+      constexpr int NEXT = decltype(next_c)::value;  // register set of chunk c+1
+      lds_sync();  // B1
+      lds_sync();  // B2
+      if (c + 1 < nchunks) {
+        const int bn = (c + 1) & 1;
+        const uint32_t mk = rows_store(rs[NEXT], sm.buf + bn * Cfg::BUF_BYTES, p, lane);
+        if (lane == 0) sm.s_ok[bn][p] = mk;
+        if (c + 3 < nchunks) rows_issue(a, s_row, c + 3, p, lane, rs[NEXT]);
+      }
+      lds_sync();  // B3
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+      step(c, std::integral_constant<int, 1>{});
+      if (c + 1 < nchunks) step(c + 1, std::integral_constant<int, 0>{});
+    }
+    lds_sync();  // the row sums
+    return;
+  }
+
+  // ---- compute waves ------------------------------------------------------------------------
+  const int col = lane & 15, grp = lane >> 4;
+  const int h = hg * kGroupHeads + col;
+  lds_sync();  // chunk 0 in buffer 0, the query staged in buffer 1
+  bf16x8 qf[18];  // B operand of q.c: head h, dims 32*ks + 8*grp .. +8
+#pragma unroll
+  for (int ks = 0; ks < 18; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(sm.buf + Cfg::BUF_BYTES + 16 * (kQPitch * col + 4 * ks + grp));
+  lds_sync();  // buffer 1 is free
+  f32x4 acc[8];
+#pragma unroll
+  for (int vt = 0; vt < 8; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max (log2 domain) of head h, equal in all compute waves
+  float l_part = 0.f;       // this lane's share of the running sum
+  const float scale2 = a.scale * kLog2e;
+  const int tr_row = 4 * grp + (col >> 2);
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int bi = c & 1;
+    const char* buf = sm.buf + bi * Cfg::BUF_BYTES;
+    float x[4];
+    {
+      const uint32_t okc = sm.s_ok[bi][wave];
+      const char* rp = buf + kBlock * wave + 64 * col + 16 * grp;
+      const f32x4 sacc = qc_bf16(rp, qf);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = ((okc >> (4 * grp + i)) & 1u) ? sacc[i] * scale2 : -INFINITY;
+        mx = fmaxf(mx, x[i]);
+      }
+      mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+      if (grp == 0) sm.s_max[wave][col] = mx;
+    }
+    lds_sync();  // B1: chunk maxima visible
+    {
+      const float cmax =
+          fmaxf(fmaxf(sm.s_max[0][col], sm.s_max[1][col]), fmaxf(sm.s_max[2][col], sm.s_max[3][col]));
+      const float m_new = fmaxf(m_run, cmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no key seen yet: p = alpha = 0
+      const float alpha = exp2f(m_run - m_use);
+      float psum = 0.f;
+      __bf16 pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = exp2f(x[i] - m_use);
+        pv[i] = static_cast<__bf16>(e);
+        psum += static_cast<float>(pv[i]);
+      }
+      l_part = l_part * alpha + psum;
+      m_run = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int vt = 0; vt < 8; ++vt) acc[vt] *= alpha;
+      }
+      __bf16* prow = sm.s_p + col * kPRow + 16 * wave + 4 * grp;
       const uint32_t w0 = uint32_t(__builtin_bit_cast(uint16_t, pv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[1])) << 16);
       const uint32_t w1 = uint32_t(__builtin_bit_cast(uint16_t, pv[2])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[3])) << 16);
       *reinterpret_cast<uint2*>(prow) = uint2{w0, w1};
     }
-    __syncthreads();  // P^T of all 64 keys in LDS
-
-    // ---- O^T[128*wave + 16*vt + (0..15)][head] += C^T . P^T over the 64 keys -------------
-    if constexpr (F32) {
-#pragma unroll
-      for (int kq = 0; kq < kChunkKeys / 4; ++kq) {
-        const int row = 4 * kq + grp;
-        const float pf = s_p[col * kPRow + row];
-        const char* rp = buf + row * Cfg::ROW_BYTES;
-        const int sw = row_swz(row);
-#pragma unroll
-        for (int vt = 0; vt < 8; ++vt) {
-          const int v = 128 * wave + 16 * vt + col;
-          const float cv = *reinterpret_cast<const float*>(rp + 16 * ((v >> 2) ^ sw) + 4 * (v & 3));
-          acc[vt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cv, pf, acc[vt], 0, 0, 0);
-        }
-      }
-    } else {
-      // K-slot 8*grp + i <-> key kb + 4*grp + i (i < 4) and kb + 16 + 4*grp + (i - 4).
-      // Transposing read: lane s of each 16-lane group names 4 values of row
-      // kb + 4*grp + s/4 (value dims v0 + 4*(s%4) ..), and receives value dim
-      // v0 + s of rows kb + 4*grp + 0..3.
-      const int tr_row = 4 * grp + (col >> 2);
+    lds_sync();  // B2: P^T of all 64 keys in LDS
+    {
+      // O^T[128*wave + 16*vt + (0..15)][head] += C^T . P^T over the 64 keys (as in attend)
       bf16x8 pf[2];
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
-        const PT* pp = s_p + col * kPRow + 32 * kq + 4 * grp;
+        const __bf16* pp = sm.s_p + col * kPRow + 32 * kq + 4 * grp;
         const uint2 plo = *reinterpret_cast<const uint2*>(pp);
         const uint2 phi = *reinterpret_cast<const uint2*>(pp + 16);
         pf[kq] = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
       }
-      // value fragment of step q = (kb = 32*(q/8), vt = q%8), read three
-      // steps ahead: lane (col, grp) names row kb + tr_row (and, 16 rows on,
-      // the next block), value dims 128*wave + 16vt + 4(col%4) .. +3, that is
-      // piece 16*wave + 2vt + (col%4)/2, half (col%4)&1
       auto vfrag = [&](int q) -> bf16x8 {
         const int kb = 32 * (q >> 3), vt = q & 7;
         const char* p0 = buf + blk_off(kb + tr_row, 16 * wave + 2 * vt + ((col >> 1) & 1)) + 8 * (col & 1);
@@ -527,39 +658,52 @@ __device__ __forceinline__ void attend(const AttnArgs& a, int r, int split, int 
             (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + kBlock));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      // LOADS: direct load q of the next chunk rides on step q (and the
-      // last two after the loop)
-      auto pc = [&](auto loads) {
-        constexpr bool LOADS = decltype(loads)::value;
-        constexpr int D = 3;
-        bf16x8 vr[D];
+      constexpr int D = 3;
+      bf16x8 vr[D];
 #pragma unroll
-        for (int i = 0; i < D; ++i) vr[i] = vfrag(i);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < D; ++i) vr[i] = vfrag(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const bf16x8 af = vr[q % D];
-          if (q + D < 16) vr[q % D] = vfrag(q + D);
-          acc[q & 7] = mfma_k32(af, pf[q >> 3], acc[q & 7]);
-          if constexpr (LOADS) bgather_load(gn, q);
-          if (q + D < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (LOADS) {
-          static_assert(Cfg::WAVE_LOADS == 18, "two loads left after the 16 steps");
-          bgather_load(gn, 16);
-          bgather_load(gn, 17);
-        }
-      };
-      if (pc_loads) pc(std::true_type{});
-      else pc(std::false_type{});
+      for (int q = 0; q < 16; ++q) {
+        const bf16x8 af = vr[q % D];
+        if (q + D < 16) vr[q % D] = vfrag(q + D);
+        acc[q & 7] = mfma_k32(af, pf[q >> 3], acc[q & 7]);
+        if (q + D < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    lds_sync();  // B3: chunk c+1 in the other buffer; every compute wave is done with this one
   }
 
-  write_result(a, r, split, splits, h, wave, col, grp, acc, m_run, l_part, s_l);
+  // epilogue: the row sums over lanes and compute waves, then the output
+  {
+    float l_w = l_part + wave_shfl_xor(l_part, 16);
+    l_w += wave_shfl_xor(l_w, 32);
+    if (grp == 0) sm.s_l[wave][col] = l_w;
+  }
+  lds_sync();
+  if (h >= a.H) return;
+  const float L = ((sm.s_l[0][col] + sm.s_l[1][col]) + sm.s_l[2][col]) + sm.s_l[3][col];
+  const int64_t rh = int64_t(r) * a.H + h;
+  const bool final_out = splits == 1;
+  const float inv = final_out ? (L > 0.f ? 1.f / L : 0.f) : 1.f;
+  float* dst = final_out ? a.out + rh * kValueDim
+                         : static_cast<float*>(a.ws) + ((int64_t(r) * splits + split) * a.H + h) * kValueDim;
+#pragma unroll
+  for (int vt = 0; vt < 8; ++vt)
+    *reinterpret_cast<float4*>(dst + 128 * wave + 16 * vt + 4 * grp) =
+        float4{acc[vt][0] * inv, acc[vt][1] * inv, acc[vt][2] * inv, acc[vt][3] * inv};
+  if (wave == 0 && grp == 0) {
+    if (final_out) {
+      if (a.lse) a.lse[rh] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      float* ml = static_cast<float*>(a.ws) + int64_t(a.R) * splits * a.H * kValueDim;
+      const int64_t slot = (int64_t(r) * splits + split) * a.H + h;
+      *reinterpret_cast<float2*>(ml + 2 * slot) = float2{m_run, L};
+    }
+  }
 }
-
 
 // ---- FP8 latent rows: e4m3 codes with one float32 scale per cache row ----------------------
 // C[s, :] = e4m3(code[s, :]) * scale[s]. The codes convert exactly to bf16

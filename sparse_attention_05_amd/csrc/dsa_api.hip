@@ -28,6 +28,7 @@ size_t align256(size_t x) {
 }
 
 constexpr int kMaxTopkRow = 1 << 20;  // longest score row the top-k accepts
+constexpr int64_t kMaxCacheRows = (int64_t(1) << 31) - 1;  // the attention keeps cache rows in 31 bits
 
 dsa_status check_index_args(const void* q, int q_dtype, const float* w, const void* keys, int k_dtype,
                             const uint16_t* k_scale, int64_t cache_rows, int B, int R, int H_I, int D_I,
@@ -65,6 +66,7 @@ dsa_status check_attn_args(const void* q_abs, int dtype, const void* latent, int
   const dsa_status lt = check_latent(dtype, latent_dtype, latent_scale);
   if (lt != DSA_OK) return lt;
   if (R < 0 || B < 1 || cache_rows < 1) return DSA_ERR_SHAPE;
+  if (cache_rows > kMaxCacheRows) return DSA_ERR_UNSUPPORTED;
   if (k < 1 || k > DSA_MAX_TOPK) return DSA_ERR_UNSUPPORTED;
   if (H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
   if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
@@ -146,7 +148,7 @@ dsa_status decode_fused_impl(const void* q_idx, const float* head_w, const void*
   if (act_dtype != DSA_F32 && act_dtype != DSA_BF16) return DSA_ERR_DTYPE;
   st = check_latent(act_dtype, latent_dtype, latent_scale);
   if (st != DSA_OK) return st;
-  if (max_len > kMaxTopkRow) return DSA_ERR_UNSUPPORTED;
+  if (max_len > kMaxTopkRow || cache_rows > kMaxCacheRows) return DSA_ERR_UNSUPPORTED;
   if (k < 1 || k > DSA_MAX_TOPK || H < 1 || H > 128) return DSA_ERR_UNSUPPORTED;
   if (!aligned16(q_abs) || !aligned16(latent) || !aligned16(out)) return DSA_ERR_ALIGN;
   const size_t need = decode_ws_bytes(R, max_len, k, H);

@@ -70,10 +70,47 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, in
   if constexpr (M == kFP8) {
     attend8(a, r, split, splits, hg, j_beg, j_end, base, s_idx, sm);
   } else {
-    QFrag<F32> qf[18];  // bf16: staged and read by attend itself
-    if constexpr (F32) load_q<F32>(a, r, h, grp, qf);
-    attend<F32>(a, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, sm);
+    f32x8 qf[18];
+    load_q<true>(a, r, h, grp, qf);
+    attend_f32(a, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, sm);
   }
+}
+
+// bf16 rows: 8 waves, the four compute waves of sparse_mla_kernel plus four
+// waves that gather the rows through registers (attend_bf16).
+__global__ __launch_bounds__(kAttnWaves8 * 64) void sparse_mla_bf16_kernel(AttnArgs a, int splits, int kps) {
+  __shared__ Smem<false> sm;
+  __shared__ int s_idx[kMaxTopk];  // the range's cache rows, -1 past it up to the chunk boundary
+  const int HG = (a.H + kGroupHeads - 1) / kGroupHeads;
+  int r, split, hg;
+  map_block(blockIdx.x, a.R, splits, HG, r, split, hg);
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int j_beg = split * kps;
+  const int j_end = (j_beg + kps < a.k) ? j_beg + kps : a.k;
+  const int span = j_end > j_beg ? (j_end - j_beg + kChunkKeys - 1) / kChunkKeys * kChunkKeys : 0;
+  // the range's indices (every load in flight before the first store), the
+  // sequence's first row, the compute waves' query fragments
+  constexpr int kPer = kMaxTopk / (kAttnWaves8 * 64);
+  int v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = t + u * kAttnWaves8 * 64;
+    const int j = j_beg + e;
+    v[u] = e < span && j < j_end ? a.idx[int64_t(r) * a.k + j] : -1;
+  }
+  const int64_t base = seq_base(a, r);
+  QRegs qr;  // the gather waves' query pieces
+  if (wave >= 4) q_issue(a, r, hg, wave - 4, lane, qr);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int e = t + u * kAttnWaves8 * 64;
+    if (e < span) s_idx[e] = v[u];
+  }
+  rows_of_indices<kAttnWaves8 * 64>(a, base, s_idx, span);  // each thread rewrites the entries it stored
+  lds_sync();
+  attend_bf16(a, r, split, splits, hg, j_beg, j_end, s_idx, qr, sm);
 }
 
 // ---- many queries: one workgroup per query for all (<= 64) heads ---------------------
@@ -493,7 +530,7 @@ hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_
   const dim3 grid(unsigned(a.R) * unsigned(plan.splits) * unsigned(plan.head_groups));
   if (a.latent_dtype == kFP8) sparse_mla_kernel<kFP8><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
   else if (a.dtype == kF32) sparse_mla_kernel<kF32><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
-  else sparse_mla_kernel<kBF16><<<grid, kAttnThreads, 0, stream>>>(a, plan.splits, plan.keys_per_split);
+  else sparse_mla_bf16_kernel<<<grid, kAttnWaves8 * 64, 0, stream>>>(a, plan.splits, plan.keys_per_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_attn_combine(a, plan, stream);

@@ -1140,11 +1140,15 @@ __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnAr
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   // The selection's global loads go out first, in one round trip: the
-  // candidate counts and words, the row's length and first cache row.
+  // candidate counts and words, the row's length and first cache row; then
+  // (bf16 rows) the gather waves' query pieces, which land during the
+  // selection.
   WindowLoads L;
   window_loads(ta, r, slices, L);
   const int64_t base = attn::seq_base(aa, r);
   const int n = row_len(ta, r);
+  attn::QRegs qr;
+  if (M != kFP8 && wave >= 4) attn::q_issue(aa, r, hg, wave - 4, t & 63, qr);
   const int k = ta.k;
   const int k_eff = n < k ? n : k;
   const int j_beg = split * kps;
@@ -1158,12 +1162,14 @@ __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnAr
   lds_barrier();  // the split's indices are in LDS; the selection's LDS is free
   if (hg == 0)
     for (int i = t; i < j_end - j_beg; i += kThreads) ta.idx[int64_t(r) * k + j_beg + i] = s_idx[i];
-  if (wave >= 4) return;  // barriers below count the four attention waves only
   if constexpr (M == kFP8) {
+    if (wave >= 4) return;  // barriers below count the four attention waves only
     attn::attend8(aa, r, split, splits, hg, j_beg, j_end, base, s_idx, u.att);
   } else {
-    bf16x8 qf[18];  // staged and read by attend itself
-    attn::attend<false>(aa, r, split, splits, hg, j_beg, j_end, base, s_idx, qf, u.att);
+    // the same thread stored these indices above: no barrier before the rewrite
+    attn::rows_of_indices<kThreads>(aa, base, s_idx, span);
+    lds_barrier();
+    attn::attend_bf16(aa, r, split, splits, hg, j_beg, j_end, s_idx, qr, u.att);
   }
 }
 
