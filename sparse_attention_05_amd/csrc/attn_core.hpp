@@ -421,8 +421,8 @@ __device__ __forceinline__ void attend_f32(const AttnArgs& a, int r, int split, 
 // lines) -- twice the bytes per request of four lanes on 64-byte halves, and
 // measured about 1.5x the per-CU rate of direct-to-LDS loads. It then stores
 // the rows into the chunk buffer in the block layout (blk_off) that the
-// compute waves read. Two chunks are in flight in registers while two sit in
-// the LDS buffers, and the barriers between the roles order LDS only: a
+// compute waves read. Chunk 0 travels alone; after it, two chunks are in
+// flight in registers while two sit in the LDS buffers, and the barriers between the roles order LDS only: a
 // plain workgroup barrier would also drain the gathers in flight.
 constexpr int kAttnWaves8 = 8;
 constexpr int kGatherLines = kLatentDim * 2 / 128;  // 128-byte lines per bf16 row (9)
@@ -549,11 +549,13 @@ __device__ __forceinline__ void attend_bf16(const AttnArgs& a, int r, int split,
     const int p = wave - 4;
     RowRegs rs[2];
     if (nchunks > 0) {
+      // chunk 0 alone first, so that it lands as early as the CU's load rate
+      // allows and its compute overlaps the transfer of the next ones
       rows_issue(a, s_row, 0, p, lane, rs[0]);
-      if (nchunks > 1) rows_issue(a, s_row, 1, p, lane, rs[1]);
       q_store(qr, sm.buf + Cfg::BUF_BYTES, p, lane);
       const uint32_t m0 = rows_store(rs[0], sm.buf, p, lane);
       if (lane == 0) sm.s_ok[0][p] = m0;
+      if (nchunks > 1) rows_issue(a, s_row, 1, p, lane, rs[1]);
       if (nchunks > 2) rows_issue(a, s_row, 2, p, lane, rs[0]);
     }
     lds_sync();  // chunk 0 in buffer 0, the query staged in buffer 1

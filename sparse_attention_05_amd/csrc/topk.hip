@@ -59,6 +59,7 @@ struct __attribute__((aligned(16))) TopkShared {
   uint32_t fill[kBins];              // bucket fill counters
   uint32_t cnt[kBins];               // bucket counts
   uint32_t coarse[64];
+  uint32_t xred[(2 + kMaxSliceTiles) * kWaves];  // candidate-launch exchange
   unsigned long long wa[kCap];       // candidate / winner words, sort ping-pong
   union {
     unsigned long long wb[kCap];
@@ -68,7 +69,7 @@ struct __attribute__((aligned(16))) TopkShared {
     uint32_t samp[kMaxSamples];      // score sample keys (split pivot)
     unsigned long long net[kCap];    // bitonic scratch
   } v;
-  uint32_t red[4 * kWaves];
+  uint32_t red[6 * kWaves];
   uint32_t misc[16];
   uint32_t work[2][6 * kMaxWork];    // dense buckets: offset, length, max (2 words), min (2 words)
 };
@@ -697,39 +698,38 @@ __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
 // [smin, smax]). The t-th largest sample is taken, t chosen so that the count
 // of keys above it (about t*SS, with a standard deviation of about
 // sqrt(t)*SS) falls below k only 3 deviations down; the pivot is the lower
-// edge of the 12-bit bin holding it, refined by a second 12-bit histogram
-// inside that bin when the bin holds more than a few samples past t (a heavy
-// tail stretches the range and widens the bins).
+// edge of the 12-bit bin holding it, refined by further 12-bit histograms
+// inside that bin (at most three passes reach single values) while the bin
+// holds more than a few samples past t: a heavy tail stretches the range and
+// widens the bins, and a tie class at the t-th sample ends on its exact
+// value, whose keys the candidate launch then lists in index order.
 __device__ __forceinline__ uint32_t sample_pivot(TopkShared& sh, int ns, int SS, int k, uint32_t smin, uint32_t smax) {
   const float kq = float(k) / float(SS);
   const float rt = 1.5f + sqrtf(2.25f + kq);
   uint32_t ts = uint32_t(ceilf(rt * rt));
   if (ts > uint32_t(ns)) ts = uint32_t(ns);
   if (!(smin < smax)) return smin;
-  int shift, nb;
-  digit_plan(smin, smax, 12, shift, nb);
-  clear_bins(sh.bins, kBins);
-  lds_barrier();
-  for (int i = int(threadIdx.x); i < ns; i += kThreads) atomicAdd(&sh.bins[(sh.v.samp[i] - smin) >> shift], 1u);
-  lds_barrier();
-  uint32_t b, above, cnt;
-  find_crossing(sh, ts, b, above, cnt);
-  const uint32_t lo1 = smin + (b << shift);
-  if (shift == 0 || above + cnt <= ts + 8) return lo1;
-  const unsigned long long top = static_cast<unsigned long long>(lo1) + ((1ull << shift) - 1ull);
-  const uint32_t hi1 = top < smax ? static_cast<uint32_t>(top) : smax;
-  int shift2, nb2;
-  digit_plan(lo1, hi1, 12, shift2, nb2);
-  clear_bins(sh.bins, kBins);  // (find_crossing's last barrier ended its reads)
-  lds_barrier();
-  for (int i = int(threadIdx.x); i < ns; i += kThreads) {
-    const uint32_t x = sh.v.samp[i];
-    if (x >= lo1 && x <= hi1) atomicAdd(&sh.bins[(x - lo1) >> shift2], 1u);
+  uint32_t lo = smin, hi = smax, target = ts;
+  for (int pass = 0; pass < 3; ++pass) {
+    int shift, nb;
+    digit_plan(lo, hi, 12, shift, nb);
+    clear_bins(sh.bins, kBins);  // (find_crossing's last barrier ended the reads of the previous pass)
+    lds_barrier();
+    for (int i = int(threadIdx.x); i < ns; i += kThreads) {
+      const uint32_t x = sh.v.samp[i];
+      if (x >= lo && x <= hi) atomicAdd(&sh.bins[(x - lo) >> shift], 1u);
+    }
+    lds_barrier();
+    uint32_t b, above, cnt;
+    find_crossing(sh, target, b, above, cnt);
+    const uint32_t blo = lo + (b << shift);
+    if (shift == 0 || above + cnt <= target + 8) return blo;
+    const unsigned long long top = static_cast<unsigned long long>(blo) + ((1ull << shift) - 1ull);
+    hi = top < hi ? static_cast<uint32_t>(top) : hi;
+    lo = blo;
+    target -= above;
   }
-  lds_barrier();
-  uint32_t b2, above2, cnt2;
-  find_crossing(sh, ts - above, b2, above2, cnt2);
-  return lo1 + (b2 << shift2);
+  return lo;
 }
 
 // Exact selection over a whole row held by `row` (any EPT), for rows whose
@@ -904,35 +904,80 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
     pivot = sample_pivot(sh, ns, SS, k, smin, smax);
   }
 
-  // ---- this slice's candidates, compacted (thread order, then tile order) -------------------
-  uint32_t c = 0, cm = 0;
+  // ---- this slice's candidates: keys above the pivot (any order), then the
+  // keys equal to it in index order (tile, then thread, then slot) --------------------------
+  uint32_t cg = 0, cm = 0, ce[T];
 #pragma unroll
   for (int j = 0; j < T; ++j) {
     const int i0 = (g * T + j) * kTile + 4 * t;
     const uint32_t key[4] = {order_key(sv[j].x), order_key(sv[j].y), order_key(sv[j].z), order_key(sv[j].w)};
+    ce[j] = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool in = i0 + e < n && key[e] >= pivot;
-      c += in;
-      cm = in ? max(cm, key[e]) : cm;
+      const bool valid = i0 + e < n;
+      cg += valid && key[e] > pivot;
+      ce[j] += valid && key[e] == pivot;
+      cm = valid && key[e] >= pivot ? max(cm, key[e]) : cm;
     }
   }
-  uint32_t total, cmax;
-  uint32_t pos = block_scan_max(c, cm, sh.red, total, cmax);
+  // one exchange: offsets of the words above the pivot (any thread order) and
+  // their largest key; offsets of the keys equal to it in (tile, thread) order
+  uint32_t G, cmax, E, pos, epos[T];
+  {
+    const uint32_t xg = wave_incl_scan(cg), xm = wave_max(cm);
+    uint32_t xe[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) xe[j] = wave_incl_scan(ce[j]);
+    if (lane_id() == 63) {
+      sh.xred[wave_id()] = xg;
+      sh.xred[kWaves + wave_id()] = xm;
+#pragma unroll
+      for (int j = 0; j < T; ++j) sh.xred[(2 + j) * kWaves + wave_id()] = xe[j];
+    }
+    lds_barrier();
+    uint32_t gb = 0, gt = 0, mm = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = sh.xred[w];
+      gb += w < wave_id() ? c : 0u;
+      gt += c;
+      mm = max(mm, sh.xred[kWaves + w]);
+    }
+    pos = gb + xg - cg;
+    G = gt;
+    cmax = mm;
+    uint32_t run = 0;
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      uint32_t eb = 0, et = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const uint32_t c = sh.xred[(2 + j) * kWaves + w];
+        eb += w < wave_id() ? c : 0u;
+        et += c;
+      }
+      epos[j] = run + eb + xe[j] - ce[j];
+      run += et;
+    }
+    E = run;
+  }
 #pragma unroll
   for (int j = 0; j < T; ++j) {
     const int i0 = (g * T + j) * kTile + 4 * t;
     const uint32_t key[4] = {order_key(sv[j].x), order_key(sv[j].y), order_key(sv[j].z), order_key(sv[j].w)};
+    uint32_t q = G + epos[j];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (i0 + e < n && key[e] >= pivot) {
-        cand[pos] = word(key[e], i0 + e);
-        ++pos;
+        const bool eq = key[e] == pivot;
+        cand[eq ? q : pos] = word(key[e], i0 + e);
+        q += eq;
+        pos += !eq;
       }
     }
   }
   if (t == 0)
-    reinterpret_cast<uint4*>(a.state)[int64_t(r) * slices + g] = uint4{total, cmax, pivot, 0u};
+    reinterpret_cast<uint4*>(a.state)[int64_t(r) * slices + g] = uint4{G + E, cmax, pivot, E};
 }
 
 // Ranks [lo, hi) of row r (hi <= min(n, k)) from the candidates of the
@@ -1022,9 +1067,59 @@ __device__ __forceinline__ void window_gather_sort(TopkShared& sh, const TopkArg
              static_cast<unsigned long long>(kmin) << 32, lo, hi, out, obase);
 }
 
+// Ranks [lo, hi) when the k-th rank falls in the class of keys equal to the
+// pivot (a tie class too large for the candidate capacity): the G keys above
+// the pivot (G < k_eff) take ranks 0 .. G-1 in their own order; rank G + j is
+// the j-th key of the class in index order (lower index first), which the
+// candidate launch listed after each slice's words above the pivot. gat and
+// eat: slice t's offsets among the words above the pivot and among the class.
+__device__ __forceinline__ void window_ties(TopkShared& sh, const TopkArgs& a, int r, int slices, uint32_t G, int lo,
+                                            int hi, int32_t* out, int obase, const WindowLoads& L, uint32_t gat,
+                                            uint32_t eat) {
+  const int t = threadIdx.x;
+  const int64_t stride = int64_t(a.slice_tiles) * kTile;  // words per slice region
+  const unsigned long long* cand = a.cand + int64_t(r) * slices * stride;
+  if (t < slices) {
+    sh.bins[t] = eat;               // first class rank of the slice
+    sh.cnt[t] = L.st.x - L.st.w;    // its words above the pivot
+    sh.fill[t] = gat;               // their offset in the order of slices
+  }
+  lds_barrier();
+  // ranks G + j: the slice is the last one whose first class rank is <= j
+  for (int q = (lo > int(G) ? lo : int(G)) + t; q < hi; q += kThreads) {
+    const uint32_t j = uint32_t(q) - G;
+    int s0 = 0, s1 = slices - 1;
+    while (s0 < s1) {
+      const int m = (s0 + s1 + 1) >> 1;
+      if (sh.bins[m] <= j) s0 = m;
+      else s1 = m - 1;
+    }
+    out[q - obase] = word_idx(cand[int64_t(s0) * stride + sh.cnt[s0] + (j - sh.bins[s0])]);
+  }
+  if (lo >= int(G)) return;
+  // ranks [lo, min(hi, G)): the words above the pivot, gathered and sorted
+  const int tps = window_tps(slices);
+  const int sg = t / tps, sl = t % tps;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (sg < slices) {
+    const int m = int(sh.cnt[sg]), o = int(sh.fill[sg]);
+    for (int i = sl; i < m; i += tps) {
+      const unsigned long long w = cand[int64_t(sg) * stride + i];
+      sh.wa[o + i] = w;
+      kmin = min(kmin, uint32_t(w >> 32));
+      kmax = max(kmax, uint32_t(w >> 32));
+    }
+  }
+  block_minmax(kmin, kmax, sh.red);  // (its barriers publish the gathered words)
+  sort_words(sh, int(G), (static_cast<unsigned long long>(kmax) << 32) | 0xFFFFFFFFull,
+             static_cast<unsigned long long>(kmin) << 32, lo, hi < int(G) ? hi : int(G), out, obase);
+}
+
 // Ranks [lo, hi) of row r (hi <= min(n, k)) from the candidates of the
-// slices, indices to out[rank - obase]; when fewer than k or more than kCap
-// keys cleared the pivot, the exact selection over the whole row instead.
+// slices, indices to out[rank - obase]; a tie class too large for the
+// candidate capacity at the k-th rank goes to window_ties; when fewer than k
+// keys, or more than kCap for another reason, cleared the pivot, the exact
+// selection over the whole row runs instead.
 // Usually the read-ahead words already are all of them: then the first
 // bucket pass works on them in registers, on digits of the range [pivot,
 // largest candidate] that the candidate kernel recorded, with no gather
@@ -1045,12 +1140,16 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
   }
   if (t == 0) sh.misc[6] = 0u;
   // one exchange: slice offsets and the total (scan of the counts), the
-  // largest candidate key, the longest slice, the pivot
-  const uint32_t cnt = L.st.x;
-  const uint32_t xs = wave_incl_scan(cnt);
+  // largest candidate key, the longest slice, the pivot, and the same scan
+  // of the counts of keys equal to the pivot
+  const uint32_t cnt = L.st.x, ecnt = L.st.w;
+  const uint32_t xs = wave_incl_scan(cnt), xe = wave_incl_scan(ecnt);
   {
     const uint32_t wm = wave_max(L.st.y), wc = wave_max(cnt);
-    if (lane_id() == 63) sh.red[wave_id()] = xs;
+    if (lane_id() == 63) {
+      sh.red[wave_id()] = xs;
+      sh.red[4 * kWaves + wave_id()] = xe;
+    }
     if (lane_id() == 0) {
       sh.red[kWaves + wave_id()] = wm;
       sh.red[2 * kWaves + wave_id()] = wc;
@@ -1058,7 +1157,7 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
     if (t == 0) sh.red[3 * kWaves] = L.st.z;
     lds_barrier();
   }
-  uint32_t C = 0, base = 0, kmax = 0, longest = 0;
+  uint32_t C = 0, base = 0, kmax = 0, longest = 0, E = 0, ebase = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     const uint32_t c = sh.red[w];
@@ -1066,9 +1165,17 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
     C += c;
     kmax = max(kmax, sh.red[kWaves + w]);
     longest = max(longest, sh.red[2 * kWaves + w]);
+    const uint32_t ce = sh.red[4 * kWaves + w];
+    ebase += w < wave_id() ? ce : 0u;
+    E += ce;
   }
   const uint32_t pivot = sh.red[3 * kWaves];
   const uint32_t at = base + xs - cnt;  // slice t's offset in the gathered order
+  const uint32_t G = C - E;             // keys above the pivot
+  if (C > uint32_t(kCap) && G < uint32_t(k_eff) && C >= uint32_t(k_eff) && G <= uint32_t(kCap)) {
+    window_ties(sh, a, r, slices, G, lo, hi, out, obase, L, at - (ebase + xe - ecnt), ebase + xe - ecnt);
+    return;
+  }
   if (C < uint32_t(k_eff) || C > uint32_t(kCap)) {
     Row<0> full;
     full.load(a.scores + int64_t(r) * a.ld, n);
