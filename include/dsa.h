@@ -115,8 +115,9 @@ dsa_status dsa_index_scores(const void* q_idx, int32_t q_dtype, const float* hea
  * scores of B sequences with q_per_seq new tokens each, row r = b *
  * q_per_seq + i at position seq_len[b] - q_per_seq + i (the tokens' keys
  * already appended), as dsa_index_scores computes them for those rows. With
- * bf16 keys and q_per_seq >= 2 each key row is read once for all of a
- * sequence's tokens (the multi-token step of dsa_decode_fused).
+ * q_per_seq >= 2 each key row (bf16 or fp8) is read once for all of a
+ * sequence's tokens (the multi-token step of dsa_decode_fused); paged caches
+ * and rows over 2^22 keys use one key stream per token.
  *
  *   q_idx [R, H_I, D_I], head_w [R, H_I], R = B * q_per_seq;
  *   q_per_seq in 1 .. DSA_MAX_TOKENS_PER_SEQ
@@ -203,8 +204,8 @@ dsa_status dsa_sparse_mla_attn(const void* q_abs, int32_t dtype, const void* lat
  * of a multi-token (MTP / speculative) step ("GLM-5: from Vibe Coding...",
  * section 2.1: multi-token prediction with shared parameters, 4 speculative
  * steps; "Zhipu AI / GLM", section 11.1: MTP steps share top-k indices and
- * the KV cache). With bf16 keys the indexer reads each key row once for all
- * of a sequence's new tokens. Enqueues the same kernels as the three entry
+ * the KV cache). The indexer reads each key row (bf16 or fp8) once for all
+ * of a sequence's new tokens (contiguous caches, rows up to 2^22 keys). Enqueues the same kernels as the three entry
  * points above, with the scores (and the indices when idx_out is NULL) kept
  * in the workspace; the attention split plan equals dsa_sparse_mla_attn's,
  * so replaying the recorded idx_out through dsa_sparse_mla_attn (q_seq[r] =

@@ -13,8 +13,8 @@ scale). Here u is taken as 2^-23 (twice the fp32 unit roundoff) so the bound
 also holds if the matrix cores truncate instead of rounding.
 
 Attention tolerance: for bf16 inputs with fp32 accumulation, max |O - O_ref|
-<= 2e-2 and ||O - O_ref||_2 / ||O_ref||_2 <= 1e-2 per case; fp32 inputs use
-1e-5 for both.
+<= 2e-2 and ||O - O_ref||_2 / ||O_ref||_2 <= 1e-2 per case and also for every
+(query, head) row of O separately; fp32 inputs use 1e-5 for all three.
 """
 import numpy as np
 
@@ -59,6 +59,20 @@ def assert_attn_close(out, ref, lse=None, lse_ref=None, fp32=False):
     assert err.max() <= atol, f"max abs err {err.max():.3e}"
     rel = np.linalg.norm(out - ref) / max(np.linalg.norm(ref), 1e-30)
     assert rel <= rtol, f"relative err {rel:.3e}"
+    # the same relative bound for every (query, head) row of O, so a wrong head
+    # or query cannot hide behind the others in the global norm; rows whose
+    # reference is zero (no key selected) must be zero
+    if out.ndim >= 2:
+        o2 = out.reshape(-1, out.shape[-1])
+        r2 = ref.reshape(-1, ref.shape[-1])
+        nr = np.linalg.norm(r2, axis=1)
+        ne = np.linalg.norm(o2 - r2, axis=1)
+        zero = nr == 0
+        assert (ne[zero] == 0).all(), "a row with no selected key is not zero"
+        per = ne[~zero] / nr[~zero]
+        if per.size:
+            worst = int(np.argmax(per))
+            assert per.max() <= rtol, f"row {np.flatnonzero(~zero)[worst]}: relative err {per.max():.3e}"
     if lse is not None:
         lse = np.asarray(lse, np.float64)
         lse_ref = np.asarray(lse_ref, np.float64)

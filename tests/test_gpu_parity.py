@@ -580,7 +580,7 @@ def _fused_multi(dsa, p, d):
     (2, [9000, 16385, 12000], "bf16", "fp8_e4m3"),
     (3, [5000, 8200, 4], "bf16", "bf16"),                   # idle wave; a sequence of 4 tokens
     (8, [10000, 2500], "bf16", "bf16"),                     # eight waves, one per token
-    (4, [9000, 3000], "fp8_e4m3", "bf16"),                  # fp8 keys: one key stream per row
+    (4, [9000, 3000], "fp8_e4m3", "bf16"),                  # fp8 keys in the shared key stream
 ])
 def test_fused_multi_token_decode(dsa, m, lens, key_dtype, latent_dtype):
     """Each token selects its own top-k over its own causal range: indices equal
@@ -818,13 +818,20 @@ def test_edges_context_parallel_one_shard(dsa):
     assert np.array_equal(out, o_parts[0]) and np.array_equal(lse, l_parts[0])   # one part: itself
 
 
-@pytest.mark.parametrize("m", [4, 6])
-def test_multi_token_fp8_keys_with_negative_scales(dsa, m):
+@pytest.mark.parametrize("m,H_I,D_I,lens", [
+    (4, 64, 128, [9000, 5000, 300]),
+    (6, 64, 128, [9000, 5000, 300]),
+    (2, 16, 64, [9000, 2500, 10]),      # one head tile, 64-d keys; a sequence shorter than a scale block
+    (4, 32, 128, [9000, 2500, 10]),
+    (3, 64, 64, [9000, 2500, 10]),
+])
+def test_multi_token_fp8_keys_with_negative_scales(dsa, m, H_I, D_I, lens):
     """fp8 keys in the shared-key-stream indexer, a tenth of the row scales
     negated (relu(scale * dot) per head there): scores within the bound of the
-    oracle's, indices the stable order of the step's own scores."""
-    p = inputs.decode_config([9000, 5000, 300], seed=70 + m, k=2048, key_dtype="fp8_e4m3", boost_frac=0.02,
-                             tokens_per_seq=m)
+    oracle's, indices the stable order of the step's own scores. Every
+    (heads, dim) instantiation of the kernel, and a sequence of 10 tokens."""
+    p = inputs.decode_config(lens, seed=70 + m + H_I + D_I, k=2048, key_dtype="fp8_e4m3", boost_frac=0.02,
+                             tokens_per_seq=m, H_I=H_I, D_I=D_I)
     rng = np.random.default_rng(m)
     neg = rng.random(p.k_scale.shape[0]) < 0.1
     p.k_scale = np.where(neg, p.k_scale | np.uint16(0x8000), p.k_scale).astype(np.uint16)
@@ -837,3 +844,38 @@ def test_multi_token_fp8_keys_with_negative_scales(dsa, m):
         C.assert_scores_close(p, r, scores[r])
     ref_o, ref_l = O.sparse_mla(p, idx)
     C.assert_attn_close(out, ref_o, lse, ref_l)
+
+
+def test_index_share_block_layers_over_recorded_indices(dsa):
+    """A block of four layers sharing one selection (cross-layer index reuse,
+    "Zhipu AI / GLM", section 11.1: one indexer per 4-layer block): layer 0
+    runs the fused step and records its indices; layers 1..3, each with its
+    own absorbed queries and latent cache, run the sparse attention over those
+    indices. Every layer's output is checked against the oracle's attention
+    over the recorded indices with that layer's own arrays; layer 0's indices
+    equal the stable order of its own scores."""
+    import torch
+    lens = [12000, 9001, 700, 20000]
+    layers = [inputs.decode_config(lens, seed=300 + l, k=2048) for l in range(4)]
+    ds = [inputs.to_torch(p, "cuda") for p in layers]
+    p0, d0 = layers[0], ds[0]
+    max_len = int(p0.seq_len.max())
+    out0, lse0, idx = dsa.dsa_decode_fused(d0.q_idx, d0.head_w, d0.k_idx, d0.q_abs, d0.latent, d0.row_off,
+                                           d0.seq_len, max_len, p0.k, p0.scale)
+    scores = dsa.dsa_index_scores(d0.q_idx, d0.head_w, d0.k_idx, d0.row_off, d0.q_pos, max_len)
+    torch.cuda.synchronize()
+    idx_np, sc = idx.cpu().numpy(), scores.cpu().numpy()
+    for r in range(p0.R):
+        n = int(p0.q_pos[r]) + 1
+        assert np.array_equal(idx_np[r], O.topk_row(sc[r, :n], p0.k)), f"layer 0 row {r}"
+    outs = [(out0.cpu().numpy(), lse0.cpu().numpy())]
+    for l in range(1, 4):
+        d = ds[l]
+        o, ls = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, idx, layers[l].scale)
+        torch.cuda.synchronize()
+        outs.append((o.cpu().numpy(), ls.cpu().numpy()))
+    for l, (o, ls) in enumerate(outs):
+        ref_o, ref_l = O.sparse_mla(layers[l], idx_np)
+        C.assert_attn_close(o, ref_o, ls, ref_l)
+    # layers differ (their own arrays), so no layer's output can stand in for another's
+    assert not np.array_equal(outs[1][0], outs[2][0])

@@ -180,3 +180,29 @@ def test_fp8_latent_equals_bf16_when_rows_are_exact():
     np.testing.assert_array_equal(idx, idxb)
     np.testing.assert_allclose(out8, outb, rtol=0, atol=1e-15)
     np.testing.assert_allclose(lse8, lseb, rtol=0, atol=1e-13)
+
+
+def test_empty_selection_is_the_identity_of_the_merge():
+    """The empty selection's (O, LSE) = (0, -inf): LSE is the log of an empty
+    sum of exponentials (log 0), and O the empty sum of weighted rows. -inf is
+    the one LSE that makes the log-sum-exp merge of a partition treat the empty
+    part as absent: the attention over A equals the merge of the attention
+    over A with the attention over no key, in either order."""
+    prob = inputs.tiny_config(seed=5)
+    q_all = O.decode(prob.q_abs, prob.act_dtype)
+    rows = O.selected_rows(prob, 0, np.arange(40))
+    o_e, l_e = O.sparse_mla_row(q_all[0], rows[:0], prob.scale)
+    assert o_e.shape == (prob.H, 512) and not o_e.any() and np.all(np.isneginf(l_e))
+    o_a, l_a = O.sparse_mla_row(q_all[0], rows, prob.scale)
+    assert np.array_equal(np.logaddexp(l_a, l_e), l_a)
+    for parts in ((o_a, o_e), (o_e, o_a)):
+        lse_parts = (l_a, l_e) if parts[0] is o_a else (l_e, l_a)
+        om, lm = O.attn_merge(np.stack(parts), np.stack(lse_parts))
+        assert np.allclose(om, o_a, rtol=1e-12, atol=0) and np.allclose(lm, l_a, rtol=1e-12, atol=0)
+    # a finite LSE for the empty part would not be the identity: the merge would move
+    om, lm = O.attn_merge(np.stack([o_a, o_e]), np.stack([l_a, np.zeros_like(l_a)]))
+    assert not np.allclose(lm, l_a, rtol=1e-6, atol=0)
+    # an index list of -1 only selects nothing
+    idx = np.full((prob.R, prob.k), -1, np.int32)
+    o_all, l_all = O.sparse_mla(prob, idx, rows=[0, 1])
+    assert not o_all.any() and np.all(np.isneginf(l_all))
