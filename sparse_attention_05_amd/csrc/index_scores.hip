@@ -179,15 +179,17 @@ __device__ __forceinline__ int64_t key_row(const IndexArgs& a, int64_t base, int
 // consumed). GLOADS loads in all.
 template <int QK, int DI>
 __device__ __forceinline__ void load_group(const IndexArgs& a, int64_t base, int64_t s0, int64_t s_end, char* dst,
-                                           uint32_t* sc_dst, int lane) {
+                                           uint32_t* sc_dst, int lane, int tile_beg = 0, int tile_end = 4) {
   using C = KeyCfg<QK, DI>;
   const char* keys = static_cast<const char*>(a.keys);
   const uint32_t to = lds_addr(dst);
   // the group's 64 keys are consecutive cache rows (a page holds whole groups)
   const int64_t g0 = key_row(a, base, s0);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // loads [tile_beg, tile_end) * LOADS/4: the rows of those 16-key tiles
 #pragma unroll
   for (int m = 0; m < C::LOADS; ++m) {
+    if (m < tile_beg * (C::LOADS / 4) || m >= tile_end * (C::LOADS / 4)) continue;
     const int pch = 64 * m + lane;      // physical chunk index in the group
     const int row = pch / C::CPR;
     const int lc = (pch % C::CPR) ^ (row & C::SWZ);
@@ -369,6 +371,11 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
   F qa[MT][NKS];
   float wr[MT][4];
   int issued = 0;
+  // One bf16 group per wave (the usual decode batch: each wave's keys fit
+  // one 64-key group): its four tiles go out two ahead, so the first tiles
+  // land early in the stream and their MFMA work overlaps the later tiles'
+  // transfer instead of all of it following the last load.
+  const bool roll = QK == 1 && groups == 1;
   if constexpr (kQLds) {
     // Query rows (H_I x DI bf16, chunks of row h XOR-permuted by h mod 8) and
     // the H_I weights go to LDS by direct loads, shared by the 4 waves; the
@@ -387,10 +394,18 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
     for (int i = threadIdx.x + qchunks; i < 16 * MT * QCPR; i += kWaves * 64)
       *reinterpret_cast<uint4*>(s_q + 16 * i) = uint4{0u, 0u, 0u, 0u};
     if (threadIdx.x >= a.H_I && threadIdx.x < 16 * MT) s_w[threadIdx.x] = 0.f;
-    // then all key stages, so the whole working set is in flight
-    for (; issued < C::NS && issued < groups; ++issued)
-      load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], s_sc[wave][issued], lane);
-    wait_groups<C::GLOADS>(issued);  // this wave's query and weight loads have landed
+    // then all key stages, so the whole working set is in flight; a wave
+    // with a single bf16 group starts with its first two 16-key tiles only
+    // and issues each later one as a tile lands (see below)
+    if (roll) {
+      load_group<QK, DI>(a, base, s_beg, s_end, smem[wave][0], s_sc[wave][0], lane, 0, 2);
+      issued = 1;
+      wait_vmcnt<2 * (C::LOADS / 4)>();  // this wave's query and weight loads have landed
+    } else {
+      for (; issued < C::NS && issued < groups; ++issued)
+        load_group<QK, DI>(a, base, s_beg + 64 * issued, s_end, smem[wave][issued], s_sc[wave][issued], lane);
+      wait_groups<C::GLOADS>(issued);  // this wave's query and weight loads have landed
+    }
     __syncthreads();
     // A operand: head 16*mt + col, dims 32*ks + 8*grp .. +8
 #pragma unroll
@@ -446,7 +461,7 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
       // the groups computed since it was issued
       const int behind = C::GLOADS * (issued - 1 - g) + spg * (g < C::NS ? g : C::NS);
       float part[4];
-      wait_ops<C::GLOADS * (C::NS - 1) + 2 * C::NS>(behind);  // group g landed
+      if (!roll) wait_ops<C::GLOADS * (C::NS - 1) + 2 * C::NS>(behind);  // group g landed
       // fp8: the row scale of the key in this lane's MFMA column for each
       // block, and of key s0 + lane (read before the stage is refilled)
       float scb[4] = {1.f, 1.f, 1.f, 1.f};
@@ -459,6 +474,15 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
       }
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
+        if (roll) {
+          // tile blk+2 goes out; tile blk has landed once only the tiles
+          // issued after it are outstanding (no store has been issued yet)
+          constexpr int LPT = C::LOADS / 4;
+          if (blk + 2 < 4) load_group<QK, DI>(a, base, s_beg, s_end, smem[wave][0], s_sc[wave][0], lane, blk + 2, blk + 3);
+          if (blk <= 1) wait_vmcnt<2 * LPT>();
+          else if (blk == 2) wait_vmcnt<LPT>();
+          else wait_vmcnt<0>();
+        }
         f32x4 acc[MT];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
