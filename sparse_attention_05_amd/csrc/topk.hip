@@ -482,7 +482,7 @@ __device__ __forceinline__ void bucket_pass(TopkShared& sh, const unsigned long 
   for (int j = 0; j < J; ++j) {
     const int i = t + j * kThreads;
     valid[j] = i < m;
-    w[j] = valid[j] ? src[off + i] : 0ull;
+    w[j] = valid[j] ? src[off + i] : mx;  // (unused slots: bucket 0, never placed)
     bk[j] = uint32_t((mx - w[j]) >> shift);
   }
   lds_barrier();
@@ -988,7 +988,8 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
 // t/tps (tps threads per slice), which covers the typical count. Issued apart
 // from the selection so that a caller can start them before other work.
 struct WindowLoads {
-  uint4 st;   // slice t's (count, largest candidate key, pivot, 0), t < slices
+  uint4 st;   // slice t's (count, largest candidate key, pivot, keys equal to it), t < slices;
+              // for slices <= 64, every wave holds the records (lane l: slice l)
   uint32_t own;  // the count of the slice whose words this thread holds
   unsigned long long x[kCap / kThreads];
 };
@@ -1004,7 +1005,8 @@ __device__ __forceinline__ void window_loads(const TopkArgs& a, int r, int slice
   const int64_t stride = int64_t(a.slice_tiles) * kTile;  // words per slice region
   const unsigned long long* cand = a.cand + int64_t(r) * slices * stride;
   const uint4* st = reinterpret_cast<const uint4*>(a.state) + int64_t(r) * slices;
-  L.st = t < slices ? st[t] : uint4{0u, 0u, 0u, 0u};
+  const int sr = slices <= 64 ? lane_id() : t;
+  L.st = sr < slices ? st[sr] : uint4{0u, 0u, 0u, 0u};
   const int tps = window_tps(slices);
   const int sg = t / tps, sl = t % tps;
   L.own = sg < slices ? st[sg].x : 0u;
@@ -1115,6 +1117,164 @@ __device__ __forceinline__ void window_ties(TopkShared& sh, const TopkArgs& a, i
              static_cast<unsigned long long>(kmin) << 32, lo, hi < int(G) ? hi : int(G), out, obase);
 }
 
+// LDS that window_select_fast expects zero on entry: the first pass's bucket
+// counts and fill counters and the dense-bucket count. Called before a
+// barrier that the caller runs anyway.
+__device__ __forceinline__ void window_fast_clear(TopkShared& sh) {
+  clear_bins(sh.cnt, kBins);
+  clear_bins(sh.fill, kBins);
+  if (threadIdx.x == 0) sh.misc[6] = 0u;
+}
+
+// window_select for the usual row, in four barriers and few instructions
+// (eight waves share four SIMDs, so each wave's instruction count is the
+// time): at most 64 slices, every candidate word already read ahead, and
+// k_eff <= C <= kCap. Each wave sums the slice records itself (DPP only, no
+// exchange); one bucket pass on 12 bits of (largest candidate - word) over
+// [pivot, largest candidate], on the keys alone (32-bit) when the digit lies
+// above the index bits; the words of the buckets that meet [lo, hi) are
+// placed into sh.u.wb, where they fill the contiguous range [s_lo, s_hi)
+// from the first such bucket's start to the last one's end, and that range
+// is ranked one word per thread (count of the larger words of its bucket);
+// dense buckets that meet the window go on to sort_levels. Expects
+// window_fast_clear's LDS zero (ordered by a barrier). Returns false, with
+// no LDS touched, when the row needs window_select.
+__device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArgs& a, int r, int slices, int n,
+                                                   int lo, int hi, int32_t* out, int obase, const WindowLoads& L) {
+  const int t = threadIdx.x;
+  const int k_eff = n < a.k ? n : a.k;
+  constexpr int J = kJ;
+  if (slices > 64) return false;
+  const int tps = window_tps(slices);
+  const int sg = t / tps, sl = t % tps;
+  const uint32_t C = wave_sum(L.st.x);
+  const uint32_t longest = wave_max(L.st.x), kmax = wave_max(L.st.y);
+  const uint32_t pivot = lane_value(L.st.z, 0);
+  if (C < uint32_t(k_eff) || C > uint32_t(kCap) || longest > uint32_t(J * tps)) return false;
+
+  const unsigned long long mx = (static_cast<unsigned long long>(kmax) << 32) | 0xFFFFFFFFull;
+  const unsigned long long mn = static_cast<unsigned long long>(pivot) << 32;
+  int shift, nb;
+  digit_plan(mn, mx, 12, shift, nb);  // nb <= kBins
+  // (mx - w) >> shift == (kmax - key) >> (shift - 32) when shift >= 32: the
+  // low halves (0xFFFFFFFF - ~index = index) never carry into the key half
+  const bool keys_only = shift >= 32;
+  const int ks = keys_only ? shift - 32 : 0;
+  auto bucket = [&](unsigned long long w) -> uint32_t {
+    return keys_only ? (kmax - uint32_t(w >> 32)) >> ks : uint32_t((mx - w) >> shift);
+  };
+  uint32_t bk[J];
+  bool valid[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    valid[j] = sg < slices && uint32_t(j * tps + sl) < L.own;
+    bk[j] = valid[j] ? bucket(L.x[j]) : 0u;  // (unused slots: bucket 0, never placed)
+    if (valid[j]) atomicAdd(&sh.cnt[bk[j]], 1u);
+  }
+  lds_barrier();
+  // bucket starts: thread t owns buckets 8t .. 8t+7 (unused ones are zero);
+  // the thread whose buckets hold rank lo (hi - 1) records where that
+  // bucket starts (ends): the placed range [s_lo, s_hi)
+  uint32_t c[8], st[8];
+  {
+    const uint4 x = *reinterpret_cast<const uint4*>(sh.cnt + 8 * t);
+    const uint4 y = *reinterpret_cast<const uint4*>(sh.cnt + 8 * t + 4);
+    c[0] = x.x; c[1] = x.y; c[2] = x.z; c[3] = x.w; c[4] = y.x; c[5] = y.y; c[6] = y.z; c[7] = y.w;
+  }
+  uint32_t tot = 0, cmax = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    tot += c[j];
+    cmax = max(cmax, c[j]);
+  }
+  {
+    const uint32_t xs = wave_incl_scan(tot);
+    if (lane_id() == 63) sh.red[wave_id()] = xs;
+    lds_barrier();
+    uint32_t base = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) base += w < wave_id() ? sh.red[w] : 0u;
+    st[0] = base + xs - tot;
+  }
+#pragma unroll
+  for (int j = 1; j < 8; ++j) st[j] = st[j - 1] + c[j - 1];
+  *reinterpret_cast<uint4*>(sh.bins + 8 * t) = uint4{st[0], st[1], st[2], st[3]};
+  *reinterpret_cast<uint4*>(sh.bins + 8 * t + 4) = uint4{st[4], st[5], st[6], st[7]};
+  const uint32_t t_end = st[0] + tot;
+  if (st[0] <= uint32_t(lo) && uint32_t(lo) < t_end) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (st[j] <= uint32_t(lo) && uint32_t(lo) < st[j] + c[j]) sh.misc[8] = st[j];
+  }
+  if (st[0] < uint32_t(hi) && uint32_t(hi) <= t_end) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (st[j] < uint32_t(hi) && uint32_t(hi) <= st[j] + c[j]) sh.misc[9] = st[j] + c[j];
+  }
+  if (cmax > uint32_t(kSmall)) {  // dense buckets that meet the window: listed for sort_levels
+    for (int j = 0; j < 8; ++j) {
+      if (c[j] > uint32_t(kSmall) && int(st[j]) < hi && int(st[j] + c[j]) > lo) {
+        const uint32_t slot = atomicAdd(&sh.misc[6], 1u);
+        if (slot < kMaxWork) {
+          const unsigned long long bmx = mx - (static_cast<unsigned long long>(8 * t + j) << shift);
+          const unsigned long long span = (1ull << shift) - 1ull;
+          const unsigned long long bmn = bmx - mn > span ? bmx - span : mn;
+          uint32_t* e = sh.work[1] + 6 * slot;
+          e[0] = st[j];
+          e[1] = c[j];
+          e[2] = uint32_t(bmx >> 32);
+          e[3] = uint32_t(bmx);
+          e[4] = uint32_t(bmn >> 32);
+          e[5] = uint32_t(bmn);
+        }
+      }
+    }
+  }
+  lds_barrier();
+  const int next = int(sh.misc[6]);
+  const uint32_t s_lo = sh.misc[8], s_hi = sh.misc[9];
+  // the words of the buckets that meet the window, placed at their bucket
+  // (slots that are not placed count on, and write to, spare words of their
+  // own, so every slot's atomic and store is issued without a branch)
+  uint32_t* spare_cnt = reinterpret_cast<uint32_t*>(sh.v.net) + t;
+  unsigned long long* spare_word = sh.v.net + kThreads + t;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t b0 = sh.bins[bk[j]], cb = sh.cnt[bk[j]];
+    const bool keep = valid[j] && b0 < uint32_t(hi) && b0 + cb > uint32_t(lo);
+    const uint32_t slot = atomicAdd(keep ? &sh.fill[bk[j]] : spare_cnt, 1u);
+    *(keep ? &sh.u.wb[b0 + slot] : spare_word) = L.x[j];
+  }
+  lds_barrier();
+  // rank of each placed word inside its (small) bucket
+  for (uint32_t p = s_lo + uint32_t(t); p < s_hi; p += kThreads) {
+    const unsigned long long w = sh.u.wb[p];
+    const uint32_t b = bucket(w);
+    const uint32_t b0 = sh.bins[b], cb = sh.cnt[b];
+    if (cb > uint32_t(kSmall)) continue;  // dense: sort_levels
+    uint32_t rk = 0;
+    for (uint32_t q0 = 0; q0 < cb; q0 += 4) {
+      unsigned long long y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = sh.u.wb[b0 + (q0 + u < cb ? q0 + u : 0u)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rk += (q0 + u < cb) & (y[u] > w);
+    }
+    const int at = int(b0 + rk);
+    if (at >= lo && at < hi) out[at - obase] = word_idx(w);
+  }
+  if (next == 0) return true;
+  if (next > kMaxWork) {
+    const uint4 rec = t < slices ? L.st : uint4{0u, 0u, 0u, 0u};
+    const uint32_t at = wave_incl_scan(rec.x) - rec.x;  // slice t's offset (t < slices <= 64)
+    lds_barrier();  // the ranking above still reads sh.bins and sh.cnt, which the gather rewrites
+    window_gather_sort(sh, a, r, slices, C, at, longest, lo, hi, out, obase, L);
+    return true;
+  }
+  sort_levels(sh, sh.u.wb, sh.wa, 1, next, 1, lo, hi, out, obase);
+  return true;
+}
+
 // Ranks [lo, hi) of row r (hi <= min(n, k)) from the candidates of the
 // slices, indices to out[rank - obase]; a tie class too large for the
 // candidate capacity at the k-th rank goes to window_ties; when fewer than k
@@ -1142,10 +1302,11 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
   // one exchange: slice offsets and the total (scan of the counts), the
   // largest candidate key, the longest slice, the pivot, and the same scan
   // of the counts of keys equal to the pivot
-  const uint32_t cnt = L.st.x, ecnt = L.st.w;
+  const uint4 st = t < slices ? L.st : uint4{0u, 0u, 0u, 0u};  // (other waves may hold copies)
+  const uint32_t cnt = st.x, ecnt = st.w;
   const uint32_t xs = wave_incl_scan(cnt), xe = wave_incl_scan(ecnt);
   {
-    const uint32_t wm = wave_max(L.st.y), wc = wave_max(cnt);
+    const uint32_t wm = wave_max(st.y), wc = wave_max(cnt);
     if (lane_id() == 63) {
       sh.red[wave_id()] = xs;
       sh.red[4 * kWaves + wave_id()] = xe;
@@ -1154,7 +1315,7 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
       sh.red[kWaves + wave_id()] = wm;
       sh.red[2 * kWaves + wave_id()] = wc;
     }
-    if (t == 0) sh.red[3 * kWaves] = L.st.z;
+    if (t == 0) sh.red[3 * kWaves] = st.z;
     lds_barrier();
   }
   uint32_t C = 0, base = 0, kmax = 0, longest = 0, E = 0, ebase = 0;
@@ -1195,7 +1356,7 @@ __device__ __forceinline__ void window_select(TopkShared& sh, const TopkArgs& a,
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     valid[j] = sg < slices && uint32_t(j * tps + sl) < L.own;
-    bk[j] = uint32_t((mx - L.x[j]) >> shift);
+    bk[j] = valid[j] ? uint32_t((mx - L.x[j]) >> shift) : 0u;  // (unused slots: bucket 0, never placed)
     if (valid[j]) atomicAdd(&sh.cnt[bk[j]], 1u);
   }
   lds_barrier();
@@ -1223,7 +1384,9 @@ __global__ __launch_bounds__(kThreads) void topk_window_kernel(TopkArgs a, int s
   if (lo >= hi) return;
   WindowLoads L;
   window_loads(a, r, slices, L);
-  window_select(sh, a, r, slices, n, lo, hi, out, 0, L);
+  window_fast_clear(sh);
+  lds_barrier();
+  if (!window_select_fast(sh, a, r, slices, n, lo, hi, out, 0, L)) window_select(sh, a, r, slices, n, lo, hi, out, 0, L);
 }
 
 // Decode with selection and attention fused: the workgroup of (query r, key
@@ -1263,9 +1426,11 @@ __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnAr
   // ranks past k_eff, and the attention's chunk tail past j_end, stay -1
   const int span = (j_end - j_beg + attn::kChunkKeys - 1) / attn::kChunkKeys * attn::kChunkKeys;
   for (int i = t; i < span; i += kThreads) s_idx[i] = -1;
+  window_fast_clear(u.sel);
   lds_barrier();
   const int hi = j_end < k_eff ? j_end : k_eff;
-  if (j_beg < hi) window_select(u.sel, ta, r, slices, n, j_beg, hi, s_idx, j_beg, L);
+  if (j_beg < hi && !window_select_fast(u.sel, ta, r, slices, n, j_beg, hi, s_idx, j_beg, L))
+    window_select(u.sel, ta, r, slices, n, j_beg, hi, s_idx, j_beg, L);
   lds_barrier();  // the split's indices are in LDS; the selection's LDS is free
   if (hg == 0)
     for (int i = t; i < j_end - j_beg; i += kThreads) ta.idx[int64_t(r) * k + j_beg + i] = s_idx[i];
