@@ -1132,11 +1132,15 @@ __device__ __forceinline__ void window_fast_clear(TopkShared& sh) {
 // k_eff <= C <= kCap. Each wave sums the slice records itself (DPP only, no
 // exchange); one bucket pass on 12 bits of (largest candidate - word) over
 // [pivot, largest candidate], on the keys alone (32-bit) when the digit lies
-// above the index bits; the words of the buckets that meet [lo, hi) are
-// placed into sh.u.wb, where they fill the contiguous range [s_lo, s_hi)
-// from the first such bucket's start to the last one's end, and that range
-// is ranked one word per thread (count of the larger words of its bucket);
-// dense buckets that meet the window go on to sort_levels. Expects
+// above the index bits. The buckets that meet [lo, hi) are the index range
+// [b_lo, b_hi] (those holding ranks lo and hi - 1 and all between), so a
+// word's bucket number alone decides whether it is placed; placed words fill
+// the contiguous range [s_lo, s_hi) of sh.u.wb (the first such bucket's
+// start to the last one's end), each beside its bucket's start and count in
+// sh.v.samp, and that range is ranked one word per thread (count of the
+// larger words of its bucket). Every LDS access of a phase is issued before
+// the first wait. Dense buckets that meet the window go on to sort_levels.
+// Expects
 // window_fast_clear's LDS zero (ordered by a barrier). Returns false, with
 // no LDS touched, when the row needs window_select.
 __device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArgs& a, int r, int slices, int n,
@@ -1173,8 +1177,8 @@ __device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArg
   }
   lds_barrier();
   // bucket starts: thread t owns buckets 8t .. 8t+7 (unused ones are zero);
-  // the thread whose buckets hold rank lo (hi - 1) records where that
-  // bucket starts (ends): the placed range [s_lo, s_hi)
+  // the thread whose buckets hold rank lo (hi - 1) records that bucket and
+  // where it starts (ends): the placed range
   uint32_t c[8], st[8];
   {
     const uint4 x = *reinterpret_cast<const uint4*>(sh.cnt + 8 * t);
@@ -1204,12 +1208,18 @@ __device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArg
   if (st[0] <= uint32_t(lo) && uint32_t(lo) < t_end) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (st[j] <= uint32_t(lo) && uint32_t(lo) < st[j] + c[j]) sh.misc[8] = st[j];
+      if (st[j] <= uint32_t(lo) && uint32_t(lo) < st[j] + c[j]) {
+        sh.misc[8] = st[j];
+        sh.misc[10] = 8 * t + j;
+      }
   }
   if (st[0] < uint32_t(hi) && uint32_t(hi) <= t_end) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (st[j] < uint32_t(hi) && uint32_t(hi) <= st[j] + c[j]) sh.misc[9] = st[j] + c[j];
+      if (st[j] < uint32_t(hi) && uint32_t(hi) <= st[j] + c[j]) {
+        sh.misc[9] = st[j] + c[j];
+        sh.misc[11] = 8 * t + j;
+      }
   }
   if (cmax > uint32_t(kSmall)) {  // dense buckets that meet the window: listed for sort_levels
     for (int j = 0; j < 8; ++j) {
@@ -1232,35 +1242,43 @@ __device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArg
   }
   lds_barrier();
   const int next = int(sh.misc[6]);
-  const uint32_t s_lo = sh.misc[8], s_hi = sh.misc[9];
+  const uint32_t s_lo = sh.misc[8], s_hi = sh.misc[9], b_lo = sh.misc[10], b_hi = sh.misc[11];
   // the words of the buckets that meet the window, placed at their bucket
-  // (slots that are not placed count on, and write to, spare words of their
-  // own, so every slot's atomic and store is issued without a branch)
-  uint32_t* spare_cnt = reinterpret_cast<uint32_t*>(sh.v.net) + t;
-  unsigned long long* spare_word = sh.v.net + kThreads + t;
+  bool keep[J];
+  uint32_t b0[J], cb[J], slot[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) keep[j] = valid[j] && bk[j] >= b_lo && bk[j] <= b_hi;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const uint32_t b0 = sh.bins[bk[j]], cb = sh.cnt[bk[j]];
-    const bool keep = valid[j] && b0 < uint32_t(hi) && b0 + cb > uint32_t(lo);
-    const uint32_t slot = atomicAdd(keep ? &sh.fill[bk[j]] : spare_cnt, 1u);
-    *(keep ? &sh.u.wb[b0 + slot] : spare_word) = L.x[j];
+    if (keep[j]) {
+      b0[j] = sh.bins[bk[j]];
+      cb[j] = sh.cnt[bk[j]];
+      slot[j] = atomicAdd(&sh.fill[bk[j]], 1u);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (keep[j]) {
+      sh.u.wb[b0[j] + slot[j]] = L.x[j];
+      sh.v.samp[b0[j] + slot[j]] = b0[j] | (cb[j] << 16);  // (both <= kCap < 2^16)
+    }
   }
   lds_barrier();
   // rank of each placed word inside its (small) bucket
   for (uint32_t p = s_lo + uint32_t(t); p < s_hi; p += kThreads) {
     const unsigned long long w = sh.u.wb[p];
-    const uint32_t b = bucket(w);
-    const uint32_t b0 = sh.bins[b], cb = sh.cnt[b];
-    if (cb > uint32_t(kSmall)) continue;  // dense: sort_levels
+    const uint32_t m = sh.v.samp[p];
+    const uint32_t wb0 = m & 0xFFFFu, wcb = m >> 16;
+    if (wcb > uint32_t(kSmall)) continue;  // dense: sort_levels
     uint32_t rk = 0;
-    for (uint32_t q0 = 0; q0 < cb; q0 += 4) {
+    for (uint32_t q0 = 0; q0 < wcb; q0 += 4) {
       unsigned long long y[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) y[u] = sh.u.wb[b0 + (q0 + u < cb ? q0 + u : 0u)];
+      for (int u = 0; u < 4; ++u) y[u] = sh.u.wb[wb0 + (q0 + u < wcb ? q0 + u : 0u)];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) rk += (q0 + u < cb) & (y[u] > w);
+      for (int u = 0; u < 4; ++u) rk += (q0 + u < wcb) & (y[u] > w);
     }
-    const int at = int(b0 + rk);
+    const int at = int(wb0 + rk);
     if (at >= lo && at < hi) out[at - obase] = word_idx(w);
   }
   if (next == 0) return true;
