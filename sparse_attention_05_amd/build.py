@@ -29,6 +29,11 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# Per-source additions. The attention kernels keep MFMA results in vector
+# registers: the compiler otherwise puts them beside the query fragments in
+# the accumulation registers, and the 8-wave prefill kernel (256 registers
+# per wave) then spills inside its chunk loop.
+EXTRA = {"sparse_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -53,9 +58,10 @@ def build(asm: bool = False, verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        flags = FLAGS + EXTRA.get(src, [])
+        jobs.append([hipcc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
         if asm:
-            jobs.append([hipcc, *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src),
+            jobs.append([hipcc, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, src),
                          "-o", os.path.join(BUILD, src.replace(".hip", f"-{ARCH}.s"))])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         for out in ex.map(_run, jobs):

@@ -115,37 +115,48 @@ __global__ __launch_bounds__(kAttnWaves8 * 64) void sparse_mla_bf16_kernel(AttnA
 
 // ---- many queries: one workgroup per query for all (<= 64) heads ---------------------
 // With a workgroup per (query, 16 heads) every selected latent row would be
-// gathered once per head group; here the 4 waves of one workgroup share each
+// gathered once per head group; here the 8 waves of one workgroup share each
 // gathered chunk of 64 rows among all 64 heads, so a row is read once per
-// query. Per chunk:
-//  * q.c split by head: wave w forms S^T for heads 16w .. 16w+15 over the 64
-//    keys (its query fragments stay in registers), so each head's maximum
-//    and sum stay within one wave; the maxima go through LDS to the p.c;
+// query. Eight waves, two per SIMD, so that each SIMD has a second
+// instruction stream to issue while the other waits (with one wave per SIMD
+// the matrix cores sat idle three quarters of the time: the softmax, the
+// LDS reads and the barriers were all exposed). Wave w = 4*kh + hg:
+//  * q.c by (key half, head group): S^T for keys 32kh .. 32kh+31 and heads
+//    16hg .. 16hg+15 (the query fragments of those heads stay in registers);
+//    each head's chunk maximum combines its two key halves through LDS;
 //  * P^T (bf16) is written into the rope part (bytes 1024..1151) of the
 //    chunk's rows, free once q.c is done: head h's 64 probabilities go to
 //    row h, so no extra LDS is needed;
-//  * p.c split by value dimension as in the 16-head kernel: wave w forms
-//    O^T[128w .. 128w+127][all heads], each transposed value fragment feeding
-//    the 4 head tiles.
+//  * p.c by value slice: wave w forms O^T[64w .. 64w+63][all heads], each
+//    transposed value fragment feeding the 4 head tiles.
 // Rows go from HBM to LDS with direct loads issued from inline assembly and
-// waited for exactly, so the gather of chunk c+1 overlaps chunk c. Chunks
-// past the last selected position are skipped (they would add exactly 0).
+// waited for exactly, so the gather of chunk c+1 overlaps chunk c: the two
+// waves of head group hg each issue half of the loads of rows
+// 16hg .. 16hg+15. Chunks past the last selected position are skipped (they
+// would add exactly 0).
 constexpr int kWideHeads = 64;
+constexpr int kWideThreads = 512;
 
 // LDS layout of a chunk (64 rows x 72 chunks of 16 bytes): wave w's rows
 // 16w .. 16w+15 form a block of 18,432 bytes in which chunk c of row p sits
-// at 1024*(c/4) + 64*p + 16*(c%4). The direct load m of a wave then covers
-// chunks 4m .. 4m+3 of all 16 rows: lane l always reads row l/4 (at 16-byte
+// at 1024*(c/4) + 64*p + 16*((c%4) ^ sw(p)), sw(p) = 2*((p/4)%2): rows 4..7
+// and 12..15 of a block hold their chunk pairs swapped, which spreads the
+// q.c reads (row per lane, a 64-byte stride), the transposed p.c reads and
+// the P^T writes over all LDS banks (without it each pass of these reads
+// met every bank twice, as the bank-conflict counter showed). The direct
+// load m of a wave then covers chunks 4m .. 4m+3 of all 16 rows: lane l
+// always reads row l/4 (its chunk 4m + ((l%4) ^ sw(l/4)) lands at 16-byte
 // offset 4m + l%4), so a gather needs one address per lane.
 constexpr int kWideBlock = 16 * 1152;
+__device__ __forceinline__ int wide_sw(int row) { return 2 * ((row >> 2) & 1); }
 __device__ __forceinline__ int wide_off(int row, int c) {
-  return kWideBlock * (row >> 4) + 1024 * (c >> 2) + 64 * (row & 15) + 16 * (c & 3);
+  return kWideBlock * (row >> 4) + 1024 * (c >> 2) + 64 * (row & 15) + 16 * ((c & 3) ^ wide_sw(row));
 }
 
-// The gather of rows 16*wave .. +15 of chunk c (raw indices in s_idx) into
+// The gather of rows 16*blk .. +15 of chunk c (raw indices in s_idx) into
 // buf: this lane's source row (a missing row reads cache row 0 and is
-// zero-filled once it has landed), the LDS base of the wave's block and the
-// 16-bit mask of present rows; load m (0..17) is then dma16(src + 64m,
+// zero-filled once it has landed), the LDS base of the block and the 16-bit
+// mask of present rows; load m (0..17) is then dma16(src + 64m,
 // lds + 1024m).
 struct WideGather {
   const char* src;
@@ -153,18 +164,18 @@ struct WideGather {
   uint32_t mask;
 };
 __device__ __forceinline__ WideGather wide_gather(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
-                                                  int wave, int lane) {
+                                                  int blk, int lane) {
   using Cfg = AttnCfg<false>;
   int64_t row;
-  const bool ok = attn_row(a, base, s_idx[kChunkKeys * c + 16 * wave + (lane >> 2)], row);
+  const bool ok = attn_row(a, base, s_idx[kChunkKeys * c + 16 * blk + (lane >> 2)], row);
   const unsigned long long okm = __ballot(ok && (lane & 3) == 0);  // bit 4i: row i
   uint32_t mask = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mask |= uint32_t((okm >> (4 * i)) & 1ull) << i;
   WideGather g;
-  g.src = static_cast<const char*>(a.latent) + row * Cfg::ROW_BYTES + 16 * (lane & 3);
+  g.src = static_cast<const char*>(a.latent) + row * Cfg::ROW_BYTES + 16 * ((lane & 3) ^ wide_sw(lane >> 2));
   g.lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(buf + kWideBlock * wave))));
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(buf + kWideBlock * blk))));
   g.mask = mask;
   return g;
 }
@@ -175,45 +186,53 @@ __device__ __forceinline__ WideGather wide_gather(const AttnArgs& a, int64_t bas
 // (exact in bf16's range, summed in fp32) and the 128-register rescale is
 // rare. The softmax stays exact: sums and outputs use the same reference,
 // the LSE adds it back.
+// 2^x by the hardware's exponential (one instruction): results below 2^-126
+// flush to 0, which only drops terms that cannot move a softmax sum whose
+// largest term is >= 1, and -inf gives 0 as the softmax needs.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float wide_ref_max(float m_run, float cmax) {
   return (m_run == -INFINITY || cmax > m_run + 8.f) ? fmaxf(m_run, cmax) : m_run;
 }
 
-__global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs a, int kps) {
+__global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs a, int kps) {
   using Cfg = AttnCfg<false>;
-  constexpr int WL = Cfg::WAVE_LOADS;  // direct loads per wave per chunk
-  static_assert(WL == 18, "one direct load of the next chunk per K-step of q.c");
+  constexpr int WL = Cfg::WAVE_LOADS;  // direct loads per 16-row block per chunk
+  static_assert(WL == 18, "18 direct loads cover a 16-row block");
+  constexpr int WLH = WL / 2;          // each of the block's two waves issues half
   __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::BUF_BYTES];
   __shared__ int s_idx[kMaxTopk];
-  __shared__ float s_max[kWideHeads];
-  __shared__ float s_l[kWideHeads];
+  __shared__ float s_max[2][kWideHeads];  // chunk maximum of each head, per key half
+  __shared__ float s_l[2][kWideHeads];
   __shared__ uint32_t s_ok[2][4];
-  __shared__ int s_last[4];
+  __shared__ int s_last[8];
   const int r = int(gridDim.x) - 1 - int(blockIdx.x);  // later queries (more keys) first
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int lane = t & 63;
   const int col = lane & 15, grp = lane >> 4;
+  const int hg = wave & 3;   // q.c heads 16hg .. 16hg+15; gathered rows 16hg .. 16hg+15
+  const int kh = wave >> 2;  // q.c keys 32kh .. 32kh+31; loads WLH*kh .. +WLH of the block
   const int64_t base = seq_base(a, r);
   const int j_end = kps < a.k ? kps : a.k;  // one split: keys 0 .. j_end-1
 
   // the range's indices; the last selected position bounds the chunks walked
   int last = -1;
-  for (int e = t; e < j_end; e += kAttnThreads) {
+  for (int e = t; e < j_end; e += kWideThreads) {
     const int v = a.idx[int64_t(r) * a.k + e];
     s_idx[e] = v;
     last = v >= 0 ? e : last;
   }
   const int span = (j_end + kChunkKeys - 1) / kChunkKeys * kChunkKeys;
-  for (int e = j_end + t; e < span; e += kAttnThreads) s_idx[e] = -1;
+  for (int e = j_end + t; e < span; e += kWideThreads) s_idx[e] = -1;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) last = max(last, __shfl_xor(last, d, 64));
   if (lane == 0) s_last[wave] = last;
 
-  // query fragments of this wave's q.c head 16*wave + col (zero past H)
+  // query fragments of this wave's q.c head 16*hg + col (zero past H)
   bf16x8 qf[18];
   {
-    const int h = 16 * wave + col;
+    const int h = 16 * hg + col;
     const bool hv = h < a.H;
     const int64_t qoff = (int64_t(r) * a.H + (hv ? h : 0)) * kLatentDim + 8 * grp;
 #pragma unroll
@@ -235,108 +254,121 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
     qf[ks] = __builtin_bit_cast(bf16x8, u);
   }
   __syncthreads();
-  const int nchunks = (max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])) + kChunkKeys) / kChunkKeys;
+  int lmax = s_last[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) lmax = max(lmax, s_last[w]);
+  const int nchunks = (lmax + kChunkKeys) / kChunkKeys;
 
   // chunk 0 now; chunk c+1 is issued during the q.c of chunk c, one direct
   // load per K-step, once every wave is done with the buffer (chunk c-1's)
   uint32_t okw[2] = {0u, 0u};
   if (nchunks > 0) {
-    const WideGather g = wide_gather(a, base, s_idx, 0, smem, wave, lane);
+    const WideGather g = wide_gather(a, base, s_idx, 0, smem, hg, lane);
 #pragma unroll
-    for (int m = 0; m < WL; ++m) dma16(g.src + 64 * m, g.lds + 1024 * m);
+    for (int m = WLH * kh; m < WLH * kh + WLH; ++m) dma16(g.src + 64 * m, g.lds + 1024 * m);
     okw[0] = g.mask;
   }
 
-  f32x4 acc[8][4];
+  f32x4 acc[4][4];  // O^T[64*wave + 16*vt + (0..15)][16*ht + (0..15)]
 #pragma unroll
-  for (int vt = 0; vt < 8; ++vt)
+  for (int vt = 0; vt < 4; ++vt)
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) acc[vt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mq = -INFINITY;  // running max of the q.c head 16*wave + col
-  float lq = 0.f;        // this lane's share of its running sum
+  float mq = -INFINITY;  // running reference max of the q.c head 16*hg + col
+  float lq = 0.f;        // this lane's share of its running sum (this key half)
   float mo[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // of the p.c heads 16ht + col
   const float scale2 = a.scale * kLog2e;
 
   for (int c = 0; c < nchunks; ++c) {
     const int bi = c & 1;
     char* buf = smem + bi * Cfg::BUF_BYTES;
-    // this wave's rows of chunk c have landed (nothing else is in flight);
-    // rows of missing keys are zeroed; then every wave's are
+    // this wave's loads of chunk c have landed (nothing else is in flight);
+    // the parts of missing rows it loaded are zeroed; then every wave's are
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (okw[bi] != 0xFFFFu) {
-      for (int q = lane; q < 16 * Cfg::ROW_CHUNKS; q += 64) {
-        const int rr = q / Cfg::ROW_CHUNKS, cc = q % Cfg::ROW_CHUNKS;
-        if (!((okw[bi] >> rr) & 1u)) *reinterpret_cast<uint4*>(buf + wide_off(16 * wave + rr, cc)) = uint4{0u, 0u, 0u, 0u};
+      for (int q = lane; q < 16 * 4 * WLH; q += 64) {
+        const int rr = q / (4 * WLH), cc = 4 * WLH * kh + q % (4 * WLH);
+        if (!((okw[bi] >> rr) & 1u)) *reinterpret_cast<uint4*>(buf + wide_off(16 * hg + rr, cc)) = uint4{0u, 0u, 0u, 0u};
       }
     }
-    if (lane == 0) s_ok[bi][wave] = okw[bi];
+    if (lane == 0 && kh == 0) s_ok[bi][hg] = okw[bi];
     __syncthreads();
     const bool more = c + 1 < nchunks;
     WideGather gn{nullptr, 0u, 0u};
-    if (more) gn = wide_gather(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, wave, lane);
+    if (more) gn = wide_gather(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, hg, lane);
 
-    // ---- q.c: S^T for keys 16kt + (0..15), heads 16*wave + (0..15) --------------------
-    // (the key fragments of K-step ks+1 are read while the MFMAs of ks run:
-    // one wave per SIMD has no other wave to hide the LDS latency)
-    f32x4 sc[4];
+    // ---- q.c: S^T for keys 32kh + 16kt + (0..15), heads 16*hg + (0..15) ------------------
+    // (the key fragments are read two K-steps ahead of their MFMAs; the
+    // loop is instantiated with and without the next chunk's loads, so that
+    // no branch splits it)
+    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    auto qc = [&](auto load_next) {
+      constexpr bool LOADS = decltype(load_next)::value;
+      // key row 16(2kh+kt) + col, dims 32ks + 8grp .. +8: chunk 4ks + grp
+      const char* fbase = buf + kWideBlock * (2 * kh) + 64 * col + 16 * (grp ^ wide_sw(col));
+      constexpr int AH = 3;  // K-steps of key fragments in flight
+      bf16x8 fa[AH][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) sc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      // key row 16kt + col, dims 32ks + 8grp .. +8: chunk 4ks + grp, one contiguous KiB per read
-      const char* fbase = buf + 64 * col + 16 * grp;
-      bf16x8 fa[2][4];
+      for (int j = 0; j < AH - 1; ++j)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) fa[0][kt] = *reinterpret_cast<const bf16x8*>(fbase + kWideBlock * kt);
-      __builtin_amdgcn_sched_barrier(0);  // the pattern below starts with the reads of K-step 1
+        for (int kt = 0; kt < 2; ++kt) fa[j][kt] = *reinterpret_cast<const bf16x8*>(fbase + kWideBlock * kt + 1024 * j);
+      __builtin_amdgcn_sched_barrier(0);  // the pattern below starts with the reads of K-step AH-1
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        if (ks + 1 < 18) {
+        if (ks + AH - 1 < 18) {
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-            fa[(ks + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(fbase + kWideBlock * kt + 1024 * (ks + 1));
+          for (int kt = 0; kt < 2; ++kt)
+            fa[(ks + AH - 1) % AH][kt] =
+                *reinterpret_cast<const bf16x8*>(fbase + kWideBlock * kt + 1024 * (ks + AH - 1));
         }
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) sc[kt] = mfma_k32(fa[ks & 1][kt], qf[ks], sc[kt]);
-        if (more) dma16(gn.src + 64 * ks, gn.lds + 1024 * ks);  // load ks of chunk c+1
-        if (ks + 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        for (int kt = 0; kt < 2; ++kt) sc[kt] = mfma_k32(fa[ks % AH][kt], qf[ks], sc[kt]);
+        if (LOADS && ks < WLH) dma16(gn.src + 64 * (WLH * kh + ks), gn.lds + 1024 * (WLH * kh + ks));
+        if (ks + AH - 1 < 18) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
-    }
-    // logits (log2 domain), -inf for missing keys; the head's maximum over the chunk
-    float x[4][4];
+    };
+    if (more) qc(std::true_type{});
+    else qc(std::false_type{});
+    // logits (log2 domain), -inf for missing keys (16-key tiles with a
+    // missing key only); the head's maximum over this key half
+    float x[2][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const uint32_t okt = s_ok[bi][kt];
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint32_t okt = s_ok[bi][2 * kh + kt];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[kt][i] = ((okt >> (4 * grp + i)) & 1u) ? sc[kt][i] * scale2 : -INFINITY;
-        mx = fmaxf(mx, x[kt][i]);
+      for (int i = 0; i < 4; ++i) x[kt][i] = sc[kt][i] * scale2;
+      if (okt != 0xFFFFu) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[kt][i] = ((okt >> (4 * grp + i)) & 1u) ? x[kt][i] : -INFINITY;
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
     }
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    if (grp == 0) s_max[16 * wave + col] = mx;
+    if (grp == 0) s_max[kh][16 * hg + col] = mx;
     __syncthreads();  // maxima visible; every wave is done with q.c of chunk c (its rope parts are free)
     okw[bi ^ 1] = gn.mask;
 
-    // ---- softmax of this wave's heads: P^T into the rope part of row h -----------------
+    // ---- softmax of this wave's heads and keys: P^T into the rope part of row h ---------
     {
-      const int h = 16 * wave + col;
-      const float m_new = wide_ref_max(mq, mx);
+      const int h = 16 * hg + col;
+      const float m_new = wide_ref_max(mq, fmaxf(s_max[0][h], s_max[1][h]));
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(mq - m_use);
+      const float alpha = fast_exp2(mq - m_use);
       float psum = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < 2; ++kt) {
         __bf16 pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = static_cast<__bf16>(exp2f(x[kt][i] - m_use));
+          pv[i] = static_cast<__bf16>(fast_exp2(x[kt][i] - m_use));
           psum += static_cast<float>(pv[i]);
         }
-        // keys 16kt + 4grp .. +3 of head h: rope chunk 64 + 2kt + grp/2 of row h, half grp&1
-        const int ch = 64 + 2 * kt + (grp >> 1);
+        // keys 16(2kh+kt) + 4grp .. +3 of head h: rope chunk 64 + 2(2kh+kt) + grp/2 of row h, half grp&1
+        const int ch = 64 + 2 * (2 * kh + kt) + (grp >> 1);
         const uint32_t w0 = uint32_t(__builtin_bit_cast(uint16_t, pv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[1])) << 16);
         const uint32_t w1 = uint32_t(__builtin_bit_cast(uint16_t, pv[2])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[3])) << 16);
         *reinterpret_cast<uint2*>(buf + wide_off(h, ch) + 8 * (grp & 1)) = uint2{w0, w1};
@@ -347,19 +379,19 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
     // rescale of the p.c accumulators by the same per-head alpha
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
-      const float cmax = s_max[16 * ht + col];
+      const float cmax = fmaxf(s_max[0][16 * ht + col], s_max[1][16 * ht + col]);
       const float m_new = wide_ref_max(mo[ht], cmax);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(mo[ht] - m_use);
+      const float alpha = fast_exp2(mo[ht] - m_use);
       mo[ht] = m_new;
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int vt = 0; vt < 8; ++vt) acc[vt][ht] *= alpha;
+        for (int vt = 0; vt < 4; ++vt) acc[vt][ht] *= alpha;
       }
     }
     __syncthreads();  // P^T of all heads in LDS
 
-    // ---- O^T[128*wave + 16*vt + (0..15)][16*ht + (0..15)] += C^T . P^T ---------------
+    // ---- O^T[64*wave + 16*vt + (0..15)][16*ht + (0..15)] += C^T . P^T ---------------
     {
       const int tr_row = 4 * grp + (col >> 2);
       // P^T of head 16ht + col for both K-steps: keys kb + 4grp .. +3 and kb + 16 + 4grp .. +3
@@ -373,13 +405,13 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
           const uint2 phi = *reinterpret_cast<const uint2*>(buf + wide_off(h, 64 + kb / 8 + 2 + (grp >> 1)) + 8 * (grp & 1));
           pf[kq][ht] = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
         }
-      // transposed value fragment of step q = (kq, vt), read one step ahead
+      // transposed value fragment of step q = (kq, vt), read one step ahead:
       // lane (col, grp) names key row 32kq + tr_row (+16 for the second
-      // read), value dims 128*wave + 16vt + 4(col%4) .. +3: chunk
-      // 16*wave + 2vt + (col%4)/2, half (col%4)&1
+      // read), value dims 64*wave + 16vt + 4(col%4) .. +3: chunk
+      // 8*wave + 2vt + (col%4)/2, half (col%4)&1
       auto vfrag = [&](int q) -> bf16x8 {
-        const int kq = q >> 3, vt = q & 7;
-        const char* p0 = buf + wide_off(32 * kq + tr_row, 16 * wave + 2 * vt + ((col & 3) >> 1)) + 8 * (col & 1);
+        const int kq = q >> 2, vt = q & 3;
+        const char* p0 = buf + wide_off(32 * kq + tr_row, 8 * wave + 2 * vt + ((col & 3) >> 1)) + 8 * (col & 1);
         const short4v t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(lds_ptr)p0);
         const short4v t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + kWideBlock));
@@ -389,34 +421,34 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_wide_kernel(AttnArgs 
       vf[0] = vfrag(0);
       __builtin_amdgcn_sched_barrier(0);  // the pattern below starts with the reads of step 1
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        if (q + 1 < 16) vf[(q + 1) & 1] = vfrag(q + 1);
+      for (int q = 0; q < 8; ++q) {
+        if (q + 1 < 8) vf[(q + 1) & 1] = vfrag(q + 1);
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) acc[q & 7][ht] = mfma_k32(vf[q & 1], pf[q >> 3][ht], acc[q & 7][ht]);
-        if (q + 1 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int ht = 0; ht < 4; ++ht) acc[q & 3][ht] = mfma_k32(vf[q & 1], pf[q >> 2][ht], acc[q & 3][ht]);
+        if (q + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
     }
   }
 
-  // ---- epilogue: row sums of each head, then O rows ----------------------------------------
+  // ---- epilogue: row sums of each head (both key halves), then O rows --------------------
   {
     float l = lq + wave_shfl_xor(lq, 16);
     l += wave_shfl_xor(l, 32);
-    if (grp == 0) s_l[16 * wave + col] = l;
+    if (grp == 0) s_l[kh][16 * hg + col] = l;
   }
   __syncthreads();
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
     const int h = 16 * ht + col;
     if (h >= a.H) continue;
-    const float L = s_l[h];
+    const float L = s_l[0][h] + s_l[1][h];
     const float inv = L > 0.f ? 1.f / L : 0.f;
     const int64_t rh = int64_t(r) * a.H + h;
     float* dst = a.out + rh * kValueDim;
 #pragma unroll
-    for (int vt = 0; vt < 8; ++vt)
-      *reinterpret_cast<float4*>(dst + 128 * wave + 16 * vt + 4 * grp) =
+    for (int vt = 0; vt < 4; ++vt)
+      *reinterpret_cast<float4*>(dst + 64 * wave + 16 * vt + 4 * grp) =
           float4{acc[vt][ht][0] * inv, acc[vt][ht][1] * inv, acc[vt][ht][2] * inv, acc[vt][ht][3] * inv};
     if (wave == 0 && grp == 0 && a.lse) a.lse[rh] = L > 0.f ? (mo[ht] + __log2f(L)) * kLn2 : -INFINITY;
   }
@@ -524,7 +556,7 @@ AttnPlan plan_attention(int R, int H, int k) {
 hipError_t launch_sparse_mla(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream) {
   if (a.R == 0) return hipSuccess;
   if (plan.wide && a.dtype == kBF16 && a.latent_dtype == kBF16) {
-    sparse_mla_wide_kernel<<<dim3(unsigned(a.R)), kAttnThreads, 0, stream>>>(a, plan.keys_per_split);
+    sparse_mla_wide_kernel<<<dim3(unsigned(a.R)), kWideThreads, 0, stream>>>(a, plan.keys_per_split);
     return hipGetLastError();
   }
   const dim3 grid(unsigned(a.R) * unsigned(plan.splits) * unsigned(plan.head_groups));
