@@ -141,15 +141,17 @@ __device__ __forceinline__ void gather_load(const AttnArgs& a, const Gather& g, 
   if ((g.ok >> rl) & 1u) __builtin_amdgcn_global_load_lds(src, (lds_ptr)(g.wbuf + 1024 * m), 16, 0, 0);
 }
 
-// bf16 chunks use the block layout instead: wave w's rows 16w .. 16w+15 form
-// a block of 18,432 bytes in which 16-byte piece p of row i sits at
-// 1024*(p/4) + 64*i + 16*(p%4) (blk_off). Lane l then always loads row
-// 16w + l/4, pieces 4m + l%4 for m = 0 .. 17: load m is the lane's row
-// pointer plus 64m into the block at 1024m, so the 18 loads of a chunk can be
-// spread over other work at the cost of one 64-bit add each.
+// bf16 chunks use the block layout instead: rows 16w .. 16w+15 form a block
+// of 18,432 bytes in which 16-byte piece p of row i sits at
+// 1024*(p/4) + 64*i + 16*((p%4) ^ blk_sw(i)) (blk_off), blk_sw(i) =
+// 2*((i/4)%2): rows 4..7 and 12..15 of a block hold their piece pairs
+// swapped. The q.c reads (one row per lane, a 64-byte stride) and the
+// transposed p.c reads then spread over all LDS banks; without the swap
+// each of their passes met every bank twice (LDS bank-conflict counter).
 constexpr int kBlock = 16 * 1152;
+__device__ __forceinline__ int blk_sw(int row) { return 2 * ((row >> 2) & 1); }
 __device__ __forceinline__ int blk_off(int row, int p) {
-  return kBlock * (row >> 4) + 1024 * (p >> 2) + 64 * (row & 15) + 16 * (p & 3);
+  return kBlock * (row >> 4) + 1024 * (p >> 2) + 64 * (row & 15) + 16 * ((p & 3) ^ blk_sw(row));
 }
 
 // The whole gather of chunk c at once; returns the mask of present rows.
@@ -507,11 +509,11 @@ __device__ __forceinline__ void q_store(const QRegs& qr, char* dst, int p, int l
 
 // Store gather wave p's rows into `buf` (rows of missing keys as zeros, so
 // that p.c adds exactly 0 for them) and return the 16-bit mask of present
-// rows. Piece 8m + q of row 16p + 8g + i goes to blk_off: per store, two
-// contiguous 512-byte runs.
+// rows. Piece 8m + q of row 16p + 8g + i goes to blk_off (blk_sw(8g + i) =
+// blk_sw(i)): per store, two 512-byte runs.
 __device__ __forceinline__ uint32_t rows_store(const RowRegs& rr, char* buf, int p, int lane) {
   const int i = lane >> 3, q = lane & 7;
-  char* dst = buf + kBlock * p + 1024 * (q >> 2) + 16 * (q & 3) + 64 * i;
+  char* dst = buf + kBlock * p + 1024 * (q >> 2) + 16 * ((q & 3) ^ blk_sw(i)) + 64 * i;
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -603,7 +605,7 @@ __device__ __forceinline__ void attend_bf16(const AttnArgs& a, int r, int split,
     float x[4];
     {
       const uint32_t okc = sm.s_ok[bi][wave];
-      const char* rp = buf + kBlock * wave + 64 * col + 16 * grp;
+      const char* rp = buf + kBlock * wave + 64 * col + 16 * (grp ^ blk_sw(col));
       const f32x4 sacc = qc_bf16(rp, qf);
       float mx = -INFINITY;
 #pragma unroll
