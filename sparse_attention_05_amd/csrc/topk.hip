@@ -699,10 +699,12 @@ __device__ __forceinline__ int row_len(const TopkArgs& a, int r) {
 // of keys above it (about t*SS, with a standard deviation of about
 // sqrt(t)*SS) falls below k only 3 deviations down; the pivot is the lower
 // edge of the 12-bit bin holding it, refined by further 12-bit histograms
-// inside that bin (at most three passes reach single values) while the bin
-// holds more than a few samples past t: a heavy tail stretches the range and
-// widens the bins, and a tie class at the t-th sample ends on its exact
-// value, whose keys the candidate launch then lists in index order.
+// over the samples of that bin (from their smallest to their largest value;
+// at most three passes reach single values) while the bin holds more than a
+// few samples past t: a heavy tail stretches the range and widens the bins.
+// A bin whose samples are all equal (a tie class at the t-th sample) ends
+// the search on that exact value, whose keys the candidate launch then lists
+// in index order.
 __device__ __forceinline__ uint32_t sample_pivot(TopkShared& sh, int ns, int SS, int k, uint32_t smin, uint32_t smax) {
   const float kq = float(k) / float(SS);
   const float rt = 1.5f + sqrtf(2.25f + kq);
@@ -725,8 +727,21 @@ __device__ __forceinline__ uint32_t sample_pivot(TopkShared& sh, int ns, int SS,
     const uint32_t blo = lo + (b << shift);
     if (shift == 0 || above + cnt <= target + 8) return blo;
     const unsigned long long top = static_cast<unsigned long long>(blo) + ((1ull << shift) - 1ull);
-    hi = top < hi ? static_cast<uint32_t>(top) : hi;
-    lo = blo;
+    const uint32_t bhi = top < hi ? static_cast<uint32_t>(top) : hi;
+    // the bin's smallest and largest sample (find_crossing's barrier ended
+    // the histogram's atomics; the exchange below orders the next clear)
+    uint32_t vmin = 0xFFFFFFFFu, vmax = 0u;
+    for (int i = int(threadIdx.x); i < ns; i += kThreads) {
+      const uint32_t x = sh.v.samp[i];
+      if (x >= blo && x <= bhi) {
+        vmin = min(vmin, x);
+        vmax = max(vmax, x);
+      }
+    }
+    block_minmax(vmin, vmax, sh.red);
+    if (vmin == vmax) return vmin;
+    lo = vmin;
+    hi = vmax;
     target -= above;
   }
   return lo;
