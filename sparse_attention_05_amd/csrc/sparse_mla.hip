@@ -124,18 +124,25 @@ __global__ __launch_bounds__(kAttnWaves8 * 64) void sparse_mla_bf16_kernel(AttnA
 //  * q.c by (key half, head group): S^T for keys 32kh .. 32kh+31 and heads
 //    16hg .. 16hg+15 (the query fragments of those heads stay in registers);
 //    each head's chunk maximum combines its two key halves through LDS;
-//  * P^T (bf16) is written into the rope part (bytes 1024..1151) of the
-//    chunk's rows, free once q.c is done: head h's 64 probabilities go to
-//    row h, so no extra LDS is needed;
+//  * softmax against each head's current reference maximum, right after the
+//    wave's own q.c and without waiting for the other waves: the reference
+//    moves only when a chunk's maximum exceeds it by more than 8 (log2), so
+//    for almost every chunk the probabilities need no exchange; a wave that
+//    sees a logit above its reference + 8 raises a flag, published with
+//    P^T, and then every wave redoes the chunk's softmax exactly from the
+//    exchanged maxima (one more barrier);
+//  * P^T (bf16) goes to an array of its own, 144-byte rows per head;
 //  * p.c by value slice: wave w forms O^T[64w .. 64w+63][all heads], each
 //    transposed value fragment feeding the 4 head tiles.
 // Rows go from HBM to LDS with direct loads issued from inline assembly and
 // waited for exactly, so the gather of chunk c+1 overlaps chunk c: the two
 // waves of head group hg each issue half of the loads of rows
-// 16hg .. 16hg+15. Chunks past the last selected position are skipped (they
-// would add exactly 0).
+// 16hg .. 16hg+15, each lane's row index loaded one chunk ahead into a
+// register. Chunks past the last selected position are skipped (they would
+// add exactly 0).
 constexpr int kWideHeads = 64;
 constexpr int kWideThreads = 512;
+constexpr int kWidePtPitch = 144;  // bytes per head row of P^T (64 keys + 8 of padding: conflict-free reads and writes)
 
 // LDS layout of a chunk (64 rows x 72 chunks of 16 bytes): wave w's rows
 // 16w .. 16w+15 form a block of 18,432 bytes in which chunk c of row p sits
@@ -153,27 +160,31 @@ __device__ __forceinline__ int wide_off(int row, int c) {
   return kWideBlock * (row >> 4) + 1024 * (c >> 2) + 64 * (row & 15) + 16 * ((c & 3) ^ wide_sw(row));
 }
 
-// The gather of rows 16*blk .. +15 of chunk c (raw indices in s_idx) into
-// buf: this lane's source row (a missing row reads cache row 0 and is
-// zero-filled once it has landed), the LDS base of the block and the 16-bit
-// mask of present rows; load m (0..17) is then dma16(src + 64m,
-// lds + 1024m).
+// The gather of rows 16*blk .. +15 of a chunk into buf, `key` being this
+// lane's raw index (of row 16*blk + lane/4; -1 past the range): this lane's
+// source row (a missing row reads cache row 0 and is zero-filled once it has
+// landed), the LDS base of the block and the 16-bit mask of present rows;
+// load m (0..17) is then dma16(src + 64m, lds + 1024m).
 struct WideGather {
   const char* src;
   uint32_t lds;
   uint32_t mask;
 };
-__device__ __forceinline__ WideGather wide_gather(const AttnArgs& a, int64_t base, const int* s_idx, int c, char* buf,
-                                                  int blk, int lane) {
+__device__ __forceinline__ WideGather wide_gather(const AttnArgs& a, int64_t base, int key, char* buf, int blk,
+                                                  int lane) {
   using Cfg = AttnCfg<false>;
   int64_t row;
-  const bool ok = attn_row(a, base, s_idx[kChunkKeys * c + 16 * blk + (lane >> 2)], row);
+  const bool ok = attn_row(a, base, key, row);
   const unsigned long long okm = __ballot(ok && (lane & 3) == 0);  // bit 4i: row i
   uint32_t mask = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mask |= uint32_t((okm >> (4 * i)) & 1ull) << i;
   WideGather g;
-  g.src = static_cast<const char*>(a.latent) + row * Cfg::ROW_BYTES + 16 * ((lane & 3) ^ wide_sw(lane >> 2));
+  // (the lane's piece offset is recomputed per call: hoisted out of the
+  // chunk loop it is a 64-bit register pair held across the whole loop)
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  g.src = static_cast<const char*>(a.latent) + row * Cfg::ROW_BYTES + 16 * ((ln & 3) ^ wide_sw(ln >> 2));
   g.lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(buf + kWideBlock * blk))));
   g.mask = mask;
@@ -201,10 +212,11 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
   static_assert(WL == 18, "18 direct loads cover a 16-row block");
   constexpr int WLH = WL / 2;          // each of the block's two waves issues half
   __shared__ __attribute__((aligned(1024))) char smem[2 * Cfg::BUF_BYTES];
-  __shared__ int s_idx[kMaxTopk];
+  __shared__ __attribute__((aligned(16))) char s_pt[kWideHeads * kWidePtPitch];  // P^T: head h's 64 keys at h*pitch
   __shared__ float s_max[2][kWideHeads];  // chunk maximum of each head, per key half
   __shared__ float s_l[2][kWideHeads];
   __shared__ uint32_t s_ok[2][4];
+  __shared__ uint32_t s_over[2][8];       // per chunk parity and wave: a logit above its reference + 8
   __shared__ int s_last[8];
   const int r = int(gridDim.x) - 1 - int(blockIdx.x);  // later queries (more keys) first
   const int t = threadIdx.x;
@@ -215,19 +227,20 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
   const int kh = wave >> 2;  // q.c keys 32kh .. 32kh+31; loads WLH*kh .. +WLH of the block
   const int64_t base = seq_base(a, r);
   const int j_end = kps < a.k ? kps : a.k;  // one split: keys 0 .. j_end-1
+  const int32_t* ridx = a.idx + int64_t(r) * a.k;
+  // this lane's raw index in chunk c: key 64c + 16hg + lane/4
+  auto key_of = [&](int c) -> int {
+    const int j = kChunkKeys * c + 16 * hg + (lane >> 2);
+    return j < j_end ? ridx[j] : -1;
+  };
 
-  // the range's indices; the last selected position bounds the chunks walked
+  // the last selected position bounds the chunks walked
   int last = -1;
-  for (int e = t; e < j_end; e += kWideThreads) {
-    const int v = a.idx[int64_t(r) * a.k + e];
-    s_idx[e] = v;
-    last = v >= 0 ? e : last;
-  }
-  const int span = (j_end + kChunkKeys - 1) / kChunkKeys * kChunkKeys;
-  for (int e = j_end + t; e < span; e += kWideThreads) s_idx[e] = -1;
+  for (int e = t; e < j_end; e += kWideThreads) last = ridx[e] >= 0 ? e : last;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) last = max(last, __shfl_xor(last, d, 64));
   if (lane == 0) s_last[wave] = last;
+  int key0 = key_of(0), key1 = key_of(1);
 
   // query fragments of this wave's q.c head 16*hg + col (zero past H)
   bf16x8 qf[18];
@@ -243,14 +256,12 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
   }
   // every load above has landed; the fragments are re-defined through an
   // empty asm, so that no wait for them is placed inside the chunk loop
-  // (where it would also wait for the next chunk's rows), and placed in
-  // accumulation registers (an MFMA reads its B operand from there too),
-  // which leaves the vector registers to the LDS fragments read ahead
+  // (where it would also wait for the next chunk's rows)
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
     uint4 u = __builtin_bit_cast(uint4, qf[ks]);
-    asm volatile("" : "+a"(u.x), "+a"(u.y), "+a"(u.z), "+a"(u.w));
+    asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
     qf[ks] = __builtin_bit_cast(bf16x8, u);
   }
   __syncthreads();
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
   // load per K-step, once every wave is done with the buffer (chunk c-1's)
   uint32_t okw[2] = {0u, 0u};
   if (nchunks > 0) {
-    const WideGather g = wide_gather(a, base, s_idx, 0, smem, hg, lane);
+    const WideGather g = wide_gather(a, base, key0, smem, hg, lane);
 #pragma unroll
     for (int m = WLH * kh; m < WLH * kh + WLH; ++m) dma16(g.src + 64 * m, g.lds + 1024 * m);
     okw[0] = g.mask;
@@ -278,6 +289,7 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
   float lq = 0.f;        // this lane's share of its running sum (this key half)
   float mo[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // of the p.c heads 16ht + col
   const float scale2 = a.scale * kLog2e;
+  const int hq = 16 * hg + col;  // this lane's q.c head
 
   for (int c = 0; c < nchunks; ++c) {
     const int bi = c & 1;
@@ -292,10 +304,12 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
       }
     }
     if (lane == 0 && kh == 0) s_ok[bi][hg] = okw[bi];
-    __syncthreads();
+    __syncthreads();  // chunk c in LDS; every wave is done with p.c of chunk c-1 (its buffer and P^T)
     const bool more = c + 1 < nchunks;
     WideGather gn{nullptr, 0u, 0u};
-    if (more) gn = wide_gather(a, base, s_idx, c + 1, smem + (bi ^ 1) * Cfg::BUF_BYTES, hg, lane);
+    if (more) gn = wide_gather(a, base, key1, smem + (bi ^ 1) * Cfg::BUF_BYTES, hg, lane);
+    key1 = key_of(c + 2);  // lands with the chunk's loads, used by the next gather
+    okw[bi ^ 1] = gn.mask;
 
     // ---- q.c: S^T for keys 32kh + 16kt + (0..15), heads 16*hg + (0..15) ------------------
     // (the key fragments are read two K-steps ahead of their MFMAs; the
@@ -330,6 +344,7 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
     };
     if (more) qc(std::true_type{});
     else qc(std::false_type{});
+
     // logits (log2 domain), -inf for missing keys (16-key tiles with a
     // missing key only); the head's maximum over this key half
     float x[2][4];
@@ -346,65 +361,79 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
     }
-    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    if (grp == 0) s_max[kh][16 * hg + col] = mx;
-    __syncthreads();  // maxima visible; every wave is done with q.c of chunk c (its rope parts are free)
-    okw[bi ^ 1] = gn.mask;
-
-    // ---- softmax of this wave's heads and keys: P^T into the rope part of row h ---------
-    {
-      const int h = 16 * hg + col;
-      const float m_new = wide_ref_max(mq, fmaxf(s_max[0][h], s_max[1][h]));
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(mq - m_use);
+    // ---- softmax against the current reference, P^T of this wave's heads and keys -------
+    // (exact whenever no logit of the chunk exceeds its head's reference by
+    // more than 8; a wave that sees one flags the chunk, and the exact form
+    // below replaces these values)
+    auto softmax = [&](float m_ref) -> float {
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         __bf16 pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = static_cast<__bf16>(fast_exp2(x[kt][i] - m_use));
+          // (the clamp only matters for a flagged chunk, whose values are replaced)
+          pv[i] = static_cast<__bf16>(fast_exp2(fminf(x[kt][i] - m_use, 8.f)));
           psum += static_cast<float>(pv[i]);
         }
-        // keys 16(2kh+kt) + 4grp .. +3 of head h: rope chunk 64 + 2(2kh+kt) + grp/2 of row h, half grp&1
-        const int ch = 64 + 2 * (2 * kh + kt) + (grp >> 1);
+        // keys 16(2kh+kt) + 4grp .. +3 of head hq
         const uint32_t w0 = uint32_t(__builtin_bit_cast(uint16_t, pv[0])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[1])) << 16);
         const uint32_t w1 = uint32_t(__builtin_bit_cast(uint16_t, pv[2])) | (uint32_t(__builtin_bit_cast(uint16_t, pv[3])) << 16);
-        *reinterpret_cast<uint2*>(buf + wide_off(h, ch) + 8 * (grp & 1)) = uint2{w0, w1};
+        *reinterpret_cast<uint2*>(s_pt + kWidePtPitch * hq + 2 * (16 * (2 * kh + kt) + 4 * grp)) = uint2{w0, w1};
       }
+      return psum;
+    };
+    float psum = softmax(mq);
+    const bool over = __ballot(mx > mq + 8.f || (mq == -INFINITY && mx > -INFINITY)) != 0ull;
+    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+    if (grp == 0) s_max[kh][hq] = mx;
+    if (lane == 0) s_over[bi][wave] = over ? 1u : 0u;
+    __syncthreads();  // P^T, the flags and the maxima visible
+    uint32_t any = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) any |= s_over[bi][w];
+    if (any) {
+      // a reference moves: new references of every head from both key halves'
+      // maxima, this wave's probabilities again against its head's, and the
+      // p.c accumulators rescaled by the same per-head factors
+      const float m_new = wide_ref_max(mq, fmaxf(s_max[0][hq], s_max[1][hq]));
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(mq - m_use);
+      psum = softmax(m_new);
       lq = lq * alpha + psum;
       mq = m_new;
-    }
-    // rescale of the p.c accumulators by the same per-head alpha
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      const float cmax = fmaxf(s_max[0][16 * ht + col], s_max[1][16 * ht + col]);
-      const float m_new = wide_ref_max(mo[ht], cmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(mo[ht] - m_use);
-      mo[ht] = m_new;
-      if (__ballot(alpha != 1.f)) {
+      for (int ht = 0; ht < 4; ++ht) {
+        const float cmax = fmaxf(s_max[0][16 * ht + col], s_max[1][16 * ht + col]);
+        const float mn = wide_ref_max(mo[ht], cmax);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        const float al = fast_exp2(mo[ht] - mu);
+        mo[ht] = mn;
+        if (__ballot(al != 1.f)) {
 #pragma unroll
-        for (int vt = 0; vt < 4; ++vt) acc[vt][ht] *= alpha;
+          for (int vt = 0; vt < 4; ++vt) acc[vt][ht] *= al;
+        }
       }
+      __syncthreads();  // the exact P^T visible
+    } else {
+      lq += psum;
     }
-    __syncthreads();  // P^T of all heads in LDS
 
     // ---- O^T[64*wave + 16*vt + (0..15)][16*ht + (0..15)] += C^T . P^T ---------------
     {
       const int tr_row = 4 * grp + (col >> 2);
-      // P^T of head 16ht + col for both K-steps: keys kb + 4grp .. +3 and kb + 16 + 4grp .. +3
-      bf16x8 pf[2][4];
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
+      // P^T of head 16ht + col for K-step kq: keys 32kq + 4grp .. +3 and 32kq + 16 + 4grp .. +3
+      auto pfrag = [&](int kq, bf16x8 (&pf)[4]) {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
-          const int h = 16 * ht + col, kb = 32 * kq;
-          const uint2 plo = *reinterpret_cast<const uint2*>(buf + wide_off(h, 64 + kb / 8 + (grp >> 1)) + 8 * (grp & 1));
-          const uint2 phi = *reinterpret_cast<const uint2*>(buf + wide_off(h, 64 + kb / 8 + 2 + (grp >> 1)) + 8 * (grp & 1));
-          pf[kq][ht] = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
+          const char* pp = s_pt + kWidePtPitch * (16 * ht + col) + 2 * (32 * kq + 4 * grp);
+          const uint2 plo = *reinterpret_cast<const uint2*>(pp);
+          const uint2 phi = *reinterpret_cast<const uint2*>(pp + 32);
+          pf[ht] = __builtin_bit_cast(bf16x8, uint4{plo.x, plo.y, phi.x, phi.y});
         }
+      };
       // transposed value fragment of step q = (kq, vt), read one step ahead:
       // lane (col, grp) names key row 32kq + tr_row (+16 for the second
       // read), value dims 64*wave + 16vt + 4(col%4) .. +3: chunk
@@ -417,16 +446,21 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
             (__attribute__((address_space(3))) short4v*)(lds_ptr)(p0 + kWideBlock));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8 vf[2];
-      vf[0] = vfrag(0);
-      __builtin_amdgcn_sched_barrier(0);  // the pattern below starts with the reads of step 1
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q + 1 < 8) vf[(q + 1) & 1] = vfrag(q + 1);
+      for (int kq = 0; kq < 2; ++kq) {
+        bf16x8 pf[4], vf[2];
+        pfrag(kq, pf);
+        vf[0] = vfrag(4 * kq);
+        __builtin_amdgcn_sched_barrier(0);  // the pattern below starts with the reads of step 1
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht) acc[q & 3][ht] = mfma_k32(vf[q & 1], pf[q >> 2][ht], acc[q & 3][ht]);
-        if (q + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        for (int vt = 0; vt < 4; ++vt) {
+          if (vt + 1 < 4) vf[(vt + 1) & 1] = vfrag(4 * kq + vt + 1);
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) acc[vt][ht] = mfma_k32(vf[vt & 1], pf[ht], acc[vt][ht]);
+          if (vt + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -435,7 +469,7 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
   {
     float l = lq + wave_shfl_xor(lq, 16);
     l += wave_shfl_xor(l, 32);
-    if (grp == 0) s_l[kh][16 * hg + col] = l;
+    if (grp == 0) s_l[kh][hq] = l;
   }
   __syncthreads();
 #pragma unroll
