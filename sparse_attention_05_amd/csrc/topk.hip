@@ -1143,9 +1143,10 @@ __device__ __forceinline__ void window_fast_clear(TopkShared& sh) {
 
 // window_select for the usual row, in four barriers and few instructions
 // (eight waves share four SIMDs, so each wave's instruction count is the
-// time): at most 64 slices, every candidate word already read ahead, and
-// k_eff <= C <= kCap. Each wave sums the slice records itself (DPP only, no
-// exchange); one bucket pass on 12 bits of (largest candidate - word) over
+// time): at most 64 slices, every candidate word among the JJ slots of the
+// threads of its slice, and k_eff <= C <= kCap; the slice records come
+// reduced (C, longest slice, largest candidate key, pivot). One bucket pass
+// on 12 bits of (largest candidate - word) over
 // [pivot, largest candidate], on the keys alone (32-bit) when the digit lies
 // above the index bits. The buckets that meet [lo, hi) are the index range
 // [b_lo, b_hi] (those holding ranks lo and hi - 1 and all between), so a
@@ -1155,22 +1156,25 @@ __device__ __forceinline__ void window_fast_clear(TopkShared& sh) {
 // sh.v.samp, and that range is ranked one word per thread (count of the
 // larger words of its bucket). Every LDS access of a phase is issued before
 // the first wait. Dense buckets that meet the window go on to sort_levels.
-// Expects
-// window_fast_clear's LDS zero (ordered by a barrier). Returns false, with
-// no LDS touched, when the row needs window_select.
-__device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArgs& a, int r, int slices, int n,
-                                                   int lo, int hi, int32_t* out, int obase, const WindowLoads& L) {
+// Expects window_fast_clear's LDS zero (ordered by a barrier).
+template <int JJ>
+__device__ __forceinline__ bool window_select_fast_j(TopkShared& sh, const TopkArgs& a, int r, int slices, int lo,
+                                                     int hi, int32_t* out, int obase, const WindowLoads& L, uint32_t C,
+                                                     uint32_t longest, uint32_t kmax, uint32_t pivot, int tps) {
   const int t = threadIdx.x;
-  const int k_eff = n < a.k ? n : a.k;
   constexpr int J = kJ;
-  if (slices > 64) return false;
-  const int tps = window_tps(slices);
   const int sg = t / tps, sl = t % tps;
-  const uint32_t C = wave_sum(L.st.x);
-  const uint32_t longest = wave_max(L.st.x), kmax = wave_max(L.st.y);
-  const uint32_t pivot = lane_value(L.st.z, 0);
-  if (C < uint32_t(k_eff) || C > uint32_t(kCap) || longest > uint32_t(J * tps)) return false;
-
+  // this thread's words: the first J read ahead, the rest (JJ > J: slices
+  // longer than the read-ahead) loaded now, all in one round trip
+  unsigned long long w[JJ];
+#pragma unroll
+  for (int j = 0; j < J; ++j) w[j] = L.x[j];
+  if constexpr (JJ > J) {
+    const int64_t stride = int64_t(a.slice_tiles) * kTile;
+    const unsigned long long* cand = a.cand + int64_t(r) * slices * stride + int64_t(sg) * stride;
+#pragma unroll
+    for (int j = J; j < JJ; ++j) w[j] = sg < slices && uint32_t(j * tps + sl) < L.own ? cand[j * tps + sl] : 0ull;
+  }
   const unsigned long long mx = (static_cast<unsigned long long>(kmax) << 32) | 0xFFFFFFFFull;
   const unsigned long long mn = static_cast<unsigned long long>(pivot) << 32;
   int shift, nb;
@@ -1179,15 +1183,15 @@ __device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArg
   // low halves (0xFFFFFFFF - ~index = index) never carry into the key half
   const bool keys_only = shift >= 32;
   const int ks = keys_only ? shift - 32 : 0;
-  auto bucket = [&](unsigned long long w) -> uint32_t {
-    return keys_only ? (kmax - uint32_t(w >> 32)) >> ks : uint32_t((mx - w) >> shift);
+  auto bucket = [&](unsigned long long v) -> uint32_t {
+    return keys_only ? (kmax - uint32_t(v >> 32)) >> ks : uint32_t((mx - v) >> shift);
   };
-  uint32_t bk[J];
-  bool valid[J];
+  uint32_t bk[JJ];
+  bool valid[JJ];
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
+  for (int j = 0; j < JJ; ++j) {
     valid[j] = sg < slices && uint32_t(j * tps + sl) < L.own;
-    bk[j] = valid[j] ? bucket(L.x[j]) : 0u;  // (unused slots: bucket 0, never placed)
+    bk[j] = valid[j] ? bucket(w[j]) : 0u;  // (unused slots: bucket 0, never placed)
     if (valid[j]) atomicAdd(&sh.cnt[bk[j]], 1u);
   }
   lds_barrier();
@@ -1259,12 +1263,12 @@ __device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArg
   const int next = int(sh.misc[6]);
   const uint32_t s_lo = sh.misc[8], s_hi = sh.misc[9], b_lo = sh.misc[10], b_hi = sh.misc[11];
   // the words of the buckets that meet the window, placed at their bucket
-  bool keep[J];
-  uint32_t b0[J], cb[J], slot[J];
+  bool keep[JJ];
+  uint32_t b0[JJ], cb[JJ], slot[JJ];
 #pragma unroll
-  for (int j = 0; j < J; ++j) keep[j] = valid[j] && bk[j] >= b_lo && bk[j] <= b_hi;
+  for (int j = 0; j < JJ; ++j) keep[j] = valid[j] && bk[j] >= b_lo && bk[j] <= b_hi;
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
+  for (int j = 0; j < JJ; ++j) {
     if (keep[j]) {
       b0[j] = sh.bins[bk[j]];
       cb[j] = sh.cnt[bk[j]];
@@ -1272,9 +1276,9 @@ __device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArg
     }
   }
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
+  for (int j = 0; j < JJ; ++j) {
     if (keep[j]) {
-      sh.u.wb[b0[j] + slot[j]] = L.x[j];
+      sh.u.wb[b0[j] + slot[j]] = w[j];
       sh.v.samp[b0[j] + slot[j]] = b0[j] | (cb[j] << 16);  // (both <= kCap < 2^16)
     }
   }
@@ -1306,6 +1310,29 @@ __device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArg
   }
   sort_levels(sh, sh.u.wb, sh.wa, 1, next, 1, lo, hi, out, obase);
   return true;
+}
+
+
+// The usual row's short form (see window_select_fast_j): the slice records
+// reduced by every wave itself, then the form whose word slots cover the
+// longest slice -- the read-ahead alone, or twice it when a row's slices
+// hold more candidates than the read-ahead (the slice count, and so the
+// read-ahead per slice, is set by the longest row of the batch). Returns
+// false, with no LDS touched, when the row needs window_select.
+__device__ __forceinline__ bool window_select_fast(TopkShared& sh, const TopkArgs& a, int r, int slices, int n,
+                                                   int lo, int hi, int32_t* out, int obase, const WindowLoads& L) {
+  const int k_eff = n < a.k ? n : a.k;
+  if (slices > 64) return false;
+  const int tps = window_tps(slices);
+  const uint32_t C = wave_sum(L.st.x);
+  const uint32_t longest = wave_max(L.st.x), kmax = wave_max(L.st.y);
+  const uint32_t pivot = lane_value(L.st.z, 0);
+  if (C < uint32_t(k_eff) || C > uint32_t(kCap)) return false;
+  if (longest <= uint32_t(kJ * tps))
+    return window_select_fast_j<kJ>(sh, a, r, slices, lo, hi, out, obase, L, C, longest, kmax, pivot, tps);
+  if (longest <= uint32_t(2 * kJ * tps))
+    return window_select_fast_j<2 * kJ>(sh, a, r, slices, lo, hi, out, obase, L, C, longest, kmax, pivot, tps);
+  return false;
 }
 
 // Ranks [lo, hi) of row r (hi <= min(n, k)) from the candidates of the
