@@ -50,6 +50,7 @@ constexpr int kMaxSamples = 8192;    // score samples behind a pivot
 constexpr int kMaxSliceTiles = 8;    // tiles of kTile keys per slice of a split row
 constexpr int kBatch = 8;            // streamed tiles in flight per pass over a long row
 constexpr int kSmall = 32;           // rank-by-counting limit
+constexpr int kFastSmall = 512;      // ... in the window selection's short form (one word per thread)
 constexpr int kMaxWork = 16;         // dense buckets split per level
 constexpr int kFullBins = 1024;      // whole-row histogram: 10-bit digits
 constexpr int kFullCopies = 8;       // ... spread over lane & 7
@@ -1154,8 +1155,11 @@ __device__ __forceinline__ void window_fast_clear(TopkShared& sh) {
 // the contiguous range [s_lo, s_hi) of sh.u.wb (the first such bucket's
 // start to the last one's end), each beside its bucket's start and count in
 // sh.v.samp, and that range is ranked one word per thread (count of the
-// larger words of its bucket). Every LDS access of a phase is issued before
-// the first wait. Dense buckets that meet the window go on to sort_levels.
+// larger words of its bucket, for buckets of up to kFastSmall words: the
+// words are ranked in parallel, so a bucket of many near-equal scores costs
+// one pass over it instead of further bucket passes). Every LDS access of a
+// phase is issued before the first wait. Denser buckets that meet the
+// window go on to sort_levels.
 // Expects window_fast_clear's LDS zero (ordered by a barrier).
 template <int JJ>
 __device__ __forceinline__ bool window_select_fast_j(TopkShared& sh, const TopkArgs& a, int r, int slices, int lo,
@@ -1240,9 +1244,9 @@ __device__ __forceinline__ bool window_select_fast_j(TopkShared& sh, const TopkA
         sh.misc[11] = 8 * t + j;
       }
   }
-  if (cmax > uint32_t(kSmall)) {  // dense buckets that meet the window: listed for sort_levels
+  if (cmax > uint32_t(kFastSmall)) {  // dense buckets that meet the window: listed for sort_levels
     for (int j = 0; j < 8; ++j) {
-      if (c[j] > uint32_t(kSmall) && int(st[j]) < hi && int(st[j] + c[j]) > lo) {
+      if (c[j] > uint32_t(kFastSmall) && int(st[j]) < hi && int(st[j] + c[j]) > lo) {
         const uint32_t slot = atomicAdd(&sh.misc[6], 1u);
         if (slot < kMaxWork) {
           const unsigned long long bmx = mx - (static_cast<unsigned long long>(8 * t + j) << shift);
@@ -1288,7 +1292,7 @@ __device__ __forceinline__ bool window_select_fast_j(TopkShared& sh, const TopkA
     const unsigned long long w = sh.u.wb[p];
     const uint32_t m = sh.v.samp[p];
     const uint32_t wb0 = m & 0xFFFFu, wcb = m >> 16;
-    if (wcb > uint32_t(kSmall)) continue;  // dense: sort_levels
+    if (wcb > uint32_t(kFastSmall)) continue;  // dense: sort_levels
     uint32_t rk = 0;
     for (uint32_t q0 = 0; q0 < wcb; q0 += 4) {
       unsigned long long y[4];
