@@ -228,57 +228,71 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
   const int64_t base = seq_base(a, r);
   const int j_end = kps < a.k ? kps : a.k;  // one split: keys 0 .. j_end-1
   const int32_t* ridx = a.idx + int64_t(r) * a.k;
-  // this lane's raw index in chunk c: key 64c + 16hg + lane/4
-  auto key_of = [&](int c) -> int {
-    const int j = kChunkKeys * c + 16 * hg + (lane >> 2);
-    return j < j_end ? ridx[j] : -1;
-  };
 
-  // the last selected position bounds the chunks walked
+  // The start's loads go out together, each unconditional (a clamped
+  // position, head 0's row past H) with its condition applied after it has
+  // landed: a load under a branch, or a select right behind it, makes the
+  // compiler wait for it on the spot, and the start then paid the latency of
+  // the index scan, the query fragments and chunk 0 one after another. First
+  // the row indices of chunks 0 and 1, then the scan of the index row for the
+  // last selected position (which bounds the chunks walked), then the query
+  // fragments of this wave's q.c head 16*hg + col; chunk 0 is gathered as soon
+  // as its indices have landed, while the rest are in flight.
+  const int jl = 16 * hg + (lane >> 2);  // this lane's key within a chunk
+  int key0 = ridx[min(jl, j_end - 1)];
+  int key1 = ridx[min(kChunkKeys + jl, j_end - 1)];
+  constexpr int kScan = 4;  // scan entries per thread held at once
+  int sv[kScan];
+  const bool scan_regs = j_end <= kScan * kWideThreads;
+#pragma unroll
+  for (int i = 0; i < kScan; ++i) sv[i] = ridx[min(t + i * kWideThreads, j_end - 1)];
+  bf16x8 qf[18];
+  const bool hv = 16 * hg + col < a.H;
+  {
+    const int64_t qoff = (int64_t(r) * a.H + (hv ? 16 * hg + col : 0)) * kLatentDim + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8,
+                                  *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qoff + 32 * ks));
+  }
+  // chunk 0 (cache row 0 stands in for a missing row, and is zeroed): issued
+  // before the chunk count is known, and drained by the epilogue's barrier
+  // when there is no chunk to walk; chunk c+1 is issued during the q.c of
+  // chunk c, one direct load per K-step, once every wave is done with the
+  // buffer (chunk c-1's)
+  uint32_t okw[2] = {0u, 0u};
+  {
+    const WideGather g = wide_gather(a, base, jl < j_end ? key0 : -1, smem, hg, lane);
+#pragma unroll
+    for (int m = WLH * kh; m < WLH * kh + WLH; ++m) dma16(g.src + 64 * m, g.lds + 1024 * m);
+    okw[0] = g.mask;
+  }
+  key1 = kChunkKeys + jl < j_end ? key1 : -1;
   int last = -1;
-  for (int e = t; e < j_end; e += kWideThreads) last = ridx[e] >= 0 ? e : last;
+  if (scan_regs) {
+#pragma unroll
+    for (int i = 0; i < kScan; ++i) last = t + i * kWideThreads < j_end && sv[i] >= 0 ? t + i * kWideThreads : last;
+  } else {
+    for (int e = t; e < j_end; e += kWideThreads) last = ridx[e] >= 0 ? e : last;
+  }
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) last = max(last, __shfl_xor(last, d, 64));
   if (lane == 0) s_last[wave] = last;
-  int key0 = key_of(0), key1 = key_of(1);
-
-  // query fragments of this wave's q.c head 16*hg + col (zero past H)
-  bf16x8 qf[18];
-  {
-    const int h = 16 * hg + col;
-    const bool hv = h < a.H;
-    const int64_t qoff = (int64_t(r) * a.H + (hv ? h : 0)) * kLatentDim + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qoff + 32 * ks);
-      qf[ks] = __builtin_bit_cast(bf16x8, hv ? x : uint4{0u, 0u, 0u, 0u});
-    }
-  }
   // every load above has landed; the fragments are re-defined through an
   // empty asm, so that no wait for them is placed inside the chunk loop
-  // (where it would also wait for the next chunk's rows)
+  // (where it would also wait for the next chunk's rows), and zeroed past H
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks) {
     uint4 u = __builtin_bit_cast(uint4, qf[ks]);
     asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-    qf[ks] = __builtin_bit_cast(bf16x8, u);
+    qf[ks] = __builtin_bit_cast(bf16x8, hv ? u : uint4{0u, 0u, 0u, 0u});
   }
   __syncthreads();
   int lmax = s_last[0];
 #pragma unroll
   for (int w = 1; w < 8; ++w) lmax = max(lmax, s_last[w]);
   const int nchunks = (lmax + kChunkKeys) / kChunkKeys;
-
-  // chunk 0 now; chunk c+1 is issued during the q.c of chunk c, one direct
-  // load per K-step, once every wave is done with the buffer (chunk c-1's)
-  uint32_t okw[2] = {0u, 0u};
-  if (nchunks > 0) {
-    const WideGather g = wide_gather(a, base, key0, smem, hg, lane);
-#pragma unroll
-    for (int m = WLH * kh; m < WLH * kh + WLH; ++m) dma16(g.src + 64 * m, g.lds + 1024 * m);
-    okw[0] = g.mask;
-  }
 
   f32x4 acc[4][4];  // O^T[64*wave + 16*vt + (0..15)][16*ht + (0..15)]
 #pragma unroll
@@ -304,11 +318,14 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
       }
     }
     if (lane == 0 && kh == 0) s_ok[bi][hg] = okw[bi];
+    if (c > 0) key1 = kChunkKeys * (c + 1) + jl < j_end ? key1 : -1;
     __syncthreads();  // chunk c in LDS; every wave is done with p.c of chunk c-1 (its buffer and P^T)
     const bool more = c + 1 < nchunks;
     WideGather gn{nullptr, 0u, 0u};
     if (more) gn = wide_gather(a, base, key1, smem + (bi ^ 1) * Cfg::BUF_BYTES, hg, lane);
-    key1 = key_of(c + 2);  // lands with the chunk's loads, used by the next gather
+    // the raw index of this lane's key in chunk c+2 (lands with the chunk's
+    // loads; its condition is applied at the next chunk, after the wait)
+    key1 = ridx[min(kChunkKeys * (c + 2) + jl, j_end - 1)];
     okw[bi ^ 1] = gn.mask;
 
     // ---- q.c: S^T for keys 32kh + 16kt + (0..15), heads 16*hg + (0..15) ------------------
@@ -388,7 +405,13 @@ __global__ __launch_bounds__(kWideThreads) void sparse_mla_wide_kernel(AttnArgs 
     const bool over = __ballot(mx > mq + 8.f || (mq == -INFINITY && mx > -INFINITY)) != 0ull;
     mx = fmaxf(mx, wave_shfl_xor(mx, 16));
     mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    if (grp == 0) s_max[kh][hq] = mx;
+    {
+      // (the address recomputed from an opaque lane index: held across the
+      // loop it is spilled, and its reload would wait for the chunk's loads)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      if ((ln >> 4) == 0) s_max[kh][16 * hg + (ln & 15)] = mx;
+    }
     if (lane == 0) s_over[bi][wave] = over ? 1u : 0u;
     __syncthreads();  // P^T, the flags and the maxima visible
     uint32_t any = 0;

@@ -271,6 +271,51 @@ def test_attention_many_queries_matches_oracle(dsa, std, k):
     C.assert_attn_close(out[rows][keep], ref[keep], lse[rows][keep], lse_ref[keep])
 
 
+@pytest.mark.parametrize("k", [2048, 512, 100])
+def test_attention_many_query_batches_agree_bitwise(dsa, k):
+    """More queries than CUs (the all-heads kernel, 750 queries): every row
+    must equal, bit for bit, the same row computed in a batch of 150-200
+    rows (a row's result may not depend on which workgroup or batch
+    position computes it), and sampled rows the oracle. Planted: empty rows,
+    rows of one, two and three chunks, holes, and a row whose only key sits
+    at the last position."""
+    import torch
+    p = inputs.decode_config([1200] * 150, seed=21, H=64, k=k, tokens_per_seq=5)
+    R = p.R
+    rng = np.random.default_rng(k)
+    idx = np.full((R, k), -1, np.int32)
+    for r in range(R):
+        n = int(p.q_pos[r]) + 1
+        m = min(k, n)
+        idx[r, :m] = rng.choice(n, size=m, replace=False)
+    idx[rng.random(idx.shape) < 0.1] = -1
+    idx[R - 1 - 256] = -1                       # empty, second of workgroup 0
+    idx[R - 2 - 256, 1:] = -1                   # one chunk
+    idx[R - 3 - 256, 100:] = -1                 # two chunks (k permitting)
+    idx[R - 4 - 256, 150:] = -1                 # three chunks
+    idx[R - 5] = -1                             # empty, first of workgroup 4
+    idx[R - 6, :] = -1
+    idx[R - 6, k - 1] = 7                       # a single key, at the last position
+    idx[R - 7, 5:] = -1                         # short first query
+    d = inputs.to_torch(p)
+    out, lse = _gpu_attn(dsa, p, idx, d)
+    assert (out[R - 1 - 256] == 0).all() and np.isneginf(lse[R - 1 - 256]).all()
+    assert (out[R - 5] == 0).all() and np.isneginf(lse[R - 5]).all()
+    # one query per workgroup: slices of 150-200 rows (still the all-heads kernel)
+    idx_d = torch.from_numpy(idx).cuda()
+    for lo in range(0, R, 200):
+        hi = min(R, lo + 200)
+        o_s = torch.full((hi - lo, p.H, 512), float("nan"), dtype=torch.float32, device="cuda")
+        l_s = torch.full((hi - lo, p.H), float("nan"), dtype=torch.float32, device="cuda")
+        dsa.dsa_sparse_mla_attn(d.q_abs[lo:hi], d.latent, d.row_off, idx_d[lo:hi], p.scale,
+                                q_seq=d.q_seq[lo:hi], out=o_s, lse=l_s)
+        assert np.array_equal(o_s.cpu().numpy(), out[lo:hi], equal_nan=True), f"rows {lo}..{hi}"
+        assert np.array_equal(l_s.cpu().numpy(), lse[lo:hi], equal_nan=True), f"rows {lo}..{hi}"
+    rows = [0, 1, R // 2, R - 1, R - 2, R - 2 - 256, R - 3 - 256, R - 4 - 256, R - 6, R - 7, R - 1 - 512]
+    ref, lse_ref = O.sparse_mla(p, idx[rows], rows=rows)
+    C.assert_attn_close(out[rows], ref, lse[rows], lse_ref)
+
+
 # ------------------------------------------------------------------------------
 # whole path
 # ------------------------------------------------------------------------------
