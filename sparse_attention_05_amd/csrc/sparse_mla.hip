@@ -603,8 +603,11 @@ AttnPlan plan_attention(int R, int H, int k) {
   p.splits = splits;
   p.keys_per_split = kps;
   // many queries (two workgroups per CU even at one split): one workgroup per
-  // query for all heads (bf16)
-  p.wide = H <= kWideHeads && int64_t(R) * p.head_groups >= 2 * int64_t(target) && splits == 1;
+  // query for all heads (bf16). Only past half as many rows as CUs: up to
+  // there the fused decode step may run its own selection + attention kernel
+  // (the 16-head core), and replaying its indices must run the same one.
+  p.wide = H <= kWideHeads && int64_t(R) * p.head_groups >= 2 * int64_t(target) && 2 * int64_t(R) > target &&
+           splits == 1;
   p.ws_bytes = splits > 1 ? size_t(R) * splits * H * (kValueDim + 2) * sizeof(float) : 0;
   p.ws_bytes = (p.ws_bytes + 255) / 256 * 256;
   return p;

@@ -401,6 +401,23 @@ def test_fused_decode_repeatable_and_replayable(dsa):
     C.assert_attn_close(out, ref_o, lse, ref_l)
 
 
+def test_fused_split_decode_replay_at_the_all_heads_boundary(dsa):
+    """As many rows as half the CUs with one row past 8K: the fused step
+    takes the split selection, and replaying its indices must run the same
+    attention kernel (the all-heads one starts at more rows), bit for bit."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    R = cus // 2
+    p = inputs.decode_config([8300] + [300] * (R - 1), seed=23, H=64, k=2048)
+    d = inputs.to_torch(p)
+    out, lse, idx = _fused(dsa, p, d)
+    rep_o, rep_l = dsa.dsa_sparse_mla_attn(d.q_abs, d.latent, d.row_off, torch.from_numpy(idx).cuda(), p.scale)
+    assert np.array_equal(rep_o.cpu().numpy(), out) and np.array_equal(rep_l.cpu().numpy(), lse)
+    rows = [0, 1, R - 1]
+    ref_o, ref_l = O.sparse_mla(p, idx[rows], rows=rows)
+    C.assert_attn_close(out[rows], ref_o, lse[rows], ref_l)
+
+
 @pytest.mark.parametrize("lens,k", [([12000, 9000, 20000], 2048), ([30000], 1000),
                                     ([9000, 16385, 12000, 10000, 9001], 512)])
 def test_fused_split_decode_matches_pipeline_and_replay(dsa, lens, k):
