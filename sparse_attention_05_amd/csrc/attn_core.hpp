@@ -281,11 +281,12 @@ __device__ __forceinline__ int64_t seq_base(const AttnArgs& a, int r) {
 }
 
 // A 16-byte store at device scope (sc1): it goes through the L2 to memory.
-// The split outputs are read by the next kernel on every XCD, so each XCD's
-// L2 must be written back at this kernel's end; stores that went through
-// already leave nothing of theirs to write back then, and the merge launch
-// starts about 1 us sooner at 4 x 32K (the same bits: the cache policy
-// changes no value). Issued from inline assembly; nothing here reads them.
+// Whatever a kernel leaves dirty in an XCD's L2 is written back at its end,
+// before the next launch on the stream can start; stores that went through
+// already leave nothing of theirs to write back then. For the split outputs
+// (read by the merge launch on every XCD) the merge starts about 1 us sooner
+// at 4 x 32K; the same bits, the cache policy changes no value. Issued from
+// inline assembly; nothing in the issuing kernel reads them.
 __device__ __forceinline__ void store_through(float* p, float4 v) {
   const f32x4 x = __builtin_bit_cast(f32x4, v);
   asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(x) : "memory");

@@ -1505,8 +1505,15 @@ __global__ __launch_bounds__(kThreads) void topk_attn_kernel(TopkArgs ta, AttnAr
   if (j_beg < hi && !window_select_fast(u.sel, ta, r, slices, n, j_beg, hi, s_idx, j_beg, L))
     window_select(u.sel, ta, r, slices, n, j_beg, hi, s_idx, j_beg, L);
   lds_barrier();  // the split's indices are in LDS; the selection's LDS is free
-  if (hg == 0)
-    for (int i = t; i < j_end - j_beg; i += kThreads) ta.idx[int64_t(r) * k + j_beg + i] = s_idx[i];
+  if (hg == 0) {
+    // the recorded indices at device scope (sc1), so that this kernel's end
+    // has none of their lines to write back (0.6 us at 4 x 32K)
+    for (int i = t; i < j_end - j_beg; i += kThreads) {
+      int32_t* dst = ta.idx + int64_t(r) * k + j_beg + i;
+      const int v = s_idx[i];
+      asm volatile("global_store_dword %0, %1, off sc1" ::"v"(dst), "v"(v) : "memory");
+    }
+  }
   if constexpr (M == kFP8) {
     if (wave >= 4) return;  // barriers below count the four attention waves only
     attn::attend8(aa, r, split, splits, hg, j_beg, j_end, base, s_idx, u.att);
