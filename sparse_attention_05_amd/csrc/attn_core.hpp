@@ -291,6 +291,14 @@ __device__ __forceinline__ void store_through(float* p, float4 v) {
   const f32x4 x = __builtin_bit_cast(f32x4, v);
   asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(x) : "memory");
 }
+__device__ __forceinline__ void store_through(float* p, float2 v) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 x = {v.x, v.y};
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(x) : "memory");
+}
+__device__ __forceinline__ void store_through(float* p, float v) {
+  asm volatile("global_store_dword %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
 
 // Epilogue of a workgroup: the row sums over the lanes and waves, then the
 // normalised output rows as float4 (splits == 1) or the split's unnormalised
@@ -315,11 +323,11 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, int r, int split
                   float4{acc[vt][0] * inv, acc[vt][1] * inv, acc[vt][2] * inv, acc[vt][3] * inv});
   if (wave == 0 && grp == 0) {
     if (final_out) {
-      if (a.lse) a.lse[rh] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
+      if (a.lse) store_through(a.lse + rh, L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY);
     } else {
       float* ml = static_cast<float*>(a.ws) + int64_t(a.R) * splits * a.H * kValueDim;
       const int64_t slot = (int64_t(r) * splits + split) * a.H + h;
-      *reinterpret_cast<float2*>(ml + 2 * slot) = float2{m_run, L};
+      store_through(ml + 2 * slot, float2{m_run, L});
     }
   }
 }
@@ -712,11 +720,11 @@ __device__ __forceinline__ void attend_bf16(const AttnArgs& a, int r, int split,
                   float4{acc[vt][0] * inv, acc[vt][1] * inv, acc[vt][2] * inv, acc[vt][3] * inv});
   if (wave == 0 && grp == 0) {
     if (final_out) {
-      if (a.lse) a.lse[rh] = L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY;
+      if (a.lse) store_through(a.lse + rh, L > 0.f ? (m_run + __log2f(L)) * kLn2 : -INFINITY);
     } else {
       float* ml = static_cast<float*>(a.ws) + int64_t(a.R) * splits * a.H * kValueDim;
       const int64_t slot = (int64_t(r) * splits + split) * a.H + h;
-      *reinterpret_cast<float2*>(ml + 2 * slot) = float2{m_run, L};
+      store_through(ml + 2 * slot, float2{m_run, L});
     }
   }
 }

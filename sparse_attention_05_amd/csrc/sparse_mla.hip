@@ -582,7 +582,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int splits) {
   // kernel's end to write back, and the next launch starts about 0.7 us
   // sooner at 4 x 32K)
   store_through(a.out + rh * kValueDim + 4 * v4, float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv});
-  if (a.lse && v4 == 0) a.lse[rh] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  if (a.lse && v4 == 0) store_through(a.lse + rh, L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY);
 }
 
 }  // namespace
