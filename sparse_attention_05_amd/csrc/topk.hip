@@ -1002,11 +1002,10 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(TopkArgs a, int sli
     }
   }
   if (t == 0) {
-    // the slice record at device scope (sc1, through the L2 to memory): the
-    // next launch reads every record first, from any XCD, and starts about
-    // 0.5 us sooner at 4 x 32K than after their write-back at this kernel's
-    // end (the values are the same; the candidate words themselves, far more
-    // bytes, measured slower that way)
+    // the slice record at device scope (sc1, through the L2 to memory), like
+    // the words: the next launch reads every record first, from any XCD, and
+    // started about 0.5 us sooner at 4 x 32K than after their write-back at
+    // this kernel's end (the values are the same)
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 rec = {G + E, cmax, pivot, E};
     uint4* dst = reinterpret_cast<uint4*>(a.state) + int64_t(r) * slices + g;
