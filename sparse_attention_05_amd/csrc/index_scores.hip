@@ -475,9 +475,31 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
         for (int blk = 0; blk < 4; ++blk) scb[blk] = bf16_bits_to_f32(scs[16 * blk + col]);
         scl = scs[lane];
       }
+      // ReLU, head weight and the sum over the lane's heads of a tile's
+      // products: this lane's part of one key's score (fp8 with a negative
+      // row scale sc: relu(sc*z) per head, the scale applied first; a
+      // non-negative scale is applied to the summed score instead, and the
+      // factor here is 1, exact, so the code has no branch to split the
+      // instruction stream the scheduler interleaves)
+      auto tile_epi = [&](const f32x4 (&c)[MT], float sc) -> float {
+        float p = 0.f;
+        if constexpr (QK == 2) {
+          const float m = sc < 0.f ? sc : 1.f;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        if (roll) {
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p += wr[mt][i] * relu_bits(m * c[mt][i]);
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p += wr[mt][i] * relu_bits(c[mt][i]);
+        }
+        return p;
+      };
+      if (roll) {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
           // tile blk+2 goes out; tile blk has landed once only the tiles
           // issued after it are outstanding (no store has been issued yet)
           constexpr int LPT = C::LOADS / 4;
@@ -485,28 +507,56 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
           if (blk <= 1) wait_vmcnt<2 * LPT>();
           else if (blk == 2) wait_vmcnt<LPT>();
           else wait_vmcnt<0>();
+          f32x4 acc[MT];
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const F kb = key_frag<QK, DI>(stage, 16 * blk + col, grp, ks);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_k32(qa[mt][ks], kb, ks ? acc[mt] : f32x4{0.f, 0.f, 0.f, 0.f});
+          }
+          part[blk] = tile_epi(acc, scb[blk]);
         }
-        f32x4 acc[MT];
+      } else {
+        // the whole group has landed: tile blk is multiplied from kb[blk&1]
+        // into acc[blk&1] while tile blk-1's epilogue runs from the other
+        // accumulators and tile blk+1's fragments are read into the other
+        // fragment registers, and the scheduler is told to interleave the
+        // three, so the epilogue and the fp8 widening run under the matrix
+        // core's work instead of after it (the same products in the same
+        // order)
+        F kb[2][NKS];
+        f32x4 acc[2][MT];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const F kb = key_frag<QK, DI>(stage, 16 * blk + col, grp, ks);
+        for (int ks = 0; ks < NKS; ++ks) kb[0][ks] = key_frag<QK, DI>(stage, col, grp, ks);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_k32(qa[mt][ks], kb, ks ? acc[mt] : f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int blk = 0; blk < 4; ++blk) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[blk & 1][mt] = mfma_k32(qa[mt][ks], kb[blk & 1][ks], ks ? acc[blk & 1][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
+          if (blk > 0) part[blk - 1] = tile_epi(acc[(blk - 1) & 1], scb[blk - 1]);
+          if (blk + 1 < 4) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) kb[(blk + 1) & 1][ks] = key_frag<QK, DI>(stage, 16 * (blk + 1) + col, grp, ks);
+          }
+          // the next tile's fragment reads first, then each MFMA followed
+          // by VALU work: the previous tile's epilogue (and, fp8, the
+          // widening of the fragments just read)
+          __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+#pragma unroll
+          for (int i = 0; i < MT * NKS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, QK == 2 ? 4 : 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+          // the epilogue's result is defined here, so that it is not sunk
+          // to the score store after the last tile
+          if (blk > 0) asm volatile("" : "+v"(part[blk - 1]));
+          __builtin_amdgcn_sched_barrier(0);
         }
-        float p = 0.f;
-        if (QK == 2 && scb[blk] < 0.f) {
-          // relu(sc*z) with a negative row scale: scale each dot first
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p += wr[mt][i] * relu_bits(scb[blk] * acc[mt][i]);
-        } else {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p += wr[mt][i] * relu_bits(acc[mt][i]);
-        }
-        part[blk] = p;
+        part[3] = tile_epi(acc[1], scb[3]);
       }
       // this stage is consumed: refill it with group g + NS
       if (issued < groups) {

@@ -178,6 +178,38 @@ def test_scores_within_error_bound(dsa, case):
         C.assert_scores_close(p, r, got[r])
 
 
+@pytest.mark.parametrize("key_dtype,lens", [
+    ("bf16", [70000, 66000, 300]),       # up to 64 rows: the length-balanced split
+    ("fp8_e4m3", [70000, 66000, 300]),
+    ("bf16", [3000] * 80),               # more rows: the (query, key chunk) grid
+    ("fp8_e4m3", [3000] * 79 + [40]),
+])
+def test_scores_several_groups_per_wave_and_negative_fp8_scales(dsa, key_dtype, lens):
+    """Rows long enough that each wave of the decode-form indexer streams
+    several 64-key groups (a tile's products multiplied while the previous
+    tile's epilogue runs), in both grid forms; fp8 keys with a tenth of the
+    row scales negated (relu(scale * dot) per head there). Scores within the
+    bound of the oracle's, through both the q_pos and the seq_len entry."""
+    import torch
+    fp8 = key_dtype == "fp8_e4m3"
+    p = inputs.decode_config(lens, seed=90 + len(lens), k=2048, key_dtype=key_dtype,
+                             boost_frac=0.02 if fp8 else 0.0)
+    if fp8:
+        rng = np.random.default_rng(len(lens))
+        neg = rng.random(p.k_scale.shape[0]) < 0.1
+        p.k_scale = np.where(neg, p.k_scale | np.uint16(0x8000), p.k_scale).astype(np.uint16)
+    _say("scores, several groups per wave", key_dtype, len(lens), "rows")
+    got, d = _gpu_scores(dsa, p)
+    dec = dsa.dsa_index_scores_decode(d.q_idx, d.head_w, d.k_idx, d.row_off, d.seq_len, int(p.seq_len.max()),
+                                      k_scale=d.k_scale)
+    torch.cuda.synchronize()
+    dec = dec.cpu().numpy()
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        C.assert_scores_close(p, r, got[r])
+        assert np.array_equal(dec[r, :n], got[r, :n]), f"row {r}: the two entries differ"
+
+
 def test_fp8_codes_decode_exactly(dsa):
     # Row s holds code (s*128 + d) mod 256 in dim d: every code appears. Two
     # heads read dim d with signs +1/-1 and weights 1 and 0.5, so the score is
