@@ -227,6 +227,23 @@ def copy_gbps(nbytes: int = 1 << 30, reps: int = 20) -> float:
     return 2 * nbytes / secs / 1e9
 
 
+def read_probe_gbps(dsa, nbytes: int, steps: int):
+    """The library's plain streaming read (dsa_read_probe) of nbytes, timed
+    like the indexer: back-to-back launches over enough copies that the
+    256 MB MALL cannot serve a repeat. Returns (GB/s, us per launch)."""
+    import torch
+    nb = (nbytes + 15) // 16 * 16
+    copies = max(2, -(-(1200 << 20) // nb))
+    bufs = [torch.ones(nb // 4, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    out = torch.empty(dsa.lib.dsa_read_probe_blocks(), dtype=torch.float32, device="cuda")
+    fn = lambda i: dsa.dsa_read_probe(bufs[i], out=out)
+    for i in range(2 * copies):
+        fn(i % copies)
+    us = timed_steps(fn, max(steps, 2 * copies), copies) * 1e3
+    del bufs
+    return nb / (us * 1e-6) / 1e9, us
+
+
 def cpu_baseline(p, budget_s: float):
     from oracle import dsa_oracle as O
     try:
@@ -520,6 +537,41 @@ def decode_run(args, name, full):
                       "indexer_dim": p.D_I, "indexer_keys": p.key_dtype, "mla_heads": p.H, "latent_dim": 576,
                       "latent": p.kv_dtype, "tokens_per_seq": m, "page_size": p.page_size or None,
                       "input_sets": n_sets}}
+    # ---- the indexer alone: K back-to-back launches of the step's first kernel -----------
+    res["indexer_roofline"] = None
+    if not paged:
+        scores = [torch.empty((p.R, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
+
+        def index(i):
+            d = sets[i]
+            dsa.dsa_index_scores_decode(d.q_idx, d.head_w, d.k_idx, d.row_off, d.seq_len, max_len, q_per_seq=m,
+                                        k_scale=d.k_scale, scores=scores[i])
+
+        # warmed up on its own for 0.5 s first, as the prefill indexer
+        t_warm, i = time.perf_counter(), 0
+        while time.perf_counter() - t_warm < 0.5:
+            index(i % n_sets)
+            i += 1
+            if i % 50 == 0:
+                torch.cuda.synchronize()
+        idx_us = timed_steps(index, args.steps, n_sets) * 1e3
+        ib = indexer_bytes(p)
+        achieved = ib / (idx_us * 1e-6) / 1e9
+        idx_tflops = 2.0 * p.H_I * p.D_I * sum(int(x) + 1 for x in p.q_pos.astype(int)) / (idx_us * 1e-6) / 1e12
+        log(f"bench: indexer {idx_us:.2f} us/launch, {achieved:,.0f} GB/s algorithmic, {idx_tflops:.0f} TFLOP/s")
+        copy = copy_gbps()
+        log(f"bench: device copy {copy:,.0f} GB/s (read + write)")
+        read_gbs, read_us = read_probe_gbps(dsa, ib, args.steps)
+        log(f"bench: plain read of the indexer's {ib / 1e6:.1f} MB {read_us:.2f} us/launch = {read_gbs:,.0f} GB/s "
+            f"(indexer at {achieved / read_gbs:.2f} of it)")
+        rec = pmc_traffic(name)
+        kr = rec["kernels"].get("index_scores_kernel") if rec else None
+        res["indexer_roofline"] = {
+            "kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": kr["bytes_per_launch"] if kr else None,
+            "bytes_per_launch": ib, "us_per_launch": idx_us, "tflops": idx_tflops, "copy_gbps_measured": copy,
+            "frac_of_copy": achieved / copy, "read_gbps_measured": read_gbs, "read_us_per_launch": read_us,
+            "frac_of_read": achieved / read_gbs}
     if not full:
         del calls, sets, base, aws, outs
         torch.cuda.empty_cache()
@@ -603,37 +655,6 @@ def decode_run(args, name, full):
             f"(merged selection equals the unsharded one: {cp['merged_equals_unsharded']})")
         res["context_parallel"] = cp
 
-    # ---- the indexer alone: K back-to-back launches of the step's first kernel -----------
-    res["indexer_roofline"] = None
-    if not paged:
-        scores = [torch.empty((p.R, (max_len + 3) // 4 * 4), dtype=torch.float32, device="cuda") for _ in sets]
-
-        def index(i):
-            d = sets[i]
-            dsa.dsa_index_scores_decode(d.q_idx, d.head_w, d.k_idx, d.row_off, d.seq_len, max_len, q_per_seq=m,
-                                        k_scale=d.k_scale, scores=scores[i])
-
-        # warmed up on its own for 0.5 s first, as the prefill indexer
-        t_warm, i = time.perf_counter(), 0
-        while time.perf_counter() - t_warm < 0.5:
-            index(i % n_sets)
-            i += 1
-            if i % 50 == 0:
-                torch.cuda.synchronize()
-        idx_us = timed_steps(index, args.steps, n_sets) * 1e3
-        ib = indexer_bytes(p)
-        achieved = ib / (idx_us * 1e-6) / 1e9
-        idx_tflops = 2.0 * p.H_I * p.D_I * sum(int(x) + 1 for x in p.q_pos.astype(int)) / (idx_us * 1e-6) / 1e12
-        log(f"bench: indexer {idx_us:.2f} us/launch, {achieved:,.0f} GB/s algorithmic, {idx_tflops:.0f} TFLOP/s")
-        copy = copy_gbps()
-        log(f"bench: device copy {copy:,.0f} GB/s (read + write)")
-        rec = pmc_traffic(name)
-        kr = rec["kernels"].get("index_scores_kernel") if rec else None
-        res["indexer_roofline"] = {
-            "kernel": "index_scores", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": kr["bytes_per_launch"] if kr else None,
-            "bytes_per_launch": ib, "us_per_launch": idx_us, "tflops": idx_tflops, "copy_gbps_measured": copy,
-            "frac_of_copy": achieved / copy}
     return p, res
 
 

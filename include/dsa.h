@@ -365,6 +365,22 @@ size_t dsa_workspace_size(int32_t entry, int32_t rows, int32_t max_len, int32_t 
 dsa_status dsa_check_indices(const int32_t* idx, const int32_t* q_pos, int32_t R, int32_t k,
                              int32_t* n_bad, void* stream);
 
+/*
+ * dsa_read_probe -- a measurement aid, no part of the method: a plain
+ * streaming read of `bytes` bytes of device memory at `buf` (16-byte aligned,
+ * bytes a positive multiple of 16), the attainable rate beside the published
+ * HBM peak for a kernel that reads its operand once (the indexer's key stream
+ * in "GLM-5: from Vibe Coding to Agentic Engineering", section 2.1.1: the
+ * indexer scores every cached key once per query). One workgroup per CU
+ * (dsa_read_probe_blocks() of them) reads the buffer in one contiguous sweep;
+ * workgroup g writes the fp32 sum of the floats it read to out[g] (device,
+ * out_len >= dsa_read_probe_blocks()), in an order that depends on the grid.
+ * Enqueued on `stream`; DSA_ERR_NULL / DSA_ERR_SHAPE / DSA_ERR_ALIGN for bad
+ * arguments before any launch.
+ */
+int32_t dsa_read_probe_blocks(void);
+dsa_status dsa_read_probe(const void* buf, uint64_t bytes, float* out, int32_t out_len, void* stream);
+
 /* Text of a status code (static storage). */
 const char* dsa_status_string(int32_t status);
 

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["index_scores.hip", "topk.hip", "sparse_mla.hip", "dsa_api.hip", "check.hip", "cp.hip"]
+SOURCES = ["index_scores.hip", "topk.hip", "sparse_mla.hip", "dsa_api.hip", "check.hip", "cp.hip", "read_probe.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

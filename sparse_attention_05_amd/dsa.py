@@ -48,6 +48,8 @@ SIGNATURES = {
     "dsa_attn_merge": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "dsa_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "dsa_check_indices": (_I32, [_P, _P, _I32, _I32, _P, _P]),
+    "dsa_read_probe_blocks": (_I32, []),
+    "dsa_read_probe": (_I32, [_P, ctypes.c_uint64, _P, _I32, _P]),
     "dsa_status_string": (ctypes.c_char_p, [_I32]),
     "dsa_last_error": (ctypes.c_char_p, []),
 }
@@ -230,6 +232,18 @@ def dsa_check_indices(idx: torch.Tensor, q_pos: torch.Tensor, *, n_bad: Optional
     st = lib.dsa_check_indices(_ptr(idx), _ptr(q_pos), R, k, _ptr(n_bad), _stream(stream))
     _check(st, "dsa_check_indices")
     return n_bad
+
+
+def dsa_read_probe(buf: torch.Tensor, *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """A plain streaming read of buf's bytes (a measurement aid, no part of
+    the method): out[g] = the fp32 sum of the floats workgroup g read, one
+    workgroup per CU; returns out."""
+    G = lib.dsa_read_probe_blocks()
+    if out is None:
+        out = torch.empty(G, dtype=torch.float32, device=buf.device)
+    st = lib.dsa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), out.numel(), _stream(stream))
+    _check(st, "dsa_read_probe")
+    return out
 
 
 def dsa_topk_pairs(scores: torch.Tensor, idx: torch.Tensor, key_offset: int, *, pair_score=None, pair_idx=None,

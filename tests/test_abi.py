@@ -190,6 +190,15 @@ def test_check_indices_rejects(dsa):
     assert lib.dsa_check_indices(None, None, 0, 64, A, None) == dsa.DSA_OK  # nothing to check
 
 
+def test_read_probe_rejects_before_any_device_call(dsa):
+    lib = dsa.lib
+    assert lib.dsa_read_probe(None, 1024, A, 256, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_read_probe(A, 1024, None, 256, None) == dsa.DSA_ERR_NULL
+    assert lib.dsa_read_probe(A, 0, A, 256, None) == dsa.DSA_ERR_SHAPE
+    assert lib.dsa_read_probe(A, 1000, A, 256, None) == dsa.DSA_ERR_SHAPE
+    assert lib.dsa_read_probe(A + 8, 1024, A, 256, None) == dsa.DSA_ERR_ALIGN
+
+
 def test_workspace_sizes_are_aligned(dsa):
     for rows, k, H in [(1, 64, 8), (4, 2048, 64), (16, 2048, 64), (8192, 2048, 64)]:
         assert dsa.dsa_workspace_size(dsa.DSA_ENTRY_SPARSE_MLA, rows, 0, k, H) % 256 == 0

@@ -210,6 +210,19 @@ def test_scores_several_groups_per_wave_and_negative_fp8_scales(dsa, key_dtype, 
         assert np.array_equal(dec[r, :n], got[r, :n]), f"row {r}: the two entries differ"
 
 
+def test_read_probe_reads_every_piece_once(dsa):
+    """The streaming-read reference (a measurement aid beside the indexer's
+    roofline) reads each 16-byte piece once: the workgroups' sums add up to
+    the buffer's, for a size that is no multiple of the grid's sweep."""
+    import torch
+    n = (1 << 20) + 12
+    x = torch.arange(n, dtype=torch.float32, device="cuda") % 7   # small integers: fp32 sums are exact
+    out = dsa.dsa_read_probe(x)
+    torch.cuda.synchronize()
+    assert out.numel() == dsa.lib.dsa_read_probe_blocks()
+    assert float(out.double().sum()) == float(x.double().sum())
+
+
 def test_fp8_codes_decode_exactly(dsa):
     # Row s holds code (s*128 + d) mod 256 in dim d: every code appears. Two
     # heads read dim d with signs +1/-1 and weights 1 and 0.5, so the score is
