@@ -664,6 +664,13 @@ constexpr int kPfWaves = 8;
 constexpr int kPfRows = kPfWaves;
 constexpr int kPfKeys = 128;  // keys per group (one barrier each)
 constexpr int kPfTiles = kPfKeys / 16;
+// fp8 keys in the multi-token form: groups of 256 keys, so that each wave
+// has as many tiles per barrier as a bf16 group gives it (the ring takes the
+// same bytes, and two of its stages take the staged queries)
+template <int QK, bool SLICED>
+constexpr int pf_keys() {
+  return QK == 2 && SLICED ? 2 * kPfKeys : kPfKeys;
+}
 constexpr int kPfStages = 4;
 
 
@@ -680,17 +687,64 @@ __device__ __forceinline__ void wait_ahead(int ahead) {
 
 
 
+// Length-balanced slices of the multi-token decode form (B <= 64 sequences,
+// a 1-D grid of G >= B workgroups): every wave works out the same shares
+// from all the sequences' lengths (lane b: sequence b, its first cache row
+// loaded in the same round trip), with no barrier. Sequence b gets
+// 1 + floor((G - B) u_b / U) workgroups, u_b its groups of PK keys (up to its
+// last token's key count) and U their sum, consecutive in the grid, each
+// taking an equal run of its groups; returns this workgroup's sequence, its
+// first cache row and length, and its key range (empty past every share).
+// A grid cut by the longest sequence alone left the CUs of the shorter
+// sequences' missing slices idle.
+template <int PK>
+__device__ __forceinline__ void balanced_slice(const IndexArgs& a, int w, int G, int& b, int64_t& base,
+                                               int64_t& slen, int64_t& k_beg, int64_t& k_lim) {
+  b = 0;
+  base = 0;
+  slen = 0;
+  k_beg = 0;
+  k_lim = 0;
+  const int lane = threadIdx.x & 63;
+  int64_t bl = 0;
+  int32_t sl = 0;
+  if (lane < a.B) {
+    bl = a.row_off[lane];
+    sl = a.seq_len[lane];
+  }
+  const int64_t nl = sl <= 0 ? 0 : (sl < a.max_n ? sl : a.max_n);
+  const uint32_t ul = uint32_t((nl + PK - 1) / PK);  // <= 2^15 groups
+  uint32_t tot = ul;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) tot += __shfl_xor(tot, d, 64);
+  uint32_t share = 0;
+  if (lane < a.B) share = 1u + (tot ? uint32_t(G - a.B) * ul / tot : 0u);  // (G - B) ul < 2^23
+  const uint32_t incl = wave_incl_scan(share);
+  const unsigned long long hit = __ballot(lane < a.B && uint32_t(w) < incl && uint32_t(w) >= incl - share);
+  if (hit == 0ull) return;
+  b = __ffsll(static_cast<long long>(hit)) - 1;
+  const uint32_t sh_b = __builtin_amdgcn_readlane(share, b);
+  const uint32_t first = __builtin_amdgcn_readlane(incl, b) - sh_b;
+  const uint32_t gpw = (__builtin_amdgcn_readlane(ul, b) + sh_b - 1) / sh_b;
+  base = (int64_t(__builtin_amdgcn_readlane(uint32_t(uint64_t(bl) >> 32), b)) << 32) |
+         __builtin_amdgcn_readlane(uint32_t(bl), b);
+  slen = int32_t(__builtin_amdgcn_readlane(uint32_t(sl), b));
+  k_beg = int64_t(w - int(first)) * gpw * PK;
+  k_lim = k_beg + int64_t(gpw) * PK;
+}
+
 // kPfWaves waves share a ring of key groups; QW query rows of one sequence
 // per workgroup, each row's tiles split over kPfWaves / QW waves (QW = 8:
-// one wave per row, all 8 tiles of a group; QW = 4: two waves per row, 4
-// tiles each).
+// one wave per row, all the tiles of a group; QW = 4: two waves per row,
+// half the tiles each).
 // SLICED false (prefill form: B = 1, q_pos given, QW = 8): workgroup
 // blockIdx.x takes rows 8*blk .. +7, counted from the last, and keys 0 ..
 // the end of its longest row.
 // SLICED true (decode form with qps <= QW new tokens per sequence):
 // workgroup (blockIdx.x, blockIdx.y) takes the qps rows of sequence
-// blockIdx.y and its keys kps*blockIdx.x .. +kps-1, so each key row is read
-// once for all of them; rows past qps are idle. With QW = 4 the query rows
+// blockIdx.y and its keys kps*blockIdx.x .. +kps-1 (kps = 0: the 1-D
+// length-balanced grid, balanced_slice), so each key row is read once for
+// all of them; rows past qps are idle. With QW = 4 the query rows
 // and head weights go to LDS once per workgroup (through ring stages 2-3,
 // while key groups 0-1 load) instead of every wave loading its row.
 // Scores (and the score sample, when asked) are stored up to each row's end.
@@ -701,24 +755,27 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   static_assert(QK == 1 || (QK == 2 && SLICED), "fp8 keys: the multi-token decode form only");
   constexpr int RW = kPfWaves;
   constexpr int NKS = DI / 32;
-  constexpr int GB = kPfKeys * C::ROW;      // bytes per group
+  constexpr int PK = pf_keys<QK, SLICED>();  // keys per group
+  constexpr int GB = PK * C::ROW;           // bytes per group
   constexpr int KL = GB / 1024 / RW;        // key loads per wave per group
-  constexpr int LPW = KL + (QK == 2 ? 1 : 0);  // + fp8: the row scales of 16 keys
-  constexpr int TPW = kPfTiles * QW / RW;   // tiles per wave per group
+  constexpr int LPW = KL + (QK == 2 ? 1 : 0);  // + fp8: the row scales of PK/8 keys
+  constexpr int TPW = PK / 16 * QW / RW;    // tiles per wave per group
   constexpr bool QLDS = SLICED && QW == 4;  // query rows staged in LDS
   constexpr int QCPR = DI / 8;              // 16-byte chunks per query row
   constexpr int QB = 16 * MT * DI * 2;      // staged bytes per query (heads padded to 16*MT)
   static_assert((GB / 1024) % RW == 0, "group loads split evenly over the waves");
   static_assert(kPfStages >= 3, "a group lands while the one before it is multiplied");
   static_assert(TPW % 4 == 0, "a wave's tiles of a group form whole 64-key score stores");
-  static_assert(!QLDS || QK != 1 || QW * QB <= 2 * GB, "the staged bf16 queries fit two ring stages");
+  constexpr bool QRING = QK == 1 || PK > kPfKeys;  // queries staged through ring stages 2-3
+  static_assert(!QLDS || !QRING || QW * QB <= 2 * GB, "the staged bf16 queries fit two ring stages");
   __shared__ __attribute__((aligned(1024))) char ring[kPfStages][GB];
   __shared__ __attribute__((aligned(16))) float s_w[QLDS ? QW : 1][64];
   // fp8: row scales (bf16 bits, zero-extended words); wave w's dma2 fills
-  // words 64w .. 64w+63, the first 16 for keys 16w .. 16w+15 of the group
+  // words 64w .. 64w+63, the first PK/8 for keys (PK/8)w .. (PK/8)(w+1)-1
+  // of the group
   __shared__ __attribute__((aligned(16))) uint32_t s_ksc[QK == 2 ? kPfStages : 1][QK == 2 ? RW * 64 : 1];
-  // fp8 stages are too small to stage the queries in: a buffer of their own
-  __shared__ __attribute__((aligned(1024))) char s_qst[QLDS && QK == 2 ? QW * QB : 16];
+  // stages too small to stage the queries in: a buffer of their own
+  __shared__ __attribute__((aligned(1024))) char s_qst[QLDS && !QRING ? QW * QB : 16];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -727,7 +784,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   const int tb = (wave / QW) * TPW;            // its first tile of each group
 
   int r0, nrows, b;
-  int64_t k_beg, k_lim;
+  int64_t k_beg, k_lim, base, slen = 0;
   if constexpr (!SLICED) {
     const int blk = int(gridDim.x) - 1 - int(blockIdx.x);
     r0 = blk * QW;
@@ -735,18 +792,24 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     b = 0;
     k_beg = 0;
     k_lim = a.max_n;
+    base = a.row_off[0];
   } else {
-    b = blockIdx.y;
+    if (kps > 0) {
+      b = blockIdx.y;
+      k_beg = int64_t(blockIdx.x) * kps;
+      k_lim = k_beg + kps;
+      base = a.row_off[b];
+      slen = a.seq_len[b];
+    } else {
+      balanced_slice<PK>(a, int(blockIdx.x), int(gridDim.x), b, base, slen, k_beg, k_lim);
+    }
     r0 = b * a.qps;
     nrows = a.qps < QW ? a.qps : QW;
-    k_beg = int64_t(blockIdx.x) * kps;
-    k_lim = k_beg + kps;
   }
-  const int64_t base = a.row_off[b];
   const bool base_ok = base >= 0 && base < a.cache_rows;
   auto row_n = [&](int i) -> int64_t {
     const int rr = r0 + i;
-    int64_t n = (a.q_pos ? int64_t(a.q_pos[rr]) : int64_t(a.seq_len[b]) - a.qps + i) + 1;
+    int64_t n = (a.q_pos ? int64_t(a.q_pos[rr]) : slen - a.qps + i) + 1;
     if (n > a.max_n) n = a.max_n;
     if (n > a.cache_rows - base) n = a.cache_rows - base;
     return base_ok && n > 0 ? n : 0;
@@ -760,7 +823,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     n_wg = ni > n_wg ? ni : n_wg;
   }
   const int64_t k_end = n_wg < k_lim ? n_wg : k_lim;
-  const int groups = k_end > k_beg ? int((k_end - k_beg + kPfKeys - 1) / kPfKeys) : 0;
+  const int groups = k_end > k_beg ? int((k_end - k_beg + PK - 1) / PK) : 0;
   if (groups == 0) return;  // the same for every wave of the workgroup
 
   // Group g is the buffer of key rows k_beg + 128*g .. k_end-1 (rows past
@@ -779,15 +842,16 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   }
   auto issue = [&](int g) {
     const uint32_t to = lds_addr(ring[g % kPfStages]);
-    const int64_t s0 = int64_t(g) * kPfKeys;
+    const int64_t s0 = int64_t(g) * PK;
     const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(keys + s0 * C::ROW), 0, int((span - s0) * C::ROW), 0x00020000);
 #pragma unroll
     for (int j = 0; j < KL; ++j) dma16_buf(src, src_off[j], to + 1024 * (wave * KL + j));
     if constexpr (QK == 2) {
-      // scales of keys s0 + 16*wave .. +15 (zero past the range)
-      const int64_t first = s0 + 16 * wave;
-      const int64_t cnt = span - first < 16 ? (span - first > 0 ? span - first : 0) : 16;
+      // scales of keys s0 + (PK/8)*wave .. +PK/8-1 (zero past the range)
+      constexpr int SPW = PK / 8;
+      const int64_t first = s0 + SPW * wave;
+      const int64_t cnt = span - first < SPW ? (span - first > 0 ? span - first : 0) : SPW;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(a.k_scale + base + k_beg + (cnt > 0 ? first : 0)), 0, int(2 * cnt), 0x00020000);
       dma2_buf(rs, uint32_t(2 * lane), lds_addr(&s_ksc[g % kPfStages][64 * wave]));
@@ -802,7 +866,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     // and idle rows zeroed) and head weights into LDS, ahead of key groups
     // 0-1; once every wave's part has landed the fragments go to registers
     // and stages 2-3 take key groups 2-3
-    char* qst = QK == 1 ? ring[2] : s_qst;
+    char* qst = QRING ? ring[2] : s_qst;
     const uint32_t qlds = lds_addr(qst);
     for (int m = wave; 64 * m < QW * 16 * MT * QCPR; m += RW) {
       const int pch = 64 * m + lane;
@@ -882,7 +946,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   };
   // fp8: row scale of key j of group g's stage
   auto key_scale = [&](int g, int j) -> float {
-    return bf16_bits_to_f32(s_ksc[g % kPfStages][64 * (j >> 4) + (j & 15)]);
+    return bf16_bits_to_f32(s_ksc[g % kPfStages][64 * (j / (PK / 8)) + (j % (PK / 8))]);
   };
   // ReLU, head weight and the sum over the lane's 4 heads of each of the MT
   // head tiles: this lane's part of the score of key 16*t + n (fp8 with a
@@ -937,7 +1001,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
     // own parts of group g+1 landed (its first tile is read during this
     // group's last one): behind them are the direct loads of the later
     // groups and spg score stores per group since
-    if (g + 1 < groups) wait_ops<LPW * (kPfStages - 2) + kPfTiles / 2 * (kPfStages - 1)>(
+    if (g + 1 < groups) wait_ops<LPW * (kPfStages - 2) + PK / 32 * (kPfStages - 1)>(
         LPW * (issued - (g + 2)) + spg * (g < kPfStages - 2 ? g : kPfStages - 2));
     // every part of g+1 has landed; every wave is done with group g-1, so
     // its stage takes group g-1 + kPfStages
@@ -980,7 +1044,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
         if (!(sc < 0.f)) v *= sc;
       }
       // non-temporal: the scores are read by the next kernel, not this one
-      const int key = g * kPfKeys + 16 * tb + 64 * h + lane;
+      const int key = g * PK + 16 * tb + 64 * h + lane;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srow, key * 4, 0, 2);
       if constexpr (SLICED) {
         if (smp) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ssmp, (key & 15) ? -16 : (key >> 4) * 4, 0, 2);
@@ -996,14 +1060,24 @@ hipError_t launch_prefill(const IndexArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Decode form with 2..8 new tokens per sequence: a workgroup per (key slice,
-// sequence), the slices sized so that the grid covers the CUs about once.
+// Decode form with 2..8 new tokens per sequence. Up to 64 sequences: one
+// workgroup per CU, the CUs shared out by the sequences' lengths
+// (balanced_slice). More: a workgroup per (key slice, sequence), the slices
+// sized so that the grid covers the CUs about once.
 template <int QK, int MT, int DI>
 hipError_t launch_multi_token(const IndexArgs& a, hipStream_t stream) {
   const int cus = device_cu_count();
+  if (a.B <= 64 && a.B <= cus) {
+    // one workgroup per CU, shared out by the sequences' lengths (read on
+    // the device)
+    if (a.qps <= 4) index_scores_prefill_kernel<QK, MT, DI, 4, true><<<dim3(unsigned(cus)), kPfWaves * 64, 0, stream>>>(a, 0);
+    else index_scores_prefill_kernel<QK, MT, DI, 8, true><<<dim3(unsigned(cus)), kPfWaves * 64, 0, stream>>>(a, 0);
+    return hipGetLastError();
+  }
   const int per_seq = (cus + a.B - 1) / a.B;
   int64_t kps = (int64_t(a.max_n) + per_seq - 1) / per_seq;
-  kps = (kps + kPfKeys - 1) / kPfKeys * kPfKeys;
+  constexpr int PK = pf_keys<QK, true>();
+  kps = (kps + PK - 1) / PK * PK;
   const unsigned slices = unsigned((a.max_n + kps - 1) / kps);
   const dim3 grid(slices, unsigned(a.B));
   if (a.qps <= 4) index_scores_prefill_kernel<QK, MT, DI, 4, true><<<grid, kPfWaves * 64, 0, stream>>>(a, int(kps));

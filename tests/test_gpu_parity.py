@@ -687,6 +687,8 @@ def _fused_multi(dsa, p, d):
     (2, [9000, 16385, 12000], "bf16", "fp8_e4m3"),
     (3, [5000, 8200, 4], "bf16", "bf16"),                   # idle wave; a sequence of 4 tokens
     (8, [10000, 2500], "bf16", "bf16"),                     # eight waves, one per token
+    (2, [700] * 66 + [3000], "bf16", "bf16"),               # over 64 sequences: the (slice, sequence) grid
+    (2, [700] * 66 + [3000], "fp8_e4m3", "bf16"),
     (4, [9000, 3000], "fp8_e4m3", "bf16"),                  # fp8 keys in the shared key stream
 ])
 def test_fused_multi_token_decode(dsa, m, lens, key_dtype, latent_dtype):
