@@ -678,7 +678,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
               "supported. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.pmc_pass:
