@@ -25,6 +25,8 @@
 // butterfly then leaves lane l with the full score of key s0 + l, so the 64
 // scores go out as one coalesced 256-byte store. Every sum has a fixed order:
 // the scores are bitwise reproducible.
+#include <type_traits>
+
 #include "dsa_common.hpp"
 #include "dsa_internal.hpp"
 
@@ -476,14 +478,16 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
         scl = scs[lane];
       }
       // ReLU, head weight and the sum over the lane's heads of a tile's
-      // products: this lane's part of one key's score (fp8 with a negative
-      // row scale sc: relu(sc*z) per head, the scale applied first; a
-      // non-negative scale is applied to the summed score instead, and the
-      // factor here is 1, exact, so the code has no branch to split the
-      // instruction stream the scheduler interleaves)
-      auto tile_epi = [&](const f32x4 (&c)[MT], float sc) -> float {
+      // products: this lane's part of one key's score. fp8 keys with a
+      // negative row scale sc (NEG: some key of the group has one): relu(sc*z)
+      // per head, the scale applied first; a non-negative scale is applied to
+      // the summed score instead, and the factor here is 1, exact, so the
+      // code has no branch to split the instruction stream the scheduler
+      // interleaves. Without NEG the factor is left out.
+      auto tile_epi = [&](const f32x4 (&c)[MT], float sc, auto neg) -> float {
+        constexpr bool NEG = decltype(neg)::value;
         float p = 0.f;
-        if constexpr (QK == 2) {
+        if constexpr (QK == 2 && NEG) {
           const float m = sc < 0.f ? sc : 1.f;
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
@@ -514,7 +518,7 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_k32(qa[mt][ks], kb, ks ? acc[mt] : f32x4{0.f, 0.f, 0.f, 0.f});
           }
-          part[blk] = tile_epi(acc, scb[blk]);
+          part[blk] = tile_epi(acc, scb[blk], std::integral_constant<bool, QK == 2>{});
         }
       } else {
         // the whole group has landed: tile blk is multiplied from kb[blk&1]
@@ -524,39 +528,47 @@ __global__ __launch_bounds__((KeyCfg<QK, DI>::W * 64)) void index_scores_kernel(
         // three, so the epilogue and the fp8 widening run under the matrix
         // core's work instead of after it (the same products in the same
         // order)
-        F kb[2][NKS];
-        f32x4 acc[2][MT];
+        auto tiles = [&](auto neg) {
+          F kb[2][NKS];
+          f32x4 acc[2][MT];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) kb[0][ks] = key_frag<QK, DI>(stage, col, grp, ks);
+          for (int ks = 0; ks < NKS; ++ks) kb[0][ks] = key_frag<QK, DI>(stage, col, grp, ks);
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          __builtin_amdgcn_sched_barrier(0);
+          for (int blk = 0; blk < 4; ++blk) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              acc[blk & 1][mt] = mfma_k32(qa[mt][ks], kb[blk & 1][ks], ks ? acc[blk & 1][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
-          if (blk > 0) part[blk - 1] = tile_epi(acc[(blk - 1) & 1], scb[blk - 1]);
-          if (blk + 1 < 4) {
+              for (int mt = 0; mt < MT; ++mt)
+                acc[blk & 1][mt] = mfma_k32(qa[mt][ks], kb[blk & 1][ks], ks ? acc[blk & 1][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
+            if (blk > 0) part[blk - 1] = tile_epi(acc[(blk - 1) & 1], scb[blk - 1], neg);
+            if (blk + 1 < 4) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) kb[(blk + 1) & 1][ks] = key_frag<QK, DI>(stage, 16 * (blk + 1) + col, grp, ks);
+              for (int ks = 0; ks < NKS; ++ks) kb[(blk + 1) & 1][ks] = key_frag<QK, DI>(stage, 16 * (blk + 1) + col, grp, ks);
+            }
+            // the next tile's fragment reads first, then each MFMA followed
+            // by VALU work: the previous tile's epilogue (and, fp8, the
+            // widening of the fragments just read)
+            __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+#pragma unroll
+            for (int i = 0; i < MT * NKS; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, QK == 2 ? 4 : 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+            // the epilogue's result is defined here, so that it is not sunk
+            // to the score store after the last tile
+            if (blk > 0) asm volatile("" : "+v"(part[blk - 1]));
+            __builtin_amdgcn_sched_barrier(0);
           }
-          // the next tile's fragment reads first, then each MFMA followed
-          // by VALU work: the previous tile's epilogue (and, fp8, the
-          // widening of the fragments just read)
-          __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
-#pragma unroll
-          for (int i = 0; i < MT * NKS; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, QK == 2 ? 4 : 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
-          // the epilogue's result is defined here, so that it is not sunk
-          // to the score store after the last tile
-          if (blk > 0) asm volatile("" : "+v"(part[blk - 1]));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        part[3] = tile_epi(acc[1], scb[3]);
+          part[3] = tile_epi(acc[1], scb[3], neg);
+        };
+        // a negative row scale among the group's keys is rare: the group runs
+        // the form without the per-head factor otherwise (same bits)
+        bool neg = false;
+        if constexpr (QK == 2) neg = __ballot(bf16_bits_to_f32(scl) < 0.f) != 0ull;
+        if (neg) tiles(std::integral_constant<bool, true>{});
+        else tiles(std::integral_constant<bool, false>{});
       }
       // this stage is consumed: refill it with group g + NS
       if (issued < groups) {
