@@ -964,14 +964,19 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   // head tiles: this lane's part of the score of key 16*t + n (fp8 with a
   // negative row scale sc: relu(sc * dot) per head; a non-negative scale is
   // applied to the summed score)
-  auto tile_epi = [&](const f32x4 (&c)[MT], float sc) -> float {
+  // (NEG: some key of the wave's tiles of the group has a negative scale;
+  // the factor is then taken branch-free, 1 (exact) for the others, so no
+  // branch splits the instruction stream the scheduler interleaves)
+  auto tile_epi = [&](const f32x4 (&c)[MT], float sc, auto neg) -> float {
+    constexpr bool NEG = decltype(neg)::value;
     float pm[MT];
-    if (QK == 2 && sc < 0.f) {
+    if constexpr (QK == 2 && NEG) {
+      const float m = sc < 0.f ? sc : 1.f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        pm[mt] = wr[mt][0] * relu_bits(sc * c[mt][0]);
+        pm[mt] = wr[mt][0] * relu_bits(m * c[mt][0]);
 #pragma unroll
-        for (int i = 1; i < 4; ++i) pm[mt] += wr[mt][i] * relu_bits(sc * c[mt][i]);
+        for (int i = 1; i < 4; ++i) pm[mt] += wr[mt][i] * relu_bits(m * c[mt][i]);
       }
     } else {
 #pragma unroll
@@ -1023,30 +1028,43 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
       ++issued;
     }
     float part[TPW];
+    auto run_tiles = [&](auto neg) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < TPW; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[t & 1][mt] =
-              mfma_k32(qa[mt][ks], kb[t & 1][ks], ks ? acc[t & 1][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
-      if (t > 0) part[t - 1] = tile_epi(acc[(t - 1) & 1], QK == 2 ? key_scale(g, 16 * (tb + t - 1) + col) : 1.f);
-      if (t + 1 < TPW) tile_frags(g, tb + t + 1, kb[(t + 1) & 1]);
-      else tile_frags(g + 1, tb, kb[(t + 1) & 1]);
-      // each MFMA followed by VALU work of the previous tile's epilogue;
-      // the fragment reads after the tile's MFMAs
+          for (int mt = 0; mt < MT; ++mt)
+            acc[t & 1][mt] =
+                mfma_k32(qa[mt][ks], kb[t & 1][ks], ks ? acc[t & 1][mt] : f32x4{0.f, 0.f, 0.f, 0.f});
+        if (t > 0) part[t - 1] = tile_epi(acc[(t - 1) & 1], QK == 2 ? key_scale(g, 16 * (tb + t - 1) + col) : 1.f, neg);
+        if (t + 1 < TPW) tile_frags(g, tb + t + 1, kb[(t + 1) & 1]);
+        else tile_frags(g + 1, tb, kb[(t + 1) & 1]);
+        // each MFMA followed by VALU work of the previous tile's epilogue;
+        // the fragment reads after the tile's MFMAs
 #pragma unroll
-      for (int i = 0; i < MT * NKS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        for (int i = 0; i < MT * NKS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      part[TPW - 1] = tile_epi(acc[(TPW - 1) & 1], QK == 2 ? key_scale(g, 16 * (tb + TPW - 1) + col) : 1.f, neg);
+    };
+    // a negative row scale among the keys of this wave's tiles is rare: the
+    // group runs the form without the per-head factor otherwise (same bits)
+    bool neg = false;
+    if constexpr (QK == 2) {
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < TPW / 4; ++u) any |= key_scale(g, 16 * tb + 64 * u + lane) < 0.f;
+      neg = __ballot(any) != 0ull;
     }
-    part[TPW - 1] = tile_epi(acc[(TPW - 1) & 1], QK == 2 ? key_scale(g, 16 * (tb + TPW - 1) + col) : 1.f);
+    if (neg) run_tiles(std::integral_constant<bool, true>{});
+    else run_tiles(std::integral_constant<bool, false>{});
 #pragma unroll
     for (int h = 0; h < TPW / 4; ++h) {
       const float p4[4] = {part[4 * h], part[4 * h + 1], part[4 * h + 2], part[4 * h + 3]};
