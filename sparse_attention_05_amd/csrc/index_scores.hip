@@ -838,7 +838,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
   const int groups = k_end > k_beg ? int((k_end - k_beg + PK - 1) / PK) : 0;
   if (groups == 0) return;  // the same for every wave of the workgroup
 
-  // Group g is the buffer of key rows k_beg + 128*g .. k_end-1 (rows past
+  // Group g is the buffer of key rows k_beg + PK*g .. k_end-1 (rows past
   // the range read as zeros); this lane's byte offset in it for each of the
   // wave's loads is the same in every group.
   const char* keys = static_cast<const char*>(a.keys) + (base + k_beg) * C::ROW;
@@ -994,7 +994,7 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
 
   // this wave's score row from key k_beg, as a buffer that ends at the row's
   // end: stores past it are dropped; likewise its score sample (every 16th
-  // key; k_beg is a multiple of 128)
+  // key; k_beg is a multiple of PK)
   const int64_t own = n_w > k_beg ? n_w - k_beg : 0;
   const __amdgpu_buffer_rsrc_t srow = __builtin_amdgcn_make_buffer_rsrc(
       a.scores + int64_t(rv ? rr : 0) * a.ld + k_beg, 0, int(own * 4), 0x00020000);
