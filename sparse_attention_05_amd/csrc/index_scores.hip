@@ -1041,15 +1041,15 @@ __global__ __launch_bounds__(kPfWaves * 64) void index_scores_prefill_kernel(Ind
         if (t > 0) part[t - 1] = tile_epi(acc[(t - 1) & 1], QK == 2 ? key_scale(g, 16 * (tb + t - 1) + col) : 1.f, neg);
         if (t + 1 < TPW) tile_frags(g, tb + t + 1, kb[(t + 1) & 1]);
         else tile_frags(g + 1, tb, kb[(t + 1) & 1]);
-        // each MFMA followed by VALU work of the previous tile's epilogue;
-        // the fragment reads after the tile's MFMAs
+        // the next tile's fragment reads first, then each MFMA followed by
+        // VALU work of the previous tile's epilogue
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
 #pragma unroll
         for (int i = 0; i < MT * NKS; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       part[TPW - 1] = tile_epi(acc[(TPW - 1) & 1], QK == 2 ? key_scale(g, 16 * (tb + TPW - 1) + col) : 1.f, neg);
