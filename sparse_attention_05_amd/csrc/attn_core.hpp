@@ -434,27 +434,22 @@ __device__ __forceinline__ void attend_f32(const AttnArgs& a, int r, int split, 
   write_result(a, r, split, splits, h, wave, col, grp, acc, m_run, l_part, sm.s_l);
 }
 
-// ---- bf16 rows, gathered through registers ------------------------------------------------
+// ---- bf16 rows, gathered by direct loads ---------------------------------------------------
 // The workgroup has 8 waves: waves 0..3 compute (the q.c / softmax / p.c of
-// attend, unchanged), waves 4..7 gather. Gather wave p brings rows 16p ..
-// 16p+15 of each 64-row chunk into registers: lane (i = lane/8, q = lane%8)
-// loads 16-byte piece q of every 128-byte line m (0..8) of rows 16p + i and
-// 16p + 8 + i, so eight lanes read one whole line (a 1152-byte row is nine
-// lines) -- twice the bytes per request of four lanes on 64-byte halves, and
-// measured about 1.5x the per-CU rate of direct-to-LDS loads. It then stores
-// the rows into the chunk buffer in the block layout (blk_off) that the
-// compute waves read. Chunk 0 travels alone; after it, two chunks are in
-// flight in registers while two sit in the LDS buffers, and the barriers between the roles order LDS only: a
-// plain workgroup barrier would also drain the gathers in flight.
+// attend, unchanged), waves 4..7 stage the query and gather. Rows 16w ..
+// 16w+15 of a 64-row chunk form block w of the chunk buffer (blk_off), and a
+// block is 18 direct loads: load m puts piece 4m + ((l%4) ^ blk_sw(l/4)) of
+// the block's row l/4 at byte 1024m + 16l of the block, which is its place
+// in the layout; a missing row's lanes write zeros there instead. Chunk 0
+// goes out from the compute waves and chunk 1 from the gather waves, both
+// before the first q.c, so a split of two chunks has all its rows in flight
+// from eight waves at once; a later chunk goes out into the buffer of the
+// chunk two before it as soon as that one's p.c is done.
 constexpr int kAttnWaves8 = 8;
-constexpr int kGatherLines = kLatentDim * 2 / 128;  // 128-byte lines per bf16 row (9)
+constexpr int kBlockLoads = kLatentDim * 2 / 64;  // 1-KiB direct loads per 16-row block (18)
 
+// A barrier that orders LDS only: the direct loads in flight stay in flight.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-struct RowRegs {
-  uint4 v[2][kGatherLines];
-  bool live[2];
-};
 
 // The range's raw indices s_idx[0 .. span) become cache rows (-1: missing
 // key), by all threads of the workgroup, every lookup in flight at once (a
@@ -477,22 +472,29 @@ __device__ __forceinline__ void rows_of_indices(const AttnArgs& a, int64_t base,
   }
 }
 
-// Issue the loads of gather wave p's rows of chunk c (cache rows in s_row,
-// -1 for a missing key, which reads row 0 and is stored as zeros).
-__device__ __forceinline__ void rows_issue(const AttnArgs& a, const int* s_row, int c, int p, int lane, RowRegs& rr) {
-  int row[2];
+// Issue the direct loads of block `blk` of chunk c (cache rows in s_row, -1
+// for a missing key) into `buf`; returns the 16-bit mask of present rows.
+// The caller waits (vm_wait_all) before the barrier that publishes the chunk.
+__device__ __forceinline__ uint32_t gather_block(const AttnArgs& a, const int* s_row, int c, char* buf, int blk,
+                                                 int lane) {
+  const int i = lane >> 2;
+  const int row = s_row[kChunkKeys * c + 16 * blk + i];
+  const bool live = row >= 0;
+  const unsigned long long okm = __ballot(live && (lane & 3) == 0);  // bit 4i: row i
+  uint32_t ok = 0;
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    row[g] = s_row[kChunkKeys * c + 16 * p + 8 * g + (lane >> 3)];
-    rr.live[g] = row[g] >= 0;
+  for (int k = 0; k < 16; ++k) ok |= uint32_t((okm >> (4 * k)) & 1ull) << k;
+  char* b = buf + kBlock * blk;
+  if (live) {
+    const char* src = static_cast<const char*>(a.latent) + int64_t(row) * 1152 + 16 * ((lane & 3) ^ blk_sw(i));
+    const uint32_t d = lds_addr(b);
+#pragma unroll
+    for (int m = 0; m < kBlockLoads; ++m) dma16(src + 64 * m, d + 1024 * m);
+  } else {
+#pragma unroll
+    for (int m = 0; m < kBlockLoads; ++m) *reinterpret_cast<uint4*>(b + 1024 * m + 16 * lane) = uint4{0u, 0u, 0u, 0u};
   }
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.latent) +
-                                                      int64_t(rr.live[g] ? row[g] : 0) * 1152 + 16 * (lane & 7));
-#pragma unroll
-    for (int m = 0; m < kGatherLines; ++m) rr.v[g][m] = src[8 * m];
-  }
+  return ok;
 }
 
 // The query rows of the workgroup's 16 heads (16 x 72 pieces of 16 bytes),
@@ -527,37 +529,17 @@ __device__ __forceinline__ void q_store(const QRegs& qr, char* dst, int p, int l
   }
 }
 
-// Store gather wave p's rows into `buf` (rows of missing keys as zeros, so
-// that p.c adds exactly 0 for them) and return the 16-bit mask of present
-// rows. Piece 8m + q of row 16p + 8g + i goes to blk_off (blk_sw(8g + i) =
-// blk_sw(i)): per store, two 512-byte runs.
-__device__ __forceinline__ uint32_t rows_store(const RowRegs& rr, char* buf, int p, int lane) {
-  const int i = lane >> 3, q = lane & 7;
-  char* dst = buf + kBlock * p + 1024 * (q >> 2) + 16 * ((q & 3) ^ blk_sw(i)) + 64 * i;
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int m = 0; m < kGatherLines; ++m)
-      *reinterpret_cast<uint4*>(dst + 2048 * m + 512 * g) = rr.live[g] ? rr.v[g][m] : uint4{0u, 0u, 0u, 0u};
-  const unsigned long long b0 = __ballot(rr.live[0] && q == 0), b1 = __ballot(rr.live[1] && q == 0);
-  uint32_t mask = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    mask |= (uint32_t((b0 >> (8 * k)) & 1ull) << k) | (uint32_t((b1 >> (8 * k)) & 1ull) << (8 + k));
-  return mask;
-}
-
 // attend() for bf16 rows with gather waves: the same split, arithmetic and
 // order of operations as attend<false>, hence the same bits. All 8 waves call
 // it; s_row holds the range's cache rows (rows_of_indices), filled by the
-// caller, and qr the gather waves' query pieces (q_issue). After a prologue
-// (chunk 0 and the query staged; the query read into the compute waves'
-// registers, which frees buffer 1), the two roles run separate loops with
-// the same barriers, per chunk c:
-//   compute: q.c(c) | B1 | softmax(c) | B2 | p.c(c)                    | B3
-//   gather :        | B1 |            | B2 | store c+1, issue c+3     | B3
-// (buffer c%2 holds chunk c; chunk c+1's buffer last held chunk c-1, whose
-// p.c ended before B1), so their registers never live at the same time.
+// caller, and qr the gather waves' query pieces (q_issue). Prologue: the
+// compute waves issue chunk 0 into buffer 0 while the gather waves stage the
+// query in buffer 1; the compute waves read the query into registers, which
+// frees buffer 1 for chunk 1 (gather waves); chunk 0 lands. Then the two
+// roles run separate loops with the same barriers, per chunk c:
+//   compute: q.c(c) | B1 | softmax(c) | B2 | p.c(c)             | B3 |
+//   gather :        | B1 |            | B2 | wait for c+1      | B3 | issue c+2
+// (buffer c%2 holds chunk c, and takes chunk c+2 once B3 has closed c's p.c).
 __device__ __forceinline__ void attend_bf16(const AttnArgs& a, int r, int split, int splits, int hg, int j_beg,
                                             int j_end, const int* s_row, const QRegs& qr, Smem<false>& sm) {
   using Cfg = AttnCfg<false>;
@@ -567,36 +549,26 @@ __device__ __forceinline__ void attend_bf16(const AttnArgs& a, int r, int split,
   const int nchunks = j_end > j_beg ? (j_end - j_beg + kChunkKeys - 1) / kChunkKeys : 0;
 
   if (wave >= 4) {
-    // ---- gather waves: chunk j travels in register set j % 2 -----------------------------
+    // ---- gather waves: block p of chunks 1, 2, ... ---------------------------------------
     const int p = wave - 4;
-    RowRegs rs[2];
-    if (nchunks > 0) {
-      // chunk 0 alone first, so that it lands as early as the CU's load rate
-      // allows and its compute overlaps the transfer of the next ones
-      rows_issue(a, s_row, 0, p, lane, rs[0]);
-      q_store(qr, sm.buf + Cfg::BUF_BYTES, p, lane);
-      const uint32_t m0 = rows_store(rs[0], sm.buf, p, lane);
-      if (lane == 0) sm.s_ok[0][p] = m0;
-      if (nchunks > 1) rows_issue(a, s_row, 1, p, lane, rs[1]);
-      if (nchunks > 2) rows_issue(a, s_row, 2, p, lane, rs[0]);
-    }
-    lds_sync();  // chunk 0 in buffer 0, the query staged in buffer 1
+    if (nchunks > 0) q_store(qr, sm.buf + Cfg::BUF_BYTES, p, lane);
+    lds_sync();  // the query staged in buffer 1
     lds_sync();  // the compute waves have read the query: buffer 1 is free
-    auto step = [&](int c, auto next_c) {
-      constexpr int NEXT = decltype(next_c)::value;  // register set of chunk c+1
+    if (nchunks > 1) {
+      const uint32_t m1 = gather_block(a, s_row, 1, sm.buf + Cfg::BUF_BYTES, p, lane);
+      if (lane == 0) sm.s_ok[1][p] = m1;
+    }
+    lds_sync();  // chunk 0 in buffer 0
+    for (int c = 0; c < nchunks; ++c) {
       lds_sync();  // B1
       lds_sync();  // B2
-      if (c + 1 < nchunks) {
-        const int bn = (c + 1) & 1;
-        const uint32_t mk = rows_store(rs[NEXT], sm.buf + bn * Cfg::BUF_BYTES, p, lane);
-        if (lane == 0) sm.s_ok[bn][p] = mk;
-        if (c + 3 < nchunks) rows_issue(a, s_row, c + 3, p, lane, rs[NEXT]);
-      }
+      if (c + 1 < nchunks) vm_wait_all();  // this wave's block of chunk c+1 has landed
       lds_sync();  // B3
-    };
-    for (int c = 0; c < nchunks; c += 2) {
-      step(c, std::integral_constant<int, 1>{});
-      if (c + 1 < nchunks) step(c + 1, std::integral_constant<int, 0>{});
+      if (c + 2 < nchunks) {
+        const int bn = c & 1;
+        const uint32_t mk = gather_block(a, s_row, c + 2, sm.buf + bn * Cfg::BUF_BYTES, p, lane);
+        if (lane == 0) sm.s_ok[bn][p] = mk;
+      }
     }
     lds_sync();  // the row sums
     return;
@@ -605,12 +577,18 @@ __device__ __forceinline__ void attend_bf16(const AttnArgs& a, int r, int split,
   // ---- compute waves ------------------------------------------------------------------------
   const int col = lane & 15, grp = lane >> 4;
   const int h = hg * kGroupHeads + col;
-  lds_sync();  // chunk 0 in buffer 0, the query staged in buffer 1
+  if (nchunks > 0) {
+    const uint32_t m0 = gather_block(a, s_row, 0, sm.buf, wave, lane);
+    if (lane == 0) sm.s_ok[0][wave] = m0;
+  }
+  lds_sync();  // the query staged in buffer 1
   bf16x8 qf[18];  // B operand of q.c: head h, dims 32*ks + 8*grp .. +8
 #pragma unroll
   for (int ks = 0; ks < 18; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8*>(sm.buf + Cfg::BUF_BYTES + 16 * (kQPitch * col + 4 * ks + grp));
   lds_sync();  // buffer 1 is free
+  vm_wait_all();  // this wave's block of chunk 0 has landed
+  lds_sync();  // chunk 0 in buffer 0
   f32x4 acc[8];
 #pragma unroll
   for (int vt = 0; vt < 8; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_mla_kernel(AttnArgs a, in
 }
 
 // bf16 rows: 8 waves, the four compute waves of sparse_mla_kernel plus four
-// waves that gather the rows through registers (attend_bf16).
+// waves that stage the query and gather rows by direct loads (attend_bf16).
 __global__ __launch_bounds__(kAttnWaves8 * 64) void sparse_mla_bf16_kernel(AttnArgs a, int splits, int kps) {
   __shared__ Smem<false> sm;
   __shared__ int s_idx[kMaxTopk];  // the range's cache rows, -1 past it up to the chunk boundary
