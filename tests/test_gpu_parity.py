@@ -295,6 +295,33 @@ def test_attention_holes_and_empty_rows(dsa):
     C.assert_attn_close(out[:3], ref[:3], lse[:3], lse_ref[:3])
 
 
+def test_attention_missing_keys_never_touch_other_rows(dsa):
+    """A missing key (-1: a hole, a row shorter than k, the chunk tail past a
+    split's end) contributes exactly nothing: the gather writes zeros for it
+    instead of loading a cache row. Every sequence's position 0 (cache row 0
+    among them) and a row past every sequence hold NaN and are never selected,
+    so a missing key that read any of them would turn the outputs into NaN."""
+    p = inputs.decode_config([3000, 2500, 4096, 100], seed=11, H=64, k=2048)
+    nan_bf16 = np.uint16(0x7FC0)
+    for b in range(p.B):
+        p.latent[int(p.row_off[b])] = nan_bf16
+    p.latent = np.concatenate([p.latent, np.full((1, 576), nan_bf16, np.uint16)])
+    rng = np.random.default_rng(5)
+    idx = np.full((p.R, 2048), -1, np.int32)
+    for r in range(p.R):
+        n = int(p.q_pos[r]) + 1
+        m = min(2048, n - 1) if r != 1 else 700           # row 1: a ragged -1 tail inside a chunk
+        idx[r, :m] = 1 + rng.choice(n - 1, size=m, replace=False)
+    idx[rng.random(idx.shape) < 0.2] = -1                   # holes anywhere
+    idx[3] = -1                                             # a row with no valid key
+    _say("attention missing keys, NaN rows unselected")
+    out, lse = _gpu_attn(dsa, p, idx)
+    ref, lse_ref = O.sparse_mla(p, idx)
+    assert np.isfinite(out).all() and np.isfinite(lse[:3]).all()
+    assert (out[3] == 0).all() and np.isneginf(lse[3]).all()
+    C.assert_attn_close(out[:3], ref[:3], lse[:3], lse_ref[:3])
+
+
 @pytest.mark.parametrize("std,k", [(1.0, 512), (30.0, 512), (3.0, 200)])
 def test_attention_many_queries_matches_oracle(dsa, std, k):
     """Enough queries for the one-workgroup-per-query (all heads) kernel:
